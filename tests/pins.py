@@ -1,0 +1,238 @@
+"""Pins for the oracle: checks against facts the pages or the mathematics fix.
+
+Each ``pin_*`` takes an attention function with the oracle's signature
+``attn(q, k, v, scale, causal, kv_len) -> (O, LSE)`` and raises AssertionError
+when it disagrees.  ``tests/test_oracle_pins.py`` runs them on the oracle;
+``tests/test_oracle_mutants.py`` runs them on copies of the oracle with a
+planted mistake and expects at least one to fail.
+"""
+import math
+
+import mpmath
+import numpy as np
+
+from exact_attention_33_amd.inputs import normal_f32
+
+mpmath.mp.dps = 50
+
+
+def _rand(seed, B, H, N, M, D):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, H, N, D)), rng.standard_normal((B, H, M, D)),
+            rng.standard_normal((B, H, M, D)))
+
+
+def brute_force(q, k, v, scale, causal, kv_len):
+    """50-digit evaluation straight from the formula, without the max shift:
+    p_j = exp(s_j) / sum exp(s_j), O = sum p_j v_j, LSE = log sum exp(s_j)."""
+    B, H, N, D = q.shape
+    M = k.shape[2]
+    O = np.zeros((B, H, N, D))
+    L = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        kvl = M if kv_len is None else int(kv_len[b])
+        for h in range(H):
+            for i in range(N):
+                keys = [j for j in range(kvl)
+                        if not causal or j - (kvl - N) <= i]
+                if not keys:
+                    continue
+                s = {j: mpmath.mpf(scale) * mpmath.fsum(
+                    mpmath.mpf(q[b, h, i, d]) * mpmath.mpf(k[b, h, j, d])
+                    for d in range(D)) for j in keys}
+                z = mpmath.fsum(mpmath.exp(s[j]) for j in keys)
+                for d in range(D):
+                    O[b, h, i, d] = float(mpmath.fsum(
+                        mpmath.exp(s[j]) * mpmath.mpf(v[b, h, j, d]) for j in keys) / z)
+                L[b, h, i] = float(mpmath.log(z))
+    return O, L
+
+
+def pin_brute_force(attn):
+    """Tiny shapes (N, M <= 8, D <= 5, the sizes of the std-lib examples in
+    "Understanding FlashAttention") against 50-digit arithmetic."""
+    cases = [
+        (11, 1, 2, 8, 6, 4, 0.5, False, None),
+        (12, 1, 2, 8, 8, 4, 0.5, True, None),
+        (13, 2, 1, 3, 7, 5, 0.7, True, [7, 4]),
+        (14, 2, 1, 3, 7, 5, 0.7, False, [2, 7]),
+        (15, 1, 1, 1, 8, 4, 0.5, True, [6]),
+        (16, 1, 1, 6, 3, 4, 1.3, True, None),     # N > M: early rows see nothing
+    ]
+    for seed, B, H, N, M, D, scale, causal, kvl in cases:
+        q, k, v = _rand(seed, B, H, N, M, D)
+        O, L = attn(q, k, v, scale, causal, kvl)
+        Ob, Lb = brute_force(q, k, v, scale, causal, kvl)
+        assert np.array_equal(np.isneginf(L), np.isneginf(Lb)), "empty-row pattern"
+        fin = np.isfinite(Lb)
+        assert np.max(np.abs(O - Ob)) <= 4e-15, ("O vs brute force", seed)
+        assert np.max(np.abs(L[fin] - Lb[fin])) <= 4e-15, ("LSE vs brute force", seed)
+
+
+def pin_rows_sum_to_one(attn):
+    """Every row of P sums to 1 ("Flash Attention: The Hidden Gem", Safe
+    Softmax: the norm factor makes the outputs sum to one).  With V = 1 the
+    output is that row sum."""
+    q, k, _ = _rand(21, 2, 2, 16, 24, 8)
+    v = np.ones_like(k)
+    for causal, kvl in ((False, None), (True, None), (True, [24, 9]), (False, [5, 24])):
+        O, L = attn(q, k, v, 0.35, causal, kvl)
+        fin = np.isfinite(L)
+        assert np.max(np.abs(O[fin] - 1.0)) <= 1e-14, (causal, kvl)
+
+
+def pin_causal_row0(attn):
+    """Causal with N = M: query 0 sees only key 0, so O_0 = v_0 exactly and
+    LSE_0 = scale * q_0 . k_0."""
+    q, k, v = _rand(31, 1, 3, 10, 10, 16)
+    scale = 0.25
+    O, L = attn(q, k, v, scale, True, None)
+    assert np.array_equal(O[:, :, 0], v[:, :, 0])
+    s00 = scale * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0])
+    assert np.max(np.abs(L[:, :, 0] - s00)) <= 1e-14
+
+
+def pin_uniform_scores(attn):
+    """Q = 0 makes every visible score 0: O_i is the mean of the visible V
+    rows and LSE_i = ln(number visible): ln M without mask, ln(i + 1) causal
+    with N = M, ln(kv_len) with a key count."""
+    _, k, v = _rand(41, 2, 2, 12, 12, 6)
+    q = np.zeros((2, 2, 12, 6))
+    O, L = attn(q, k, v, 0.4, False, None)
+    assert np.max(np.abs(O - v.mean(axis=2, keepdims=True))) <= 1e-14
+    assert np.max(np.abs(L - math.log(12))) <= 1e-14
+    O, L = attn(q, k, v, 0.4, True, None)
+    for i in range(12):
+        assert np.max(np.abs(O[:, :, i] - v[:, :, :i + 1].mean(axis=2))) <= 1e-14
+        assert np.max(np.abs(L[:, :, i] - math.log(i + 1))) <= 1e-14
+    O, L = attn(q, k, v, 0.4, False, [7, 3])
+    assert np.max(np.abs(O[0] - v[0, :, :7].mean(axis=1, keepdims=True))) <= 1e-14
+    assert np.max(np.abs(O[1] - v[1, :, :3].mean(axis=1, keepdims=True))) <= 1e-14
+    assert np.max(np.abs(L[0] - math.log(7))) <= 1e-14
+    assert np.max(np.abs(L[1] - math.log(3))) <= 1e-14
+
+
+def pin_overflow_shift(attn):
+    """Adding the same constant to every score of a row changes nothing but
+    LSE ("Flash Attention: The Hidden Gem", Safe Softmax).  Setting K[:, 0] = 1
+    and adding delta/scale to Q[:, 0] shifts every score by delta; at
+    delta = 800 a plain exp overflows ("Now break it": [nan nan nan nan])."""
+    q, k, v = _rand(51, 1, 2, 9, 11, 4)
+    scale = 0.5
+    k[..., 0] = 1.0
+    O0, L0 = attn(q, k, v, scale, False, None)
+    for delta in (100.0, 800.0, -800.0):
+        q2 = q.copy()
+        q2[..., 0] += delta / scale
+        O1, L1 = attn(q2, k, v, scale, False, None)
+        assert np.all(np.isfinite(O1)) and np.all(np.isfinite(L1))
+        assert np.max(np.abs(O1 - O0)) <= 1e-11, delta
+        assert np.max(np.abs((L1 - L0) - delta)) <= 1e-11, delta
+
+
+def pin_single_and_two_keys(attn):
+    """M = 1: the weight is 1, O = v_0, LSE = s_0.  M = 2: the weight of key 0
+    is the logistic 1 / (1 + e^(s_1 - s_0)) and LSE = logaddexp(s_0, s_1)."""
+    q, k, v = _rand(61, 1, 2, 5, 1, 3)
+    O, L = attn(q, k, v, 0.9, False, None)
+    assert np.max(np.abs(O - v)) <= 1e-15
+    assert np.max(np.abs(L - 0.9 * (q @ np.swapaxes(k, -1, -2))[..., 0])) <= 1e-14
+    q, k, v = _rand(62, 1, 2, 5, 2, 3)
+    O, L = attn(q, k, v, 0.9, False, None)
+    s = 0.9 * np.einsum("bhnd,bhmd->bhnm", q, k)
+    w0 = 1.0 / (1.0 + np.exp(s[..., 1] - s[..., 0]))
+    expect = w0[..., None] * v[:, :, None, 0] + (1 - w0)[..., None] * v[:, :, None, 1]
+    assert np.max(np.abs(O - expect)) <= 1e-14
+    assert np.max(np.abs(L - np.logaddexp(s[..., 0], s[..., 1]))) <= 1e-14
+
+
+def pin_key_permutation(attn):
+    """Without a causal mask the keys form a set: permuting K and V rows
+    together leaves O and LSE unchanged."""
+    q, k, v = _rand(71, 1, 2, 7, 9, 5)
+    perm = np.random.default_rng(3).permutation(9)
+    O0, L0 = attn(q, k, v, 0.6, False, None)
+    O1, L1 = attn(q, k[:, :, perm], v[:, :, perm], 0.6, False, None)
+    assert np.max(np.abs(O0 - O1)) <= 1e-14
+    assert np.max(np.abs(L0 - L1)) <= 1e-14
+
+
+def pin_decode_history(attn):
+    """One query against a KV cache ("Understanding FlashAttention",
+    Attention: N = 1 while M holds the history): with the causal flag the
+    query still sees every cached key, so the result equals the unmasked one;
+    and a key count equals cutting the cache to that many rows."""
+    q, k, v = _rand(81, 3, 2, 1, 12, 4)
+    kvl = [12, 5, 1]
+    Oc, Lc = attn(q, k, v, 0.5, True, kvl)
+    On, Ln = attn(q, k, v, 0.5, False, kvl)
+    assert np.max(np.abs(Oc - On)) <= 1e-15 and np.max(np.abs(Lc - Ln)) <= 1e-15
+    for b, n in enumerate(kvl):
+        Ot, Lt = attn(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], 0.5, False, None)
+        assert np.max(np.abs(On[b:b + 1] - Ot)) <= 1e-15
+        assert np.max(np.abs(Ln[b:b + 1] - Lt)) <= 1e-15
+
+
+def pin_masked_rows(attn):
+    """A row with no visible key returns O = 0 and LSE = -inf, never NaN, and
+    NaN stored in keys/values past kv_len never reaches the output."""
+    q, k, v = _rand(91, 2, 1, 4, 6, 3)
+    k[1, :, 2:] = np.nan
+    v[1, :, 2:] = np.nan
+    O, L = attn(q, k, v, 0.5, False, [0, 2])
+    assert np.all(O[0] == 0) and np.all(np.isneginf(L[0]))
+    assert np.all(np.isfinite(O[1])) and np.all(np.isfinite(L[1]))
+    # causal with N > kv_len: the first N - kv_len rows see nothing
+    O, L = attn(q, k, v, 0.5, True, [6, 2])
+    assert np.all(np.isneginf(L[1, :, :2])) and np.all(O[1, :, :2] == 0)
+    assert np.all(np.isfinite(L[1, :, 2:]))
+
+
+def pin_scale_on_scores(attn):
+    """The scale multiplies the scores; applying it to Q first is the same
+    function ("Understanding FlashAttention", Attention, Simplification 1)."""
+    q, k, v = _rand(95, 1, 2, 6, 7, 4)
+    O0, L0 = attn(q, k, v, 0.3, True, None)
+    O1, L1 = attn(q * 0.3, k, v, 1.0, True, None)
+    assert np.max(np.abs(O0 - O1)) <= 1e-14 and np.max(np.abs(L0 - L1)) <= 1e-14
+
+
+ALL_ATTN_PINS = [pin_brute_force, pin_rows_sum_to_one, pin_causal_row0,
+                 pin_uniform_scores, pin_overflow_shift, pin_single_and_two_keys,
+                 pin_key_permutation, pin_decode_history, pin_masked_rows,
+                 pin_scale_on_scores]
+
+
+def read_golden(name):
+    from tests.conftest import golden_path
+    rows = {}
+    with open(golden_path(name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            rows.setdefault(key, []).append(vals)
+    return rows
+
+
+def pin_p2_online_row(safe_softmax, online_softmax):
+    """The 32-score row of "FlashAttention: attention was never
+    compute-bound", Online softmax: the whole idea, in two variables."""
+    g = read_golden("p2_online_softmax_row.txt")
+    seed = int(g["row_seed"][0][0])
+    scale = float(g["row_scale"][0][0])
+    n = int(g["row_len"][0][0])
+    blk = int(g["block"][0][0])
+    row = np.random.default_rng(seed).standard_normal(n) * scale
+    ordinary = safe_softmax(row)[0]
+    online = online_softmax(row, block=blk)
+    broken = online_softmax(row, block=blk, rescale=False)
+    as_f = lambda key: np.array([float(x) for x in g[key][0]])
+    assert np.allclose(ordinary[:6], as_f("correct_first6"), rtol=0, atol=5e-7)
+    assert np.allclose(online[:6], as_f("online_first6"), rtol=0, atol=5e-7)
+    assert np.allclose(broken[:6], as_f("broken_first6"), rtol=0, atol=5e-7)
+    assert float(f"{np.max(np.abs(online - ordinary)):.2e}") == float(g["online_vs_ordinary_maxabs"][0][0])
+    assert float(f"{np.max(np.abs(broken - ordinary)):.2e}") == float(g["norescale_vs_ordinary_maxabs"][0][0])
+    assert f"{broken.sum():.6f}" == g["norescale_sum"][0][0]
+    return row, ordinary, online, broken

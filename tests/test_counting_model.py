@@ -1,0 +1,68 @@
+"""The counting model against every printed row of the explainer's tables."""
+import math
+
+from oracle import counting as C
+from tests.pins import read_golden
+
+D = 64
+
+
+def fmt(x, nd):
+    return f"{x:.{nd}f}"
+
+
+def test_traffic_table():
+    for n, mb, gf, bpf, share in read_golden("p2_counting_tables.txt")["traffic"]:
+        n = int(n)
+        nb = C.naive_bytes(n, D)
+        fl = C.attention_flops(n, D)
+        assert fmt(nb / C.MiB, 2) == mb
+        assert fmt(fl / 1e9, 3) == gf
+        assert fmt(nb / fl, 3) == bpf
+        assert fmt(100 * 4 * n * n / C.naive_elems(n, D), 1) == share
+
+
+def test_tiling_table():
+    for n, std_kb, fl_kb, std_mb, fl_mb in read_golden("p2_counting_tables.txt")["tiling"]:
+        n = int(n)
+        assert fmt(4 * C.std_peak_elems(n) / 1024, 1) == std_kb
+        assert fmt(4 * C.working_set_elems(D, 64, 64) / 1024, 1) == fl_kb
+        assert fmt(C.naive_bytes(n, D) / C.MiB, 2) == std_mb
+        assert fmt(C.flash_bytes(n, D, 64) / C.MiB, 2) == fl_mb
+
+
+def test_block_size_table():
+    for blk, mb, ws_kb, fits in read_golden("p2_counting_tables.txt")["block"]:
+        blk = int(blk)
+        assert fmt(C.flash_bytes(1024, D, blk) / C.MiB, 2) == mb
+        ws = 4 * C.working_set_elems(D, blk, blk) / 1024
+        assert fmt(ws, 1) == ws_kb
+        assert (ws <= 96) == (fits == "yes")
+    assert fmt(C.naive_bytes(1024, D) / C.MiB, 2) == "17.00"
+
+
+def test_backward_table():
+    for n, std_mb, fl_mb, std_gf, fl_gf, extra in read_golden("p2_counting_tables.txt")["backward"]:
+        n = int(n)
+        assert fmt(4 * C.bwd_std_stored_elems(n, D) / C.MiB, 2) == std_mb
+        assert fmt(4 * C.bwd_flash_stored_elems(n, D) / C.MiB, 2) == fl_mb
+        assert fmt(C.bwd_std_flops(n, D) / 1e9, 2) == std_gf
+        assert fmt(C.bwd_flash_flops(n, D) / 1e9, 2) == fl_gf
+        assert round(100 * (C.bwd_flash_flops(n, D) / C.bwd_std_flops(n, D) - 1)) == int(extra)
+
+
+def test_same_flops_table():
+    for n, sg, fg, smb, fmb, cut in read_golden("p2_counting_tables.txt")["same_flops"]:
+        n = int(n)
+        assert fmt(C.attention_flops(n, D) / 1e9, 3) == sg == fg
+        assert fmt(C.naive_bytes(n, D) / C.MiB, 2) == smb
+        assert fmt(C.flash_bytes(n, D, 64) / C.MiB, 2) == fmb
+        assert fmt(C.naive_bytes(n, D) / C.flash_bytes(n, D, 64), 1) == cut
+
+
+def test_long_prefill_naive_bytes():
+    """The n = 8192, d = 64 row (1032 MB per head) scaled to B=2, H=32."""
+    assert C.naive_bytes(8192, 64) == 1032 * (1 << 20)
+    assert 64 * C.naive_bytes(8192, 64) == 69_256_347_648
+    assert 64 * C.naive_bytes(8192, 128, elem=2) == 34_896_609_280
+    assert math.isclose(C.attention_flops(8192, 64) / 1e9, 17.179869184)
