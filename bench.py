@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused exact-attention forward on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+  1. the fused prefill forward (bf16, causal) on B=2, H=32, N=M=8192, D=128;
+  2. the split-KV decode (partial + merge kernels) on B=32 sequences, H=32,
+     N=1, D=128, per-sequence KV length uniform in [1024, 32768].
+Inputs are N(0, 1) drawn on the device from fixed seeds and are resident in
+HBM before timing starts.
+
+`value` is the prefill throughput in TFLOP/s with the FLOP convention
+4*B*H*N*M*D, halved for causal; the decode throughput (KV-cache bytes read
+per second) is reported beside it.  Each launch is timed with HIP events on
+the stream it runs on.  The CPU oracle (fp64 NumPy) is timed on a bounded
+sample of the same tensors on this host, and its results double as a parity
+check of the sampled heads.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak; decode KV GB/s & % HBM peak"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "exact_attention_33_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+SOURCES = {"prefill": ["prefill_bf16.hip", "device_common.h", "fa_internal.h"],
+           "decode": ["decode_bf16.hip", "device_common.h", "fa_internal.h"]}
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch from the committed counter profile, or None when
+    the kernel source changed since the counters were taken."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f).get(kind)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_sha(SOURCES[kind]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="run one leg only (for counter runs); 'copy' runs a plain "
+                         "device copy of known size for counter calibration")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="prefill heads the oracle times")
+    ap.add_argument("--cpu-decode-heads", type=int, default=1024)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU "
+              "only (no collectives, no sharding); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import exact_attention_33_amd as fa
+    from exact_attention_33_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fa.lib()  # fail loudly if the HIP library is missing
+    stream = torch.cuda.Stream(device=dev)
+
+    if args.only == "copy":
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": nbytes, "launches": args.steps}))
+        return 0
+
+    wp = inputs.WORKLOADS["prefill_long_d128"]
+    wd = inputs.WORKLOADS["decode"]
+    do_p = args.only in ("all", "prefill")
+    do_d = args.only in ("all", "decode")
+
+    # ---- inputs, resident in HBM before timing ----
+    if do_p:
+        qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
+        op = torch.empty_like(qp)
+        lp = torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
+        scale_p = 1.0 / math.sqrt(wp.D)
+        flop_p = 4.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0   # causal convention
+    if do_d:
+        kvl_h = inputs.kv_lens(wd.kv_seed, wd.B, *wd.kv_range)
+        Md = int(kvl_h.max())
+        qd, kd, vd = inputs.qkv_device(wd.seed, wd.B, wd.H, 1, Md, wd.D, "bf16", dev)
+        kvl_d = torch.as_tensor(kvl_h, device=dev)
+        od = torch.empty_like(qd)
+        ld = torch.empty((wd.B, wd.H, 1), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, fa.workspace_bytes(wd.B, wd.H, 1, Md, wd.D)), dtype=torch.uint8,
+                         device=dev)
+        scale_d = 1.0 / math.sqrt(wd.D)
+        kv_bytes = float(kvl_h.astype(np.int64).sum()) * wd.H * wd.D * 2 * 2
+        plan_d = fa.plan(wd.B, wd.H, 1, Md, wd.D)
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        with torch.cuda.stream(stream):
+            if do_p:
+                if evs: evs[0].record(stream)
+                fa.fwd(qp, kp, vp, scale=scale_p, causal=True, out=op, lse=lp, stream=stream)
+                if evs: evs[1].record(stream)
+            if do_d:
+                if evs: evs[2].record(stream)
+                fa.fwd(qd, kd, vd, scale=scale_d, causal=False, kv_len=kvl_d, out=od, lse=ld,
+                       workspace=ws, stream=stream)
+                if evs: evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_p = [e[0].elapsed_time(e[1]) for e in events] if do_p else []
+    ms_d = [e[2].elapsed_time(e[3]) for e in events] if do_d else []
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": 1e3 * wall / max(1, args.steps), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic: Q/K/V i.i.d. N(0,1) from fixed seeds (device generator), "
+                   "decode KV lengths uniform [1024, 32768] from seed 7"}
+    cfg = {"workload": "causal prefill B=2 H=32 N=M=8192 D=128 bf16 + split-KV decode "
+                       "B=32 H=32 N=1 D=128 bf16 kv_len~U[1024,32768]",
+           "prefill": {"B": wp.B, "H": wp.H, "N": wp.N, "M": wp.M, "D": wp.D, "causal": True},
+           "decode": {"B": wd.B, "H": wd.H, "N": 1, "D": wd.D, "kv_seed": wd.kv_seed,
+                      "kv_range": list(wd.kv_range)}}
+    if do_p:
+        avg_p = sum(ms_p) / len(ms_p)
+        tfs = flop_p / (avg_p * 1e-3) / 1e12
+        out.update({"value": tfs, "unit": "TFLOP/s"})
+        out["prefill"] = {"ms_mean": avg_p, "ms_min": min(ms_p), "tflops": tfs,
+                          "frac_bf16_peak": tfs / PEAK_BF16_TFLOPS, "flop_per_launch": flop_p}
+        traffic = measured_traffic("prefill")
+        out["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,causal>",
+                           "achieved": tfs, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tfs / PEAK_BF16_TFLOPS, "traffic": traffic}
+    if do_d:
+        avg_d = sum(ms_d) / len(ms_d)
+        gbs = kv_bytes / (avg_d * 1e-3) / 1e9
+        out["decode"] = {"ms_mean": avg_d, "ms_min": min(ms_d), "kv_bytes": kv_bytes,
+                         "value": gbs, "unit": "GB/s", "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+                         "splits": plan_d["splits"], "split_keys": plan_d["block_k"],
+                         "roofline": {"bound": "hbm", "kernel": "splitkv partial + merge",
+                                      "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": gbs / PEAK_HBM_GBS,
+                                      "traffic": measured_traffic("decode")}}
+        if not do_p:
+            out.update({"value": gbs, "unit": "GB/s"})
+    out["config"] = cfg
+
+    if not args.no_cpu_baseline and args.only == "all":
+        out["cpu_baseline"] = cpu_baseline(args, np, torch, qp, kp, vp, op, lp, scale_p, wp,
+                                           qd, kd, vd, od, ld, kvl_h, scale_d, wd)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(args, np, torch, qp, kp, vp, op, lp, scale_p, wp, qd, kd, vd, od, ld, kvl_h,
+                 scale_d, wd):
+    """The oracle as it stands, timed on this host on a bounded sample of the
+    same tensors; its outputs are also compared with the GPU's."""
+    from oracle.attention import attention_ref
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(0)
+    # prefill sample: whole heads (every query row, all keys)
+    heads = [(0, 0), (wp.B - 1, wp.H - 1)] + [
+        (int(rng.integers(wp.B)), int(rng.integers(wp.H))) for _ in range(max(0, args.cpu_heads - 2))]
+    t_cpu, eo, el = 0.0, 0.0, 0.0
+    for b, h in heads:
+        q, k, v = f64(qp[b, h])[None, None], f64(kp[b, h])[None, None], f64(vp[b, h])[None, None]
+        t0 = time.perf_counter()
+        O, L = attention_ref(q, k, v, scale_p, True)
+        t_cpu += time.perf_counter() - t0
+        eo = max(eo, float(np.max(np.abs(f64(op[b, h]) - O[0, 0]))))
+        el = max(el, float(np.max(np.abs(f64(lp[b, h]) - L[0, 0]))))
+    flop = len(heads) * 4.0 * wp.N * wp.M * wp.D / 2.0
+    res = {"value": flop / t_cpu / 1e12, "unit": "TFLOP/s", "cores": blas_threads,
+           "kind": "oracle", "seconds": t_cpu,
+           "sample": f"{len(heads)} whole heads (N=M=8192, D=128, causal) of the bench's "
+                     f"prefill tensors, fp64 NumPy, same FLOP convention",
+           "parity_vs_gpu": {"O_max_abs": eo, "LSE_max_abs": el, "tol": [2e-2, 1e-3]}}
+    # decode sample
+    dh = [(0, 0), (wd.B - 1, wd.H - 1)] + [
+        (int(rng.integers(wd.B)), int(rng.integers(wd.H))) for _ in range(max(0, args.cpu_decode_heads - 2))]
+    t_cpu, eo, el, nbytes = 0.0, 0.0, 0.0, 0.0
+    for b, h in dh:
+        n = int(kvl_h[b])
+        q, k, v = f64(qd[b, h])[None, None], f64(kd[b, h, :n])[None, None], f64(vd[b, h, :n])[None, None]
+        t0 = time.perf_counter()
+        O, L = attention_ref(q, k, v, scale_d, False)
+        t_cpu += time.perf_counter() - t0
+        nbytes += n * wd.D * 2 * 2
+        eo = max(eo, float(np.max(np.abs(f64(od[b, h]) - O[0, 0]))))
+        el = max(el, float(np.max(np.abs(f64(ld[b, h]) - L[0, 0]))))
+    res["decode"] = {"value": nbytes / t_cpu / 1e9, "unit": "GB/s", "seconds": t_cpu,
+                     "sample": f"{len(dh)} (batch, head) pairs of the bench's decode tensors",
+                     "parity_vs_gpu": {"O_max_abs": eo, "LSE_max_abs": el, "tol": [2e-2, 1e-3]}}
+    return res
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,1 +1,180 @@
-"""exact_attention_33_amd: fused exact-attention forward for MI355X (gfx950)."""
+"""exact_attention_33_amd: fused exact-attention forward for MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/fa_mi355x.h``.  It only
+marshals arguments: torch allocates the outputs and the workspace and supplies
+the stream; every step of the computation runs in the HIP kernels of
+``lib/libfa_mi355x.so``.  There is no fallback: if the library is missing the
+first call raises.
+
+    o, lse = exact_attention_33_amd.fwd(q, k, v, scale=None, causal=False, kv_len=None)
+
+q [B,H,N,D], k/v [B,H,M,D] contiguous CUDA tensors (bf16 or float32, D in
+{64, 128}); kv_len an int32 tensor [B] on the same device (or None).  Returns
+O [B,H,N,D] (input dtype) and LSE [B,H,N] (float32, natural log).
+"""
+import ctypes
+import math
+import os
+
+__all__ = ["fwd", "plan", "workspace_bytes", "lib", "library_path", "FaError",
+           "PATH_AUTO", "PATH_PREFILL", "PATH_SPLITKV", "PATH_F32",
+           "F32", "BF16", "EXPORTS"]
+
+F32, BF16 = 0, 1
+PATH_AUTO, PATH_PREFILL, PATH_SPLITKV, PATH_F32 = 0, 1, 2, 3
+PATH_NAMES = {PATH_PREFILL: "prefill", PATH_SPLITKV: "splitkv", PATH_F32: "f32"}
+
+# Every symbol include/fa_mi355x.h declares.
+EXPORTS = ["fa_plan_query", "fa_fwd_workspace_bytes", "fa_fwd", "fa_fwd_ex",
+           "fa_status_str", "fa_last_error", "fa_abi_version"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "lib", "libfa_mi355x.so")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, name, detail):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+        self.name = name
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("M", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("split_keys", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("block_q", ctypes.c_int32),
+                ("block_k", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing: build it with "
+            "`python -m exact_attention_33_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(library_path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    L.fa_plan_query.argtypes = [Shape, i32, i32, ctypes.POINTER(Options), ctypes.POINTER(PlanInfo)]
+    L.fa_plan_query.restype = i32
+    L.fa_fwd_workspace_bytes.argtypes = [Shape, i32, i32, ctypes.POINTER(Options)]
+    L.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
+    fwd_args = [vp, vp, vp, vp, vp, vp, Shape, i32, f32, i32, vp, ctypes.c_size_t, vp]
+    L.fa_fwd.argtypes = fwd_args
+    L.fa_fwd.restype = i32
+    L.fa_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(Options)]
+    L.fa_fwd_ex.restype = i32
+    L.fa_status_str.argtypes = [i32]
+    L.fa_status_str.restype = ctypes.c_char_p
+    L.fa_last_error.argtypes = []
+    L.fa_last_error.restype = ctypes.c_char_p
+    L.fa_abi_version.argtypes = []
+    L.fa_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def _check(st):
+    if st != 0:
+        L = lib()
+        raise FaError(st, L.fa_status_str(st).decode(), L.fa_last_error().decode())
+
+
+def _options(path, split_keys):
+    if path in (None, PATH_AUTO) and not split_keys:
+        return None
+    return Options(PATH_AUTO if path is None else int(path), int(split_keys or 0))
+
+
+def _opt_ptr(o):
+    return ctypes.byref(o) if o is not None else None
+
+
+def plan(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0):
+    """The planner's decision for a shape, as a dict (host only)."""
+    info = PlanInfo()
+    o = _options(path, split_keys)
+    _check(lib().fa_plan_query(Shape(B, H, N, M, D), int(dtype), int(bool(causal)),
+                               _opt_ptr(o), ctypes.byref(info)))
+    d = {f: getattr(info, f) for f, _ in PlanInfo._fields_}
+    d["path_name"] = PATH_NAMES.get(d["path"], "?")
+    return d
+
+
+def workspace_bytes(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0):
+    o = _options(path, split_keys)
+    return int(lib().fa_fwd_workspace_bytes(Shape(B, H, N, M, D), int(dtype),
+                                            int(bool(causal)), _opt_ptr(o)))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
+        workspace=None, path=None, split_keys=0, stream=None):
+    """Exact attention forward through the C ABI; returns (O, LSE)."""
+    import torch
+    L = lib()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N|M, D]")
+    B, H, N, D = q.shape
+    M = k.shape[2]
+    if tuple(k.shape) != (B, H, M, D) or tuple(v.shape) != (B, H, M, D):
+        raise ValueError("k and v must be [B, H, M, D] matching q [B, H, N, D]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    dt = _dtype_code(q)
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if kv_len is not None:
+        if not isinstance(kv_len, torch.Tensor):
+            kv_len = torch.as_tensor(kv_len, dtype=torch.int32)
+        kv_len = kv_len.to(device=dev, dtype=torch.int32).contiguous()
+        if kv_len.numel() != B:
+            raise ValueError("kv_len must have B entries")
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    opts = _options(path, split_keys)
+    shape = Shape(B, H, N, M, D)
+    ws_need = int(L.fa_fwd_workspace_bytes(shape, dt, int(bool(causal)), _opt_ptr(opts)))
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = L.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                     kv_len.data_ptr() if kv_len is not None else None,
+                     out.data_ptr(), lse.data_ptr(), shape, dt, float(scale),
+                     int(bool(causal)), ws_ptr, ws_len, sptr or None, _opt_ptr(opts))
+    _check(st)
+    return out, lse

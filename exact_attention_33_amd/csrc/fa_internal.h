@@ -1,0 +1,70 @@
+// Internal interface between the C-ABI shim, the planner and the kernels.
+// Not installed; the public interface is include/fa_mi355x.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "fa_mi355x.h"
+
+namespace fa {
+
+// Problem description handed to every launcher.  Pointers are device
+// pointers; tensors are contiguous [B,H,N|M,D] with D fastest.
+struct Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* kv_len;  // [B] or nullptr (= M for all)
+  void* o;
+  float* lse;
+  int32_t B, H, N, M, D;
+  float scale;
+  int causal;
+};
+
+// Planner output (host-only; see plan.cpp).
+struct Plan {
+  fa_path path;
+  int32_t block_q;
+  int32_t block_k;
+  int32_t threads;
+  int32_t lds_bytes;
+  int32_t splits;       // split-KV only
+  int64_t grid;
+  size_t ws_bytes;
+  size_t ws_lse_offset;  // split-KV: byte offset of the partial LSE array
+};
+
+// Returns FA_OK and fills `plan`, or an error status with `why` set.
+fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
+                    const fa_options* opt, Plan* plan, const char** why);
+
+// Kernel launchers: enqueue on `stream`, return the launch status.
+hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, hipStream_t stream);
+hipError_t launch_fwd_f32(const Problem& p, const Plan& plan, hipStream_t stream);
+hipError_t launch_splitkv_bf16(const Problem& p, const Plan& plan, void* workspace,
+                               hipStream_t stream);
+
+// Tile constants shared by the planner and the kernels.
+constexpr int kPrefillBlockQ = 128;   // 4 waves x 32 queries
+constexpr int kPrefillBlockK = 64;    // keys per K/V tile
+constexpr int kPrefillThreads = 256;
+constexpr int kPrefillPad = 8;        // bf16 elements of padding per LDS row
+
+constexpr int kF32BlockQ = 16;        // 16 query rows x 16 lanes
+constexpr int kF32BlockK = 32;
+constexpr int kF32Threads = 256;
+
+constexpr int kSplitThreads = 256;
+constexpr int kMergeThreads = 64;
+
+inline int prefill_lds_bytes(int D) {
+  // K tile and V tile, both [block_k][D + pad] bf16.
+  return 2 * kPrefillBlockK * (D + kPrefillPad) * 2;
+}
+inline int f32_lds_bytes(int D) { return 2 * kF32BlockK * D * 4; }
+
+}  // namespace fa

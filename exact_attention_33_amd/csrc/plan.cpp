@@ -1,0 +1,129 @@
+// Tiling and launch planner: a pure host function of the shape and options.
+//
+// The tile sizes follow the counting argument of "FlashAttention: attention
+// was never compute-bound", How big should a tile be?: K and V are re-read
+// once per query tile, so the query tile is the largest that keeps its
+// working set on chip.  On gfx950 the working set lives in registers (Q, the
+// score tile, the output accumulator) and LDS (one K tile and one V tile,
+// 34 KB at D = 128), so two workgroups of 128 queries fit one compute unit.
+// Batch, heads and query tiles are independent ("Understanding
+// FlashAttention", Attention: batch and heads only repeat the problem), so
+// the grid spans all three.
+#include <climits>
+#include <cstdint>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Keys per split for split-KV decode: large enough to stream long runs of
+// contiguous K/V rows, small enough that the grid covers the GPU several
+// times over.
+int32_t auto_split_keys(const fa_shape& s) {
+  int32_t sk = 1024;
+  while (sk > 128 && (int64_t)s.B * s.H * ceil_div(s.M, sk) < 4096) sk /= 2;
+  return sk;
+}
+
+}  // namespace
+
+fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
+                    const fa_options* opt, Plan* plan, const char** why) {
+  (void)causal;
+  *plan = Plan{};
+  if (s.B < 0 || s.H < 0 || s.N < 0 || s.M < 0 || s.D < 0) {
+    *why = "B, H, N, M and D must be non-negative";
+    return FA_ERR_SHAPE;
+  }
+  if (dt != FA_F32 && dt != FA_BF16) {
+    *why = "dtype must be FA_F32 or FA_BF16";
+    return FA_ERR_UNSUPPORTED;
+  }
+  if (s.D != 64 && s.D != 128) {
+    *why = "head dimension D must be 64 or 128";
+    return FA_ERR_UNSUPPORTED;
+  }
+  const int32_t req = opt ? opt->path : FA_PATH_AUTO;
+  if (req < FA_PATH_AUTO || req > FA_PATH_F32) {
+    *why = "options.path is not a fa_path value";
+    return FA_ERR_ARG;
+  }
+  if (opt && (opt->split_keys < 0 || opt->split_keys % 64 != 0)) {
+    *why = "options.split_keys must be 0 or a positive multiple of 64";
+    return FA_ERR_ARG;
+  }
+  // Element counts must fit comfortably in 64-bit byte offsets.
+  const int64_t bh = (int64_t)s.B * s.H;
+  if (bh > INT32_MAX || (bh > 0 && ((int64_t)s.N * s.D > INT64_MAX / 8 / bh ||
+                                    (int64_t)s.M * s.D > INT64_MAX / 8 / bh))) {
+    *why = "tensor sizes overflow 64-bit offsets";
+    return FA_ERR_SHAPE;
+  }
+
+  fa_path path;
+  if (dt == FA_F32) {
+    if (req != FA_PATH_AUTO && req != FA_PATH_F32) {
+      *why = "float32 inputs run only on FA_PATH_F32";
+      return FA_ERR_UNSUPPORTED;
+    }
+    path = FA_PATH_F32;
+  } else {
+    if (req == FA_PATH_F32) {
+      *why = "FA_PATH_F32 needs float32 inputs";
+      return FA_ERR_UNSUPPORTED;
+    }
+    if (req == FA_PATH_SPLITKV && s.N != 1) {
+      *why = "FA_PATH_SPLITKV needs N == 1 (one query per sequence)";
+      return FA_ERR_UNSUPPORTED;
+    }
+    path = req == FA_PATH_AUTO ? (s.N == 1 ? FA_PATH_SPLITKV : FA_PATH_PREFILL)
+                               : (fa_path)req;
+  }
+
+  plan->path = path;
+  switch (path) {
+    case FA_PATH_PREFILL:
+      plan->block_q = kPrefillBlockQ;
+      plan->block_k = kPrefillBlockK;
+      plan->threads = kPrefillThreads;
+      plan->lds_bytes = prefill_lds_bytes(s.D);
+      plan->grid = ceil_div(s.N, kPrefillBlockQ) * bh;
+      break;
+    case FA_PATH_F32:
+      plan->block_q = kF32BlockQ;
+      plan->block_k = kF32BlockK;
+      plan->threads = kF32Threads;
+      plan->lds_bytes = f32_lds_bytes(s.D);
+      plan->grid = ceil_div(s.N, kF32BlockQ) * bh;
+      break;
+    case FA_PATH_SPLITKV: {
+      const int32_t sk = (opt && opt->split_keys) ? opt->split_keys : auto_split_keys(s);
+      plan->block_q = 1;
+      plan->block_k = sk;
+      plan->threads = kSplitThreads;
+      plan->splits = (int32_t)ceil_div(s.M, sk);
+      plan->lds_bytes = 0;
+      plan->grid = (int64_t)plan->splits * bh;
+      const size_t parts = (size_t)bh * (size_t)plan->splits;
+      plan->ws_lse_offset = align_up(parts * (size_t)s.D * sizeof(float), 256);
+      plan->ws_bytes = parts ? align_up(plan->ws_lse_offset + parts * sizeof(float), 256) : 0;
+      break;
+    }
+    default:
+      *why = "internal: no path";
+      return FA_ERR_UNSUPPORTED;
+  }
+  if (plan->grid > INT32_MAX) {
+    *why = "grid exceeds 2^31 - 1 workgroups";
+    return FA_ERR_SHAPE;
+  }
+  return FA_OK;
+}
+
+}  // namespace fa

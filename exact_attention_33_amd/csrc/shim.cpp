@@ -1,0 +1,134 @@
+// C-ABI shim: argument checks, planning and dispatch to the kernels.
+// The declarations and their contracts are in include/fa_mi355x.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fa_status fail(fa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+fa_status fail(fa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_str(fa_status st) {
+  switch (st) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    case FA_ERR_ARG: return "FA_ERR_ARG";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+fa_status fa_plan_query(fa_shape s, fa_dtype dtype, int causal,
+                        const fa_options* opt, fa_plan* out) {
+  if (!out) return fail(FA_ERR_NULL, "fa_plan_query: out is NULL");
+  fa::Plan plan;
+  const char* why = "";
+  fa_status st = fa::make_plan(s, dtype, causal, opt, &plan, &why);
+  if (st != FA_OK) return fail(st, "fa_plan_query: %s", why);
+  out->path = plan.path;
+  out->block_q = plan.block_q;
+  out->block_k = plan.block_k;
+  out->threads = plan.threads;
+  out->lds_bytes = plan.lds_bytes;
+  out->splits = plan.splits;
+  out->grid = plan.grid;
+  out->workspace_bytes = plan.ws_bytes;
+  g_last_error[0] = 0;
+  return FA_OK;
+}
+
+size_t fa_fwd_workspace_bytes(fa_shape s, fa_dtype dtype, int causal,
+                              const fa_options* opt) {
+  fa::Plan plan;
+  const char* why = "";
+  if (fa::make_plan(s, dtype, causal, opt, &plan, &why) != FA_OK) return 0;
+  return plan.ws_bytes;
+}
+
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v,
+                    const int32_t* kv_len, void* o, float* lse,
+                    fa_shape s, fa_dtype dtype, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    const fa_options* opt) {
+  fa::Plan plan;
+  const char* why = "";
+  fa_status st = fa::make_plan(s, dtype, causal, opt, &plan, &why);
+  if (st != FA_OK) return fail(st, "fa_fwd: %s", why);
+  if (!std::isfinite(scale) || scale < 0.0f)
+    return fail(FA_ERR_ARG, "fa_fwd: scale must be finite and >= 0 (got %g)", (double)scale);
+
+  const int64_t bh = (int64_t)s.B * s.H;
+  const bool no_rows = bh == 0 || s.N == 0;
+  if (no_rows) {  // nothing to compute and nothing to write
+    g_last_error[0] = 0;
+    return FA_OK;
+  }
+  const bool has_kv = s.M > 0;
+  if (!q || !o || !lse) return fail(FA_ERR_NULL, "fa_fwd: q, o and lse must be non-NULL");
+  if (has_kv && (!k || !v)) return fail(FA_ERR_NULL, "fa_fwd: k and v must be non-NULL when M > 0");
+  if (!aligned(q, 16) || !aligned(o, 16) || (has_kv && (!aligned(k, 16) || !aligned(v, 16))))
+    return fail(FA_ERR_ALIGN, "fa_fwd: q, k, v and o must be 16-byte aligned");
+  if (!aligned(lse, 4) || (kv_len && !aligned(kv_len, 4)))
+    return fail(FA_ERR_ALIGN, "fa_fwd: lse and kv_len must be 4-byte aligned");
+  if (plan.ws_bytes) {
+    if (!workspace)
+      return fail(FA_ERR_WORKSPACE, "fa_fwd: this shape needs %zu workspace bytes, got NULL",
+                  plan.ws_bytes);
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(FA_ERR_WORKSPACE, "fa_fwd: this shape needs %zu workspace bytes, got %zu",
+                  plan.ws_bytes, workspace_bytes);
+    if (!aligned(workspace, 256))
+      return fail(FA_ERR_ALIGN, "fa_fwd: workspace must be 256-byte aligned");
+  }
+
+  fa::Problem p{q, k, v, kv_len, o, lse, s.B, s.H, s.N, s.M, s.D, scale, causal ? 1 : 0};
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t err = hipSuccess;
+  switch (plan.path) {
+    case FA_PATH_PREFILL: err = fa::launch_prefill_bf16(p, plan, hs); break;
+    case FA_PATH_F32: err = fa::launch_fwd_f32(p, plan, hs); break;
+    case FA_PATH_SPLITKV: err = fa::launch_splitkv_bf16(p, plan, workspace, hs); break;
+    default: return fail(FA_ERR_UNSUPPORTED, "fa_fwd: internal: no path");
+  }
+  if (err != hipSuccess)
+    return fail(FA_ERR_HIP, "fa_fwd: launch failed: %s", hipGetErrorString(err));
+  g_last_error[0] = 0;
+  return FA_OK;
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v,
+                 const int32_t* kv_len, void* o, float* lse,
+                 fa_shape s, fa_dtype dtype, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_fwd_ex(q, k, v, kv_len, o, lse, s, dtype, scale, causal, workspace,
+                   workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+/*
+ * fa_mi355x.h -- C ABI of the fused exact-attention forward for MI355X (gfx950).
+ *
+ * The operation (per batch b and head h, all arithmetic described in real
+ * numbers; the library's rounding is documented per path below):
+ *
+ *   S[i][j]   = scale * sum_d Q[b][h][i][d] * K[b][h][j][d]
+ *   visible   : j < kv_len[b]  and  (not causal  or  j <= i + kv_len[b] - N)
+ *   O[b][h][i]  = sum_{visible j} softmax_j(S[i][.]) * V[b][h][j]
+ *   LSE[b][h][i] = ln sum_{visible j} exp(S[i][j])
+ *
+ * Sources: "Flash Attention: The Hidden Gem" -- Background (the attention
+ * formula softmax(Q K^T / sqrt(d_k)) V), The Algorithm (the forward returns O
+ * and the log-sum-exp L = m + log(l) kept for the backward pass);
+ * "Understanding FlashAttention" -- Attention (Q [N,D], K [M,D], V [M,D],
+ * N = 1 when decoding against a KV cache of M keys, an elementwise mask that
+ * does not depend on the scores, batch and heads as independent repeats, D
+ * fixed at compile time, scaling by 1/sqrt(D)).
+ *
+ * Readings where the pages are silent: the causal mask is aligned to the
+ * bottom-right corner (the last query sees the last visible key; with
+ * N == kv_len it is the usual j <= i, with N == 1 the query sees its whole
+ * history); kv_len masks keys only; a query with no visible key gets O = 0
+ * and LSE = -inf; LSE is a natural logarithm and always float32.
+ *
+ * Memory and ownership.  Every pointer argument except `stream` is a device
+ * pointer on the current HIP device.  The caller allocates and frees every
+ * buffer, including the workspace; the library allocates nothing, holds no
+ * device state, never synchronises and never copies to the host.  Calls are
+ * enqueued on `stream` (NULL = the default stream) and return at once; the
+ * outputs are ready when the stream reaches that point.  Functions are
+ * reentrant and never throw across the ABI.
+ *
+ * Layout.  Q [B,H,N,D], K and V [B,H,M,D] and O [B,H,N,D] are contiguous,
+ * row-major, D fastest, all of element type `dtype`; LSE [B,H,N] is float32;
+ * kv_len [B] is int32 (NULL means M for every batch).  Device-side kv_len
+ * values cannot be checked without a synchronisation: values outside [0, M]
+ * are clamped to that range by the kernels.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  FA_ERR_SHAPE = 2,       /* a dimension is negative or the sizes overflow       */
+  FA_ERR_UNSUPPORTED = 3, /* D not in {64, 128}, unknown dtype, path not usable  */
+  FA_ERR_ALIGN = 4,       /* Q/K/V/O not 16-byte aligned, LSE/kv_len not 4-byte  */
+  FA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required             */
+  FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch         */
+  FA_ERR_ARG = 7          /* scale not finite or negative, bad option value      */
+} fa_status;
+
+typedef struct { int32_t B, H, N, M, D; } fa_shape;
+
+typedef enum {
+  FA_PATH_AUTO = 0,     /* planner's choice                                      */
+  FA_PATH_PREFILL = 1,  /* fused tiled kernel, bf16 MFMA (bf16 only)             */
+  FA_PATH_SPLITKV = 2,  /* split-KV partial kernel + log-sum-exp merge (bf16, N=1) */
+  FA_PATH_F32 = 3       /* float32 inputs/outputs, float64 internal arithmetic   */
+} fa_path;
+
+/* Optional controls; pass NULL for the planner's defaults. */
+typedef struct {
+  int32_t path;        /* fa_path                                                */
+  int32_t split_keys;  /* split-KV: keys per split, a multiple of 64; 0 = auto   */
+} fa_options;
+
+/* What the planner decided for a shape (host-only, no device call). */
+typedef struct {
+  int32_t path;            /* fa_path actually used                              */
+  int32_t block_q;         /* queries per workgroup                              */
+  int32_t block_k;         /* keys per K/V tile (prefill) or per split (split-KV) */
+  int32_t threads;         /* threads per workgroup                              */
+  int32_t lds_bytes;       /* static LDS per workgroup                           */
+  int32_t splits;          /* split-KV: number of key splits per (b, h)          */
+  int64_t grid;            /* workgroups of the main kernel                      */
+  size_t workspace_bytes;  /* bytes the caller must pass as workspace            */
+} fa_plan;
+
+/*
+ * fa_plan_query -- run the planner only.  Pure host function: it reads no
+ * device state and launches nothing.  Returns the same status fa_fwd_ex
+ * would return for the shape-level checks (FA_ERR_SHAPE, FA_ERR_UNSUPPORTED,
+ * FA_ERR_ARG); `out` (non-NULL) receives the plan on FA_OK.
+ */
+fa_status fa_plan_query(fa_shape s, fa_dtype dtype, int causal,
+                        const fa_options* opt, fa_plan* out);
+
+/*
+ * fa_fwd_workspace_bytes -- bytes of device workspace fa_fwd needs for this
+ * shape (0 unless the split-KV path is chosen).  Returns 0 for a shape the
+ * planner rejects.  The value depends on the shape and options only.
+ */
+size_t fa_fwd_workspace_bytes(fa_shape s, fa_dtype dtype, int causal,
+                              const fa_options* opt);
+
+/*
+ * fa_fwd -- the exact-attention forward: O and LSE as defined at the top of
+ * this file.  `scale` is applied in float32 to the float32 score (bf16 path)
+ * or in float64 (float32 path); pass 1/sqrt(D) for the usual scaling.
+ * Checks run before any launch; on a non-OK status nothing is enqueued and
+ * fa_last_error() describes the failure.  A problem with no work
+ * (B*H*N == 0) returns FA_OK without launching.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v,
+                 const int32_t* kv_len, void* o, float* lse,
+                 fa_shape s, fa_dtype dtype, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_fwd_ex -- fa_fwd with explicit options (NULL = defaults). */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v,
+                    const int32_t* kv_len, void* o, float* lse,
+                    fa_shape s, fa_dtype dtype, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    const fa_options* opt);
+
+/* Static name of a status code. */
+const char* fa_status_str(fa_status st);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* fa_last_error(void);
+
+/* FA_ABI_VERSION of the built library. */
+int32_t fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,135 @@
+"""The C-ABI library on the host: it loads, exports what the header declares,
+plans shapes, and rejects bad arguments before any launch (no GPU needed).
+
+Every fa_fwd call here fails a host-side check, so nothing is ever launched:
+the fake pointers below are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_33_amd as fa
+from exact_attention_33_amd import Options, Shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.library_path),
+                                reason="library not built (python -m exact_attention_33_amd.build)")
+
+# Fake but 256-byte aligned device addresses; only used where a check fails first.
+P = 0x10000
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = fa.lib()
+    declared = header_functions()
+    assert sorted(fa.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.fa_abi_version() == 1
+
+
+def test_status_strings():
+    L = fa.lib()
+    names = [L.fa_status_str(i).decode() for i in range(8)]
+    assert names == ["FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED",
+                     "FA_ERR_ALIGN", "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_ERR_ARG"]
+    assert L.fa_status_str(99).decode() == "FA_ERR_UNKNOWN"
+
+
+def test_planner_paths():
+    p = fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True)
+    assert p["path_name"] == "prefill" and p["block_q"] == 128 and p["block_k"] == 64
+    assert p["grid"] == 64 * 64 and p["workspace_bytes"] == 0
+    assert p["lds_bytes"] <= 160 * 1024 // 2   # two workgroups per compute unit
+    p = fa.plan(1, 1, 128, 128, 64, fa.F32, False)
+    assert p["path_name"] == "f32" and p["grid"] == 8
+    p = fa.plan(32, 32, 1, 32768, 128, fa.BF16, False)
+    assert p["path_name"] == "splitkv"
+    assert p["splits"] * p["block_k"] >= 32768
+    assert p["workspace_bytes"] >= 32 * 32 * p["splits"] * (128 + 1) * 4
+    # forcing paths
+    assert fa.plan(1, 2, 1, 500, 64, fa.BF16, True, path=fa.PATH_PREFILL)["path_name"] == "prefill"
+    p = fa.plan(1, 2, 1, 500, 64, fa.BF16, False, path=fa.PATH_SPLITKV, split_keys=64)
+    assert p["splits"] == 8 and p["block_k"] == 64
+    # empty problems plan fine and need nothing
+    assert fa.plan(0, 4, 16, 16, 64)["grid"] == 0
+    assert fa.workspace_bytes(1, 1, 1, 0, 64) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 1, 16, 16, 96, fa.BF16, False), "FA_ERR_UNSUPPORTED"),
+    ((1, 1, 16, 16, 64, 7, False), "FA_ERR_UNSUPPORTED"),
+    ((-1, 1, 16, 16, 64, fa.BF16, False), "FA_ERR_SHAPE"),
+    ((1, 1, 16, -16, 64, fa.BF16, False), "FA_ERR_SHAPE"),
+])
+def test_planner_rejects(args, status):
+    with pytest.raises(fa.FaError) as ei:
+        fa.plan(*args)
+    assert ei.value.name == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(path=fa.PATH_PREFILL), "FA_ERR_UNSUPPORTED"),   # f32 data on the bf16 path
+    (dict(path=9), "FA_ERR_ARG"),
+])
+def test_planner_rejects_options_f32(kw, status):
+    with pytest.raises(fa.FaError) as ei:
+        fa.plan(1, 1, 16, 16, 64, fa.F32, False, **kw)
+    assert ei.value.name == status
+
+
+def test_planner_rejects_options_bf16():
+    with pytest.raises(fa.FaError) as ei:
+        fa.plan(1, 1, 4, 16, 64, fa.BF16, False, path=fa.PATH_SPLITKV)
+    assert ei.value.name == "FA_ERR_UNSUPPORTED"
+    with pytest.raises(fa.FaError) as ei:
+        fa.plan(1, 1, 1, 16, 64, fa.BF16, False, split_keys=100)
+    assert ei.value.name == "FA_ERR_ARG"
+    with pytest.raises(fa.FaError) as ei:
+        fa.plan(1, 1, 1, 16, 64, fa.BF16, False, path=fa.PATH_F32)
+    assert ei.value.name == "FA_ERR_UNSUPPORTED"
+
+
+def call(q=P, k=P, v=P, kvl=None, o=P, lse=P, shape=(1, 2, 16, 16, 64), dt=fa.BF16,
+         scale=0.125, causal=0, ws=None, ws_len=0, opt=None):
+    L = fa.lib()
+    st = L.fa_fwd_ex(q, k, v, kvl, o, lse, Shape(*shape), dt, scale, causal, ws, ws_len,
+                     None, ctypes.byref(opt) if opt else None)
+    return L.fa_status_str(st).decode(), L.fa_last_error().decode()
+
+
+def test_fwd_rejects_before_launch():
+    assert call(q=None)[0] == "FA_ERR_NULL"
+    assert call(o=None)[0] == "FA_ERR_NULL"
+    assert call(lse=None)[0] == "FA_ERR_NULL"
+    assert call(k=None)[0] == "FA_ERR_NULL"
+    assert call(q=P + 8)[0] == "FA_ERR_ALIGN"
+    assert call(v=P + 4)[0] == "FA_ERR_ALIGN"
+    assert call(lse=P + 2)[0] == "FA_ERR_ALIGN"
+    assert call(kvl=P + 1)[0] == "FA_ERR_ALIGN"
+    assert call(scale=float("nan"))[0] == "FA_ERR_ARG"
+    assert call(scale=float("inf"))[0] == "FA_ERR_ARG"
+    assert call(scale=-1.0)[0] == "FA_ERR_ARG"
+    assert call(shape=(1, 2, 16, 16, 80))[0] == "FA_ERR_UNSUPPORTED"
+    assert call(shape=(1, 2, -3, 16, 64))[0] == "FA_ERR_SHAPE"
+    st, msg = call(shape=(1, 2, 1, 4096, 64))   # split-KV needs a workspace
+    assert st == "FA_ERR_WORKSPACE" and "workspace" in msg
+    need = fa.workspace_bytes(1, 2, 1, 4096, 64)
+    assert call(shape=(1, 2, 1, 4096, 64), ws=P, ws_len=need - 1)[0] == "FA_ERR_WORKSPACE"
+    assert call(shape=(1, 2, 1, 4096, 64), ws=P + 16, ws_len=need)[0] == "FA_ERR_ALIGN"
+
+
+def test_fwd_empty_problem_is_a_no_op():
+    # B*H*N == 0: nothing to compute, so OK without touching any pointer.
+    assert call(q=None, k=None, v=None, o=None, lse=None, shape=(0, 2, 16, 16, 64))[0] == "FA_OK"
+    assert call(q=None, k=None, v=None, o=None, lse=None, shape=(1, 2, 0, 16, 64))[0] == "FA_OK"
