@@ -62,8 +62,8 @@ constexpr int kSplitThreads = 256;
 constexpr int kMergeThreads = 64;
 
 inline int prefill_lds_bytes(int D) {
-  // K tile and V tile, both [block_k][D + pad] bf16.
-  return 2 * kPrefillBlockK * (D + kPrefillPad) * 2;
+  // Two buffers of (K tile [block_k][D + pad], V tile [block_k][D]) bf16.
+  return 2 * kPrefillBlockK * (2 * D + kPrefillPad) * 2;
 }
 inline int f32_lds_bytes(int D) { return 2 * kF32BlockK * D * 4; }
 
