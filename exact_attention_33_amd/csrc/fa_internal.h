@@ -59,7 +59,7 @@ constexpr int kF32BlockK = 32;
 constexpr int kF32Threads = 256;
 
 constexpr int kSplitThreads = 256;
-constexpr int kMergeThreads = 64;
+constexpr int kMergeThreads = 256;
 
 inline int prefill_lds_bytes(int D) {
   // Two buffers of (K tile [block_k][D + pad], V tile [block_k][D]) bf16.
