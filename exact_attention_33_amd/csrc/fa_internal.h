@@ -52,7 +52,6 @@ hipError_t launch_splitkv_bf16(const Problem& p, const Plan& plan, void* workspa
 constexpr int kPrefillBlockQ = 128;   // 4 waves x 32 queries
 constexpr int kPrefillBlockK = 64;    // keys per K/V tile
 constexpr int kPrefillThreads = 256;
-constexpr int kPrefillPad = 8;        // bf16 elements of padding per LDS row
 
 constexpr int kF32BlockQ = 16;        // 16 query rows x 16 lanes
 constexpr int kF32BlockK = 32;
@@ -62,8 +61,8 @@ constexpr int kSplitThreads = 256;
 constexpr int kMergeThreads = 256;
 
 inline int prefill_lds_bytes(int D) {
-  // Two buffers of (K tile [block_k][D + pad], V tile [block_k][D]) bf16.
-  return 2 * kPrefillBlockK * (2 * D + kPrefillPad) * 2;
+  // Two K and two V tiles, each [block_k][D] bf16 (swizzled, unpadded).
+  return 4 * kPrefillBlockK * D * 2;
 }
 inline int f32_lds_bytes(int D) { return 2 * kF32BlockK * D * 4; }
 

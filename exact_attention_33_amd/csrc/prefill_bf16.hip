@@ -34,14 +34,20 @@
 //    ds_read_b64_tr_b16 transposing reads per MFMA.  The row sum adds the
 //    float32 weights before rounding (a sum of bf16-rounded weights would
 //    carry their 2^-9 relative error into LSE for rows with few keys);
-//  * K and V move HBM -> registers -> LDS with 16-byte loads into a double
-//    buffer: tile t+1 is written while tile t is read, tile t+2 is in flight
-//    from HBM, and one barrier per tile separates them;
-//  * LDS bank conflicts: K rows are padded by 16 bytes, so the 16 rows a
-//    16-lane group reads with ds_read_b128 start 4 banks apart; V rows are
-//    not padded but their 16-byte chunks are XOR-swizzled by row, so the 4
-//    rows x 64 bytes that 32 lanes read with ds_read_b64_tr_b16 cover all 64
-//    banks once;
+//  * K and V move HBM -> LDS directly (global_load_lds_dwordx4: each lane's
+//    16 bytes land at M0 + 16 * lane, so one wave instruction fills a 1 KB
+//    block and the per-lane global address picks what goes where), with no
+//    staging registers.  Two K and two V buffers, each its own LDS array so
+//    the compiler can see that reading one never waits on a load into another;
+//  * software pipeline inside each wave: iteration t issues the loads of
+//    K(t+2) and V(t+1), computes the softmax of tile t while the MFMAs of
+//    S(t+1) = K(t+1) Q^T run, then O += P(t) V(t); one barrier per tile;
+//  * LDS bank conflicts: rows are unpadded and their 16-byte chunks are
+//    XOR-swizzled by row: for K so that the 16 rows a 16-lane group reads
+//    with ds_read_b128 hit 16 different bank groups, for V so that the
+//    4 rows x 64 bytes that 32 lanes read with ds_read_b64_tr_b16 cover all
+//    64 banks once.  Rows past kv_len in the last tile are filled from the
+//    last valid row (finite data; their weights are exactly 0);
 //  * causal: tiles past the workgroup's last visible key are never visited,
 //    waves skip tiles they cannot see, and only tiles that cross the diagonal
 //    or the kv_len boundary are masked element by element;
@@ -73,19 +79,22 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t wg, int64_t G) {
   return x * q + (x < r ? x : r) + j;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(Problem p, int n_qtiles) {
   constexpr int BQ = kPrefillBlockQ, BK = kPrefillBlockK;
-  constexpr int LROW = D + kPrefillPad;           // K row length in LDS (bf16 elements)
-  constexpr int KTILE = BK * LROW;                // one K tile in LDS
-  constexpr int VTILE = BK * D;                   // one V tile in LDS (swizzled, unpadded)
-  constexpr int BUF = KTILE + VTILE;
-  constexpr int CPR = D / 8;                      // 16-byte chunks per row
-  constexpr int CH = BK * CPR / kPrefillThreads;  // chunks per thread per tile
-  static_assert(BK * CPR % kPrefillThreads == 0, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];  // K0 V0 K1 V1
-  // V chunk swizzle: rows r..r+3 (r % 4 == 0) x any 4 aligned chunks land on
-  // 16 distinct 16-byte bank groups (D = 128: 16 chunks per row; D = 64: 8).
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int TILE = BK * D;               // elements of one K or V tile
+  constexpr int NLD = TILE * 2 / 1024 / 4;   // 1 KB load instructions per wave per tile
+  static_assert(NLD >= 1 && TILE * 2 == NLD * 4 * 1024, "tile must split into 1 KB blocks");
+  __shared__ __attribute__((aligned(1024))) __bf16 Kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vb1[TILE];
+  // Chunk swizzles (see the header): K keeps 16 consecutive rows on distinct
+  // bank groups, V keeps rows r..r+3 (r % 4 == 0) x 4 aligned chunks distinct.
+  auto kswz = [](int row) { return CPR == 16 ? (row & 15) : ((row >> 1) & 7); };
   auto vswz = [](int row) { return CPR == 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); };
 
   const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
@@ -119,159 +128,168 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(Proble
       qf[kb] = bf16x8{};
   }
 
+  // Per-lane source rows/columns of this wave's 1 KB load blocks: LDS chunk
+  // slot = (block * 64 + lane) holds row slot / CPR, swizzled chunk slot % CPR.
+  int lrow[NLD], kcol[NLD], vcol[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int slot = (w * NLD + i) * 64 + lane;
+    lrow[i] = slot / CPR;
+    kcol[i] = ((slot % CPR) ^ kswz(lrow[i])) * 8;
+    vcol[i] = ((slot % CPR) ^ vswz(lrow[i])) * 8;
+  }
+  auto load_tile = [&](const __bf16* src, int t, const int* col, __bf16* dst) {
+    const int k0 = t * BK;
+    __bf16* d = dst + w * NLD * 512;
+    if (k0 + BK <= kvl) {
+      const __bf16* base = src + (size_t)k0 * D;  // uniform
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(base + lrow[i] * D + col[i]),
+                                         (lds_ptr)(d + i * 512), 16, 0, 0);
+    } else {  // last tile: rows past kv_len repeat the last valid row
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int row = min(k0 + lrow[i], kvl - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)row * D + col[i]),
+                                         (lds_ptr)(d + i * 512), 16, 0, 0);
+      }
+    }
+  };
+
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  f32x16 sacc0[BK / 32], sacc1[BK / 32];
   float m_run = -INFINITY;  // reference max of t = s * scale * log2(e)
   float l_run = 0.f;        // this lane's part of the running sum
   // A scale of 0 would turn a masked -inf score into NaN (-inf * 0); a floor
   // of 1e-30 changes the weights of finite scores by less than 1e-20.
   const float c = fmaxf(p.scale * kLog2e, 1e-30f);
 
-  uint4 kreg[CH], vreg[CH];
-  auto gload = [&](int t) {
-    const int k0 = t * BK;
-    if (k0 + BK <= kvl) {  // whole tile inside the sequence
+  // a wave none of whose queries sees a key of tile t skips its math
+  auto active = [&](int t) { return !CAUSAL || t * BK <= qw0 + 31 + off; };
+
+  // ---- S^T = K Q^T for 64 keys x 32 queries ----
+  auto compute_s = [&](const __bf16* Ks, f32x16* sacc) {
 #pragma unroll
-      for (int r = 0; r < CH; ++r) {
-        const int ch = r * kPrefillThreads + tid;
-        const int key = ch / CPR, dc = ch % CPR;
-        kreg[r] = *(const uint4*)(Kg + (size_t)(k0 + key) * D + dc * 8);
-        vreg[r] = *(const uint4*)(Vg + (size_t)(k0 + key) * D + dc * 8);
-      }
-    } else {
+    for (int nb = 0; nb < BK / 32; ++nb) sacc[nb] = f32x16{};
 #pragma unroll
-      for (int r = 0; r < CH; ++r) {
-        const int ch = r * kPrefillThreads + tid;
-        const int key = ch / CPR, dc = ch % CPR;
-        if (k0 + key < kvl) {
-          kreg[r] = *(const uint4*)(Kg + (size_t)(k0 + key) * D + dc * 8);
-          vreg[r] = *(const uint4*)(Vg + (size_t)(k0 + key) * D + dc * 8);
-        } else {  // past the keys of this sequence: zeros, never read from HBM
-          kreg[r] = make_uint4(0, 0, 0, 0);
-          vreg[r] = make_uint4(0, 0, 0, 0);
-        }
+    for (int kb = 0; kb < D / 16; ++kb) {
+#pragma unroll
+      for (int nb = 0; nb < BK / 32; ++nb) {
+        const int row = nb * 32 + ql;
+        const int ch = (2 * kb + hl) ^ kswz(row);
+        const bf16x8 kf = *(const bf16x8*)(Ks + row * D + ch * 8);
+        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], sacc[nb], 0, 0, 0);
       }
     }
   };
-  auto lstore = [&](int buf) {
-    __bf16* Ks = lds + buf * BUF;
-    __bf16* Vs = Ks + KTILE;
+
+  // ---- softmax, part A: mask, running max, move the reference if needed ----
+  auto softmax_max = [&](int t, f32x16* sacc) {
+    const int k0 = t * BK;
+    const bool need_mask = (k0 + BK > kvl) || (CAUSAL && k0 + BK - 1 > qw0 + off);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(kvl - 1, qrow + off) : kvl - 1;  // last visible key
 #pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      const int ch = r * kPrefillThreads + tid;
-      const int key = ch / CPR, dc = ch % CPR;
-      *(uint4*)(Ks + key * LROW + dc * 8) = kreg[r];
-      *(uint4*)(Vs + key * D + ((dc ^ vswz(key)) * 8)) = vreg[r];
+      for (int nb = 0; nb < BK / 32; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + nb * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+          if (key > lim) sacc[nb][r] = -INFINITY;
+        }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < BK / 32; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxc = mx * c;  // -inf stays -inf (c > 0)
+    if (__any(mxc > m_run + kLazyRescale)) {
+      const float m_new = fmaxf(m_run, mxc);
+      // e^(m_old - m_new); nothing accumulated yet when m_old = -inf
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+  };
+
+  // ---- softmax, part B: weights 2^(t - m) as the bf16 B operand, row sums ----
+  auto softmax_exp = [&](const f32x16* sacc, bf16x8* pf) {
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // no visible key yet: all weights 0
+    float psum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < BK / 32; ++nb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = (2 * t2 + e / 4) * 4 + (e % 4);
+          const float pv = fast_exp2(fmaf(sacc[nb][r], c, -m_use));
+          psum += pv;
+          pf[nb * 2 + t2][e] = (__bf16)pv;
+        }
+    l_run += psum;
+  };
+
+  // ---- O^T += V^T P^T ----
+  // B operand slot 8*hl + e of 16-key block (nb, t2) is key
+  // 32 nb + 16 t2 + 8 (e / 4) + 4 hl + e % 4.  The A operand (V^T) for the
+  // same slots comes from two transposing reads of 4 consecutive keys each:
+  // within a 16-lane group, lane j reads row kbase + j / 4 at column
+  // dsrc + 4 (j % 4), and lane i receives the 4 keys at column dsrc + i.
+  // Rows krow and krow + 8 share one swizzle pattern.
+  auto pv = [&](const __bf16* Vs, const bf16x8* pf) {
+#pragma unroll
+    for (int nb = 0; nb < BK / 32; ++nb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int krow = nb * 32 + t2 * 16 + 4 * hl + (lane % 16) / 4;
+        const int sw = vswz(krow);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int dsrc = db * 32 + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
+          const int col = (((dsrc >> 3) ^ sw) << 3) + (dsrc & 7);
+          const s16x4 lo = lds_read_tr16(Vs + krow * D + col);
+          const s16x4 hi = lds_read_tr16(Vs + (krow + 8) * D + col);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb * 2 + t2], oacc[db], 0, 0, 0);
+        }
+      }
+  };
+
+  // One pipeline step for tile t with buffers fixed at compile time:
+  // reads K(t+1) from Knext and V(t) from Vcur; loads K(t+2) into Kload and
+  // V(t+1) into Vload; S(t) is in scur, S(t+1) goes to snext.  The MFMAs of
+  // S(t+1) do not depend on the softmax of tile t, so the two overlap.
+  auto step = [&](int t, const __bf16* Knext, const __bf16* Vcur, __bf16* Kload, __bf16* Vload,
+                  f32x16* scur, f32x16* snext) {
+    if (t + 2 < n_tiles) load_tile(Kg, t + 2, kcol, Kload);
+    if (t + 1 < n_tiles) load_tile(Vg, t + 1, vcol, Vload);
+    if (active(t)) {
+      bf16x8 pf[BK / 16];
+      softmax_max(t, scur);
+      softmax_exp(scur, pf);
+      if (t + 1 < n_tiles && active(t + 1)) compute_s(Knext, snext);
+      pv(Vcur, pf);
+    }
+    __syncthreads();  // loads of this step have landed; buffers read here are free
   };
 
   if (n_tiles > 0) {
-    gload(0);
-    lstore(0);
-    if (n_tiles > 1) gload(1);
+    load_tile(Kg, 0, kcol, Kb0);
+    load_tile(Vg, 0, vcol, Vb0);
+    if (n_tiles > 1) load_tile(Kg, 1, kcol, Kb1);
   }
   __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int k0 = t * BK;
-    const __bf16* Ks = lds + (t & 1) * BUF;
-    const __bf16* Vs = Ks + KTILE;
-    // a wave none of whose queries sees a key of this tile skips the math
-    const bool active = !CAUSAL || k0 <= qw0 + 31 + off;
-    if (active) {
-      // ---- S^T = K Q^T for 64 keys x 32 queries ----
-      f32x16 sacc[BK / 32];
-#pragma unroll
-      for (int nb = 0; nb < BK / 32; ++nb) sacc[nb] = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < D / 16; ++kb) {
-#pragma unroll
-        for (int nb = 0; nb < BK / 32; ++nb) {
-          const bf16x8 kf = *(const bf16x8*)(Ks + (nb * 32 + ql) * LROW + kb * 16 + hl * 8);
-          sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], sacc[nb], 0, 0, 0);
-        }
-      }
-
-      // ---- mask (only on tiles that cross the kv_len end or the diagonal) ----
-      const bool need_mask = (k0 + BK > kvl) || (CAUSAL && k0 + BK - 1 > qw0 + off);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(kvl - 1, qrow + off) : kvl - 1;  // last visible key
-#pragma unroll
-        for (int nb = 0; nb < BK / 32; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + nb * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
-            if (key > lim) sacc[nb][r] = -INFINITY;
-          }
-      }
-
-      // ---- row max; move the reference only when needed ----
-      float mx = -INFINITY;
-#pragma unroll
-      for (int nb = 0; nb < BK / 32; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mxc = mx * c;  // -inf stays -inf (c > 0)
-      if (__any(mxc > m_run + kLazyRescale)) {
-        const float m_new = fmaxf(m_run, mxc);
-        // e^(m_old - m_new); nothing accumulated yet when m_old = -inf
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // no visible key yet: all weights 0
-
-      // ---- weights 2^(t - m), bf16 B operand of the PV product, row sums ----
-      bf16x8 pf[BK / 16];
-      float psum = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < BK / 32; ++nb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = (2 * t2 + e / 4) * 4 + (e % 4);
-            const float pv = fast_exp2(fmaf(sacc[nb][r], c, -m_use));
-            psum += pv;
-            pf[nb * 2 + t2][e] = (__bf16)pv;
-          }
-      l_run += psum;
-
-      // ---- O^T += V^T P^T ----
-      // B operand slot 8*hl + e of 16-key block (nb, t2) is key
-      // 32 nb + 16 t2 + 8 (e / 4) + 4 hl + e % 4.  The A operand (V^T) for the
-      // same slots comes from two transposing reads of 4 consecutive keys each:
-      // within a 16-lane group, lane j reads row kbase + j / 4 at column
-      // dsrc + 4 (j % 4), and lane i receives the 4 keys at column dsrc + i.
-      // Rows krow and krow + 8 share one swizzle pattern.
-#pragma unroll
-      for (int nb = 0; nb < BK / 32; ++nb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const int krow = nb * 32 + t2 * 16 + 4 * hl + (lane % 16) / 4;
-          const int sw = vswz(krow);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const int dsrc = db * 32 + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
-            const int col = (((dsrc >> 3) ^ sw) << 3) + (dsrc & 7);
-            const s16x4 lo = lds_read_tr16(Vs + krow * D + col);
-            const s16x4 hi = lds_read_tr16(Vs + (krow + 8) * D + col);
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb * 2 + t2], oacc[db], 0, 0, 0);
-          }
-        }
-    }
-
-    // ---- stage the next tile; start loading the one after ----
-    if (t + 1 < n_tiles) {
-      lstore((t + 1) & 1);  // that buffer's last readers passed the previous barrier
-      if (t + 2 < n_tiles) gload(t + 2);
-    }
-    __syncthreads();
+  if (n_tiles > 0 && active(0)) compute_s(Kb0, sacc0);
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, Kb1, Vb0, Kb0, Vb1, sacc0, sacc1);
+    if (t + 1 < n_tiles) step(t + 1, Kb0, Vb1, Kb1, Vb0, sacc1, sacc0);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
