@@ -14,7 +14,15 @@
 // and weight tiles never leave registers.
 //
 // gfx950 mapping:
-//  * workgroup = 4 waves = 128 queries; wave w owns queries [32w, 32w + 32);
+//  * workgroup = 8 waves = 256 queries; wave w owns queries [32w, 32w + 32).
+//    Waves w and w + 4 share a SIMD.  They run the per-tile work in two
+//    phases -- an MFMA phase (S(t+1) = K(t+1) Q^T and O += P(t) V(t)) and a
+//    VALU phase (mask, row max and exponentials of tile t+1) -- offset by one
+//    phase: while waves 0-3 are in their MFMA phase, waves 4-7 are in their
+//    VALU phase and vice versa, with a workgroup barrier between phases.
+//    MFMA and VALU instructions of two waves on one SIMD overlap almost
+//    perfectly (measured on MI355X), so each SIMD keeps its matrix pipe busy
+//    while the other wave does the softmax arithmetic;
 //  * the score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: Q is the B operand and stays in registers for
 //    the whole sweep, K comes from LDS.  Lane (h, c) of a wave (h = lane / 32,
@@ -39,15 +47,21 @@
 //    block and the per-lane global address picks what goes where), with no
 //    staging registers.  Two K and two V buffers, each its own LDS array so
 //    the compiler can see that reading one never waits on a load into another;
-//  * software pipeline inside each wave: iteration t issues the loads of
-//    K(t+2) and V(t+1), computes the softmax of tile t while the MFMAs of
-//    S(t+1) = K(t+1) Q^T run, then O += P(t) V(t); one barrier per tile;
-//  * LDS bank conflicts: rows are unpadded and their 16-byte chunks are
-//    XOR-swizzled by row: for K so that the 16 rows a 16-lane group reads
-//    with ds_read_b128 hit 16 different bank groups, for V so that the
-//    4 rows x 64 bytes that 32 lanes read with ds_read_b64_tr_b16 cover all
-//    64 banks once.  Rows past kv_len in the last tile are filled from the
-//    last valid row (finite data; their weights are exactly 0);
+//  * pipeline: K(t+2) and V(t+1) are loaded while tiles t and t+1 are in use;
+//    a load has two phases (one tile) to land before the barrier that
+//    waits for it;
+//  * LDS layouts are padded so that every operand read is one per-lane base
+//    register plus a compile-time offset (no per-step address arithmetic, no
+//    address registers held across the loop) and conflict-free on the 64
+//    banks: K and Q rows carry 16 bytes of padding, so the 16 rows that a
+//    16-lane group reads with ds_read_b128 start 4 banks apart; V rows carry
+//    64 bytes, so the 4 rows x 64 bytes that 32 lanes read with
+//    ds_read_b64_tr_b16 start 16 banks apart.  Loads into LDS are 1 KB
+//    blocks of 64 lanes x 16 bytes; the slots that fall on padding receive
+//    a copy of valid data that is never read;
+//  * Q stays in LDS (each wave's 32 rows) and is read as the B operand in the
+//    MFMA phase, which leaves the registers for operand prefetch: each MFMA's
+//    operands are fetched a few MFMAs ahead;
 //  * causal: tiles past the workgroup's last visible key are never visited,
 //    waves skip tiles they cannot see, and only tiles that cross the diagonal
 //    or the kv_len boundary are masked element by element;
@@ -56,6 +70,7 @@
 //    (batch, head), heaviest first when causal) are mapped to one XCD so that
 //    the workgroups sharing a head's K/V run together on one L2.
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.h"
 #include "fa_internal.h"
@@ -82,20 +97,22 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t wg, int64_t G) {
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(Problem p, int n_qtiles) {
+__global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(Problem p, int n_qtiles) {
   constexpr int BQ = kPrefillBlockQ, BK = kPrefillBlockK;
-  constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int TILE = BK * D;               // elements of one K or V tile
-  constexpr int NLD = TILE * 2 / 1024 / 4;   // 1 KB load instructions per wave per tile
-  static_assert(NLD >= 1 && TILE * 2 == NLD * 4 * 1024, "tile must split into 1 KB blocks");
-  __shared__ __attribute__((aligned(1024))) __bf16 Kb0[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 Kb1[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 Vb0[TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 Vb1[TILE];
-  // Chunk swizzles (see the header): K keeps 16 consecutive rows on distinct
-  // bank groups, V keeps rows r..r+3 (r % 4 == 0) x 4 aligned chunks distinct.
-  auto kswz = [](int row) { return CPR == 16 ? (row & 15) : ((row >> 1) & 7); };
-  auto vswz = [](int row) { return CPR == 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); };
+  constexpr int NW = kPrefillThreads / 64;   // waves per workgroup
+  constexpr int CPR = D / 8;                 // 16-byte chunks of data per row
+  constexpr int KROW = D + 8;                // K/Q row stride in LDS (elements)
+  constexpr int VROW = D + 32;               // V row stride in LDS (elements)
+  constexpr int KCH = KROW / 8, VCH = VROW / 8;        // 16-byte slots per row
+  constexpr int KBLK = (BK * KCH + 63) / 64;           // 1 KB blocks per K tile
+  constexpr int VBLK = (BK * VCH + 63) / 64;           // 1 KB blocks per V tile
+  constexpr int QBLK = (32 * KCH + 63) / 64;           // 1 KB blocks per wave's Q rows
+  static_assert(NW == 8 && BQ == 32 * NW, "8 waves of 32 queries");
+  __shared__ __attribute__((aligned(1024))) __bf16 Kb0[KBLK * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Kb1[KBLK * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vb0[VBLK * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vb1[VBLK * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Qs_all[NW * QBLK * 512];
 
   const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
   int qt = (int)(logical % n_qtiles);
@@ -105,6 +122,7 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(Proble
   const int N = p.N, M = p.M;
   const int tid = threadIdx.x;
   const int w = tid / 64, lane = tid % 64, hl = lane / 32, ql = lane % 32;
+  const bool group_a = w < NW / 2;  // waves 0-3 lead, waves 4-7 follow one phase behind
   const int kvl = clamp_kv(p.kv_len, b, M);
   const int q0 = qt * BQ;
   const int qw0 = q0 + 32 * w;  // first query of this wave
@@ -118,49 +136,89 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(Proble
   const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D;
   const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D;
 
-  // Q as the B operand of S^T = K Q^T: lane (hl, ql) holds Q[qrow][16 kb + 8 hl .. + 8).
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int kb = 0; kb < D / 16; ++kb) {
-    if (qrow < N)
-      qf[kb] = *(const bf16x8*)(Qg + (size_t)qrow * D + kb * 16 + hl * 8);
-    else
-      qf[kb] = bf16x8{};
-  }
-
-  // Per-lane source rows/columns of this wave's 1 KB load blocks: LDS chunk
-  // slot = (block * 64 + lane) holds row slot / CPR, swizzled chunk slot % CPR.
-  int lrow[NLD], kcol[NLD], vcol[NLD];
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int slot = (w * NLD + i) * 64 + lane;
-    lrow[i] = slot / CPR;
-    kcol[i] = ((slot % CPR) ^ kswz(lrow[i])) * 8;
-    vcol[i] = ((slot % CPR) ^ vswz(lrow[i])) * 8;
-  }
-  auto load_tile = [&](const __bf16* src, int t, const int* col, __bf16* dst) {
-    const int k0 = t * BK;
-    __bf16* d = dst + w * NLD * 512;
-    if (k0 + BK <= kvl) {
-      const __bf16* base = src + (size_t)k0 * D;  // uniform
-#pragma unroll
-      for (int i = 0; i < NLD; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(base + lrow[i] * D + col[i]),
-                                         (lds_ptr)(d + i * 512), 16, 0, 0);
-    } else {  // last tile: rows past kv_len repeat the last valid row
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int row = min(k0 + lrow[i], kvl - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)row * D + col[i]),
-                                         (lds_ptr)(d + i * 512), 16, 0, 0);
-      }
+  // Slot s of a padded tile holds row s / CH, chunk s % CH; slots on the
+  // padding (chunk >= CPR) load chunk 0 of that row (valid data, never read).
+  auto load_padded = [&](const __bf16* src, int row0, int row_max, __bf16* dst, int nblk, int ch,
+                         int first_blk, int blk_step) {
+    for (int blk = first_blk; blk < nblk; blk += blk_step) {
+      const int slot = blk * 64 + lane;
+      const int r = slot / ch, c = slot % ch;
+      const int row = min(row0 + r, row_max);
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)row * D + (c < CPR ? c * 8 : 0)),
+                                       (lds_ptr)(dst + blk * 512), 16, 0, 0);
     }
   };
+  // K and V tiles: this wave loads blocks w, w + NW, ... of each.  The
+  // per-lane byte offsets of those blocks' slots within a tile (< 64 KB) are
+  // fixed, so they are computed once and kept two to a register; a tile load
+  // is then a shift or mask and an add per block, with the tile base in
+  // scalar registers.  Rows past kv_len (last tile only) repeat the last
+  // valid row (finite data whose weights are exactly 0).
+  constexpr int KPW = (KBLK + NW - 1) / NW, VPW = (VBLK + NW - 1) / NW;
+  constexpr int ROWB = D * 2, LOG_ROWB = D == 128 ? 8 : 7;  // bytes per global row
+  static_assert(ROWB == 1 << LOG_ROWB && BK * ROWB <= 65536, "row bytes");
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  auto slot_off = [&](int blk, int ch) -> uint32_t {
+    const int slot = blk * 64 + lane, r = slot / ch, cc = slot % ch;
+    return (uint32_t)(r * ROWB + (cc < CPR ? cc * 16 : 0));
+  };
+  uint32_t koff[(KPW + 1) / 2], voff[(VPW + 1) / 2];
+#pragma unroll
+  for (int i = 0; i < KPW; i += 2)
+    koff[i / 2] = slot_off(ws + i * NW, KCH) | (i + 1 < KPW ? slot_off(ws + (i + 1) * NW, KCH) << 16 : 0u);
+#pragma unroll
+  for (int i = 0; i < VPW; i += 2)
+    voff[i / 2] = slot_off(ws + i * NW, VCH) | (i + 1 < VPW ? slot_off(ws + (i + 1) * NW, VCH) << 16 : 0u);
+  auto load_tile = [&](const __bf16* src, int t, __bf16* dst, const uint32_t* offs, int nblk,
+                       auto npw_c) {
+    constexpr int npw = decltype(npw_c)::value;
+    const char* base = (const char*)(src + (size_t)t * BK * D);
+    const int rmax = kvl - 1 - t * BK;  // last valid row of this tile (>= 0)
+    // Opaque copies: the unpacked offsets must not be hoisted out of the
+    // main loop, where they would hold twice the registers.
+    uint32_t pk[(npw + 1) / 2];
+#pragma unroll
+    for (int i = 0; i < (npw + 1) / 2; ++i) {
+      pk[i] = offs[i];
+      asm volatile("" : "+v"(pk[i]));
+    }
+    offs = pk;
+    if (rmax >= BK - 1) {
+#pragma unroll
+      for (int i = 0; i < npw; ++i)
+        if (ws + i * NW < nblk) {
+          const uint32_t o = i % 2 ? offs[i / 2] >> 16 : offs[i / 2] & 0xFFFFu;
+          __builtin_amdgcn_global_load_lds((const void*)(base + o),
+                                           (lds_ptr)(dst + (ws + i * NW) * 512), 16, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < npw; ++i)
+        if (ws + i * NW < nblk) {
+          const uint32_t u = i % 2 ? offs[i / 2] >> 16 : offs[i / 2] & 0xFFFFu;
+          const uint32_t o = (uint32_t)min((int)(u >> LOG_ROWB), rmax) << LOG_ROWB | (u & (ROWB - 1));
+          __builtin_amdgcn_global_load_lds((const void*)(base + o),
+                                           (lds_ptr)(dst + (ws + i * NW) * 512), 16, 0, 0);
+        }
+    }
+  };
+  auto load_k = [&](int t, __bf16* dst) { load_tile(Kg, t, dst, koff, KBLK, std::integral_constant<int, KPW>{}); };
+  auto load_v = [&](int t, __bf16* dst) { load_tile(Vg, t, dst, voff, VBLK, std::integral_constant<int, VPW>{}); };
+
+  // This wave's 32 query rows (rows past N: any finite data, never written out).
+  __bf16* Qs = Qs_all + w * QBLK * 512;
+  load_padded(Qg, qw0, N - 1, Qs, QBLK, KCH, 0, 1);
+
+  // Per-lane base offsets (elements) of the three operand reads.
+  const int kbase = ql * KROW + hl * 8;   // + (32 nb) KROW + 16 kb
+  const int vbase = (4 * hl + (lane % 16) / 4) * VROW + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
+                                          // + (32 nb + 16 t2) VROW + 32 db, + 8 VROW for the upper 4 keys
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
   f32x16 sacc0[BK / 32], sacc1[BK / 32];
+  bf16x8 pf[BK / 16];       // weights of the tile whose PV is next
   float m_run = -INFINITY;  // reference max of t = s * scale * log2(e)
   float l_run = 0.f;        // this lane's part of the running sum
   // A scale of 0 would turn a masked -inf score into NaN (-inf * 0); a floor
@@ -168,26 +226,43 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(Proble
   const float c = fmaxf(p.scale * kLog2e, 1e-30f);
 
   // a wave none of whose queries sees a key of tile t skips its math
-  auto active = [&](int t) { return !CAUSAL || t * BK <= qw0 + 31 + off; };
+  auto active = [&](int t) { return t < n_tiles && (!CAUSAL || t * BK <= qw0 + 31 + off); };
 
-  // ---- S^T = K Q^T for 64 keys x 32 queries ----
+  // ---- operand fetches ----
+  auto fetch_k = [&](const __bf16* Ks, int kb, int nb) -> bf16x8 {
+    return *(const bf16x8*)(Ks + kbase + nb * 32 * KROW + kb * 16);
+  };
+  auto fetch_q = [&](int kb) -> bf16x8 { return *(const bf16x8*)(Qs + kbase + kb * 16); };
+  // V^T operand of PV MFMA i = (nb, t2, db).  B operand slot 8*hl + e of
+  // 16-key block (nb, t2) is key 32 nb + 16 t2 + 8 (e / 4) + 4 hl + e % 4;
+  // the A operand for the same slots comes from two transposing reads of 4
+  // consecutive keys each: within a 16-lane group, lane j reads row
+  // kbase + j / 4 at column dsrc + 4 (j % 4), and lane i receives the 4 keys
+  // at column dsrc + i.
+  auto fetch_v = [&](const __bf16* Vs, int i) -> bf16x8 {
+    const int nb = i / (2 * (D / 32)), t2 = (i / (D / 32)) % 2, db = i % (D / 32);
+    const __bf16* a = Vs + vbase + (nb * 32 + t2 * 16) * VROW + db * 32;
+    const s16x4 lo = lds_read_tr16(a);
+    const s16x4 hi = lds_read_tr16(a + 8 * VROW);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // ---- S^T = K Q^T for 64 keys x 32 queries (prologue only) ----
   auto compute_s = [&](const __bf16* Ks, f32x16* sacc) {
 #pragma unroll
     for (int nb = 0; nb < BK / 32; ++nb) sacc[nb] = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) {
+      const bf16x8 qv = fetch_q(kb);
 #pragma unroll
-      for (int nb = 0; nb < BK / 32; ++nb) {
-        const int row = nb * 32 + ql;
-        const int ch = (2 * kb + hl) ^ kswz(row);
-        const bf16x8 kf = *(const bf16x8*)(Ks + row * D + ch * 8);
-        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kb], sacc[nb], 0, 0, 0);
-      }
+      for (int nb = 0; nb < BK / 32; ++nb)
+        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fetch_k(Ks, kb, nb), qv, sacc[nb], 0, 0, 0);
     }
   };
 
-  // ---- softmax, part A: mask, running max, move the reference if needed ----
-  auto softmax_max = [&](int t, f32x16* sacc) {
+  // ---- softmax of tile t: mask, running max, weights 2^(t - m) as the
+  //      bf16 B operand of the PV product, row sums ----
+  auto softmax = [&](int t, f32x16* sacc) {
     const int k0 = t * BK;
     const bool need_mask = (k0 + BK > kvl) || (CAUSAL && k0 + BK - 1 > qw0 + off);
     if (need_mask) {
@@ -216,10 +291,6 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(Proble
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
       m_run = m_new;
     }
-  };
-
-  // ---- softmax, part B: weights 2^(t - m) as the bf16 B operand, row sums ----
-  auto softmax_exp = [&](const f32x16* sacc, bf16x8* pf) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // no visible key yet: all weights 0
     float psum = 0.f;
 #pragma unroll
@@ -236,60 +307,136 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_bf16_kernel(Proble
     l_run += psum;
   };
 
-  // ---- O^T += V^T P^T ----
-  // B operand slot 8*hl + e of 16-key block (nb, t2) is key
-  // 32 nb + 16 t2 + 8 (e / 4) + 4 hl + e % 4.  The A operand (V^T) for the
-  // same slots comes from two transposing reads of 4 consecutive keys each:
-  // within a 16-lane group, lane j reads row kbase + j / 4 at column
-  // dsrc + 4 (j % 4), and lane i receives the 4 keys at column dsrc + i.
-  // Rows krow and krow + 8 share one swizzle pattern.
-  auto pv = [&](const __bf16* Vs, const bf16x8* pf) {
+  // MFMA phase of tile t: S(t+1) from Knext into snext (when with_s), then
+  // O += P(t) V(t), as one sequence of MFMAs whose LDS operands are fetched
+  // ahead (KPD steps of S, VPD MFMAs of PV).  Scheduling barriers pin this
+  // order: left alone, the compiler fetches each operand just before its
+  // MFMA and every MFMA then waits out a full LDS round trip.
+  constexpr int NPV = (BK / 16) * (D / 32);  // MFMAs of O += P V
+  constexpr int KPD = 2, VPD = 4;
+  auto mfma_phase = [&](bool with_s, const __bf16* Ks, const __bf16* Vs, f32x16* snext) {
+    bf16x8 vfr[VPD];
+    if (with_s) {
+      bf16x8 kfr[KPD][BK / 32], qfr[KPD];
 #pragma unroll
-    for (int nb = 0; nb < BK / 32; ++nb)
+      for (int kb = 0; kb < KPD; ++kb) {
+        qfr[kb] = fetch_q(kb);
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int krow = nb * 32 + t2 * 16 + 4 * hl + (lane % 16) / 4;
-        const int sw = vswz(krow);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int dsrc = db * 32 + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
-          const int col = (((dsrc >> 3) ^ sw) << 3) + (dsrc & 7);
-          const s16x4 lo = lds_read_tr16(Vs + krow * D + col);
-          const s16x4 hi = lds_read_tr16(Vs + (krow + 8) * D + col);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb * 2 + t2], oacc[db], 0, 0, 0);
-        }
+        for (int nb = 0; nb < BK / 32; ++nb) kfr[kb][nb] = fetch_k(Ks, kb, nb);
       }
-  };
-
-  // One pipeline step for tile t with buffers fixed at compile time:
-  // reads K(t+1) from Knext and V(t) from Vcur; loads K(t+2) into Kload and
-  // V(t+1) into Vload; S(t) is in scur, S(t+1) goes to snext.  The MFMAs of
-  // S(t+1) do not depend on the softmax of tile t, so the two overlap.
-  auto step = [&](int t, const __bf16* Knext, const __bf16* Vcur, __bf16* Kload, __bf16* Vload,
-                  f32x16* scur, f32x16* snext) {
-    if (t + 2 < n_tiles) load_tile(Kg, t + 2, kcol, Kload);
-    if (t + 1 < n_tiles) load_tile(Vg, t + 1, vcol, Vload);
-    if (active(t)) {
-      bf16x8 pf[BK / 16];
-      softmax_max(t, scur);
-      softmax_exp(scur, pf);
-      if (t + 1 < n_tiles && active(t + 1)) compute_s(Knext, snext);
-      pv(Vcur, pf);
+#pragma unroll
+      for (int kb = 0; kb < D / 16; ++kb) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int slot = kb % KPD;
+        const bf16x8 qcur = qfr[slot];
+        bf16x8 kcur[BK / 32];
+#pragma unroll
+        for (int nb = 0; nb < BK / 32; ++nb) kcur[nb] = kfr[slot][nb];
+        const int nx = kb + KPD;  // next fetch: S operands, then the first PV operands
+        if (nx < D / 16) {
+          qfr[slot] = fetch_q(nx);
+#pragma unroll
+          for (int nb = 0; nb < BK / 32; ++nb) kfr[slot][nb] = fetch_k(Ks, nx, nb);
+        } else if (nx - D / 16 < VPD) {
+          vfr[nx - D / 16] = fetch_v(Vs, nx - D / 16);
+        }
+#pragma unroll
+        for (int nb = 0; nb < BK / 32; ++nb)
+          snext[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[nb], qcur, kb == 0 ? f32x16{} : snext[nb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = KPD; i < VPD; ++i) vfr[i] = fetch_v(Vs, i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VPD; ++i) vfr[i] = fetch_v(Vs, i);
     }
-    __syncthreads();  // loads of this step have landed; buffers read here are free
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 vcur = vfr[i % VPD];
+      if (i + VPD < NPV) vfr[i % VPD] = fetch_v(Vs, i + VPD);
+      const int nb = i / (2 * (D / 32)), t2 = (i / (D / 32)) % 2, db = i % (D / 32);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, pf[nb * 2 + t2], oacc[db], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto phase_mfma = [&](int t, const __bf16* Knext, const __bf16* Vcur, f32x16* snext) {
+    if (active(t + 1)) {
+      mfma_phase(true, Knext, Vcur, snext);  // active(t+1) implies active(t)
+    } else {
+      // snext is not read again; defining it on this path too ends the live
+      // range of the value it held (otherwise both accumulators stay live)
+#pragma unroll
+      for (int nb = 0; nb < BK / 32; ++nb) snext[nb] = f32x16{};
+      if (active(t)) mfma_phase(false, Knext, Vcur, snext);
+    }
+  };
+  // VALU phase of tile t: softmax of tile t+1 (its weights feed the next PV).
+  auto phase_valu = [&](int t, f32x16* snext) {
+    if (active(t + 1)) softmax(t + 1, snext);
+  };
+  // Barrier that only aligns the phases of the two wave groups: nothing is
+  // written to LDS that a read on its far side depends on, so it carries no
+  // memory fence (a fence would also wait for the in-flight tile loads).
+  auto align = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Prologue: Q, tiles 0 (K, V) and 1 (K) in LDS; S(0) and its softmax in
+  // every wave (the following group then idles through its first VALU phase).
   if (n_tiles > 0) {
-    load_tile(Kg, 0, kcol, Kb0);
-    load_tile(Vg, 0, vcol, Vb0);
-    if (n_tiles > 1) load_tile(Kg, 1, kcol, Kb1);
+    load_k(0, Kb0);
+    load_v(0, Vb0);
+    if (n_tiles > 1) load_k(1, Kb1);
   }
   __syncthreads();
-  if (n_tiles > 0 && active(0)) compute_s(Kb0, sacc0);
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, Kb1, Vb0, Kb0, Vb1, sacc0, sacc1);
-    if (t + 1 < n_tiles) step(t + 1, Kb0, Vb1, Kb1, Vb0, sacc1, sacc0);
+  if (active(0)) {
+    compute_s(Kb0, sacc0);
+    softmax(0, sacc0);
+  }
+  __syncthreads();  // every wave is done with K(0) before slot 0 loads K(2) over it
+
+  // Phase slots: the leading group runs M(t) in slot 2t and V(t) in slot
+  // 2t + 1; the following group runs V(t - 1) in slot 2t and M(t) in slot
+  // 2t + 1.  Slot 2t also issues the loads of K(t+2) and V(t+1); the full
+  // barrier after slot 2t + 1 waits for them.  Each group has its own loop
+  // (same barriers, same count), so each keeps only one score accumulator
+  // live at a time; both loops are unrolled by two tiles so that every LDS
+  // buffer and accumulator is fixed at compile time.
+  auto loads = [&](int t, __bf16* Kdst, __bf16* Vdst) {
+    if (t + 2 < n_tiles) load_k(t + 2, Kdst);
+    if (t + 1 < n_tiles) load_v(t + 1, Vdst);
+  };
+  if (group_a) {
+    for (int t = 0; t < n_tiles; t += 2) {
+      loads(t, Kb0, Vb1);
+      phase_mfma(t, Kb1, Vb0, sacc1);
+      align();
+      phase_valu(t, sacc1);
+      __syncthreads();
+      if (t + 1 >= n_tiles) break;
+      loads(t + 1, Kb1, Vb0);
+      phase_mfma(t + 1, Kb0, Vb1, sacc0);
+      align();
+      phase_valu(t + 1, sacc0);
+      __syncthreads();
+    }
+  } else {
+    for (int t = 0; t < n_tiles; t += 2) {
+      loads(t, Kb0, Vb1);
+      if (t > 0) phase_valu(t - 1, sacc0);
+      align();
+      phase_mfma(t, Kb1, Vb0, sacc1);
+      __syncthreads();
+      if (t + 1 >= n_tiles) break;
+      loads(t + 1, Kb1, Vb0);
+      phase_valu(t, sacc1);
+      align();
+      phase_mfma(t + 1, Kb0, Vb1, sacc0);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
