@@ -49,9 +49,9 @@ hipError_t launch_splitkv_bf16(const Problem& p, const Plan& plan, void* workspa
                                hipStream_t stream);
 
 // Tile constants shared by the planner and the kernels.
-constexpr int kPrefillBlockQ = 256;   // 8 waves x 32 queries
+constexpr int kPrefillBlockQ = 256;   // 4 waves x 64 queries
 constexpr int kPrefillBlockK = 64;    // keys per K/V tile
-constexpr int kPrefillThreads = 512;
+constexpr int kPrefillThreads = 256;
 
 constexpr int kF32BlockQ = 16;        // 16 query rows x 16 lanes
 constexpr int kF32BlockK = 32;
@@ -61,11 +61,10 @@ constexpr int kSplitThreads = 256;
 constexpr int kMergeThreads = 256;
 
 inline int prefill_lds_bytes(int D) {
-  // Two K and two V tiles and each wave's Q rows, padded, in 1 KB blocks.
+  // Two K and two V tiles, padded, in 1 KB blocks.
   const int kblk = (kPrefillBlockK * (D + 8) / 8 + 63) / 64;
   const int vblk = (kPrefillBlockK * (D + 32) / 8 + 63) / 64;
-  const int qblk = (32 * (D + 8) / 8 + 63) / 64;
-  return 1024 * (2 * kblk + 2 * vblk + (kPrefillThreads / 64) * qblk);
+  return 1024 * (2 * kblk + 2 * vblk);
 }
 inline int f32_lds_bytes(int D) { return 2 * kF32BlockK * D * 4; }
 

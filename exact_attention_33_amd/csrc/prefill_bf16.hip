@@ -14,63 +14,68 @@
 // and weight tiles never leave registers.
 //
 // gfx950 mapping:
-//  * workgroup = 8 waves = 256 queries; wave w owns queries [32w, 32w + 32).
-//    Waves w and w + 4 share a SIMD.  They run the per-tile work in two
-//    phases -- an MFMA phase (S(t+1) = K(t+1) Q^T and O += P(t) V(t)) and a
-//    VALU phase (mask, row max and exponentials of tile t+1) -- offset by one
-//    phase: while waves 0-3 are in their MFMA phase, waves 4-7 are in their
-//    VALU phase and vice versa, with a workgroup barrier between phases.
-//    MFMA and VALU instructions of two waves on one SIMD overlap almost
-//    perfectly (measured on MI355X), so each SIMD keeps its matrix pipe busy
-//    while the other wave does the softmax arithmetic;
+//  * workgroup = 4 waves = 256 queries, one wave per SIMD; wave w owns the 64
+//    queries [64w, 64w + 64) as two 32-query blocks.  With one wave per SIMD
+//    a wave has 512 registers: Q (64 rows), the output accumulator, two score
+//    tiles and two weight tiles all stay in registers.  Each wave reads whole
+//    K and V tiles from LDS, so 64 queries per wave halve the LDS traffic per
+//    FLOP against 32 (LDS bandwidth, about 150-185 B/clk per CU measured on
+//    MI355X, bounds a 32-query design);
+//  * software pipeline inside the wave: iteration t issues the MFMAs of
+//    S(t+2) = K(t+2) Q^T and O += P(t) V(t) and, between them, the softmax of
+//    tile t+1 (mask, row max, exponentials, row sum) on the VALU.  The three
+//    have no data dependence, and one wave keeps its matrix pipe nearly full
+//    while it issues about four VALU instructions per MFMA (measured: 64
+//    MFMAs with that VALU mix and their LDS operand reads take about 2,600
+//    cycles against 2,048 for the MFMAs alone).  Scheduling barriers fix the
+//    interleave: step j of an iteration holds one MFMA, the LDS reads of the
+//    operands two fragments ahead, a slice of the softmax and at most one
+//    tile load;
 //  * the score tile is computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: Q is the B operand and stays in registers for
-//    the whole sweep, K comes from LDS.  Lane (h, c) of a wave (h = lane / 32,
-//    c = lane % 32) then holds 16 scores of query c per 32-key block, at keys
-//    8*(r/4) + 4*h + r%4, so row max and row sum are in-lane plus one
-//    exchange between the two half-waves;
+//    v_mfma_f32_32x32x16_bf16: Q is the B operand, K comes from LDS.  Lane
+//    (h, c) of a wave (h = lane / 32, c = lane % 32) then holds, per 32-query
+//    block, 16 scores of query c per 32-key block, at keys 8*(r/4) + 4*h + r%4,
+//    so row max and row sum are in-lane plus one swap between the half-waves
+//    (v_permlane32_swap);
 //  * scores are kept in base 2: t = s * scale * log2(e), weights 2^(t - m) on
 //    v_exp_f32; the scale is applied in float32 to the float32 score;
 //  * the reference max m moves only when a row's max exceeds it by more than
-//    2^8 (or on the first visible key): the pages subtract the max only to
-//    keep the exponentials finite, and any reference at or above
-//    (row max - 8) keeps every weight <= 256.  The rescale of l and the
-//    accumulator then almost never runs; the result is the same function;
+//    8 (or on the first visible key): the pages subtract the max only to keep
+//    the exponentials finite, and any reference at or above (row max - 8)
+//    keeps every weight <= 256.  When it moves, l is rescaled at once and the
+//    output accumulator after the iteration's P V products (which still use
+//    the old reference), so the rescale never waits on the matrix pipe;
 //  * the output is accumulated transposed, O^T += V^T P^T, with the same MFMA:
 //    the weights convert to bf16 straight into the B operand (no LDS round
 //    trip) and V^T comes from V's natural [key][d] layout in LDS through two
-//    ds_read_b64_tr_b16 transposing reads per MFMA.  The row sum adds the
+//    ds_read_b64_tr_b16 transposing reads per fragment.  The row sum adds the
 //    float32 weights before rounding (a sum of bf16-rounded weights would
 //    carry their 2^-9 relative error into LSE for rows with few keys);
 //  * K and V move HBM -> LDS directly (global_load_lds_dwordx4: each lane's
 //    16 bytes land at M0 + 16 * lane, so one wave instruction fills a 1 KB
 //    block and the per-lane global address picks what goes where), with no
 //    staging registers.  Two K and two V buffers, each its own LDS array so
-//    the compiler can see that reading one never waits on a load into another;
-//  * pipeline: K(t+2) and V(t+1) are loaded while tiles t and t+1 are in use;
-//    a load has two phases (one tile) to land before the barrier that
-//    waits for it;
+//    the compiler can see that reading one never waits on a load into
+//    another.  Iteration t loads K(t+3) and V(t+1), spread over its first
+//    steps; the barrier that ends the iteration waits for them;
 //  * LDS layouts are padded so that every operand read is one per-lane base
-//    register plus a compile-time offset (no per-step address arithmetic, no
-//    address registers held across the loop) and conflict-free on the 64
-//    banks: K and Q rows carry 16 bytes of padding, so the 16 rows that a
-//    16-lane group reads with ds_read_b128 start 4 banks apart; V rows carry
-//    64 bytes, so the 4 rows x 64 bytes that 32 lanes read with
-//    ds_read_b64_tr_b16 start 16 banks apart.  Loads into LDS are 1 KB
-//    blocks of 64 lanes x 16 bytes; the slots that fall on padding receive
-//    a copy of valid data that is never read;
-//  * Q stays in LDS (each wave's 32 rows) and is read as the B operand in the
-//    MFMA phase, which leaves the registers for operand prefetch: each MFMA's
-//    operands are fetched a few MFMAs ahead;
+//    register plus a compile-time offset and conflict-free on the 64 banks:
+//    K rows carry 16 bytes of padding, so the 16 rows that a 16-lane group
+//    reads with ds_read_b128 start 4 banks apart; V rows carry 64 bytes, so
+//    the 4 rows x 64 bytes that 32 lanes read with ds_read_b64_tr_b16 start
+//    16 banks apart.  The slots of a 1 KB load block that fall on padding
+//    receive a copy of valid data that is never read;
 //  * causal: tiles past the workgroup's last visible key are never visited,
-//    waves skip tiles they cannot see, and only tiles that cross the diagonal
-//    or the kv_len boundary are masked element by element;
+//    a wave skips the work of tiles none of its queries sees, and only tiles
+//    that cross the diagonal or the kv_len boundary are masked element by
+//    element;
 //  * workgroup order: gfx950 deals workgroups round-robin to its 8 XCDs, each
 //    with its own L2.  Consecutive logical work items (the query tiles of one
 //    (batch, head), heaviest first when causal) are mapped to one XCD so that
 //    the workgroups sharing a head's K/V run together on one L2.
 #include <cmath>
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "fa_internal.h"
@@ -80,11 +85,61 @@ namespace {
 
 constexpr int kNumXcd = 8;
 constexpr float kLazyRescale = 8.0f;  // log2 of the largest weight allowed
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs (untyped 32-bit
+// data, no swizzle); out-of-range reads return zeros.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
 }
+
+// The two halves of a wave combined: every lane receives op(x[i], x[i ^ 32]).
+__device__ __forceinline__ float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// 16 bytes per lane from base + voff into LDS at dst + 16 * lane (one buffer
+// load into LDS), against a descriptor of `nbytes` bytes: lanes whose offset
+// is out of range read zeros.  The body exists only in the device pass: the
+// host pass of a HIP source has no buffer-descriptor type, and clang then
+// drops the host stubs of the kernels that use it.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, uint32_t voff,
+                                                  lds_ptr dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags), dst,
+      16, voff, 0, 0, 0);
+#endif
+}
+
+// S^T += K Q^T fragment products with the accumulator in VGPRs.  The score
+// tile is read by the softmax right after it is formed; the compiler places
+// every MFMA accumulator of this kernel in AGPRs, and reading AGPRs back
+// between MFMAs costs about twice a VALU operation per value (measured).
+// The output accumulator stays in AGPRs (it is read only at the end).  These
+// asm MFMAs are invisible to the compiler's hazard tracking, so their users
+// keep the rules themselves: back-to-back accumulation into the same VGPRs
+// (same opcode, exact overlap) needs no wait; a VALU read of a result waits
+// 16 wait states after the last MFMA that wrote it (mfma_guard; an 8-pass
+// MFMA needs 11); an operand register is overwritten no sooner than two
+// fragments (four MFMAs) after its last use.
+// The B operand (Q) is taken from AGPRs: Q is read only here, and keeping its
+// 64 registers out of the VGPRs leaves room for the score tile.
+__device__ __forceinline__ void mfma_s_first(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_s_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_guard() { asm volatile("s_nop 7\n\ts_nop 7"); }
 
 // Logical work item of workgroup `wg` when workgroups are dealt round-robin
 // to kNumXcd XCDs: XCD x gets a contiguous range of logical items.
@@ -94,25 +149,42 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t wg, int64_t G) {
   return x * q + (x < r ? x : r) + j;
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
+// f(integral_constant<int, J>) for J = 0 .. N-1, expanded at compile time (the
+// pipelined loops are too large for the unroller, and their register arrays
+// must only ever see constant indices).
+template <class F, int... J>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(Problem p, int n_qtiles) {
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_bf16_kernel(Problem p, int n_qtiles) {
   constexpr int BQ = kPrefillBlockQ, BK = kPrefillBlockK;
   constexpr int NW = kPrefillThreads / 64;   // waves per workgroup
+  constexpr int QW = BQ / NW;                // queries per wave
+  constexpr int NQB = QW / 32;               // 32-query blocks per wave
+  constexpr int NKB = BK / 32;               // 32-key blocks per tile
+  constexpr int NP = BK / 16;                // 16-key weight fragments per query block
+  constexpr int DK = D / 16;                 // k-steps of S
+  constexpr int DB = D / 32;                 // 32-wide d-blocks of O
+  constexpr int NF = NKB * DK;               // K fragments per tile (= V fragments)
+  static_assert(NF == NP * DB, "K and V fragment counts match");
   constexpr int CPR = D / 8;                 // 16-byte chunks of data per row
-  constexpr int KROW = D + 8;                // K/Q row stride in LDS (elements)
+  constexpr int KROW = D + 8;                // K row stride in LDS (elements)
   constexpr int VROW = D + 32;               // V row stride in LDS (elements)
   constexpr int KCH = KROW / 8, VCH = VROW / 8;        // 16-byte slots per row
   constexpr int KBLK = (BK * KCH + 63) / 64;           // 1 KB blocks per K tile
   constexpr int VBLK = (BK * VCH + 63) / 64;           // 1 KB blocks per V tile
-  constexpr int QBLK = (32 * KCH + 63) / 64;           // 1 KB blocks per wave's Q rows
-  static_assert(NW == 8 && BQ == 32 * NW, "8 waves of 32 queries");
+  static_assert(NW == 4 && QW == 64, "4 waves of 64 queries");
   __shared__ __attribute__((aligned(1024))) __bf16 Kb0[KBLK * 512];
   __shared__ __attribute__((aligned(1024))) __bf16 Kb1[KBLK * 512];
   __shared__ __attribute__((aligned(1024))) __bf16 Vb0[VBLK * 512];
   __shared__ __attribute__((aligned(1024))) __bf16 Vb1[VBLK * 512];
-  __shared__ __attribute__((aligned(1024))) __bf16 Qs_all[NW * QBLK * 512];
 
   const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
   int qt = (int)(logical % n_qtiles);
@@ -121,13 +193,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(Problem p
   const int b = (int)(bh / p.H);
   const int N = p.N, M = p.M;
   const int tid = threadIdx.x;
-  const int w = tid / 64, lane = tid % 64, hl = lane / 32, ql = lane % 32;
-  const bool group_a = w < NW / 2;  // waves 0-3 lead, waves 4-7 follow one phase behind
-  const int kvl = clamp_kv(p.kv_len, b, M);
+  const int lane = tid % 64, hl = lane / 32, ql = lane % 32;
+  const int ws = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index (uniform)
+  // uniform in fact; readfirstlane lets the compiler keep it (and every tile
+  // descriptor built from it) in scalar registers
+  const int kvl = __builtin_amdgcn_readfirstlane(clamp_kv(p.kv_len, b, M));
   const int q0 = qt * BQ;
-  const int qw0 = q0 + 32 * w;  // first query of this wave
-  const int qrow = qw0 + ql;    // this lane's query
-  const int off = kvl - N;      // key j visible to query i iff j < kvl and (!causal or j <= i + off)
+  const int qw0 = q0 + QW * ws;  // first query of this wave
+  const int off = kvl - N;       // key j visible to query i iff j < kvl and (!causal or j <= i + off)
   const int q_last = min(q0 + BQ, N) - 1;
   const int kv_end = CAUSAL ? min(kvl, q_last + off + 1) : kvl;
   const int n_tiles = kv_end > 0 ? (kv_end + BK - 1) / BK : 0;
@@ -136,325 +209,393 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(Problem p
   const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D;
   const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D;
 
+  // ---- tile loads ----
   // Slot s of a padded tile holds row s / CH, chunk s % CH; slots on the
   // padding (chunk >= CPR) load chunk 0 of that row (valid data, never read).
-  auto load_padded = [&](const __bf16* src, int row0, int row_max, __bf16* dst, int nblk, int ch,
-                         int first_blk, int blk_step) {
-    for (int blk = first_blk; blk < nblk; blk += blk_step) {
-      const int slot = blk * 64 + lane;
-      const int r = slot / ch, c = slot % ch;
-      const int row = min(row0 + r, row_max);
-      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)row * D + (c < CPR ? c * 8 : 0)),
-                                       (lds_ptr)(dst + blk * 512), 16, 0, 0);
-    }
-  };
-  // K and V tiles: this wave loads blocks w, w + NW, ... of each.  The
-  // per-lane byte offsets of those blocks' slots within a tile (< 64 KB) are
-  // fixed, so they are computed once and kept two to a register; a tile load
-  // is then a shift or mask and an add per block, with the tile base in
-  // scalar registers.  Rows past kv_len (last tile only) repeat the last
-  // valid row (finite data whose weights are exactly 0).
+  // Wave ws loads blocks ws, ws + NW, ... of each tile; a wave with fewer
+  // blocks than the others loads the tile's last block again (the same bytes
+  // to the same place), so every wave issues the same loads without a branch.
+  // The per-lane byte offsets of a wave's slots within a tile (< 64 KB) are
+  // fixed, so they are computed once and kept two to a register.  Loads are
+  // buffer loads into LDS against a descriptor that ends at kv_len: rows past
+  // it (last tile) and whole tiles past it read as zeros -- finite data whose
+  // weights are 0 -- with no clamping arithmetic.  (Buffer rather than global
+  // loads also keep the compiler's LDS wait counting exact: it treats a global
+  // load into LDS like a flat access and then waits for every LDS read.)
   constexpr int KPW = (KBLK + NW - 1) / NW, VPW = (VBLK + NW - 1) / NW;
-  constexpr int ROWB = D * 2, LOG_ROWB = D == 128 ? 8 : 7;  // bytes per global row
-  static_assert(ROWB == 1 << LOG_ROWB && BK * ROWB <= 65536, "row bytes");
-  const int ws = __builtin_amdgcn_readfirstlane(w);
+  constexpr int NITEM = KPW + VPW;  // load items per wave per iteration
+  constexpr int ROWB = D * 2;       // bytes per global row
+  static_assert(BK * ROWB <= 65536, "tile offsets fit 16 bits");
   auto slot_off = [&](int blk, int ch) -> uint32_t {
     const int slot = blk * 64 + lane, r = slot / ch, cc = slot % ch;
     return (uint32_t)(r * ROWB + (cc < CPR ? cc * 16 : 0));
   };
+  auto kblock = [&](int i) { return min(ws + i * NW, KBLK - 1); };
+  auto vblock = [&](int i) { return min(ws + i * NW, VBLK - 1); };
   uint32_t koff[(KPW + 1) / 2], voff[(VPW + 1) / 2];
 #pragma unroll
   for (int i = 0; i < KPW; i += 2)
-    koff[i / 2] = slot_off(ws + i * NW, KCH) | (i + 1 < KPW ? slot_off(ws + (i + 1) * NW, KCH) << 16 : 0u);
+    koff[i / 2] = slot_off(kblock(i), KCH) | (i + 1 < KPW ? slot_off(kblock(i + 1), KCH) << 16 : 0u);
 #pragma unroll
   for (int i = 0; i < VPW; i += 2)
-    voff[i / 2] = slot_off(ws + i * NW, VCH) | (i + 1 < VPW ? slot_off(ws + (i + 1) * NW, VCH) << 16 : 0u);
-  auto load_tile = [&](const __bf16* src, int t, __bf16* dst, const uint32_t* offs, int nblk,
-                       auto npw_c) {
-    constexpr int npw = decltype(npw_c)::value;
-    const char* base = (const char*)(src + (size_t)t * BK * D);
-    const int rmax = kvl - 1 - t * BK;  // last valid row of this tile (>= 0)
-    // Opaque copies: the unpacked offsets must not be hoisted out of the
-    // main loop, where they would hold twice the registers.
-    uint32_t pk[(npw + 1) / 2];
-#pragma unroll
-    for (int i = 0; i < (npw + 1) / 2; ++i) {
-      pk[i] = offs[i];
-      asm volatile("" : "+v"(pk[i]));
-    }
-    offs = pk;
-    if (rmax >= BK - 1) {
-#pragma unroll
-      for (int i = 0; i < npw; ++i)
-        if (ws + i * NW < nblk) {
-          const uint32_t o = i % 2 ? offs[i / 2] >> 16 : offs[i / 2] & 0xFFFFu;
-          __builtin_amdgcn_global_load_lds((const void*)(base + o),
-                                           (lds_ptr)(dst + (ws + i * NW) * 512), 16, 0, 0);
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < npw; ++i)
-        if (ws + i * NW < nblk) {
-          const uint32_t u = i % 2 ? offs[i / 2] >> 16 : offs[i / 2] & 0xFFFFu;
-          const uint32_t o = (uint32_t)min((int)(u >> LOG_ROWB), rmax) << LOG_ROWB | (u & (ROWB - 1));
-          __builtin_amdgcn_global_load_lds((const void*)(base + o),
-                                           (lds_ptr)(dst + (ws + i * NW) * 512), 16, 0, 0);
-        }
-    }
+    voff[i / 2] = slot_off(vblock(i), VCH) | (i + 1 < VPW ? slot_off(vblock(i + 1), VCH) << 16 : 0u);
+  // One block: slots of block blk of tile t of src into block blk of dst,
+  // against a descriptor that ends at kv_len.  (readfirstlane: the clamp has
+  // no scalar instruction, and a descriptor the compiler cannot prove uniform
+  // costs a loop around every load.)
+  auto load_block = [&](const __bf16* src, int t, __bf16* dst, uint32_t packed, int i, int blk) {
+    asm volatile("" : "+v"(packed));  // keep the unpacking next to its use
+    const uint32_t u = i % 2 ? packed >> 16 : packed & 0xFFFFu;
+    const int nrec = __builtin_amdgcn_readfirstlane(max(0, min(kvl - t * BK, BK)) * ROWB);
+    buffer_load_lds16(src + (size_t)t * BK * D, nrec, u, (lds_ptr)(dst + blk * 512));
   };
-  auto load_k = [&](int t, __bf16* dst) { load_tile(Kg, t, dst, koff, KBLK, std::integral_constant<int, KPW>{}); };
-  auto load_v = [&](int t, __bf16* dst) { load_tile(Vg, t, dst, voff, VBLK, std::integral_constant<int, VPW>{}); };
+  auto load_k_item = [&](int i, int t, __bf16* dst) { load_block(Kg, t, dst, koff[i / 2], i, kblock(i)); };
+  auto load_v_item = [&](int i, int t, __bf16* dst) { load_block(Vg, t, dst, voff[i / 2], i, vblock(i)); };
+  auto load_k = [&](int t, __bf16* dst) {
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) load_k_item(i, t, dst);
+  };
+  auto load_v = [&](int t, __bf16* dst) {
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) load_v_item(i, t, dst);
+  };
+  // Load item j of iteration t: K(t+3) blocks into Kdst, then V(t+1) blocks
+  // into Vdst (tiles past the last read as zeros).
+  auto load_item = [&](int j, int t, __bf16* Kdst, __bf16* Vdst) {
+    if (j < KPW) load_k_item(j, t + 3, Kdst);
+    else if (j < NITEM) load_v_item(j - KPW, t + 1, Vdst);
+  };
 
-  // This wave's 32 query rows (rows past N: any finite data, never written out).
-  __bf16* Qs = Qs_all + w * QBLK * 512;
-  load_padded(Qg, qw0, N - 1, Qs, QBLK, KCH, 0, 1);
+  // ---- Q in registers: B operand of S^T = K Q^T ----
+  // Fragment (qb, kb): lane (h, c) holds Q[qw0 + 32 qb + c][16 kb + 8 h .. + 8].
+  // Rows past N hold a copy of row N - 1 (finite, never written out).
+  bf16x8 qf[NQB][DK];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int row = min(qw0 + 32 * qb + ql, N - 1);
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb) qf[qb][kb] = *(const bf16x8*)(Qg + (size_t)row * D + kb * 16 + hl * 8);
+  }
 
-  // Per-lane base offsets (elements) of the three operand reads.
+  // Per-lane base offsets (elements) of the operand reads.
   const int kbase = ql * KROW + hl * 8;   // + (32 nb) KROW + 16 kb
   const int vbase = (4 * hl + (lane % 16) / 4) * VROW + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
                                           // + (32 nb + 16 t2) VROW + 32 db, + 8 VROW for the upper 4 keys
 
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  f32x16 sacc0[BK / 32], sacc1[BK / 32];
-  bf16x8 pf[BK / 16];       // weights of the tile whose PV is next
-  float m_run = -INFINITY;  // reference max of t = s * scale * log2(e)
-  float l_run = 0.f;        // this lane's part of the running sum
-  // A scale of 0 would turn a masked -inf score into NaN (-inf * 0); a floor
-  // of 1e-30 changes the weights of finite scores by less than 1e-20.
-  const float c = fmaxf(p.scale * kLog2e, 1e-30f);
-
-  // a wave none of whose queries sees a key of tile t skips its math
-  auto active = [&](int t) { return t < n_tiles && (!CAUSAL || t * BK <= qw0 + 31 + off); };
-
-  // ---- operand fetches ----
-  auto fetch_k = [&](const __bf16* Ks, int kb, int nb) -> bf16x8 {
+  // K fragment i (kb-major): rows 32 nb .. + 32, columns 16 kb .. + 16.
+  auto fetch_k = [&](const __bf16* Ks, int i) -> bf16x8 {
+    const int kb = i / NKB, nb = i % NKB;
     return *(const bf16x8*)(Ks + kbase + nb * 32 * KROW + kb * 16);
   };
-  auto fetch_q = [&](int kb) -> bf16x8 { return *(const bf16x8*)(Qs + kbase + kb * 16); };
-  // V^T operand of PV MFMA i = (nb, t2, db).  B operand slot 8*hl + e of
-  // 16-key block (nb, t2) is key 32 nb + 16 t2 + 8 (e / 4) + 4 hl + e % 4;
-  // the A operand for the same slots comes from two transposing reads of 4
-  // consecutive keys each: within a 16-lane group, lane j reads row
-  // kbase + j / 4 at column dsrc + 4 (j % 4), and lane i receives the 4 keys
-  // at column dsrc + i.
+  // V^T fragment i = (nb, t2, db), db fastest.  B operand slot 8*hl + e of
+  // 16-key block (nb, t2) is key 32 nb + 16 t2 + 8 (e / 4) + 4 hl + e % 4 (the
+  // order in which the score layout hands the weights over); the A operand
+  // for the same slots comes from two transposing reads of 4 consecutive keys
+  // each: within a 16-lane group, lane j reads row kbase + j / 4 at column
+  // dsrc + 4 (j % 4), and lane i receives the 4 keys at column dsrc + i.
   auto fetch_v = [&](const __bf16* Vs, int i) -> bf16x8 {
-    const int nb = i / (2 * (D / 32)), t2 = (i / (D / 32)) % 2, db = i % (D / 32);
+    const int nb = i / (2 * DB), t2 = (i / DB) % 2, db = i % DB;
     const __bf16* a = Vs + vbase + (nb * 32 + t2 * 16) * VROW + db * 32;
     const s16x4 lo = lds_read_tr16(a);
     const s16x4 hi = lds_read_tr16(a + 8 * VROW);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // ---- S^T = K Q^T for 64 keys x 32 queries (prologue only) ----
-  auto compute_s = [&](const __bf16* Ks, f32x16* sacc) {
+  f32x16 oacc[DB][NQB];
 #pragma unroll
-    for (int nb = 0; nb < BK / 32; ++nb) sacc[nb] = f32x16{};
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-      const bf16x8 qv = fetch_q(kb);
+    for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = f32x16{};
+  f32x16 sacc[NKB][NQB];  // score tile: S(t+1), then S(t+2), during iteration t
+  bf16x8 pacc[NQB][NP];   // weight tile: P(t), then P(t+1), during iteration t
+  float m_run[NQB], l_run[NQB], alpha[NQB];  // reference max (base 2), this lane's part of the sum
 #pragma unroll
-      for (int nb = 0; nb < BK / 32; ++nb)
-        sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fetch_k(Ks, kb, nb), qv, sacc[nb], 0, 0, 0);
-    }
+  for (int qb = 0; qb < NQB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+    alpha[qb] = 1.f;
+  }
+  bool rescale = false;  // wave-uniform: the accumulator owes a rescale by alpha
+  // A scale of 0 would turn a masked -inf score into NaN (-inf * 0); a floor
+  // of 1e-30 changes the weights of finite scores by less than 1e-20.
+  const float c = fmaxf(p.scale * kLog2e, 1e-30f);
+
+  // Tiles that cross the diagonal or the kv_len boundary -- and tiles past
+  // the workgroup's last one, whose LDS holds stale data -- are masked
+  // element by element; every other tile is fully visible to the wave.
+  auto need_mask = [&](int t) {
+    return (t * BK + BK > kvl) || (CAUSAL && t * BK + BK - 1 > qw0 + off);
   };
 
-  // ---- softmax of tile t: mask, running max, weights 2^(t - m) as the
-  //      bf16 B operand of the PV product, row sums ----
-  auto softmax = [&](int t, f32x16* sacc) {
+  // ---- softmax of one tile, in small units that the pipeline spreads out ----
+  // The weights of a tile are computed speculatively against the current
+  // reference m (the common case: the reference moves only when a row max
+  // exceeds it by more than 8), while the tile's row max is gathered:
+  //   EM units (key block 0): max, weight, sum and bf16 weight of 2 scores;
+  //   MX units (key block 1): max of 4 scores;
+  //   check (after all EM and MX units, scores still intact): if any row's
+  //     tile max exceeds m + 8 -- or m is still -inf -- the reference moves
+  //     and key block 0 is computed again against it (rare, not pipelined);
+  //   EX units (key block 1): weight, sum and bf16 weight of 2 scores.
+  // Each score is read from the accumulator once per use and consumed at
+  // once, so no copy of the score tile stays live.
+  constexpr int NU_EM = NQB * 8, NU_MX = NQB * 4, NU_EX = NQB * 8;
+  float mxp[NQB][2], m_use[NQB], ps[NQB][2];
+  auto sm_begin = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      mxp[qb][0] = mxp[qb][1] = -INFINITY;
+      ps[qb][0] = ps[qb][1] = 0.f;
+      m_use[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+    }
+  };
+  // weights of 2 scores (pair `pair` of 16-key half t2 of key block nb)
+  auto exp_pair = [&](f32x16 (&s)[NKB][NQB], int nb, int qb, int t2, int pair, bool with_max) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * pair + h, r = (2 * t2 + e / 4) * 4 + (e % 4);
+      const float v = s[nb][qb][r];
+      if (with_max) mxp[qb][h] = fmaxf(mxp[qb][h], v);
+      const float pv = fast_exp2(fmaf(v, c, -m_use[qb]));
+      ps[qb][h] += pv;
+      pacc[qb][nb * 2 + t2][e] = (__bf16)pv;
+    }
+  };
+  auto unit_em = [&](f32x16 (&s)[NKB][NQB], auto uc) {
+    constexpr int u = decltype(uc)::value, qb = u / 8, t2 = (u / 4) % 2, pair = u % 4;
+    exp_pair(s, 0, qb, t2, pair, true);
+  };
+  auto unit_mx = [&](f32x16 (&s)[NKB][NQB], auto uc) {
+    constexpr int u = decltype(uc)::value, qb = u / 4, r0 = (u % 4) * 4;
+    float& mref = mxp[qb][u % 2];
+    mref = fmaxf(fmaxf(mref, s[1][qb][r0]), s[1][qb][r0 + 1]);
+    mref = fmaxf(fmaxf(mref, s[1][qb][r0 + 2]), s[1][qb][r0 + 3]);
+  };
+  auto unit_ex = [&](f32x16 (&s)[NKB][NQB], auto uc) {
+    constexpr int u = decltype(uc)::value, qb = u / 8, t2 = (u / 4) % 2, pair = u % 4;
+    exp_pair(s, 1, qb, t2, pair, false);
+  };
+  auto sm_check = [&](f32x16 (&s)[NKB][NQB]) {
+    bool over = false;
+    float mxc[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      mxc[qb] = swap_halves_max(fmaxf(mxp[qb][0], mxp[qb][1])) * c;  // -inf stays -inf (c > 0)
+      over |= mxc[qb] > m_run[qb] + kLazyRescale;  // also true when m is -inf and a score is not
+    }
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform, rare
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float m_new = fmaxf(m_run[qb], mxc[qb]);
+        // e^(m_old - m_new); nothing accumulated yet when m_old = -inf
+        const float a = m_run[qb] == -INFINITY ? 0.f : fast_exp2(m_run[qb] - m_new);
+        alpha[qb] *= a;
+        l_run[qb] *= a;
+        m_run[qb] = m_new;
+        m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
+        ps[qb][0] = ps[qb][1] = 0.f;
+      }
+      rescale = true;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int pair = 0; pair < 4; ++pair) exp_pair(s, 0, qb, t2, pair, false);
+    }
+  };
+  auto sm_end = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) l_run[qb] += ps[qb][0] + ps[qb][1];
+  };
+  // Results computed so far must exist here: an empty statement that reads
+  // them keeps the compiler from sinking their arithmetic past the branch
+  // that follows (which would pull it out of the interleaved block).
+  auto pin_weights = [&](int nb) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      asm volatile("" ::"v"(pacc[qb][nb * 2]), "v"(pacc[qb][nb * 2 + 1]));
+      asm volatile("" ::"v"(ps[qb][0]), "v"(ps[qb][1]), "v"(mxp[qb][0]), "v"(mxp[qb][1]));
+    }
+  };
+  auto apply_mask = [&](int t, f32x16 (&s)[NKB][NQB]) {
     const int k0 = t * BK;
-    const bool need_mask = (k0 + BK > kvl) || (CAUSAL && k0 + BK - 1 > qw0 + off);
-    if (need_mask) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qrow = qw0 + 32 * qb + ql;
       const int lim = CAUSAL ? min(kvl - 1, qrow + off) : kvl - 1;  // last visible key
 #pragma unroll
-      for (int nb = 0; nb < BK / 32; ++nb)
+      for (int nb = 0; nb < NKB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + nb * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
-          if (key > lim) sacc[nb][r] = -INFINITY;
+          if (key > lim) s[nb][qb][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+  };
+  // Whole softmax of tile t (prologue only).
+  auto softmax_all = [&](int t, f32x16 (&s)[NKB][NQB]) {
+    mfma_guard();  // compute_s just wrote the scores
+    if (need_mask(t)) apply_mask(t, s);
+    sm_begin();
+    static_for<NU_EM>([&](auto uc) { unit_em(s, uc); });
+    static_for<NU_MX>([&](auto uc) { unit_mx(s, uc); });
+    sm_check(s);
+    static_for<NU_EX>([&](auto uc) { unit_ex(s, uc); });
+    sm_end();
+  };
+  // S^T = K Q^T for one tile, not interleaved (prologue only).
+  auto compute_s = [&](const __bf16* Ks, f32x16 (&s)[NKB][NQB]) {
 #pragma unroll
-    for (int nb = 0; nb < BK / 32; ++nb)
+    for (int i = 0; i < NF; ++i) {
+      const bf16x8 kf = fetch_k(Ks, i);
+      const int kb = i / NKB, nb = i % NKB;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxc = mx * c;  // -inf stays -inf (c > 0)
-    if (__any(mxc > m_run + kLazyRescale)) {
-      const float m_new = fmaxf(m_run, mxc);
-      // e^(m_old - m_new); nothing accumulated yet when m_old = -inf
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-      m_run = m_new;
+      for (int qb = 0; qb < NQB; ++qb) {
+        if (kb == 0) mfma_s_first(s[nb][qb], kf, qf[qb][kb]);
+        else mfma_s_acc(s[nb][qb], kf, qf[qb][kb]);
+      }
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // no visible key yet: all weights 0
-    float psum = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < BK / 32; ++nb)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = (2 * t2 + e / 4) * 4 + (e % 4);
-          const float pv = fast_exp2(fmaf(sacc[nb][r], c, -m_use));
-          psum += pv;
-          pf[nb * 2 + t2][e] = (__bf16)pv;
-        }
-    l_run += psum;
   };
 
-  // MFMA phase of tile t: S(t+1) from Knext into snext (when with_s), then
-  // O += P(t) V(t), as one sequence of MFMAs whose LDS operands are fetched
-  // ahead (KPD steps of S, VPD MFMAs of PV).  Scheduling barriers pin this
-  // order: left alone, the compiler fetches each operand just before its
-  // MFMA and every MFMA then waits out a full LDS round trip.
-  constexpr int NPV = (BK / 16) * (D / 32);  // MFMAs of O += P V
-  constexpr int KPD = 2, VPD = 4;
-  auto mfma_phase = [&](bool with_s, const __bf16* Ks, const __bf16* Vs, f32x16* snext) {
-    bf16x8 vfr[VPD];
-    if (with_s) {
-      bf16x8 kfr[KPD][BK / 32], qfr[KPD];
+  // ---- one pipelined iteration ----
+  // Work of iteration t: O += P(t) V(t), the softmax of S(t+1) into P(t+1),
+  // S(t+2) = K(t+2) Q^T.  One score and one weight tile suffice because the
+  // steps run in three phases, one MFMA per step:
+  //   A: the P V MFMAs (fragment j / 2, query block j % 2), with the MX
+  //      units and then the EM units; then the check;
+  //   B: the S MFMAs of key block 0 -- whose scores have been consumed --
+  //      with the EX units;
+  //   C: the S MFMAs of key block 1.
+  // Operands are read PF fragments ahead; tile load item k goes at step
+  // 3k + 1.
+  constexpr int PF = 2;
+  constexpr int NSA = 2 * NF, NSB = NQB * DK;  // steps of phases A and B (C = B)
+  auto iteration = [&](int t, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst) {
+    sm_begin();
+    // K operands: a ring of PF + 2, so that a read overwrites a register two
+    // fragments after the asm MFMAs last used it
+    constexpr int KR = PF + 2;
+    bf16x8 vr[PF + 1], kr[KR];
 #pragma unroll
-      for (int kb = 0; kb < KPD; ++kb) {
-        qfr[kb] = fetch_q(kb);
-#pragma unroll
-        for (int nb = 0; nb < BK / 32; ++nb) kfr[kb][nb] = fetch_k(Ks, kb, nb);
-      }
-#pragma unroll
-      for (int kb = 0; kb < D / 16; ++kb) {
-        __builtin_amdgcn_sched_barrier(0);
-        const int slot = kb % KPD;
-        const bf16x8 qcur = qfr[slot];
-        bf16x8 kcur[BK / 32];
-#pragma unroll
-        for (int nb = 0; nb < BK / 32; ++nb) kcur[nb] = kfr[slot][nb];
-        const int nx = kb + KPD;  // next fetch: S operands, then the first PV operands
-        if (nx < D / 16) {
-          qfr[slot] = fetch_q(nx);
-#pragma unroll
-          for (int nb = 0; nb < BK / 32; ++nb) kfr[slot][nb] = fetch_k(Ks, nx, nb);
-        } else if (nx - D / 16 < VPD) {
-          vfr[nx - D / 16] = fetch_v(Vs, nx - D / 16);
-        }
-#pragma unroll
-        for (int nb = 0; nb < BK / 32; ++nb)
-          snext[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[nb], qcur, kb == 0 ? f32x16{} : snext[nb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = KPD; i < VPD; ++i) vfr[i] = fetch_v(Vs, i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < VPD; ++i) vfr[i] = fetch_v(Vs, i);
-    }
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
+    for (int i = 0; i < PF; ++i) vr[i] = fetch_v(Vs, i);
+    // phase A
+    static_for<NSA>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 vcur = vfr[i % VPD];
-      if (i + VPD < NPV) vfr[i % VPD] = fetch_v(Vs, i + VPD);
-      const int nb = i / (2 * (D / 32)), t2 = (i / (D / 32)) % 2, db = i % (D / 32);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, pf[nb * 2 + t2], oacc[db], 0, 0, 0);
-    }
+      constexpr int i = j / 2, qb = j % 2;
+      constexpr int nb = i / (2 * DB), t2 = (i / DB) % 2, db = i % DB;
+      oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % (PF + 1)], pacc[qb][nb * 2 + t2],
+                                                            oacc[db][qb], 0, 0, 0);
+      if constexpr (qb == 0 && i + PF < NF) vr[(i + PF) % (PF + 1)] = fetch_v(Vs, i + PF);
+      // MX units over the first half of the steps, EM units over the second:
+      // the MFMAs of the first half read P(t)'s key block 0, which the EM
+      // units overwrite with P(t+1)'s
+      constexpr int H = NSA / 2;
+      if constexpr (j < H) {
+        constexpr int u0 = (j * NU_MX + H - 1) / H, u1 = ((j + 1) * NU_MX + H - 1) / H;
+        static_for<u1 - u0>([&](auto uc) { unit_mx(sacc, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
+      } else {
+        constexpr int u0 = ((j - H) * NU_EM + H - 1) / H, u1 = ((j - H + 1) * NU_EM + H - 1) / H;
+        static_for<u1 - u0>([&](auto uc) { unit_em(sacc, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
+      }
+      if constexpr (j % 3 == 1 && j / 3 < NITEM) load_item(j / 3, t, Kdst, Vdst);
+      // the first K operands of phase B, during the last steps of phase A
+      if constexpr (j >= NSA - PF) kr[j - (NSA - PF)] = fetch_k(Ks, (j - (NSA - PF)) * NKB);
+    });
     __builtin_amdgcn_sched_barrier(0);
-  };
-  auto phase_mfma = [&](int t, const __bf16* Knext, const __bf16* Vcur, f32x16* snext) {
-    if (active(t + 1)) {
-      mfma_phase(true, Knext, Vcur, snext);  // active(t+1) implies active(t)
-    } else {
-      // snext is not read again; defining it on this path too ends the live
-      // range of the value it held (otherwise both accumulators stay live)
 #pragma unroll
-      for (int nb = 0; nb < BK / 32; ++nb) snext[nb] = f32x16{};
-      if (active(t)) mfma_phase(false, Knext, Vcur, snext);
+    for (int k = (NSA + 1) / 3; k < NITEM; ++k) load_item(k, t, Kdst, Vdst);
+    pin_weights(0);
+    sm_check(sacc);
+    // phases B and C: S fragments (kb, nb) in order nb-major, kb, query block
+    static_for<2 * NSB>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int f = j / NQB, qb = j % NQB;     // f-th S fragment of this iteration
+      constexpr int nb = f / DK, kb = f % DK;
+      if constexpr (kb == 0) mfma_s_first(sacc[nb][qb], kr[f % KR], qf[qb][kb]);
+      else mfma_s_acc(sacc[nb][qb], kr[f % KR], qf[qb][kb]);
+      if constexpr (qb == 0 && f + PF < NF) {
+        constexpr int f2 = f + PF;
+        kr[f2 % KR] = fetch_k(Ks, (f2 % DK) * NKB + f2 / DK);
+      }
+      if constexpr (j < NSB) {
+        constexpr int u0 = (j * NU_EX + NSB - 1) / NSB, u1 = ((j + 1) * NU_EX + NSB - 1) / NSB;
+        static_for<u1 - u0>([&](auto uc) { unit_ex(sacc, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
+      }
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    pin_weights(1);
+    sm_end();
+  };
+  // Iteration t: K(t+2) in Ks, V(t) in Vs; loads K(t+3) into Kdst and V(t+1)
+  // into Vdst.  Every wave runs the whole pipeline every iteration: a tile
+  // that none of a wave's queries sees is fully masked and adds weights of
+  // exactly 0 (at most two iterations per workgroup and the diagonal tiles of
+  // the later waves; one code path keeps the interleave and the register
+  // assignment fixed).
+  auto step_tile = [&](int t, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst) {
+    mfma_guard();  // the last iteration's final MFMAs wrote the scores
+    if (need_mask(t + 1)) apply_mask(t + 1, sacc);
+    iteration(t, Ks, Vs, Kdst, Vdst);
+    // the iteration's P V products used the old reference: rescale now
+    if (rescale) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha[qb];
+        alpha[qb] = 1.f;
+      }
+      rescale = false;
     }
-  };
-  // VALU phase of tile t: softmax of tile t+1 (its weights feed the next PV).
-  auto phase_valu = [&](int t, f32x16* snext) {
-    if (active(t + 1)) softmax(t + 1, snext);
-  };
-  // Barrier that only aligns the phases of the two wave groups: nothing is
-  // written to LDS that a read on its far side depends on, so it carries no
-  // memory fence (a fence would also wait for the in-flight tile loads).
-  auto align = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
   };
 
-  // Prologue: Q, tiles 0 (K, V) and 1 (K) in LDS; S(0) and its softmax in
-  // every wave (the following group then idles through its first VALU phase).
+  // Prologue: K(0), K(1), V(0) in LDS; S(0) and its softmax, S(1); K(2) in.
   if (n_tiles > 0) {
     load_k(0, Kb0);
     load_v(0, Vb0);
     if (n_tiles > 1) load_k(1, Kb1);
   }
   __syncthreads();
-  if (active(0)) {
-    compute_s(Kb0, sacc0);
-    softmax(0, sacc0);
-  }
-  __syncthreads();  // every wave is done with K(0) before slot 0 loads K(2) over it
+  compute_s(Kb0, sacc);
+  __syncthreads();  // every wave is done with K(0) before K(2) goes over it
+  if (n_tiles > 2) load_k(2, Kb0);
+  softmax_all(0, sacc);
+  compute_s(Kb1, sacc);
+  // nothing accumulated yet: a reference move only resets the bookkeeping
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) alpha[qb] = 1.f;
+  rescale = false;
+  __syncthreads();
 
-  // Phase slots: the leading group runs M(t) in slot 2t and V(t) in slot
-  // 2t + 1; the following group runs V(t - 1) in slot 2t and M(t) in slot
-  // 2t + 1.  Slot 2t also issues the loads of K(t+2) and V(t+1); the full
-  // barrier after slot 2t + 1 waits for them.  Each group has its own loop
-  // (same barriers, same count), so each keeps only one score accumulator
-  // live at a time; both loops are unrolled by two tiles so that every LDS
-  // buffer and accumulator is fixed at compile time.
-  auto loads = [&](int t, __bf16* Kdst, __bf16* Vdst) {
-    if (t + 2 < n_tiles) load_k(t + 2, Kdst);
-    if (t + 1 < n_tiles) load_v(t + 1, Vdst);
-  };
-  if (group_a) {
-    for (int t = 0; t < n_tiles; t += 2) {
-      loads(t, Kb0, Vb1);
-      phase_mfma(t, Kb1, Vb0, sacc1);
-      align();
-      phase_valu(t, sacc1);
-      __syncthreads();
-      if (t + 1 >= n_tiles) break;
-      loads(t + 1, Kb1, Vb0);
-      phase_mfma(t + 1, Kb0, Vb1, sacc0);
-      align();
-      phase_valu(t + 1, sacc0);
-      __syncthreads();
-    }
-  } else {
-    for (int t = 0; t < n_tiles; t += 2) {
-      loads(t, Kb0, Vb1);
-      if (t > 0) phase_valu(t - 1, sacc0);
-      align();
-      phase_mfma(t, Kb1, Vb0, sacc1);
-      __syncthreads();
-      if (t + 1 >= n_tiles) break;
-      loads(t + 1, Kb1, Vb0);
-      phase_valu(t, sacc1);
-      align();
-      phase_mfma(t + 1, Kb0, Vb1, sacc0);
-      __syncthreads();
-    }
+  for (int t = 0; t < n_tiles; t += 2) {
+    step_tile(t, Kb0, Vb0, Kb1, Vb1);
+    if (t + 1 >= n_tiles) break;
+    step_tile(t + 1, Kb1, Vb1, Kb0, Vb0);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qrow < N) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* Orow = (__bf16*)p.o + (size_t)bh * N * D + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int qrow = qw0 + 32 * qb + ql;
+    const float l_tot = swap_halves_sum(l_run[qb]);
+    if (qrow < N) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      __bf16* Orow = (__bf16*)p.o + (size_t)bh * N * D + (size_t)qrow * D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x4 ov;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[db][4 * j + i] * inv);
-        *(bf16x4*)(Orow + db * 32 + 8 * j + 4 * hl) = ov;
-      }
-    if (hl == 0)
-      p.lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 ov;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[db][qb][4 * j + i] * inv);
+          *(bf16x4*)(Orow + db * 32 + 8 * j + 4 * hl) = ov;
+        }
+      if (hl == 0)
+        p.lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run[qb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    }
   }
 }
 

@@ -49,7 +49,7 @@ def test_status_strings():
 def test_planner_paths():
     p = fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True)
     assert p["path_name"] == "prefill" and p["block_k"] == 64
-    assert p["block_q"] == 32 * p["threads"] // 64          # 32 queries per wave
+    assert p["block_q"] == p["threads"] and p["block_q"] % 64 == 0  # 64 queries per wave
     assert p["grid"] == -(-8192 // p["block_q"]) * 64 and p["workspace_bytes"] == 0
     assert p["lds_bytes"] <= 160 * 1024                      # fits one compute unit's LDS
     p = fa.plan(1, 1, 128, 128, 64, fa.F32, False)
