@@ -61,10 +61,10 @@ constexpr int kSplitThreads = 256;
 constexpr int kMergeThreads = 256;
 
 inline int prefill_lds_bytes(int D) {
-  // Two K and two V tiles, padded, in 1 KB blocks.
+  // Three K and three V tiles, padded, in 1 KB blocks.
   const int kblk = (kPrefillBlockK * (D + 8) / 8 + 63) / 64;
   const int vblk = (kPrefillBlockK * (D + 32) / 8 + 63) / 64;
-  return 1024 * (2 * kblk + 2 * vblk);
+  return 1024 * (3 * kblk + 3 * vblk);
 }
 inline int f32_lds_bytes(int D) { return 2 * kF32BlockK * D * 4; }
 

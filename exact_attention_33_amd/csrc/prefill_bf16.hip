@@ -54,10 +54,11 @@
 //  * K and V move HBM -> LDS directly (global_load_lds_dwordx4: each lane's
 //    16 bytes land at M0 + 16 * lane, so one wave instruction fills a 1 KB
 //    block and the per-lane global address picks what goes where), with no
-//    staging registers.  Two K and two V buffers, each its own LDS array so
-//    the compiler can see that reading one never waits on a load into
-//    another.  Iteration t loads K(t+3) and V(t+1), spread over its first
-//    steps; the barrier that ends the iteration waits for them;
+//    staging registers.  Three K and three V buffers, each its own LDS array
+//    so the compiler can see that reading one never waits on a load into
+//    another.  Iteration t loads K(t+4) and V(t+2), spread over its phase A,
+//    and iteration t + 1 ends by waiting for them: every load has a whole
+//    iteration more than its issue to land;
 //  * LDS layouts are padded so that every operand read is one per-lane base
 //    register plus a compile-time offset and conflict-free on the 64 banks:
 //    K rows carry 16 bytes of padding, so the 16 rows that a 16-lane group
@@ -183,8 +184,10 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   static_assert(NW == 4 && QW == 64, "4 waves of 64 queries");
   __shared__ __attribute__((aligned(1024))) __bf16 Kb0[KBLK * 512];
   __shared__ __attribute__((aligned(1024))) __bf16 Kb1[KBLK * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Kb2[KBLK * 512];
   __shared__ __attribute__((aligned(1024))) __bf16 Vb0[VBLK * 512];
   __shared__ __attribute__((aligned(1024))) __bf16 Vb1[VBLK * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vb2[VBLK * 512];
 
   const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
   int qt = (int)(logical % n_qtiles);
@@ -259,11 +262,11 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
 #pragma unroll
     for (int i = 0; i < VPW; ++i) load_v_item(i, t, dst);
   };
-  // Load item j of iteration t: K(t+3) blocks into Kdst, then V(t+1) blocks
+  // Load item j of iteration t: K(t+4) blocks into Kdst, then V(t+2) blocks
   // into Vdst (tiles past the last read as zeros).
   auto load_item = [&](int j, int t, __bf16* Kdst, __bf16* Vdst) {
-    if (j < KPW) load_k_item(j, t + 3, Kdst);
-    else if (j < NITEM) load_v_item(j - KPW, t + 1, Vdst);
+    if (j < KPW) load_k_item(j, t + 4, Kdst);
+    else if (j < NITEM) load_v_item(j - KPW, t + 2, Vdst);
   };
 
   // ---- Q in registers: B operand of S^T = K Q^T ----
@@ -308,14 +311,12 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
     for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = f32x16{};
   f32x16 sacc[NKB][NQB];  // score tile: S(t+1), then S(t+2), during iteration t
   bf16x8 pacc[NQB][NP];   // weight tile: P(t), then P(t+1), during iteration t
-  float m_run[NQB], l_run[NQB], alpha[NQB];  // reference max (base 2), this lane's part of the sum
+  float m_run[NQB], l_run[NQB];  // reference max (base 2), this lane's part of the sum
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     m_run[qb] = -INFINITY;
     l_run[qb] = 0.f;
-    alpha[qb] = 1.f;
   }
-  bool rescale = false;  // wave-uniform: the accumulator owes a rescale by alpha
   // A scale of 0 would turn a masked -inf score into NaN (-inf * 0); a floor
   // of 1e-30 changes the weights of finite scores by less than 1e-20.
   const float c = fmaxf(p.scale * kLog2e, 1e-30f);
@@ -333,9 +334,11 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // exceeds it by more than 8), while the tile's row max is gathered:
   //   EM units (key block 0): max, weight, sum and bf16 weight of 2 scores;
   //   MX units (key block 1): max of 4 scores;
-  //   check (after all EM and MX units, scores still intact): if any row's
-  //     tile max exceeds m + 8 -- or m is still -inf -- the reference moves
-  //     and key block 0 is computed again against it (rare, not pipelined);
+  //   check (after all EM and MX units, scores still intact, and after the
+  //     P V products of the previous tile): if any row's tile max exceeds
+  //     m + 8 -- or m is still -inf -- the reference moves, l and the output
+  //     accumulator are rescaled and key block 0 is computed again against
+  //     the new reference (rare, not pipelined);
   //   EX units (key block 1): weight, sum and bf16 weight of 2 scores.
   // Each score is read from the accumulator once per use and consumed at
   // once, so no copy of the score tile stays live.
@@ -389,13 +392,13 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
         const float m_new = fmaxf(m_run[qb], mxc[qb]);
         // e^(m_old - m_new); nothing accumulated yet when m_old = -inf
         const float a = m_run[qb] == -INFINITY ? 0.f : fast_exp2(m_run[qb] - m_new);
-        alpha[qb] *= a;
         l_run[qb] *= a;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db][qb] *= a;
         m_run[qb] = m_new;
         m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
         ps[qb][0] = ps[qb][1] = 0.f;
       }
-      rescale = true;
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -468,9 +471,10 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   //      with the EX units;
   //   C: the S MFMAs of key block 1.
   // Operands are read PF fragments ahead; tile load item k goes at step
-  // 3k + 1.
+  // 3k + 1 (measured: spreading them over all steps gains nothing).
   constexpr int PF = 2;
   constexpr int NSA = 2 * NF, NSB = NQB * DK;  // steps of phases A and B (C = B)
+  constexpr int LSTEP = 3;  // tile load item k at step LSTEP k + 1 of phase A
   auto iteration = [&](int t, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst) {
     sm_begin();
     // K operands: a ring of PF + 2, so that a read overwrites a register two
@@ -499,13 +503,13 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
         constexpr int u0 = ((j - H) * NU_EM + H - 1) / H, u1 = ((j - H + 1) * NU_EM + H - 1) / H;
         static_for<u1 - u0>([&](auto uc) { unit_em(sacc, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
       }
-      if constexpr (j % 3 == 1 && j / 3 < NITEM) load_item(j / 3, t, Kdst, Vdst);
+      if constexpr (j % LSTEP == 1 && j / LSTEP < NITEM) load_item(j / LSTEP, t, Kdst, Vdst);
       // the first K operands of phase B, during the last steps of phase A
       if constexpr (j >= NSA - PF) kr[j - (NSA - PF)] = fetch_k(Ks, (j - (NSA - PF)) * NKB);
     });
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = (NSA + 1) / 3; k < NITEM; ++k) load_item(k, t, Kdst, Vdst);
+    for (int k = (NSA + LSTEP - 2) / LSTEP; k < NITEM; ++k) load_item(k, t, Kdst, Vdst);  // items past phase A
     pin_weights(0);
     sm_check(sacc);
     // phases B and C: S fragments (kb, nb) in order nb-major, kb, query block
@@ -529,7 +533,7 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
     pin_weights(1);
     sm_end();
   };
-  // Iteration t: K(t+2) in Ks, V(t) in Vs; loads K(t+3) into Kdst and V(t+1)
+  // Iteration t: K(t+2) in Ks, V(t) in Vs; loads K(t+4) into Kdst and V(t+2)
   // into Vdst.  Every wave runs the whole pipeline every iteration: a tile
   // that none of a wave's queries sees is fully masked and adds weights of
   // exactly 0 (at most two iterations per workgroup and the diagonal tiles of
@@ -539,41 +543,39 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
     mfma_guard();  // the last iteration's final MFMAs wrote the scores
     if (need_mask(t + 1)) apply_mask(t + 1, sacc);
     iteration(t, Ks, Vs, Kdst, Vdst);
-    // the iteration's P V products used the old reference: rescale now
-    if (rescale) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha[qb];
-        alpha[qb] = 1.f;
-      }
-      rescale = false;
-    }
-    __syncthreads();
+    // This wave's loads of the previous iteration (K(t+3), V(t+1)) are done
+    // (loads complete in order: only this iteration's NITEM may be pending),
+    // and so are its LDS reads; the barrier then makes every wave's loads
+    // visible and frees the buffers read in this iteration for the next
+    // iteration's loads.
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NITEM) : "memory");
   };
 
-  // Prologue: K(0), K(1), V(0) in LDS; S(0) and its softmax, S(1); K(2) in.
+  // Prologue: K(0) .. K(2), V(0), V(1) in LDS; S(0) and its softmax, S(1);
+  // K(3) loaded over K(0) once every wave has read K(0).
   if (n_tiles > 0) {
     load_k(0, Kb0);
+    load_k(1, Kb1);
+    load_k(2, Kb2);
     load_v(0, Vb0);
-    if (n_tiles > 1) load_k(1, Kb1);
+    load_v(1, Vb1);
   }
   __syncthreads();
   compute_s(Kb0, sacc);
-  __syncthreads();  // every wave is done with K(0) before K(2) goes over it
-  if (n_tiles > 2) load_k(2, Kb0);
+  __syncthreads();  // every wave is done with K(0) before K(3) goes over it
+  if (n_tiles > 0) load_k(3, Kb0);
   softmax_all(0, sacc);
   compute_s(Kb1, sacc);
-  // nothing accumulated yet: a reference move only resets the bookkeeping
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) alpha[qb] = 1.f;
-  rescale = false;
-  __syncthreads();
+  // K(1) is read by every wave before iteration 0 loads K(4) over it; K(3)
+  // may still be in flight (iteration 0 waits for it)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  for (int t = 0; t < n_tiles; t += 2) {
-    step_tile(t, Kb0, Vb0, Kb1, Vb1);
+  for (int t = 0; t < n_tiles; t += 3) {
+    step_tile(t, Kb2, Vb0, Kb1, Vb2);
     if (t + 1 >= n_tiles) break;
-    step_tile(t + 1, Kb1, Vb1, Kb0, Vb0);
+    step_tile(t + 1, Kb0, Vb1, Kb2, Vb0);
+    if (t + 2 >= n_tiles) break;
+    step_tile(t + 2, Kb1, Vb2, Kb0, Vb1);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
