@@ -51,10 +51,10 @@
 //    ds_read_b64_tr_b16 transposing reads per fragment.  The row sum adds the
 //    float32 weights before rounding (a sum of bf16-rounded weights would
 //    carry their 2^-9 relative error into LSE for rows with few keys);
-//  * K and V move HBM -> LDS directly (global_load_lds_dwordx4: each lane's
-//    16 bytes land at M0 + 16 * lane, so one wave instruction fills a 1 KB
-//    block and the per-lane global address picks what goes where), with no
-//    staging registers.  Three K and three V buffers, each its own LDS array
+//  * K and V move HBM -> LDS directly (buffer loads into LDS, 16 bytes per
+//    lane: each lane's bytes land at M0 + 16 * lane, so one wave instruction
+//    fills a 1 KB block and the per-lane offset picks what goes where), with
+//    no staging registers.  Three K and three V buffers, each its own LDS array
 //    so the compiler can see that reading one never waits on a load into
 //    another.  Iteration t loads K(t+4) and V(t+2), spread over its phase A,
 //    and iteration t + 1 ends by waiting for them: every load has a whole
