@@ -61,10 +61,12 @@ constexpr int kSplitThreads = 256;
 constexpr int kMergeThreads = 256;
 
 inline int prefill_lds_bytes(int D) {
-  // Three K and three V tiles, padded, in 1 KB blocks.
+  // Three K and three V tiles, padded, in 1 KB blocks, rounded up to a whole
+  // number of blocks per wave.
+  const int waves = kPrefillThreads / 64;
   const int kblk = (kPrefillBlockK * (D + 8) / 8 + 63) / 64;
   const int vblk = (kPrefillBlockK * (D + 32) / 8 + 63) / 64;
-  return 1024 * (3 * kblk + 3 * vblk);
+  return 1024 * 3 * ((kblk + waves - 1) / waves * waves + (vblk + waves - 1) / waves * waves);
 }
 inline int f32_lds_bytes(int D) { return 2 * kF32BlockK * D * 4; }
 

@@ -90,6 +90,12 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
   plan->path = path;
   switch (path) {
     case FA_PATH_PREFILL:
+      // The prefill kernel addresses one (batch, head) of K or V with 32-bit
+      // byte offsets.
+      if ((int64_t)s.M * s.D * 2 > INT32_MAX) {
+        *why = "FA_PATH_PREFILL needs M * D * 2 < 2^31 (K/V bytes per batch and head)";
+        return FA_ERR_UNSUPPORTED;
+      }
       plan->block_q = kPrefillBlockQ;
       plan->block_k = kPrefillBlockK;
       plan->threads = kPrefillThreads;

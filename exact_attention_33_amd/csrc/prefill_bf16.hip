@@ -181,13 +181,16 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   constexpr int KCH = KROW / 8, VCH = VROW / 8;        // 16-byte slots per row
   constexpr int KBLK = (BK * KCH + 63) / 64;           // 1 KB blocks per K tile
   constexpr int VBLK = (BK * VCH + 63) / 64;           // 1 KB blocks per V tile
+  constexpr int KPW = (KBLK + NW - 1) / NW, VPW = (VBLK + NW - 1) / NW;  // blocks per wave
   static_assert(NW == 4 && QW == 64, "4 waves of 64 queries");
-  __shared__ __attribute__((aligned(1024))) __bf16 Kb0[KBLK * 512];
-  __shared__ __attribute__((aligned(1024))) __bf16 Kb1[KBLK * 512];
-  __shared__ __attribute__((aligned(1024))) __bf16 Kb2[KBLK * 512];
-  __shared__ __attribute__((aligned(1024))) __bf16 Vb0[VBLK * 512];
-  __shared__ __attribute__((aligned(1024))) __bf16 Vb1[VBLK * 512];
-  __shared__ __attribute__((aligned(1024))) __bf16 Vb2[VBLK * 512];
+  // Every wave loads the same number of blocks; the blocks past a tile's last
+  // (KBLK .. NW * KPW) receive bytes that are never read.
+  __shared__ __attribute__((aligned(1024))) __bf16 Kb0[NW * KPW * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Kb1[NW * KPW * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Kb2[NW * KPW * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vb0[NW * VPW * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vb1[NW * VPW * 512];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vb2[NW * VPW * 512];
 
   const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
   int qt = (int)(logical % n_qtiles);
@@ -215,45 +218,47 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // ---- tile loads ----
   // Slot s of a padded tile holds row s / CH, chunk s % CH; slots on the
   // padding (chunk >= CPR) load chunk 0 of that row (valid data, never read).
-  // Wave ws loads blocks ws, ws + NW, ... of each tile; a wave with fewer
-  // blocks than the others loads the tile's last block again (the same bytes
-  // to the same place), so every wave issues the same loads without a branch.
-  // The per-lane byte offsets of a wave's slots within a tile (< 64 KB) are
-  // fixed, so they are computed once and kept two to a register.  Loads are
-  // buffer loads into LDS against a descriptor that ends at kv_len: rows past
-  // it (last tile) and whole tiles past it read as zeros -- finite data whose
-  // weights are 0 -- with no clamping arithmetic.  (Buffer rather than global
-  // loads also keep the compiler's LDS wait counting exact: it treats a global
-  // load into LDS like a flat access and then waits for every LDS read.)
-  constexpr int KPW = (KBLK + NW - 1) / NW, VPW = (VBLK + NW - 1) / NW;
+  // Wave ws loads blocks ws, ws + NW, ... of each tile.  The per-lane byte
+  // offsets of a wave's slots within a tile (< 64 KB) are fixed, so they are
+  // computed once and kept two to a register.  Loads are buffer loads into
+  // LDS against one descriptor per (batch, head) that ends at kv_len: rows
+  // past it (last tile) and whole tiles past it read as zeros -- finite data
+  // whose weights are 0 -- with no clamping arithmetic, and the descriptors
+  // stay in 8 scalar registers for the whole kernel.  (Buffer rather than
+  // global loads also keep the compiler's LDS wait counting exact: it treats
+  // a global load into LDS like a flat access and then waits for every LDS
+  // read.)
   constexpr int NITEM = KPW + VPW;  // load items per wave per iteration
   constexpr int ROWB = D * 2;       // bytes per global row
-  static_assert(BK * ROWB <= 65536, "tile offsets fit 16 bits");
+  static_assert((NW * KPW * 64 / KCH + 1) * ROWB <= 65536 && (NW * VPW * 64 / VCH + 1) * ROWB <= 65536,
+                "slot offsets fit 16 bits");
   auto slot_off = [&](int blk, int ch) -> uint32_t {
     const int slot = blk * 64 + lane, r = slot / ch, cc = slot % ch;
     return (uint32_t)(r * ROWB + (cc < CPR ? cc * 16 : 0));
   };
-  auto kblock = [&](int i) { return min(ws + i * NW, KBLK - 1); };
-  auto vblock = [&](int i) { return min(ws + i * NW, VBLK - 1); };
   uint32_t koff[(KPW + 1) / 2], voff[(VPW + 1) / 2];
 #pragma unroll
   for (int i = 0; i < KPW; i += 2)
-    koff[i / 2] = slot_off(kblock(i), KCH) | (i + 1 < KPW ? slot_off(kblock(i + 1), KCH) << 16 : 0u);
+    koff[i / 2] = slot_off(ws + i * NW, KCH) | (i + 1 < KPW ? slot_off(ws + (i + 1) * NW, KCH) << 16 : 0u);
 #pragma unroll
   for (int i = 0; i < VPW; i += 2)
-    voff[i / 2] = slot_off(vblock(i), VCH) | (i + 1 < VPW ? slot_off(vblock(i + 1), VCH) << 16 : 0u);
-  // One block: slots of block blk of tile t of src into block blk of dst,
-  // against a descriptor that ends at kv_len.  (readfirstlane: the clamp has
-  // no scalar instruction, and a descriptor the compiler cannot prove uniform
-  // costs a loop around every load.)
-  auto load_block = [&](const __bf16* src, int t, __bf16* dst, uint32_t packed, int i, int blk) {
+    voff[i / 2] = slot_off(ws + i * NW, VCH) | (i + 1 < VPW ? slot_off(ws + (i + 1) * NW, VCH) << 16 : 0u);
+  // K and V bytes this (batch, head) may read; the planner keeps M * D * 2
+  // below 2^31, so every offset below fits 32 bits.
+  const int nrec = kvl * ROWB;
+  // Block i of this wave: its slots of tile t of src into dst.  The wave's
+  // block offset goes through an empty asm so that the compiler forms each
+  // LDS address next to its load instead of keeping all of them (three
+  // buffers x NITEM blocks) in scalar registers.
+  auto load_block = [&](const __bf16* src, int t, __bf16* dst, uint32_t packed, int i) {
     asm volatile("" : "+v"(packed));  // keep the unpacking next to its use
-    const uint32_t u = i % 2 ? packed >> 16 : packed & 0xFFFFu;
-    const int nrec = __builtin_amdgcn_readfirstlane(max(0, min(kvl - t * BK, BK)) * ROWB);
-    buffer_load_lds16(src + (size_t)t * BK * D, nrec, u, (lds_ptr)(dst + blk * 512));
+    const uint32_t u = (i % 2 ? packed >> 16 : packed & 0xFFFFu) + (uint32_t)t * (BK * ROWB);
+    int wofs = ws * 512;
+    asm volatile("" : "+s"(wofs));
+    buffer_load_lds16(src, nrec, u, (lds_ptr)(dst + wofs + i * NW * 512));
   };
-  auto load_k_item = [&](int i, int t, __bf16* dst) { load_block(Kg, t, dst, koff[i / 2], i, kblock(i)); };
-  auto load_v_item = [&](int i, int t, __bf16* dst) { load_block(Vg, t, dst, voff[i / 2], i, vblock(i)); };
+  auto load_k_item = [&](int i, int t, __bf16* dst) { load_block(Kg, t, dst, koff[i / 2], i); };
+  auto load_v_item = [&](int i, int t, __bf16* dst) { load_block(Vg, t, dst, voff[i / 2], i); };
   auto load_k = [&](int t, __bf16* dst) {
 #pragma unroll
     for (int i = 0; i < KPW; ++i) load_k_item(i, t, dst);
@@ -421,18 +426,22 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
       asm volatile("" ::"v"(ps[qb][0]), "v"(ps[qb][1]), "v"(mxp[qb][0]), "v"(mxp[qb][1]));
     }
   };
+  // Scores of keys past a row's last visible key become -inf.  The select is
+  // a sign mask and a bit insert, not a compare: a compare per score writes a
+  // scalar register pair, and the compiler would keep dozens of them live.
   auto apply_mask = [&](int t, f32x16 (&s)[NKB][NQB]) {
-    const int k0 = t * BK;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qrow = qw0 + 32 * qb + ql;
       const int lim = CAUSAL ? min(kvl - 1, qrow + off) : kvl - 1;  // last visible key
+      const int base = lim - (t * BK + 4 * hl);  // >= 0 iff key k0 + 4 hl is visible
 #pragma unroll
       for (int nb = 0; nb < NKB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + nb * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
-          if (key > lim) s[nb][qb][r] = -INFINITY;
+          const uint32_t hide = (uint32_t)((base - (nb * 32 + 8 * (r / 4) + (r % 4))) >> 31);
+          const uint32_t v = __float_as_uint(s[nb][qb][r]);
+          s[nb][qb][r] = __uint_as_float((hide & 0xFF800000u) | (~hide & v));
         }
     }
   };

@@ -66,7 +66,8 @@ typedef struct { int32_t B, H, N, M, D; } fa_shape;
 
 typedef enum {
   FA_PATH_AUTO = 0,     /* planner's choice                                      */
-  FA_PATH_PREFILL = 1,  /* fused tiled kernel, bf16 MFMA (bf16 only)             */
+  FA_PATH_PREFILL = 1,  /* fused tiled kernel, bf16 MFMA (bf16 only; K/V bytes
+                           per batch and head, M * D * 2, below 2^31)            */
   FA_PATH_SPLITKV = 2,  /* split-KV partial kernel + log-sum-exp merge (bf16, N=1) */
   FA_PATH_F32 = 3       /* float32 inputs/outputs, float64 internal arithmetic   */
 } fa_path;

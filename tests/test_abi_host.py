@@ -60,6 +60,8 @@ def test_planner_paths():
     assert p["workspace_bytes"] >= 32 * 32 * p["splits"] * (128 + 1) * 4
     # forcing paths
     assert fa.plan(1, 2, 1, 500, 64, fa.BF16, True, path=fa.PATH_PREFILL)["path_name"] == "prefill"
+    # the largest K/V that prefill addresses: M * D * 2 = 2^31 - 256 bytes
+    assert fa.plan(1, 1, 16, (1 << 23) - 1, 128, fa.BF16, False)["path_name"] == "prefill"
     p = fa.plan(1, 2, 1, 500, 64, fa.BF16, False, path=fa.PATH_SPLITKV, split_keys=64)
     assert p["splits"] == 8 and p["block_k"] == 64
     # empty problems plan fine and need nothing
@@ -72,6 +74,8 @@ def test_planner_paths():
     ((1, 1, 16, 16, 64, 7, False), "FA_ERR_UNSUPPORTED"),
     ((-1, 1, 16, 16, 64, fa.BF16, False), "FA_ERR_SHAPE"),
     ((1, 1, 16, -16, 64, fa.BF16, False), "FA_ERR_SHAPE"),
+    # prefill addresses one (batch, head) of K/V with 32-bit byte offsets
+    ((1, 1, 16, 1 << 23, 128, fa.BF16, False), "FA_ERR_UNSUPPORTED"),
 ])
 def test_planner_rejects(args, status):
     with pytest.raises(fa.FaError) as ei:
