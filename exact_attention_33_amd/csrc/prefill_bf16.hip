@@ -512,13 +512,10 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
         constexpr int u0 = ((j - H) * NU_EM + H - 1) / H, u1 = ((j - H + 1) * NU_EM + H - 1) / H;
         static_for<u1 - u0>([&](auto uc) { unit_em(sacc, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
       }
-      if constexpr (j % LSTEP == 1 && j / LSTEP < NITEM) load_item(j / LSTEP, t, Kdst, Vdst);
       // the first K operands of phase B, during the last steps of phase A
       if constexpr (j >= NSA - PF) kr[j - (NSA - PF)] = fetch_k(Ks, (j - (NSA - PF)) * NKB);
     });
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = (NSA + LSTEP - 2) / LSTEP; k < NITEM; ++k) load_item(k, t, Kdst, Vdst);  // items past phase A
     pin_weights(0);
     sm_check(sacc);
     // phases B and C: S fragments (kb, nb) in order nb-major, kb, query block
@@ -532,6 +529,14 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
       if constexpr (qb == 0 && f + PF < NF) {
         constexpr int f2 = f + PF;
         kr[f2 % KR] = fetch_k(Ks, (f2 % DK) * NKB + f2 / DK);
+      }
+      // tile loads in phase C, which carries no VALU work: item i at step
+      // NSB + i NSB / NITEM
+      if constexpr (j >= NSB) {
+        static_for<NITEM>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (NSB + i * NSB / NITEM == j) load_item(i, t, Kdst, Vdst);
+        });
       }
       if constexpr (j < NSB) {
         constexpr int u0 = (j * NU_EX + NSB - 1) / NSB, u1 = ((j + 1) * NU_EX + NSB - 1) / NSB;
