@@ -23,28 +23,30 @@
 //    MI355X, bounds a 32-query design);
 //  * software pipeline inside the wave: iteration t issues the MFMAs of
 //    S(t+2) = K(t+2) Q^T and O += P(t) V(t) and, between them, the softmax of
-//    tile t+1 (mask, row max, exponentials, row sum) on the VALU.  The three
+//    tile t+1 (mask, exponentials, row sum) on the VALU.  The three
 //    have no data dependence, and one wave keeps its matrix pipe nearly full
 //    while it issues about four VALU instructions per MFMA (measured: 64
 //    MFMAs with that VALU mix and their LDS operand reads take about 2,600
 //    cycles against 2,048 for the MFMAs alone).  Scheduling barriers fix the
 //    interleave: step j of an iteration holds one MFMA, the LDS reads of the
-//    operands two fragments ahead, a slice of the softmax and at most one
-//    tile load;
+//    operands two fragments ahead, and a slice of the softmax or a tile
+//    load (the loads go with the S MFMAs of key block 1, which carry no
+//    softmax work);
 //  * the score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: Q is the B operand, K comes from LDS.  Lane
 //    (h, c) of a wave (h = lane / 32, c = lane % 32) then holds, per 32-query
 //    block, 16 scores of query c per 32-key block, at keys 8*(r/4) + 4*h + r%4,
-//    so row max and row sum are in-lane plus one swap between the half-waves
-//    (v_permlane32_swap);
+//    so a row's sum (and, on the rare path, its max) is in-lane plus one swap
+//    between the half-waves (v_permlane32_swap);
 //  * scores are kept in base 2: t = s * scale * log2(e), weights 2^(t - m) on
 //    v_exp_f32; the scale is applied in float32 to the float32 score;
-//  * the reference max m moves only when a row's max exceeds it by more than
-//    8 (or on the first visible key): the pages subtract the max only to keep
-//    the exponentials finite, and any reference at or above (row max - 8)
-//    keeps every weight <= 256.  When it moves, l is rescaled at once and the
-//    output accumulator after the iteration's P V products (which still use
-//    the old reference), so the rescale never waits on the matrix pipe;
+//  * no row max on the common path: the pages subtract the max only to keep
+//    the exponentials finite, and any reference m that keeps every weight at
+//    most 2^20 gives the same l, O and L.  A weight above that shows in the
+//    lane's sum of the tile's weights; that, or a row's first visible key,
+//    sends the wave to a rare path that moves m up to the row max of the key
+//    block and rescales l and the output accumulator (after the iteration's
+//    P V products, which still use the old reference);
 //  * the output is accumulated transposed, O^T += V^T P^T, with the same MFMA:
 //    the weights convert to bf16 straight into the B operand (no LDS round
 //    trip) and V^T comes from V's natural [key][d] layout in LDS through two
@@ -85,7 +87,6 @@ namespace fa {
 namespace {
 
 constexpr int kNumXcd = 8;
-constexpr float kLazyRescale = 8.0f;  // log2 of the largest weight allowed
 // Word 3 of a raw buffer descriptor on gfx9-family GPUs (untyped 32-bit
 // data, no swizzle); out-of-range reads return zeros.
 constexpr int kBufferFlags = 0x00020000;
@@ -140,6 +141,14 @@ __device__ __forceinline__ void mfma_s_first(f32x16& d, const bf16x8& a, const b
 __device__ __forceinline__ void mfma_s_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
+// max of three floats as one v_max3_f32 (fmaxf would first quiet each
+// operand with an extra instruction; the scores are never signalling NaNs).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 __device__ __forceinline__ void mfma_guard() { asm volatile("s_nop 7\n\ts_nop 7"); }
 
 // Logical work item of workgroup `wg` when workgroups are dealt round-robin
@@ -334,87 +343,128 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   };
 
   // ---- softmax of one tile, in small units that the pipeline spreads out ----
-  // The weights of a tile are computed speculatively against the current
-  // reference m (the common case: the reference moves only when a row max
-  // exceeds it by more than 8), while the tile's row max is gathered:
-  //   EM units (key block 0): max, weight, sum and bf16 weight of 2 scores;
-  //   MX units (key block 1): max of 4 scores;
-  //   check (after all EM and MX units, scores still intact, and after the
-  //     P V products of the previous tile): if any row's tile max exceeds
-  //     m + 8 -- or m is still -inf -- the reference moves, l and the output
-  //     accumulator are rescaled and key block 0 is computed again against
-  //     the new reference (rare, not pipelined);
-  //   EX units (key block 1): weight, sum and bf16 weight of 2 scores.
-  // Each score is read from the accumulator once per use and consumed at
-  // once, so no copy of the score tile stays live.
-  constexpr int NU_EM = NQB * 8, NU_MX = NQB * 4, NU_EX = NQB * 8;
-  float mxp[NQB][2], m_use[NQB], ps[NQB][2];
+  // The weights of a tile are formed against the current reference m with no
+  // row max at all: the pages subtract the max only to keep the exponentials
+  // finite, and any reference that keeps every weight at most 2^20 (sums of
+  // a million keys stay far inside float32) gives the same l, O and L.  A
+  // weight above that shows in the lane's sum of the tile's weights, so two
+  // cheap checks replace the max:
+  //   EM units (key block 0): weight, sum and bf16 weight of 2 scores;
+  //   check 1 (after the EM units and the P V products of the previous tile,
+  //     block-0 scores intact): a lane's block-0 sum above 2^20, or a row
+  //     with no reference yet (m = -inf) that sees a key of block 0, moves
+  //     the reference up to block 0's row max (rare): l and the output
+  //     accumulator are rescaled and key block 0 is computed again;
+  //   EX units (key block 1): as EM;
+  //   check 2 (after the EX units, block-1 scores intact): the same for the
+  //     whole tile's sum and block 1 (rarer still): l, the output
+  //     accumulator and block 0's weights and sum are rescaled and key block
+  //     1 is computed again.
+  // Once a row has a reference, its l is at least 1 (the key that set it
+  // weighs exactly 1), so weights that underflow are negligible.  Each score
+  // is read from the accumulator once and consumed at once.
+  constexpr int NU_EM = NQB * 8, NU_EX = NQB * 8;
+  constexpr float kSumLimit = 1048576.0f;  // 2^20
+  float m_use[NQB], ps0[NQB][2], ps1[NQB][2];  // reference in use; block 0 and block 1 sums
+  bool vis[NKB][NQB];  // the row sees a key of key block nb
   auto sm_begin = [&]() {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      mxp[qb][0] = mxp[qb][1] = -INFINITY;
-      ps[qb][0] = ps[qb][1] = 0.f;
+      ps0[qb][0] = ps0[qb][1] = ps1[qb][0] = ps1[qb][1] = 0.f;
       m_use[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
     }
   };
   // weights of 2 scores (pair `pair` of 16-key half t2 of key block nb)
-  auto exp_pair = [&](f32x16 (&s)[NKB][NQB], int nb, int qb, int t2, int pair, bool with_max) {
+  auto exp_pair = [&](f32x16 (&s)[NKB][NQB], int nb, int qb, int t2, int pair) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int e = 2 * pair + h, r = (2 * t2 + e / 4) * 4 + (e % 4);
-      const float v = s[nb][qb][r];
-      if (with_max) mxp[qb][h] = fmaxf(mxp[qb][h], v);
-      const float pv = fast_exp2(fmaf(v, c, -m_use[qb]));
-      ps[qb][h] += pv;
+      const float pv = fast_exp2(fmaf(s[nb][qb][r], c, -m_use[qb]));
+      (nb == 0 ? ps0 : ps1)[qb][h] += pv;
       pacc[qb][nb * 2 + t2][e] = (__bf16)pv;
     }
   };
+  // EM unit u: t2-major, so that the units of the first 16-key half come
+  // first (the P V products release that half of the weight tile first)
   auto unit_em = [&](f32x16 (&s)[NKB][NQB], auto uc) {
-    constexpr int u = decltype(uc)::value, qb = u / 8, t2 = (u / 4) % 2, pair = u % 4;
-    exp_pair(s, 0, qb, t2, pair, true);
-  };
-  auto unit_mx = [&](f32x16 (&s)[NKB][NQB], auto uc) {
-    constexpr int u = decltype(uc)::value, qb = u / 4, r0 = (u % 4) * 4;
-    float& mref = mxp[qb][u % 2];
-    mref = fmaxf(fmaxf(mref, s[1][qb][r0]), s[1][qb][r0 + 1]);
-    mref = fmaxf(fmaxf(mref, s[1][qb][r0 + 2]), s[1][qb][r0 + 3]);
+    constexpr int u = decltype(uc)::value, t2 = u / 8, qb = (u / 4) % 2, pair = u % 4;
+    exp_pair(s, 0, qb, t2, pair);
   };
   auto unit_ex = [&](f32x16 (&s)[NKB][NQB], auto uc) {
     constexpr int u = decltype(uc)::value, qb = u / 8, t2 = (u / 4) % 2, pair = u % 4;
-    exp_pair(s, 1, qb, t2, pair, false);
+    exp_pair(s, 1, qb, t2, pair);
   };
-  auto sm_check = [&](f32x16 (&s)[NKB][NQB]) {
-    bool over = false;
-    float mxc[NQB];
+  // Move row qb's reference to mx (its new row max, base 2): returns the
+  // factor e^(m_old - m_new) for everything accumulated so far.
+  auto move_ref = [&](int qb, float mx) -> float {
+    const float m_new = fmaxf(m_run[qb], mx);
+    const float a = m_run[qb] == -INFINITY ? 0.f : fast_exp2(m_run[qb] - m_new);  // nothing accumulated yet
+    l_run[qb] *= a;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      mxc[qb] = swap_halves_max(fmaxf(mxp[qb][0], mxp[qb][1])) * c;  // -inf stays -inf (c > 0)
-      over |= mxc[qb] > m_run[qb] + kLazyRescale;  // also true when m is -inf and a score is not
+    for (int db = 0; db < DB; ++db) {
+      // read inside the branch, in place: no copy of the accumulator
+      // outside it
+      asm volatile("" : "+a"(oacc[db][qb]));
+      oacc[db][qb] *= a;
     }
+    m_run[qb] = m_new;
+    m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
+    return a;
+  };
+  auto sm_check1 = [&](f32x16 (&s)[NKB][NQB]) __attribute__((always_inline)) {
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+      over |= (ps0[qb][0] + ps0[qb][1] > kSumLimit) | ((m_run[qb] == -INFINITY) & vis[0][qb]);
     if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform, rare
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        const float m_new = fmaxf(m_run[qb], mxc[qb]);
-        // e^(m_old - m_new); nothing accumulated yet when m_old = -inf
-        const float a = m_run[qb] == -INFINITY ? 0.f : fast_exp2(m_run[qb] - m_new);
-        l_run[qb] *= a;
+        float mx = -INFINITY;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db][qb] *= a;
-        m_run[qb] = m_new;
-        m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
-        ps[qb][0] = ps[qb][1] = 0.f;
+        for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[0][qb][r], s[0][qb][r + 1]);
+        move_ref(qb, swap_halves_max(mx) * c);  // -inf stays -inf (c > 0)
+        ps0[qb][0] = ps0[qb][1] = 0.f;
       }
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-          for (int pair = 0; pair < 4; ++pair) exp_pair(s, 0, qb, t2, pair, false);
+          for (int pair = 0; pair < 4; ++pair) exp_pair(s, 0, qb, t2, pair);
+    }
+  };
+  auto sm_check2 = [&](f32x16 (&s)[NKB][NQB]) __attribute__((always_inline)) {
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+      over |= (ps0[qb][0] + ps0[qb][1] + ps1[qb][0] + ps1[qb][1] > kSumLimit) |
+              ((m_run[qb] == -INFINITY) & vis[1][qb]);
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform, rarer still
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[1][qb][r], s[1][qb][r + 1]);
+        const float a = move_ref(qb, swap_halves_max(mx) * c);
+        ps0[qb][0] *= a;
+        ps0[qb][1] *= a;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pacc[qb][t2][e] = (__bf16)((float)pacc[qb][t2][e] * a);
+        ps1[qb][0] = ps1[qb][1] = 0.f;
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int pair = 0; pair < 4; ++pair) exp_pair(s, 1, qb, t2, pair);
     }
   };
   auto sm_end = [&]() {
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) l_run[qb] += ps[qb][0] + ps[qb][1];
+    for (int qb = 0; qb < NQB; ++qb) l_run[qb] += (ps0[qb][0] + ps0[qb][1]) + (ps1[qb][0] + ps1[qb][1]);
   };
   // Results computed so far must exist here: an empty statement that reads
   // them keeps the compiler from sinking their arithmetic past the branch
@@ -423,7 +473,7 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       asm volatile("" ::"v"(pacc[qb][nb * 2]), "v"(pacc[qb][nb * 2 + 1]));
-      asm volatile("" ::"v"(ps[qb][0]), "v"(ps[qb][1]), "v"(mxp[qb][0]), "v"(mxp[qb][1]));
+      asm volatile("" ::"v"(ps0[qb][0]), "v"(ps0[qb][1]), "v"(ps1[qb][0]), "v"(ps1[qb][1]));
     }
   };
   // Scores of keys past a row's last visible key become -inf.  The select is
@@ -434,6 +484,8 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
     for (int qb = 0; qb < NQB; ++qb) {
       const int qrow = qw0 + 32 * qb + ql;
       const int lim = CAUSAL ? min(kvl - 1, qrow + off) : kvl - 1;  // last visible key
+#pragma unroll
+      for (int nb = 0; nb < NKB; ++nb) vis[nb][qb] = lim >= t * BK + 32 * nb;
       const int base = lim - (t * BK + 4 * hl);  // >= 0 iff key k0 + 4 hl is visible
 #pragma unroll
       for (int nb = 0; nb < NKB; ++nb)
@@ -448,12 +500,14 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // Whole softmax of tile t (prologue only).
   auto softmax_all = [&](int t, f32x16 (&s)[NKB][NQB]) {
     mfma_guard();  // compute_s just wrote the scores
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
     if (need_mask(t)) apply_mask(t, s);
     sm_begin();
     static_for<NU_EM>([&](auto uc) { unit_em(s, uc); });
-    static_for<NU_MX>([&](auto uc) { unit_mx(s, uc); });
-    sm_check(s);
+    sm_check1(s);
     static_for<NU_EX>([&](auto uc) { unit_ex(s, uc); });
+    sm_check2(s);
     sm_end();
   };
   // S^T = K Q^T for one tile, not interleaved (prologue only).
@@ -474,11 +528,11 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // Work of iteration t: O += P(t) V(t), the softmax of S(t+1) into P(t+1),
   // S(t+2) = K(t+2) Q^T.  One score and one weight tile suffice because the
   // steps run in three phases, one MFMA per step:
-  //   A: the P V MFMAs (fragment j / 2, query block j % 2), with the MX
-  //      units and then the EM units; then the check;
+  //   A: the P V MFMAs (fragment j / 2, query block j % 2), with the EM
+  //      units; then check 1;
   //   B: the S MFMAs of key block 0 -- whose scores have been consumed --
-  //      with the EX units;
-  //   C: the S MFMAs of key block 1.
+  //      with the EX units; then check 2;
+  //   C: the S MFMAs of key block 1, with the tile loads.
   // Operands are read PF fragments ahead; tile load item k goes at step
   // 3k + 1 (measured: spreading them over all steps gains nothing).
   constexpr int PF = 2;
@@ -501,27 +555,35 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
       oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % (PF + 1)], pacc[qb][nb * 2 + t2],
                                                             oacc[db][qb], 0, 0, 0);
       if constexpr (qb == 0 && i + PF < NF) vr[(i + PF) % (PF + 1)] = fetch_v(Vs, i + PF);
-      // MX units over the first half of the steps, EM units over the second:
-      // the MFMAs of the first half read P(t)'s key block 0, which the EM
-      // units overwrite with P(t+1)'s
-      constexpr int H = NSA / 2;
-      if constexpr (j < H) {
-        constexpr int u0 = (j * NU_MX + H - 1) / H, u1 = ((j + 1) * NU_MX + H - 1) / H;
-        static_for<u1 - u0>([&](auto uc) { unit_mx(sacc, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
-      } else {
-        constexpr int u0 = ((j - H) * NU_EM + H - 1) / H, u1 = ((j - H + 1) * NU_EM + H - 1) / H;
-        static_for<u1 - u0>([&](auto uc) { unit_em(sacc, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
+      // EM units over the last three quarters of the steps: an EM unit of
+      // 16-key half t2 overwrites weight fragment t2 of P(t), which the P V
+      // MFMAs of fragment t2 (steps 2 DB t2 .. + 2 DB) read first
+      constexpr int Q1 = NSA / 4;
+      if constexpr (j >= Q1) {
+        constexpr int W = NSA - Q1;
+        constexpr int u0 = ((j - Q1) * NU_EM + W - 1) / W, u1 = ((j - Q1 + 1) * NU_EM + W - 1) / W;
+        static_for<u1 - u0>([&](auto uc) {
+          constexpr int u = u0 + decltype(uc)::value;
+          static_assert(j >= 2 * DB * (u / (NU_EM / 2) + 1), "EM unit after the P V MFMAs of its fragment");
+          unit_em(sacc, std::integral_constant<int, u>{});
+        });
       }
       // the first K operands of phase B, during the last steps of phase A
       if constexpr (j >= NSA - PF) kr[j - (NSA - PF)] = fetch_k(Ks, (j - (NSA - PF)) * NKB);
     });
     __builtin_amdgcn_sched_barrier(0);
     pin_weights(0);
-    sm_check(sacc);
+    sm_check1(sacc);
     // phases B and C: S fragments (kb, nb) in order nb-major, kb, query block
     static_for<2 * NSB>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (j == NSB) {
+        // check 2, before phase C overwrites key block 1's scores
+        pin_weights(1);
+        sm_check2(sacc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       constexpr int f = j / NQB, qb = j % NQB;     // f-th S fragment of this iteration
       constexpr int nb = f / DK, kb = f % DK;
       if constexpr (kb == 0) mfma_s_first(sacc[nb][qb], kr[f % KR], qf[qb][kb]);
@@ -555,6 +617,8 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // assignment fixed).
   auto step_tile = [&](int t, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst) {
     mfma_guard();  // the last iteration's final MFMAs wrote the scores
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
     if (need_mask(t + 1)) apply_mask(t + 1, sacc);
     iteration(t, Ks, Vs, Kdst, Vdst);
     // This wave's loads of the previous iteration (K(t+3), V(t+1)) are done
