@@ -109,6 +109,25 @@ def test_prefill_large_scores_no_overflow():
     full_check(q, k, v, default_scale(128), True, None, "bf16", "prefill x16")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_reference_moves_in_later_blocks(D, causal):
+    """Scores that jump by ~29 (base 2) at later 32-key blocks -- in key block
+    1 of tile 1, key block 0 of tile 3 and key block 1 of tile 4 -- push the
+    weights of rows that already have a reference far above 2^20, so the
+    reference has to move in the middle of a row (both rare paths)."""
+    q, k, v = make(33, 1, 2, 384, 384, D, "bf16")
+    scale = default_scale(D)
+    lam = 20.0 / scale                      # q_0 = lam, k_j0 = b_j: score + 20 b_j (natural)
+    b = torch.zeros(384)
+    b[96:128] = 1.0                         # tile 1, key block 1
+    b[192:224] = 2.0                        # tile 3, key block 0
+    b[288:320] = 3.0                        # tile 4, key block 1
+    q[..., 0] = torch.tensor(lam, dtype=torch.bfloat16)
+    k[..., 0] = b.to(device=DEV, dtype=torch.bfloat16)
+    full_check(q, k, v, scale, causal, None, "bf16", f"reference moves D={D} causal={causal}")
+
+
 def test_prefill_scale_zero_is_uniform():
     q, k, v = make(32, 1, 2, 200, 150, 64, "bf16")
     o, l = run(q, k, v, 0.0, False)
