@@ -1,4 +1,4 @@
-"""exact_attention_33_amd: fused exact-attention forward for MI355X (gfx950).
+"""exact_attention_33_amd: fused exact attention for MI355X (gfx950).
 
 A thin ctypes binding over the C ABI in ``include/fa_mi355x.h``.  It only
 marshals arguments: torch allocates the outputs and the workspace and supplies
@@ -7,16 +7,20 @@ the stream; every step of the computation runs in the HIP kernels of
 first call raises.
 
     o, lse = exact_attention_33_amd.fwd(q, k, v, scale=None, causal=False, kv_len=None)
+    dq, dk, dv = exact_attention_33_amd.bwd(q, k, v, o, lse, do, scale=None, causal=False,
+                                            kv_len=None)
 
 q [B,H,N,D], k/v [B,H,M,D] contiguous CUDA tensors (bf16 or float32, D in
 {64, 128}); kv_len an int32 tensor [B] on the same device (or None).  Returns
-O [B,H,N,D] (input dtype) and LSE [B,H,N] (float32, natural log).
+O [B,H,N,D] (input dtype) and LSE [B,H,N] (float32, natural log).  ``bwd``
+takes the forward's inputs and outputs and the upstream gradient dO (bf16)
+and returns dQ, dK, dV (bf16).
 """
 import ctypes
 import math
 import os
 
-__all__ = ["fwd", "plan", "workspace_bytes", "lib", "library_path", "FaError",
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "plan", "workspace_bytes", "lib", "library_path", "FaError",
            "PATH_AUTO", "PATH_PREFILL", "PATH_SPLITKV", "PATH_F32",
            "F32", "BF16", "EXPORTS"]
 
@@ -26,6 +30,7 @@ PATH_NAMES = {PATH_PREFILL: "prefill", PATH_SPLITKV: "splitkv", PATH_F32: "f32"}
 
 # Every symbol include/fa_mi355x.h declares.
 EXPORTS = ["fa_plan_query", "fa_fwd_workspace_bytes", "fa_fwd", "fa_fwd_ex",
+           "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_status_str", "fa_last_error", "fa_abi_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +83,10 @@ def lib():
     L.fa_fwd.restype = i32
     L.fa_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(Options)]
     L.fa_fwd_ex.restype = i32
+    L.fa_bwd_workspace_bytes.argtypes = [Shape, i32, i32]
+    L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_bwd.argtypes = [vp] * 10 + [Shape, i32, f32, i32, vp, ctypes.c_size_t, vp]
+    L.fa_bwd.restype = i32
     L.fa_status_str.argtypes = [i32]
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_last_error.argtypes = []
@@ -178,3 +187,63 @@ def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
                      int(bool(causal)), ws_ptr, ws_len, sptr or None, _opt_ptr(opts))
     _check(st)
     return out, lse
+
+
+def bwd_workspace_bytes(B, H, N, M, D, dtype=BF16, causal=False):
+    return int(lib().fa_bwd_workspace_bytes(Shape(B, H, N, M, D), int(dtype), int(bool(causal))))
+
+
+def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_len=None, *, dq=None, dk=None,
+        dv=None, workspace=None, stream=None):
+    """Gradients of the forward through the C ABI; returns (dQ, dK, dV).
+
+    ``o`` and ``lse`` must be what ``fwd`` returned for the same q, k, v,
+    scale, causal and kv_len; ``do`` is the upstream gradient, shaped like o.
+    """
+    import torch
+    L = lib()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, N, D = q.shape
+    M = k.shape[2]
+    if tuple(k.shape) != (B, H, M, D) or tuple(v.shape) != (B, H, M, D):
+        raise ValueError("k and v must be [B, H, M, D] matching q [B, H, N, D]")
+    if tuple(o.shape) != (B, H, N, D) or tuple(do.shape) != (B, H, N, D):
+        raise ValueError("o and do must be shaped like q")
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == do.dtype):
+        raise TypeError("q, k, v, o and do must share one dtype")
+    dt = _dtype_code(q)
+    dev = q.device
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if kv_len is not None:
+        if not isinstance(kv_len, torch.Tensor):
+            kv_len = torch.as_tensor(kv_len, dtype=torch.int32)
+        kv_len = kv_len.to(device=dev, dtype=torch.int32).contiguous()
+        if kv_len.numel() != B:
+            raise ValueError("kv_len must have B entries")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    shape = Shape(B, H, N, M, D)
+    need = int(L.fa_bwd_workspace_bytes(shape, dt, int(bool(causal))))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = L.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                  do.data_ptr(), kv_len.data_ptr() if kv_len is not None else None,
+                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), shape, dt, float(scale),
+                  int(bool(causal)), ws_ptr, ws_len, sptr or None)
+    _check(st)
+    return dq, dk, dv

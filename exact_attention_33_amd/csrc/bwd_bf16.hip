@@ -1,0 +1,650 @@
+// Backward of the fused exact attention, bf16 inputs, float32 accumulation,
+// for gfx950 (CDNA4, wave64, bf16 MFMA).
+//
+// Method ("Flash Attention: The Hidden Gem", Phase 2: Backward Pass):
+//  * the row statistic D_i = rowsum(dO_i * O_i) (The D Shortcut) is computed
+//    once, in its own pass over dO and O, before anything else (The
+//    Algorithm, step 4);
+//  * the weights are recomputed from the saved log-sum-exp, P = exp(S - L),
+//    never stored (steps 10-11), and the score gradient is
+//    dS = P * (dP - D) with dP = dO V^T (steps 13-14, The Softmax Jacobian);
+//  * dV = P^T dO and dK = dS^T Q accumulate on chip over all query tiles and
+//    are written once per key tile (steps 5-8, 12, 16, 18: key/value tiles
+//    on the outside);
+//  * dQ = dS K.  The pages accumulate it with a read-modify-write of dQ in
+//    HBM on every inner step (step 15).  Here it has a pass of its own with
+//    the query tiles on the outside: it recomputes S and dP (two more tile
+//    products out of seven) and then writes each dQ row once, with no
+//    read-modify-write traffic, no atomics and a result that does not
+//    depend on the order in which workgroups run.
+// With S = scale * Q K^T the chain rule puts the scale on both score
+// gradients: dQ = scale * dS K and dK = scale * dS^T Q.
+//
+// gfx950 mapping (both tile passes):
+//  * v_mfma_f32_32x32x16_bf16, 4 waves per workgroup, one per SIMD, 512
+//    registers per wave;
+//  * dK/dV pass: wave w owns 64 keys.  Their K and V fragments stay in
+//    registers (B operands of S = Q K^T and dP = dO V^T) and their dK^T and
+//    dV^T accumulators too.  Query tiles of 64 stream through LDS (Q, dO,
+//    LSE, D) and are processed 32 queries at a time.  S and dP come out
+//    with one key per lane and 16 queries per lane, so the weights and score
+//    gradients convert to bf16 straight into the B operands of
+//    dV^T += dO^T P and dK^T += Q^T dS (the contraction over queries runs in
+//    the order in which the accumulator layout hands the queries over);
+//    dO^T and Q^T come from transposing LDS reads;
+//  * dQ pass: wave w owns 64 queries.  Their Q and dO fragments stay in
+//    registers (B operands of S^T = K Q^T and dP^T = V dO^T) with the dQ^T
+//    accumulator; key tiles of 64 stream through LDS.  S^T has one query per
+//    lane, so LSE and D are two per-lane values, and dS^T converts straight
+//    into the B operand of dQ^T += K^T dS^T, with K^T from transposing reads;
+//  * each wave reads every staged tile twice (row reads for S and dP,
+//    transposing reads for the gradient products): 64 keys (or queries) per
+//    wave keep that to 16 bytes of LDS per MFMA cycle;
+//  * LDS tiles: rows of 2 D + 64 bytes, and the four 16-byte chunks of each
+//    64-byte group of a row are permuted by XOR with bits 2-3 of the row
+//    index.  Row reads (16 rows x 16 bytes per 16 lanes) and transposing
+//    reads (4 rows x 64 bytes per 32 lanes) are then both free of bank
+//    conflicts; no single padding serves both patterns;
+//  * tiles move HBM -> LDS with buffer loads into LDS against descriptors
+//    that end at the last valid row, so ragged tails read as zeros; two
+//    stages, the next one loading while the current one is computed;
+//  * causal: tiles that no query of a wave sees are skipped, and only tiles
+//    that cross the diagonal are masked element by element.
+#include <cmath>
+#include <type_traits>
+
+#include "device_common.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int NW = kBwdThreads / 64;  // waves per workgroup
+
+// v_mfma_f32_32x32x16_bf16 with the register file of each operand fixed
+// (the compiler's own choice moves accumulators between VGPRs and AGPRs on
+// every iteration).  D = A B (+ D); A, B hold 8 bf16 per lane.
+//   _vv: D in VGPRs (read by the VALU afterwards), A and B in VGPRs;
+//   _va: D in VGPRs, A in VGPRs, B in AGPRs;
+//   _aa: D in AGPRs (accumulated over the whole kernel), A and B in VGPRs.
+// The asm is invisible to the compiler's hazard tracking, so the rules are
+// kept here: each MFMA starts with 2 wait states (a VALU write of a register
+// an MFMA reads needs 2, and the compiler may place a copy of an operand
+// right before the asm); a VALU (or v_accvgpr_read) access to a result waits
+// 16 wait states after the last MFMA that wrote it (mfma_guard, tied to the
+// results); registers written by the VALU wait 5 more before an MFMA reads
+// them (valu_guard, tied to the operands).
+__device__ __forceinline__ void mfma_vv0(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vv(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_va0(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_va(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_aa(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// 16 wait states, ordered after the MFMAs that wrote x and y and before
+// every later access to them.
+__device__ __forceinline__ void mfma_guard_v(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void mfma_guard_a(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7" : "+a"(x)); }
+__device__ __forceinline__ void valu_guard(bf16x8& x, bf16x8& y) {
+  asm volatile("s_nop 4" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void agpr_guard(f32x16& x) { asm volatile("s_nop 4" : "+a"(x)); }
+
+// vmcnt(0), other counters untouched (gfx9 s_waitcnt encoding).
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <class T>
+__device__ __forceinline__ const T* lds_at(const void* base, int byte_off) {
+  return (const T*)((const char*)base + byte_off);
+}
+
+// ---------------------------------------------------------------------------
+// Staged tiles.  A stage holds 64 rows of a [rows][D] bf16 tensor, row r at
+// byte r * ROWB, its 16-byte chunk c at position c ^ ((r >> 2) & 3).
+// ---------------------------------------------------------------------------
+template <int D>
+struct Stage {
+  static constexpr int ROWB = 2 * D + 64;   // LDS bytes per row
+  static constexpr int CPR = D / 8;         // data chunks per row
+  static constexpr int CH = ROWB / 16;      // 16-byte slots per row
+  static constexpr int ROWS = 64;
+  static constexpr int BLK = ROWS * CH / 64;  // 1 KB load blocks per stage
+  static constexpr int BPW = BLK / NW;        // blocks per wave
+  static_assert(BLK % NW == 0, "load blocks split evenly over the waves");
+  static constexpr int BYTES = ROWS * ROWB;
+
+  // Global byte offset (relative to the stage's first row) of slot `slot`.
+  // Padding slots load the row's chunk 0 (valid data, never read).
+  __device__ static uint32_t slot_src(int slot) {
+    const int r = slot / CH, pos = slot % CH;
+    const int c = pos < CPR ? (pos ^ ((r >> 2) & 3)) : 0;
+    return (uint32_t)(r * (2 * D) + 16 * c);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Pass 1: Lg[i] = LSE_i * log2(e) (+inf where LSE = -inf or i >= N) and
+// D_i = rowsum(dO_i * O_i), per (batch, head), Npad rows.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_rowstat_kernel(BwdProblem p, int nchunk) {
+  constexpr int LPR = D / 8;                 // lanes per row, 16 bytes each
+  constexpr int RPP = kBwdThreads / LPR;     // rows per pass
+  constexpr int ROWS = 64;                   // rows per workgroup
+  const int chunk = (int)(blockIdx.x % nchunk);
+  const int64_t bh = blockIdx.x / nchunk;
+  const int N = p.N;
+  const int sub = threadIdx.x % LPR;
+  const __bf16* O = (const __bf16*)p.o + (size_t)bh * N * D;
+  const __bf16* dO = (const __bf16*)p.dout + (size_t)bh * N * D;
+  float* Lg = p.ws + (size_t)bh * 2 * p.Npad;
+  float* Dg = Lg + p.Npad;
+#pragma unroll
+  for (int pass = 0; pass < ROWS / RPP; ++pass) {
+    const int row = chunk * ROWS + pass * RPP + (int)threadIdx.x / LPR;
+    float acc = 0.f;
+    if (row < N) {
+      const bf16x8 o = *(const bf16x8*)(O + (size_t)row * D + sub * 8);
+      const bf16x8 g = *(const bf16x8*)(dO + (size_t)row * D + sub * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
+    }
+    acc = group_sum<LPR>(acc);
+    if (sub == 0) {
+      const float L = row < N ? p.lse[(size_t)bh * N + row] : -INFINITY;
+      Lg[row] = L == -INFINITY ? INFINITY : L * kLog2e;
+      Dg[row] = acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: dK and dV.  Workgroup = 4 waves x 64 keys; query stages of 64.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
+  using St = Stage<D>;
+  constexpr int ROWB = St::ROWB;
+  constexpr int KBW = 2;             // 32-key blocks per wave
+  constexpr int KW = 32 * KBW;       // keys per wave
+  constexpr int DK = D / 16;         // k-steps over d
+  constexpr int DB = D / 32;         // 32-wide d blocks
+  static_assert(NW * KW == kBwdBlockKV, "keys per workgroup");
+  static_assert(St::ROWS == kBwdStageQ, "stage rows");
+
+  __shared__ __attribute__((aligned(1024))) char Qs0[St::BYTES];
+  __shared__ __attribute__((aligned(1024))) char Qs1[St::BYTES];
+  __shared__ __attribute__((aligned(1024))) char Gs0[St::BYTES];   // dO
+  __shared__ __attribute__((aligned(1024))) char Gs1[St::BYTES];
+  __shared__ __attribute__((aligned(1024))) float Ls0[256];        // [0,64) Lg, [64,128) D
+  __shared__ __attribute__((aligned(1024))) float Ls1[256];
+
+  const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int kt = (int)(logical % n_ktiles);   // causal: low key tiles see the most queries
+  const int64_t bh = logical / n_ktiles;
+  const int b = (int)(bh / p.H);
+  const int N = p.N, M = p.M;
+  const int tid = threadIdx.x;
+  const int lane = tid % 64, h = lane / 32, l32 = lane % 32;
+  const int ws = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int kvl = __builtin_amdgcn_readfirstlane(clamp_kv(p.kv_len, b, M));
+  const int off = kvl - N;                    // key j visible to query i iff j <= i + off
+  const int k0 = kt * kBwdBlockKV;
+  const int jw0 = k0 + ws * KW;               // first key of this wave
+
+  const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
+  const __bf16* Gg = (const __bf16*)p.dout + (size_t)bh * N * D;
+  const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D;
+  const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D;
+  const float* Wg = p.ws + (size_t)bh * 2 * p.Npad;
+
+  // Query stages this workgroup visits.
+  const int n_stage_all = (N + St::ROWS - 1) / St::ROWS;
+  int s_lo = 0;
+  if (CAUSAL) s_lo = min(max(k0 - off, 0) / St::ROWS, n_stage_all);
+  const int n_stages = k0 < kvl ? n_stage_all - s_lo : 0;
+
+  // ---- K and V fragments of the wave's keys (B operands), zero past kv_len ----
+  bf16x8 kf[KBW][DK], vf[KBW][DK];
+#pragma unroll
+  for (int kb2 = 0; kb2 < KBW; ++kb2) {
+    const int key = jw0 + 32 * kb2 + l32;
+    const bool ok = key < kvl;
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb) {
+      const size_t e = (size_t)(ok ? key : 0) * D + kb * 16 + h * 8;
+      kf[kb2][kb] = ok ? *(const bf16x8*)(Kg + e) : bf16x8{};
+      vf[kb2][kb] = ok ? *(const bf16x8*)(Vg + e) : bf16x8{};
+    }
+  }
+
+  // ---- stage loads: rows [64 s, 64 s + 64) of Q, dO, Lg, D ----
+  uint32_t soff[St::BPW];
+#pragma unroll
+  for (int i = 0; i < St::BPW; ++i) soff[i] = St::slot_src((ws + i * NW) * 64 + lane);
+  const int nrec_q = N * 2 * D;  // the planner keeps this below 2^31
+  // Lane l of wave 0's extra block: Lg (l < 16) or D (16 <= l < 32) chunk.
+  const uint32_t loff = (uint32_t)((lane < 16 ? lane : (lane < 32 ? p.Npad / 4 + lane - 16 : 0)) * 16);
+  auto load_stage = [&](int s, char* Qd, char* Gd, float* Ld) __attribute__((always_inline)) {
+    const uint32_t rb = (uint32_t)s * St::ROWS * 2 * D;
+#pragma unroll
+    for (int i = 0; i < St::BPW; ++i) {
+      int wofs = (ws + i * NW) * 1024;
+      asm volatile("" : "+s"(wofs));
+      buffer_load_lds16(Qg, nrec_q, soff[i] + rb, (lds_ptr)(Qd + wofs));
+      buffer_load_lds16(Gg, nrec_q, soff[i] + rb, (lds_ptr)(Gd + wofs));
+    }
+    if (ws == 0)
+      buffer_load_lds16(Wg + s * St::ROWS, (int)((2 * p.Npad - s * St::ROWS) * 4), loff, (lds_ptr)Ld);
+  };
+
+  // ---- per-lane LDS read bases ----
+  // Row reads (A operand of S and dP): row 32 u + l32, chunk 2 kb + h.
+  const int G = (l32 >> 2) & 3;
+  const int rbase0 = l32 * ROWB + 16 * ((0 + h) ^ G);   // kb even; + 32 u ROWB + 64 (kb / 2)
+  const int rbase1 = l32 * ROWB + 16 * ((2 + h) ^ G);   // kb odd
+  // Transposing reads (A operand of dV^T, dK^T): lane j of 16-lane group g
+  // reads row 32 u + 16 s' + 8 hi + 4 h + j / 4, columns 32 db + 16 (g % 2) +
+  // 4 (j % 4) .. + 4.
+  const int j16 = lane % 16, g2 = (lane / 16) % 2;
+  const int tbase0 = (4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (0 + h)) + 8 * (j16 % 2);
+  const int tbase1 = (8 + 4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (2 + h)) + 8 * (j16 % 2);
+
+  f32x16 dkacc[KBW][DB], dvacc[KBW][DB];
+#pragma unroll
+  for (int kb2 = 0; kb2 < KBW; ++kb2)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dkacc[kb2][db] = f32x16{};
+      dvacc[kb2][db] = f32x16{};
+      agpr_guard(dkacc[kb2][db]);
+      agpr_guard(dvacc[kb2][db]);
+    }
+  const float c = fmaxf(p.scale * kLog2e, 1e-30f);
+  // Causal: query i sees the lane's key j iff i >= j - off; register r of a
+  // step holds query qs0 + 8 (r / 4) + 4 h + r % 4, masked iff
+  // qs0 + 8 (r / 4) + r % 4 < thr.
+  int thr[KBW];
+#pragma unroll
+  for (int kb2 = 0; kb2 < KBW; ++kb2) thr[kb2] = jw0 + 32 * kb2 + l32 - off - 4 * h;
+
+  // One 32-query step of stage s from buffers (Qs, Gs, Ls).
+  auto qstep = [&](int s, int u, const char* Qs, const char* Gs, const float* Ls, auto MASK) __attribute__((always_inline)) {
+    constexpr bool mask = decltype(MASK)::value;
+    const int qs0 = s * St::ROWS + 32 * u;
+    f32x16 sacc[KBW], pacc[KBW];
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb) {
+      const int o = 32 * u * ROWB + 64 * (kb / 2) + ((kb & 1) ? rbase1 : rbase0);
+      const bf16x8 qa = *lds_at<bf16x8>(Qs, o);
+      const bf16x8 ga = *lds_at<bf16x8>(Gs, o);
+#pragma unroll
+      for (int kb2 = 0; kb2 < KBW; ++kb2) {
+        if (kb == 0) {
+          mfma_vv0(sacc[kb2], qa, kf[kb2][kb]);
+          mfma_vv0(pacc[kb2], ga, vf[kb2][kb]);
+        } else {
+          mfma_vv(sacc[kb2], qa, kf[kb2][kb]);
+          mfma_vv(pacc[kb2], ga, vf[kb2][kb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int kb2 = 0; kb2 < KBW; ++kb2) mfma_guard_v(sacc[kb2], pacc[kb2]);
+    // P = 2^(S c - Lg), dS = P (dP - D).  Lane: key jw0 + 32 kb2 + l32,
+    // register r: query qs0 + 8 (r / 4) + 4 h + r % 4.
+    bf16x8 pf[KBW][2], sf[KBW][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 L4 = *(const float4*)(Ls + 32 * u + 8 * g + 4 * h);
+      const float4 D4 = *(const float4*)(Ls + 64 + 32 * u + 8 * g + 4 * h);
+      const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+      const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+#pragma unroll
+        for (int kb2 = 0; kb2 < KBW; ++kb2) {
+          float pv = fast_exp2(fmaf(sacc[kb2][r], c, -Lv[e]));
+          if constexpr (mask) pv = qs0 + 8 * g + e < thr[kb2] ? 0.f : pv;
+          const float dsv = pv * (pacc[kb2][r] - Dv[e]);
+          pf[kb2][r / 8][r % 8] = (__bf16)pv;
+          sf[kb2][r / 8][r % 8] = (__bf16)dsv;
+        }
+      }
+    }
+#pragma unroll
+    for (int kb2 = 0; kb2 < KBW; ++kb2) valu_guard(pf[kb2][0], sf[kb2][0]), valu_guard(pf[kb2][1], sf[kb2][1]);
+    // dV^T += dO^T P, dK^T += Q^T dS over the step's 32 queries.
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int o = (32 * u + 16 * sp) * ROWB + 64 * db;
+        const s16x4 glo = lds_read_tr16((const __bf16*)(Gs + o + tbase0));
+        const s16x4 ghi = lds_read_tr16((const __bf16*)(Gs + o + tbase1));
+        const s16x4 qlo = lds_read_tr16((const __bf16*)(Qs + o + tbase0));
+        const s16x4 qhi = lds_read_tr16((const __bf16*)(Qs + o + tbase1));
+        const bf16x8 gt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int kb2 = 0; kb2 < KBW; ++kb2) {
+          mfma_aa(dvacc[kb2][db], gt, pf[kb2][sp]);
+          mfma_aa(dkacc[kb2][db], qt, sf[kb2][sp]);
+        }
+      }
+  };
+
+  // Every branch below is uniform over the workgroup and no step is skipped
+  // inside a loop: control flow that joins with the accumulators live makes
+  // the register allocator shuffle them between AGPRs.
+  auto iteration = [&](int t, const char* Qs, const char* Gs, const float* Ls, char* Qn, char* Gn,
+                       float* Ln, auto MASK) __attribute__((always_inline)) {
+    wait_vm0();
+    __syncthreads();
+    if (t + 1 < n_stages) load_stage(s_lo + t + 1, Qn, Gn, Ln);
+    qstep(s_lo + t, 0, Qs, Gs, Ls, MASK);
+    qstep(s_lo + t, 1, Qs, Gs, Ls, MASK);
+  };
+
+  // Causal: the first n_mask stages hold queries that do not see every key
+  // of the workgroup and are masked element by element (an even number, so
+  // that the unmasked loop starts on buffer 0, or all stages).
+  int n_mask = 0;
+  if (CAUSAL) {
+    const int rows = k0 + kBwdBlockKV - 1 - off - s_lo * St::ROWS;  // masked rows from stage s_lo on
+    n_mask = rows > 0 ? min((rows + 2 * St::ROWS - 1) / (2 * St::ROWS) * 2, n_stages) : 0;
+  }
+  if (n_stages > 0) load_stage(s_lo, Qs0, Gs0, Ls0);
+  int t = 0;
+  for (; t + 1 < n_mask; t += 2) {
+    iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::true_type{});
+    iteration(t + 1, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, std::true_type{});
+  }
+  if (t < n_mask) {  // n_mask == n_stages, odd: the last stage
+    iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::true_type{});
+    ++t;
+  }
+  for (; t + 1 < n_stages; t += 2) {
+    iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::false_type{});
+    iteration(t + 1, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, std::false_type{});
+  }
+  if (t < n_stages) iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::false_type{});
+
+#pragma unroll
+  for (int kb2 = 0; kb2 < KBW; ++kb2)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      mfma_guard_a(dkacc[kb2][db]);
+      mfma_guard_a(dvacc[kb2][db]);
+    }
+  // ---- write dK = scale * dK^T^T and dV (zero for keys at or past kv_len) ----
+  // Accumulator (kb2, db), register r: d = 32 db + 8 (r / 4) + 4 h + r % 4,
+  // key jw0 + 32 kb2 + l32.
+  __bf16* dK = (__bf16*)p.dk + (size_t)bh * M * D;
+  __bf16* dV = (__bf16*)p.dv + (size_t)bh * M * D;
+  const float sc = p.scale;
+#pragma unroll
+  for (int kb2 = 0; kb2 < KBW; ++kb2) {
+    const int key = jw0 + 32 * kb2 + l32;
+    if (key >= M) continue;
+    const bool ok = key < kvl;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 kv4, vv4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv4[e] = (__bf16)(ok ? dkacc[kb2][db][4 * g + e] * sc : 0.f);
+          vv4[e] = (__bf16)(ok ? dvacc[kb2][db][4 * g + e] : 0.f);
+        }
+        const size_t at = (size_t)key * D + 32 * db + 8 * g + 4 * h;
+        *(bf16x4*)(dK + at) = kv4;
+        *(bf16x4*)(dV + at) = vv4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3: dQ.  Workgroup = 4 waves x 64 queries; key stages of 64.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
+  using St = Stage<D>;
+  constexpr int ROWB = St::ROWB;
+  constexpr int QW = 64;             // queries per wave
+  constexpr int NQB = QW / 32;       // 32-query blocks per wave
+  constexpr int DK = D / 16;
+  constexpr int DB = D / 32;
+  static_assert(NW * QW == kBwdBlockQ, "queries per workgroup");
+  static_assert(St::ROWS == kBwdStageK, "stage rows");
+
+  __shared__ __attribute__((aligned(1024))) char Ks0[St::BYTES];
+  __shared__ __attribute__((aligned(1024))) char Ks1[St::BYTES];
+  __shared__ __attribute__((aligned(1024))) char Vs0[St::BYTES];
+  __shared__ __attribute__((aligned(1024))) char Vs1[St::BYTES];
+
+  const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
+  int qt = (int)(logical % n_qtiles);
+  const int64_t bh = logical / n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;   // heaviest query tiles first
+  const int b = (int)(bh / p.H);
+  const int N = p.N, M = p.M;
+  const int tid = threadIdx.x;
+  const int lane = tid % 64, h = lane / 32, l32 = lane % 32;
+  const int ws = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int kvl = __builtin_amdgcn_readfirstlane(clamp_kv(p.kv_len, b, M));
+  const int off = kvl - N;
+  const int q0 = qt * kBwdBlockQ;
+  const int qw0 = q0 + ws * QW;
+  const int q_last = min(q0 + kBwdBlockQ, N) - 1;
+  const int kv_end = CAUSAL ? min(kvl, q_last + off + 1) : kvl;
+  const int n_stages = kv_end > 0 ? (kv_end + St::ROWS - 1) / St::ROWS : 0;
+
+  const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
+  const __bf16* Gg = (const __bf16*)p.dout + (size_t)bh * N * D;
+  const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D;
+  const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D;
+  const float* Wg = p.ws + (size_t)bh * 2 * p.Npad;
+
+  // ---- Q and dO fragments of the wave's queries (B operands) ----
+  // Rows past N hold zeros; their Lg is +inf, so their weights are 0.
+  bf16x8 qf[NQB][DK], gf[NQB][DK];
+  float Lq[NQB], Dq[NQB];
+  int lim[NQB];                  // last key the lane's query sees
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int row = qw0 + 32 * qb + l32;
+    const bool ok = row < N;
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb) {
+      const size_t e = (size_t)(ok ? row : 0) * D + kb * 16 + h * 8;
+      qf[qb][kb] = ok ? *(const bf16x8*)(Qg + e) : bf16x8{};
+      gf[qb][kb] = ok ? *(const bf16x8*)(Gg + e) : bf16x8{};
+    }
+    Lq[qb] = Wg[row];            // row < Npad
+    Dq[qb] = Wg[p.Npad + row];
+    lim[qb] = CAUSAL ? min(row + off, kvl - 1) : kvl - 1;
+  }
+
+  uint32_t soff[St::BPW];
+#pragma unroll
+  for (int i = 0; i < St::BPW; ++i) soff[i] = St::slot_src((ws + i * NW) * 64 + lane);
+  const int nrec_k = kvl * 2 * D;  // the planner keeps M * D * 2 below 2^31
+  auto load_stage = [&](int s, char* Kd, char* Vd) __attribute__((always_inline)) {
+    const uint32_t rb = (uint32_t)s * St::ROWS * 2 * D;
+#pragma unroll
+    for (int i = 0; i < St::BPW; ++i) {
+      int wofs = (ws + i * NW) * 1024;
+      asm volatile("" : "+s"(wofs));
+      buffer_load_lds16(Kg, nrec_k, soff[i] + rb, (lds_ptr)(Kd + wofs));
+      buffer_load_lds16(Vg, nrec_k, soff[i] + rb, (lds_ptr)(Vd + wofs));
+    }
+  };
+
+  const int G = (l32 >> 2) & 3;
+  const int rbase0 = l32 * ROWB + 16 * ((0 + h) ^ G);
+  const int rbase1 = l32 * ROWB + 16 * ((2 + h) ^ G);
+  const int j16 = lane % 16, g2 = (lane / 16) % 2;
+  const int tbase0 = (4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (0 + h)) + 8 * (j16 % 2);
+  const int tbase1 = (8 + 4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (2 + h)) + 8 * (j16 % 2);
+
+  f32x16 dqacc[NQB][DB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dqacc[qb][db] = f32x16{};
+      agpr_guard(dqacc[qb][db]);
+    }
+  const float c = fmaxf(p.scale * kLog2e, 1e-30f);
+
+  // 32 keys (block kb2) of stage s.
+  auto kstep = [&](int s, int kb2, const char* Ks, const char* Vs, auto MASK) __attribute__((always_inline)) {
+    constexpr bool mask = decltype(MASK)::value;
+    const int kk0 = s * St::ROWS + 32 * kb2;
+    f32x16 sacc[NQB], pacc[NQB];
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb) {
+      const int o = 32 * kb2 * ROWB + 64 * (kb / 2) + ((kb & 1) ? rbase1 : rbase0);
+      const bf16x8 ka = *lds_at<bf16x8>(Ks, o);
+      const bf16x8 va = *lds_at<bf16x8>(Vs, o);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        if (kb == 0) {
+          mfma_vv0(sacc[qb], ka, qf[qb][kb]);
+          mfma_vv0(pacc[qb], va, gf[qb][kb]);
+        } else {
+          mfma_vv(sacc[qb], ka, qf[qb][kb]);
+          mfma_vv(pacc[qb], va, gf[qb][kb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) mfma_guard_v(sacc[qb], pacc[qb]);
+    // Lane: query qw0 + 32 qb + l32; register r: key kk0 + 8 (r / 4) + 4 h + r % 4.
+    bf16x8 sf[NQB][2];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = fast_exp2(fmaf(sacc[qb][r], c, -Lq[qb]));
+        if constexpr (mask) {
+          const int key = kk0 + 8 * (r / 4) + 4 * h + r % 4;
+          pv = key > lim[qb] ? 0.f : pv;
+        }
+        sf[qb][r / 8][r % 8] = (__bf16)(pv * (pacc[qb][r] - Dq[qb]));
+      }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) valu_guard(sf[qb][0], sf[qb][1]);
+    // dQ^T += K^T dS^T over the 32 keys.
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int o = (32 * kb2 + 16 * sp) * ROWB + 64 * db;
+        const s16x4 klo = lds_read_tr16((const __bf16*)(Ks + o + tbase0));
+        const s16x4 khi = lds_read_tr16((const __bf16*)(Ks + o + tbase1));
+        const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(klo, khi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) mfma_aa(dqacc[qb][db], kt, sf[qb][sp]);
+      }
+  };
+
+  // As in the dK/dV pass: uniform branches only, no step skipped in a loop.
+  auto iteration = [&](int t, const char* Ks, const char* Vs, char* Kn, char* Vn, auto MASK)
+                       __attribute__((always_inline)) {
+    wait_vm0();
+    __syncthreads();
+    if (t + 1 < n_stages) load_stage(t + 1, Kn, Vn);
+    kstep(t, 0, Ks, Vs, MASK);
+    kstep(t, 1, Ks, Vs, MASK);
+  };
+
+  // Stages before n_clean (an even number) are seen whole by every query of
+  // the workgroup: no key past kv_len and, causal, none past the first
+  // query's last key.  The rest are masked element by element.
+  int n_clean = kvl / St::ROWS;
+  if (CAUSAL) n_clean = min(n_clean, q0 + off + 1 > 0 ? (q0 + off + 1) / St::ROWS : 0);
+  n_clean = min(n_clean, n_stages) / 2 * 2;
+  if (n_stages > 0) load_stage(0, Ks0, Vs0);
+  int t = 0;
+  for (; t < n_clean; t += 2) {
+    iteration(t, Ks0, Vs0, Ks1, Vs1, std::false_type{});
+    iteration(t + 1, Ks1, Vs1, Ks0, Vs0, std::false_type{});
+  }
+  for (; t + 1 < n_stages; t += 2) {
+    iteration(t, Ks0, Vs0, Ks1, Vs1, std::true_type{});
+    iteration(t + 1, Ks1, Vs1, Ks0, Vs0, std::true_type{});
+  }
+  if (t < n_stages) iteration(t, Ks0, Vs0, Ks1, Vs1, std::true_type{});
+
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) mfma_guard_a(dqacc[qb][db]);
+  // ---- write dQ = scale * (dQ^T)^T ----
+  // Accumulator (qb, db), register r: d = 32 db + 8 (r / 4) + 4 h + r % 4,
+  // query qw0 + 32 qb + l32.
+  __bf16* dQ = (__bf16*)p.dq + (size_t)bh * N * D;
+  const float sc = p.scale;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int row = qw0 + 32 * qb + l32;
+    if (row >= N) continue;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 q4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q4[e] = (__bf16)(dqacc[qb][db][4 * g + e] * sc);
+        *(bf16x4*)(dQ + (size_t)row * D + 32 * db + 8 * g + 4 * h) = q4;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdProblem& p, hipStream_t stream) {
+  const int64_t bh = (int64_t)p.B * p.H;
+  const dim3 block(kBwdThreads);
+  if (p.N > 0) {
+    const int nchunk = p.Npad / 64;
+    hipLaunchKernelGGL(bwd_rowstat_kernel<D>, dim3((unsigned)(bh * nchunk)), block, 0, stream, p, nchunk);
+  }
+  if (p.M > 0) {
+    const int n_kt = (p.M + kBwdBlockKV - 1) / kBwdBlockKV;
+    const dim3 grid((unsigned)(bh * n_kt));
+    if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, block, 0, stream, p, n_kt);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, block, 0, stream, p, n_kt);
+  }
+  if (p.N > 0) {
+    const int n_qt = (p.N + kBwdBlockQ - 1) / kBwdBlockQ;
+    const dim3 grid((unsigned)(bh * n_qt));
+    if (p.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, block, 0, stream, p, n_qt);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, block, 0, stream, p, n_qt);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdProblem& p, hipStream_t stream) {
+  if ((int64_t)p.B * p.H == 0) return hipSuccess;
+  return p.D == 64 ? launch_bwd_d<64>(p, stream) : launch_bwd_d<128>(p, stream);
+}
+
+}  // namespace fa

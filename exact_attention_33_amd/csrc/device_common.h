@@ -2,6 +2,8 @@
 #pragma once
 
 #include <cstdint>
+#include <type_traits>
+#include <utility>
 
 #include <hip/hip_runtime.h>
 
@@ -53,6 +55,56 @@ __device__ __forceinline__ int clamp_kv(const int32_t* kv_len, int b, int M) {
   if (!kv_len) return M;
   const int x = kv_len[b];
   return x < 0 ? 0 : (x > M ? M : x);
+}
+
+// XCDs of a gfx950 GPU; workgroups are dealt to them round-robin.
+constexpr int kNumXcd = 8;
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs (untyped 32-bit
+// data, no swizzle); out-of-range reads return zeros.
+constexpr int kBufferFlags = 0x00020000;
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane j supplies the address of 4 consecutive bf16 of row j / 4 of a 4 x 16
+// block, and lane i receives the 4 rows' elements of column i.
+__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// 16 bytes per lane from base + voff into LDS at dst + 16 * lane (one buffer
+// load into LDS), against a descriptor of `nbytes` bytes: lanes whose offset
+// is out of range read zeros.  The body exists only in the device pass: the
+// host pass of a HIP source has no buffer-descriptor type, and clang then
+// drops the host stubs of the kernels that use it.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, uint32_t voff,
+                                                  lds_ptr dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags), dst,
+      16, voff, 0, 0, 0);
+#endif
+}
+
+// Logical work item of workgroup `wg` when workgroups are dealt round-robin
+// to kNumXcd XCDs: XCD x gets a contiguous range of logical items.
+__device__ __forceinline__ int64_t xcd_logical(int64_t wg, int64_t G) {
+  const int64_t x = wg % kNumXcd, j = wg / kNumXcd;
+  const int64_t q = G / kNumXcd, r = G % kNumXcd;
+  return x * q + (x < r ? x : r) + j;
+}
+
+// f(integral_constant<int, J>) for J = 0 .. N-1, expanded at compile time (the
+// pipelined loops are too large for the unroller, and their register arrays
+// must only ever see constant indices).
+template <class F, int... J>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace fa

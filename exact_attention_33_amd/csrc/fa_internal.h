@@ -70,4 +70,46 @@ inline int prefill_lds_bytes(int D) {
 }
 inline int f32_lds_bytes(int D) { return 2 * kF32BlockK * D * 4; }
 
+// ---- backward ----
+
+// Problem description handed to the backward launchers.  q, k, v, o, dout,
+// dq, dk, dv are contiguous [B,H,N|M,D] device tensors; lse [B,H,N] float32.
+// The workspace holds, per (batch, head), Npad float32 values of
+// LSE * log2(e) (+inf for a row with no visible key and for the padding
+// rows) followed by Npad values of the row statistic D = rowsum(dO * O).
+struct BwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  const int32_t* kv_len;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws;
+  int32_t B, H, N, M, D, Npad;
+  float scale;
+  int causal;
+};
+
+constexpr int kBwdThreads = 256;
+constexpr int kBwdRowPad = 256;        // Npad = N rounded up to this
+constexpr int kBwdStageQ = 64;         // dK/dV kernel: queries per LDS stage
+constexpr int kBwdBlockKV = 256;       // dK/dV kernel: keys per workgroup (4 waves x 64)
+constexpr int kBwdBlockQ = 256;        // dQ kernel: queries per workgroup (4 waves x 64)
+constexpr int kBwdStageK = 64;         // dQ kernel: keys per LDS stage
+
+inline int64_t bwd_npad(int N) { return ((int64_t)N + kBwdRowPad - 1) / kBwdRowPad * kBwdRowPad; }
+inline size_t bwd_workspace_bytes(const fa_shape& s) {
+  return (size_t)s.B * (size_t)s.H * (size_t)bwd_npad(s.N) * 2 * sizeof(float);
+}
+// Row stride in LDS of a staged [rows][D] bf16 tile: 64 bytes of padding.
+inline int bwd_lds_row_bytes(int D) { return 2 * D + 64; }
+inline int bwd_dkdv_lds_bytes(int D) { return 2 * (2 * kBwdStageQ * bwd_lds_row_bytes(D) + 1024); }
+inline int bwd_dq_lds_bytes(int D) { return 2 * (2 * kBwdStageK * bwd_lds_row_bytes(D)); }
+
+hipError_t launch_bwd_bf16(const BwdProblem& p, hipStream_t stream);
+
 }  // namespace fa

@@ -86,15 +86,6 @@
 namespace fa {
 namespace {
 
-constexpr int kNumXcd = 8;
-// Word 3 of a raw buffer descriptor on gfx9-family GPUs (untyped 32-bit
-// data, no swizzle); out-of-range reads return zeros.
-constexpr int kBufferFlags = 0x00020000;
-
-__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-}
 
 // The two halves of a wave combined: every lane receives op(x[i], x[i ^ 32]).
 __device__ __forceinline__ float swap_halves_max(float x) {
@@ -106,21 +97,6 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// 16 bytes per lane from base + voff into LDS at dst + 16 * lane (one buffer
-// load into LDS), against a descriptor of `nbytes` bytes: lanes whose offset
-// is out of range read zeros.  The body exists only in the device pass: the
-// host pass of a HIP source has no buffer-descriptor type, and clang then
-// drops the host stubs of the kernels that use it.
-__device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, uint32_t voff,
-                                                  lds_ptr dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags), dst,
-      16, voff, 0, 0, 0);
-#endif
-}
 
 // S^T += K Q^T fragment products with the accumulator in VGPRs.  The score
 // tile is read by the softmax right after it is formed; the compiler places
@@ -151,25 +127,6 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 
 __device__ __forceinline__ void mfma_guard() { asm volatile("s_nop 7\n\ts_nop 7"); }
 
-// Logical work item of workgroup `wg` when workgroups are dealt round-robin
-// to kNumXcd XCDs: XCD x gets a contiguous range of logical items.
-__device__ __forceinline__ int64_t xcd_logical(int64_t wg, int64_t G) {
-  const int64_t x = wg % kNumXcd, j = wg / kNumXcd;
-  const int64_t q = G / kNumXcd, r = G % kNumXcd;
-  return x * q + (x < r ? x : r) + j;
-}
-
-// f(integral_constant<int, J>) for J = 0 .. N-1, expanded at compile time (the
-// pipelined loops are too large for the unroller, and their register arrays
-// must only ever see constant indices).
-template <class F, int... J>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
-  (f(std::integral_constant<int, J>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))

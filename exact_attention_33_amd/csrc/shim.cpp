@@ -1,5 +1,6 @@
 // C-ABI shim: argument checks, planning and dispatch to the kernels.
 // The declarations and their contracts are in include/fa_mi355x.h.
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -129,6 +130,67 @@ fa_status fa_fwd(const void* q, const void* k, const void* v,
                  void* workspace, size_t workspace_bytes, void* stream) {
   return fa_fwd_ex(q, k, v, kv_len, o, lse, s, dtype, scale, causal, workspace,
                    workspace_bytes, stream, nullptr);
+}
+
+size_t fa_bwd_workspace_bytes(fa_shape s, fa_dtype dtype, int causal) {
+  (void)causal;
+  if (dtype != FA_BF16 || s.B < 0 || s.H < 0 || s.N < 0 || s.M < 0) return 0;
+  return fa::bwd_workspace_bytes(s);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, const int32_t* kv_len, void* dq, void* dk, void* dv,
+                 fa_shape s, fa_dtype dtype, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (s.B < 0 || s.H < 0 || s.N < 0 || s.M < 0 || s.D < 0)
+    return fail(FA_ERR_SHAPE, "fa_bwd: B, H, N, M and D must be non-negative");
+  if (dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: only FA_BF16 inputs are supported");
+  if (s.D != 64 && s.D != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: head dimension D must be 64 or 128");
+  if (!std::isfinite(scale) || scale < 0.0f)
+    return fail(FA_ERR_ARG, "fa_bwd: scale must be finite and >= 0 (got %g)", (double)scale);
+  const int64_t bh = (int64_t)s.B * s.H;
+  // The tile passes address one (batch, head) of Q, dO, K or V with 32-bit
+  // byte offsets, and their grids must fit 32 bits.
+  if ((int64_t)s.N * s.D * 2 > INT32_MAX || (int64_t)s.M * s.D * 2 > INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: needs N * D * 2 and M * D * 2 below 2^31");
+  if (bh > INT32_MAX ||
+      bh * ((fa::bwd_npad(s.N) + 63) / 64) > INT32_MAX ||
+      bh * (((int64_t)s.M + fa::kBwdBlockKV - 1) / fa::kBwdBlockKV) > INT32_MAX)
+    return fail(FA_ERR_SHAPE, "fa_bwd: grid exceeds 2^31 - 1 workgroups");
+  if (bh == 0 || (s.N == 0 && s.M == 0)) {
+    g_last_error[0] = 0;
+    return FA_OK;
+  }
+  const bool has_q = s.N > 0, has_kv = s.M > 0;
+  if (has_q && (!q || !o || !lse || !dout || !dq))
+    return fail(FA_ERR_NULL, "fa_bwd: q, o, lse, dout and dq must be non-NULL when N > 0");
+  if (has_kv && (!k || !v || !dk || !dv))
+    return fail(FA_ERR_NULL, "fa_bwd: k, v, dk and dv must be non-NULL when M > 0");
+  const void* a16[] = {q, o, dout, dq, k, v, dk, dv};
+  for (const void* ptr : a16)
+    if (ptr && !aligned(ptr, 16))
+      return fail(FA_ERR_ALIGN, "fa_bwd: q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+  if ((lse && !aligned(lse, 4)) || (kv_len && !aligned(kv_len, 4)))
+    return fail(FA_ERR_ALIGN, "fa_bwd: lse and kv_len must be 4-byte aligned");
+  const size_t need = fa::bwd_workspace_bytes(s);
+  if (need) {
+    if (!workspace)
+      return fail(FA_ERR_WORKSPACE, "fa_bwd: this shape needs %zu workspace bytes, got NULL", need);
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "fa_bwd: this shape needs %zu workspace bytes, got %zu", need,
+                  workspace_bytes);
+    if (!aligned(workspace, 256))
+      return fail(FA_ERR_ALIGN, "fa_bwd: workspace must be 256-byte aligned");
+  }
+  fa::BwdProblem p{q, k, v, o, dout, lse, kv_len, dq, dk, dv, (float*)workspace,
+                   s.B, s.H, s.N, s.M, s.D, (int32_t)fa::bwd_npad(s.N), scale, causal ? 1 : 0};
+  const hipError_t err = fa::launch_bwd_bf16(p, (hipStream_t)stream);
+  if (err != hipSuccess)
+    return fail(FA_ERR_HIP, "fa_bwd: launch failed: %s", hipGetErrorString(err));
+  g_last_error[0] = 0;
+  return FA_OK;
 }
 
 }  // extern "C"

@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "normal_f32", "qkv_host", "kv_lens",
-           "score_row", "qkv_device", "to_device", "poison_tail"]
+           "score_row", "qkv_device", "grad_device", "to_device", "poison_tail"]
 
 
 @dataclass(frozen=True)
@@ -108,6 +108,22 @@ def qkv_device(seed, B, H, N, M, D, dtype, device, chunk_rows=1 << 22):
     k = out[1].view(B, H, M, D)
     v = out[2].view(B, H, M, D)
     return q, k, v
+
+
+def grad_device(seed, B, H, N, D, dtype, device, chunk_rows=1 << 22):
+    """An upstream gradient dO [B,H,N,D], N(0, 1) drawn on ``device`` with a
+    seeded generator (chunked like ``qkv_device``)."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    rows = B * H * N
+    t = torch.empty((rows, D), dtype=tdt, device=device)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        t[r0:r1] = torch.randn((r1 - r0, D), generator=gen, device=device,
+                               dtype=torch.float32).to(tdt)
+    return t.view(B, H, N, D)
 
 
 def poison_tail(k, v, kv_len):

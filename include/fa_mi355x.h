@@ -1,5 +1,6 @@
 /*
- * fa_mi355x.h -- C ABI of the fused exact-attention forward for MI355X (gfx950).
+ * fa_mi355x.h -- C ABI of the fused exact attention for MI355X (gfx950):
+ * the forward and its backward.
  *
  * The operation (per batch b and head h, all arithmetic described in real
  * numbers; the library's rounding is documented per path below):
@@ -126,6 +127,57 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v,
                     fa_shape s, fa_dtype dtype, float scale, int causal,
                     void* workspace, size_t workspace_bytes, void* stream,
                     const fa_options* opt);
+
+/*
+ * ---- Backward ----
+ *
+ * The gradients of the forward above for an upstream gradient dO = dL/dO
+ * (per batch b and head h; P is the softmax of the visible scores):
+ *
+ *   dV[j]  = sum_i P[i][j] * dO[i]                        (j < kv_len[b])
+ *   dP[i][j] = dO[i] . V[j]
+ *   D[i]   = sum_j dP[i][j] * P[i][j]  = dO[i] . O[i]
+ *   dS[i][j] = P[i][j] * (dP[i][j] - D[i])
+ *   dQ[i]  = scale * sum_j dS[i][j] * K[j]
+ *   dK[j]  = scale * sum_i dS[i][j] * Q[i]                (j < kv_len[b])
+ *
+ * and dK[j] = dV[j] = 0 for keys at or past kv_len[b]; a query with no
+ * visible key gets dQ = 0.  Sources: "Flash Attention: The Hidden Gem" --
+ * Phase 2: Backward Pass (Chain Rule Through a Matrix Multiply: dV = P^T dO,
+ * dP = dO V^T; The Softmax Jacobian: dS = P (dP - D); The D Shortcut:
+ * D = rowsum(dO * O); The Algorithm: P recomputed as exp(S - L) from the
+ * saved log-sum-exp, dQ = dS K, dK = dS^T Q).  The pages write S = Q K^T;
+ * with the forward's S = scale * Q K^T the chain rule puts the scale on dQ
+ * and dK as above.
+ *
+ * Inputs are those of the forward plus its outputs: O [B,H,N,D] and LSE
+ * [B,H,N] exactly as fa_fwd wrote them for the same q, k, v, kv_len, scale
+ * and causal (the backward recomputes P from LSE and takes D from O), and
+ * dout [B,H,N,D].  Outputs dq [B,H,N,D], dk and dv [B,H,M,D].  All tensors
+ * contiguous, D fastest, element type `dtype` except LSE (float32); the same
+ * alignment rules as fa_fwd (16 bytes for tensors, 4 for lse and kv_len,
+ * 256 for the workspace).  Every output element is written; no output may
+ * alias an input.  Accumulation is float32; P and dS are rounded to bf16
+ * before the products that use them; outputs are rounded once (RNE).
+ * The result is bitwise reproducible: no atomics, fixed summation order.
+ *
+ * Memory, streams and errors as for fa_fwd: caller-owned device buffers,
+ * enqueued on `stream`, checks before any launch, FA_ERR_* on failure with
+ * fa_last_error() describing it.  Supported: dtype FA_BF16, D in {64, 128},
+ * N * D * 2 and M * D * 2 below 2^31.  A problem with B * H == 0, or with
+ * N == M == 0, returns FA_OK without launching.
+ */
+
+/* fa_bwd_workspace_bytes -- device workspace fa_bwd needs: 8 bytes per
+ * (batch, head, query row) with the rows rounded up to a multiple of 256
+ * (0 for an unsupported dtype). */
+size_t fa_bwd_workspace_bytes(fa_shape s, fa_dtype dtype, int causal);
+
+/* fa_bwd -- dq, dk, dv as defined above. */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, const int32_t* kv_len, void* dq, void* dk, void* dv,
+                 fa_shape s, fa_dtype dtype, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static name of a status code. */
 const char* fa_status_str(fa_status st);

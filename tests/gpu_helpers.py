@@ -52,3 +52,62 @@ def sample_picks(B, H, N, n_heads=6, seed=0, extra_rows=6):
 
 def default_scale(D):
     return 1.0 / math.sqrt(D)
+
+
+# ---- backward ----
+#
+# Elementwise error bound of the bf16 backward for one (batch, head), from
+# the arithmetic of the kernels (all in fp64 here):
+#   * the kernel forms D_i from the bf16 forward output O^ it is given:
+#     |dD_i| <= |sum_d dO_id (O^_id - O_id)| + float32 rounding;
+#   * it recomputes P from the float32 LSE the forward returned:
+#     relative error |LSE^_i - LSE_i| + float32 slack (scores accumulated in
+#     float32, exp2 of a float32 argument);
+#   * P and dS are rounded to bf16 (unit roundoff 2^-9, taken as 2^-8)
+#     before the products that use them, which accumulate in float32
+#     (n terms: n 2^-24 of the absolute sum, worst case), and each output is
+#     rounded to bf16 once.
+# The test accepts |GPU - oracle| <= 2 * bound elementwise.
+U_BWD = 2.0 ** -8
+F32 = 2.0 ** -24
+
+
+def bwd_bound(r, q, k, v, do, O_gpu, lse_gpu, lse_ref, scale):
+    """Bounds (bq [N,D], bk [M,D], bv [M,D]) for oracle head result ``r``
+    (``oracle.backward.head_backward``) and the exact inputs of that head."""
+    P, dP, dS, delta = r["p"], r["dp"], r["ds"], r["delta"]
+    N, D = q.shape
+    M = k.shape[0]
+    kvl = P.shape[1]
+    kv, vv = k[:kvl], v[:kvl]
+    aq, akv, avv, ado = np.abs(q), np.abs(kv), np.abs(vv), np.abs(do)
+    dD = np.abs(np.sum(do * (O_gpu - r["o"]), axis=1)) + 4 * D * F32 * np.sum(np.abs(do * O_gpu), axis=1)
+    fin = np.isfinite(lse_ref)
+    L_ref = np.where(fin, lse_ref, 0.0)
+    dL = np.where(fin, np.abs(np.where(fin, lse_gpu, 0.0) - L_ref), 0.0)
+    relP = (dL + 16 * F32 * (1.0 + np.abs(L_ref)))[:, None] + scale * 4 * D * F32 * (aq @ akv.T)
+    dP_err = 4 * D * F32 * (ado @ avv.T)
+    dS_err = (U_BWD * np.abs(dS) + P * dD[:, None] + relP * P * np.abs(dP - delta[:, None])
+              + P * dP_err)
+    bv = np.zeros((M, D))
+    bk = np.zeros((M, D))
+    bv[:kvl] = (((U_BWD + relP) * P).T @ ado + N * F32 * (P.T @ ado) + U_BWD * np.abs(r["dv"][:kvl]))
+    bk[:kvl] = (scale * (dS_err.T @ aq) + N * F32 * scale * (np.abs(dS).T @ aq)
+                + U_BWD * np.abs(r["dk"][:kvl]))
+    bq = scale * (dS_err @ akv) + max(kvl, 1) * F32 * scale * (np.abs(dS) @ akv) + U_BWD * np.abs(r["dq"])
+    return bq, bk, bv
+
+
+def compare_bwd(got, want, bound, what):
+    """|got - want| <= 2 * bound elementwise; returns the worst ratio."""
+    got = np.asarray(got, dtype=np.float64)
+    assert not np.isnan(got).any(), f"{what}: NaN"
+    err = np.abs(got - want)
+    lim = 2 * bound + 1e-30
+    bad = err > lim
+    if bad.any():
+        idx = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} elements over the bound; first at "
+                             f"{tuple(int(x) for x in idx)}: got {got[tuple(idx)]:.6g} "
+                             f"want {want[tuple(idx)]:.6g} bound {lim[tuple(idx)]:.3g}")
+    return float(np.max(err / lim)) if err.size else 0.0

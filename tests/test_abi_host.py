@@ -138,3 +138,52 @@ def test_fwd_empty_problem_is_a_no_op():
     # B*H*N == 0: nothing to compute, so OK without touching any pointer.
     assert call(q=None, k=None, v=None, o=None, lse=None, shape=(0, 2, 16, 16, 64))[0] == "FA_OK"
     assert call(q=None, k=None, v=None, o=None, lse=None, shape=(1, 2, 0, 16, 64))[0] == "FA_OK"
+
+
+def bwd_call(shape=(1, 2, 16, 16, 64), dt=fa.BF16, scale=0.125, causal=0, ws=P, ws_len=None,
+             **ptrs):
+    names = ["q", "k", "v", "o", "lse", "do", "kvl", "dq", "dk", "dv"]
+    vals = {n: P for n in names}
+    vals["kvl"] = None
+    vals.update(ptrs)
+    if ws_len is None:
+        ws_len = fa.bwd_workspace_bytes(*shape)
+    L = fa.lib()
+    st = L.fa_bwd(*[vals[n] for n in names], Shape(*shape), dt, scale, causal, ws, ws_len, None)
+    return L.fa_status_str(st).decode(), L.fa_last_error().decode()
+
+
+def test_bwd_workspace_size():
+    # Lg and D per row, rows rounded up to 256
+    assert fa.bwd_workspace_bytes(2, 32, 8192, 8192, 128) == 2 * 32 * 8192 * 8
+    assert fa.bwd_workspace_bytes(1, 3, 300, 10, 64) == 3 * 512 * 8
+    assert fa.bwd_workspace_bytes(1, 1, 0, 10, 64) == 0
+    assert fa.bwd_workspace_bytes(1, 1, 16, 16, 64, dtype=fa.F32) == 0
+
+
+def test_bwd_rejects_before_launch():
+    for name in ("q", "o", "lse", "do", "dq", "k", "v", "dk", "dv"):
+        assert bwd_call(**{name: None})[0] == "FA_ERR_NULL", name
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        assert bwd_call(**{name: P + 8})[0] == "FA_ERR_ALIGN", name
+    assert bwd_call(lse=P + 2)[0] == "FA_ERR_ALIGN"
+    assert bwd_call(kvl=P + 1)[0] == "FA_ERR_ALIGN"
+    assert bwd_call(dt=fa.F32)[0] == "FA_ERR_UNSUPPORTED"
+    assert bwd_call(shape=(1, 2, 16, 16, 80))[0] == "FA_ERR_UNSUPPORTED"
+    assert bwd_call(shape=(1, 2, -3, 16, 64))[0] == "FA_ERR_SHAPE"
+    # Q/dO (or K/V) bytes per (batch, head) must stay below 2^31
+    assert bwd_call(shape=(1, 1, 1 << 23, 16, 128))[0] == "FA_ERR_UNSUPPORTED"
+    assert bwd_call(shape=(1, 1, 16, 1 << 23, 128))[0] == "FA_ERR_UNSUPPORTED"
+    for bad in (float("nan"), float("inf"), -1.0):
+        assert bwd_call(scale=bad)[0] == "FA_ERR_ARG"
+    st, msg = bwd_call(ws=None)
+    assert st == "FA_ERR_WORKSPACE" and "workspace" in msg
+    need = fa.bwd_workspace_bytes(1, 2, 16, 16, 64)
+    assert bwd_call(ws_len=need - 1)[0] == "FA_ERR_WORKSPACE"
+    assert bwd_call(ws=P + 16)[0] == "FA_ERR_ALIGN"
+
+
+def test_bwd_empty_problem_is_a_no_op():
+    none = {n: None for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")}
+    assert bwd_call(shape=(0, 2, 16, 16, 64), ws=None, **none)[0] == "FA_OK"
+    assert bwd_call(shape=(1, 2, 0, 0, 64), ws=None, **none)[0] == "FA_OK"

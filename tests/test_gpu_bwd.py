@@ -1,0 +1,136 @@
+"""GPU parity of the backward: the HIP kernels through the C ABI against the
+fp64 oracle (``oracle.backward``) on the same seeded inputs.
+
+The forward runs first on the GPU; its O and LSE are what the backward is
+given.  Each gradient element must lie within twice the elementwise bound
+that ``gpu_helpers.bwd_bound`` derives from the kernels' arithmetic; masked
+keys get exactly zero gradients and rows with no visible key exactly zero dQ.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import exact_attention_33_amd as fa
+from exact_attention_33_amd import inputs
+from oracle.attention import clamp_kv_len
+from oracle.backward import head_backward
+from tests.gpu_helpers import bwd_bound, compare_bwd, host64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(B, H, N, M, D, causal, kv_len, seed, device, poison=True):
+    import torch
+    q, k, v = inputs.qkv_device(seed, B, H, N, M, D, "bf16", device)
+    do = inputs.grad_device(seed + 1000, B, H, N, D, "bf16", device)
+    kvt = None
+    if kv_len is not None:
+        kvt = torch.tensor(kv_len, dtype=torch.int32, device=device)
+        if poison:
+            inputs.poison_tail(k, v, kv_len)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = fa.fwd(q, k, v, scale=scale, causal=causal, kv_len=kvt)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale=scale, causal=causal, kv_len=kvt)
+    torch.cuda.synchronize()
+    return dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, scale=scale)
+
+
+def _check_head(t, b, h, causal, kvl, what):
+    q, k, v, do = (host64(t[n][b, h]) for n in ("q", "k", "v", "do"))
+    k = np.where(np.isnan(k), 0.0, k)          # the poisoned tail is never read
+    v = np.where(np.isnan(v), 0.0, v)
+    O_gpu, L_gpu = host64(t["o"][b, h]), host64(t["lse"][b, h])
+    r = head_backward(q, k, v, do, t["scale"], causal, kvl)
+    # the exact forward's LSE for the same head
+    S = t["scale"] * (q @ k[:kvl].T)
+    N = q.shape[0]
+    from oracle.attention import visible_mask
+    S = np.where(visible_mask(N, kvl, causal), S, -np.inf)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        m = S.max(axis=1) if kvl else np.full(N, -np.inf)
+        L_ref = np.where(np.isfinite(m), m + np.log(np.sum(np.exp(S - m[:, None]), axis=1)), -np.inf) \
+            if kvl else np.full(N, -np.inf)
+    bq, bk, bv = bwd_bound(r, q, k, v, do, O_gpu, L_gpu, L_ref, t["scale"])
+    dq, dk, dv = (host64(t[n][b, h]) for n in ("dq", "dk", "dv"))
+    worst = [compare_bwd(dq, r["dq"], bq, f"{what} dQ"),
+             compare_bwd(dk, r["dk"], bk, f"{what} dK"),
+             compare_bwd(dv, r["dv"], bv, f"{what} dV")]
+    # exact zeros where the definition gives exact zeros
+    assert np.all(dk[kvl:] == 0) and np.all(dv[kvl:] == 0), f"{what}: masked keys"
+    assert np.all(dq[np.isneginf(L_ref)] == 0), f"{what}: rows with no visible key"
+    return max(worst)
+
+
+CASES = [
+    # B, H, N, M, D, causal, kv_len
+    (1, 2, 128, 128, 128, False, None),
+    (1, 2, 128, 128, 128, True, None),
+    (2, 3, 200, 200, 64, True, None),           # ragged: not a multiple of 64
+    (1, 2, 70, 300, 128, False, None),          # N != M, both ragged
+    (2, 2, 96, 333, 128, True, [333, 150]),     # bottom-right causal with kv_len
+    (2, 2, 300, 100, 64, True, None),           # N > M: early rows see no key
+    (1, 1, 1, 513, 128, False, None),           # one query
+    (2, 2, 257, 257, 128, True, [0, 257]),      # an empty batch
+    (1, 1, 600, 700, 64, False, [650]),
+    (1, 2, 520, 520, 128, True, None),          # several key tiles and query stages
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}N{}M{}D{}{}{}".format(
+    *c[:5], "c" if c[5] else "", "kv" if c[6] else ""))
+def test_bwd_matches_oracle(case):
+    import torch
+    B, H, N, M, D, causal, kv_len = case
+    dev = torch.device("cuda:0")
+    print(f"[bwd] case {case}", flush=True)
+    t = _run(B, H, N, M, D, causal, kv_len, seed=40 + N + M, device=dev)
+    kvs = clamp_kv_len(kv_len, B, M)
+    for b in range(B):
+        for h in range(H):
+            _check_head(t, b, h, causal, kvs[b], f"{case} b{b} h{h}")
+
+
+def test_bwd_degenerate_sizes():
+    """M = 0: dQ = 0; N = 0: dK = dV = 0; both written by the kernels."""
+    import torch
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 2, 40, 64, device=dev).to(torch.bfloat16)
+    e = torch.empty(1, 2, 0, 64, device=dev, dtype=torch.bfloat16)
+    lse = torch.full((1, 2, 40), float("-inf"), device=dev)
+    o = torch.zeros_like(q)
+    dq, dk, dv = fa.bwd(q, e, e, o, lse, q.clone(), dq=torch.full_like(q, 7.0))
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0)
+    kk = torch.randn(1, 2, 50, 64, device=dev).to(torch.bfloat16)
+    dq, dk, dv = fa.bwd(e, kk, kk, e, torch.empty(1, 2, 0, device=dev), e,
+                        dk=torch.full_like(kk, 7.0), dv=torch.full_like(kk, 7.0))
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_bwd_is_deterministic():
+    import torch
+    dev = torch.device("cuda:0")
+    t = _run(2, 4, 1000, 1000, 128, True, None, seed=77, device=dev)
+    dq, dk, dv = fa.bwd(t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, t["dq"]) and torch.equal(dk, t["dk"]) and torch.equal(dv, t["dv"])
+
+
+@pytest.mark.parametrize("name,causal,heads", [
+    ("prefill_small", True, [(0, h) for h in range(8)]),
+    ("prefill_mid", True, [(0, 0), (3, 15)]),
+    ("prefill_mid", False, [(1, 7)]),
+    ("prefill_long_d64", True, [(1, 31)]),
+    ("prefill_long_d128", True, [(0, 0)]),
+])
+def test_bwd_workloads_sampled_heads(name, causal, heads):
+    """The prefill workloads at full size; the oracle checks whole heads."""
+    import torch
+    w = inputs.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    print(f"[bwd] workload {name} causal={causal}", flush=True)
+    t = _run(w.B, w.H, w.N, w.M, w.D, causal, None, seed=w.seed, device=dev)
+    for b, h in heads:
+        _check_head(t, b, h, causal, w.M, f"{name} b{b} h{h}")
