@@ -4,7 +4,9 @@
 One step is one pass of the whole hot path over one batch of synthetic input:
   1. the fused prefill forward (bf16, causal) on B=2, H=32, N=M=8192, D=128;
   2. the split-KV decode (partial + merge kernels) on B=32 sequences, H=32,
-     N=1, D=128, per-sequence KV length uniform in [1024, 32768].
+     N=1, D=128, per-sequence KV length uniform in [1024, 32768];
+  3. the backward of the prefill (row statistic, dK/dV and dQ kernels) for an
+     upstream gradient dO ~ N(0, 1), reported beside the forward.
 Inputs are N(0, 1) drawn on the device from fixed seeds and are resident in
 HBM before timing starts.
 
@@ -43,7 +45,8 @@ def kernel_source_sha(files):
 
 
 SOURCES = {"prefill": ["prefill_bf16.hip", "device_common.h", "fa_internal.h"],
-           "decode": ["decode_bf16.hip", "device_common.h", "fa_internal.h"]}
+           "decode": ["decode_bf16.hip", "device_common.h", "fa_internal.h"],
+           "backward": ["bwd_bf16.hip", "device_common.h", "fa_internal.h"]}
 
 
 def measured_traffic(kind):
@@ -64,7 +67,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "copy"], default="all",
                     help="run one leg only (for counter runs); 'copy' runs a plain "
                          "device copy of known size for counter calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,6 +109,7 @@ def main():
     wd = inputs.WORKLOADS["decode"]
     do_p = args.only in ("all", "prefill")
     do_d = args.only in ("all", "decode")
+    do_b = args.only in ("all", "backward")
 
     # ---- inputs, resident in HBM before timing ----
     if do_p:
@@ -126,6 +130,20 @@ def main():
         scale_d = 1.0 / math.sqrt(wd.D)
         kv_bytes = float(kvl_h.astype(np.int64).sum()) * wd.H * wd.D * 2 * 2
         plan_d = fa.plan(wd.B, wd.H, 1, Md, wd.D)
+    if do_b:
+        # backward of the same causal prefill: the forward's O and LSE, an
+        # upstream gradient dO ~ N(0, 1), and the gradient buffers
+        if not do_p:
+            qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
+            scale_p = 1.0 / math.sqrt(wp.D)
+        ob, lb = fa.fwd(qp, kp, vp, scale=scale_p, causal=True)
+        gb = inputs.grad_device(wp.seed + 1000, wp.B, wp.H, wp.N, wp.D, "bf16", dev)
+        dqb, dkb, dvb = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
+        wsb = torch.empty(fa.bwd_workspace_bytes(wp.B, wp.H, wp.N, wp.M, wp.D), dtype=torch.uint8,
+                          device=dev)
+        # five tile products (S recomputed, dP, dV, dK, dQ) of 2 N M D each,
+        # halved for causal: 2.5 x the forward's count
+        flop_b = 10.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0
     torch.cuda.synchronize()
 
     def step(evs=None):
@@ -139,11 +157,16 @@ def main():
                 fa.fwd(qd, kd, vd, scale=scale_d, causal=False, kv_len=kvl_d, out=od, lse=ld,
                        workspace=ws, stream=stream)
                 if evs: evs[3].record(stream)
+            if do_b:
+                if evs: evs[4].record(stream)
+                fa.bwd(qp, kp, vp, ob, lb, gb, scale=scale_p, causal=True, dq=dqb, dk=dkb,
+                       dv=dvb, workspace=wsb, stream=stream)
+                if evs: evs[5].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -152,6 +175,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_p = [e[0].elapsed_time(e[1]) for e in events] if do_p else []
     ms_d = [e[2].elapsed_time(e[3]) for e in events] if do_d else []
+    ms_b = [e[4].elapsed_time(e[5]) for e in events] if do_b else []
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": 1e3 * wall / max(1, args.steps), "higher_is_better": True,
@@ -185,11 +209,29 @@ def main():
                                       "traffic": measured_traffic("decode")}}
         if not do_p:
             out.update({"value": gbs, "unit": "GB/s"})
+    if do_b:
+        avg_b = sum(ms_b) / len(ms_b)
+        tfb = flop_b / (avg_b * 1e-3) / 1e12
+        out["backward"] = {"ms_mean": avg_b, "ms_min": min(ms_b), "value": tfb, "unit": "TFLOP/s",
+                           "frac_bf16_peak": tfb / PEAK_BF16_TFLOPS, "flop_per_call": flop_b,
+                           "flop_convention": "10 B H N M D / 2 (S recomputed, dP, dV, dK, dQ; "
+                                              "causal halved)",
+                           "roofline": {"bound": "mfma",
+                                        "kernel": "fa_bwd: rowstat + dkdv + dq (whole call)",
+                                        "achieved": tfb, "peak": PEAK_BF16_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": tfb / PEAK_BF16_TFLOPS,
+                                        "traffic": measured_traffic("backward")}}
+        cfg["backward"] = {"B": wp.B, "H": wp.H, "N": wp.N, "M": wp.M, "D": wp.D, "causal": True,
+                           "dO": "N(0,1), seed %d" % (wp.seed + 1000)}
+        if not do_p and not do_d:
+            out.update({"value": tfb, "unit": "TFLOP/s"})
     out["config"] = cfg
 
     if not args.no_cpu_baseline and args.only == "all":
         out["cpu_baseline"] = cpu_baseline(args, np, torch, qp, kp, vp, op, lp, scale_p, wp,
                                            qd, kd, vd, od, ld, kvl_h, scale_d, wd)
+        out["cpu_baseline"]["backward"] = cpu_baseline_bwd(np, qp, kp, vp, gb, dqb, dkb, dvb,
+                                                           scale_p, wp)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -240,6 +282,25 @@ def cpu_baseline(args, np, torch, qp, kp, vp, op, lp, scale_p, wp, qd, kd, vd, o
                      "sample": f"{len(dh)} (batch, head) pairs of the bench's decode tensors",
                      "parity_vs_gpu": {"O_max_abs": eo, "LSE_max_abs": el, "tol": [2e-2, 1e-3]}}
     return res
+
+
+def cpu_baseline_bwd(np, qp, kp, vp, gb, dqb, dkb, dvb, scale_p, wp, heads=((0, 0),)):
+    """The backward oracle timed on whole heads of the bench's tensors."""
+    from oracle.backward import head_backward
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    t_cpu, err = 0.0, {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b, h in heads:
+        q, k, v, g = f64(qp[b, h]), f64(kp[b, h]), f64(vp[b, h]), f64(gb[b, h])
+        t0 = time.perf_counter()
+        r = head_backward(q, k, v, g, scale_p, True, wp.M)
+        t_cpu += time.perf_counter() - t0
+        for n, t in (("dq", dqb), ("dk", dkb), ("dv", dvb)):
+            err[n] = max(err[n], float(np.max(np.abs(f64(t[b, h]) - r[n]))))
+    flop = len(heads) * 10.0 * wp.N * wp.M * wp.D / 2.0
+    return {"value": flop / t_cpu / 1e12, "unit": "TFLOP/s", "seconds": t_cpu,
+            "sample": f"{len(heads)} whole head(s) (N=M=8192, D=128, causal) of the bench's "
+                      "backward tensors, fp64 NumPy, same FLOP convention",
+            "max_abs_vs_gpu": err}
 
 
 if __name__ == "__main__":
