@@ -30,7 +30,7 @@ PATH_NAMES = {PATH_PREFILL: "prefill", PATH_SPLITKV: "splitkv", PATH_F32: "f32"}
 
 # Every symbol include/fa_mi355x.h declares.
 EXPORTS = ["fa_plan_query", "fa_fwd_workspace_bytes", "fa_fwd", "fa_fwd_ex",
-           "fa_bwd_workspace_bytes", "fa_bwd",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_ex",
            "fa_status_str", "fa_last_error", "fa_abi_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,7 +50,9 @@ class Shape(ctypes.Structure):
 
 
 class Options(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("split_keys", ctypes.c_int32)]
+    _fields_ = [("path", ctypes.c_int32), ("split_keys", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("window_right", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -87,6 +89,8 @@ def lib():
     L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.fa_bwd.argtypes = [vp] * 10 + [Shape, i32, f32, i32, vp, ctypes.c_size_t, vp]
     L.fa_bwd.restype = i32
+    L.fa_bwd_ex.argtypes = L.fa_bwd.argtypes + [ctypes.POINTER(Options)]
+    L.fa_bwd_ex.restype = i32
     L.fa_status_str.argtypes = [i32]
     L.fa_status_str.restype = ctypes.c_char_p
     L.fa_last_error.argtypes = []
@@ -103,20 +107,25 @@ def _check(st):
         raise FaError(st, L.fa_status_str(st).decode(), L.fa_last_error().decode())
 
 
-def _options(path, split_keys):
-    if path in (None, PATH_AUTO) and not split_keys:
+def _options(path, split_keys, window=None):
+    """fa_options for the call, or None for the defaults.  ``window`` is None
+    or (left, right): key j visible to query i only if
+    i + off - left <= j <= i + off + right (off = kv_len - N)."""
+    if path in (None, PATH_AUTO) and not split_keys and window is None:
         return None
-    return Options(PATH_AUTO if path is None else int(path), int(split_keys or 0))
+    wl, wr = (int(window[0]), int(window[1])) if window is not None else (0, 0)
+    return Options(PATH_AUTO if path is None else int(path), int(split_keys or 0),
+                   1 if window is not None else 0, wl, wr)
 
 
 def _opt_ptr(o):
     return ctypes.byref(o) if o is not None else None
 
 
-def plan(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0):
+def plan(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0, window=None):
     """The planner's decision for a shape, as a dict (host only)."""
     info = PlanInfo()
-    o = _options(path, split_keys)
+    o = _options(path, split_keys, window)
     _check(lib().fa_plan_query(Shape(B, H, N, M, D), int(dtype), int(bool(causal)),
                                _opt_ptr(o), ctypes.byref(info)))
     d = {f: getattr(info, f) for f, _ in PlanInfo._fields_}
@@ -124,8 +133,9 @@ def plan(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0):
     return d
 
 
-def workspace_bytes(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0):
-    o = _options(path, split_keys)
+def workspace_bytes(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0,
+                    window=None):
+    o = _options(path, split_keys, window)
     return int(lib().fa_fwd_workspace_bytes(Shape(B, H, N, M, D), int(dtype),
                                             int(bool(causal)), _opt_ptr(o)))
 
@@ -140,8 +150,12 @@ def _dtype_code(t):
 
 
 def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
-        workspace=None, path=None, split_keys=0, stream=None):
-    """Exact attention forward through the C ABI; returns (O, LSE)."""
+        workspace=None, path=None, split_keys=0, window=None, stream=None):
+    """Exact attention forward through the C ABI; returns (O, LSE).
+
+    ``window=(left, right)`` restricts query i to keys
+    i + off - left .. i + off + right (off = kv_len - N; causal caps right
+    at 0): ``causal=True, window=(127, 0)`` is a 128-wide local window."""
     import torch
     L = lib()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -171,7 +185,7 @@ def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
         out = torch.empty((B, H, N, D), dtype=q.dtype, device=dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    opts = _options(path, split_keys)
+    opts = _options(path, split_keys, window)
     shape = Shape(B, H, N, M, D)
     ws_need = int(L.fa_fwd_workspace_bytes(shape, dt, int(bool(causal)), _opt_ptr(opts)))
     if ws_need and workspace is None:
@@ -194,7 +208,7 @@ def bwd_workspace_bytes(B, H, N, M, D, dtype=BF16, causal=False):
 
 
 def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_len=None, *, dq=None, dk=None,
-        dv=None, workspace=None, stream=None):
+        dv=None, workspace=None, window=None, stream=None):
     """Gradients of the forward through the C ABI; returns (dQ, dK, dV).
 
     ``o`` and ``lse`` must be what ``fwd`` returned for the same q, k, v,
@@ -241,9 +255,10 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_len=None, *, dq=None, 
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    st = L.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                  do.data_ptr(), kv_len.data_ptr() if kv_len is not None else None,
-                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), shape, dt, float(scale),
-                  int(bool(causal)), ws_ptr, ws_len, sptr or None)
+    opts = _options(None, 0, window)
+    st = L.fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     do.data_ptr(), kv_len.data_ptr() if kv_len is not None else None,
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), shape, dt, float(scale),
+                     int(bool(causal)), ws_ptr, ws_len, sptr or None, _opt_ptr(opts))
     _check(st)
     return dq, dk, dv

@@ -23,6 +23,10 @@ struct Problem {
   int32_t B, H, N, M, D;
   float scale;
   int causal;
+  // Local window (options.window): key j visible to query i only if
+  // i + off - wl <= j <= i + off + wr, off = kv_len - N.  window == 0: none.
+  int window;
+  int32_t wl, wr;
 };
 
 // Planner output (host-only; see plan.cpp).
@@ -92,6 +96,8 @@ struct BwdProblem {
   int32_t B, H, N, M, D, Npad;
   float scale;
   int causal;
+  int window;            // as in Problem
+  int32_t wl, wr;
 };
 
 constexpr int kBwdThreads = 256;

@@ -33,8 +33,14 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(Problem p, int n_q
   const int i = qt * BQ + r;
   const int kvl = clamp_kv(p.kv_len, b, M);
   const int off = kvl - N;  // causal: key j visible to query i iff j <= i + off
+  // Local window: query i sees keys i + off - wl .. i + off + wr only; causal
+  // caps wr at 0.
+  const bool upper = p.causal || p.window;
+  const int wl = p.window ? min(p.wl, N + kvl) : 0;
+  const int wr = p.causal ? 0 : (p.window ? min(p.wr, N + kvl) : 0);
   const int i_last = min(qt * BQ + BQ, N) - 1;
-  const int kv_end = p.causal ? min(kvl, i_last + off + 1) : kvl;
+  const int kv_end = upper ? min(kvl, i_last + off + wr + 1) : kvl;
+  const int kv_start = p.window ? max(0, qt * BQ + off - wl) / BK * BK : 0;
 
   const float* Q = (const float*)p.q + (size_t)bh * N * D;
   const float* K = (const float*)p.k + (size_t)bh * M * D;
@@ -49,7 +55,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(Problem p, int n_q
   double m = -INFINITY, l = 0.0;
   const double sc = (double)p.scale;
 
-  for (int j0 = 0; j0 < kv_end; j0 += BK) {
+  for (int j0 = kv_start; j0 < kv_end; j0 += BK) {
     __syncthreads();
     for (int c = threadIdx.x; c < BK * D / 4; c += kF32Threads) {
       const int key = c / (D / 4), dc = c % (D / 4);
@@ -75,7 +81,8 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(Problem p, int n_q
       part += __shfl_xor(part, 2, 16);
       part += __shfl_xor(part, 1, 16);
       const int key = j0 + jj;
-      const bool vis = key < kvl && (!p.causal || key <= i + off);
+      const bool vis = key < kvl && (!upper || key <= i + off + wr) &&
+                       (!p.window || key >= i + off - wl);
       s[jj] = vis ? part * sc : -INFINITY;
       mx = fmax(mx, s[jj]);
     }

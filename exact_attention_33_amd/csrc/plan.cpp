@@ -59,6 +59,15 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
     *why = "options.split_keys must be 0 or a positive multiple of 64";
     return FA_ERR_ARG;
   }
+  const bool window = opt && opt->window;
+  if (opt && (opt->window != 0 && opt->window != 1)) {
+    *why = "options.window must be 0 or 1";
+    return FA_ERR_ARG;
+  }
+  if (window && (opt->window_left < 0 || opt->window_right < 0)) {
+    *why = "options.window_left and window_right must be >= 0";
+    return FA_ERR_ARG;
+  }
   // Element counts must fit comfortably in 64-bit byte offsets.
   const int64_t bh = (int64_t)s.B * s.H;
   if (bh > INT32_MAX || (bh > 0 && ((int64_t)s.N * s.D > INT64_MAX / 8 / bh ||
@@ -83,7 +92,13 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
       *why = "FA_PATH_SPLITKV needs N == 1 (one query per sequence)";
       return FA_ERR_UNSUPPORTED;
     }
-    path = req == FA_PATH_AUTO ? (s.N == 1 ? FA_PATH_SPLITKV : FA_PATH_PREFILL)
+    if (req == FA_PATH_SPLITKV && window) {
+      *why = "FA_PATH_SPLITKV has no window; a windowed query runs on FA_PATH_PREFILL";
+      return FA_ERR_UNSUPPORTED;
+    }
+    // A window bounds a query's keys, so one query is cheap on the prefill
+    // kernel; the split-KV path streams whole caches.
+    path = req == FA_PATH_AUTO ? (s.N == 1 && !window ? FA_PATH_SPLITKV : FA_PATH_PREFILL)
                                : (fa_path)req;
   }
 

@@ -128,7 +128,7 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 __device__ __forceinline__ void mfma_guard() { asm volatile("s_nop 7\n\ts_nop 7"); }
 
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_bf16_kernel(Problem p, int n_qtiles) {
   constexpr int BQ = kPrefillBlockQ, BK = kPrefillBlockK;
@@ -173,13 +173,21 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   const int q0 = qt * BQ;
   const int qw0 = q0 + QW * ws;  // first query of this wave
   const int off = kvl - N;       // key j visible to query i iff j < kvl and (!causal or j <= i + off)
+  // Local window: query i sees keys i + off - wl .. i + off + wr only; causal
+  // caps wr at 0.  (Clamped so that no bound overflows.)
+  constexpr bool UPPER = CAUSAL || WINDOW;   // rows have a last key before kvl - 1
+  const int wl = WINDOW ? min(p.wl, N + kvl) : 0;
+  const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
   const int q_last = min(q0 + BQ, N) - 1;
-  const int kv_end = CAUSAL ? min(kvl, q_last + off + 1) : kvl;
-  const int n_tiles = kv_end > 0 ? (kv_end + BK - 1) / BK : 0;
+  const int kv_end = UPPER ? min(kvl, q_last + off + wr + 1) : kvl;
+  // Window: tiles before the first query's first key are never visited; the
+  // K/V descriptors start at tile t0, so the loop counts tiles from there.
+  const int t0 = WINDOW ? max(0, q0 + off - wl) / BK : 0;
+  const int n_tiles = kv_end > t0 * BK ? (kv_end + BK - 1) / BK - t0 : 0;
 
   const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
-  const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D;
-  const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D;
+  const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D + (size_t)t0 * BK * D;
+  const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D + (size_t)t0 * BK * D;
 
   // ---- tile loads ----
   // Slot s of a padded tile holds row s / CH, chunk s % CH; slots on the
@@ -211,7 +219,7 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
     voff[i / 2] = slot_off(ws + i * NW, VCH) | (i + 1 < VPW ? slot_off(ws + (i + 1) * NW, VCH) << 16 : 0u);
   // K and V bytes this (batch, head) may read; the planner keeps M * D * 2
   // below 2^31, so every offset below fits 32 bits.
-  const int nrec = kvl * ROWB;
+  const int nrec = (kvl - t0 * BK) * ROWB;
   // Block i of this wave: its slots of tile t of src into dst.  The wave's
   // block offset goes through an empty asm so that the compiler forms each
   // LDS address next to its load instead of keeping all of them (three
@@ -296,7 +304,9 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // the workgroup's last one, whose LDS holds stale data -- are masked
   // element by element; every other tile is fully visible to the wave.
   auto need_mask = [&](int t) {
-    return (t * BK + BK > kvl) || (CAUSAL && t * BK + BK - 1 > qw0 + off);
+    const int k0 = (t + t0) * BK;
+    return (k0 + BK > kvl) || (UPPER && k0 + BK - 1 > qw0 + off + wr) ||
+           (WINDOW && k0 < qw0 + QW - 1 + off - wl);
   };
 
   // ---- softmax of one tile, in small units that the pipeline spreads out ----
@@ -437,18 +447,24 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // a sign mask and a bit insert, not a compare: a compare per score writes a
   // scalar register pair, and the compiler would keep dozens of them live.
   auto apply_mask = [&](int t, f32x16 (&s)[NKB][NQB]) {
+    const int k0 = (t + t0) * BK;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qrow = qw0 + 32 * qb + ql;
-      const int lim = CAUSAL ? min(kvl - 1, qrow + off) : kvl - 1;  // last visible key
+      const int lim = UPPER ? min(kvl - 1, qrow + off + wr) : kvl - 1;  // last visible key
+      const int lo = qrow + off - wl;                                   // first (window)
 #pragma unroll
-      for (int nb = 0; nb < NKB; ++nb) vis[nb][qb] = lim >= t * BK + 32 * nb;
-      const int base = lim - (t * BK + 4 * hl);  // >= 0 iff key k0 + 4 hl is visible
+      for (int nb = 0; nb < NKB; ++nb)
+        vis[nb][qb] = lim >= k0 + 32 * nb && (!WINDOW || lo <= k0 + 32 * nb + 31);
+      const int base = lim - (k0 + 4 * hl);  // >= 0 iff key k0 + 4 hl is visible
+      const int base_lo = k0 + 4 * hl - lo;  // >= 0 iff key k0 + 4 hl is past the window start
 #pragma unroll
       for (int nb = 0; nb < NKB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t hide = (uint32_t)((base - (nb * 32 + 8 * (r / 4) + (r % 4))) >> 31);
+          const int idx = nb * 32 + 8 * (r / 4) + (r % 4);
+          uint32_t hide = (uint32_t)((base - idx) >> 31);
+          if constexpr (WINDOW) hide |= (uint32_t)((base_lo + idx) >> 31);
           const uint32_t v = __float_as_uint(s[nb][qb][r]);
           s[nb][qb][r] = __uint_as_float((hide & 0xFF800000u) | (~hide & v));
         }
@@ -636,19 +652,26 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   }
 }
 
+template <int D>
+void launch_prefill_d(const Problem& p, dim3 grid, hipStream_t stream, int n_qtiles) {
+  const dim3 block(kPrefillThreads);
+  if (p.window) {
+    if (p.causal) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), grid, block, 0, stream, p, n_qtiles);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), grid, block, 0, stream, p, n_qtiles);
+  } else {
+    if (p.causal) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), grid, block, 0, stream, p, n_qtiles);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), grid, block, 0, stream, p, n_qtiles);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, hipStream_t stream) {
   if (plan.grid == 0) return hipSuccess;
   const int n_qtiles = (p.N + kPrefillBlockQ - 1) / kPrefillBlockQ;
-  const dim3 grid((unsigned)plan.grid), block(kPrefillThreads);
-  if (p.D == 64) {
-    if (p.causal) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, p, n_qtiles);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, p, n_qtiles);
-  } else {
-    if (p.causal) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, p, n_qtiles);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, p, n_qtiles);
-  }
+  const dim3 grid((unsigned)plan.grid);
+  if (p.D == 64) launch_prefill_d<64>(p, grid, stream, n_qtiles);
+  else launch_prefill_d<128>(p, grid, stream, n_qtiles);
   return hipGetLastError();
 }
 

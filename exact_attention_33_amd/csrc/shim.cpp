@@ -109,7 +109,9 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v,
       return fail(FA_ERR_ALIGN, "fa_fwd: workspace must be 256-byte aligned");
   }
 
-  fa::Problem p{q, k, v, kv_len, o, lse, s.B, s.H, s.N, s.M, s.D, scale, causal ? 1 : 0};
+  const bool win = opt && opt->window;
+  fa::Problem p{q, k, v, kv_len, o, lse, s.B, s.H, s.N, s.M, s.D, scale, causal ? 1 : 0,
+                win ? 1 : 0, win ? opt->window_left : 0, win ? opt->window_right : 0};
   hipStream_t hs = (hipStream_t)stream;
   hipError_t err = hipSuccess;
   switch (plan.path) {
@@ -142,6 +144,21 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const void* dout, const int32_t* kv_len, void* dq, void* dk, void* dv,
                  fa_shape s, fa_dtype dtype, float scale, int causal,
                  void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_ex(q, k, v, o, lse, dout, kv_len, dq, dk, dv, s, dtype, scale, causal, workspace,
+                   workspace_bytes, stream, nullptr);
+}
+
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, const int32_t* kv_len, void* dq,
+                    void* dk, void* dv, fa_shape s, fa_dtype dtype, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    const fa_options* opt) {
+  if (opt && opt->window != 0 && opt->window != 1)
+    return fail(FA_ERR_ARG, "fa_bwd: options.window must be 0 or 1");
+  const bool win = opt && opt->window;
+  if (win && (opt->window_left < 0 || opt->window_right < 0))
+    return fail(FA_ERR_ARG, "fa_bwd: options.window_left and window_right must be >= 0");
+  if (win) return fail(FA_ERR_UNSUPPORTED, "fa_bwd: the backward kernels take no window");
   if (s.B < 0 || s.H < 0 || s.N < 0 || s.M < 0 || s.D < 0)
     return fail(FA_ERR_SHAPE, "fa_bwd: B, H, N, M and D must be non-negative");
   if (dtype != FA_BF16)
@@ -185,7 +202,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
       return fail(FA_ERR_ALIGN, "fa_bwd: workspace must be 256-byte aligned");
   }
   fa::BwdProblem p{q, k, v, o, dout, lse, kv_len, dq, dk, dv, (float*)workspace,
-                   s.B, s.H, s.N, s.M, s.D, (int32_t)fa::bwd_npad(s.N), scale, causal ? 1 : 0};
+                   s.B, s.H, s.N, s.M, s.D, (int32_t)fa::bwd_npad(s.N), scale, causal ? 1 : 0,
+                   win ? 1 : 0, win ? opt->window_left : 0, win ? opt->window_right : 0};
   const hipError_t err = fa::launch_bwd_bf16(p, (hipStream_t)stream);
   if (err != hipSuccess)
     return fail(FA_ERR_HIP, "fa_bwd: launch failed: %s", hipGetErrorString(err));

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 
@@ -68,15 +68,29 @@ typedef struct { int32_t B, H, N, M, D; } fa_shape;
 typedef enum {
   FA_PATH_AUTO = 0,     /* planner's choice                                      */
   FA_PATH_PREFILL = 1,  /* fused tiled kernel, bf16 MFMA (bf16 only; K/V bytes
-                           per batch and head, M * D * 2, below 2^31)            */
-  FA_PATH_SPLITKV = 2,  /* split-KV partial kernel + log-sum-exp merge (bf16, N=1) */
+                           per batch and head, M * D * 2, below 2^31); with a
+                           window it also serves N = 1                           */
+  FA_PATH_SPLITKV = 2,  /* split-KV partial kernel + log-sum-exp merge (bf16, N=1,
+                           no window)                                             */
   FA_PATH_F32 = 3       /* float32 inputs/outputs, float64 internal arithmetic   */
 } fa_path;
 
-/* Optional controls; pass NULL for the planner's defaults. */
+/* Optional controls; pass NULL for the planner's defaults.  A zero-filled
+ * struct means the defaults too. */
 typedef struct {
   int32_t path;        /* fa_path                                                */
   int32_t split_keys;  /* split-KV: keys per split, a multiple of 64; 0 = auto   */
+  int32_t window;      /* 0: no window.  1: local (banded) attention: key j is
+                          visible to query i only if
+                            i + off - window_left <= j <= i + off + window_right
+                          with off = kv_len[b] - N (the causal alignment), in
+                          addition to j < kv_len[b] and the causal rule (which
+                          caps window_right at 0).  window_left = W - 1,
+                          window_right = 0 with causal gives each query the W
+                          most recent keys: "a 128-wide local window" is
+                          window_left = 127.                                    */
+  int32_t window_left;   /* >= 0, used when window == 1                         */
+  int32_t window_right;  /* >= 0, used when window == 1                         */
 } fa_options;
 
 /* What the planner decided for a shape (host-only, no device call). */
@@ -178,6 +192,15 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const void* dout, const int32_t* kv_len, void* dq, void* dk, void* dv,
                  fa_shape s, fa_dtype dtype, float scale, int causal,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_bwd_ex -- fa_bwd for a forward run with options `opt` (NULL = none):
+ * a window must be the one the forward used.  `path` and `split_keys` are
+ * ignored. */
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, const int32_t* kv_len, void* dq,
+                    void* dk, void* dv, fa_shape s, fa_dtype dtype, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    const fa_options* opt);
 
 /* Static name of a status code. */
 const char* fa_status_str(fa_status st);

@@ -28,6 +28,14 @@ Readings where the pages leave a step open (each listed in the design notes):
     exp(scale * q.k).
   * ``scale`` multiplies the score matrix; the value passed in is upcast to
     fp64 exactly, as are the inputs.
+  * local window ("FlashAttention: attention was never compute-bound", Exact
+    means exact, compares with "a 128-wide local window" without defining it):
+    ``window = (left, right)`` keeps key j for query i only if
+    i + off - left <= j <= i + off + right (off = kv_len - N, the causal
+    alignment); with ``causal`` the right bound is min(right, 0).  A causal
+    128-wide window is ``(127, 0)``: each query sees its 128 most recent keys.
+    It is an elementwise mask that does not depend on the scores, the kind
+    "Understanding FlashAttention", Attention, allows.
 """
 import numpy as np
 
@@ -45,17 +53,25 @@ def clamp_kv_len(kv_len, B, M):
     return [int(min(max(int(x), 0), M)) for x in kv]
 
 
-def visible_mask(N, kv_len_b, causal):
+def visible_mask(N, kv_len_b, causal, window=None):
     """Boolean [N, kv_len_b]: is key j visible to query i.
 
     Keys at or past ``kv_len_b`` are not part of the matrix at all.  With
     ``causal`` the bottom-right alignment applies: j <= i + (kv_len_b - N).
+    ``window = (left, right)`` further keeps only
+    i + off - left <= j <= i + off + right.
     """
     i = np.arange(N)[:, None]
     j = np.arange(kv_len_b)[None, :]
+    off = kv_len_b - N
     vis = np.ones((N, kv_len_b), dtype=bool)
     if causal:
-        vis &= j <= i + (kv_len_b - N)
+        vis &= j <= i + off
+    if window is not None:
+        left, right = (int(x) for x in window)
+        if left < 0 or right < 0:
+            raise ValueError("window bounds must be >= 0")
+        vis &= (j >= i + off - left) & (j <= i + off + right)
     return vis
 
 
@@ -80,7 +96,7 @@ def _scores(q, k, scale):
     return np.float64(scale) * (q @ k.T)
 
 
-def _head(q, k, v, scale, causal, kvl, rows=None):
+def _head(q, k, v, scale, causal, kvl, rows=None, window=None):
     """One (batch, head) problem.  q [N,D], k/v [M,D] fp64.
 
     Returns O [len(rows), D] and LSE [len(rows)] for the requested query rows
@@ -95,7 +111,7 @@ def _head(q, k, v, scale, causal, kvl, rows=None):
     if kvl == 0 or rows.size == 0:
         return O, LSE
     S = _scores(q[rows], k, scale)                      # step 1: materialise S
-    vis = visible_mask(N, kvl, causal)[rows]
+    vis = visible_mask(N, kvl, causal, window)[rows]
     S = np.where(vis, S, -np.inf)                       # step 2: mask
     for r in range(rows.size):                          # steps 3-5: softmax
         p, m, l = safe_softmax(S[r])
@@ -106,7 +122,7 @@ def _head(q, k, v, scale, causal, kvl, rows=None):
     return O, LSE
 
 
-def attention_ref(q, k, v, scale, causal=False, kv_len=None):
+def attention_ref(q, k, v, scale, causal=False, kv_len=None, window=None):
     """Exact attention forward for [B, H, N, D] / [B, H, M, D] inputs.
 
     Returns (O [B,H,N,D] fp64, LSE [B,H,N] fp64).
@@ -124,11 +140,11 @@ def attention_ref(q, k, v, scale, causal=False, kv_len=None):
     for b in range(B):
         for h in range(H):
             O[b, h], LSE[b, h] = _head(q[b, h], k[b, h], v[b, h], scale,
-                                       causal, kvs[b])
+                                       causal, kvs[b], window=window)
     return O, LSE
 
 
-def attention_rows(q, k, v, scale, causal, kv_len, picks):
+def attention_rows(q, k, v, scale, causal, kv_len, picks, window=None):
     """The same definition evaluated only for selected outputs.
 
     ``picks`` is a sequence of (b, h, i).  ``q`` may be [B,H,N,D] or a callable
@@ -152,7 +168,7 @@ def attention_rows(q, k, v, scale, causal, kv_len, picks):
             outO = np.zeros((len(picks), D))
         kvl = min(max(int(M if kv_len is None else np.asarray(kv_len).reshape(-1)[b]), 0), M)
         rows = [i for _, i in lst]
-        O, L = _head(qh, kh, vh, scale, causal, kvl, rows)
+        O, L = _head(qh, kh, vh, scale, causal, kvl, rows, window=window)
         for r, (idx, _) in enumerate(lst):
             outO[idx] = O[r]
             outL[idx] = L[r]

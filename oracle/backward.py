@@ -37,7 +37,7 @@ from .attention import clamp_kv_len, safe_softmax, visible_mask
 __all__ = ["head_backward", "attention_bwd_ref"]
 
 
-def head_backward(q, k, v, do, scale, causal, kvl):
+def head_backward(q, k, v, do, scale, causal, kvl, window=None):
     """One (batch, head) problem in fp64: q, do [N,D]; k, v [M,D].
 
     Returns a dict with the gradients ``dq`` [N,D], ``dk`` [M,D], ``dv``
@@ -51,7 +51,7 @@ def head_backward(q, k, v, do, scale, causal, kvl):
     kv, vv = k[:kvl], v[:kvl]
     # forward, as defined: scores, mask, row softmax, weighted sum of V
     S = np.float64(scale) * (q @ kv.T)
-    S = np.where(visible_mask(N, kvl, causal), S, -np.inf)
+    S = np.where(visible_mask(N, kvl, causal, window), S, -np.inf)
     P = np.zeros((N, kvl))
     for i in range(N):
         P[i] = safe_softmax(S[i])[0]      # a row with no visible key stays 0
@@ -72,7 +72,7 @@ def head_backward(q, k, v, do, scale, causal, kvl):
             "p": P, "dp": dP, "ds": dS, "o": O}
 
 
-def attention_bwd_ref(q, k, v, do, scale, causal=False, kv_len=None):
+def attention_bwd_ref(q, k, v, do, scale, causal=False, kv_len=None, window=None):
     """Gradients of O = attention(Q, K, V) for the upstream gradient dO.
 
     q, do [B,H,N,D]; k, v [B,H,M,D].  Returns (dQ, dK, dV, D) in fp64 with
@@ -90,6 +90,6 @@ def attention_bwd_ref(q, k, v, do, scale, causal=False, kv_len=None):
     delta = np.zeros((B, H, N))
     for b in range(B):
         for h in range(H):
-            r = head_backward(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, kvs[b])
+            r = head_backward(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, kvs[b], window)
             dQ[b, h], dK[b, h], dV[b, h], delta[b, h] = r["dq"], r["dk"], r["dv"], r["delta"]
     return dQ, dK, dV, delta

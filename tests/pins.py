@@ -22,9 +22,10 @@ def _rand(seed, B, H, N, M, D):
             rng.standard_normal((B, H, M, D)))
 
 
-def brute_force(q, k, v, scale, causal, kv_len):
+def brute_force(q, k, v, scale, causal, kv_len, window=None):
     """50-digit evaluation straight from the formula, without the max shift:
-    p_j = exp(s_j) / sum exp(s_j), O = sum p_j v_j, LSE = log sum exp(s_j)."""
+    p_j = exp(s_j) / sum exp(s_j), O = sum p_j v_j, LSE = log sum exp(s_j).
+    ``window = (left, right)``: only keys i + off - left .. i + off + right."""
     B, H, N, D = q.shape
     M = k.shape[2]
     O = np.zeros((B, H, N, D))
@@ -33,8 +34,10 @@ def brute_force(q, k, v, scale, causal, kv_len):
         kvl = M if kv_len is None else int(kv_len[b])
         for h in range(H):
             for i in range(N):
+                off = kvl - N
                 keys = [j for j in range(kvl)
-                        if not causal or j - (kvl - N) <= i]
+                        if (not causal or j <= i + off) and
+                        (window is None or i + off - window[0] <= j <= i + off + window[1])]
                 if not keys:
                     continue
                 s = {j: mpmath.mpf(scale) * mpmath.fsum(
@@ -197,10 +200,62 @@ def pin_scale_on_scores(attn):
     assert np.max(np.abs(O0 - O1)) <= 1e-14 and np.max(np.abs(L0 - L1)) <= 1e-14
 
 
+def pin_window_brute_force(attn):
+    """Local windows against 50-digit arithmetic: one-sided and two-sided
+    bands, causal and not, N != M, kv_len, windows wider than the sequence."""
+    cases = [
+        # seed, B, H, N, M, D, scale, causal, kv_len, window
+        (41, 1, 1, 8, 8, 3, 0.6, True, None, (2, 0)),
+        (42, 1, 1, 7, 9, 3, 0.8, False, None, (1, 2)),
+        (43, 2, 1, 4, 9, 3, 0.5, True, [9, 5], (3, 0)),
+        (44, 1, 2, 6, 6, 2, 1.1, False, None, (0, 0)),
+        (45, 1, 1, 5, 3, 3, 0.7, True, None, (1, 4)),   # N > M: empty rows
+        (46, 1, 1, 6, 6, 3, 0.9, True, None, (50, 50)),
+    ]
+    for seed, B, H, N, M, D, scale, causal, kvl, win in cases:
+        q, k, v = _rand(seed, B, H, N, M, D)
+        O, L = attn(q, k, v, scale, causal, kvl, window=win)
+        Ob, Lb = brute_force(q, k, v, scale, causal, kvl, window=win)
+        assert np.array_equal(np.isneginf(L), np.isneginf(Lb)), ("empty rows", seed)
+        fin = np.isfinite(Lb)
+        assert np.max(np.abs(O - Ob)) <= 4e-15, ("O vs brute force", seed)
+        assert np.max(np.abs(L[fin] - Lb[fin])) <= 4e-15, ("LSE vs brute force", seed)
+
+
+def pin_window_single_key(attn):
+    """window (0, 0): query i sees key i + off alone, so O_i = v_(i+off) and
+    LSE_i = s_(i,i+off) exactly; rows with i + off outside [0, kv_len) see
+    nothing."""
+    q, k, v = _rand(47, 1, 1, 6, 8, 4)
+    for kvl in (8, 5):
+        O, L = attn(q, k, v, 0.5, False, [kvl], window=(0, 0))
+        off = kvl - 6
+        for i in range(6):
+            j = i + off
+            if 0 <= j < kvl:
+                assert np.array_equal(O[0, 0, i], v[0, 0, j]), (kvl, i)
+                assert abs(L[0, 0, i] - 0.5 * q[0, 0, i] @ k[0, 0, j]) <= 1e-15
+            else:
+                assert L[0, 0, i] == -np.inf and not O[0, 0, i].any(), (kvl, i)
+
+
+def pin_window_locality(attn):
+    """A key outside row i's band does not change row i; one inside does."""
+    q, k, v = _rand(48, 1, 1, 10, 10, 3)
+    O, _ = attn(q, k, v, 0.7, True, None, window=(2, 0))
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 0, 3] += 5.0
+    v2[0, 0, 3] -= 3.0
+    O2, _ = attn(q, k2, v2, 0.7, True, None, window=(2, 0))
+    changed = np.abs(O2 - O).max(axis=-1)[0, 0] > 1e-12
+    assert changed.tolist() == [i in (3, 4, 5) for i in range(10)], changed
+
+
 ALL_ATTN_PINS = [pin_brute_force, pin_rows_sum_to_one, pin_causal_row0,
                  pin_uniform_scores, pin_overflow_shift, pin_single_and_two_keys,
                  pin_key_permutation, pin_decode_history, pin_masked_rows,
-                 pin_scale_on_scores]
+                 pin_scale_on_scores, pin_window_brute_force, pin_window_single_key,
+                 pin_window_locality]
 
 
 def read_golden(name):

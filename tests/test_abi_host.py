@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
     assert sorted(fa.EXPORTS) == declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.fa_abi_version() == 1
+    assert L.fa_abi_version() == 2
 
 
 def test_status_strings():
@@ -187,3 +187,26 @@ def test_bwd_empty_problem_is_a_no_op():
     none = {n: None for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")}
     assert bwd_call(shape=(0, 2, 16, 16, 64), ws=None, **none)[0] == "FA_OK"
     assert bwd_call(shape=(1, 2, 0, 0, 64), ws=None, **none)[0] == "FA_OK"
+
+
+def test_window_options_checked():
+    with pytest.raises(fa.FaError) as e:
+        fa.plan(1, 1, 16, 16, 64, window=(-1, 0))
+    assert e.value.name == "FA_ERR_ARG"
+    L = fa.lib()
+    info = fa.PlanInfo()
+    bad = Options(0, 0, 2, 0, 0)
+    st = L.fa_plan_query(Shape(1, 1, 16, 16, 64), fa.BF16, 0, ctypes.byref(bad), ctypes.byref(info))
+    assert L.fa_status_str(st).decode() == "FA_ERR_ARG"
+    # a windowed single query runs on the prefill kernel; split-KV has no window
+    assert fa.plan(4, 2, 1, 50000, 128, window=(127, 0))["path_name"] == "prefill"
+    assert fa.plan(4, 2, 1, 50000, 128)["path_name"] == "splitkv"
+    with pytest.raises(fa.FaError) as e:
+        fa.plan(4, 2, 1, 50000, 128, path=fa.PATH_SPLITKV, window=(127, 0))
+    assert e.value.name == "FA_ERR_UNSUPPORTED"
+    assert fa.plan(1, 1, 16, 16, 64, fa.F32, window=(3, 0))["path_name"] == "f32"
+    # the backward takes no window
+    opt = Options(0, 0, 1, 127, 0)
+    st = L.fa_bwd_ex(*([P] * 6), None, P, P, P, Shape(1, 2, 16, 16, 64), fa.BF16, 0.125, 1, P,
+                     fa.bwd_workspace_bytes(1, 2, 16, 16, 64), None, ctypes.byref(opt))
+    assert L.fa_status_str(st).decode() == "FA_ERR_UNSUPPORTED"

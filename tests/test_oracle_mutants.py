@@ -16,8 +16,12 @@ MUTANTS = {
     "lse_sign": ("LSE[r] = m + np.log(l)", "LSE[r] = m - np.log(l)"),
     "no_max_shift": ("e = np.exp(x - m)", "e = np.exp(x)"),
     "no_divide": ("return e / l, m, l", "return e, m, l"),
-    "top_left_causal": ("vis &= j <= i + (kv_len_b - N)", "vis &= j <= i"),
-    "strict_causal": ("vis &= j <= i + (kv_len_b - N)", "vis &= j < i + (kv_len_b - N)"),
+    "top_left_causal": ("        vis &= j <= i + off\n", "        vis &= j <= i\n"),
+    "strict_causal": ("        vis &= j <= i + off\n", "        vis &= j < i + off\n"),
+    "window_lower_strict": ("vis &= (j >= i + off - left)", "vis &= (j > i + off - left)"),
+    "window_top_left": ("vis &= (j >= i + off - left) & (j <= i + off + right)",
+                        "vis &= (j >= i - left) & (j <= i + right)"),
+    "window_ignored": ("vis &= (j >= i + off - left) & (j <= i + off + right)", "pass"),
     "scale_twice": ("return np.float64(scale) * (q @ k.T)",
                     "return np.float64(scale) ** 2 * (q @ k.T)"),
     "scale_dropped": ("return np.float64(scale) * (q @ k.T)", "return (q @ k.T)"),
@@ -40,8 +44,8 @@ def load_mutant(old, new):
 def test_pins_catch_mutant(name):
     mod = load_mutant(*MUTANTS[name])
 
-    def attn(q, k, v, scale, causal, kv_len):
-        return mod.attention_ref(q, k, v, scale, causal, kv_len)
+    def attn(q, k, v, scale, causal, kv_len, window=None):
+        return mod.attention_ref(q, k, v, scale, causal, kv_len, window=window)
 
     caught = []
     with np.errstate(all="ignore"):

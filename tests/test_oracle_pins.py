@@ -9,8 +9,8 @@ from oracle import streamed as S
 from tests import pins
 
 
-def oracle_attn(q, k, v, scale, causal, kv_len):
-    return A.attention_ref(q, k, v, scale, causal, kv_len)
+def oracle_attn(q, k, v, scale, causal, kv_len, window=None):
+    return A.attention_ref(q, k, v, scale, causal, kv_len, window=window)
 
 
 @pytest.mark.parametrize("pin", pins.ALL_ATTN_PINS, ids=lambda p: p.__name__)
