@@ -6,7 +6,9 @@ One step is one pass of the whole hot path over one batch of synthetic input:
   2. the split-KV decode (partial + merge kernels) on B=32 sequences, H=32,
      N=1, D=128, per-sequence KV length uniform in [1024, 32768];
   3. the backward of the prefill (row statistic, dK/dV and dQ kernels) for an
-     upstream gradient dO ~ N(0, 1), reported beside the forward.
+     upstream gradient dO ~ N(0, 1), reported beside the forward;
+  4. the same prefill with a causal local window of 128 keys per query (the
+     pages' 128-wide window) and of 2048 keys, reported beside it.
 Inputs are N(0, 1) drawn on the device from fixed seeds and are resident in
 HBM before timing starts.
 
@@ -67,7 +69,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "window", "copy"],
+                    default="all",
                     help="run one leg only (for counter runs); 'copy' runs a plain "
                          "device copy of known size for counter calibration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -110,6 +113,8 @@ def main():
     do_p = args.only in ("all", "prefill")
     do_d = args.only in ("all", "decode")
     do_b = args.only in ("all", "backward")
+    do_w = args.only in ("all", "window")
+    WINDOWS = (128, 2048)  # keys per query (causal band: window_left = W - 1)
 
     # ---- inputs, resident in HBM before timing ----
     if do_p:
@@ -144,6 +149,14 @@ def main():
         # five tile products (S recomputed, dP, dV, dK, dQ) of 2 N M D each,
         # halved for causal: 2.5 x the forward's count
         flop_b = 10.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0
+    if do_w:
+        if not (do_p or do_b):
+            qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
+            scale_p = 1.0 / math.sqrt(wp.D)
+        ow, lw = torch.empty_like(qp), torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
+        # visible (query, key) pairs per head of a causal band of W keys
+        pairs_w = {W: W * wp.N - W * (W - 1) // 2 for W in WINDOWS}
+        bytes_w = (4.0 * wp.N * wp.D * 2 + wp.N * 4) * wp.B * wp.H   # Q, K, V read, O and LSE written
     torch.cuda.synchronize()
 
     def step(evs=None):
@@ -157,6 +170,12 @@ def main():
                 fa.fwd(qd, kd, vd, scale=scale_d, causal=False, kv_len=kvl_d, out=od, lse=ld,
                        workspace=ws, stream=stream)
                 if evs: evs[3].record(stream)
+            if do_w:
+                for wi, W in enumerate(WINDOWS):
+                    if evs: evs[6 + 2 * wi].record(stream)
+                    fa.fwd(qp, kp, vp, scale=scale_p, causal=True, out=ow, lse=lw,
+                           window=(W - 1, 0), stream=stream)
+                    if evs: evs[7 + 2 * wi].record(stream)
             if do_b:
                 if evs: evs[4].record(stream)
                 fa.bwd(qp, kp, vp, ob, lb, gb, scale=scale_p, causal=True, dq=dqb, dk=dkb,
@@ -166,7 +185,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -176,6 +195,8 @@ def main():
     ms_p = [e[0].elapsed_time(e[1]) for e in events] if do_p else []
     ms_d = [e[2].elapsed_time(e[3]) for e in events] if do_d else []
     ms_b = [e[4].elapsed_time(e[5]) for e in events] if do_b else []
+    ms_w = {W: [e[6 + 2 * wi].elapsed_time(e[7 + 2 * wi]) for e in events]
+            for wi, W in enumerate(WINDOWS)} if do_w else {}
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": 1e3 * wall / max(1, args.steps), "higher_is_better": True,
@@ -225,6 +246,29 @@ def main():
                            "dO": "N(0,1), seed %d" % (wp.seed + 1000)}
         if not do_p and not do_d:
             out.update({"value": tfb, "unit": "TFLOP/s"})
+    if do_w:
+        res = {}
+        for W in WINDOWS:
+            avg = sum(ms_w[W]) / len(ms_w[W])
+            flop = 4.0 * wp.D * pairs_w[W] * wp.B * wp.H
+            tf = flop / (avg * 1e-3) / 1e12
+            gbs = bytes_w / (avg * 1e-3) / 1e9
+            # the bound is the resource with the longer time at its peak
+            mfma_bound = flop / (PEAK_BF16_TFLOPS * 1e12) >= bytes_w / (PEAK_HBM_GBS * 1e9)
+            roof = ({"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS} if mfma_bound else
+                    {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS})
+            roof.update({"kernel": "prefill_bf16_kernel<128,causal,window>", "traffic": None})
+            res[f"w{W}"] = {"window": [W - 1, 0], "ms_mean": avg, "ms_min": min(ms_w[W]),
+                            "tflops": tf, "gbs": gbs, "flop_per_launch": flop,
+                            "bytes_per_launch": bytes_w, "roofline": roof}
+        out["window"] = dict(res, flop_convention="4 D x visible (query, key) pairs per head "
+                                                  "(exact count), B H heads")
+        cfg["window"] = {"B": wp.B, "H": wp.H, "N": wp.N, "M": wp.M, "D": wp.D, "causal": True,
+                         "keys_per_query": list(WINDOWS)}
+        if not (do_p or do_d or do_b):
+            out.update({"value": res[f"w{WINDOWS[0]}"]["gbs"], "unit": "GB/s"})
     out["config"] = cfg
 
     if not args.no_cpu_baseline and args.only == "all":
