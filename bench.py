@@ -4,11 +4,16 @@
 One step is one pass of the whole hot path over one batch of synthetic input:
   1. the fused prefill forward (bf16, causal) on B=2, H=32, N=M=8192, D=128;
   2. the split-KV decode (partial + merge kernels) on B=32 sequences, H=32,
-     N=1, D=128, per-sequence KV length uniform in [1024, 32768];
+     N=1, D=128, per-sequence KV length uniform in [1024, 32768].
+After the timed steps, the wider rows are timed one by one on the same
+tensors (each with its own warmup), so they never share a timed region with
+the hot path:
   3. the backward of the prefill (row statistic, dK/dV and dQ kernels) for an
      upstream gradient dO ~ N(0, 1), reported beside the forward;
   4. the same prefill with a causal local window of 128 keys per query (the
-     pages' 128-wide window) and of 2048 keys, reported beside it.
+     pages' 128-wide window) and of 2048 keys, reported beside it;
+  5. the key/value-outer ablation of the same prefill (the first version's
+     loop order), one query tile per workgroup and one workgroup per head.
 Inputs are N(0, 1) drawn on the device from fixed seeds and are resident in
 HBM before timing starts.
 
@@ -69,7 +74,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "window", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "window", "kvouter",
+                                       "copy"],
                     default="all",
                     help="run one leg only (for counter runs); 'copy' runs a plain "
                          "device copy of known size for counter calibration")
@@ -114,6 +120,8 @@ def main():
     do_d = args.only in ("all", "decode")
     do_b = args.only in ("all", "backward")
     do_w = args.only in ("all", "window")
+    do_k = args.only in ("all", "kvouter")
+    KVO = (("tile_per_group", 1), ("head_per_group", 1 << 20))  # 256-query tiles per workgroup
     WINDOWS = (128, 2048)  # keys per query (causal band: window_left = W - 1)
 
     # ---- inputs, resident in HBM before timing ----
@@ -149,6 +157,14 @@ def main():
         # five tile products (S recomputed, dP, dV, dK, dQ) of 2 N M D each,
         # halved for causal: 2.5 x the forward's count
         flop_b = 10.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0
+    if do_k:
+        if not (do_p or do_b or do_w):
+            qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
+            scale_p = 1.0 / math.sqrt(wp.D)
+        ok_, lk_ = torch.empty_like(qp), torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
+        wsk = torch.empty(fa.workspace_bytes(wp.B, wp.H, wp.N, wp.M, wp.D, causal=True,
+                                             path=fa.PATH_KVOUTER), dtype=torch.uint8, device=dev)
+        flop_k = 4.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0
     if do_w:
         if not (do_p or do_b):
             qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
@@ -159,7 +175,8 @@ def main():
         bytes_w = (4.0 * wp.N * wp.D * 2 + wp.N * 4) * wp.B * wp.H   # Q, K, V read, O and LSE written
     torch.cuda.synchronize()
 
-    def step(evs=None):
+    def main_step(evs=None):
+        """One pass of the hot path: the causal prefill and the split-KV decode."""
         with torch.cuda.stream(stream):
             if do_p:
                 if evs: evs[0].record(stream)
@@ -170,33 +187,48 @@ def main():
                 fa.fwd(qd, kd, vd, scale=scale_d, causal=False, kv_len=kvl_d, out=od, lse=ld,
                        workspace=ws, stream=stream)
                 if evs: evs[3].record(stream)
-            if do_w:
-                for wi, W in enumerate(WINDOWS):
-                    if evs: evs[6 + 2 * wi].record(stream)
-                    fa.fwd(qp, kp, vp, scale=scale_p, causal=True, out=ow, lse=lw,
-                           window=(W - 1, 0), stream=stream)
-                    if evs: evs[7 + 2 * wi].record(stream)
-            if do_b:
-                if evs: evs[4].record(stream)
-                fa.bwd(qp, kp, vp, ob, lb, gb, scale=scale_p, causal=True, dq=dqb, dk=dkb,
-                       dv=dvb, workspace=wsb, stream=stream)
-                if evs: evs[5].record(stream)
 
+    def timed(fn, steps, warmup):
+        """HIP events on the library's stream around each of `steps` calls."""
+        for _ in range(warmup):
+            with torch.cuda.stream(stream):
+                fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            with torch.cuda.stream(stream):
+                a.record(stream)
+                fn()
+                b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    # ---- the timed region of the hot path ----
     for _ in range(args.warmup):
-        step()
+        main_step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        main_step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_p = [e[0].elapsed_time(e[1]) for e in events] if do_p else []
     ms_d = [e[2].elapsed_time(e[3]) for e in events] if do_d else []
-    ms_b = [e[4].elapsed_time(e[5]) for e in events] if do_b else []
-    ms_w = {W: [e[6 + 2 * wi].elapsed_time(e[7 + 2 * wi]) for e in events]
-            for wi, W in enumerate(WINDOWS)} if do_w else {}
+
+    # ---- the wider rows, each timed on its own after the hot path ----
+    ms_b = timed(lambda: fa.bwd(qp, kp, vp, ob, lb, gb, scale=scale_p, causal=True, dq=dqb,
+                                dk=dkb, dv=dvb, workspace=wsb, stream=stream),
+                 args.steps, args.warmup) if do_b else []
+    ms_w = {W: timed(lambda W=W: fa.fwd(qp, kp, vp, scale=scale_p, causal=True, out=ow, lse=lw,
+                                        window=(W - 1, 0), stream=stream),
+                     args.steps, args.warmup) for W in WINDOWS} if do_w else {}
+    ms_k = {name: timed(lambda tpg=tpg: fa.fwd(qp, kp, vp, scale=scale_p, causal=True, out=ok_,
+                                               lse=lk_, workspace=wsk, path=fa.PATH_KVOUTER,
+                                               kvouter_query_tiles=tpg, stream=stream),
+                        max(2, args.steps // 4), 1) for name, tpg in KVO} if do_k else {}
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": 1e3 * wall / max(1, args.steps), "higher_is_better": True,
@@ -269,6 +301,21 @@ def main():
                          "keys_per_query": list(WINDOWS)}
         if not (do_p or do_d or do_b):
             out.update({"value": res[f"w{WINDOWS[0]}"]["gbs"], "unit": "GB/s"})
+    if do_k:
+        res = {}
+        for name, tpg in KVO:
+            avg = sum(ms_k[name]) / len(ms_k[name])
+            tf = flop_k / (avg * 1e-3) / 1e12
+            res[name] = {"query_tiles_per_group": min(tpg, -(-wp.N // 256)), "ms_mean": avg,
+                         "ms_min": min(ms_k[name]), "tflops": tf,
+                         "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+                         "slowdown_vs_prefill": (avg / (sum(ms_p) / len(ms_p))) if do_p else None}
+        out["kvouter"] = dict(res, note="ablation: key/value tiles outside, output accumulator "
+                                        "and m, l read and written back per key tile (float32 "
+                                        "workspace); same FLOP convention as the prefill")
+        cfg["kvouter"] = {"B": wp.B, "H": wp.H, "N": wp.N, "M": wp.M, "D": wp.D, "causal": True}
+        if not (do_p or do_d or do_b or do_w):
+            out.update({"value": res["tile_per_group"]["tflops"], "unit": "TFLOP/s"})
     out["config"] = cfg
 
     if not args.no_cpu_baseline and args.only == "all":

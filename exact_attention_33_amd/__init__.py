@@ -21,12 +21,13 @@ import math
 import os
 
 __all__ = ["fwd", "bwd", "bwd_workspace_bytes", "plan", "workspace_bytes", "lib", "library_path", "FaError",
-           "PATH_AUTO", "PATH_PREFILL", "PATH_SPLITKV", "PATH_F32",
+           "PATH_AUTO", "PATH_PREFILL", "PATH_SPLITKV", "PATH_F32", "PATH_KVOUTER",
            "F32", "BF16", "EXPORTS"]
 
 F32, BF16 = 0, 1
-PATH_AUTO, PATH_PREFILL, PATH_SPLITKV, PATH_F32 = 0, 1, 2, 3
-PATH_NAMES = {PATH_PREFILL: "prefill", PATH_SPLITKV: "splitkv", PATH_F32: "f32"}
+PATH_AUTO, PATH_PREFILL, PATH_SPLITKV, PATH_F32, PATH_KVOUTER = 0, 1, 2, 3, 4
+PATH_NAMES = {PATH_PREFILL: "prefill", PATH_SPLITKV: "splitkv", PATH_F32: "f32",
+              PATH_KVOUTER: "kvouter"}
 
 # Every symbol include/fa_mi355x.h declares.
 EXPORTS = ["fa_plan_query", "fa_fwd_workspace_bytes", "fa_fwd", "fa_fwd_ex",
@@ -52,7 +53,7 @@ class Shape(ctypes.Structure):
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_keys", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("window_left", ctypes.c_int32),
-                ("window_right", ctypes.c_int32)]
+                ("window_right", ctypes.c_int32), ("kvouter_query_tiles", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -107,25 +108,26 @@ def _check(st):
         raise FaError(st, L.fa_status_str(st).decode(), L.fa_last_error().decode())
 
 
-def _options(path, split_keys, window=None):
+def _options(path, split_keys, window=None, kvouter_query_tiles=0):
     """fa_options for the call, or None for the defaults.  ``window`` is None
     or (left, right): key j visible to query i only if
     i + off - left <= j <= i + off + right (off = kv_len - N)."""
-    if path in (None, PATH_AUTO) and not split_keys and window is None:
+    if path in (None, PATH_AUTO) and not split_keys and window is None and not kvouter_query_tiles:
         return None
     wl, wr = (int(window[0]), int(window[1])) if window is not None else (0, 0)
     return Options(PATH_AUTO if path is None else int(path), int(split_keys or 0),
-                   1 if window is not None else 0, wl, wr)
+                   1 if window is not None else 0, wl, wr, int(kvouter_query_tiles or 0))
 
 
 def _opt_ptr(o):
     return ctypes.byref(o) if o is not None else None
 
 
-def plan(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0, window=None):
+def plan(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0, window=None,
+         kvouter_query_tiles=0):
     """The planner's decision for a shape, as a dict (host only)."""
     info = PlanInfo()
-    o = _options(path, split_keys, window)
+    o = _options(path, split_keys, window, kvouter_query_tiles)
     _check(lib().fa_plan_query(Shape(B, H, N, M, D), int(dtype), int(bool(causal)),
                                _opt_ptr(o), ctypes.byref(info)))
     d = {f: getattr(info, f) for f, _ in PlanInfo._fields_}
@@ -134,8 +136,8 @@ def plan(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0, windo
 
 
 def workspace_bytes(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0,
-                    window=None):
-    o = _options(path, split_keys, window)
+                    window=None, kvouter_query_tiles=0):
+    o = _options(path, split_keys, window, kvouter_query_tiles)
     return int(lib().fa_fwd_workspace_bytes(Shape(B, H, N, M, D), int(dtype),
                                             int(bool(causal)), _opt_ptr(o)))
 
@@ -150,7 +152,8 @@ def _dtype_code(t):
 
 
 def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
-        workspace=None, path=None, split_keys=0, window=None, stream=None):
+        workspace=None, path=None, split_keys=0, window=None, kvouter_query_tiles=0,
+        stream=None):
     """Exact attention forward through the C ABI; returns (O, LSE).
 
     ``window=(left, right)`` restricts query i to keys
@@ -185,7 +188,7 @@ def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
         out = torch.empty((B, H, N, D), dtype=q.dtype, device=dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    opts = _options(path, split_keys, window)
+    opts = _options(path, split_keys, window, kvouter_query_tiles)
     shape = Shape(B, H, N, M, D)
     ws_need = int(L.fa_fwd_workspace_bytes(shape, dt, int(bool(causal)), _opt_ptr(opts)))
     if ws_need and workspace is None:

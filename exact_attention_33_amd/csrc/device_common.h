@@ -51,6 +51,16 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// The two halves of a wave combined: every lane receives op(x[i], x[i ^ 32]).
+__device__ __forceinline__ float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int clamp_kv(const int32_t* kv_len, int b, int M) {
   if (!kv_len) return M;
   const int x = kv_len[b];

@@ -51,6 +51,8 @@ hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, hipStream_t s
 hipError_t launch_fwd_f32(const Problem& p, const Plan& plan, hipStream_t stream);
 hipError_t launch_splitkv_bf16(const Problem& p, const Plan& plan, void* workspace,
                                hipStream_t stream);
+hipError_t launch_kvouter_bf16(const Problem& p, const Plan& plan, void* workspace,
+                               hipStream_t stream);
 
 // Tile constants shared by the planner and the kernels.
 constexpr int kPrefillBlockQ = 256;   // 4 waves x 64 queries

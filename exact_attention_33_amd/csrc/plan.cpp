@@ -9,6 +9,7 @@
 // Batch, heads and query tiles are independent ("Understanding
 // FlashAttention", Attention: batch and heads only repeat the problem), so
 // the grid spans all three.
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 
@@ -51,7 +52,7 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
     return FA_ERR_UNSUPPORTED;
   }
   const int32_t req = opt ? opt->path : FA_PATH_AUTO;
-  if (req < FA_PATH_AUTO || req > FA_PATH_F32) {
+  if (req < FA_PATH_AUTO || req > FA_PATH_KVOUTER) {
     *why = "options.path is not a fa_path value";
     return FA_ERR_ARG;
   }
@@ -62,6 +63,10 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
   const bool window = opt && opt->window;
   if (opt && (opt->window != 0 && opt->window != 1)) {
     *why = "options.window must be 0 or 1";
+    return FA_ERR_ARG;
+  }
+  if (opt && opt->kvouter_query_tiles < 0) {
+    *why = "options.kvouter_query_tiles must be >= 0";
     return FA_ERR_ARG;
   }
   if (window && (opt->window_left < 0 || opt->window_right < 0)) {
@@ -90,6 +95,10 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
     }
     if (req == FA_PATH_SPLITKV && s.N != 1) {
       *why = "FA_PATH_SPLITKV needs N == 1 (one query per sequence)";
+      return FA_ERR_UNSUPPORTED;
+    }
+    if (req == FA_PATH_KVOUTER && window) {
+      *why = "FA_PATH_KVOUTER takes no window";
       return FA_ERR_UNSUPPORTED;
     }
     if (req == FA_PATH_SPLITKV && window) {
@@ -135,6 +144,23 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
       const size_t parts = (size_t)bh * (size_t)plan->splits;
       plan->ws_lse_offset = align_up(parts * (size_t)s.D * sizeof(float), 256);
       plan->ws_bytes = parts ? align_up(plan->ws_lse_offset + parts * sizeof(float), 256) : 0;
+      break;
+    }
+    case FA_PATH_KVOUTER: {
+      if ((int64_t)s.M * s.D * 2 > INT32_MAX) {
+        *why = "FA_PATH_KVOUTER needs M * D * 2 < 2^31 (K/V bytes per batch and head)";
+        return FA_ERR_UNSUPPORTED;
+      }
+      const int64_t n_qt = ceil_div(s.N, 256);
+      const int64_t tpg = std::max<int64_t>(1, std::min<int64_t>(
+          n_qt, (opt && opt->kvouter_query_tiles) ? opt->kvouter_query_tiles : 1));
+      plan->block_q = (int32_t)(256 * tpg);
+      plan->block_k = 64;
+      plan->threads = 256;
+      plan->lds_bytes = 2 * 64 * (2 * s.D + 64);
+      plan->grid = n_qt ? ceil_div(n_qt, tpg) * bh : 0;
+      // float32 accumulator [B,H,N,D], then m and l [B,H,N] each
+      plan->ws_bytes = align_up((size_t)bh * (size_t)s.N * ((size_t)s.D + 2) * sizeof(float), 256);
       break;
     }
     default:

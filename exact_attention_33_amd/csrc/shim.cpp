@@ -118,6 +118,7 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v,
     case FA_PATH_PREFILL: err = fa::launch_prefill_bf16(p, plan, hs); break;
     case FA_PATH_F32: err = fa::launch_fwd_f32(p, plan, hs); break;
     case FA_PATH_SPLITKV: err = fa::launch_splitkv_bf16(p, plan, workspace, hs); break;
+    case FA_PATH_KVOUTER: err = fa::launch_kvouter_bf16(p, plan, workspace, hs); break;
     default: return fail(FA_ERR_UNSUPPORTED, "fa_fwd: internal: no path");
   }
   if (err != hipSuccess)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
 
@@ -72,7 +72,11 @@ typedef enum {
                            window it also serves N = 1                           */
   FA_PATH_SPLITKV = 2,  /* split-KV partial kernel + log-sum-exp merge (bf16, N=1,
                            no window)                                             */
-  FA_PATH_F32 = 3       /* float32 inputs/outputs, float64 internal arithmetic   */
+  FA_PATH_F32 = 3,      /* float32 inputs/outputs, float64 internal arithmetic   */
+  FA_PATH_KVOUTER = 4   /* ablation, never chosen by the planner: the same result
+                           with key/value tiles in the outer loop and the output
+                           accumulator, m and l read and written back in a
+                           float32 workspace for every key tile (bf16, no window) */
 } fa_path;
 
 /* Optional controls; pass NULL for the planner's defaults.  A zero-filled
@@ -91,6 +95,9 @@ typedef struct {
                           window_left = 127.                                    */
   int32_t window_left;   /* >= 0, used when window == 1                         */
   int32_t window_right;  /* >= 0, used when window == 1                         */
+  int32_t kvouter_query_tiles;  /* FA_PATH_KVOUTER: 256-query tiles per workgroup
+                                   (0 = 1); a value >= ceil(N / 256) gives one
+                                   workgroup per (batch, head)                  */
 } fa_options;
 
 /* What the planner decided for a shape (host-only, no device call). */
