@@ -13,7 +13,9 @@ the hot path:
   4. the same prefill with a causal local window of 128 keys per query (the
      pages' 128-wide window) and of 2048 keys, reported beside it;
   5. the key/value-outer ablation of the same prefill (the first version's
-     loop order), one query tile per workgroup and one workgroup per head.
+     loop order), one query tile per workgroup and one workgroup per head;
+  6. the same prefill on E4M3 inputs (the prefill's tensors quantized per
+     tensor) on the fp8 matrix cores.
 Inputs are N(0, 1) drawn on the device from fixed seeds and are resident in
 HBM before timing starts.
 
@@ -39,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak; decode KV GB/s & % HBM peak"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -75,7 +78,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "window", "kvouter",
-                                       "copy"],
+                                       "fp8", "copy"],
                     default="all",
                     help="run one leg only (for counter runs); 'copy' runs a plain "
                          "device copy of known size for counter calibration")
@@ -121,6 +124,7 @@ def main():
     do_b = args.only in ("all", "backward")
     do_w = args.only in ("all", "window")
     do_k = args.only in ("all", "kvouter")
+    do_8 = args.only in ("all", "fp8")
     KVO = (("tile_per_group", 1), ("head_per_group", 1 << 20))  # 256-query tiles per workgroup
     WINDOWS = (128, 2048)  # keys per query (causal band: window_left = W - 1)
 
@@ -157,6 +161,19 @@ def main():
         # five tile products (S recomputed, dP, dV, dK, dQ) of 2 N M D each,
         # halved for causal: 2.5 x the forward's count
         flop_b = 10.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0
+    if do_8:
+        # the prefill's tensors quantized per tensor to E4M3 (scale = amax / 448)
+        if not (do_p or do_b):
+            qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
+            scale_p = 1.0 / math.sqrt(wp.D)
+        q8s, d8 = [], []
+        for t in (qp, kp, vp):
+            d = float(t.abs().max()) / 448.0
+            q8s.append((t.float() / d).to(torch.float8_e4m3fn))
+            d8.append(d)
+        o8 = torch.empty_like(qp)
+        l8 = torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
+        flop_8 = 4.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0
     if do_k:
         if not (do_p or do_b or do_w):
             qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
@@ -225,6 +242,9 @@ def main():
     ms_w = {W: timed(lambda W=W: fa.fwd(qp, kp, vp, scale=scale_p, causal=True, out=ow, lse=lw,
                                         window=(W - 1, 0), stream=stream),
                      args.steps, args.warmup) for W in WINDOWS} if do_w else {}
+    ms_8 = timed(lambda: fa.fwd(q8s[0], q8s[1], q8s[2], scale=scale_p, causal=True, out=o8, lse=l8,
+                                descale=tuple(d8), stream=stream),
+                 args.steps, args.warmup) if do_8 else []
     ms_k = {name: timed(lambda tpg=tpg: fa.fwd(qp, kp, vp, scale=scale_p, causal=True, out=ok_,
                                                lse=lk_, workspace=wsk, path=fa.PATH_KVOUTER,
                                                kvouter_query_tiles=tpg, stream=stream),
@@ -301,6 +321,19 @@ def main():
                          "keys_per_query": list(WINDOWS)}
         if not (do_p or do_d or do_b):
             out.update({"value": res[f"w{WINDOWS[0]}"]["gbs"], "unit": "GB/s"})
+    if do_8:
+        avg8 = sum(ms_8) / len(ms_8)
+        tf8 = flop_8 / (avg8 * 1e-3) / 1e12
+        out["fp8"] = {"ms_mean": avg8, "ms_min": min(ms_8), "value": tf8, "unit": "TFLOP/s",
+                      "frac_fp8_peak": tf8 / PEAK_FP8_TFLOPS, "flop_per_launch": flop_8,
+                      "speedup_vs_bf16_prefill": ((sum(ms_p) / len(ms_p)) / avg8) if do_p else None,
+                      "roofline": {"bound": "mfma", "kernel": "prefill_fp8_kernel<128,causal>",
+                                   "achieved": tf8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": None}}
+        cfg["fp8"] = {"B": wp.B, "H": wp.H, "N": wp.N, "M": wp.M, "D": wp.D, "causal": True,
+                      "inputs": "E4M3, per-tensor scale amax/448 of the prefill's tensors"}
+        if not (do_p or do_d):
+            out.update({"value": tf8, "unit": "TFLOP/s"})
     if do_k:
         res = {}
         for name, tpg in KVO:

@@ -21,13 +21,14 @@ import math
 import os
 
 __all__ = ["fwd", "bwd", "bwd_workspace_bytes", "plan", "workspace_bytes", "lib", "library_path", "FaError",
-           "PATH_AUTO", "PATH_PREFILL", "PATH_SPLITKV", "PATH_F32", "PATH_KVOUTER",
+           "PATH_AUTO", "PATH_PREFILL", "PATH_SPLITKV", "PATH_F32", "PATH_KVOUTER", "PATH_FP8",
+           "FP8",
            "F32", "BF16", "EXPORTS"]
 
-F32, BF16 = 0, 1
-PATH_AUTO, PATH_PREFILL, PATH_SPLITKV, PATH_F32, PATH_KVOUTER = 0, 1, 2, 3, 4
+F32, BF16, FP8 = 0, 1, 2
+PATH_AUTO, PATH_PREFILL, PATH_SPLITKV, PATH_F32, PATH_KVOUTER, PATH_FP8 = 0, 1, 2, 3, 4, 5
 PATH_NAMES = {PATH_PREFILL: "prefill", PATH_SPLITKV: "splitkv", PATH_F32: "f32",
-              PATH_KVOUTER: "kvouter"}
+              PATH_KVOUTER: "kvouter", PATH_FP8: "fp8"}
 
 # Every symbol include/fa_mi355x.h declares.
 EXPORTS = ["fa_plan_query", "fa_fwd_workspace_bytes", "fa_fwd", "fa_fwd_ex",
@@ -53,7 +54,9 @@ class Shape(ctypes.Structure):
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_keys", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("window_left", ctypes.c_int32),
-                ("window_right", ctypes.c_int32), ("kvouter_query_tiles", ctypes.c_int32)]
+                ("window_right", ctypes.c_int32), ("kvouter_query_tiles", ctypes.c_int32),
+                ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float),
+                ("v_descale", ctypes.c_float)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -108,15 +111,19 @@ def _check(st):
         raise FaError(st, L.fa_status_str(st).decode(), L.fa_last_error().decode())
 
 
-def _options(path, split_keys, window=None, kvouter_query_tiles=0):
+def _options(path, split_keys, window=None, kvouter_query_tiles=0, descale=None):
     """fa_options for the call, or None for the defaults.  ``window`` is None
     or (left, right): key j visible to query i only if
-    i + off - left <= j <= i + off + right (off = kv_len - N)."""
-    if path in (None, PATH_AUTO) and not split_keys and window is None and not kvouter_query_tiles:
+    i + off - left <= j <= i + off + right (off = kv_len - N).  ``descale``
+    is None or (dq, dk, dv) for fp8 inputs."""
+    if (path in (None, PATH_AUTO) and not split_keys and window is None
+            and not kvouter_query_tiles and descale is None):
         return None
     wl, wr = (int(window[0]), int(window[1])) if window is not None else (0, 0)
+    dq, dk, dv = (float(x) for x in descale) if descale is not None else (0.0, 0.0, 0.0)
     return Options(PATH_AUTO if path is None else int(path), int(split_keys or 0),
-                   1 if window is not None else 0, wl, wr, int(kvouter_query_tiles or 0))
+                   1 if window is not None else 0, wl, wr, int(kvouter_query_tiles or 0),
+                   dq, dk, dv)
 
 
 def _opt_ptr(o):
@@ -148,17 +155,22 @@ def _dtype_code(t):
         return BF16
     if t.dtype == torch.float32:
         return F32
-    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16, torch.float32 or "
+                    "torch.float8_e4m3fn")
 
 
 def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
         workspace=None, path=None, split_keys=0, window=None, kvouter_query_tiles=0,
-        stream=None):
+        descale=None, stream=None):
     """Exact attention forward through the C ABI; returns (O, LSE).
 
     ``window=(left, right)`` restricts query i to keys
     i + off - left .. i + off + right (off = kv_len - N; causal caps right
-    at 0): ``causal=True, window=(127, 0)`` is a 128-wide local window."""
+    at 0): ``causal=True, window=(127, 0)`` is a 128-wide local window.
+    float8_e4m3fn inputs (FP8) give a bf16 O; ``descale=(dq, dk, dv)`` says
+    that they stand for dq*Q, dk*K, dv*V."""
     import torch
     L = lib()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -185,10 +197,10 @@ def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
         if kv_len.numel() != B:
             raise ValueError("kv_len must have B entries")
     if out is None:
-        out = torch.empty((B, H, N, D), dtype=q.dtype, device=dev)
+        out = torch.empty((B, H, N, D), dtype=torch.bfloat16 if dt == FP8 else q.dtype, device=dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    opts = _options(path, split_keys, window, kvouter_query_tiles)
+    opts = _options(path, split_keys, window, kvouter_query_tiles, descale)
     shape = Shape(B, H, N, M, D)
     ws_need = int(L.fa_fwd_workspace_bytes(shape, dt, int(bool(causal)), _opt_ptr(opts)))
     if ws_need and workspace is None:

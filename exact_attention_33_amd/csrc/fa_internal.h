@@ -27,6 +27,8 @@ struct Problem {
   // i + off - wl <= j <= i + off + wr, off = kv_len - N.  window == 0: none.
   int window;
   int32_t wl, wr;
+  // FA_FP8: the inputs stand for q_descale * Q8, k_descale * K8, v_descale * V8.
+  float q_descale, k_descale, v_descale;
 };
 
 // Planner output (host-only; see plan.cpp).
@@ -53,6 +55,7 @@ hipError_t launch_splitkv_bf16(const Problem& p, const Plan& plan, void* workspa
                                hipStream_t stream);
 hipError_t launch_kvouter_bf16(const Problem& p, const Plan& plan, void* workspace,
                                hipStream_t stream);
+hipError_t launch_prefill_fp8(const Problem& p, const Plan& plan, hipStream_t stream);
 
 // Tile constants shared by the planner and the kernels.
 constexpr int kPrefillBlockQ = 256;   // 4 waves x 64 queries
@@ -62,6 +65,9 @@ constexpr int kPrefillThreads = 256;
 constexpr int kF32BlockQ = 16;        // 16 query rows x 16 lanes
 constexpr int kF32BlockK = 32;
 constexpr int kF32Threads = 256;
+
+constexpr int kFp8BlockQ = 256;       // 8 waves x 32 queries
+constexpr int kFp8Threads = 512;
 
 constexpr int kSplitThreads = 256;
 constexpr int kMergeThreads = 256;

@@ -43,8 +43,8 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
     *why = "B, H, N, M and D must be non-negative";
     return FA_ERR_SHAPE;
   }
-  if (dt != FA_F32 && dt != FA_BF16) {
-    *why = "dtype must be FA_F32 or FA_BF16";
+  if (dt != FA_F32 && dt != FA_BF16 && dt != FA_FP8) {
+    *why = "dtype must be FA_F32, FA_BF16 or FA_FP8";
     return FA_ERR_UNSUPPORTED;
   }
   if (s.D != 64 && s.D != 128) {
@@ -52,7 +52,7 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
     return FA_ERR_UNSUPPORTED;
   }
   const int32_t req = opt ? opt->path : FA_PATH_AUTO;
-  if (req < FA_PATH_AUTO || req > FA_PATH_KVOUTER) {
+  if (req < FA_PATH_AUTO || req > FA_PATH_FP8) {
     *why = "options.path is not a fa_path value";
     return FA_ERR_ARG;
   }
@@ -81,8 +81,26 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
     return FA_ERR_SHAPE;
   }
 
+  if (opt && !(opt->q_descale >= 0.f && opt->k_descale >= 0.f && opt->v_descale >= 0.f &&
+               opt->q_descale < 3.4e38f && opt->k_descale < 3.4e38f && opt->v_descale < 3.4e38f)) {
+    *why = "options.q_descale, k_descale and v_descale must be finite and >= 0";
+    return FA_ERR_ARG;
+  }
   fa_path path;
-  if (dt == FA_F32) {
+  if (dt == FA_FP8) {
+    if (req != FA_PATH_AUTO && req != FA_PATH_FP8) {
+      *why = "FA_FP8 inputs run only on FA_PATH_FP8";
+      return FA_ERR_UNSUPPORTED;
+    }
+    if (window) {
+      *why = "FA_PATH_FP8 takes no window";
+      return FA_ERR_UNSUPPORTED;
+    }
+    path = FA_PATH_FP8;
+  } else if (req == FA_PATH_FP8) {
+    *why = "FA_PATH_FP8 needs FA_FP8 inputs";
+    return FA_ERR_UNSUPPORTED;
+  } else if (dt == FA_F32) {
     if (req != FA_PATH_AUTO && req != FA_PATH_F32) {
       *why = "float32 inputs run only on FA_PATH_F32";
       return FA_ERR_UNSUPPORTED;
@@ -146,6 +164,18 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
       plan->ws_bytes = parts ? align_up(plan->ws_lse_offset + parts * sizeof(float), 256) : 0;
       break;
     }
+    case FA_PATH_FP8:
+      // one (batch, head) of K or V is addressed with 32-bit byte offsets
+      if ((int64_t)s.M * s.D > INT32_MAX) {
+        *why = "FA_PATH_FP8 needs M * D < 2^31 (K/V bytes per batch and head)";
+        return FA_ERR_UNSUPPORTED;
+      }
+      plan->block_q = kFp8BlockQ;
+      plan->block_k = 64;
+      plan->threads = kFp8Threads;
+      plan->lds_bytes = 4 * 64 * s.D;
+      plan->grid = ceil_div(s.N, kFp8BlockQ) * bh;
+      break;
     case FA_PATH_KVOUTER: {
       if ((int64_t)s.M * s.D * 2 > INT32_MAX) {
         *why = "FA_PATH_KVOUTER needs M * D * 2 < 2^31 (K/V bytes per batch and head)";

@@ -110,8 +110,11 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v,
   }
 
   const bool win = opt && opt->window;
+  auto descale = [](float x) { return x == 0.f ? 1.f : x; };
   fa::Problem p{q, k, v, kv_len, o, lse, s.B, s.H, s.N, s.M, s.D, scale, causal ? 1 : 0,
-                win ? 1 : 0, win ? opt->window_left : 0, win ? opt->window_right : 0};
+                win ? 1 : 0, win ? opt->window_left : 0, win ? opt->window_right : 0,
+                opt ? descale(opt->q_descale) : 1.f, opt ? descale(opt->k_descale) : 1.f,
+                opt ? descale(opt->v_descale) : 1.f};
   hipStream_t hs = (hipStream_t)stream;
   hipError_t err = hipSuccess;
   switch (plan.path) {
@@ -119,6 +122,7 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v,
     case FA_PATH_F32: err = fa::launch_fwd_f32(p, plan, hs); break;
     case FA_PATH_SPLITKV: err = fa::launch_splitkv_bf16(p, plan, workspace, hs); break;
     case FA_PATH_KVOUTER: err = fa::launch_kvouter_bf16(p, plan, workspace, hs); break;
+    case FA_PATH_FP8: err = fa::launch_prefill_fp8(p, plan, hs); break;
     default: return fail(FA_ERR_UNSUPPORTED, "fa_fwd: internal: no path");
   }
   if (err != hipSuccess)

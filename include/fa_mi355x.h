@@ -33,7 +33,8 @@
  * reentrant and never throw across the ABI.
  *
  * Layout.  Q [B,H,N,D], K and V [B,H,M,D] and O [B,H,N,D] are contiguous,
- * row-major, D fastest, all of element type `dtype`; LSE [B,H,N] is float32;
+ * row-major, D fastest, all of element type `dtype` (O is bf16 for FA_FP8);
+ * LSE [B,H,N] is float32;
  * kv_len [B] is int32 (NULL means M for every batch).  Device-side kv_len
  * values cannot be checked without a synchronisation: values outside [0, M]
  * are clamped to that range by the kernels.
@@ -48,9 +49,11 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
-typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+/* FA_FP8: OCP E4M3 (finite max 448, no infinities) Q, K, V with per-tensor
+ * descale factors (fa_options); O is then bf16 and LSE float32. */
+typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_FP8 = 2 } fa_dtype;
 
 typedef enum {
   FA_OK = 0,
@@ -73,10 +76,13 @@ typedef enum {
   FA_PATH_SPLITKV = 2,  /* split-KV partial kernel + log-sum-exp merge (bf16, N=1,
                            no window)                                             */
   FA_PATH_F32 = 3,      /* float32 inputs/outputs, float64 internal arithmetic   */
-  FA_PATH_KVOUTER = 4   /* ablation, never chosen by the planner: the same result
+  FA_PATH_KVOUTER = 4,  /* ablation, never chosen by the planner: the same result
                            with key/value tiles in the outer loop and the output
                            accumulator, m and l read and written back in a
                            float32 workspace for every key tile (bf16, no window) */
+  FA_PATH_FP8 = 5       /* fused tiled kernel on the fp8 matrix cores: FA_FP8
+                           inputs only, any N, no window; the weights are rounded
+                           to E4M3 before the P V product                          */
 } fa_path;
 
 /* Optional controls; pass NULL for the planner's defaults.  A zero-filled
@@ -98,6 +104,9 @@ typedef struct {
   int32_t kvouter_query_tiles;  /* FA_PATH_KVOUTER: 256-query tiles per workgroup
                                    (0 = 1); a value >= ceil(N / 256) gives one
                                    workgroup per (batch, head)                  */
+  float q_descale;     /* FA_FP8: Q stands for q_descale * Q8 (0 means 1)       */
+  float k_descale;     /* FA_FP8: K stands for k_descale * K8 (0 means 1)       */
+  float v_descale;     /* FA_FP8: V stands for v_descale * V8 (0 means 1)       */
 } fa_options;
 
 /* What the planner decided for a shape (host-only, no device call). */

@@ -111,3 +111,40 @@ def compare_bwd(got, want, bound, what):
                              f"{tuple(int(x) for x in idx)}: got {got[tuple(idx)]:.6g} "
                              f"want {want[tuple(idx)]:.6g} bound {lim[tuple(idx)]:.3g}")
     return float(np.max(err / lim)) if err.size else 0.0
+
+
+# ---- fp8 (E4M3) forward ----
+#
+# The kernel forms weights w_j = 2^(t_j - m) against a reference m with
+# m <= max_j t_j <= m + 8 (t in log2 units), rounds them to E4M3 (round to
+# nearest even: relative error <= 2^-4 for w >= 2^-6, absolute <= 2^-10
+# below, where E4M3 is subnormal) before P V, and divides by the float32 sum
+# of the unrounded weights.  With P the exact softmax and
+# l_rel = sum_j exp(s_j - max_k s_k) >= 1, per element:
+#   |dO_id| <= 2^-4 sum_j P_ij |v_jd| + 2^-10 sum_(visible j) |v_jd| / l_rel_i
+# plus one bf16 rounding of O (2^-8 |O| taken) and float32 slack.  The test
+# accepts twice that; LSE keeps the bf16 path's 1e-3 (the sums are float32
+# over float32 weights, the scores exact products accumulated in float32).
+U_E4M3 = 2.0 ** -4
+E4M3_SUB = 2.0 ** -10
+
+
+def fp8_bound(q, k, v, scale, causal, kvl, window=None):
+    """Elementwise bound [N, D] for one head from the exact (dequantized) inputs."""
+    from oracle.attention import visible_mask
+    N, D = q.shape
+    kv, vv = k[:kvl], v[:kvl]
+    if kvl == 0:
+        return np.full((N, D), 1e-6)
+    S = scale * (q @ kv.T)
+    vis = visible_mask(N, kvl, causal, window)
+    S = np.where(vis, S, -np.inf)
+    m = S.max(axis=1, keepdims=True)
+    fin = np.isfinite(m)[:, 0]
+    E = np.where(vis & fin[:, None], np.exp(np.where(fin[:, None], S - np.where(fin[:, None], m, 0), -np.inf)), 0.0)
+    l_rel = E.sum(axis=1)
+    P = E / np.where(l_rel > 0, l_rel, 1.0)[:, None]
+    av = np.abs(vv)
+    O = P @ vv
+    b = U_E4M3 * (P @ av) + E4M3_SUB * (vis.astype(np.float64) @ av) / np.where(l_rel > 0, l_rel, 1.0)[:, None]
+    return b + 2.0 ** -8 * np.abs(O) + 1e-6

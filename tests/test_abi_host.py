@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
     assert sorted(fa.EXPORTS) == declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.fa_abi_version() == 3
+    assert L.fa_abi_version() == 4
 
 
 def test_status_strings():
@@ -195,7 +195,7 @@ def test_window_options_checked():
     assert e.value.name == "FA_ERR_ARG"
     L = fa.lib()
     info = fa.PlanInfo()
-    bad = Options(0, 0, 2, 0, 0, 0)
+    bad = Options(0, 0, 2, 0, 0, 0, 0.0, 0.0, 0.0)
     st = L.fa_plan_query(Shape(1, 1, 16, 16, 64), fa.BF16, 0, ctypes.byref(bad), ctypes.byref(info))
     assert L.fa_status_str(st).decode() == "FA_ERR_ARG"
     # a windowed single query runs on the prefill kernel; split-KV has no window
@@ -206,7 +206,7 @@ def test_window_options_checked():
     assert e.value.name == "FA_ERR_UNSUPPORTED"
     assert fa.plan(1, 1, 16, 16, 64, fa.F32, window=(3, 0))["path_name"] == "f32"
     # the backward takes no window
-    opt = Options(0, 0, 1, 127, 0, 0)
+    opt = Options(0, 0, 1, 127, 0, 0, 0.0, 0.0, 0.0)
     st = L.fa_bwd_ex(*([P] * 6), None, P, P, P, Shape(1, 2, 16, 16, 64), fa.BF16, 0.125, 1, P,
                      fa.bwd_workspace_bytes(1, 2, 16, 16, 64), None, ctypes.byref(opt))
     assert L.fa_status_str(st).decode() == "FA_ERR_UNSUPPORTED"
@@ -230,3 +230,23 @@ def test_kvouter_plan():
     with pytest.raises(fa.FaError) as e:
         fa.plan(1, 1, 16, 16, 64, fa.F32, path=fa.PATH_KVOUTER)
     assert e.value.name == "FA_ERR_UNSUPPORTED"
+
+
+def test_fp8_plan():
+    p = fa.plan(2, 32, 8192, 8192, 128, fa.FP8, True)
+    assert p["path_name"] == "fp8" and p["threads"] == 512 and p["grid"] == 32 * 64
+    assert fa.plan(4, 2, 1, 5000, 64, fa.FP8)["path_name"] == "fp8"   # no split-KV for fp8
+    for kw, st in ((dict(window=(3, 0)), "FA_ERR_UNSUPPORTED"),
+                   (dict(path=fa.PATH_PREFILL), "FA_ERR_UNSUPPORTED"),
+                   (dict(path=fa.PATH_SPLITKV), "FA_ERR_UNSUPPORTED")):
+        with pytest.raises(fa.FaError) as e:
+            fa.plan(1, 1, 16, 16, 64, fa.FP8, **kw)
+        assert e.value.name == st, kw
+    with pytest.raises(fa.FaError) as e:
+        fa.plan(1, 1, 16, 16, 64, fa.BF16, path=fa.PATH_FP8)
+    assert e.value.name == "FA_ERR_UNSUPPORTED"
+    L = fa.lib()
+    info = fa.PlanInfo()
+    bad = Options(0, 0, 0, 0, 0, 0, -1.0, 0.0, 0.0)
+    st = L.fa_plan_query(Shape(1, 1, 16, 16, 64), fa.FP8, 0, ctypes.byref(bad), ctypes.byref(info))
+    assert L.fa_status_str(st).decode() == "FA_ERR_ARG"

@@ -163,3 +163,20 @@ def test_oracle_float32_inputs_upcast_exactly():
     O64, L64 = A.attention_ref(q.astype(np.float64), k.astype(np.float64),
                                v.astype(np.float64), 0.125, False)
     assert np.array_equal(O32, O64) and np.array_equal(L32, L64)
+
+
+def test_e4m3_decoding_used_by_the_fp8_tests():
+    """torch's float8_e4m3fn -> float conversion, which the fp8 tests use to
+    hand the oracle the exact input values, against the OCP E4M3 definition:
+    sign, 4 exponent bits (bias 7), 3 mantissa bits, subnormals at exponent
+    0, NaN for S.1111.111 and no infinities."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    got = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            assert np.isnan(got[c]), c
+            continue
+        val = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        assert got[c] == (-val if s else val), (c, got[c])
