@@ -63,6 +63,9 @@ namespace {
 using namespace asmk;
 static_assert(NW == kBwdThreads / 64, "waves per workgroup");
 
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
 // ---------------------------------------------------------------------------
 // Pass 1: Lg[i] = LSE_i * log2(e) (+inf where LSE = -inf or i >= N) and
 // D_i = rowsum(dO_i * O_i), per (batch, head), Npad rows.
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rowstat_kernel(BwdProblem p, 
 // ---------------------------------------------------------------------------
 // Pass 2: dK and dV.  Workgroup = 4 waves x 64 keys; query stages of 64.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   using St = Stage<D>;
@@ -140,11 +143,18 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D;
   const float* Wg = p.ws + (size_t)bh * 2 * p.Npad;
 
+  // Local window: key j is seen by queries j - off - wr .. j - off + wl
+  // (causal: wr = 0).  LOWQ: a key has a first query; WINDOW: and a last.
+  constexpr bool LOWQ = CAUSAL || WINDOW;
+  const int wl = WINDOW ? min(p.wl, N + kvl) : 0;
+  const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
   // Query stages this workgroup visits.
   const int n_stage_all = (N + St::ROWS - 1) / St::ROWS;
   int s_lo = 0;
-  if (CAUSAL) s_lo = min(max(k0 - off, 0) / St::ROWS, n_stage_all);
-  const int n_stages = k0 < kvl ? n_stage_all - s_lo : 0;
+  if (LOWQ) s_lo = min(max(k0 - off - wr, 0) / St::ROWS, n_stage_all);
+  int s_end = n_stage_all;
+  if (WINDOW) s_end = clampi(floor_div(k0 + kBwdBlockKV - 1 - off + wl, St::ROWS) + 1, s_lo, n_stage_all);
+  const int n_stages = k0 < kvl ? s_end - s_lo : 0;
 
   // ---- K and V fragments of the wave's keys (B operands), zero past kv_len ----
   bf16x8 kf[KBW][DK], vf[KBW][DK];
@@ -203,12 +213,16 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
       agpr_guard(dvacc[kb2][db]);
     }
   const float c = fmaxf(p.scale * kLog2e, 1e-30f);
-  // Causal: query i sees the lane's key j iff i >= j - off; register r of a
-  // step holds query qs0 + 8 (r / 4) + 4 h + r % 4, masked iff
-  // qs0 + 8 (r / 4) + r % 4 < thr.
-  int thr[KBW];
+  // Query i sees the lane's key j iff j - off - wr <= i (causal, window) and
+  // i <= j - off + wl (window); register r of a step holds query
+  // qs0 + 8 (r / 4) + 4 h + r % 4, masked iff qs0 + 8 (r / 4) + r % 4 < thr
+  // or > thr_hi.
+  int thr[KBW], thr_hi[KBW];
 #pragma unroll
-  for (int kb2 = 0; kb2 < KBW; ++kb2) thr[kb2] = jw0 + 32 * kb2 + l32 - off - 4 * h;
+  for (int kb2 = 0; kb2 < KBW; ++kb2) {
+    thr[kb2] = jw0 + 32 * kb2 + l32 - off - wr - 4 * h;
+    thr_hi[kb2] = jw0 + 32 * kb2 + l32 - off + wl - 4 * h;
+  }
 
   // One 32-query step of stage s from buffers (Qs, Gs, Ls).
   auto qstep = [&](int s, int u, const char* Qs, const char* Gs, const float* Ls, auto MASK) __attribute__((always_inline)) {
@@ -248,7 +262,12 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
 #pragma unroll
         for (int kb2 = 0; kb2 < KBW; ++kb2) {
           float pv = fast_exp2(fmaf(sacc[kb2][r], c, -Lv[e]));
-          if constexpr (mask) pv = qs0 + 8 * g + e < thr[kb2] ? 0.f : pv;
+          if constexpr (mask) {
+            const int qi = qs0 + 8 * g + e;
+            bool hide = qi < thr[kb2];
+            if constexpr (WINDOW) hide = hide | (qi > thr_hi[kb2]);
+            pv = hide ? 0.f : pv;
+          }
           const float dsv = pv * (pacc[kb2][r] - Dv[e]);
           pf[kb2][r / 8][r % 8] = (__bf16)pv;
           sf[kb2][r / 8][r % 8] = (__bf16)dsv;
@@ -289,29 +308,52 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
     qstep(s_lo + t, 1, Qs, Gs, Ls, MASK);
   };
 
-  // Causal: the first n_mask stages hold queries that do not see every key
-  // of the workgroup and are masked element by element (an even number, so
-  // that the unmasked loop starts on buffer 0, or all stages).
-  int n_mask = 0;
-  if (CAUSAL) {
-    const int rows = k0 + kBwdBlockKV - 1 - off - s_lo * St::ROWS;  // masked rows from stage s_lo on
-    n_mask = rows > 0 ? min((rows + 2 * St::ROWS - 1) / (2 * St::ROWS) * 2, n_stages) : 0;
-  }
   if (n_stages > 0) load_stage(s_lo, Qs0, Gs0, Ls0);
-  int t = 0;
-  for (; t + 1 < n_mask; t += 2) {
-    iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::true_type{});
-    iteration(t + 1, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, std::true_type{});
+  if constexpr (!WINDOW) {
+    // Causal: the first n_mask stages hold queries that do not see every key
+    // of the workgroup and are masked element by element (an even number, so
+    // that the unmasked loop starts on buffer 0, or all stages).
+    int n_mask = 0;
+    if (CAUSAL) {
+      const int rows = k0 + kBwdBlockKV - 1 - off - s_lo * St::ROWS;  // masked rows from stage s_lo on
+      n_mask = rows > 0 ? min((rows + 2 * St::ROWS - 1) / (2 * St::ROWS) * 2, n_stages) : 0;
+    }
+    int t = 0;
+    for (; t + 1 < n_mask; t += 2) {
+      iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::true_type{});
+      iteration(t + 1, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, std::true_type{});
+    }
+    if (t < n_mask) {  // n_mask == n_stages, odd: the last stage
+      iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::true_type{});
+      ++t;
+    }
+    for (; t + 1 < n_stages; t += 2) {
+      iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::false_type{});
+      iteration(t + 1, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, std::false_type{});
+    }
+    if (t < n_stages) iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::false_type{});
+  } else {
+    // Window: stages before nA hold queries before some key's first viewer,
+    // stages from nC on queries past some key's last viewer; both masked,
+    // the stages between are seen whole.  Stage t uses buffer t % 2.
+    const int nA = clampi(floor_div(k0 + kBwdBlockKV - 1 - off - wr + St::ROWS - 1, St::ROWS) - s_lo,
+                          0, n_stages);
+    const int nC = clampi(floor_div(k0 - off + wl - (St::ROWS - 1), St::ROWS) + 1 - s_lo, nA, n_stages);
+    auto segment = [&](int t, int t_end, auto MASK) __attribute__((always_inline)) {
+      if ((t & 1) && t < t_end) {
+        iteration(t, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, MASK);
+        ++t;
+      }
+      for (; t + 1 < t_end; t += 2) {
+        iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, MASK);
+        iteration(t + 1, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, MASK);
+      }
+      if (t < t_end) iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, MASK);
+    };
+    segment(0, nA, std::true_type{});
+    segment(nA, nC, std::false_type{});
+    segment(nC, n_stages, std::true_type{});
   }
-  if (t < n_mask) {  // n_mask == n_stages, odd: the last stage
-    iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::true_type{});
-    ++t;
-  }
-  for (; t + 1 < n_stages; t += 2) {
-    iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::false_type{});
-    iteration(t + 1, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, std::false_type{});
-  }
-  if (t < n_stages) iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::false_type{});
 
 #pragma unroll
   for (int kb2 = 0; kb2 < KBW; ++kb2)
@@ -351,7 +393,7 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
 // ---------------------------------------------------------------------------
 // Pass 3: dQ.  Workgroup = 4 waves x 64 queries; key stages of 64.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   using St = Stage<D>;
@@ -382,8 +424,14 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   const int q0 = qt * kBwdBlockQ;
   const int qw0 = q0 + ws * QW;
   const int q_last = min(q0 + kBwdBlockQ, N) - 1;
-  const int kv_end = CAUSAL ? min(kvl, q_last + off + 1) : kvl;
-  const int n_stages = kv_end > 0 ? (kv_end + St::ROWS - 1) / St::ROWS : 0;
+  // Local window: query i sees keys i + off - wl .. i + off + wr (causal: wr = 0).
+  constexpr bool UPPER = CAUSAL || WINDOW;
+  const int wl = WINDOW ? min(p.wl, N + kvl) : 0;
+  const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
+  const int kv_end = UPPER ? min(kvl, q_last + off + wr + 1) : kvl;
+  // first key stage (window: the first query's first key)
+  const int t0 = WINDOW ? max(0, q0 + off - wl) / St::ROWS : 0;
+  const int n_stages = kv_end > t0 * St::ROWS ? (kv_end + St::ROWS - 1) / St::ROWS - t0 : 0;
 
   const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
   const __bf16* Gg = (const __bf16*)p.dout + (size_t)bh * N * D;
@@ -396,6 +444,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   bf16x8 qf[NQB][DK], gf[NQB][DK];
   float Lq[NQB], Dq[NQB];
   int lim[NQB];                  // last key the lane's query sees
+  int lim_lo[NQB];               // first key (window)
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int row = qw0 + 32 * qb + l32;
@@ -408,7 +457,8 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
     }
     Lq[qb] = Wg[row];            // row < Npad
     Dq[qb] = Wg[p.Npad + row];
-    lim[qb] = CAUSAL ? min(row + off, kvl - 1) : kvl - 1;
+    lim[qb] = UPPER ? min(row + off + wr, kvl - 1) : kvl - 1;
+    lim_lo[qb] = row + off - wl;
   }
 
   uint32_t soff[St::BPW];
@@ -475,7 +525,9 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
         float pv = fast_exp2(fmaf(sacc[qb][r], c, -Lq[qb]));
         if constexpr (mask) {
           const int key = kk0 + 8 * (r / 4) + 4 * h + r % 4;
-          pv = key > lim[qb] ? 0.f : pv;
+          bool hide = key > lim[qb];
+          if constexpr (WINDOW) hide = hide | (key < lim_lo[qb]);
+          pv = hide ? 0.f : pv;
         }
         sf[qb][r / 8][r % 8] = (__bf16)(pv * (pacc[qb][r] - Dq[qb]));
       }
@@ -500,28 +552,52 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
                        __attribute__((always_inline)) {
     wait_vm0();
     __syncthreads();
-    if (t + 1 < n_stages) load_stage(t + 1, Kn, Vn);
-    kstep(t, 0, Ks, Vs, MASK);
-    kstep(t, 1, Ks, Vs, MASK);
+    if (t + 1 < n_stages) load_stage(t0 + t + 1, Kn, Vn);
+    kstep(t0 + t, 0, Ks, Vs, MASK);
+    kstep(t0 + t, 1, Ks, Vs, MASK);
   };
 
   // Stages before n_clean (an even number) are seen whole by every query of
   // the workgroup: no key past kv_len and, causal, none past the first
   // query's last key.  The rest are masked element by element.
-  int n_clean = kvl / St::ROWS;
-  if (CAUSAL) n_clean = min(n_clean, q0 + off + 1 > 0 ? (q0 + off + 1) / St::ROWS : 0);
-  n_clean = min(n_clean, n_stages) / 2 * 2;
-  if (n_stages > 0) load_stage(0, Ks0, Vs0);
-  int t = 0;
-  for (; t < n_clean; t += 2) {
-    iteration(t, Ks0, Vs0, Ks1, Vs1, std::false_type{});
-    iteration(t + 1, Ks1, Vs1, Ks0, Vs0, std::false_type{});
+  if (n_stages > 0) load_stage(t0, Ks0, Vs0);
+  if constexpr (!WINDOW) {
+    int n_clean = kvl / St::ROWS;
+    if (CAUSAL) n_clean = min(n_clean, q0 + off + 1 > 0 ? (q0 + off + 1) / St::ROWS : 0);
+    n_clean = min(n_clean, n_stages) / 2 * 2;
+    int t = 0;
+    for (; t < n_clean; t += 2) {
+      iteration(t, Ks0, Vs0, Ks1, Vs1, std::false_type{});
+      iteration(t + 1, Ks1, Vs1, Ks0, Vs0, std::false_type{});
+    }
+    for (; t + 1 < n_stages; t += 2) {
+      iteration(t, Ks0, Vs0, Ks1, Vs1, std::true_type{});
+      iteration(t + 1, Ks1, Vs1, Ks0, Vs0, std::true_type{});
+    }
+    if (t < n_stages) iteration(t, Ks0, Vs0, Ks1, Vs1, std::true_type{});
+  } else {
+    // Window: stages before nA hold keys before the last query's first key,
+    // stages from nC on keys past the first query's last key (or kv_len);
+    // both masked, the stages between are seen whole.  Stage t uses buffer
+    // t % 2.
+    const int nA = clampi(floor_div(q_last + off - wl + St::ROWS - 1, St::ROWS) - t0, 0, n_stages);
+    const int last_all = min(UPPER ? q0 + off + wr : kvl - 1, kvl - 1);  // last key every query sees
+    const int nC = clampi(floor_div(last_all - (St::ROWS - 1), St::ROWS) + 1 - t0, nA, n_stages);
+    auto segment = [&](int t, int t_end, auto MASK) __attribute__((always_inline)) {
+      if ((t & 1) && t < t_end) {
+        iteration(t, Ks1, Vs1, Ks0, Vs0, MASK);
+        ++t;
+      }
+      for (; t + 1 < t_end; t += 2) {
+        iteration(t, Ks0, Vs0, Ks1, Vs1, MASK);
+        iteration(t + 1, Ks1, Vs1, Ks0, Vs0, MASK);
+      }
+      if (t < t_end) iteration(t, Ks0, Vs0, Ks1, Vs1, MASK);
+    };
+    segment(0, nA, std::true_type{});
+    segment(nA, nC, std::false_type{});
+    segment(nC, n_stages, std::true_type{});
   }
-  for (; t + 1 < n_stages; t += 2) {
-    iteration(t, Ks0, Vs0, Ks1, Vs1, std::true_type{});
-    iteration(t + 1, Ks1, Vs1, Ks0, Vs0, std::true_type{});
-  }
-  if (t < n_stages) iteration(t, Ks0, Vs0, Ks1, Vs1, std::true_type{});
 
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb)
@@ -559,14 +635,24 @@ hipError_t launch_bwd_d(const BwdProblem& p, hipStream_t stream) {
   if (p.M > 0) {
     const int n_kt = (p.M + kBwdBlockKV - 1) / kBwdBlockKV;
     const dim3 grid((unsigned)(bh * n_kt));
-    if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, block, 0, stream, p, n_kt);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, block, 0, stream, p, n_kt);
+    if (p.window) {
+      if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), grid, block, 0, stream, p, n_kt);
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), grid, block, 0, stream, p, n_kt);
+    } else {
+      if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), grid, block, 0, stream, p, n_kt);
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), grid, block, 0, stream, p, n_kt);
+    }
   }
   if (p.N > 0) {
     const int n_qt = (p.N + kBwdBlockQ - 1) / kBwdBlockQ;
     const dim3 grid((unsigned)(bh * n_qt));
-    if (p.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, block, 0, stream, p, n_qt);
-    else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, block, 0, stream, p, n_qt);
+    if (p.window) {
+      if (p.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), grid, block, 0, stream, p, n_qt);
+      else hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), grid, block, 0, stream, p, n_qt);
+    } else {
+      if (p.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), grid, block, 0, stream, p, n_qt);
+      else hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), grid, block, 0, stream, p, n_qt);
+    }
   }
   return hipGetLastError();
 }

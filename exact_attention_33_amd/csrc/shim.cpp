@@ -163,7 +163,6 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   const bool win = opt && opt->window;
   if (win && (opt->window_left < 0 || opt->window_right < 0))
     return fail(FA_ERR_ARG, "fa_bwd: options.window_left and window_right must be >= 0");
-  if (win) return fail(FA_ERR_UNSUPPORTED, "fa_bwd: the backward kernels take no window");
   if (s.B < 0 || s.H < 0 || s.N < 0 || s.M < 0 || s.D < 0)
     return fail(FA_ERR_SHAPE, "fa_bwd: B, H, N, M and D must be non-negative");
   if (dtype != FA_BF16)

@@ -210,8 +210,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* fa_bwd_ex -- fa_bwd for a forward run with options `opt` (NULL = none):
- * a window must be the one the forward used.  `path` and `split_keys` are
- * ignored. */
+ * a window must be the one the forward used (the gradients above then run
+ * over the keys visible under it).  `path`, `split_keys`, the fp8 descales
+ * and `kvouter_query_tiles` are ignored. */
 fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, const int32_t* kv_len, void* dq,
                     void* dk, void* dv, fa_shape s, fa_dtype dtype, float scale, int causal,

@@ -21,9 +21,9 @@ def _rand(seed, B, H, N, M, D):
             rng.standard_normal((B, H, M, D)), rng.standard_normal((B, H, N, D)))
 
 
-def _loss(q, k, v, do, scale, causal, kv_len):
+def _loss(q, k, v, do, scale, causal, kv_len, window=None):
     """The scalar whose gradient the backward returns: sum(dO * O)."""
-    O, _ = attention_ref(q, k, v, scale, causal, kv_len)
+    O, _ = attention_ref(q, k, v, scale, causal, kv_len, window=window)
     return float(np.sum(do * O))
 
 
@@ -115,5 +115,20 @@ def pin_causal_row0(bwd):
     assert np.max(np.abs(dq[0, 0, 1])) > 1e-3
 
 
-ALL_BWD_PINS = [pin_finite_differences, pin_delta_shortcut, pin_single_key,
+def pin_window_finite_differences(bwd):
+    """Central differences through the windowed forward oracle: one- and
+    two-sided bands, causal and not, with kv_len."""
+    h = 1e-5
+    for seed, B, H, N, M, D, scale, causal, kvl, win in [
+            (51, 1, 1, 6, 6, 3, 0.7, True, None, (2, 0)),
+            (52, 1, 1, 5, 7, 3, 0.6, False, [6], (1, 2))]:
+        q, k, v, do = _rand(seed, B, H, N, M, D)
+        dq, dk, dv, _ = bwd(q, k, v, do, scale, causal, kvl, window=win)
+        for name, x, g in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
+            fd = _central_diff(lambda: _loss(q, k, v, do, scale, causal, kvl, win), x, h)
+            err = np.max(np.abs(np.asarray(g) - fd))
+            assert err < 1e-7 * max(1.0, np.max(np.abs(fd))), (name, seed, err)
+
+
+ALL_BWD_PINS = [pin_finite_differences, pin_window_finite_differences, pin_delta_shortcut, pin_single_key,
                 pin_uniform_scores, pin_dk_sums_to_zero, pin_causal_row0]

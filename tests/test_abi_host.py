@@ -205,11 +205,11 @@ def test_window_options_checked():
         fa.plan(4, 2, 1, 50000, 128, path=fa.PATH_SPLITKV, window=(127, 0))
     assert e.value.name == "FA_ERR_UNSUPPORTED"
     assert fa.plan(1, 1, 16, 16, 64, fa.F32, window=(3, 0))["path_name"] == "f32"
-    # the backward takes no window
-    opt = Options(0, 0, 1, 127, 0, 0, 0.0, 0.0, 0.0)
+    # the backward checks its window the same way
+    opt = Options(0, 0, 1, -1, 0, 0, 0.0, 0.0, 0.0)
     st = L.fa_bwd_ex(*([P] * 6), None, P, P, P, Shape(1, 2, 16, 16, 64), fa.BF16, 0.125, 1, P,
                      fa.bwd_workspace_bytes(1, 2, 16, 16, 64), None, ctypes.byref(opt))
-    assert L.fa_status_str(st).decode() == "FA_ERR_UNSUPPORTED"
+    assert L.fa_status_str(st).decode() == "FA_ERR_ARG"
 
 
 def test_kvouter_plan():

@@ -20,7 +20,7 @@ from tests.gpu_helpers import bwd_bound, compare_bwd, host64
 pytestmark = pytest.mark.gpu
 
 
-def _run(B, H, N, M, D, causal, kv_len, seed, device, poison=True):
+def _run(B, H, N, M, D, causal, kv_len, seed, device, poison=True, window=None):
     import torch
     q, k, v = inputs.qkv_device(seed, B, H, N, M, D, "bf16", device)
     do = inputs.grad_device(seed + 1000, B, H, N, D, "bf16", device)
@@ -30,23 +30,23 @@ def _run(B, H, N, M, D, causal, kv_len, seed, device, poison=True):
         if poison:
             inputs.poison_tail(k, v, kv_len)
     scale = 1.0 / math.sqrt(D)
-    o, lse = fa.fwd(q, k, v, scale=scale, causal=causal, kv_len=kvt)
-    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale=scale, causal=causal, kv_len=kvt)
+    o, lse = fa.fwd(q, k, v, scale=scale, causal=causal, kv_len=kvt, window=window)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale=scale, causal=causal, kv_len=kvt, window=window)
     torch.cuda.synchronize()
     return dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, scale=scale)
 
 
-def _check_head(t, b, h, causal, kvl, what):
+def _check_head(t, b, h, causal, kvl, what, window=None):
     q, k, v, do = (host64(t[n][b, h]) for n in ("q", "k", "v", "do"))
     k = np.where(np.isnan(k), 0.0, k)          # the poisoned tail is never read
     v = np.where(np.isnan(v), 0.0, v)
     O_gpu, L_gpu = host64(t["o"][b, h]), host64(t["lse"][b, h])
-    r = head_backward(q, k, v, do, t["scale"], causal, kvl)
+    r = head_backward(q, k, v, do, t["scale"], causal, kvl, window)
     # the exact forward's LSE for the same head
     S = t["scale"] * (q @ k[:kvl].T)
     N = q.shape[0]
     from oracle.attention import visible_mask
-    S = np.where(visible_mask(N, kvl, causal), S, -np.inf)
+    S = np.where(visible_mask(N, kvl, causal, window), S, -np.inf)
     with np.errstate(divide="ignore", invalid="ignore"):
         m = S.max(axis=1) if kvl else np.full(N, -np.inf)
         L_ref = np.where(np.isfinite(m), m + np.log(np.sum(np.exp(S - m[:, None]), axis=1)), -np.inf) \
@@ -89,6 +89,31 @@ def test_bwd_matches_oracle(case):
     for b in range(B):
         for h in range(H):
             _check_head(t, b, h, causal, kvs[b], f"{case} b{b} h{h}")
+
+
+WINDOW_CASES = [
+    # B, H, N, M, D, causal, kv_len, window
+    (1, 2, 300, 300, 128, True, None, (127, 0)),       # the pages' 128-wide window
+    (1, 2, 600, 600, 64, True, None, (300, 0)),        # wider than a key tile
+    (2, 2, 257, 400, 128, False, [400, 199], (50, 70)),  # two-sided, N != M, kv_len
+    (1, 1, 200, 90, 128, True, None, (10, 0)),         # N > M: early rows see nothing
+    (1, 2, 130, 130, 64, False, None, (0, 0)),         # one key per query
+    (1, 1, 700, 700, 128, True, None, (5000, 0)),      # wider than the sequence
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "B{}H{}N{}M{}D{}{}w{}-{}".format(
+    *c[:5], "c" if c[5] else "", *c[7]))
+def test_bwd_window_matches_oracle(case):
+    import torch
+    B, H, N, M, D, causal, kv_len, win = case
+    print(f"[bwd] window case {case}", flush=True)
+    t = _run(B, H, N, M, D, causal, kv_len, seed=140 + N + M, device=torch.device("cuda:0"),
+             window=win)
+    kvs = clamp_kv_len(kv_len, B, M)
+    for b in range(B):
+        for h in range(H):
+            _check_head(t, b, h, causal, kvs[b], f"{case} b{b} h{h}", window=win)
 
 
 def test_bwd_degenerate_sizes():
