@@ -130,5 +130,5 @@ def pin_window_finite_differences(bwd):
             assert err < 1e-7 * max(1.0, np.max(np.abs(fd))), (name, seed, err)
 
 
-ALL_BWD_PINS = [pin_finite_differences, pin_window_finite_differences, pin_delta_shortcut, pin_single_key,
-                pin_uniform_scores, pin_dk_sums_to_zero, pin_causal_row0]
+ALL_BWD_PINS = [pin_finite_differences, pin_window_finite_differences, pin_delta_shortcut,
+                pin_single_key, pin_uniform_scores, pin_dk_sums_to_zero, pin_causal_row0]
