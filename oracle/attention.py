@@ -36,11 +36,17 @@ Readings where the pages leave a step open (each listed in the design notes):
     128-wide window is ``(127, 0)``: each query sees its 128 most recent keys.
     It is an elementwise mask that does not depend on the scores, the kind
     "Understanding FlashAttention", Attention, allows.
+  * any other elementwise mask (the same section: mask() covers causal
+    masking "and other kinds", each a constant that does not depend on the
+    scores): ``mask`` is a boolean array [Bm, Hm, N, M] (Bm in {1, B}, Hm in
+    {1, H}; size 1 means shared by every batch or head); key j is visible to
+    query i of (b, h) only if ``mask[b or 0, h or 0, i, j]`` is true, on top of
+    kv_len, causal and the window.
 """
 import numpy as np
 
 __all__ = ["visible_mask", "safe_softmax", "attention_ref", "attention_rows",
-           "attention_probs", "clamp_kv_len"]
+           "attention_probs", "clamp_kv_len", "mask_of_head"]
 
 
 def clamp_kv_len(kv_len, B, M):
@@ -53,13 +59,14 @@ def clamp_kv_len(kv_len, B, M):
     return [int(min(max(int(x), 0), M)) for x in kv]
 
 
-def visible_mask(N, kv_len_b, causal, window=None):
+def visible_mask(N, kv_len_b, causal, window=None, allow=None):
     """Boolean [N, kv_len_b]: is key j visible to query i.
 
     Keys at or past ``kv_len_b`` are not part of the matrix at all.  With
     ``causal`` the bottom-right alignment applies: j <= i + (kv_len_b - N).
     ``window = (left, right)`` further keeps only
-    i + off - left <= j <= i + off + right.
+    i + off - left <= j <= i + off + right.  ``allow`` (boolean [N, >= kv_len_b])
+    further keeps only the pairs it marks true.
     """
     i = np.arange(N)[:, None]
     j = np.arange(kv_len_b)[None, :]
@@ -72,6 +79,11 @@ def visible_mask(N, kv_len_b, causal, window=None):
         if left < 0 or right < 0:
             raise ValueError("window bounds must be >= 0")
         vis &= (j >= i + off - left) & (j <= i + off + right)
+    if allow is not None:
+        allow = np.asarray(allow, dtype=bool)
+        if allow.shape[0] != N or allow.shape[1] < kv_len_b:
+            raise ValueError("allow must be [N, >= kv_len] booleans")
+        vis &= allow[:, :kv_len_b]
     return vis
 
 
@@ -96,7 +108,7 @@ def _scores(q, k, scale):
     return np.float64(scale) * (q @ k.T)
 
 
-def _head(q, k, v, scale, causal, kvl, rows=None, window=None):
+def _head(q, k, v, scale, causal, kvl, rows=None, window=None, allow=None):
     """One (batch, head) problem.  q [N,D], k/v [M,D] fp64.
 
     Returns O [len(rows), D] and LSE [len(rows)] for the requested query rows
@@ -111,7 +123,7 @@ def _head(q, k, v, scale, causal, kvl, rows=None, window=None):
     if kvl == 0 or rows.size == 0:
         return O, LSE
     S = _scores(q[rows], k, scale)                      # step 1: materialise S
-    vis = visible_mask(N, kvl, causal, window)[rows]
+    vis = visible_mask(N, kvl, causal, window, allow)[rows]
     S = np.where(vis, S, -np.inf)                       # step 2: mask
     for r in range(rows.size):                          # steps 3-5: softmax
         p, m, l = safe_softmax(S[r])
@@ -122,7 +134,18 @@ def _head(q, k, v, scale, causal, kvl, rows=None, window=None):
     return O, LSE
 
 
-def attention_ref(q, k, v, scale, causal=False, kv_len=None, window=None):
+def mask_of_head(mask, b, h):
+    """The [N, M] slice of an elementwise mask [Bm, Hm, N, M] that applies to
+    (batch b, head h); a size-1 batch or head axis is shared.  None -> None."""
+    if mask is None:
+        return None
+    mask = np.asarray(mask, dtype=bool)
+    if mask.ndim != 4:
+        raise ValueError("mask must be [Bm, Hm, N, M]")
+    return mask[b if mask.shape[0] > 1 else 0, h if mask.shape[1] > 1 else 0]
+
+
+def attention_ref(q, k, v, scale, causal=False, kv_len=None, window=None, mask=None):
     """Exact attention forward for [B, H, N, D] / [B, H, M, D] inputs.
 
     Returns (O [B,H,N,D] fp64, LSE [B,H,N] fp64).
@@ -140,17 +163,18 @@ def attention_ref(q, k, v, scale, causal=False, kv_len=None, window=None):
     for b in range(B):
         for h in range(H):
             O[b, h], LSE[b, h] = _head(q[b, h], k[b, h], v[b, h], scale,
-                                       causal, kvs[b], window=window)
+                                       causal, kvs[b], window=window,
+                                       allow=mask_of_head(mask, b, h))
     return O, LSE
 
 
-def attention_rows(q, k, v, scale, causal, kv_len, picks, window=None):
+def attention_rows(q, k, v, scale, causal, kv_len, picks, window=None, mask=None):
     """The same definition evaluated only for selected outputs.
 
     ``picks`` is a sequence of (b, h, i).  ``q`` may be [B,H,N,D] or a callable
     ``q(b, h) -> [N, D]`` (likewise ``k``, ``v`` with [M, D]) so that large
     device tensors can be copied back one head at a time.  Returns
-    (O [P, D], LSE [P]) in fp64.
+    (O [P, D], LSE [P]) in fp64.  ``mask`` is as in ``attention_ref``.
     """
     def head_of(t, b, h):
         return np.asarray(t(b, h) if callable(t) else t[b, h], dtype=np.float64)
@@ -168,7 +192,8 @@ def attention_rows(q, k, v, scale, causal, kv_len, picks, window=None):
             outO = np.zeros((len(picks), D))
         kvl = min(max(int(M if kv_len is None else np.asarray(kv_len).reshape(-1)[b]), 0), M)
         rows = [i for _, i in lst]
-        O, L = _head(qh, kh, vh, scale, causal, kvl, rows, window=window)
+        O, L = _head(qh, kh, vh, scale, causal, kvl, rows, window=window,
+                     allow=mask_of_head(mask, b, h))
         for r, (idx, _) in enumerate(lst):
             outO[idx] = O[r]
             outL[idx] = L[r]

@@ -22,10 +22,11 @@ def _rand(seed, B, H, N, M, D):
             rng.standard_normal((B, H, M, D)))
 
 
-def brute_force(q, k, v, scale, causal, kv_len, window=None):
+def brute_force(q, k, v, scale, causal, kv_len, window=None, mask=None):
     """50-digit evaluation straight from the formula, without the max shift:
     p_j = exp(s_j) / sum exp(s_j), O = sum p_j v_j, LSE = log sum exp(s_j).
-    ``window = (left, right)``: only keys i + off - left .. i + off + right."""
+    ``window = (left, right)``: only keys i + off - left .. i + off + right.
+    ``mask`` (booleans [Bm, Hm, N, M], size-1 axes shared): only keys it marks."""
     B, H, N, D = q.shape
     M = k.shape[2]
     O = np.zeros((B, H, N, D))
@@ -37,7 +38,9 @@ def brute_force(q, k, v, scale, causal, kv_len, window=None):
                 off = kvl - N
                 keys = [j for j in range(kvl)
                         if (not causal or j <= i + off) and
-                        (window is None or i + off - window[0] <= j <= i + off + window[1])]
+                        (window is None or i + off - window[0] <= j <= i + off + window[1]) and
+                        (mask is None or mask[min(b, mask.shape[0] - 1),
+                                              min(h, mask.shape[1] - 1), i, j])]
                 if not keys:
                     continue
                 s = {j: mpmath.mpf(scale) * mpmath.fsum(
@@ -251,11 +254,90 @@ def pin_window_locality(attn):
     assert changed.tolist() == [i in (3, 4, 5) for i in range(10)], changed
 
 
+def _rand_mask(seed, shape, p_keep):
+    return np.random.default_rng(seed).random(shape) < p_keep
+
+
+def pin_mask_brute_force(attn):
+    """Elementwise masks against 50-digit arithmetic: shared and per-head
+    masks, with causal, kv_len and a window on top, rows that the mask
+    empties, N != M."""
+    cases = [
+        # seed, B, H, N, M, D, scale, causal, kv_len, window, mask shape, keep
+        (61, 1, 1, 7, 7, 3, 0.6, False, None, None, (1, 1, 7, 7), 0.5),
+        (62, 2, 2, 5, 8, 3, 0.8, True, [8, 6], None, (1, 2, 5, 8), 0.6),
+        (63, 2, 1, 6, 6, 2, 0.9, False, None, (2, 1), (2, 1, 6, 6), 0.7),
+        (64, 1, 2, 4, 9, 3, 1.1, False, [7], None, (1, 1, 4, 9), 0.3),
+    ]
+    for seed, B, H, N, M, D, scale, causal, kvl, win, mshape, keep in cases:
+        q, k, v = _rand(seed, B, H, N, M, D)
+        mask = _rand_mask(seed + 100, mshape, keep)
+        mask[0, 0, 1] = False                                   # a row the mask empties
+        O, L = attn(q, k, v, scale, causal, kvl, window=win, mask=mask)
+        Ob, Lb = brute_force(q, k, v, scale, causal, kvl, window=win, mask=mask)
+        assert np.array_equal(np.isneginf(L), np.isneginf(Lb)), ("empty rows", seed)
+        assert np.isneginf(L[0, 0, 1]) and not O[0, 0, 1].any(), ("emptied row", seed)
+        fin = np.isfinite(Lb)
+        assert np.max(np.abs(O - Ob)) <= 4e-15, ("O vs brute force", seed)
+        assert np.max(np.abs(L[fin] - Lb[fin])) <= 4e-15, ("LSE vs brute force", seed)
+
+
+def pin_mask_as_key_subset(attn):
+    """Row i under a mask is plain attention of query i over just the keys
+    the mask keeps: gather those keys and call the unmasked function."""
+    q, k, v = _rand(65, 1, 2, 6, 9, 4)
+    mask = _rand_mask(66, (1, 2, 6, 9), 0.5)
+    O, L = attn(q, k, v, 0.7, False, None, mask=mask)
+    for h in range(2):
+        for i in range(6):
+            keep = np.flatnonzero(mask[0, h, i])
+            if keep.size == 0:
+                assert L[0, h, i] == -np.inf and not O[0, h, i].any()
+                continue
+            Oi, Li = attn(q[:, h:h + 1, i:i + 1], k[:, h:h + 1, keep], v[:, h:h + 1, keep],
+                          0.7, False, None)
+            assert np.max(np.abs(O[0, h, i] - Oi[0, 0, 0])) <= 1e-15, (h, i)
+            assert abs(L[0, h, i] - Li[0, 0, 0]) <= 1e-15, (h, i)
+
+
+def pin_mask_matches_causal_and_window(attn):
+    """A mask that spells out the bottom-right causal pattern (or a band)
+    gives the result of the causal flag (or the window) bit for bit."""
+    q, k, v = _rand(67, 2, 1, 5, 8, 3)
+    i = np.arange(5)[:, None]
+    j = np.arange(8)[None, :]
+    causal_bits = (j <= i + 3)[None, None]
+    O1, L1 = attn(q, k, v, 0.6, True, None)
+    O2, L2 = attn(q, k, v, 0.6, False, None, mask=causal_bits)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    band = ((j >= i + 3 - 2) & (j <= i + 3 + 1))[None, None]
+    O1, L1 = attn(q, k, v, 0.6, False, None, window=(2, 1))
+    O2, L2 = attn(q, k, v, 0.6, False, None, mask=band)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def pin_mask_broadcast(attn):
+    """A [1, 1, N, M] mask applies to every batch and head: the same as the
+    mask repeated to [B, H, N, M]; a per-head mask differs per head."""
+    q, k, v = _rand(68, 2, 3, 4, 6, 3)
+    m1 = _rand_mask(69, (1, 1, 4, 6), 0.5)
+    O1, L1 = attn(q, k, v, 0.8, False, None, mask=m1)
+    O2, L2 = attn(q, k, v, 0.8, False, None, mask=np.broadcast_to(m1, (2, 3, 4, 6)).copy())
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+    mh = _rand_mask(70, (1, 3, 4, 6), 0.5)
+    O3, _ = attn(q, k, v, 0.8, False, None, mask=mh)
+    for h in range(3):
+        Oh, _ = attn(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], 0.8, False, None,
+                     mask=mh[:, h:h + 1])
+        assert np.array_equal(O3[:, h], Oh[:, 0]), h
+
+
 ALL_ATTN_PINS = [pin_brute_force, pin_rows_sum_to_one, pin_causal_row0,
                  pin_uniform_scores, pin_overflow_shift, pin_single_and_two_keys,
                  pin_key_permutation, pin_decode_history, pin_masked_rows,
                  pin_scale_on_scores, pin_window_brute_force, pin_window_single_key,
-                 pin_window_locality]
+                 pin_window_locality, pin_mask_brute_force, pin_mask_as_key_subset,
+                 pin_mask_matches_causal_and_window, pin_mask_broadcast]
 
 
 def read_golden(name):

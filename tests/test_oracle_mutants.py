@@ -22,6 +22,12 @@ MUTANTS = {
     "window_top_left": ("vis &= (j >= i + off - left) & (j <= i + off + right)",
                         "vis &= (j >= i - left) & (j <= i + right)"),
     "window_ignored": ("vis &= (j >= i + off - left) & (j <= i + off + right)", "pass"),
+    "mask_ignored": ("        vis &= allow[:, :kv_len_b]\n", "        pass\n"),
+    "mask_inverted": ("        vis &= allow[:, :kv_len_b]\n", "        vis &= ~allow[:, :kv_len_b]\n"),
+    "mask_transposed_broadcast": ("mask[b if mask.shape[0] > 1 else 0, h if mask.shape[1] > 1 else 0]",
+                                  "mask[h if mask.shape[0] > 1 else 0, b if mask.shape[1] > 1 else 0]"),
+    "mask_shared_by_heads": ("mask[b if mask.shape[0] > 1 else 0, h if mask.shape[1] > 1 else 0]",
+                             "mask[b if mask.shape[0] > 1 else 0, 0]"),
     "scale_twice": ("return np.float64(scale) * (q @ k.T)",
                     "return np.float64(scale) ** 2 * (q @ k.T)"),
     "scale_dropped": ("return np.float64(scale) * (q @ k.T)", "return (q @ k.T)"),
@@ -44,8 +50,8 @@ def load_mutant(old, new):
 def test_pins_catch_mutant(name):
     mod = load_mutant(*MUTANTS[name])
 
-    def attn(q, k, v, scale, causal, kv_len, window=None):
-        return mod.attention_ref(q, k, v, scale, causal, kv_len, window=window)
+    def attn(q, k, v, scale, causal, kv_len, window=None, mask=None):
+        return mod.attention_ref(q, k, v, scale, causal, kv_len, window=window, mask=mask)
 
     caught = []
     with np.errstate(all="ignore"):

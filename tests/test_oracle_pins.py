@@ -9,8 +9,8 @@ from oracle import streamed as S
 from tests import pins
 
 
-def oracle_attn(q, k, v, scale, causal, kv_len, window=None):
-    return A.attention_ref(q, k, v, scale, causal, kv_len, window=window)
+def oracle_attn(q, k, v, scale, causal, kv_len, window=None, mask=None):
+    return A.attention_ref(q, k, v, scale, causal, kv_len, window=window, mask=mask)
 
 
 @pytest.mark.parametrize("pin", pins.ALL_ATTN_PINS, ids=lambda p: p.__name__)
