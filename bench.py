@@ -15,7 +15,11 @@ the hot path:
   5. the key/value-outer ablation of the same prefill (the first version's
      loop order), one query tile per workgroup and one workgroup per head;
   6. the same prefill on E4M3 inputs (the prefill's tensors quantized per
-     tensor) on the fp8 matrix cores.
+     tensor) on the fp8 matrix cores;
+  7. the same prefill with an element mask shared by every batch and head:
+     8 packed documents (a query sees its own document's keys), and an
+     unstructured mask keeping each (query, key) pair with probability 1/2
+     (every tile applies bits); the tile-list pre-pass is inside the timing.
 Inputs are N(0, 1) drawn on the device from fixed seeds and are resident in
 HBM before timing starts.
 
@@ -78,7 +82,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "window", "kvouter",
-                                       "fp8", "copy"],
+                                       "fp8", "mask", "copy"],
                     default="all",
                     help="run one leg only (for counter runs); 'copy' runs a plain "
                          "device copy of known size for counter calibration")
@@ -125,15 +129,18 @@ def main():
     do_w = args.only in ("all", "window")
     do_k = args.only in ("all", "kvouter")
     do_8 = args.only in ("all", "fp8")
+    do_m = args.only in ("all", "mask")
     KVO = (("tile_per_group", 1), ("head_per_group", 1 << 20))  # 256-query tiles per workgroup
     WINDOWS = (128, 2048)  # keys per query (causal band: window_left = W - 1)
 
     # ---- inputs, resident in HBM before timing ----
-    if do_p:
+    if do_p or do_b or do_w or do_k or do_8 or do_m:
+        # the long prefill's Q, K, V, shared by every prefill leg
         qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
+        scale_p = 1.0 / math.sqrt(wp.D)
+    if do_p:
         op = torch.empty_like(qp)
         lp = torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
-        scale_p = 1.0 / math.sqrt(wp.D)
         flop_p = 4.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0   # causal convention
     if do_d:
         kvl_h = inputs.kv_lens(wd.kv_seed, wd.B, *wd.kv_range)
@@ -150,9 +157,6 @@ def main():
     if do_b:
         # backward of the same causal prefill: the forward's O and LSE, an
         # upstream gradient dO ~ N(0, 1), and the gradient buffers
-        if not do_p:
-            qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
-            scale_p = 1.0 / math.sqrt(wp.D)
         ob, lb = fa.fwd(qp, kp, vp, scale=scale_p, causal=True)
         gb = inputs.grad_device(wp.seed + 1000, wp.B, wp.H, wp.N, wp.D, "bf16", dev)
         dqb, dkb, dvb = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
@@ -163,9 +167,6 @@ def main():
         flop_b = 10.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0
     if do_8:
         # the prefill's tensors quantized per tensor to E4M3 (scale = amax / 448)
-        if not (do_p or do_b):
-            qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
-            scale_p = 1.0 / math.sqrt(wp.D)
         q8s, d8 = [], []
         for t in (qp, kp, vp):
             d = float(t.abs().max()) / 448.0
@@ -175,21 +176,26 @@ def main():
         l8 = torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
         flop_8 = 4.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0
     if do_k:
-        if not (do_p or do_b or do_w):
-            qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
-            scale_p = 1.0 / math.sqrt(wp.D)
         ok_, lk_ = torch.empty_like(qp), torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
         wsk = torch.empty(fa.workspace_bytes(wp.B, wp.H, wp.N, wp.M, wp.D, causal=True,
                                              path=fa.PATH_KVOUTER), dtype=torch.uint8, device=dev)
         flop_k = 4.0 * wp.B * wp.H * wp.N * wp.M * wp.D / 2.0
     if do_w:
-        if not (do_p or do_b):
-            qp, kp, vp = inputs.qkv_device(wp.seed, wp.B, wp.H, wp.N, wp.M, wp.D, "bf16", dev)
-            scale_p = 1.0 / math.sqrt(wp.D)
         ow, lw = torch.empty_like(qp), torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
         # visible (query, key) pairs per head of a causal band of W keys
         pairs_w = {W: W * wp.N - W * (W - 1) // 2 for W in WINDOWS}
         bytes_w = (4.0 * wp.N * wp.D * 2 + wp.N * 4) * wp.B * wp.H   # Q, K, V read, O and LSE written
+    if do_m:
+        om, lm = torch.empty_like(qp), torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
+        masks = {"documents8": inputs.document_mask(7, wp.N, wp.M, 8),
+                 "random50": inputs.random_mask(11, 1, 1, wp.N, wp.M, 0.5)}
+        causal_pairs = np.tril(np.ones((wp.N, wp.M), dtype=bool), wp.M - wp.N)
+        # visible (query, key) pairs per head: the mask and the causal rule
+        pairs_m = {k: int(np.count_nonzero(m[0, 0] & causal_pairs)) for k, m in masks.items()}
+        words_m = {k: fa.pack_mask(torch.from_numpy(m).to(dev)) for k, m in masks.items()}
+        del masks, causal_pairs
+        wsm = torch.empty(fa.workspace_bytes(wp.B, wp.H, wp.N, wp.M, wp.D, causal=True,
+                                             mask_shape=(1, 1)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def main_step(evs=None):
@@ -245,6 +251,10 @@ def main():
     ms_8 = timed(lambda: fa.fwd(q8s[0], q8s[1], q8s[2], scale=scale_p, causal=True, out=o8, lse=l8,
                                 descale=tuple(d8), stream=stream),
                  args.steps, args.warmup) if do_8 else []
+    ms_m = {name: timed(lambda name=name: fa.fwd(qp, kp, vp, scale=scale_p, causal=True, out=om,
+                                                 lse=lm, mask=words_m[name], workspace=wsm,
+                                                 stream=stream),
+                        args.steps, args.warmup) for name in words_m} if do_m else {}
     ms_k = {name: timed(lambda tpg=tpg: fa.fwd(qp, kp, vp, scale=scale_p, causal=True, out=ok_,
                                                lse=lk_, workspace=wsk, path=fa.PATH_KVOUTER,
                                                kvouter_query_tiles=tpg, stream=stream),
@@ -321,6 +331,26 @@ def main():
                          "keys_per_query": list(WINDOWS)}
         if not (do_p or do_d or do_b):
             out.update({"value": res[f"w{WINDOWS[0]}"]["gbs"], "unit": "GB/s"})
+    if do_m:
+        res = {}
+        for name in ms_m:
+            avg = sum(ms_m[name]) / len(ms_m[name])
+            flop = 4.0 * wp.D * pairs_m[name] * wp.B * wp.H
+            tf = flop / (avg * 1e-3) / 1e12
+            res[name] = {"ms_mean": avg, "ms_min": min(ms_m[name]), "tflops": tf,
+                         "visible_pairs_per_head": pairs_m[name],
+                         "visible_fraction_of_causal": pairs_m[name] / (wp.N * (wp.N + 1) / 2),
+                         "speedup_vs_unmasked_causal": ((sum(ms_p) / len(ms_p)) / avg) if do_p else None,
+                         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,causal,mask>",
+                                      "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": tf / PEAK_BF16_TFLOPS, "traffic": None}}
+        out["mask"] = dict(res, flop_convention="4 D x visible (query, key) pairs per head "
+                                                "(exact count), B H heads")
+        cfg["mask"] = {"B": wp.B, "H": wp.H, "N": wp.N, "M": wp.M, "D": wp.D, "causal": True,
+                       "masks": {"documents8": "8 packed documents (seed 7), shared by all heads",
+                                 "random50": "each pair kept with p = 1/2 (seed 11), shared"}}
+        if not (do_p or do_d or do_b or do_w):
+            out.update({"value": res["documents8"]["tflops"], "unit": "TFLOP/s"})
     if do_8:
         avg8 = sum(ms_8) / len(ms_8)
         tf8 = flop_8 / (avg8 * 1e-3) / 1e12

@@ -14,13 +14,16 @@ q [B,H,N,D], k/v [B,H,M,D] contiguous CUDA tensors (bf16 or float32, D in
 {64, 128}); kv_len an int32 tensor [B] on the same device (or None).  Returns
 O [B,H,N,D] (input dtype) and LSE [B,H,N] (float32, natural log).  ``bwd``
 takes the forward's inputs and outputs and the upstream gradient dO (bf16)
-and returns dQ, dK, dV (bf16).
+and returns dQ, dK, dV (bf16).  ``fwd`` also takes a local window and an
+element mask (``pack_mask`` turns a boolean [Bm, Hm, N, M] into the packed
+words the library reads).
 """
 import ctypes
 import math
 import os
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "plan", "workspace_bytes", "lib", "library_path", "FaError",
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "plan", "workspace_bytes", "pack_mask", "lib",
+           "library_path", "FaError",
            "PATH_AUTO", "PATH_PREFILL", "PATH_SPLITKV", "PATH_F32", "PATH_KVOUTER", "PATH_FP8",
            "FP8",
            "F32", "BF16", "EXPORTS"]
@@ -56,7 +59,8 @@ class Options(ctypes.Structure):
                 ("window", ctypes.c_int32), ("window_left", ctypes.c_int32),
                 ("window_right", ctypes.c_int32), ("kvouter_query_tiles", ctypes.c_int32),
                 ("q_descale", ctypes.c_float), ("k_descale", ctypes.c_float),
-                ("v_descale", ctypes.c_float)]
+                ("v_descale", ctypes.c_float), ("mask", ctypes.c_void_p),
+                ("mask_batches", ctypes.c_int32), ("mask_heads", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -111,19 +115,21 @@ def _check(st):
         raise FaError(st, L.fa_status_str(st).decode(), L.fa_last_error().decode())
 
 
-def _options(path, split_keys, window=None, kvouter_query_tiles=0, descale=None):
+def _options(path, split_keys, window=None, kvouter_query_tiles=0, descale=None, mask=None):
     """fa_options for the call, or None for the defaults.  ``window`` is None
     or (left, right): key j visible to query i only if
     i + off - left <= j <= i + off + right (off = kv_len - N).  ``descale``
-    is None or (dq, dk, dv) for fp8 inputs."""
+    is None or (dq, dk, dv) for fp8 inputs.  ``mask`` is None or
+    (device pointer, mask batches, mask heads) of packed mask words."""
     if (path in (None, PATH_AUTO) and not split_keys and window is None
-            and not kvouter_query_tiles and descale is None):
+            and not kvouter_query_tiles and descale is None and mask is None):
         return None
     wl, wr = (int(window[0]), int(window[1])) if window is not None else (0, 0)
     dq, dk, dv = (float(x) for x in descale) if descale is not None else (0.0, 0.0, 0.0)
+    mp, mb, mh = mask if mask is not None else (None, 0, 0)
     return Options(PATH_AUTO if path is None else int(path), int(split_keys or 0),
                    1 if window is not None else 0, wl, wr, int(kvouter_query_tiles or 0),
-                   dq, dk, dv)
+                   dq, dk, dv, mp, int(mb), int(mh))
 
 
 def _opt_ptr(o):
@@ -131,10 +137,13 @@ def _opt_ptr(o):
 
 
 def plan(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0, window=None,
-         kvouter_query_tiles=0):
-    """The planner's decision for a shape, as a dict (host only)."""
+         kvouter_query_tiles=0, mask_shape=None):
+    """The planner's decision for a shape, as a dict (host only).
+    ``mask_shape=(Bm, Hm)`` plans for an element mask of that many batches
+    and heads (no pointer is needed to plan)."""
     info = PlanInfo()
-    o = _options(path, split_keys, window, kvouter_query_tiles)
+    o = _options(path, split_keys, window, kvouter_query_tiles,
+                 mask=None if mask_shape is None else (1, mask_shape[0], mask_shape[1]))
     _check(lib().fa_plan_query(Shape(B, H, N, M, D), int(dtype), int(bool(causal)),
                                _opt_ptr(o), ctypes.byref(info)))
     d = {f: getattr(info, f) for f, _ in PlanInfo._fields_}
@@ -143,8 +152,10 @@ def plan(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0, windo
 
 
 def workspace_bytes(B, H, N, M, D, dtype=BF16, causal=False, path=None, split_keys=0,
-                    window=None, kvouter_query_tiles=0):
-    o = _options(path, split_keys, window, kvouter_query_tiles)
+                    window=None, kvouter_query_tiles=0, mask_shape=None):
+    """Device workspace fwd needs; ``mask_shape=(Bm, Hm)`` for an element mask."""
+    o = _options(path, split_keys, window, kvouter_query_tiles,
+                 mask=None if mask_shape is None else (1, mask_shape[0], mask_shape[1]))
     return int(lib().fa_fwd_workspace_bytes(Shape(B, H, N, M, D), int(dtype),
                                             int(bool(causal)), _opt_ptr(o)))
 
@@ -161,16 +172,37 @@ def _dtype_code(t):
                     "torch.float8_e4m3fn")
 
 
+def pack_mask(allowed):
+    """Pack a boolean mask [Bm, Hm, N, M] (True = key visible) into the
+    library's words: int32 [Bm, Hm, N, ceil(M / 32)], bit j % 32 of word
+    j / 32 for key j.  Runs where ``allowed`` lives (torch ops only)."""
+    import torch
+    if allowed.dim() != 4:
+        raise ValueError("mask must be [Bm, Hm, N, M]")
+    Bm, Hm, N, M = allowed.shape
+    W = (M + 31) // 32
+    bits = torch.zeros((Bm, Hm, N, W * 32), dtype=torch.int64, device=allowed.device)
+    bits[..., :M] = allowed.to(torch.int64)
+    weights = torch.bitwise_left_shift(
+        torch.ones(32, dtype=torch.int64, device=allowed.device),
+        torch.arange(32, dtype=torch.int64, device=allowed.device))
+    words = (bits.view(Bm, Hm, N, W, 32) * weights).sum(dim=-1)      # < 2^32
+    words = torch.where(words >= 2 ** 31, words - 2 ** 32, words)     # as int32 bits
+    return words.to(torch.int32).contiguous()
+
+
 def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
         workspace=None, path=None, split_keys=0, window=None, kvouter_query_tiles=0,
-        descale=None, stream=None):
+        descale=None, mask=None, stream=None):
     """Exact attention forward through the C ABI; returns (O, LSE).
 
     ``window=(left, right)`` restricts query i to keys
     i + off - left .. i + off + right (off = kv_len - N; causal caps right
     at 0): ``causal=True, window=(127, 0)`` is a 128-wide local window.
     float8_e4m3fn inputs (FP8) give a bf16 O; ``descale=(dq, dk, dv)`` says
-    that they stand for dq*Q, dk*K, dv*V."""
+    that they stand for dq*Q, dk*K, dv*V.  ``mask`` is an element mask as
+    packed words, int32 [Bm, Hm, N, ceil(M / 32)] on the device
+    (``pack_mask``), Bm in {1, B}, Hm in {1, H}."""
     import torch
     L = lib()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -200,7 +232,17 @@ def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
         out = torch.empty((B, H, N, D), dtype=torch.bfloat16 if dt == FP8 else q.dtype, device=dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    opts = _options(path, split_keys, window, kvouter_query_tiles, descale)
+    mask_arg = None
+    if mask is not None:
+        if mask.dim() != 4 or mask.dtype != torch.int32 or not mask.is_contiguous():
+            raise ValueError("mask must be contiguous int32 [Bm, Hm, N, ceil(M / 32)]")
+        if not mask.is_cuda or mask.device != dev:
+            raise ValueError("mask must be on the device of q")
+        Bm, Hm, Nm, Wm = mask.shape
+        if Nm != N or Wm != (M + 31) // 32 or Bm not in (1, B) or Hm not in (1, H):
+            raise ValueError("mask must be [1 or B, 1 or H, N, ceil(M / 32)]")
+        mask_arg = (mask.data_ptr(), Bm, Hm)
+    opts = _options(path, split_keys, window, kvouter_query_tiles, descale, mask_arg)
     shape = Shape(B, H, N, M, D)
     ws_need = int(L.fa_fwd_workspace_bytes(shape, dt, int(bool(causal)), _opt_ptr(opts)))
     if ws_need and workspace is None:

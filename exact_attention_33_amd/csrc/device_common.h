@@ -97,6 +97,16 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, 
 #endif
 }
 
+// 4 bytes per lane from base + voff into LDS at dst + 4 * lane, as above.
+__device__ __forceinline__ void buffer_load_lds4(const void* base, int nbytes, uint32_t voff,
+                                                 lds_ptr dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags), dst,
+      4, voff, 0, 0, 0);
+#endif
+}
+
 // Logical work item of workgroup `wg` when workgroups are dealt round-robin
 // to kNumXcd XCDs: XCD x gets a contiguous range of logical items.
 __device__ __forceinline__ int64_t xcd_logical(int64_t wg, int64_t G) {

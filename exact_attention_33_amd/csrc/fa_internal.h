@@ -29,6 +29,10 @@ struct Problem {
   int32_t wl, wr;
   // FA_FP8: the inputs stand for q_descale * Q8, k_descale * K8, v_descale * V8.
   float q_descale, k_descale, v_descale;
+  // Element mask (options.mask): words [mask_b][mask_h][N][mask_w], bit j % 32
+  // of word j / 32 set = key j visible; nullptr: none.
+  const uint32_t* mask;
+  int32_t mask_b, mask_h, mask_w;
 };
 
 // Planner output (host-only; see plan.cpp).
@@ -42,6 +46,7 @@ struct Plan {
   int64_t grid;
   size_t ws_bytes;
   size_t ws_lse_offset;  // split-KV: byte offset of the partial LSE array
+  int32_t mask_tiles;    // prefill with a mask: int32 entries per tile list
 };
 
 // Returns FA_OK and fills `plan`, or an error status with `why` set.
@@ -49,7 +54,8 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
                     const fa_options* opt, Plan* plan, const char** why);
 
 // Kernel launchers: enqueue on `stream`, return the launch status.
-hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, hipStream_t stream);
+hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, void* workspace,
+                               hipStream_t stream);
 hipError_t launch_fwd_f32(const Problem& p, const Plan& plan, hipStream_t stream);
 hipError_t launch_splitkv_bf16(const Problem& p, const Plan& plan, void* workspace,
                                hipStream_t stream);
@@ -61,6 +67,16 @@ hipError_t launch_prefill_fp8(const Problem& p, const Plan& plan, hipStream_t st
 constexpr int kPrefillBlockQ = 256;   // 4 waves x 64 queries
 constexpr int kPrefillBlockK = 64;    // keys per K/V tile
 constexpr int kPrefillThreads = 256;
+
+// Element mask on the prefill path: the workspace holds, per (mask batch,
+// mask head, 256-query tile), a list of kMaskListStride(M) int32: the count,
+// then the key tiles (64 keys) in which some query of the tile sees a masked-in
+// key, ascending, bit 31 set on tiles the mask does not keep whole.  The
+// kernel copies a list into LDS, so a list holds at most kMaskMaxTiles - 1
+// tiles.
+constexpr int kMaskMaxTiles = 4096;
+inline int32_t mask_list_stride(int M) { return (M + kPrefillBlockK - 1) / kPrefillBlockK + 1; }
+inline int32_t mask_words(int M) { return (M + 31) / 32; }
 
 constexpr int kF32BlockQ = 16;        // 16 query rows x 16 lanes
 constexpr int kF32BlockK = 32;

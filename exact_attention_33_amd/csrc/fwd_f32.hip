@@ -7,6 +7,9 @@
 // Factor) and adds the tile's weights; the output is divided by l once at the
 // end and L = m + log(l) is written beside it.
 //
+// An element mask (bit j % 32 of word j / 32 of the query's mask row) hides
+// keys on top of kv_len, causal and the window; its bits are read per score.
+//
 // This path exists for exactness, not speed: scores, exponentials and sums are
 // float64 so that O and LSE round to float32 only once (an fp32 score at
 // |S| ~ 90 already carries an ulp of 7.6e-6).
@@ -41,6 +44,13 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(Problem p, int n_q
   const int i_last = min(qt * BQ + BQ, N) - 1;
   const int kv_end = upper ? min(kvl, i_last + off + wr + 1) : kvl;
   const int kv_start = p.window ? max(0, qt * BQ + off - wl) / BK * BK : 0;
+
+  // this query's row of the element mask (none: nullptr)
+  const uint32_t* mrow = nullptr;
+  if (p.mask && i < N) {
+    const int64_t mb = p.mask_b > 1 ? b : 0, mh = p.mask_h > 1 ? bh % p.H : 0;
+    mrow = p.mask + ((size_t)(mb * p.mask_h + mh) * N + i) * p.mask_w;
+  }
 
   const float* Q = (const float*)p.q + (size_t)bh * N * D;
   const float* K = (const float*)p.k + (size_t)bh * M * D;
@@ -82,7 +92,8 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(Problem p, int n_q
       part += __shfl_xor(part, 1, 16);
       const int key = j0 + jj;
       const bool vis = key < kvl && (!upper || key <= i + off + wr) &&
-                       (!p.window || key >= i + off - wl);
+                       (!p.window || key >= i + off - wl) &&
+                       (!p.mask || (mrow && ((mrow[key >> 5] >> (key & 31)) & 1u)));
       s[jj] = vis ? part * sc : -INFINITY;
       mx = fmax(mx, s[jj]);
     }

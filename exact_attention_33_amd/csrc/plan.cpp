@@ -73,6 +73,13 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
     *why = "options.window_left and window_right must be >= 0";
     return FA_ERR_ARG;
   }
+  const bool mask = opt && opt->mask;
+  const int32_t mask_b = mask && opt->mask_batches ? opt->mask_batches : 1;
+  const int32_t mask_h = mask && opt->mask_heads ? opt->mask_heads : 1;
+  if (mask && ((mask_b != 1 && mask_b != s.B) || (mask_h != 1 && mask_h != s.H))) {
+    *why = "options.mask_batches must be 1 or B and options.mask_heads 1 or H";
+    return FA_ERR_ARG;
+  }
   // Element counts must fit comfortably in 64-bit byte offsets.
   const int64_t bh = (int64_t)s.B * s.H;
   if (bh > INT32_MAX || (bh > 0 && ((int64_t)s.N * s.D > INT64_MAX / 8 / bh ||
@@ -92,8 +99,8 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
       *why = "FA_FP8 inputs run only on FA_PATH_FP8";
       return FA_ERR_UNSUPPORTED;
     }
-    if (window) {
-      *why = "FA_PATH_FP8 takes no window";
+    if (window || mask) {
+      *why = "FA_PATH_FP8 takes no window and no element mask";
       return FA_ERR_UNSUPPORTED;
     }
     path = FA_PATH_FP8;
@@ -115,18 +122,21 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
       *why = "FA_PATH_SPLITKV needs N == 1 (one query per sequence)";
       return FA_ERR_UNSUPPORTED;
     }
-    if (req == FA_PATH_KVOUTER && window) {
-      *why = "FA_PATH_KVOUTER takes no window";
+    if (req == FA_PATH_KVOUTER && (window || mask)) {
+      *why = "FA_PATH_KVOUTER takes no window and no element mask";
       return FA_ERR_UNSUPPORTED;
     }
-    if (req == FA_PATH_SPLITKV && window) {
-      *why = "FA_PATH_SPLITKV has no window; a windowed query runs on FA_PATH_PREFILL";
+    if (req == FA_PATH_SPLITKV && (window || mask)) {
+      *why = "FA_PATH_SPLITKV has no window and no element mask; such a query runs on "
+             "FA_PATH_PREFILL";
       return FA_ERR_UNSUPPORTED;
     }
     // A window bounds a query's keys, so one query is cheap on the prefill
-    // kernel; the split-KV path streams whole caches.
-    path = req == FA_PATH_AUTO ? (s.N == 1 && !window ? FA_PATH_SPLITKV : FA_PATH_PREFILL)
-                               : (fa_path)req;
+    // kernel, and the prefill kernel is the one that reads element masks; the
+    // split-KV path streams whole caches.
+    path = req == FA_PATH_AUTO
+               ? (s.N == 1 && !window && !mask ? FA_PATH_SPLITKV : FA_PATH_PREFILL)
+               : (fa_path)req;
   }
 
   plan->path = path;
@@ -143,6 +153,22 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
       plan->threads = kPrefillThreads;
       plan->lds_bytes = prefill_lds_bytes(s.D);
       plan->grid = ceil_div(s.N, kPrefillBlockQ) * bh;
+      if (mask) {
+        // the kernel holds one query tile's list of key tiles in LDS, and
+        // addresses one (mask batch, mask head) of the mask with 32-bit byte
+        // offsets
+        plan->mask_tiles = mask_list_stride(s.M);
+        if (plan->mask_tiles > kMaskMaxTiles) {
+          *why = "an element mask on FA_PATH_PREFILL needs M <= 262080";
+          return FA_ERR_UNSUPPORTED;
+        }
+        if ((int64_t)s.N * mask_words(s.M) * 4 > INT32_MAX) {
+          *why = "an element mask on FA_PATH_PREFILL needs N * ceil(M / 32) * 4 < 2^31";
+          return FA_ERR_UNSUPPORTED;
+        }
+        plan->ws_bytes = align_up((size_t)mask_b * (size_t)mask_h * (size_t)ceil_div(s.N, kPrefillBlockQ) *
+                                      (size_t)plan->mask_tiles * sizeof(int32_t), 256);
+      }
       break;
     case FA_PATH_F32:
       plan->block_q = kF32BlockQ;

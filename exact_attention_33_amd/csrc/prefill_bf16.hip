@@ -75,7 +75,16 @@
 //  * workgroup order: gfx950 deals workgroups round-robin to its 8 XCDs, each
 //    with its own L2.  Consecutive logical work items (the query tiles of one
 //    (batch, head), heaviest first when causal) are mapped to one XCD so that
-//    the workgroups sharing a head's K/V run together on one L2.
+//    the workgroups sharing a head's K/V run together on one L2;
+//  * element masks ("Understanding FlashAttention", Attention: mask() is any
+//    elementwise constant, causal being one kind): a pre-pass reduces the
+//    mask over each 256-query x 64-key tile and lists, per query tile, the
+//    key tiles in which some query keeps a key, flagging those it does not
+//    keep whole.  The workgroup copies its list to LDS and visits only the
+//    listed tiles (the general form of the causal tile skip).  Each wave's
+//    mask words for a tile (64 rows x 2 words) travel HBM -> LDS with the
+//    tile loads, three tiles ahead, and the bits are applied only on flagged
+//    tiles.
 #include <cmath>
 #include <type_traits>
 #include <utility>
@@ -119,9 +128,60 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 __device__ __forceinline__ void mfma_guard() { asm volatile("s_nop 7\n\ts_nop 7"); }
 
 
-template <int D, bool CAUSAL, bool WINDOW>
+// Tile lists of an element mask: one workgroup per (mask batch, mask head,
+// 256-query tile); thread t classifies key tiles t, t + 256, ... by OR and
+// AND over the tile's real query rows (bits of keys >= M do not count), and
+// the wave ballots compact the non-empty tiles in ascending order.
+__global__ __launch_bounds__(256) void mask_tiles_kernel(const uint32_t* __restrict__ mask, int N,
+                                                         int M, int W, int n_qtiles, int stride,
+                                                         int32_t* __restrict__ lists) {
+  const int g = blockIdx.x, qt = g % n_qtiles;
+  const int64_t mbh = g / n_qtiles;
+  const uint32_t* rows = mask + (size_t)mbh * N * W;
+  const int r0 = qt * kPrefillBlockQ, r1 = min(r0 + kPrefillBlockQ, N);
+  const int n_kt = stride - 1;
+  int32_t* L = lists + (size_t)g * stride;
+  __shared__ int wave_n[4];
+  const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
+  int base = 0;
+  for (int c = 0; c < n_kt; c += 256) {
+    const int kt = c + tid;
+    bool any = false, all = true;
+    if (kt < n_kt) {
+      const int k0 = kt * kPrefillBlockK;
+      const int n0 = min(max(M - k0, 0), 32), n1 = min(max(M - k0 - 32, 0), 32);
+      const uint32_t v0 = n0 == 32 ? ~0u : (1u << n0) - 1u;  // keys < M of each word
+      const uint32_t v1 = n1 == 32 ? ~0u : (1u << n1) - 1u;
+      const bool has1 = 2 * kt + 1 < W;
+      uint32_t o0 = 0u, o1 = 0u, a0 = ~0u, a1 = ~0u;
+#pragma unroll 8
+      for (int r = r0; r < r1; ++r) {
+        const uint32_t* row = rows + (size_t)r * W + 2 * kt;
+        const uint32_t w0 = row[0], w1 = has1 ? row[1] : 0u;
+        o0 |= w0;
+        o1 |= w1;
+        a0 &= w0;
+        a1 &= w1;
+      }
+      any = ((o0 & v0) | (o1 & v1)) != 0u;
+      all = ((a0 | ~v0) & (a1 | ~v1)) == ~0u;
+    }
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(any);
+    if (lane == 0) wave_n[wv] = __builtin_popcountll(bal);
+    __syncthreads();
+    int pos = base + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+    for (int w = 0; w < wv; ++w) pos += wave_n[w];
+    if (any) L[1 + pos] = all ? kt : (int32_t)((uint32_t)kt | 0x80000000u);
+    base += wave_n[0] + wave_n[1] + wave_n[2] + wave_n[3];
+    __syncthreads();
+  }
+  if (tid == 0) L[0] = base;
+}
+
+template <int D, bool CAUSAL, bool WINDOW, bool BITS>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefill_bf16_kernel(Problem p, int n_qtiles) {
+void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ tile_lists,
+                         int list_stride) {
   constexpr int BQ = kPrefillBlockQ, BK = kPrefillBlockK;
   constexpr int NW = kPrefillThreads / 64;   // waves per workgroup
   constexpr int QW = BQ / NW;                // queries per wave
@@ -148,6 +208,12 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   __shared__ __attribute__((aligned(1024))) __bf16 Vb0[NW * VPW * 512];
   __shared__ __attribute__((aligned(1024))) __bf16 Vb1[NW * VPW * 512];
   __shared__ __attribute__((aligned(1024))) __bf16 Vb2[NW * VPW * 512];
+  // Element mask: the workgroup's list of key tiles, and a ring of three
+  // tiles' mask words, per wave [word][64 rows].
+  __shared__ int tlist[BITS ? kMaskMaxTiles : 1];
+  __shared__ __attribute__((aligned(256))) uint32_t Mb0[BITS ? NW * 128 : 1];
+  __shared__ __attribute__((aligned(256))) uint32_t Mb1[BITS ? NW * 128 : 1];
+  __shared__ __attribute__((aligned(256))) uint32_t Mb2[BITS ? NW * 128 : 1];
 
   const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
   int qt = (int)(logical % n_qtiles);
@@ -171,10 +237,43 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
   const int q_last = min(q0 + BQ, N) - 1;
   const int kv_end = UPPER ? min(kvl, q_last + off + wr + 1) : kvl;
-  // Window: tiles before the first query's first key are never visited; the
-  // K/V descriptors start at tile t0, so the loop counts tiles from there.
-  const int t0 = WINDOW ? max(0, q0 + off - wl) / BK : 0;
-  const int n_tiles = kv_end > t0 * BK ? (kv_end + BK - 1) / BK - t0 : 0;
+  // Window: tiles before the first query's first key are never visited.
+  // Without a mask the K/V descriptors start at that tile, t0, and the loop
+  // counts tiles from there; with a mask the loop walks the listed tiles in
+  // [tw, t_end) and tiles are addressed from 0.
+  const int tw = WINDOW ? max(0, q0 + off - wl) / BK : 0;
+  const int t_end = kv_end > tw * BK ? (kv_end + BK - 1) / BK : tw;
+  const int t0 = BITS ? 0 : tw;
+  int n_tiles = t_end - tw;
+  int lo = 0;  // with a mask: list position of the first tile visited
+  if constexpr (BITS) {
+    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+    const int32_t* L = tile_lists + ((int64_t)(bm * p.mask_h + hm) * n_qtiles + qt) * list_stride;
+    const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
+    for (int i = tid; i < cnt; i += kPrefillThreads) tlist[i] = L[1 + i];
+    __syncthreads();
+    // the list ascends: count the entries below tw and below t_end
+    int below_lo = 0, below_hi = 0;
+    for (int i0 = 0; i0 < cnt; i0 += 64) {
+      const int e = i0 + lane < cnt ? (tlist[i0 + lane] & 0x7FFFFFFF) : 0x7FFFFFFF;
+      below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < tw));
+      below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t_end));
+    }
+    lo = __builtin_amdgcn_readfirstlane(below_lo);
+    n_tiles = __builtin_amdgcn_readfirstlane(below_hi) - lo;
+    __syncthreads();  // every wave has read the list
+    // after the last visited tile: one past kv_len, whose loads read zeros
+    // and whose keys are all masked (lo + n_tiles <= cnt < kMaskMaxTiles)
+    if (tid == 0) tlist[lo + n_tiles] = (kvl + BK - 1) / BK;
+    __syncthreads();
+  }
+  // Entry of the t-th visited tile: its index (relative to t0), with bit 31
+  // set when the mask does not keep it whole.  Without a mask, t itself.
+  auto tile_entry = [&](int t) -> int {
+    if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + min(t, n_tiles)]);
+    else return t;
+  };
+  auto tile_index = [&](int e) -> int { return BITS ? (e & 0x7FFFFFFF) : e; };
 
   const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
   const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D + (size_t)t0 * BK * D;
@@ -193,7 +292,8 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // global loads also keep the compiler's LDS wait counting exact: it treats
   // a global load into LDS like a flat access and then waits for every LDS
   // read.)
-  constexpr int NITEM = KPW + VPW;  // load items per wave per iteration
+  constexpr int NMI = BITS ? 2 : 0;  // mask load items (one per word of a row's tile)
+  constexpr int NITEM = KPW + VPW + NMI;  // load items per wave per iteration
   constexpr int ROWB = D * 2;       // bytes per global row
   static_assert((NW * KPW * 64 / KCH + 1) * ROWB <= 65536 && (NW * VPW * 64 / VCH + 1) * ROWB <= 65536,
                 "slot offsets fit 16 bits");
@@ -224,6 +324,24 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   };
   auto load_k_item = [&](int i, int t, __bf16* dst) { load_block(Kg, t, dst, koff[i / 2], i); };
   auto load_v_item = [&](int i, int t, __bf16* dst) { load_block(Vg, t, dst, voff[i / 2], i); };
+  // Mask word w of key tile t for the wave's 64 query rows (lane = row; rows
+  // past N read row N - 1): one 4-byte buffer load per lane into LDS.
+  const uint32_t* Mg = nullptr;
+  int mbytes = 0;
+  uint32_t mrow = 0;
+  if constexpr (BITS) {
+    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+    Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
+    mbytes = N * p.mask_w * 4;
+    mrow = (uint32_t)min(qw0 + lane, N - 1) * (uint32_t)p.mask_w;
+  }
+  auto load_mask_item = [&](int w, int t, uint32_t* dst) {
+    if constexpr (BITS) {
+      int wofs = ws * 128 + w * 64;
+      asm volatile("" : "+s"(wofs));
+      buffer_load_lds4(Mg, mbytes, (mrow + 2u * (uint32_t)t + (uint32_t)w) * 4u, (lds_ptr)(dst + wofs));
+    }
+  };
   auto load_k = [&](int t, __bf16* dst) {
 #pragma unroll
     for (int i = 0; i < KPW; ++i) load_k_item(i, t, dst);
@@ -232,11 +350,17 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
 #pragma unroll
     for (int i = 0; i < VPW; ++i) load_v_item(i, t, dst);
   };
+  auto load_mask = [&](int t, uint32_t* dst) {
+#pragma unroll
+    for (int w = 0; w < NMI; ++w) load_mask_item(w, t, dst);
+  };
   // Load item j of iteration t: K(t+4) blocks into Kdst, then V(t+2) blocks
-  // into Vdst (tiles past the last read as zeros).
-  auto load_item = [&](int j, int t, __bf16* Kdst, __bf16* Vdst) {
-    if (j < KPW) load_k_item(j, t + 4, Kdst);
-    else if (j < NITEM) load_v_item(j - KPW, t + 2, Vdst);
+  // into Vdst, then (mask) the mask words of tile t+3 into Mdst; eK, eV, eM
+  // are those tiles' entries (tiles past the last read as zeros).
+  auto load_item = [&](int j, int eK, int eV, int eM, __bf16* Kdst, __bf16* Vdst, uint32_t* Mdst) {
+    if (j < KPW) load_k_item(j, tile_index(eK), Kdst);
+    else if (j < KPW + VPW) load_v_item(j - KPW, tile_index(eV), Vdst);
+    else if (j < NITEM) load_mask_item(j - KPW - VPW, tile_index(eM), Mdst);
   };
 
   // ---- Q in registers: B operand of S^T = K Q^T ----
@@ -294,9 +418,9 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // Tiles that cross the diagonal or the kv_len boundary -- and tiles past
   // the workgroup's last one, whose LDS holds stale data -- are masked
   // element by element; every other tile is fully visible to the wave.
-  auto need_mask = [&](int t) {
-    const int k0 = (t + t0) * BK;
-    return (k0 + BK > kvl) || (UPPER && k0 + BK - 1 > qw0 + off + wr) ||
+  auto need_mask = [&](int e) {
+    const int k0 = (tile_index(e) + t0) * BK;
+    return (BITS && e < 0) || (k0 + BK > kvl) || (UPPER && k0 + BK - 1 > qw0 + off + wr) ||
            (WINDOW && k0 < qw0 + QW - 1 + off - wl);
   };
 
@@ -437,16 +561,26 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // Scores of keys past a row's last visible key become -inf.  The select is
   // a sign mask and a bit insert, not a compare: a compare per score writes a
   // scalar register pair, and the compiler would keep dozens of them live.
-  auto apply_mask = [&](int t, f32x16 (&s)[NKB][NQB]) {
-    const int k0 = (t + t0) * BK;
+  // With a mask, Ms holds the tile's mask words and key 8 (r / 4) + 4 hl + r % 4
+  // of key block nb is bit 8 (r / 4) + r % 4 of this lane's word shifted down
+  // by 4 hl.
+  auto apply_mask = [&](int e, f32x16 (&s)[NKB][NQB], const uint32_t* Ms) {
+    const int k0 = (tile_index(e) + t0) * BK;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qrow = qw0 + 32 * qb + ql;
       const int lim = UPPER ? min(kvl - 1, qrow + off + wr) : kvl - 1;  // last visible key
       const int lo = qrow + off - wl;                                   // first (window)
+      uint32_t hid[NKB];  // masked-out keys of the row's two key blocks (bit set)
 #pragma unroll
-      for (int nb = 0; nb < NKB; ++nb)
+      for (int nb = 0; nb < NKB; ++nb) {
         vis[nb][qb] = lim >= k0 + 32 * nb && (!WINDOW || lo <= k0 + 32 * nb + 31);
+        if constexpr (BITS) {
+          const uint32_t w = Ms[ws * 128 + nb * 64 + 32 * qb + ql];
+          vis[nb][qb] = vis[nb][qb] && w != 0u;  // a hint: a false "sees" only costs time
+          hid[nb] = ~w >> (4 * hl);
+        }
+      }
       const int base = lim - (k0 + 4 * hl);  // >= 0 iff key k0 + 4 hl is visible
       const int base_lo = k0 + 4 * hl - lo;  // >= 0 iff key k0 + 4 hl is past the window start
 #pragma unroll
@@ -456,17 +590,18 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
           const int idx = nb * 32 + 8 * (r / 4) + (r % 4);
           uint32_t hide = (uint32_t)((base - idx) >> 31);
           if constexpr (WINDOW) hide |= (uint32_t)((base_lo + idx) >> 31);
+          if constexpr (BITS) hide |= (uint32_t)__builtin_amdgcn_sbfe((int)hid[nb], 8 * (r / 4) + r % 4, 1);
           const uint32_t v = __float_as_uint(s[nb][qb][r]);
           s[nb][qb][r] = __uint_as_float((hide & 0xFF800000u) | (~hide & v));
         }
     }
   };
-  // Whole softmax of tile t (prologue only).
-  auto softmax_all = [&](int t, f32x16 (&s)[NKB][NQB]) {
+  // Whole softmax of the tile with entry e (prologue only).
+  auto softmax_all = [&](int e, f32x16 (&s)[NKB][NQB], const uint32_t* Ms) {
     mfma_guard();  // compute_s just wrote the scores
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-    if (need_mask(t)) apply_mask(t, s);
+    if (need_mask(e)) apply_mask(e, s, Ms);
     sm_begin();
     static_for<NU_EM>([&](auto uc) { unit_em(s, uc); });
     sm_check1(s);
@@ -501,8 +636,8 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // 3k + 1 (measured: spreading them over all steps gains nothing).
   constexpr int PF = 2;
   constexpr int NSA = 2 * NF, NSB = NQB * DK;  // steps of phases A and B (C = B)
-  constexpr int LSTEP = 3;  // tile load item k at step LSTEP k + 1 of phase A
-  auto iteration = [&](int t, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst) {
+  auto iteration = [&](int eK, int eV, int eM, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst,
+                       __bf16* Vdst, uint32_t* Mdst) {
     sm_begin();
     // K operands: a ring of PF + 2, so that a read overwrites a register two
     // fragments after the asm MFMAs last used it
@@ -561,7 +696,7 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
       if constexpr (j >= NSB) {
         static_for<NITEM>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          if constexpr (NSB + i * NSB / NITEM == j) load_item(i, t, Kdst, Vdst);
+          if constexpr (NSB + i * NSB / NITEM == j) load_item(i, eK, eV, eM, Kdst, Vdst, Mdst);
         });
       }
       if constexpr (j < NSB) {
@@ -579,12 +714,17 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   // exactly 0 (at most two iterations per workgroup and the diagonal tiles of
   // the later waves; one code path keeps the interleave and the register
   // assignment fixed).
-  auto step_tile = [&](int t, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst) {
+  // With a mask, Ms holds the words of tile t+1 and Mdst receives those of
+  // tile t+3.
+  auto step_tile = [&](int t, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst,
+                       const uint32_t* Ms, uint32_t* Mdst) {
+    const int e1 = tile_entry(t + 1), e2 = tile_entry(t + 2), e3 = tile_entry(t + 3),
+              e4 = tile_entry(t + 4);
     mfma_guard();  // the last iteration's final MFMAs wrote the scores
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-    if (need_mask(t + 1)) apply_mask(t + 1, sacc);
-    iteration(t, Ks, Vs, Kdst, Vdst);
+    if (need_mask(e1)) apply_mask(e1, sacc, Ms);
+    iteration(e4, e2, e3, Ks, Vs, Kdst, Vdst, Mdst);
     // This wave's loads of the previous iteration (K(t+3), V(t+1)) are done
     // (loads complete in order: only this iteration's NITEM may be pending),
     // and so are its LDS reads; the barrier then makes every wave's loads
@@ -595,29 +735,34 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
 
   // Prologue: K(0) .. K(2), V(0), V(1) in LDS; S(0) and its softmax, S(1);
   // K(3) loaded over K(0) once every wave has read K(0).
+  const int e0 = tile_entry(0);
   if (n_tiles > 0) {
-    load_k(0, Kb0);
-    load_k(1, Kb1);
-    load_k(2, Kb2);
-    load_v(0, Vb0);
-    load_v(1, Vb1);
+    const int e1 = tile_entry(1), e2 = tile_entry(2);
+    load_k(tile_index(e0), Kb0);
+    load_k(tile_index(e1), Kb1);
+    load_k(tile_index(e2), Kb2);
+    load_v(tile_index(e0), Vb0);
+    load_v(tile_index(e1), Vb1);
+    load_mask(tile_index(e0), Mb0);
+    load_mask(tile_index(e1), Mb1);
+    load_mask(tile_index(e2), Mb2);
   }
   __syncthreads();
   compute_s(Kb0, sacc);
   __syncthreads();  // every wave is done with K(0) before K(3) goes over it
-  if (n_tiles > 0) load_k(3, Kb0);
-  softmax_all(0, sacc);
+  if (n_tiles > 0) load_k(tile_index(tile_entry(3)), Kb0);
+  softmax_all(e0, sacc, Mb0);
   compute_s(Kb1, sacc);
   // K(1) is read by every wave before iteration 0 loads K(4) over it; K(3)
   // may still be in flight (iteration 0 waits for it)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   for (int t = 0; t < n_tiles; t += 3) {
-    step_tile(t, Kb2, Vb0, Kb1, Vb2);
+    step_tile(t, Kb2, Vb0, Kb1, Vb2, Mb1, Mb0);
     if (t + 1 >= n_tiles) break;
-    step_tile(t + 1, Kb0, Vb1, Kb2, Vb0);
+    step_tile(t + 1, Kb0, Vb1, Kb2, Vb0, Mb2, Mb1);
     if (t + 2 >= n_tiles) break;
-    step_tile(t + 2, Kb1, Vb2, Kb0, Vb1);
+    step_tile(t + 2, Kb1, Vb2, Kb0, Vb1, Mb0, Mb2);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
@@ -643,26 +788,47 @@ void prefill_bf16_kernel(Problem p, int n_qtiles) {
   }
 }
 
-template <int D>
-void launch_prefill_d(const Problem& p, dim3 grid, hipStream_t stream, int n_qtiles) {
+template <int D, bool BITS>
+void launch_prefill_dm(const Problem& p, dim3 grid, hipStream_t stream, int n_qtiles,
+                       const int32_t* lists, int stride) {
   const dim3 block(kPrefillThreads);
   if (p.window) {
-    if (p.causal) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), grid, block, 0, stream, p, n_qtiles);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), grid, block, 0, stream, p, n_qtiles);
+    if (p.causal)
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride);
   } else {
-    if (p.causal) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), grid, block, 0, stream, p, n_qtiles);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), grid, block, 0, stream, p, n_qtiles);
+    if (p.causal)
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride);
   }
+}
+
+template <int D>
+void launch_prefill_d(const Problem& p, dim3 grid, hipStream_t stream, int n_qtiles,
+                      const int32_t* lists, int stride) {
+  if (p.mask) launch_prefill_dm<D, true>(p, grid, stream, n_qtiles, lists, stride);
+  else launch_prefill_dm<D, false>(p, grid, stream, n_qtiles, lists, stride);
 }
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, hipStream_t stream) {
+hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, void* workspace,
+                               hipStream_t stream) {
   if (plan.grid == 0) return hipSuccess;
   const int n_qtiles = (p.N + kPrefillBlockQ - 1) / kPrefillBlockQ;
   const dim3 grid((unsigned)plan.grid);
-  if (p.D == 64) launch_prefill_d<64>(p, grid, stream, n_qtiles);
-  else launch_prefill_d<128>(p, grid, stream, n_qtiles);
+  int32_t* lists = nullptr;
+  if (p.mask) {
+    // the tile lists, one per (mask batch, mask head, query tile)
+    lists = (int32_t*)workspace;
+    const int64_t n_lists = (int64_t)p.mask_b * p.mask_h * n_qtiles;
+    hipLaunchKernelGGL(mask_tiles_kernel, dim3((unsigned)n_lists), dim3(256), 0, stream, p.mask,
+                       p.N, p.M, p.mask_w, n_qtiles, plan.mask_tiles, lists);
+  }
+  if (p.D == 64) launch_prefill_d<64>(p, grid, stream, n_qtiles, lists, plan.mask_tiles);
+  else launch_prefill_d<128>(p, grid, stream, n_qtiles, lists, plan.mask_tiles);
   return hipGetLastError();
 }
 

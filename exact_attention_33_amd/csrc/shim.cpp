@@ -111,14 +111,18 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v,
 
   const bool win = opt && opt->window;
   auto descale = [](float x) { return x == 0.f ? 1.f : x; };
+  const uint32_t* mask = opt ? opt->mask : nullptr;
+  if (mask && !aligned(mask, 4)) return fail(FA_ERR_ALIGN, "fa_fwd: options.mask must be 4-byte aligned");
   fa::Problem p{q, k, v, kv_len, o, lse, s.B, s.H, s.N, s.M, s.D, scale, causal ? 1 : 0,
                 win ? 1 : 0, win ? opt->window_left : 0, win ? opt->window_right : 0,
                 opt ? descale(opt->q_descale) : 1.f, opt ? descale(opt->k_descale) : 1.f,
-                opt ? descale(opt->v_descale) : 1.f};
+                opt ? descale(opt->v_descale) : 1.f, mask,
+                mask && opt->mask_batches ? opt->mask_batches : 1,
+                mask && opt->mask_heads ? opt->mask_heads : 1, fa::mask_words(s.M)};
   hipStream_t hs = (hipStream_t)stream;
   hipError_t err = hipSuccess;
   switch (plan.path) {
-    case FA_PATH_PREFILL: err = fa::launch_prefill_bf16(p, plan, hs); break;
+    case FA_PATH_PREFILL: err = fa::launch_prefill_bf16(p, plan, workspace, hs); break;
     case FA_PATH_F32: err = fa::launch_fwd_f32(p, plan, hs); break;
     case FA_PATH_SPLITKV: err = fa::launch_splitkv_bf16(p, plan, workspace, hs); break;
     case FA_PATH_KVOUTER: err = fa::launch_kvouter_bf16(p, plan, workspace, hs); break;
@@ -160,6 +164,8 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                     const fa_options* opt) {
   if (opt && opt->window != 0 && opt->window != 1)
     return fail(FA_ERR_ARG, "fa_bwd: options.window must be 0 or 1");
+  if (opt && opt->mask)
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: an element mask is not supported by the backward");
   const bool win = opt && opt->window;
   if (win && (opt->window_left < 0 || opt->window_right < 0))
     return fail(FA_ERR_ARG, "fa_bwd: options.window_left and window_right must be >= 0");

@@ -133,3 +133,42 @@ def poison_tail(k, v, kv_len):
         k[b, :, int(n):] = float("nan")
         v[b, :, int(n):] = float("nan")
     return k, v
+
+
+# ---- element masks (boolean [Bm, Hm, N, M], True = key visible) ----
+# Synthetic stand-ins for the kinds of masks attention serves besides causal
+# and a window: packed documents, a bidirectional prefix, random block
+# sparsity and unstructured masks.
+
+def document_mask(seed, N, M, n_docs):
+    """Packed sequences: the N queries and M keys are cut at the same
+    ``n_docs - 1`` random points (queries scaled to M), and a query sees only
+    the keys of its own document.  [1, 1, N, M]."""
+    rng = np.random.default_rng(seed)
+    cuts = np.sort(rng.choice(np.arange(1, M), size=n_docs - 1, replace=False))
+    key_doc = np.searchsorted(cuts, np.arange(M), side="right")
+    qpos = (np.arange(N) * M) // max(N, 1)
+    q_doc = np.searchsorted(cuts, qpos, side="right")
+    return (q_doc[:, None] == key_doc[None, :])[None, None]
+
+
+def prefix_mask(N, M, prefix):
+    """A bidirectional prefix of ``prefix`` keys that every query sees, and
+    bottom-right causal order after it.  [1, 1, N, M]."""
+    i = np.arange(N)[:, None]
+    j = np.arange(M)[None, :]
+    return ((j < prefix) | (j <= i + (M - N)))[None, None]
+
+
+def block_mask(seed, Bm, Hm, N, M, block_q, block_k, p_keep):
+    """Random blocks of ``block_q`` x ``block_k`` kept whole or dropped whole,
+    each with probability ``p_keep``.  [Bm, Hm, N, M]."""
+    rng = np.random.default_rng(seed)
+    nb_q, nb_k = -(-N // block_q), -(-M // block_k)
+    blocks = rng.random((Bm, Hm, nb_q, nb_k)) < p_keep
+    return np.repeat(np.repeat(blocks, block_q, axis=2), block_k, axis=3)[:, :, :N, :M]
+
+
+def random_mask(seed, Bm, Hm, N, M, p_keep):
+    """Each (query, key) pair kept independently with probability ``p_keep``."""
+    return np.random.default_rng(seed).random((Bm, Hm, N, M)) < p_keep

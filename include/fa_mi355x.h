@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 /* FA_FP8: OCP E4M3 (finite max 448, no infinities) Q, K, V with per-tensor
  * descale factors (fa_options); O is then bf16 and LSE float32. */
@@ -72,17 +72,19 @@ typedef enum {
   FA_PATH_AUTO = 0,     /* planner's choice                                      */
   FA_PATH_PREFILL = 1,  /* fused tiled kernel, bf16 MFMA (bf16 only; K/V bytes
                            per batch and head, M * D * 2, below 2^31); with a
-                           window it also serves N = 1                           */
+                           window or an element mask it also serves N = 1        */
   FA_PATH_SPLITKV = 2,  /* split-KV partial kernel + log-sum-exp merge (bf16, N=1,
-                           no window)                                             */
-  FA_PATH_F32 = 3,      /* float32 inputs/outputs, float64 internal arithmetic   */
+                           no window, no element mask)                            */
+  FA_PATH_F32 = 3,      /* float32 inputs/outputs, float64 internal arithmetic;
+                           takes a window and an element mask                    */
   FA_PATH_KVOUTER = 4,  /* ablation, never chosen by the planner: the same result
                            with key/value tiles in the outer loop and the output
                            accumulator, m and l read and written back in a
-                           float32 workspace for every key tile (bf16, no window) */
+                           float32 workspace for every key tile (bf16, no window,
+                           no element mask)                                       */
   FA_PATH_FP8 = 5       /* fused tiled kernel on the fp8 matrix cores: FA_FP8
-                           inputs only, any N, no window; the weights are rounded
-                           to E4M3 before the P V product                          */
+                           inputs only, any N, no window, no element mask; the
+                           weights are rounded to E4M3 before the P V product      */
 } fa_path;
 
 /* Optional controls; pass NULL for the planner's defaults.  A zero-filled
@@ -107,6 +109,21 @@ typedef struct {
   float q_descale;     /* FA_FP8: Q stands for q_descale * Q8 (0 means 1)       */
   float k_descale;     /* FA_FP8: K stands for k_descale * K8 (0 means 1)       */
   float v_descale;     /* FA_FP8: V stands for v_descale * V8 (0 means 1)       */
+  /* Element mask ("Understanding FlashAttention", Attention: mask() covers
+   * causal masking and other kinds, each an elementwise constant that does
+   * not depend on the scores).  NULL: none.  Otherwise a device array of
+   * uint32 words [mask_batches][mask_heads][N][W], W = ceil(M / 32), rows of
+   * W words contiguous: key j is visible to query i of batch b, head h only
+   * if bit (j % 32) of word [b'][h'][i][j / 32] is 1 (b' = b, or 0 when
+   * mask_batches == 1; h' likewise), in addition to kv_len, the causal rule
+   * and the window.  Bits of keys >= M are ignored.  4-byte aligned; the
+   * caller keeps it alive until the call's work on the stream is done.
+   * Paths: FA_PATH_PREFILL (which then needs workspace for its list of
+   * key tiles per query tile: fa_fwd_workspace_bytes; M up to 262080 and
+   * N * W * 4 below 2^31) and FA_PATH_F32.                                  */
+  const uint32_t* mask;
+  int32_t mask_batches;  /* 1 or B (0 means 1)                               */
+  int32_t mask_heads;    /* 1 or H (0 means 1)                               */
 } fa_options;
 
 /* What the planner decided for a shape (host-only, no device call). */
@@ -132,7 +149,8 @@ fa_status fa_plan_query(fa_shape s, fa_dtype dtype, int causal,
 
 /*
  * fa_fwd_workspace_bytes -- bytes of device workspace fa_fwd needs for this
- * shape (0 unless the split-KV path is chosen).  Returns 0 for a shape the
+ * shape (0 unless the split-KV path, the key/value-outer path or an element
+ * mask on the prefill path is chosen).  Returns 0 for a shape the
  * planner rejects.  The value depends on the shape and options only.
  */
 size_t fa_fwd_workspace_bytes(fa_shape s, fa_dtype dtype, int causal,
@@ -212,7 +230,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 /* fa_bwd_ex -- fa_bwd for a forward run with options `opt` (NULL = none):
  * a window must be the one the forward used (the gradients above then run
  * over the keys visible under it).  `path`, `split_keys`, the fp8 descales
- * and `kvouter_query_tiles` are ignored. */
+ * and `kvouter_query_tiles` are ignored; an element mask is not supported
+ * here (FA_ERR_UNSUPPORTED). */
 fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, const int32_t* kv_len, void* dq,
                     void* dk, void* dv, fa_shape s, fa_dtype dtype, float scale, int causal,

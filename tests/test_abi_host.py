@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
     assert sorted(fa.EXPORTS) == declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.fa_abi_version() == 4
+    assert L.fa_abi_version() == 5
 
 
 def test_status_strings():
@@ -250,3 +250,56 @@ def test_fp8_plan():
     bad = Options(0, 0, 0, 0, 0, 0, -1.0, 0.0, 0.0)
     st = L.fa_plan_query(Shape(1, 1, 16, 16, 64), fa.FP8, 0, ctypes.byref(bad), ctypes.byref(info))
     assert L.fa_status_str(st).decode() == "FA_ERR_ARG"
+
+
+def test_mask_plan():
+    """An element mask runs on the prefill path (also for N = 1) and the
+    fp32 path; the prefill path then needs workspace for its tile lists."""
+    p = fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True, mask_shape=(1, 1))
+    assert p["path_name"] == "prefill"
+    assert p["workspace_bytes"] == 16640      # 32 lists of 129 int32, rounded up to 256 B
+    p2 = fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True, mask_shape=(2, 32))
+    assert p2["workspace_bytes"] >= 2 * 32 * 32 * 129 * 4
+    assert fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True)["workspace_bytes"] == 0
+    assert fa.plan(4, 2, 1, 5000, 64, fa.BF16, mask_shape=(4, 1))["path_name"] == "prefill"
+    assert fa.plan(4, 2, 5, 50, 64, fa.F32, mask_shape=(1, 2))["workspace_bytes"] == 0
+    for kw, st in ((dict(path=fa.PATH_SPLITKV), "FA_ERR_UNSUPPORTED"),
+                   (dict(path=fa.PATH_KVOUTER), "FA_ERR_UNSUPPORTED")):
+        with pytest.raises(fa.FaError) as e:
+            fa.plan(2, 2, 1, 700, 64, fa.BF16, mask_shape=(1, 1), **kw)
+        assert e.value.name == st, kw
+    with pytest.raises(fa.FaError) as e:
+        fa.plan(1, 1, 16, 16, 64, fa.FP8, mask_shape=(1, 1))
+    assert e.value.name == "FA_ERR_UNSUPPORTED"
+    for shape in ((3, 1), (1, 5), (-1, 1)):            # B = 2, H = 4
+        with pytest.raises(fa.FaError) as e:
+            fa.plan(2, 4, 16, 16, 64, fa.BF16, mask_shape=shape)
+        assert e.value.name == "FA_ERR_ARG", shape
+    with pytest.raises(fa.FaError) as e:               # the list outgrows LDS
+        fa.plan(1, 1, 16, 262144, 64, fa.BF16, mask_shape=(1, 1))
+    assert e.value.name == "FA_ERR_UNSUPPORTED"
+    assert fa.plan(1, 1, 16, 262080, 64, fa.BF16, mask_shape=(1, 1))["path_name"] == "prefill"
+
+
+def test_bwd_rejects_mask():
+    L = fa.lib()
+    opt = Options(0, 0, 0, 0, 0, 0, 0.0, 0.0, 0.0, 64, 1, 1)
+    st = L.fa_bwd_ex(*([None] * 10), Shape(1, 1, 4, 4, 64), fa.BF16, 0.1, 0, None, 0, None,
+                     ctypes.byref(opt))
+    assert L.fa_status_str(st).decode() == "FA_ERR_UNSUPPORTED"
+
+
+def test_pack_mask_layout():
+    """Bit j % 32 of word j / 32 is key j (numpy's little-endian bit packing
+    read as little-endian words gives the same words)."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(3)
+    for M in (1, 31, 32, 33, 100, 130):
+        a = rng.random((2, 3, 5, M)) < 0.5
+        got = fa.pack_mask(torch.from_numpy(a)).numpy().view(np.uint32)
+        W = (M + 31) // 32
+        padded = np.zeros((2, 3, 5, W * 32), dtype=bool)
+        padded[..., :M] = a
+        want = np.packbits(padded, axis=-1, bitorder="little").view("<u4")
+        assert got.shape == (2, 3, 5, W) and np.array_equal(got, want), M

@@ -1,0 +1,135 @@
+"""GPU parity of element masks: the HIP kernels with a packed bitmask against
+the fp64 oracle with the same boolean mask ("Understanding FlashAttention",
+Attention: mask() covers causal masking and other kinds, each an elementwise
+constant that does not depend on the scores).
+
+Key j is visible to query i of (b, h) only if the mask keeps it, on top of
+kv_len, the causal rule and the window.  Cases cover masks shared by every
+batch and head and per-head masks; tiles the mask drops whole (skipped),
+keeps whole and keeps in part; rows the mask empties; N != M, ragged tails,
+single queries and the fp32 path.  The long workload is compared on sampled
+rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_33_amd as fa
+from exact_attention_33_amd import inputs
+from oracle.attention import attention_ref, attention_rows
+from tests.gpu_helpers import compare, default_scale, host64, sample_picks
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def make(seed, B, H, N, M, D, dtype):
+    q, k, v = inputs.qkv_host(seed, B, H, N, M, D)
+    return tuple(inputs.to_device(x, dtype, DEV) for x in (q, k, v))
+
+
+def mask_for(kind, B, H, N, M):
+    if kind == "random":
+        return inputs.random_mask(91, 1, 1, N, M, 0.5)
+    if kind == "random_per_head":
+        return inputs.random_mask(92, 1, H, N, M, 0.3)
+    if kind == "per_batch_head_blocks":
+        return inputs.block_mask(93, B, H, N, M, 64, 64, 0.5)
+    if kind == "documents":
+        return inputs.document_mask(94, N, M, 5)
+    if kind == "prefix":
+        return inputs.prefix_mask(N, M, M // 3)
+    if kind == "blocks_ragged":
+        return inputs.block_mask(95, 1, 1, N, M, 100, 37, 0.4)
+    if kind == "empty_rows":
+        m = inputs.random_mask(96, 1, 1, N, M, 0.6)
+        m[0, 0, ::7] = False
+        return m
+    raise ValueError(kind)
+
+
+CASES = [
+    # B, H, N, M, D, causal, kv_len, window, mask kind
+    (1, 2, 300, 300, 128, False, None, None, "random"),
+    (2, 2, 300, 517, 64, True, [517, 200], None, "random_per_head"),
+    (2, 2, 600, 640, 128, False, None, None, "per_batch_head_blocks"),
+    (1, 2, 1000, 1000, 128, True, None, None, "documents"),
+    (1, 1, 700, 700, 64, False, None, None, "prefix"),
+    (1, 2, 513, 900, 128, False, [650], (200, 50), "blocks_ragged"),
+    (2, 1, 260, 260, 128, True, None, None, "empty_rows"),
+    (2, 2, 1, 3000, 128, False, [3000, 1111], None, "random"),      # single queries
+    (1, 1, 150, 90, 128, True, None, None, "random"),                # N > M
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}N{}M{}D{}{}-{}".format(
+    *c[:5], "c" if c[5] else "", c[8]))
+def test_mask_bf16(case):
+    B, H, N, M, D, causal, kvl, win, kind = case
+    print(f"[mask] case {case}", flush=True)
+    q, k, v = make(70 + N, B, H, N, M, D, "bf16")
+    kvt = None if kvl is None else torch.tensor(kvl, dtype=torch.int32, device=DEV)
+    if kvl is not None:
+        inputs.poison_tail(k, v, kvl)
+    allowed = mask_for(kind, B, H, N, M)
+    words = fa.pack_mask(torch.from_numpy(allowed).to(DEV))
+    o, l = fa.fwd(q, k, v, scale=default_scale(D), causal=causal, kv_len=kvt, window=win,
+                  mask=words)
+    torch.cuda.synchronize()
+    kk, vv = host64(k), host64(v)
+    kk[np.isnan(kk)] = 0
+    vv[np.isnan(vv)] = 0
+    Or, Lr = attention_ref(host64(q), kk, vv, default_scale(D), causal,
+                           None if kvl is None else np.asarray(kvl), window=win, mask=allowed)
+    compare(host64(o), host64(l), Or, Lr, "bf16", f"mask {case}")
+
+
+def test_all_ones_mask_matches_unmasked_bitwise():
+    """A mask that keeps every key lists every tile as whole: the same tiles
+    in the same order as without a mask, so the results are identical."""
+    q, k, v = make(97, 1, 2, 700, 700, 128, "bf16")
+    words = fa.pack_mask(torch.ones((1, 1, 700, 700), dtype=torch.bool, device=DEV))
+    for causal in (False, True):
+        o1, l1 = fa.fwd(q, k, v, causal=causal)
+        o2, l2 = fa.fwd(q, k, v, causal=causal, mask=words)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), causal
+
+
+def test_mask_is_deterministic():
+    q, k, v = make(98, 1, 2, 500, 500, 128, "bf16")
+    words = fa.pack_mask(torch.from_numpy(inputs.random_mask(99, 1, 2, 500, 500, 0.5)).to(DEV))
+    o1, l1 = fa.fwd(q, k, v, mask=words)
+    o2, l2 = fa.fwd(q, k, v, mask=words)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_f32(causal):
+    q, k, v = make(72, 1, 2, 150, 170, 64, "f32")
+    allowed = inputs.random_mask(73, 1, 2, 150, 170, 0.4)
+    words = fa.pack_mask(torch.from_numpy(allowed).to(DEV))
+    o, l = fa.fwd(q, k, v, scale=0.2, causal=causal, mask=words)
+    torch.cuda.synchronize()
+    Or, Lr = attention_ref(host64(q), host64(k), host64(v), 0.2, causal, mask=allowed)
+    compare(host64(o), host64(l), Or, Lr, "f32", f"f32 mask causal={causal}")
+
+
+def test_mask_long_workload_sampled():
+    """B=2, H=32, N=M=8192, D=128 causal with 8 packed documents shared by
+    every batch and head, as the bench runs it."""
+    w = inputs.WORKLOADS["prefill_long_d128"]
+    print("[mask] long workload, documents", flush=True)
+    q, k, v = inputs.qkv_device(w.seed, w.B, w.H, w.N, w.M, w.D, "bf16", torch.device(DEV))
+    allowed = inputs.document_mask(7, w.N, w.M, 8)
+    words = fa.pack_mask(torch.from_numpy(allowed).to(DEV))
+    o, l = fa.fwd(q, k, v, causal=True, mask=words)
+    torch.cuda.synchronize()
+    picks = sample_picks(w.B, w.H, w.N, n_heads=4, seed=8)
+    Or, Lr = attention_rows(lambda b, h: host64(q[b, h]), lambda b, h: host64(k[b, h]),
+                            lambda b, h: host64(v[b, h]), default_scale(w.D), True, None,
+                            picks, mask=allowed)
+    og = np.stack([host64(o[b, h, i]) for b, h, i in picks])
+    lg = np.array([float(l[b, h, i]) for b, h, i in picks])
+    compare(og, lg, Or, Lr, "bf16", "long documents")
