@@ -60,12 +60,17 @@ def kernel_source_sha(files):
 
 SOURCES = {"prefill": ["prefill_bf16.hip", "device_common.h", "fa_internal.h"],
            "decode": ["decode_bf16.hip", "device_common.h", "fa_internal.h"],
-           "backward": ["bwd_bf16.hip", "device_common.h", "fa_internal.h"]}
+           "backward": ["bwd_bf16.hip", "device_common.h", "fa_internal.h", "mfma_asm.h"],
+           "fp8": ["prefill_fp8.hip", "device_common.h", "fa_internal.h"],
+           "kvouter": ["kvouter_bf16.hip", "device_common.h", "fa_internal.h", "mfma_asm.h"]}
+SOURCES["window"] = SOURCES["mask"] = SOURCES["prefill"]
 
 
-def measured_traffic(kind):
-    """HBM bytes per launch from the committed counter profile, or None when
-    the kernel source changed since the counters were taken."""
+def measured_traffic(kind, case=None):
+    """HBM bytes per launch (per call for several launches) from the committed
+    counter profile, or None when the kernel sources changed since the
+    counters were taken.  ``case`` picks one configuration of a leg that
+    times several (a window width, a mask)."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f).get(kind)
@@ -73,6 +78,10 @@ def measured_traffic(kind):
         return None
     if not rec or rec.get("source_sha") != kernel_source_sha(SOURCES[kind]):
         return None
+    if case is not None:
+        rec = rec.get("cases", {}).get(case)
+        if not rec:
+            return None
     return rec.get("bytes_per_launch")
 
 
@@ -277,7 +286,7 @@ def main():
         out["prefill"] = {"ms_mean": avg_p, "ms_min": min(ms_p), "tflops": tfs,
                           "frac_bf16_peak": tfs / PEAK_BF16_TFLOPS, "flop_per_launch": flop_p}
         traffic = measured_traffic("prefill")
-        out["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,causal>",
+        out["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, true, false, false>",
                            "achieved": tfs, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": tfs / PEAK_BF16_TFLOPS, "traffic": traffic}
     if do_d:
@@ -321,7 +330,8 @@ def main():
                      "frac": tf / PEAK_BF16_TFLOPS} if mfma_bound else
                     {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS})
-            roof.update({"kernel": "prefill_bf16_kernel<128,causal,window>", "traffic": None})
+            roof.update({"kernel": "prefill_bf16_kernel<128, true, true, false>",
+                         "traffic": measured_traffic("window", f"w{W}")})
             res[f"w{W}"] = {"window": [W - 1, 0], "ms_mean": avg, "ms_min": min(ms_w[W]),
                             "tflops": tf, "gbs": gbs, "flop_per_launch": flop,
                             "bytes_per_launch": bytes_w, "roofline": roof}
@@ -341,9 +351,11 @@ def main():
                          "visible_pairs_per_head": pairs_m[name],
                          "visible_fraction_of_causal": pairs_m[name] / (wp.N * (wp.N + 1) / 2),
                          "speedup_vs_unmasked_causal": ((sum(ms_p) / len(ms_p)) / avg) if do_p else None,
-                         "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel<128,causal,mask>",
+                         "roofline": {"bound": "mfma",
+                                      "kernel": "mask_tiles_kernel + prefill_bf16_kernel<128, true, false, true>",
                                       "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                      "frac": tf / PEAK_BF16_TFLOPS, "traffic": None}}
+                                      "frac": tf / PEAK_BF16_TFLOPS,
+                                      "traffic": measured_traffic("mask", name)}}
         out["mask"] = dict(res, flop_convention="4 D x visible (query, key) pairs per head "
                                                 "(exact count), B H heads")
         cfg["mask"] = {"B": wp.B, "H": wp.H, "N": wp.N, "M": wp.M, "D": wp.D, "causal": True,
@@ -357,9 +369,9 @@ def main():
         out["fp8"] = {"ms_mean": avg8, "ms_min": min(ms_8), "value": tf8, "unit": "TFLOP/s",
                       "frac_fp8_peak": tf8 / PEAK_FP8_TFLOPS, "flop_per_launch": flop_8,
                       "speedup_vs_bf16_prefill": ((sum(ms_p) / len(ms_p)) / avg8) if do_p else None,
-                      "roofline": {"bound": "mfma", "kernel": "prefill_fp8_kernel<128,causal>",
+                      "roofline": {"bound": "mfma", "kernel": "prefill_fp8_kernel<128, true>",
                                    "achieved": tf8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                                   "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": None}}
+                                   "frac": tf8 / PEAK_FP8_TFLOPS, "traffic": measured_traffic("fp8")}}
         cfg["fp8"] = {"B": wp.B, "H": wp.H, "N": wp.N, "M": wp.M, "D": wp.D, "causal": True,
                       "inputs": "E4M3, per-tensor scale amax/448 of the prefill's tensors"}
         if not (do_p or do_d):
@@ -372,7 +384,8 @@ def main():
             res[name] = {"query_tiles_per_group": min(tpg, -(-wp.N // 256)), "ms_mean": avg,
                          "ms_min": min(ms_k[name]), "tflops": tf,
                          "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
-                         "slowdown_vs_prefill": (avg / (sum(ms_p) / len(ms_p))) if do_p else None}
+                         "slowdown_vs_prefill": (avg / (sum(ms_p) / len(ms_p))) if do_p else None,
+                         "traffic": measured_traffic("kvouter", name)}
         out["kvouter"] = dict(res, note="ablation: key/value tiles outside, output accumulator "
                                         "and m, l read and written back per key tile (float32 "
                                         "workspace); same FLOP convention as the prefill")
