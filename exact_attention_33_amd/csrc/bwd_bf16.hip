@@ -229,22 +229,34 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
     constexpr bool mask = decltype(MASK)::value;
     const int qs0 = s * St::ROWS + 32 * u;
     f32x16 sacc[KBW], pacc[KBW];
-#pragma unroll
-    for (int kb = 0; kb < DK; ++kb) {
+    // Operands are read one fragment ahead of their MFMAs, in a ring of
+    // three: a read overwrites a register two fragments after the asm MFMAs
+    // last read it.  Scheduling barriers keep the reads where they are (the
+    // scheduler would otherwise sink them next to their use and expose the
+    // LDS latency before every fragment).
+    bf16x8 qa[3], ga[3];
+    auto read_qg = [&](int kb) __attribute__((always_inline)) {
       const int o = 32 * u * ROWB + 64 * (kb / 2) + ((kb & 1) ? rbase1 : rbase0);
-      const bf16x8 qa = *lds_at<bf16x8>(Qs, o);
-      const bf16x8 ga = *lds_at<bf16x8>(Gs, o);
+      qa[kb % 3] = *lds_at<bf16x8>(Qs, o);
+      ga[kb % 3] = *lds_at<bf16x8>(Gs, o);
+    };
+    read_qg(0);
+    static_for<DK>([&](auto kc) {
+      constexpr int kb = decltype(kc)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kb + 1 < DK) read_qg(kb + 1);
 #pragma unroll
       for (int kb2 = 0; kb2 < KBW; ++kb2) {
-        if (kb == 0) {
-          mfma_vv0(sacc[kb2], qa, kf[kb2][kb]);
-          mfma_vv0(pacc[kb2], ga, vf[kb2][kb]);
+        if constexpr (kb == 0) {
+          mfma_vv0(sacc[kb2], qa[kb % 3], kf[kb2][kb]);
+          mfma_vv0(pacc[kb2], ga[kb % 3], vf[kb2][kb]);
         } else {
-          mfma_vv(sacc[kb2], qa, kf[kb2][kb]);
-          mfma_vv(pacc[kb2], ga, vf[kb2][kb]);
+          mfma_vv(sacc[kb2], qa[kb % 3], kf[kb2][kb]);
+          mfma_vv(pacc[kb2], ga[kb % 3], vf[kb2][kb]);
         }
       }
-    }
+    });
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb2 = 0; kb2 < KBW; ++kb2) mfma_guard_v(sacc[kb2], pacc[kb2]);
     // P = 2^(S c - Lg), dS = P (dP - D).  Lane: key jw0 + 32 kb2 + l32,
@@ -276,24 +288,30 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
     }
 #pragma unroll
     for (int kb2 = 0; kb2 < KBW; ++kb2) valu_guard(pf[kb2][0], sf[kb2][0]), valu_guard(pf[kb2][1], sf[kb2][1]);
-    // dV^T += dO^T P, dK^T += Q^T dS over the step's 32 queries.
+    // dV^T += dO^T P, dK^T += Q^T dS over the step's 32 queries; fragment
+    // i = (sp, db), operands read one fragment ahead in a ring of three.
+    bf16x8 gt[3], qt[3];
+    auto read_t = [&](int i) __attribute__((always_inline)) {
+      const int o = (32 * u + 16 * (i / DB)) * ROWB + 64 * (i % DB);
+      const s16x4 glo = lds_read_tr16((const __bf16*)(Gs + o + tbase0));
+      const s16x4 ghi = lds_read_tr16((const __bf16*)(Gs + o + tbase1));
+      const s16x4 qlo = lds_read_tr16((const __bf16*)(Qs + o + tbase0));
+      const s16x4 qhi = lds_read_tr16((const __bf16*)(Qs + o + tbase1));
+      gt[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
+      qt[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    read_t(0);
+    static_for<2 * DB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value, sp = i / DB, db = i % DB;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i + 1 < 2 * DB) read_t(i + 1);
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int o = (32 * u + 16 * sp) * ROWB + 64 * db;
-        const s16x4 glo = lds_read_tr16((const __bf16*)(Gs + o + tbase0));
-        const s16x4 ghi = lds_read_tr16((const __bf16*)(Gs + o + tbase1));
-        const s16x4 qlo = lds_read_tr16((const __bf16*)(Qs + o + tbase0));
-        const s16x4 qhi = lds_read_tr16((const __bf16*)(Qs + o + tbase1));
-        const bf16x8 gt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int kb2 = 0; kb2 < KBW; ++kb2) {
-          mfma_aa(dvacc[kb2][db], gt, pf[kb2][sp]);
-          mfma_aa(dkacc[kb2][db], qt, sf[kb2][sp]);
-        }
+      for (int kb2 = 0; kb2 < KBW; ++kb2) {
+        mfma_aa(dvacc[kb2][db], gt[i % 3], pf[kb2][sp]);
+        mfma_aa(dkacc[kb2][db], qt[i % 3], sf[kb2][sp]);
       }
+    });
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Every branch below is uniform over the workgroup and no step is skipped
@@ -498,22 +516,30 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
     constexpr bool mask = decltype(MASK)::value;
     const int kk0 = s * St::ROWS + 32 * kb2;
     f32x16 sacc[NQB], pacc[NQB];
-#pragma unroll
-    for (int kb = 0; kb < DK; ++kb) {
+    // Operands one fragment ahead, in a ring of three (as in the dK/dV pass).
+    bf16x8 ka[3], va[3];
+    auto read_kv = [&](int kb) __attribute__((always_inline)) {
       const int o = 32 * kb2 * ROWB + 64 * (kb / 2) + ((kb & 1) ? rbase1 : rbase0);
-      const bf16x8 ka = *lds_at<bf16x8>(Ks, o);
-      const bf16x8 va = *lds_at<bf16x8>(Vs, o);
+      ka[kb % 3] = *lds_at<bf16x8>(Ks, o);
+      va[kb % 3] = *lds_at<bf16x8>(Vs, o);
+    };
+    read_kv(0);
+    static_for<DK>([&](auto kc) {
+      constexpr int kb = decltype(kc)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kb + 1 < DK) read_kv(kb + 1);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        if (kb == 0) {
-          mfma_vv0(sacc[qb], ka, qf[qb][kb]);
-          mfma_vv0(pacc[qb], va, gf[qb][kb]);
+        if constexpr (kb == 0) {
+          mfma_vv0(sacc[qb], ka[kb % 3], qf[qb][kb]);
+          mfma_vv0(pacc[qb], va[kb % 3], gf[qb][kb]);
         } else {
-          mfma_vv(sacc[qb], ka, qf[qb][kb]);
-          mfma_vv(pacc[qb], va, gf[qb][kb]);
+          mfma_vv(sacc[qb], ka[kb % 3], qf[qb][kb]);
+          mfma_vv(pacc[qb], va[kb % 3], gf[qb][kb]);
         }
       }
-    }
+    });
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) mfma_guard_v(sacc[qb], pacc[qb]);
     // Lane: query qw0 + 32 qb + l32; register r: key kk0 + 8 (r / 4) + 4 h + r % 4.
@@ -533,18 +559,24 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
       }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) valu_guard(sf[qb][0], sf[qb][1]);
-    // dQ^T += K^T dS^T over the 32 keys.
+    // dQ^T += K^T dS^T over the 32 keys; fragment i = (sp, db), operands
+    // one fragment ahead in a ring of three.
+    bf16x8 kt[3];
+    auto read_t = [&](int i) __attribute__((always_inline)) {
+      const int o = (32 * kb2 + 16 * (i / DB)) * ROWB + 64 * (i % DB);
+      const s16x4 klo = lds_read_tr16((const __bf16*)(Ks + o + tbase0));
+      const s16x4 khi = lds_read_tr16((const __bf16*)(Ks + o + tbase1));
+      kt[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(klo, khi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    read_t(0);
+    static_for<2 * DB>([&](auto ic) {
+      constexpr int i = decltype(ic)::value, sp = i / DB, db = i % DB;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i + 1 < 2 * DB) read_t(i + 1);
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int o = (32 * kb2 + 16 * sp) * ROWB + 64 * db;
-        const s16x4 klo = lds_read_tr16((const __bf16*)(Ks + o + tbase0));
-        const s16x4 khi = lds_read_tr16((const __bf16*)(Ks + o + tbase1));
-        const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(klo, khi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) mfma_aa(dqacc[qb][db], kt, sf[qb][sp]);
-      }
+      for (int qb = 0; qb < NQB; ++qb) mfma_aa(dqacc[qb][db], kt[i % 3], sf[qb][sp]);
+    });
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // As in the dK/dV pass: uniform branches only, no step skipped in a loop.
