@@ -26,19 +26,23 @@ Readings where the pages leave a step open (each listed in the design notes):
   * a masked entry has P = 0 and therefore dS = 0: it passes no gradient.
     Keys at or past kv_len[b] get dK = dV = 0; a query row with no visible key
     gets dQ = 0 and D = 0.
+  * an element mask (``oracle.attention``: a constant that does not depend
+    on the scores) enters only through which entries are visible, so it
+    changes nothing in the chain rule: its hidden entries pass no gradient.
   * dO is the gradient of the loss with respect to O, same shape as O; the
     gradient with respect to LSE is not an input (the pages keep L for the
     backward pass only, never as a result of the layer).
 """
 import numpy as np
 
-from .attention import clamp_kv_len, safe_softmax, visible_mask
+from .attention import clamp_kv_len, mask_of_head, safe_softmax, visible_mask
 
 __all__ = ["head_backward", "attention_bwd_ref"]
 
 
-def head_backward(q, k, v, do, scale, causal, kvl, window=None):
-    """One (batch, head) problem in fp64: q, do [N,D]; k, v [M,D].
+def head_backward(q, k, v, do, scale, causal, kvl, window=None, allow=None):
+    """One (batch, head) problem in fp64: q, do [N,D]; k, v [M,D]; ``allow``
+    an optional boolean [N, M] element mask.
 
     Returns a dict with the gradients ``dq`` [N,D], ``dk`` [M,D], ``dv``
     [M,D], the row statistic ``delta`` [N] and the intermediates ``p``,
@@ -51,7 +55,7 @@ def head_backward(q, k, v, do, scale, causal, kvl, window=None):
     kv, vv = k[:kvl], v[:kvl]
     # forward, as defined: scores, mask, row softmax, weighted sum of V
     S = np.float64(scale) * (q @ kv.T)
-    S = np.where(visible_mask(N, kvl, causal, window), S, -np.inf)
+    S = np.where(visible_mask(N, kvl, causal, window, allow), S, -np.inf)
     P = np.zeros((N, kvl))
     for i in range(N):
         P[i] = safe_softmax(S[i])[0]      # a row with no visible key stays 0
@@ -72,10 +76,11 @@ def head_backward(q, k, v, do, scale, causal, kvl, window=None):
             "p": P, "dp": dP, "ds": dS, "o": O}
 
 
-def attention_bwd_ref(q, k, v, do, scale, causal=False, kv_len=None, window=None):
+def attention_bwd_ref(q, k, v, do, scale, causal=False, kv_len=None, window=None, mask=None):
     """Gradients of O = attention(Q, K, V) for the upstream gradient dO.
 
-    q, do [B,H,N,D]; k, v [B,H,M,D].  Returns (dQ, dK, dV, D) in fp64 with
+    q, do [B,H,N,D]; k, v [B,H,M,D]; ``mask`` as in
+    ``oracle.attention.attention_ref``.  Returns (dQ, dK, dV, D) in fp64 with
     D [B,H,N] the row statistic sum_k dP_ik P_ik.
     """
     q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
@@ -90,6 +95,7 @@ def attention_bwd_ref(q, k, v, do, scale, causal=False, kv_len=None, window=None
     delta = np.zeros((B, H, N))
     for b in range(B):
         for h in range(H):
-            r = head_backward(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, kvs[b], window)
+            r = head_backward(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, kvs[b], window,
+                              mask_of_head(mask, b, h))
             dQ[b, h], dK[b, h], dV[b, h], delta[b, h] = r["dq"], r["dk"], r["dv"], r["delta"]
     return dQ, dK, dV, delta

@@ -21,9 +21,9 @@ def _rand(seed, B, H, N, M, D):
             rng.standard_normal((B, H, M, D)), rng.standard_normal((B, H, N, D)))
 
 
-def _loss(q, k, v, do, scale, causal, kv_len, window=None):
+def _loss(q, k, v, do, scale, causal, kv_len, window=None, mask=None):
     """The scalar whose gradient the backward returns: sum(dO * O)."""
-    O, _ = attention_ref(q, k, v, scale, causal, kv_len, window=window)
+    O, _ = attention_ref(q, k, v, scale, causal, kv_len, window=window, mask=mask)
     return float(np.sum(do * O))
 
 
@@ -130,5 +130,24 @@ def pin_window_finite_differences(bwd):
             assert err < 1e-7 * max(1.0, np.max(np.abs(fd))), (name, seed, err)
 
 
-ALL_BWD_PINS = [pin_finite_differences, pin_window_finite_differences, pin_delta_shortcut,
+def pin_mask_finite_differences(bwd):
+    """Central differences through the forward oracle under an element mask
+    (shared and per-head, with causal and kv_len, a row the mask empties)."""
+    h = 1e-5
+    for seed, B, H, N, M, D, scale, causal, kvl, mshape in [
+            (53, 1, 2, 5, 6, 3, 0.7, False, None, (1, 2, 5, 6)),
+            (54, 2, 1, 6, 6, 3, 0.9, True, [6, 4], (1, 1, 6, 6))]:
+        q, k, v, do = _rand(seed, B, H, N, M, D)
+        mask = np.random.default_rng(seed + 7).random(mshape) < 0.6
+        mask[0, 0, 2] = False
+        dq, dk, dv, _ = bwd(q, k, v, do, scale, causal, kvl, mask=mask)
+        assert not np.asarray(dq)[:, 0, 2].any()     # the emptied row of head 0
+        for name, x, g in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
+            fd = _central_diff(lambda: _loss(q, k, v, do, scale, causal, kvl, mask=mask), x, h)
+            err = np.max(np.abs(np.asarray(g) - fd))
+            assert err < 1e-7 * max(1.0, np.max(np.abs(fd))), (name, seed, err)
+
+
+ALL_BWD_PINS = [pin_finite_differences, pin_window_finite_differences,
+                pin_mask_finite_differences, pin_delta_shortcut,
                 pin_single_key, pin_uniform_scores, pin_dk_sums_to_zero, pin_causal_row0]

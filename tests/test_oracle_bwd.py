@@ -68,9 +68,10 @@ MUTANTS = {
     "dv_uses_q": ("dV = P.T @ do", "dV = P.T @ q"),
     "dp_uses_k": ("dP = do @ vv.T", "dP = do @ kv.T"),
     "delta_from_dp_only": ('delta = np.einsum("ij,ij->i", dP, P)', "delta = dP.sum(axis=1)"),
-    "top_left_causal": ("S = np.where(visible_mask(N, kvl, causal, window), S, -np.inf)",
+    "top_left_causal": ("S = np.where(visible_mask(N, kvl, causal, window, allow), S, -np.inf)",
                         "S = np.where(visible_mask(N, N, causal)[:, :kvl] if kvl <= N else "
                         "visible_mask(N, kvl, causal), S, -np.inf)"),
+    "mask_ignored": ("visible_mask(N, kvl, causal, window, allow)", "visible_mask(N, kvl, causal, window)"),
 }
 
 
