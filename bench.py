@@ -19,7 +19,8 @@ the hot path:
   7. the same prefill with an element mask shared by every batch and head:
      8 packed documents (a query sees its own document's keys), and an
      unstructured mask keeping each (query, key) pair with probability 1/2
-     (every tile applies bits); the tile-list pre-pass is inside the timing.
+     (every tile applies bits); the tile-list pre-pass is inside the timing;
+     the backward under the 8-document mask is timed beside them.
 Inputs are N(0, 1) drawn on the device from fixed seeds and are resident in
 HBM before timing starts.
 
@@ -205,6 +206,12 @@ def main():
         del masks, causal_pairs
         wsm = torch.empty(fa.workspace_bytes(wp.B, wp.H, wp.N, wp.M, wp.D, causal=True,
                                              mask_shape=(1, 1)), dtype=torch.uint8, device=dev)
+        # backward under the document mask: the forward's O and LSE, dO ~ N(0, 1)
+        omb, lmb = fa.fwd(qp, kp, vp, scale=scale_p, causal=True, mask=words_m["documents8"])
+        gmb = inputs.grad_device(wp.seed + 1000, wp.B, wp.H, wp.N, wp.D, "bf16", dev)
+        dqm, dkm, dvm = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
+        wsmb = torch.empty(fa.bwd_workspace_bytes(wp.B, wp.H, wp.N, wp.M, wp.D, mask_shape=(1, 1)),
+                           dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def main_step(evs=None):
@@ -264,6 +271,10 @@ def main():
                                                  lse=lm, mask=words_m[name], workspace=wsm,
                                                  stream=stream),
                         args.steps, args.warmup) for name in words_m} if do_m else {}
+    ms_mb = timed(lambda: fa.bwd(qp, kp, vp, omb, lmb, gmb, scale=scale_p, causal=True, dq=dqm,
+                                 dk=dkm, dv=dvm, workspace=wsmb, mask=words_m["documents8"],
+                                 stream=stream),
+                  args.steps, args.warmup) if do_m else []
     ms_k = {name: timed(lambda tpg=tpg: fa.fwd(qp, kp, vp, scale=scale_p, causal=True, out=ok_,
                                                lse=lk_, workspace=wsk, path=fa.PATH_KVOUTER,
                                                kvouter_query_tiles=tpg, stream=stream),
@@ -356,8 +367,17 @@ def main():
                                       "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                       "frac": tf / PEAK_BF16_TFLOPS,
                                       "traffic": measured_traffic("mask", name)}}
-        out["mask"] = dict(res, flop_convention="4 D x visible (query, key) pairs per head "
-                                                "(exact count), B H heads")
+        avg_b = sum(ms_mb) / len(ms_mb)
+        flop_mb = 10.0 * wp.D * pairs_m["documents8"] * wp.B * wp.H
+        tf_mb = flop_mb / (avg_b * 1e-3) / 1e12
+        res["backward_documents8"] = {
+            "ms_mean": avg_b, "ms_min": min(ms_mb), "tflops": tf_mb,
+            "speedup_vs_unmasked_backward": ((sum(ms_b) / len(ms_b)) / avg_b) if do_b else None,
+            "roofline": {"bound": "mfma", "kernel": "fa_bwd with a mask: rowstat + dkdv + dq (whole call)",
+                         "achieved": tf_mb, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf_mb / PEAK_BF16_TFLOPS, "traffic": None}}
+        out["mask"] = dict(res, flop_convention="forward 4 D, backward 10 D x visible (query, key) "
+                                                "pairs per head (exact count), B H heads")
         cfg["mask"] = {"B": wp.B, "H": wp.H, "N": wp.N, "M": wp.M, "D": wp.D, "causal": True,
                        "masks": {"documents8": "8 packed documents (seed 7), shared by all heads",
                                  "random50": "each pair kept with p = 1/2 (seed 11), shared"}}

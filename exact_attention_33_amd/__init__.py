@@ -35,7 +35,7 @@ PATH_NAMES = {PATH_PREFILL: "prefill", PATH_SPLITKV: "splitkv", PATH_F32: "f32",
 
 # Every symbol include/fa_mi355x.h declares.
 EXPORTS = ["fa_plan_query", "fa_fwd_workspace_bytes", "fa_fwd", "fa_fwd_ex",
-           "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_ex",
+           "fa_bwd_workspace_bytes", "fa_bwd_workspace_bytes_ex", "fa_bwd", "fa_bwd_ex",
            "fa_status_str", "fa_last_error", "fa_abi_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +95,8 @@ def lib():
     L.fa_fwd_ex.restype = i32
     L.fa_bwd_workspace_bytes.argtypes = [Shape, i32, i32]
     L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_bwd_workspace_bytes_ex.argtypes = [Shape, i32, i32, ctypes.POINTER(Options)]
+    L.fa_bwd_workspace_bytes_ex.restype = ctypes.c_size_t
     L.fa_bwd.argtypes = [vp] * 10 + [Shape, i32, f32, i32, vp, ctypes.c_size_t, vp]
     L.fa_bwd.restype = i32
     L.fa_bwd_ex.argtypes = L.fa_bwd.argtypes + [ctypes.POINTER(Options)]
@@ -232,17 +234,8 @@ def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
         out = torch.empty((B, H, N, D), dtype=torch.bfloat16 if dt == FP8 else q.dtype, device=dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    mask_arg = None
-    if mask is not None:
-        if mask.dim() != 4 or mask.dtype != torch.int32 or not mask.is_contiguous():
-            raise ValueError("mask must be contiguous int32 [Bm, Hm, N, ceil(M / 32)]")
-        if not mask.is_cuda or mask.device != dev:
-            raise ValueError("mask must be on the device of q")
-        Bm, Hm, Nm, Wm = mask.shape
-        if Nm != N or Wm != (M + 31) // 32 or Bm not in (1, B) or Hm not in (1, H):
-            raise ValueError("mask must be [1 or B, 1 or H, N, ceil(M / 32)]")
-        mask_arg = (mask.data_ptr(), Bm, Hm)
-    opts = _options(path, split_keys, window, kvouter_query_tiles, descale, mask_arg)
+    opts = _options(path, split_keys, window, kvouter_query_tiles, descale,
+                    _mask_arg(mask, B, H, N, M, dev))
     shape = Shape(B, H, N, M, D)
     ws_need = int(L.fa_fwd_workspace_bytes(shape, dt, int(bool(causal)), _opt_ptr(opts)))
     if ws_need and workspace is None:
@@ -260,16 +253,35 @@ def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
     return out, lse
 
 
-def bwd_workspace_bytes(B, H, N, M, D, dtype=BF16, causal=False):
-    return int(lib().fa_bwd_workspace_bytes(Shape(B, H, N, M, D), int(dtype), int(bool(causal))))
+def bwd_workspace_bytes(B, H, N, M, D, dtype=BF16, causal=False, mask_shape=None):
+    """Device workspace bwd needs; ``mask_shape=(Bm, Hm)`` for an element mask."""
+    o = None if mask_shape is None else _options(None, 0, mask=(1, mask_shape[0], mask_shape[1]))
+    return int(lib().fa_bwd_workspace_bytes_ex(Shape(B, H, N, M, D), int(dtype), int(bool(causal)),
+                                               _opt_ptr(o)))
+
+
+def _mask_arg(mask, B, H, N, M, dev):
+    """(pointer, Bm, Hm) of packed mask words after checking their shape."""
+    import torch
+    if mask is None:
+        return None
+    if mask.dim() != 4 or mask.dtype != torch.int32 or not mask.is_contiguous():
+        raise ValueError("mask must be contiguous int32 [Bm, Hm, N, ceil(M / 32)]")
+    if not mask.is_cuda or mask.device != dev:
+        raise ValueError("mask must be on the device of q")
+    Bm, Hm, Nm, Wm = mask.shape
+    if Nm != N or Wm != (M + 31) // 32 or Bm not in (1, B) or Hm not in (1, H):
+        raise ValueError("mask must be [1 or B, 1 or H, N, ceil(M / 32)]")
+    return (mask.data_ptr(), Bm, Hm)
 
 
 def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_len=None, *, dq=None, dk=None,
-        dv=None, workspace=None, window=None, stream=None):
+        dv=None, workspace=None, window=None, mask=None, stream=None):
     """Gradients of the forward through the C ABI; returns (dQ, dK, dV).
 
     ``o`` and ``lse`` must be what ``fwd`` returned for the same q, k, v,
-    scale, causal and kv_len; ``do`` is the upstream gradient, shaped like o.
+    scale, causal, kv_len, window and mask; ``do`` is the upstream gradient,
+    shaped like o.
     """
     import torch
     L = lib()
@@ -304,7 +316,8 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_len=None, *, dq=None, 
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     shape = Shape(B, H, N, M, D)
-    need = int(L.fa_bwd_workspace_bytes(shape, dt, int(bool(causal))))
+    opts = _options(None, 0, window, mask=_mask_arg(mask, B, H, N, M, dev))
+    need = int(L.fa_bwd_workspace_bytes_ex(shape, dt, int(bool(causal)), _opt_ptr(opts)))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -312,7 +325,6 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_len=None, *, dq=None, 
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    opts = _options(None, 0, window)
     st = L.fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                      do.data_ptr(), kv_len.data_ptr() if kv_len is not None else None,
                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), shape, dt, float(scale),

@@ -49,7 +49,15 @@
 //    that end at the last valid row, so ragged tails read as zeros; two
 //    stages, the next one loading while the current one is computed;
 //  * causal: tiles that no query of a wave sees are skipped, and only tiles
-//    that cross the diagonal are masked element by element.
+//    that cross the diagonal are masked element by element;
+//  * element masks: the dQ pass walks the forward's list of key tiles per
+//    query tile, the dK/dV pass a list of query stages per key tile built
+//    the same way (stages and tiles the mask drops are skipped).  Both stage
+//    the mask words of a stage in
+//    LDS beside the tiles and apply the bits on every stage: dQ as the
+//    forward does (lane = query, a word per 32 keys), dK/dV transposed
+//    (lane = key: words stored [word][query row], so one 16-byte read gives
+//    a lane the words of four consecutive queries).
 #include <cmath>
 #include <type_traits>
 
@@ -103,9 +111,64 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rowstat_kernel(BwdProblem p, 
 }
 
 // ---------------------------------------------------------------------------
+// Stage lists of an element mask for pass 2: one workgroup per (mask batch,
+// mask head, 256-key tile).  Wave w classifies query stages w, w + 4, ...
+// (lane = row) by OR and AND over the 8 words of the tile's keys (bits of
+// keys >= M and rows >= N do not count); wave 0 then compacts the stages
+// that keep some key, ascending, bit 31 set where the stage does not keep
+// the whole tile.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mask_stages_kernel(const uint32_t* __restrict__ mask, int N,
+                                                          int M, int W, int n_ktiles, int stride,
+                                                          int32_t* __restrict__ lists) {
+  const int g = blockIdx.x, kt = g % n_ktiles;
+  const int64_t mbh = g / n_ktiles;
+  const uint32_t* rows = mask + (size_t)mbh * N * W;
+  const int n_st = stride - 1;
+  int32_t* L = lists + (size_t)g * stride;
+  __shared__ signed char cls[kMaskMaxTiles];  // 0: no key kept; 1: all; -1: some
+  const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
+  const int w0 = kt * (kBwdBlockKV / 32);     // the tile's first word
+  for (int st = wv; st < n_st; st += 4) {
+    const int r = st * kBwdStageQ + lane;
+    bool any = false, all = true;
+    if (r < N) {
+      uint32_t o = 0u, a = ~0u;
+#pragma unroll
+      for (int w = 0; w < kBwdBlockKV / 32; ++w) {
+        const int n = min(max(M - (w0 + w) * 32, 0), 32);
+        const uint32_t v = n == 32 ? ~0u : (1u << n) - 1u;  // keys < M of the word
+        const uint32_t x = w0 + w < W ? rows[(size_t)r * W + w0 + w] : 0u;
+        o |= x & v;
+        a &= x | ~v;
+      }
+      any = o != 0u;
+      all = a == ~0u;
+    }
+    const bool st_any = __builtin_amdgcn_ballot_w64(any) != 0;
+    const bool st_all = __builtin_amdgcn_ballot_w64(!all) == 0;
+    if (lane == 0) cls[st] = st_any ? (st_all ? 1 : -1) : 0;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    int base = 0;
+    for (int c = 0; c < n_st; c += 64) {
+      const int st = c + lane;
+      const int k = st < n_st ? cls[st] : 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(k != 0);
+      if (k != 0)
+        L[1 + base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] =
+            k > 0 ? st : (int32_t)((uint32_t)st | 0x80000000u);
+      base += __builtin_popcountll(bal);
+    }
+    if (lane == 0) L[0] = base;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pass 2: dK and dV.  Workgroup = 4 waves x 64 keys; query stages of 64.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool WINDOW>
+template <int D, bool CAUSAL, bool WINDOW, bool BITS>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   using St = Stage<D>;
@@ -123,6 +186,10 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   __shared__ __attribute__((aligned(1024))) char Gs1[St::BYTES];
   __shared__ __attribute__((aligned(1024))) float Ls0[256];        // [0,64) Lg, [64,128) D
   __shared__ __attribute__((aligned(1024))) float Ls1[256];
+  // element mask: the stage's words [8 words of the workgroup's keys][64 rows]
+  __shared__ __attribute__((aligned(256))) uint32_t Ms0[BITS ? 512 : 1];
+  __shared__ __attribute__((aligned(256))) uint32_t Ms1[BITS ? 512 : 1];
+  __shared__ int tlist[BITS ? kMaskMaxTiles : 1];   // the key tile's listed query stages
 
   const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
   const int kt = (int)(logical % n_ktiles);   // causal: low key tiles see the most queries
@@ -154,7 +221,31 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   if (LOWQ) s_lo = min(max(k0 - off - wr, 0) / St::ROWS, n_stage_all);
   int s_end = n_stage_all;
   if (WINDOW) s_end = clampi(floor_div(k0 + kBwdBlockKV - 1 - off + wl, St::ROWS) + 1, s_lo, n_stage_all);
-  const int n_stages = k0 < kvl ? s_end - s_lo : 0;
+  int n_stages = k0 < kvl ? s_end - s_lo : 0;
+  // Element mask: the listed stages in [s_lo, s_lo + n_stages), from list
+  // position lo (the list ascends).
+  int lo = 0;
+  if constexpr (BITS) {
+    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+    const int stride = mask_stage_stride(N);
+    const int32_t* L = p.stage_lists + ((int64_t)(bm * p.mask_h + hm) * n_ktiles + kt) * stride;
+    const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
+    for (int i = tid; i < cnt; i += kBwdThreads) tlist[i] = L[1 + i] & 0x7FFFFFFF;
+    __syncthreads();
+    int below_lo = 0, below_hi = 0;
+    for (int i0 = 0; i0 < cnt; i0 += 64) {
+      const int e = i0 + lane < cnt ? tlist[i0 + lane] : 0x7FFFFFFF;
+      below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < s_lo));
+      below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < s_lo + n_stages));
+    }
+    lo = __builtin_amdgcn_readfirstlane(below_lo);
+    n_stages = __builtin_amdgcn_readfirstlane(below_hi) - lo;
+  }
+  // query stage of the t-th visited stage
+  auto stage_of = [&](int t) -> int {
+    if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + t]);
+    else return s_lo + t;
+  };
 
   // ---- K and V fragments of the wave's keys (B operands), zero past kv_len ----
   bf16x8 kf[KBW][DK], vf[KBW][DK];
@@ -177,7 +268,16 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   const int nrec_q = N * 2 * D;  // the planner keeps this below 2^31
   // Lane l of wave 0's extra block: Lg (l < 16) or D (16 <= l < 32) chunk.
   const uint32_t loff = (uint32_t)((lane < 16 ? lane : (lane < 32 ? p.Npad / 4 + lane - 16 : 0)) * 16);
-  auto load_stage = [&](int s, char* Qd, char* Gd, float* Ld) __attribute__((always_inline)) {
+  // Element mask: wave ws loads words 2 ws and 2 ws + 1 of the workgroup's
+  // 256 keys for the stage's 64 rows (lane = row; rows past N read row N - 1).
+  const uint32_t* Mg = nullptr;
+  int mbytes = 0;
+  if constexpr (BITS) {
+    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+    Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
+    mbytes = N * p.mask_w * 4;
+  }
+  auto load_stage = [&](int s, char* Qd, char* Gd, float* Ld, uint32_t* Md) __attribute__((always_inline)) {
     const uint32_t rb = (uint32_t)s * St::ROWS * 2 * D;
 #pragma unroll
     for (int i = 0; i < St::BPW; ++i) {
@@ -188,6 +288,16 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
     }
     if (ws == 0)
       buffer_load_lds16(Wg + s * St::ROWS, (int)((2 * p.Npad - s * St::ROWS) * 4), loff, (lds_ptr)Ld);
+    if constexpr (BITS) {
+      const uint32_t row = (uint32_t)min(s * St::ROWS + lane, N - 1);
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        int mofs = (2 * ws + w) * 64;
+        asm volatile("" : "+s"(mofs));
+        buffer_load_lds4(Mg, mbytes, (row * (uint32_t)p.mask_w + (uint32_t)(k0 / 32 + 2 * ws + w)) * 4u,
+                         (lds_ptr)(Md + mofs));
+      }
+    }
   };
 
   // ---- per-lane LDS read bases ----
@@ -224,8 +334,9 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
     thr_hi[kb2] = jw0 + 32 * kb2 + l32 - off + wl - 4 * h;
   }
 
-  // One 32-query step of stage s from buffers (Qs, Gs, Ls).
-  auto qstep = [&](int s, int u, const char* Qs, const char* Gs, const float* Ls, auto MASK) __attribute__((always_inline)) {
+  // One 32-query step of stage s from buffers (Qs, Gs, Ls, Ms).
+  auto qstep = [&](int s, int u, const char* Qs, const char* Gs, const float* Ls, const uint32_t* Ms,
+                   auto MASK) __attribute__((always_inline)) {
     constexpr bool mask = decltype(MASK)::value;
     const int qs0 = s * St::ROWS + 32 * u;
     f32x16 sacc[KBW], pacc[KBW];
@@ -268,6 +379,19 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
       const float4 D4 = *(const float4*)(Ls + 64 + 32 * u + 8 * g + 4 * h);
       const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
       const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+      // mask words of the four queries 32 u + 8 g + 4 h + e, for each of the
+      // wave's 32-key blocks: bit l32 is the lane's key; the eight bits the
+      // lane needs are gathered into one register, bit 4 kb2 + e
+      [[maybe_unused]] uint32_t mvis = 0u;
+      if constexpr (BITS) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < KBW; ++kb2) {
+          const uint4 w4 = *(const uint4*)(Ms + (2 * ws + kb2) * 64 + 32 * u + 8 * g + 4 * h);
+          const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mvis |= ((w[e] >> l32) & 1u) << (4 * kb2 + e);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
@@ -276,8 +400,10 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
           float pv = fast_exp2(fmaf(sacc[kb2][r], c, -Lv[e]));
           if constexpr (mask) {
             const int qi = qs0 + 8 * g + e;
-            bool hide = qi < thr[kb2];
+            bool hide = false;
+            if constexpr (LOWQ) hide = qi < thr[kb2];
             if constexpr (WINDOW) hide = hide | (qi > thr_hi[kb2]);
+            if constexpr (BITS) hide = hide | (((mvis >> (4 * kb2 + e)) & 1u) == 0u);
             pv = hide ? 0.f : pv;
           }
           const float dsv = pv * (pacc[kb2][r] - Dv[e]);
@@ -317,17 +443,27 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   // Every branch below is uniform over the workgroup and no step is skipped
   // inside a loop: control flow that joins with the accumulators live makes
   // the register allocator shuffle them between AGPRs.
-  auto iteration = [&](int t, const char* Qs, const char* Gs, const float* Ls, char* Qn, char* Gn,
-                       float* Ln, auto MASK) __attribute__((always_inline)) {
+  auto iteration = [&](int t, const char* Qs, const char* Gs, const float* Ls, const uint32_t* Ms,
+                       char* Qn, char* Gn, float* Ln, uint32_t* Mn, auto MASK) __attribute__((always_inline)) {
     wait_vm0();
     __syncthreads();
-    if (t + 1 < n_stages) load_stage(s_lo + t + 1, Qn, Gn, Ln);
-    qstep(s_lo + t, 0, Qs, Gs, Ls, MASK);
-    qstep(s_lo + t, 1, Qs, Gs, Ls, MASK);
+    const int s_cur = stage_of(t);
+    if (t + 1 < n_stages) load_stage(stage_of(t + 1), Qn, Gn, Ln, Mn);
+    qstep(s_cur, 0, Qs, Gs, Ls, Ms, MASK);
+    qstep(s_cur, 1, Qs, Gs, Ls, Ms, MASK);
   };
 
-  if (n_stages > 0) load_stage(s_lo, Qs0, Gs0, Ls0);
-  if constexpr (!WINDOW) {
+  if (n_stages > 0) load_stage(stage_of(0), Qs0, Gs0, Ls0, Ms0);
+  if constexpr (BITS) {
+    // element mask: every listed stage applies its bits (and the causal
+    // and window rules)
+    int t = 0;
+    for (; t + 1 < n_stages; t += 2) {
+      iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
+      iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, std::true_type{});
+    }
+    if (t < n_stages) iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
+  } else if constexpr (!WINDOW) {
     // Causal: the first n_mask stages hold queries that do not see every key
     // of the workgroup and are masked element by element (an even number, so
     // that the unmasked loop starts on buffer 0, or all stages).
@@ -338,18 +474,18 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
     }
     int t = 0;
     for (; t + 1 < n_mask; t += 2) {
-      iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::true_type{});
-      iteration(t + 1, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, std::true_type{});
+      iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
+      iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, std::true_type{});
     }
     if (t < n_mask) {  // n_mask == n_stages, odd: the last stage
-      iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::true_type{});
+      iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
       ++t;
     }
     for (; t + 1 < n_stages; t += 2) {
-      iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::false_type{});
-      iteration(t + 1, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, std::false_type{});
+      iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::false_type{});
+      iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, std::false_type{});
     }
-    if (t < n_stages) iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, std::false_type{});
+    if (t < n_stages) iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::false_type{});
   } else {
     // Window: stages before nA hold queries before some key's first viewer,
     // stages from nC on queries past some key's last viewer; both masked,
@@ -359,14 +495,14 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
     const int nC = clampi(floor_div(k0 - off + wl - (St::ROWS - 1), St::ROWS) + 1 - s_lo, nA, n_stages);
     auto segment = [&](int t, int t_end, auto MASK) __attribute__((always_inline)) {
       if ((t & 1) && t < t_end) {
-        iteration(t, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, MASK);
+        iteration(t, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, MASK);
         ++t;
       }
       for (; t + 1 < t_end; t += 2) {
-        iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, MASK);
-        iteration(t + 1, Qs1, Gs1, Ls1, Qs0, Gs0, Ls0, MASK);
+        iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, MASK);
+        iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, MASK);
       }
-      if (t < t_end) iteration(t, Qs0, Gs0, Ls0, Qs1, Gs1, Ls1, MASK);
+      if (t < t_end) iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, MASK);
     };
     segment(0, nA, std::true_type{});
     segment(nA, nC, std::false_type{});
@@ -411,7 +547,7 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
 // ---------------------------------------------------------------------------
 // Pass 3: dQ.  Workgroup = 4 waves x 64 queries; key stages of 64.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool WINDOW>
+template <int D, bool CAUSAL, bool WINDOW, bool BITS>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   using St = Stage<D>;
@@ -427,6 +563,11 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   __shared__ __attribute__((aligned(1024))) char Ks1[St::BYTES];
   __shared__ __attribute__((aligned(1024))) char Vs0[St::BYTES];
   __shared__ __attribute__((aligned(1024))) char Vs1[St::BYTES];
+  // element mask: the workgroup's list of key tiles (stages), and per stage
+  // each wave's mask words [word][64 rows]
+  __shared__ int tlist[BITS ? kMaskMaxTiles : 1];
+  __shared__ __attribute__((aligned(256))) uint32_t Mq0[BITS ? NW * 128 : 1];
+  __shared__ __attribute__((aligned(256))) uint32_t Mq1[BITS ? NW * 128 : 1];
 
   const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
   int qt = (int)(logical % n_qtiles);
@@ -449,7 +590,31 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   const int kv_end = UPPER ? min(kvl, q_last + off + wr + 1) : kvl;
   // first key stage (window: the first query's first key)
   const int t0 = WINDOW ? max(0, q0 + off - wl) / St::ROWS : 0;
-  const int n_stages = kv_end > t0 * St::ROWS ? (kv_end + St::ROWS - 1) / St::ROWS - t0 : 0;
+  int n_stages = kv_end > t0 * St::ROWS ? (kv_end + St::ROWS - 1) / St::ROWS - t0 : 0;
+  // Element mask: the listed stages in [t0, t0 + n_stages), from list
+  // position lo (the list ascends; see the forward).
+  int lo = 0;
+  if constexpr (BITS) {
+    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+    const int stride = mask_list_stride(M);
+    const int32_t* L = p.lists + ((int64_t)(bm * p.mask_h + hm) * n_qtiles + qt) * stride;
+    const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
+    for (int i = tid; i < cnt; i += kBwdThreads) tlist[i] = L[1 + i] & 0x7FFFFFFF;
+    __syncthreads();
+    int below_lo = 0, below_hi = 0;
+    for (int i0 = 0; i0 < cnt; i0 += 64) {
+      const int e = i0 + lane < cnt ? tlist[i0 + lane] : 0x7FFFFFFF;
+      below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t0));
+      below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t0 + n_stages));
+    }
+    lo = __builtin_amdgcn_readfirstlane(below_lo);
+    n_stages = __builtin_amdgcn_readfirstlane(below_hi) - lo;
+  }
+  // key stage of the t-th visited stage
+  auto stage_of = [&](int t) -> int {
+    if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + t]);
+    else return t0 + t;
+  };
 
   const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
   const __bf16* Gg = (const __bf16*)p.dout + (size_t)bh * N * D;
@@ -483,7 +648,26 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
 #pragma unroll
   for (int i = 0; i < St::BPW; ++i) soff[i] = St::slot_src((ws + i * NW) * 64 + lane);
   const int nrec_k = kvl * 2 * D;  // the planner keeps M * D * 2 below 2^31
-  auto load_stage = [&](int s, char* Kd, char* Vd) __attribute__((always_inline)) {
+  // Element mask: words 2 s and 2 s + 1 of the wave's 64 query rows (lane =
+  // row; rows past N read row N - 1).
+  const uint32_t* Mg = nullptr;
+  int mbytes = 0;
+  uint32_t mrow = 0;
+  if constexpr (BITS) {
+    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+    Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
+    mbytes = N * p.mask_w * 4;
+    mrow = (uint32_t)min(qw0 + lane, N - 1) * (uint32_t)p.mask_w;
+  }
+  auto load_stage = [&](int s, char* Kd, char* Vd, uint32_t* Md) __attribute__((always_inline)) {
+    if constexpr (BITS) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        int mofs = ws * 128 + w * 64;
+        asm volatile("" : "+s"(mofs));
+        buffer_load_lds4(Mg, mbytes, (mrow + 2u * (uint32_t)s + (uint32_t)w) * 4u, (lds_ptr)(Md + mofs));
+      }
+    }
     const uint32_t rb = (uint32_t)s * St::ROWS * 2 * D;
 #pragma unroll
     for (int i = 0; i < St::BPW; ++i) {
@@ -512,7 +696,8 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   const float c = fmaxf(p.scale * kLog2e, 1e-30f);
 
   // 32 keys (block kb2) of stage s.
-  auto kstep = [&](int s, int kb2, const char* Ks, const char* Vs, auto MASK) __attribute__((always_inline)) {
+  auto kstep = [&](int s, int kb2, const char* Ks, const char* Vs, const uint32_t* Ms, auto MASK)
+                   __attribute__((always_inline)) {
     constexpr bool mask = decltype(MASK)::value;
     const int kk0 = s * St::ROWS + 32 * kb2;
     f32x16 sacc[NQB], pacc[NQB];
@@ -544,6 +729,13 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
     for (int qb = 0; qb < NQB; ++qb) mfma_guard_v(sacc[qb], pacc[qb]);
     // Lane: query qw0 + 32 qb + l32; register r: key kk0 + 8 (r / 4) + 4 h + r % 4.
     bf16x8 sf[NQB][2];
+    // mask: key kk0 + 8 (r / 4) + 4 h + r % 4 is bit 8 (r / 4) + r % 4 of the
+    // row's word shifted down by 4 h (bit set: hidden)
+    [[maybe_unused]] uint32_t hid[NQB];
+    if constexpr (BITS) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) hid[qb] = ~Ms[ws * 128 + kb2 * 64 + 32 * qb + l32] >> (4 * h);
+    }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -553,6 +745,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
           const int key = kk0 + 8 * (r / 4) + 4 * h + r % 4;
           bool hide = key > lim[qb];
           if constexpr (WINDOW) hide = hide | (key < lim_lo[qb]);
+          if constexpr (BITS) hide = hide | (((hid[qb] >> (8 * (r / 4) + r % 4)) & 1u) != 0u);
           pv = hide ? 0.f : pv;
         }
         sf[qb][r / 8][r % 8] = (__bf16)(pv * (pacc[qb][r] - Dq[qb]));
@@ -580,33 +773,43 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   };
 
   // As in the dK/dV pass: uniform branches only, no step skipped in a loop.
-  auto iteration = [&](int t, const char* Ks, const char* Vs, char* Kn, char* Vn, auto MASK)
-                       __attribute__((always_inline)) {
+  auto iteration = [&](int t, const char* Ks, const char* Vs, const uint32_t* Ms, char* Kn, char* Vn,
+                       uint32_t* Mn, auto MASK) __attribute__((always_inline)) {
     wait_vm0();
     __syncthreads();
-    if (t + 1 < n_stages) load_stage(t0 + t + 1, Kn, Vn);
-    kstep(t0 + t, 0, Ks, Vs, MASK);
-    kstep(t0 + t, 1, Ks, Vs, MASK);
+    const int s_cur = stage_of(t);
+    if (t + 1 < n_stages) load_stage(stage_of(t + 1), Kn, Vn, Mn);
+    kstep(s_cur, 0, Ks, Vs, Ms, MASK);
+    kstep(s_cur, 1, Ks, Vs, Ms, MASK);
   };
 
   // Stages before n_clean (an even number) are seen whole by every query of
   // the workgroup: no key past kv_len and, causal, none past the first
   // query's last key.  The rest are masked element by element.
-  if (n_stages > 0) load_stage(t0, Ks0, Vs0);
-  if constexpr (!WINDOW) {
+  if (n_stages > 0) load_stage(stage_of(0), Ks0, Vs0, Mq0);
+  if constexpr (BITS) {
+    // element mask: every listed stage applies its bits (and the causal,
+    // window and kv_len rules)
+    int t = 0;
+    for (; t + 1 < n_stages; t += 2) {
+      iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
+      iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, std::true_type{});
+    }
+    if (t < n_stages) iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
+  } else if constexpr (!WINDOW) {
     int n_clean = kvl / St::ROWS;
     if (CAUSAL) n_clean = min(n_clean, q0 + off + 1 > 0 ? (q0 + off + 1) / St::ROWS : 0);
     n_clean = min(n_clean, n_stages) / 2 * 2;
     int t = 0;
     for (; t < n_clean; t += 2) {
-      iteration(t, Ks0, Vs0, Ks1, Vs1, std::false_type{});
-      iteration(t + 1, Ks1, Vs1, Ks0, Vs0, std::false_type{});
+      iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::false_type{});
+      iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, std::false_type{});
     }
     for (; t + 1 < n_stages; t += 2) {
-      iteration(t, Ks0, Vs0, Ks1, Vs1, std::true_type{});
-      iteration(t + 1, Ks1, Vs1, Ks0, Vs0, std::true_type{});
+      iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
+      iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, std::true_type{});
     }
-    if (t < n_stages) iteration(t, Ks0, Vs0, Ks1, Vs1, std::true_type{});
+    if (t < n_stages) iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
   } else {
     // Window: stages before nA hold keys before the last query's first key,
     // stages from nC on keys past the first query's last key (or kv_len);
@@ -617,14 +820,14 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
     const int nC = clampi(floor_div(last_all - (St::ROWS - 1), St::ROWS) + 1 - t0, nA, n_stages);
     auto segment = [&](int t, int t_end, auto MASK) __attribute__((always_inline)) {
       if ((t & 1) && t < t_end) {
-        iteration(t, Ks1, Vs1, Ks0, Vs0, MASK);
+        iteration(t, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, MASK);
         ++t;
       }
       for (; t + 1 < t_end; t += 2) {
-        iteration(t, Ks0, Vs0, Ks1, Vs1, MASK);
-        iteration(t + 1, Ks1, Vs1, Ks0, Vs0, MASK);
+        iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, MASK);
+        iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, MASK);
       }
-      if (t < t_end) iteration(t, Ks0, Vs0, Ks1, Vs1, MASK);
+      if (t < t_end) iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, MASK);
     };
     segment(0, nA, std::true_type{});
     segment(nA, nC, std::false_type{});
@@ -656,6 +859,34 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   }
 }
 
+template <int D, bool BITS>
+void launch_bwd_passes(const BwdProblem& p, hipStream_t stream) {
+  const int64_t bh = (int64_t)p.B * p.H;
+  const dim3 block(kBwdThreads);
+  if (p.M > 0) {
+    const int n_kt = (p.M + kBwdBlockKV - 1) / kBwdBlockKV;
+    const dim3 grid((unsigned)(bh * n_kt));
+    if (p.window) {
+      if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true, BITS>), grid, block, 0, stream, p, n_kt);
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true, BITS>), grid, block, 0, stream, p, n_kt);
+    } else {
+      if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, BITS>), grid, block, 0, stream, p, n_kt);
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false, BITS>), grid, block, 0, stream, p, n_kt);
+    }
+  }
+  if (p.N > 0) {
+    const int n_qt = (p.N + kBwdBlockQ - 1) / kBwdBlockQ;
+    const dim3 grid((unsigned)(bh * n_qt));
+    if (p.window) {
+      if (p.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, BITS>), grid, block, 0, stream, p, n_qt);
+      else hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, BITS>), grid, block, 0, stream, p, n_qt);
+    } else {
+      if (p.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, BITS>), grid, block, 0, stream, p, n_qt);
+      else hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, BITS>), grid, block, 0, stream, p, n_qt);
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdProblem& p, hipStream_t stream) {
   const int64_t bh = (int64_t)p.B * p.H;
@@ -664,27 +895,19 @@ hipError_t launch_bwd_d(const BwdProblem& p, hipStream_t stream) {
     const int nchunk = p.Npad / 64;
     hipLaunchKernelGGL(bwd_rowstat_kernel<D>, dim3((unsigned)(bh * nchunk)), block, 0, stream, p, nchunk);
   }
-  if (p.M > 0) {
-    const int n_kt = (p.M + kBwdBlockKV - 1) / kBwdBlockKV;
-    const dim3 grid((unsigned)(bh * n_kt));
-    if (p.window) {
-      if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), grid, block, 0, stream, p, n_kt);
-      else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), grid, block, 0, stream, p, n_kt);
-    } else {
-      if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), grid, block, 0, stream, p, n_kt);
-      else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), grid, block, 0, stream, p, n_kt);
+  if (p.mask) {
+    // the dQ pass's tile lists (the forward's) and the dK/dV pass's stage
+    // lists, then both passes with bits
+    if (p.N > 0) launch_mask_tiles(p.mask, p.N, p.M, p.mask_w, p.mask_b, p.mask_h, p.lists, stream);
+    if (p.M > 0) {
+      const int n_kt = (p.M + kBwdBlockKV - 1) / kBwdBlockKV;
+      hipLaunchKernelGGL(mask_stages_kernel, dim3((unsigned)((int64_t)p.mask_b * p.mask_h * n_kt)),
+                         dim3(256), 0, stream, p.mask, p.N, p.M, p.mask_w, n_kt,
+                         mask_stage_stride(p.N), p.stage_lists);
     }
-  }
-  if (p.N > 0) {
-    const int n_qt = (p.N + kBwdBlockQ - 1) / kBwdBlockQ;
-    const dim3 grid((unsigned)(bh * n_qt));
-    if (p.window) {
-      if (p.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), grid, block, 0, stream, p, n_qt);
-      else hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), grid, block, 0, stream, p, n_qt);
-    } else {
-      if (p.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), grid, block, 0, stream, p, n_qt);
-      else hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), grid, block, 0, stream, p, n_qt);
-    }
+    launch_bwd_passes<D, true>(p, stream);
+  } else {
+    launch_bwd_passes<D, false>(p, stream);
   }
   return hipGetLastError();
 }

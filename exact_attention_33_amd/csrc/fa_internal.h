@@ -62,6 +62,10 @@ hipError_t launch_splitkv_bf16(const Problem& p, const Plan& plan, void* workspa
 hipError_t launch_kvouter_bf16(const Problem& p, const Plan& plan, void* workspace,
                                hipStream_t stream);
 hipError_t launch_prefill_fp8(const Problem& p, const Plan& plan, hipStream_t stream);
+// Tile lists of an element mask (layout below), one per (mask batch, mask
+// head, 256-query tile), into `lists`.
+void launch_mask_tiles(const uint32_t* mask, int N, int M, int mask_w, int mask_b, int mask_h,
+                       int32_t* lists, hipStream_t stream);
 
 // Tile constants shared by the planner and the kernels.
 constexpr int kPrefillBlockQ = 256;   // 4 waves x 64 queries
@@ -75,8 +79,8 @@ constexpr int kPrefillThreads = 256;
 // kernel copies a list into LDS, so a list holds at most kMaskMaxTiles - 1
 // tiles.
 constexpr int kMaskMaxTiles = 4096;
-inline int32_t mask_list_stride(int M) { return (M + kPrefillBlockK - 1) / kPrefillBlockK + 1; }
-inline int32_t mask_words(int M) { return (M + 31) / 32; }
+__host__ __device__ inline int32_t mask_list_stride(int M) { return (M + kPrefillBlockK - 1) / kPrefillBlockK + 1; }
+__host__ __device__ inline int32_t mask_words(int M) { return (M + 31) / 32; }
 
 constexpr int kF32BlockQ = 16;        // 16 query rows x 16 lanes
 constexpr int kF32BlockK = 32;
@@ -122,6 +126,13 @@ struct BwdProblem {
   int causal;
   int window;            // as in Problem
   int32_t wl, wr;
+  // Element mask, as in Problem (nullptr: none); with a mask the workspace
+  // continues, at byte offset bwd_mask_lists_offset, with the tile lists of
+  // the dQ pass (the forward's lists).
+  const uint32_t* mask;
+  int32_t mask_b, mask_h, mask_w;
+  int32_t* lists;        // dQ pass: per 256-query tile, the key stages (64 keys)
+  int32_t* stage_lists;  // dK/dV pass: per 256-key tile, the query stages (64 queries)
 };
 
 constexpr int kBwdThreads = 256;
@@ -132,8 +143,29 @@ constexpr int kBwdBlockQ = 256;        // dQ kernel: queries per workgroup (4 wa
 constexpr int kBwdStageK = 64;         // dQ kernel: keys per LDS stage
 
 inline int64_t bwd_npad(int N) { return ((int64_t)N + kBwdRowPad - 1) / kBwdRowPad * kBwdRowPad; }
-inline size_t bwd_workspace_bytes(const fa_shape& s) {
+inline size_t bwd_stats_bytes(const fa_shape& s) {
   return (size_t)s.B * (size_t)s.H * (size_t)bwd_npad(s.N) * 2 * sizeof(float);
+}
+inline size_t bwd_mask_lists_offset(const fa_shape& s) { return (bwd_stats_bytes(s) + 255) / 256 * 256; }
+// dK/dV pass with a mask: per (mask batch, mask head, 256-key tile), the
+// count and then the ascending 64-query stages in which some query keeps
+// one of the tile's keys.
+__host__ __device__ inline int32_t mask_stage_stride(int N) { return (N + kBwdStageQ - 1) / kBwdStageQ + 1; }
+inline size_t bwd_lists_bytes(const fa_shape& s, int mask_b, int mask_h) {
+  const size_t n = (size_t)mask_b * (size_t)mask_h * (size_t)((s.N + kBwdBlockQ - 1) / kBwdBlockQ) *
+                   (size_t)mask_list_stride(s.M) * sizeof(int32_t);
+  return (n + 255) / 256 * 256;
+}
+inline size_t bwd_stage_lists_bytes(const fa_shape& s, int mask_b, int mask_h) {
+  const size_t n = (size_t)mask_b * (size_t)mask_h * (size_t)((s.M + kBwdBlockKV - 1) / kBwdBlockKV) *
+                   (size_t)mask_stage_stride(s.N) * sizeof(int32_t);
+  return (n + 255) / 256 * 256;
+}
+// mask_b, mask_h: 0 without a mask
+inline size_t bwd_workspace_bytes(const fa_shape& s, int mask_b = 0, int mask_h = 0) {
+  if (!mask_b) return bwd_stats_bytes(s);
+  return bwd_mask_lists_offset(s) + bwd_lists_bytes(s, mask_b, mask_h) +
+         bwd_stage_lists_bytes(s, mask_b, mask_h);
 }
 // Row stride in LDS of a staged [rows][D] bf16 tile: 64 bytes of padding.
 inline int bwd_lds_row_bytes(int D) { return 2 * D + 64; }

@@ -814,6 +814,15 @@ void launch_prefill_d(const Problem& p, dim3 grid, hipStream_t stream, int n_qti
 
 }  // namespace
 
+void launch_mask_tiles(const uint32_t* mask, int N, int M, int mask_w, int mask_b, int mask_h,
+                       int32_t* lists, hipStream_t stream) {
+  const int n_qtiles = (N + kPrefillBlockQ - 1) / kPrefillBlockQ;
+  const int64_t n_lists = (int64_t)mask_b * mask_h * n_qtiles;
+  if (n_lists == 0) return;
+  hipLaunchKernelGGL(mask_tiles_kernel, dim3((unsigned)n_lists), dim3(256), 0, stream, mask, N, M,
+                     mask_w, n_qtiles, mask_list_stride(M), lists);
+}
+
 hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, void* workspace,
                                hipStream_t stream) {
   if (plan.grid == 0) return hipSuccess;
@@ -823,9 +832,7 @@ hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, void* workspa
   if (p.mask) {
     // the tile lists, one per (mask batch, mask head, query tile)
     lists = (int32_t*)workspace;
-    const int64_t n_lists = (int64_t)p.mask_b * p.mask_h * n_qtiles;
-    hipLaunchKernelGGL(mask_tiles_kernel, dim3((unsigned)n_lists), dim3(256), 0, stream, p.mask,
-                       p.N, p.M, p.mask_w, n_qtiles, plan.mask_tiles, lists);
+    launch_mask_tiles(p.mask, p.N, p.M, p.mask_w, p.mask_b, p.mask_h, lists, stream);
   }
   if (p.D == 64) launch_prefill_d<64>(p, grid, stream, n_qtiles, lists, plan.mask_tiles);
   else launch_prefill_d<128>(p, grid, stream, n_qtiles, lists, plan.mask_tiles);

@@ -144,9 +144,17 @@ fa_status fa_fwd(const void* q, const void* k, const void* v,
 }
 
 size_t fa_bwd_workspace_bytes(fa_shape s, fa_dtype dtype, int causal) {
+  return fa_bwd_workspace_bytes_ex(s, dtype, causal, nullptr);
+}
+
+size_t fa_bwd_workspace_bytes_ex(fa_shape s, fa_dtype dtype, int causal, const fa_options* opt) {
   (void)causal;
   if (dtype != FA_BF16 || s.B < 0 || s.H < 0 || s.N < 0 || s.M < 0) return 0;
-  return fa::bwd_workspace_bytes(s);
+  if (!opt || !opt->mask) return fa::bwd_workspace_bytes(s);
+  const int32_t mb = opt->mask_batches ? opt->mask_batches : 1;
+  const int32_t mh = opt->mask_heads ? opt->mask_heads : 1;
+  if ((mb != 1 && mb != s.B) || (mh != 1 && mh != s.H)) return 0;
+  return fa::bwd_workspace_bytes(s, mb, mh);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -164,8 +172,11 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                     const fa_options* opt) {
   if (opt && opt->window != 0 && opt->window != 1)
     return fail(FA_ERR_ARG, "fa_bwd: options.window must be 0 or 1");
-  if (opt && opt->mask)
-    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: an element mask is not supported by the backward");
+  const uint32_t* mask = opt ? opt->mask : nullptr;
+  const int32_t mask_b = mask && opt->mask_batches ? opt->mask_batches : 1;
+  const int32_t mask_h = mask && opt->mask_heads ? opt->mask_heads : 1;
+  if (mask && ((mask_b != 1 && mask_b != s.B) || (mask_h != 1 && mask_h != s.H)))
+    return fail(FA_ERR_ARG, "fa_bwd: options.mask_batches must be 1 or B and options.mask_heads 1 or H");
   const bool win = opt && opt->window;
   if (win && (opt->window_left < 0 || opt->window_right < 0))
     return fail(FA_ERR_ARG, "fa_bwd: options.window_left and window_right must be >= 0");
@@ -182,6 +193,13 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   // byte offsets, and their grids must fit 32 bits.
   if ((int64_t)s.N * s.D * 2 > INT32_MAX || (int64_t)s.M * s.D * 2 > INT32_MAX)
     return fail(FA_ERR_UNSUPPORTED, "fa_bwd: needs N * D * 2 and M * D * 2 below 2^31");
+  // With a mask the dQ pass holds a list of key tiles in LDS, and both passes
+  // address one (mask batch, mask head) of the mask with 32-bit byte offsets.
+  if (mask && (fa::mask_list_stride(s.M) > fa::kMaskMaxTiles ||
+               fa::mask_stage_stride(s.N) > fa::kMaskMaxTiles ||
+               (int64_t)s.N * fa::mask_words(s.M) * 4 > INT32_MAX))
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: an element mask needs N and M <= 262080 and "
+                                    "N * ceil(M / 32) * 4 < 2^31");
   if (bh > INT32_MAX ||
       bh * ((fa::bwd_npad(s.N) + 63) / 64) > INT32_MAX ||
       bh * (((int64_t)s.M + fa::kBwdBlockKV - 1) / fa::kBwdBlockKV) > INT32_MAX)
@@ -199,9 +217,9 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   for (const void* ptr : a16)
     if (ptr && !aligned(ptr, 16))
       return fail(FA_ERR_ALIGN, "fa_bwd: q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
-  if ((lse && !aligned(lse, 4)) || (kv_len && !aligned(kv_len, 4)))
-    return fail(FA_ERR_ALIGN, "fa_bwd: lse and kv_len must be 4-byte aligned");
-  const size_t need = fa::bwd_workspace_bytes(s);
+  if ((lse && !aligned(lse, 4)) || (kv_len && !aligned(kv_len, 4)) || (mask && !aligned(mask, 4)))
+    return fail(FA_ERR_ALIGN, "fa_bwd: lse, kv_len and options.mask must be 4-byte aligned");
+  const size_t need = mask ? fa::bwd_workspace_bytes(s, mask_b, mask_h) : fa::bwd_workspace_bytes(s);
   if (need) {
     if (!workspace)
       return fail(FA_ERR_WORKSPACE, "fa_bwd: this shape needs %zu workspace bytes, got NULL", need);
@@ -213,7 +231,12 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   }
   fa::BwdProblem p{q, k, v, o, dout, lse, kv_len, dq, dk, dv, (float*)workspace,
                    s.B, s.H, s.N, s.M, s.D, (int32_t)fa::bwd_npad(s.N), scale, causal ? 1 : 0,
-                   win ? 1 : 0, win ? opt->window_left : 0, win ? opt->window_right : 0};
+                   win ? 1 : 0, win ? opt->window_left : 0, win ? opt->window_right : 0,
+                   mask, mask_b, mask_h, fa::mask_words(s.M),
+                   mask ? (int32_t*)((char*)workspace + fa::bwd_mask_lists_offset(s)) : nullptr,
+                   mask ? (int32_t*)((char*)workspace + fa::bwd_mask_lists_offset(s) +
+                                     fa::bwd_lists_bytes(s, mask_b, mask_h))
+                        : nullptr};
   const hipError_t err = fa::launch_bwd_bf16(p, (hipStream_t)stream);
   if (err != hipSuccess)
     return fail(FA_ERR_HIP, "fa_bwd: launch failed: %s", hipGetErrorString(err));

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 /* FA_FP8: OCP E4M3 (finite max 448, no infinities) Q, K, V with per-tensor
  * descale factors (fa_options); O is then bf16 and LSE float32. */
@@ -221,6 +221,12 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v,
  * (0 for an unsupported dtype). */
 size_t fa_bwd_workspace_bytes(fa_shape s, fa_dtype dtype, int causal);
 
+/* fa_bwd_workspace_bytes_ex -- the same for fa_bwd_ex with options `opt`
+ * (NULL = none): with an element mask the workspace also holds the dQ
+ * pass's lists of key tiles, as the forward's prefill path does (0 for an
+ * unsupported dtype or mask shape). */
+size_t fa_bwd_workspace_bytes_ex(fa_shape s, fa_dtype dtype, int causal, const fa_options* opt);
+
 /* fa_bwd -- dq, dk, dv as defined above. */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dout, const int32_t* kv_len, void* dq, void* dk, void* dv,
@@ -229,9 +235,11 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 
 /* fa_bwd_ex -- fa_bwd for a forward run with options `opt` (NULL = none):
  * a window must be the one the forward used (the gradients above then run
- * over the keys visible under it).  `path`, `split_keys`, the fp8 descales
- * and `kvouter_query_tiles` are ignored; an element mask is not supported
- * here (FA_ERR_UNSUPPORTED). */
+ * over the keys visible under it), and so must an element mask (the same
+ * words, mask_batches and mask_heads; the gradients of the entries it hides
+ * are 0; workspace from fa_bwd_workspace_bytes_ex; M up to 262080 and
+ * N * ceil(M / 32) * 4 below 2^31).  `path`, `split_keys`, the fp8 descales
+ * and `kvouter_query_tiles` are ignored. */
 fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, const int32_t* kv_len, void* dq,
                     void* dk, void* dv, fa_shape s, fa_dtype dtype, float scale, int causal,

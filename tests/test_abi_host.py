@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
     assert sorted(fa.EXPORTS) == declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.fa_abi_version() == 5
+    assert L.fa_abi_version() == 6
 
 
 def test_status_strings():
@@ -281,12 +281,34 @@ def test_mask_plan():
     assert fa.plan(1, 1, 16, 262080, 64, fa.BF16, mask_shape=(1, 1))["path_name"] == "prefill"
 
 
-def test_bwd_rejects_mask():
+def test_bwd_mask_checks():
+    """The backward takes an element mask: its workspace adds the dQ pass's
+    tile lists; bad mask shapes and sizes are rejected before any launch."""
     L = fa.lib()
-    opt = Options(0, 0, 0, 0, 0, 0, 0.0, 0.0, 0.0, 64, 1, 1)
-    st = L.fa_bwd_ex(*([None] * 10), Shape(1, 1, 4, 4, 64), fa.BF16, 0.1, 0, None, 0, None,
+    base = fa.bwd_workspace_bytes(2, 4, 1000, 1000, 64)
+    with_mask = fa.bwd_workspace_bytes(2, 4, 1000, 1000, 64, mask_shape=(2, 1))
+    lists = 2 * 1 * 4 * (16 + 1) * 4                    # 4 query tiles, 16 key tiles + count
+    stages = 2 * 1 * 4 * (16 + 1) * 4                   # 4 key tiles, 16 query stages + count
+    assert with_mask == (base + 255) // 256 * 256 + (lists + 255) // 256 * 256 + \
+        (stages + 255) // 256 * 256
+    assert fa.bwd_workspace_bytes(2, 4, 1000, 1000, 64, mask_shape=(3, 1)) == 0
+    for mb, mh, shape, st_want in ((3, 1, (2, 4, 16, 16, 64), "FA_ERR_ARG"),
+                                   (1, 5, (2, 4, 16, 16, 64), "FA_ERR_ARG"),
+                                   (1, 1, (1, 1, 16, 262144, 64), "FA_ERR_UNSUPPORTED"),
+                                   (1, 1, (1, 1, 262144, 16, 64), "FA_ERR_UNSUPPORTED")):
+        opt = Options(0, 0, 0, 0, 0, 0, 0.0, 0.0, 0.0, P, mb, mh)
+        st = L.fa_bwd_ex(*([P] * 10), Shape(*shape), fa.BF16, 0.1, 0, P, 1 << 30, None,
+                         ctypes.byref(opt))
+        assert L.fa_status_str(st).decode() == st_want, (mb, mh, shape)
+    opt = Options(0, 0, 0, 0, 0, 0, 0.0, 0.0, 0.0, P + 2, 1, 1)     # misaligned words
+    st = L.fa_bwd_ex(*([P] * 10), Shape(1, 1, 16, 16, 64), fa.BF16, 0.1, 0, P, 1 << 30, None,
                      ctypes.byref(opt))
-    assert L.fa_status_str(st).decode() == "FA_ERR_UNSUPPORTED"
+    assert L.fa_status_str(st).decode() == "FA_ERR_ALIGN"
+    opt = Options(0, 0, 0, 0, 0, 0, 0.0, 0.0, 0.0, P, 1, 1)          # workspace too small
+    need = fa.bwd_workspace_bytes(1, 1, 16, 16, 64, mask_shape=(1, 1))
+    st = L.fa_bwd_ex(*([P] * 10), Shape(1, 1, 16, 16, 64), fa.BF16, 0.1, 0, P, need - 1, None,
+                     ctypes.byref(opt))
+    assert L.fa_status_str(st).decode() == "FA_ERR_WORKSPACE"
 
 
 def test_pack_mask_layout():

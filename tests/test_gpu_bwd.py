@@ -20,8 +20,9 @@ from tests.gpu_helpers import bwd_bound, compare_bwd, host64
 pytestmark = pytest.mark.gpu
 
 
-def _run(B, H, N, M, D, causal, kv_len, seed, device, poison=True, window=None):
+def _run(B, H, N, M, D, causal, kv_len, seed, device, poison=True, window=None, mask=None):
     import torch
+    words = None if mask is None else fa.pack_mask(torch.from_numpy(mask).to(device))
     q, k, v = inputs.qkv_device(seed, B, H, N, M, D, "bf16", device)
     do = inputs.grad_device(seed + 1000, B, H, N, D, "bf16", device)
     kvt = None
@@ -30,23 +31,24 @@ def _run(B, H, N, M, D, causal, kv_len, seed, device, poison=True, window=None):
         if poison:
             inputs.poison_tail(k, v, kv_len)
     scale = 1.0 / math.sqrt(D)
-    o, lse = fa.fwd(q, k, v, scale=scale, causal=causal, kv_len=kvt, window=window)
-    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale=scale, causal=causal, kv_len=kvt, window=window)
+    o, lse = fa.fwd(q, k, v, scale=scale, causal=causal, kv_len=kvt, window=window, mask=words)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale=scale, causal=causal, kv_len=kvt, window=window,
+                        mask=words)
     torch.cuda.synchronize()
     return dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, scale=scale)
 
 
-def _check_head(t, b, h, causal, kvl, what, window=None):
+def _check_head(t, b, h, causal, kvl, what, window=None, allow=None):
     q, k, v, do = (host64(t[n][b, h]) for n in ("q", "k", "v", "do"))
     k = np.where(np.isnan(k), 0.0, k)          # the poisoned tail is never read
     v = np.where(np.isnan(v), 0.0, v)
     O_gpu, L_gpu = host64(t["o"][b, h]), host64(t["lse"][b, h])
-    r = head_backward(q, k, v, do, t["scale"], causal, kvl, window)
+    r = head_backward(q, k, v, do, t["scale"], causal, kvl, window, allow)
     # the exact forward's LSE for the same head
     S = t["scale"] * (q @ k[:kvl].T)
     N = q.shape[0]
     from oracle.attention import visible_mask
-    S = np.where(visible_mask(N, kvl, causal, window), S, -np.inf)
+    S = np.where(visible_mask(N, kvl, causal, window, allow), S, -np.inf)
     with np.errstate(divide="ignore", invalid="ignore"):
         m = S.max(axis=1) if kvl else np.full(N, -np.inf)
         L_ref = np.where(np.isfinite(m), m + np.log(np.sum(np.exp(S - m[:, None]), axis=1)), -np.inf) \
@@ -114,6 +116,63 @@ def test_bwd_window_matches_oracle(case):
     for b in range(B):
         for h in range(H):
             _check_head(t, b, h, causal, kvs[b], f"{case} b{b} h{h}", window=win)
+
+
+MASK_CASES = [
+    # B, H, N, M, D, causal, kv_len, window, mask kind
+    (1, 2, 300, 300, 128, False, None, None, "random"),
+    (2, 2, 260, 517, 64, True, [517, 200], None, "random_per_head"),
+    (1, 2, 700, 700, 128, True, None, None, "documents"),
+    (2, 1, 513, 600, 128, False, [600, 333], (200, 50), "blocks_per_batch"),
+    (1, 1, 200, 90, 128, True, None, None, "random"),            # N > M
+    (1, 1, 1, 700, 128, False, None, None, "random"),            # one query
+]
+
+
+def _mask_of(kind, B, H, N, M):
+    if kind == "random":
+        return inputs.random_mask(111, 1, 1, N, M, 0.5)
+    if kind == "random_per_head":
+        m = inputs.random_mask(112, 1, H, N, M, 0.4)
+        m[0, 0, ::5] = False                                        # rows the mask empties
+        return m
+    if kind == "documents":
+        return inputs.document_mask(113, N, M, 4)
+    if kind == "blocks_per_batch":
+        return inputs.block_mask(114, B, 1, N, M, 64, 64, 0.5)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=lambda c: "B{}H{}N{}M{}D{}{}-{}".format(
+    *c[:5], "c" if c[5] else "", c[8]))
+def test_bwd_mask_matches_oracle(case):
+    """Element masks: the gradients of the masked forward, hidden entries
+    passing none (dQ walks the forward's tile lists; dK/dV applies the bits
+    on every stage)."""
+    import torch
+    from oracle.attention import mask_of_head
+    B, H, N, M, D, causal, kv_len, win, kind = case
+    print(f"[bwd] mask case {case}", flush=True)
+    allowed = _mask_of(kind, B, H, N, M)
+    t = _run(B, H, N, M, D, causal, kv_len, seed=170 + N + M, device=torch.device("cuda:0"),
+             window=win, mask=allowed)
+    kvs = clamp_kv_len(kv_len, B, M)
+    for b in range(B):
+        for h in range(H):
+            _check_head(t, b, h, causal, kvs[b], f"{case} b{b} h{h}", window=win,
+                        allow=mask_of_head(allowed, b, h))
+
+
+def test_bwd_all_ones_mask_matches_unmasked():
+    """A mask that keeps every key gives the unmasked gradients bit for bit
+    (the same tiles, the same arithmetic on the kept entries)."""
+    import torch
+    dev = torch.device("cuda:0")
+    t = _run(1, 2, 600, 600, 128, True, None, seed=91, device=dev)
+    words = fa.pack_mask(torch.ones((1, 1, 600, 600), dtype=torch.bool, device=dev))
+    dq, dk, dv = fa.bwd(t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], causal=True, mask=words)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, t["dq"]) and torch.equal(dk, t["dk"]) and torch.equal(dv, t["dv"])
 
 
 def test_bwd_degenerate_sizes():
