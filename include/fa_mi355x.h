@@ -7,6 +7,8 @@
  *
  *   S[i][j]   = scale * sum_d Q[b][h][i][d] * K[b][h][j][d]
  *   visible   : j < kv_len[b]  and  (not causal  or  j <= i + kv_len[b] - N)
+ *               and, when fa_options asks for them, inside the local window
+ *               and kept by the element mask
  *   O[b][h][i]  = sum_{visible j} softmax_j(S[i][.]) * V[b][h][j]
  *   LSE[b][h][i] = ln sum_{visible j} exp(S[i][j])
  *
