@@ -218,3 +218,16 @@ def test_bwd_workloads_sampled_heads(name, causal, heads):
     t = _run(w.B, w.H, w.N, w.M, w.D, causal, None, seed=w.seed, device=dev)
     for b, h in heads:
         _check_head(t, b, h, causal, w.M, f"{name} b{b} h{h}")
+
+
+def test_bwd_long_workload_documents_mask():
+    """B=2, H=32, N=M=8192, D=128 causal under the bench's 8-document mask
+    (shared by every batch and head), whole heads checked."""
+    import torch
+    w = inputs.WORKLOADS["prefill_long_d128"]
+    dev = torch.device("cuda:0")
+    print("[bwd] long workload, documents mask", flush=True)
+    allowed = inputs.document_mask(7, w.N, w.M, 8)
+    t = _run(w.B, w.H, w.N, w.M, w.D, True, None, seed=w.seed, device=dev, mask=allowed)
+    for b, h in [(0, 3), (1, 30)]:
+        _check_head(t, b, h, True, w.M, f"documents b{b} h{h}", allow=allowed[0, 0])
