@@ -116,13 +116,15 @@ def test_mask_f32(causal):
     compare(host64(o), host64(l), Or, Lr, "f32", f"f32 mask causal={causal}")
 
 
-def test_mask_long_workload_sampled():
-    """B=2, H=32, N=M=8192, D=128 causal with 8 packed documents shared by
-    every batch and head, as the bench runs it."""
+@pytest.mark.parametrize("kind", ["documents8", "random50"])
+def test_mask_long_workload_sampled(kind):
+    """B=2, H=32, N=M=8192, D=128 causal with the bench's masks (8 packed
+    documents; each pair kept with p = 1/2), shared by every batch and head."""
     w = inputs.WORKLOADS["prefill_long_d128"]
-    print("[mask] long workload, documents", flush=True)
+    print(f"[mask] long workload, {kind}", flush=True)
     q, k, v = inputs.qkv_device(w.seed, w.B, w.H, w.N, w.M, w.D, "bf16", torch.device(DEV))
-    allowed = inputs.document_mask(7, w.N, w.M, 8)
+    allowed = (inputs.document_mask(7, w.N, w.M, 8) if kind == "documents8"
+               else inputs.random_mask(11, 1, 1, w.N, w.M, 0.5))
     words = fa.pack_mask(torch.from_numpy(allowed).to(DEV))
     o, l = fa.fwd(q, k, v, causal=True, mask=words)
     torch.cuda.synchronize()
@@ -132,4 +134,4 @@ def test_mask_long_workload_sampled():
                             picks, mask=allowed)
     og = np.stack([host64(o[b, h, i]) for b, h, i in picks])
     lg = np.array([float(l[b, h, i]) for b, h, i in picks])
-    compare(og, lg, Or, Lr, "bf16", "long documents")
+    compare(og, lg, Or, Lr, "bf16", f"long {kind}")
