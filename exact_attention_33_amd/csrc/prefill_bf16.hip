@@ -335,11 +335,16 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
     mbytes = N * p.mask_w * 4;
     mrow = (uint32_t)min(qw0 + lane, N - 1) * (uint32_t)p.mask_w;
   }
-  auto load_mask_item = [&](int w, int t, uint32_t* dst) {
+  // A tile the mask keeps whole (entry e >= 0) never reads its words: its
+  // load still goes out (the end-of-iteration wait counts every load) but
+  // from one address, so it touches one line instead of 64 rows.
+  auto load_mask_item = [&](int w, int e, uint32_t* dst) {
     if constexpr (BITS) {
       int wofs = ws * 128 + w * 64;
       asm volatile("" : "+s"(wofs));
-      buffer_load_lds4(Mg, mbytes, (mrow + 2u * (uint32_t)t + (uint32_t)w) * 4u, (lds_ptr)(dst + wofs));
+      const uint32_t part = (uint32_t)(e >> 31);  // all ones for a partial tile
+      const uint32_t at = ((mrow + 2u * (uint32_t)tile_index(e) + (uint32_t)w) * 4u) & part;
+      buffer_load_lds4(Mg, mbytes, at, (lds_ptr)(dst + wofs));
     }
   };
   auto load_k = [&](int t, __bf16* dst) {
@@ -350,9 +355,9 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
 #pragma unroll
     for (int i = 0; i < VPW; ++i) load_v_item(i, t, dst);
   };
-  auto load_mask = [&](int t, uint32_t* dst) {
+  auto load_mask = [&](int e, uint32_t* dst) {
 #pragma unroll
-    for (int w = 0; w < NMI; ++w) load_mask_item(w, t, dst);
+    for (int w = 0; w < NMI; ++w) load_mask_item(w, e, dst);
   };
   // Load item j of iteration t: K(t+4) blocks into Kdst, then V(t+2) blocks
   // into Vdst, then (mask) the mask words of tile t+3 into Mdst; eK, eV, eM
@@ -360,7 +365,7 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
   auto load_item = [&](int j, int eK, int eV, int eM, __bf16* Kdst, __bf16* Vdst, uint32_t* Mdst) {
     if (j < KPW) load_k_item(j, tile_index(eK), Kdst);
     else if (j < KPW + VPW) load_v_item(j - KPW, tile_index(eV), Vdst);
-    else if (j < NITEM) load_mask_item(j - KPW - VPW, tile_index(eM), Mdst);
+    else if (j < NITEM) load_mask_item(j - KPW - VPW, eM, Mdst);
   };
 
   // ---- Q in registers: B operand of S^T = K Q^T ----
@@ -576,7 +581,8 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
       for (int nb = 0; nb < NKB; ++nb) {
         vis[nb][qb] = lim >= k0 + 32 * nb && (!WINDOW || lo <= k0 + 32 * nb + 31);
         if constexpr (BITS) {
-          const uint32_t w = Ms[ws * 128 + nb * 64 + 32 * qb + ql];
+          // a tile the mask keeps whole has no words in LDS: all ones
+          const uint32_t w = Ms[ws * 128 + nb * 64 + 32 * qb + ql] | ~(uint32_t)(e >> 31);
           vis[nb][qb] = vis[nb][qb] && w != 0u;  // a hint: a false "sees" only costs time
           hid[nb] = ~w >> (4 * hl);
         }
@@ -743,9 +749,9 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
     load_k(tile_index(e2), Kb2);
     load_v(tile_index(e0), Vb0);
     load_v(tile_index(e1), Vb1);
-    load_mask(tile_index(e0), Mb0);
-    load_mask(tile_index(e1), Mb1);
-    load_mask(tile_index(e2), Mb2);
+    load_mask(e0, Mb0);
+    load_mask(e1, Mb1);
+    load_mask(e2, Mb2);
   }
   __syncthreads();
   compute_s(Kb0, sacc);
