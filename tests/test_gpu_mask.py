@@ -135,3 +135,66 @@ def test_mask_long_workload_sampled(kind):
     og = np.stack([host64(o[b, h, i]) for b, h, i in picks])
     lg = np.array([float(l[b, h, i]) for b, h, i in picks])
     compare(og, lg, Or, Lr, "bf16", f"long {kind}")
+
+
+def _expected_lists(allowed, rows_per, cols_per, transpose=False):
+    """Per (mask batch, mask head, tile of `rows_per` rows): the ascending
+    tiles of `cols_per` columns holding a True, bit 31 set where not all are
+    True (rows past the end and columns past the end do not count)."""
+    Bm, Hm, N, M = allowed.shape
+    a = allowed.transpose(0, 1, 3, 2) if transpose else allowed
+    R, C = (M, N) if transpose else (N, M)
+    out = []
+    for bm in range(Bm):
+        for hm in range(Hm):
+            for r0 in range(0, R, rows_per):
+                lst = []
+                for ci, c0 in enumerate(range(0, C, cols_per)):
+                    blk = a[bm, hm, r0:r0 + rows_per, c0:c0 + cols_per]
+                    if blk.any():
+                        lst.append(ci if blk.all() else ci | (1 << 31))
+                out.append(lst)
+    return out
+
+
+def _read_lists(ws_words, n_lists, stride):
+    got = []
+    for i in range(n_lists):
+        cnt = int(ws_words[i * stride])
+        got.append([int(x) & 0xFFFFFFFF for x in ws_words[i * stride + 1:i * stride + 1 + cnt]])
+    return got
+
+
+def test_tile_lists_match_the_mask():
+    """The pre-passes' lists, read back from the workspace: the forward's key
+    tiles per query tile and the backward's query stages per key tile, with
+    the partial-tile flags, equal a NumPy classification of the mask."""
+    B, H, N, M, D = 2, 2, 600, 700, 64
+    allowed = inputs.block_mask(120, B, 1, N, M, 32, 32, 0.5)     # whole, partial and empty tiles
+    allowed[1, 0, :, 640:] = True                                  # a ragged last tile kept whole
+    q, k, v = make(121, B, H, N, M, D, "bf16")
+    words = fa.pack_mask(torch.from_numpy(allowed).to(DEV))
+    ws = torch.zeros(fa.workspace_bytes(B, H, N, M, D, mask_shape=(B, 1)), dtype=torch.uint8, device=DEV)
+    o, l = fa.fwd(q, k, v, mask=words, workspace=ws)
+    torch.cuda.synchronize()
+    stride = (M + 63) // 64 + 1
+    n_qt = (N + 255) // 256
+    got = _read_lists(ws.view(torch.int32).cpu().numpy(), B * n_qt, stride)
+    assert got == _expected_lists(allowed, 256, 64)
+    # the backward's dK/dV stage lists sit after its statistics and dQ lists
+    g = inputs.to_device(inputs.normal_f32(122, (B, H, N, D)), "bf16", DEV)
+    wsb = torch.zeros(fa.bwd_workspace_bytes(B, H, N, M, D, mask_shape=(B, 1)), dtype=torch.uint8,
+                      device=DEV)
+    fa.bwd(q, k, v, o, l, g, mask=words, workspace=wsb)
+    torch.cuda.synchronize()
+    npad = (N + 255) // 256 * 256
+    stats = B * H * npad * 2 * 4
+    off = (stats + 255) // 256 * 256
+    dq_lists = B * n_qt * stride * 4
+    off_st = off + (dq_lists + 255) // 256 * 256
+    words_b = wsb.view(torch.int32).cpu().numpy()
+    assert _read_lists(words_b[off // 4:], B * n_qt, stride) == _expected_lists(allowed, 256, 64)
+    n_kt = (M + 255) // 256
+    stride_s = (N + 63) // 64 + 1
+    assert _read_lists(words_b[off_st // 4:], B * n_kt, stride_s) == \
+        _expected_lists(allowed, 256, 64, transpose=True)
