@@ -126,6 +126,8 @@ MASK_CASES = [
     (2, 1, 513, 600, 128, False, [600, 333], (200, 50), "blocks_per_batch"),
     (1, 1, 200, 90, 128, True, None, None, "random"),            # N > M
     (1, 1, 1, 700, 128, False, None, None, "random"),            # one query
+    (2, 1, 130, 260, 128, True, [260, 0], None, "random"),       # an empty sequence
+    (1, 2, 70, 40, 64, False, None, None, "random_per_head"),    # M below one key tile
 ]
 
 

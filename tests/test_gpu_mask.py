@@ -59,6 +59,8 @@ CASES = [
     (2, 1, 260, 260, 128, True, None, None, "empty_rows"),
     (2, 2, 1, 3000, 128, False, [3000, 1111], None, "random"),      # single queries
     (1, 1, 150, 90, 128, True, None, None, "random"),                # N > M
+    (2, 1, 130, 260, 128, True, [260, 0], None, "random"),           # an empty sequence
+    (1, 2, 70, 40, 64, False, None, None, "random_per_head"),        # M below one key tile
 ]
 
 
