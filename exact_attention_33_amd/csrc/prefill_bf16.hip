@@ -483,20 +483,36 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
   };
   // Move row qb's reference to mx (its new row max, base 2): returns the
   // factor e^(m_old - m_new) for everything accumulated so far.
-  auto move_ref = [&](int qb, float mx) -> float {
-    const float m_new = fmaxf(m_run[qb], mx);
+  // Only the rows that ask for it move (trig); the others keep their
+  // reference (factor 1).  A row that moves from -inf has accumulated
+  // nothing (factor 0 on zeros), so the output accumulator is rescaled only
+  // when some row with a reference moves it up (rescale_acc).  Both half-waves
+  // hold every row and must take the same decision: trig is combined over
+  // the pair first.
+  auto row_any = [&](bool x) -> bool {
+    const uint32_t v = x ? 1u : 0u;
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (r[0] | r[1]) != 0u;
+  };
+  auto move_ref = [&](int qb, float mx, bool trig, bool& moved_up) -> float {
+    const float m_new = trig ? fmaxf(m_run[qb], mx) : m_run[qb];
     const float a = m_run[qb] == -INFINITY ? 0.f : fast_exp2(m_run[qb] - m_new);  // nothing accumulated yet
+    moved_up = (m_run[qb] != -INFINITY) & (m_new > m_run[qb]);
     l_run[qb] *= a;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      // read inside the branch, in place: no copy of the accumulator
-      // outside it
-      asm volatile("" : "+a"(oacc[db][qb]));
-      oacc[db][qb] *= a;
-    }
     m_run[qb] = m_new;
     m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
     return a;
+  };
+  auto rescale_acc = [&](const float (&a)[NQB]) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        // read inside the branch, in place: no copy of the accumulator
+        // outside it
+        asm volatile("" : "+a"(oacc[db][qb]));
+        oacc[db][qb] *= a[qb];
+      }
   };
   auto sm_check1 = [&](f32x16 (&s)[NKB][NQB]) __attribute__((always_inline)) {
     bool over = false;
@@ -504,14 +520,21 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
     for (int qb = 0; qb < NQB; ++qb)
       over |= (ps0[qb][0] + ps0[qb][1] > kSumLimit) | ((m_run[qb] == -INFINITY) & vis[0][qb]);
     if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform, rare
+      float a[NQB];
+      bool up = false;
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
+        const bool trig = row_any(ps0[qb][0] + ps0[qb][1] > kSumLimit) |
+                          ((m_run[qb] == -INFINITY) & vis[0][qb]);
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[0][qb][r], s[0][qb][r + 1]);
-        move_ref(qb, swap_halves_max(mx) * c);  // -inf stays -inf (c > 0)
+        bool moved_up;
+        a[qb] = move_ref(qb, swap_halves_max(mx) * c, trig, moved_up);  // -inf stays -inf (c > 0)
+        up |= moved_up;
         ps0[qb][0] = ps0[qb][1] = 0.f;
       }
+      if (__builtin_amdgcn_ballot_w64(up) != 0) rescale_acc(a);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -527,20 +550,27 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
       over |= (ps0[qb][0] + ps0[qb][1] + ps1[qb][0] + ps1[qb][1] > kSumLimit) |
               ((m_run[qb] == -INFINITY) & vis[1][qb]);
     if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform, rarer still
+      float a[NQB];
+      bool up = false;
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
+        const bool trig = row_any(ps0[qb][0] + ps0[qb][1] + ps1[qb][0] + ps1[qb][1] > kSumLimit) |
+                          ((m_run[qb] == -INFINITY) & vis[1][qb]);
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[1][qb][r], s[1][qb][r + 1]);
-        const float a = move_ref(qb, swap_halves_max(mx) * c);
-        ps0[qb][0] *= a;
-        ps0[qb][1] *= a;
+        bool moved_up;
+        a[qb] = move_ref(qb, swap_halves_max(mx) * c, trig, moved_up);
+        up |= moved_up;
+        ps0[qb][0] *= a[qb];
+        ps0[qb][1] *= a[qb];
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pacc[qb][t2][e] = (__bf16)((float)pacc[qb][t2][e] * a);
+          for (int e = 0; e < 8; ++e) pacc[qb][t2][e] = (__bf16)((float)pacc[qb][t2][e] * a[qb]);
         ps1[qb][0] = ps1[qb][1] = 0.f;
       }
+      if (__builtin_amdgcn_ballot_w64(up) != 0) rescale_acc(a);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
