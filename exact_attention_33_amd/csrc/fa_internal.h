@@ -71,6 +71,8 @@ void launch_mask_tiles(const uint32_t* mask, int N, int M, int mask_w, int mask_
 constexpr int kPrefillBlockQ = 256;   // 4 waves x 64 queries
 constexpr int kPrefillBlockK = 64;    // keys per K/V tile
 constexpr int kPrefillThreads = 256;
+// Persistent causal prefill: at most one workgroup per CU of an MI355X.
+constexpr int kPrefillPersistGrid = 256;
 
 // Element mask on the prefill path: the workspace holds, per (mask batch,
 // mask head, 256-query tile), a list of kMaskListStride(M) int32: the count,

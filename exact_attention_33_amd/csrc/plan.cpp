@@ -153,6 +153,10 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
       plan->threads = kPrefillThreads;
       plan->lds_bytes = prefill_lds_bytes(s.D);
       plan->grid = ceil_div(s.N, kPrefillBlockQ) * bh;
+      // causal without a window or a mask: persistent workgroups, one per CU
+      // (a multiple of the 8 XCDs), each walking several query tiles
+      if (causal && !window && !mask)
+        plan->grid = std::min<int64_t>((plan->grid + 7) / 8 * 8, kPrefillPersistGrid);
       if (mask) {
         // the kernel holds one query tile's list of key tiles in LDS, and
         // addresses one (mask batch, mask head) of the mask with 32-bit byte

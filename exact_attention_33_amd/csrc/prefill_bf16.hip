@@ -215,612 +215,642 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
   __shared__ __attribute__((aligned(256))) uint32_t Mb1[BITS ? NW * 128 : 1];
   __shared__ __attribute__((aligned(256))) uint32_t Mb2[BITS ? NW * 128 : 1];
 
-  const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
-  int qt = (int)(logical % n_qtiles);
-  const int64_t bh = logical / n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest query tiles first
-  const int b = (int)(bh / p.H);
-  const int N = p.N, M = p.M;
-  const int tid = threadIdx.x;
-  const int lane = tid % 64, hl = lane / 32, ql = lane % 32;
-  const int ws = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index (uniform)
-  // uniform in fact; readfirstlane lets the compiler keep it (and every tile
-  // descriptor built from it) in scalar registers
-  const int kvl = __builtin_amdgcn_readfirstlane(clamp_kv(p.kv_len, b, M));
-  const int q0 = qt * BQ;
-  const int qw0 = q0 + QW * ws;  // first query of this wave
-  const int off = kvl - N;       // key j visible to query i iff j < kvl and (!causal or j <= i + off)
-  // Local window: query i sees keys i + off - wl .. i + off + wr only; causal
-  // caps wr at 0.  (Clamped so that no bound overflows.)
-  constexpr bool UPPER = CAUSAL || WINDOW;   // rows have a last key before kvl - 1
-  const int wl = WINDOW ? min(p.wl, N + kvl) : 0;
-  const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
-  const int q_last = min(q0 + BQ, N) - 1;
-  const int kv_end = UPPER ? min(kvl, q_last + off + wr + 1) : kvl;
-  // Window: tiles before the first query's first key are never visited.
-  // Without a mask the K/V descriptors start at that tile, t0, and the loop
-  // counts tiles from there; with a mask the loop walks the listed tiles in
-  // [tw, t_end) and tiles are addressed from 0.
-  const int tw = WINDOW ? max(0, q0 + off - wl) / BK : 0;
-  const int t_end = kv_end > tw * BK ? (kv_end + BK - 1) / BK : tw;
-  const int t0 = BITS ? 0 : tw;
-  int n_tiles = t_end - tw;
-  int lo = 0;  // with a mask: list position of the first tile visited
-  if constexpr (BITS) {
-    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
-    const int32_t* L = tile_lists + ((int64_t)(bm * p.mask_h + hm) * n_qtiles + qt) * list_stride;
-    const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
-    for (int i = tid; i < cnt; i += kPrefillThreads) tlist[i] = L[1 + i];
-    __syncthreads();
-    // the list ascends: count the entries below tw and below t_end
-    int below_lo = 0, below_hi = 0;
-    for (int i0 = 0; i0 < cnt; i0 += 64) {
-      const int e = i0 + lane < cnt ? (tlist[i0 + lane] & 0x7FFFFFFF) : 0x7FFFFFFF;
-      below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < tw));
-      below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t_end));
+  // Causal without a window or a mask: persistent workgroups, one per CU
+  // (the planner's grid), each walking the work items of its XCD.  Round k
+  // takes item k W + u (even k) or k W + W - 1 - u (odd k), W workgroups
+  // per XCD and u this workgroup's place among them: the items of one
+  // (batch, head) run together on one XCD as before, and since a causal
+  // head's query tiles come heaviest first, a workgroup's heavy and light
+  // tiles alternate (measured on MI355X: -3% at N = 8192, -14% at N = 4096
+  // against one workgroup per item, results identical; with uneven work
+  // per item -- windows, masks -- the dispatcher's own balancing wins).
+  constexpr bool PERSIST = CAUSAL && !WINDOW && !BITS;
+  const int64_t n_items = (int64_t)n_qtiles * p.B * p.H;
+  const int xcd = blockIdx.x % kNumXcd, u = blockIdx.x / kNumXcd, W = gridDim.x / kNumXcd;
+  const int64_t qx = n_items / kNumXcd, rx = n_items % kNumXcd;
+  const int64_t x_start = xcd * qx + (xcd < rx ? xcd : rx), x_count = qx + (xcd < rx ? 1 : 0);
+  for (int64_t k = 0;; ++k) {
+    int64_t logical;
+    if constexpr (PERSIST) {
+      const int64_t within = k * W + ((k & 1) ? W - 1 - u : u);
+      if (within >= x_count) break;
+      logical = x_start + within;
+      // the previous item's loads into LDS (some past its last tile) have
+      // landed, and every wave is done reading
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    } else {
+      if (k > 0) break;
+      logical = xcd_logical(blockIdx.x, gridDim.x);
     }
-    lo = __builtin_amdgcn_readfirstlane(below_lo);
-    n_tiles = __builtin_amdgcn_readfirstlane(below_hi) - lo;
-    __syncthreads();  // every wave has read the list
-    // after the last visited tile: one past kv_len, whose loads read zeros
-    // and whose keys are all masked (lo + n_tiles <= cnt < kMaskMaxTiles)
-    if (tid == 0) tlist[lo + n_tiles] = (kvl + BK - 1) / BK;
-    __syncthreads();
-  }
-  // Entry of the t-th visited tile: its index (relative to t0), with bit 31
-  // set when the mask does not keep it whole.  Without a mask, t itself.
-  auto tile_entry = [&](int t) -> int {
-    if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + min(t, n_tiles)]);
-    else return t;
-  };
-  auto tile_index = [&](int e) -> int { return BITS ? (e & 0x7FFFFFFF) : e; };
-
-  const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
-  const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D + (size_t)t0 * BK * D;
-  const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D + (size_t)t0 * BK * D;
-
-  // ---- tile loads ----
-  // Slot s of a padded tile holds row s / CH, chunk s % CH; slots on the
-  // padding (chunk >= CPR) load chunk 0 of that row (valid data, never read).
-  // Wave ws loads blocks ws, ws + NW, ... of each tile.  The per-lane byte
-  // offsets of a wave's slots within a tile (< 64 KB) are fixed, so they are
-  // computed once and kept two to a register.  Loads are buffer loads into
-  // LDS against one descriptor per (batch, head) that ends at kv_len: rows
-  // past it (last tile) and whole tiles past it read as zeros -- finite data
-  // whose weights are 0 -- with no clamping arithmetic, and the descriptors
-  // stay in 8 scalar registers for the whole kernel.  (Buffer rather than
-  // global loads also keep the compiler's LDS wait counting exact: it treats
-  // a global load into LDS like a flat access and then waits for every LDS
-  // read.)
-  constexpr int NMI = BITS ? 2 : 0;  // mask load items (one per word of a row's tile)
-  constexpr int NITEM = KPW + VPW + NMI;  // load items per wave per iteration
-  constexpr int ROWB = D * 2;       // bytes per global row
-  static_assert((NW * KPW * 64 / KCH + 1) * ROWB <= 65536 && (NW * VPW * 64 / VCH + 1) * ROWB <= 65536,
-                "slot offsets fit 16 bits");
-  auto slot_off = [&](int blk, int ch) -> uint32_t {
-    const int slot = blk * 64 + lane, r = slot / ch, cc = slot % ch;
-    return (uint32_t)(r * ROWB + (cc < CPR ? cc * 16 : 0));
-  };
-  uint32_t koff[(KPW + 1) / 2], voff[(VPW + 1) / 2];
-#pragma unroll
-  for (int i = 0; i < KPW; i += 2)
-    koff[i / 2] = slot_off(ws + i * NW, KCH) | (i + 1 < KPW ? slot_off(ws + (i + 1) * NW, KCH) << 16 : 0u);
-#pragma unroll
-  for (int i = 0; i < VPW; i += 2)
-    voff[i / 2] = slot_off(ws + i * NW, VCH) | (i + 1 < VPW ? slot_off(ws + (i + 1) * NW, VCH) << 16 : 0u);
-  // K and V bytes this (batch, head) may read; the planner keeps M * D * 2
-  // below 2^31, so every offset below fits 32 bits.
-  const int nrec = (kvl - t0 * BK) * ROWB;
-  // Block i of this wave: its slots of tile t of src into dst.  The wave's
-  // block offset goes through an empty asm so that the compiler forms each
-  // LDS address next to its load instead of keeping all of them (three
-  // buffers x NITEM blocks) in scalar registers.
-  auto load_block = [&](const __bf16* src, int t, __bf16* dst, uint32_t packed, int i) {
-    asm volatile("" : "+v"(packed));  // keep the unpacking next to its use
-    const uint32_t u = (i % 2 ? packed >> 16 : packed & 0xFFFFu) + (uint32_t)t * (BK * ROWB);
-    int wofs = ws * 512;
-    asm volatile("" : "+s"(wofs));
-    buffer_load_lds16(src, nrec, u, (lds_ptr)(dst + wofs + i * NW * 512));
-  };
-  auto load_k_item = [&](int i, int t, __bf16* dst) { load_block(Kg, t, dst, koff[i / 2], i); };
-  auto load_v_item = [&](int i, int t, __bf16* dst) { load_block(Vg, t, dst, voff[i / 2], i); };
-  // Mask word w of key tile t for the wave's 64 query rows (lane = row; rows
-  // past N read row N - 1): one 4-byte buffer load per lane into LDS.
-  const uint32_t* Mg = nullptr;
-  int mbytes = 0;
-  uint32_t mrow = 0;
-  if constexpr (BITS) {
-    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
-    Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
-    mbytes = N * p.mask_w * 4;
-    mrow = (uint32_t)min(qw0 + lane, N - 1) * (uint32_t)p.mask_w;
-  }
-  // A tile the mask keeps whole (entry e >= 0) never reads its words: its
-  // load still goes out (the end-of-iteration wait counts every load) but
-  // from one address, so it touches one line instead of 64 rows.
-  auto load_mask_item = [&](int w, int e, uint32_t* dst) {
+  {
+    int qt = (int)(logical % n_qtiles);
+    const int64_t bh = logical / n_qtiles;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest query tiles first
+    const int b = (int)(bh / p.H);
+    const int N = p.N, M = p.M;
+    const int tid = threadIdx.x;
+    const int lane = tid % 64, hl = lane / 32, ql = lane % 32;
+    const int ws = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index (uniform)
+    // uniform in fact; readfirstlane lets the compiler keep it (and every tile
+    // descriptor built from it) in scalar registers
+    const int kvl = __builtin_amdgcn_readfirstlane(clamp_kv(p.kv_len, b, M));
+    const int q0 = qt * BQ;
+    const int qw0 = q0 + QW * ws;  // first query of this wave
+    const int off = kvl - N;       // key j visible to query i iff j < kvl and (!causal or j <= i + off)
+    // Local window: query i sees keys i + off - wl .. i + off + wr only; causal
+    // caps wr at 0.  (Clamped so that no bound overflows.)
+    constexpr bool UPPER = CAUSAL || WINDOW;   // rows have a last key before kvl - 1
+    const int wl = WINDOW ? min(p.wl, N + kvl) : 0;
+    const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
+    const int q_last = min(q0 + BQ, N) - 1;
+    const int kv_end = UPPER ? min(kvl, q_last + off + wr + 1) : kvl;
+    // Window: tiles before the first query's first key are never visited.
+    // Without a mask the K/V descriptors start at that tile, t0, and the loop
+    // counts tiles from there; with a mask the loop walks the listed tiles in
+    // [tw, t_end) and tiles are addressed from 0.
+    const int tw = WINDOW ? max(0, q0 + off - wl) / BK : 0;
+    const int t_end = kv_end > tw * BK ? (kv_end + BK - 1) / BK : tw;
+    const int t0 = BITS ? 0 : tw;
+    int n_tiles = t_end - tw;
+    int lo = 0;  // with a mask: list position of the first tile visited
     if constexpr (BITS) {
-      int wofs = ws * 128 + w * 64;
+      const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+      const int32_t* L = tile_lists + ((int64_t)(bm * p.mask_h + hm) * n_qtiles + qt) * list_stride;
+      const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
+      for (int i = tid; i < cnt; i += kPrefillThreads) tlist[i] = L[1 + i];
+      __syncthreads();
+      // the list ascends: count the entries below tw and below t_end
+      int below_lo = 0, below_hi = 0;
+      for (int i0 = 0; i0 < cnt; i0 += 64) {
+        const int e = i0 + lane < cnt ? (tlist[i0 + lane] & 0x7FFFFFFF) : 0x7FFFFFFF;
+        below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < tw));
+        below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t_end));
+      }
+      lo = __builtin_amdgcn_readfirstlane(below_lo);
+      n_tiles = __builtin_amdgcn_readfirstlane(below_hi) - lo;
+      __syncthreads();  // every wave has read the list
+      // after the last visited tile: one past kv_len, whose loads read zeros
+      // and whose keys are all masked (lo + n_tiles <= cnt < kMaskMaxTiles)
+      if (tid == 0) tlist[lo + n_tiles] = (kvl + BK - 1) / BK;
+      __syncthreads();
+    }
+    // Entry of the t-th visited tile: its index (relative to t0), with bit 31
+    // set when the mask does not keep it whole.  Without a mask, t itself.
+    auto tile_entry = [&](int t) -> int {
+      if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + min(t, n_tiles)]);
+      else return t;
+    };
+    auto tile_index = [&](int e) -> int { return BITS ? (e & 0x7FFFFFFF) : e; };
+
+    const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
+    const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D + (size_t)t0 * BK * D;
+    const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D + (size_t)t0 * BK * D;
+
+    // ---- tile loads ----
+    // Slot s of a padded tile holds row s / CH, chunk s % CH; slots on the
+    // padding (chunk >= CPR) load chunk 0 of that row (valid data, never read).
+    // Wave ws loads blocks ws, ws + NW, ... of each tile.  The per-lane byte
+    // offsets of a wave's slots within a tile (< 64 KB) are fixed, so they are
+    // computed once and kept two to a register.  Loads are buffer loads into
+    // LDS against one descriptor per (batch, head) that ends at kv_len: rows
+    // past it (last tile) and whole tiles past it read as zeros -- finite data
+    // whose weights are 0 -- with no clamping arithmetic, and the descriptors
+    // stay in 8 scalar registers for the whole kernel.  (Buffer rather than
+    // global loads also keep the compiler's LDS wait counting exact: it treats
+    // a global load into LDS like a flat access and then waits for every LDS
+    // read.)
+    constexpr int NMI = BITS ? 2 : 0;  // mask load items (one per word of a row's tile)
+    constexpr int NITEM = KPW + VPW + NMI;  // load items per wave per iteration
+    constexpr int ROWB = D * 2;       // bytes per global row
+    static_assert((NW * KPW * 64 / KCH + 1) * ROWB <= 65536 && (NW * VPW * 64 / VCH + 1) * ROWB <= 65536,
+                  "slot offsets fit 16 bits");
+    auto slot_off = [&](int blk, int ch) -> uint32_t {
+      const int slot = blk * 64 + lane, r = slot / ch, cc = slot % ch;
+      return (uint32_t)(r * ROWB + (cc < CPR ? cc * 16 : 0));
+    };
+    uint32_t koff[(KPW + 1) / 2], voff[(VPW + 1) / 2];
+  #pragma unroll
+    for (int i = 0; i < KPW; i += 2)
+      koff[i / 2] = slot_off(ws + i * NW, KCH) | (i + 1 < KPW ? slot_off(ws + (i + 1) * NW, KCH) << 16 : 0u);
+  #pragma unroll
+    for (int i = 0; i < VPW; i += 2)
+      voff[i / 2] = slot_off(ws + i * NW, VCH) | (i + 1 < VPW ? slot_off(ws + (i + 1) * NW, VCH) << 16 : 0u);
+    // K and V bytes this (batch, head) may read; the planner keeps M * D * 2
+    // below 2^31, so every offset below fits 32 bits.
+    const int nrec = (kvl - t0 * BK) * ROWB;
+    // Block i of this wave: its slots of tile t of src into dst.  The wave's
+    // block offset goes through an empty asm so that the compiler forms each
+    // LDS address next to its load instead of keeping all of them (three
+    // buffers x NITEM blocks) in scalar registers.
+    auto load_block = [&](const __bf16* src, int t, __bf16* dst, uint32_t packed, int i) {
+      asm volatile("" : "+v"(packed));  // keep the unpacking next to its use
+      const uint32_t u = (i % 2 ? packed >> 16 : packed & 0xFFFFu) + (uint32_t)t * (BK * ROWB);
+      int wofs = ws * 512;
       asm volatile("" : "+s"(wofs));
-      const uint32_t part = (uint32_t)(e >> 31);  // all ones for a partial tile
-      const uint32_t at = ((mrow + 2u * (uint32_t)tile_index(e) + (uint32_t)w) * 4u) & part;
-      buffer_load_lds4(Mg, mbytes, at, (lds_ptr)(dst + wofs));
+      buffer_load_lds16(src, nrec, u, (lds_ptr)(dst + wofs + i * NW * 512));
+    };
+    auto load_k_item = [&](int i, int t, __bf16* dst) { load_block(Kg, t, dst, koff[i / 2], i); };
+    auto load_v_item = [&](int i, int t, __bf16* dst) { load_block(Vg, t, dst, voff[i / 2], i); };
+    // Mask word w of key tile t for the wave's 64 query rows (lane = row; rows
+    // past N read row N - 1): one 4-byte buffer load per lane into LDS.
+    const uint32_t* Mg = nullptr;
+    int mbytes = 0;
+    uint32_t mrow = 0;
+    if constexpr (BITS) {
+      const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+      Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
+      mbytes = N * p.mask_w * 4;
+      mrow = (uint32_t)min(qw0 + lane, N - 1) * (uint32_t)p.mask_w;
     }
-  };
-  auto load_k = [&](int t, __bf16* dst) {
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) load_k_item(i, t, dst);
-  };
-  auto load_v = [&](int t, __bf16* dst) {
-#pragma unroll
-    for (int i = 0; i < VPW; ++i) load_v_item(i, t, dst);
-  };
-  auto load_mask = [&](int e, uint32_t* dst) {
-#pragma unroll
-    for (int w = 0; w < NMI; ++w) load_mask_item(w, e, dst);
-  };
-  // Load item j of iteration t: K(t+4) blocks into Kdst, then V(t+2) blocks
-  // into Vdst, then (mask) the mask words of tile t+3 into Mdst; eK, eV, eM
-  // are those tiles' entries (tiles past the last read as zeros).
-  auto load_item = [&](int j, int eK, int eV, int eM, __bf16* Kdst, __bf16* Vdst, uint32_t* Mdst) {
-    if (j < KPW) load_k_item(j, tile_index(eK), Kdst);
-    else if (j < KPW + VPW) load_v_item(j - KPW, tile_index(eV), Vdst);
-    else if (j < NITEM) load_mask_item(j - KPW - VPW, eM, Mdst);
-  };
+    // A tile the mask keeps whole (entry e >= 0) never reads its words: its
+    // load still goes out (the end-of-iteration wait counts every load) but
+    // from one address, so it touches one line instead of 64 rows.
+    auto load_mask_item = [&](int w, int e, uint32_t* dst) {
+      if constexpr (BITS) {
+        int wofs = ws * 128 + w * 64;
+        asm volatile("" : "+s"(wofs));
+        const uint32_t part = (uint32_t)(e >> 31);  // all ones for a partial tile
+        const uint32_t at = ((mrow + 2u * (uint32_t)tile_index(e) + (uint32_t)w) * 4u) & part;
+        buffer_load_lds4(Mg, mbytes, at, (lds_ptr)(dst + wofs));
+      }
+    };
+    auto load_k = [&](int t, __bf16* dst) {
+  #pragma unroll
+      for (int i = 0; i < KPW; ++i) load_k_item(i, t, dst);
+    };
+    auto load_v = [&](int t, __bf16* dst) {
+  #pragma unroll
+      for (int i = 0; i < VPW; ++i) load_v_item(i, t, dst);
+    };
+    auto load_mask = [&](int e, uint32_t* dst) {
+  #pragma unroll
+      for (int w = 0; w < NMI; ++w) load_mask_item(w, e, dst);
+    };
+    // Load item j of iteration t: K(t+4) blocks into Kdst, then V(t+2) blocks
+    // into Vdst, then (mask) the mask words of tile t+3 into Mdst; eK, eV, eM
+    // are those tiles' entries (tiles past the last read as zeros).
+    auto load_item = [&](int j, int eK, int eV, int eM, __bf16* Kdst, __bf16* Vdst, uint32_t* Mdst) {
+      if (j < KPW) load_k_item(j, tile_index(eK), Kdst);
+      else if (j < KPW + VPW) load_v_item(j - KPW, tile_index(eV), Vdst);
+      else if (j < NITEM) load_mask_item(j - KPW - VPW, eM, Mdst);
+    };
 
-  // ---- Q in registers: B operand of S^T = K Q^T ----
-  // Fragment (qb, kb): lane (h, c) holds Q[qw0 + 32 qb + c][16 kb + 8 h .. + 8].
-  // Rows past N hold a copy of row N - 1 (finite, never written out).
-  bf16x8 qf[NQB][DK];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int row = min(qw0 + 32 * qb + ql, N - 1);
-#pragma unroll
-    for (int kb = 0; kb < DK; ++kb) qf[qb][kb] = *(const bf16x8*)(Qg + (size_t)row * D + kb * 16 + hl * 8);
-  }
-
-  // Per-lane base offsets (elements) of the operand reads.
-  const int kbase = ql * KROW + hl * 8;   // + (32 nb) KROW + 16 kb
-  const int vbase = (4 * hl + (lane % 16) / 4) * VROW + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
-                                          // + (32 nb + 16 t2) VROW + 32 db, + 8 VROW for the upper 4 keys
-
-  // K fragment i (kb-major): rows 32 nb .. + 32, columns 16 kb .. + 16.
-  auto fetch_k = [&](const __bf16* Ks, int i) -> bf16x8 {
-    const int kb = i / NKB, nb = i % NKB;
-    return *(const bf16x8*)(Ks + kbase + nb * 32 * KROW + kb * 16);
-  };
-  // V^T fragment i = (nb, t2, db), db fastest.  B operand slot 8*hl + e of
-  // 16-key block (nb, t2) is key 32 nb + 16 t2 + 8 (e / 4) + 4 hl + e % 4 (the
-  // order in which the score layout hands the weights over); the A operand
-  // for the same slots comes from two transposing reads of 4 consecutive keys
-  // each: within a 16-lane group, lane j reads row kbase + j / 4 at column
-  // dsrc + 4 (j % 4), and lane i receives the 4 keys at column dsrc + i.
-  auto fetch_v = [&](const __bf16* Vs, int i) -> bf16x8 {
-    const int nb = i / (2 * DB), t2 = (i / DB) % 2, db = i % DB;
-    const __bf16* a = Vs + vbase + (nb * 32 + t2 * 16) * VROW + db * 32;
-    const s16x4 lo = lds_read_tr16(a);
-    const s16x4 hi = lds_read_tr16(a + 8 * VROW);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-
-  f32x16 oacc[DB][NQB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = f32x16{};
-  f32x16 sacc[NKB][NQB];  // score tile: S(t+1), then S(t+2), during iteration t
-  bf16x8 pacc[NQB][NP];   // weight tile: P(t), then P(t+1), during iteration t
-  float m_run[NQB], l_run[NQB];  // reference max (base 2), this lane's part of the sum
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-  }
-  // A scale of 0 would turn a masked -inf score into NaN (-inf * 0); a floor
-  // of 1e-30 changes the weights of finite scores by less than 1e-20.
-  const float c = fmaxf(p.scale * kLog2e, 1e-30f);
-
-  // Tiles that cross the diagonal or the kv_len boundary -- and tiles past
-  // the workgroup's last one, whose LDS holds stale data -- are masked
-  // element by element; every other tile is fully visible to the wave.
-  auto need_mask = [&](int e) {
-    const int k0 = (tile_index(e) + t0) * BK;
-    return (BITS && e < 0) || (k0 + BK > kvl) || (UPPER && k0 + BK - 1 > qw0 + off + wr) ||
-           (WINDOW && k0 < qw0 + QW - 1 + off - wl);
-  };
-
-  // ---- softmax of one tile, in small units that the pipeline spreads out ----
-  // The weights of a tile are formed against the current reference m with no
-  // row max at all: the pages subtract the max only to keep the exponentials
-  // finite, and any reference that keeps every weight at most 2^20 (sums of
-  // a million keys stay far inside float32) gives the same l, O and L.  A
-  // weight above that shows in the lane's sum of the tile's weights, so two
-  // cheap checks replace the max:
-  //   EM units (key block 0): weight, sum and bf16 weight of 2 scores;
-  //   check 1 (after the EM units and the P V products of the previous tile,
-  //     block-0 scores intact): a lane's block-0 sum above 2^20, or a row
-  //     with no reference yet (m = -inf) that sees a key of block 0, moves
-  //     the reference up to block 0's row max (rare): l and the output
-  //     accumulator are rescaled and key block 0 is computed again;
-  //   EX units (key block 1): as EM;
-  //   check 2 (after the EX units, block-1 scores intact): the same for the
-  //     whole tile's sum and block 1 (rarer still): l, the output
-  //     accumulator and block 0's weights and sum are rescaled and key block
-  //     1 is computed again.
-  // Once a row has a reference, its l is at least 1 (the key that set it
-  // weighs exactly 1), so weights that underflow are negligible.  Each score
-  // is read from the accumulator once and consumed at once.
-  constexpr int NU_EM = NQB * 8, NU_EX = NQB * 8;
-  constexpr float kSumLimit = 1048576.0f;  // 2^20
-  float m_use[NQB], ps0[NQB][2], ps1[NQB][2];  // reference in use; block 0 and block 1 sums
-  bool vis[NKB][NQB];  // the row sees a key of key block nb
-  auto sm_begin = [&]() {
-#pragma unroll
+    // ---- Q in registers: B operand of S^T = K Q^T ----
+    // Fragment (qb, kb): lane (h, c) holds Q[qw0 + 32 qb + c][16 kb + 8 h .. + 8].
+    // Rows past N hold a copy of row N - 1 (finite, never written out).
+    bf16x8 qf[NQB][DK];
+  #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      ps0[qb][0] = ps0[qb][1] = ps1[qb][0] = ps1[qb][1] = 0.f;
-      m_use[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+      const int row = min(qw0 + 32 * qb + ql, N - 1);
+  #pragma unroll
+      for (int kb = 0; kb < DK; ++kb) qf[qb][kb] = *(const bf16x8*)(Qg + (size_t)row * D + kb * 16 + hl * 8);
     }
-  };
-  // weights of 2 scores (pair `pair` of 16-key half t2 of key block nb)
-  auto exp_pair = [&](f32x16 (&s)[NKB][NQB], int nb, int qb, int t2, int pair) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = 2 * pair + h, r = (2 * t2 + e / 4) * 4 + (e % 4);
-      const float pv = fast_exp2(fmaf(s[nb][qb][r], c, -m_use[qb]));
-      (nb == 0 ? ps0 : ps1)[qb][h] += pv;
-      pacc[qb][nb * 2 + t2][e] = (__bf16)pv;
-    }
-  };
-  // EM unit u: t2-major, so that the units of the first 16-key half come
-  // first (the P V products release that half of the weight tile first)
-  auto unit_em = [&](f32x16 (&s)[NKB][NQB], auto uc) {
-    constexpr int u = decltype(uc)::value, t2 = u / 8, qb = (u / 4) % 2, pair = u % 4;
-    exp_pair(s, 0, qb, t2, pair);
-  };
-  auto unit_ex = [&](f32x16 (&s)[NKB][NQB], auto uc) {
-    constexpr int u = decltype(uc)::value, qb = u / 8, t2 = (u / 4) % 2, pair = u % 4;
-    exp_pair(s, 1, qb, t2, pair);
-  };
-  // Move row qb's reference to mx (its new row max, base 2): returns the
-  // factor e^(m_old - m_new) for everything accumulated so far.
-  // Only the rows that ask for it move (trig); the others keep their
-  // reference (factor 1).  A row that moves from -inf has accumulated
-  // nothing (factor 0 on zeros), so the output accumulator is rescaled only
-  // when some row with a reference moves it up (rescale_acc).  Both half-waves
-  // hold every row and must take the same decision: trig is combined over
-  // the pair first.
-  auto row_any = [&](bool x) -> bool {
-    const uint32_t v = x ? 1u : 0u;
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return (r[0] | r[1]) != 0u;
-  };
-  auto move_ref = [&](int qb, float mx, bool trig, bool& moved_up) -> float {
-    const float m_new = trig ? fmaxf(m_run[qb], mx) : m_run[qb];
-    const float a = m_run[qb] == -INFINITY ? 0.f : fast_exp2(m_run[qb] - m_new);  // nothing accumulated yet
-    moved_up = (m_run[qb] != -INFINITY) & (m_new > m_run[qb]);
-    l_run[qb] *= a;
-    m_run[qb] = m_new;
-    m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
-    return a;
-  };
-  auto rescale_acc = [&](const float (&a)[NQB]) {
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        // read inside the branch, in place: no copy of the accumulator
-        // outside it
-        asm volatile("" : "+a"(oacc[db][qb]));
-        oacc[db][qb] *= a[qb];
-      }
-  };
-  auto sm_check1 = [&](f32x16 (&s)[NKB][NQB]) __attribute__((always_inline)) {
-    bool over = false;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-      over |= (ps0[qb][0] + ps0[qb][1] > kSumLimit) | ((m_run[qb] == -INFINITY) & vis[0][qb]);
-    if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform, rare
-      float a[NQB];
-      bool up = false;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const bool trig = row_any(ps0[qb][0] + ps0[qb][1] > kSumLimit) |
-                          ((m_run[qb] == -INFINITY) & vis[0][qb]);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[0][qb][r], s[0][qb][r + 1]);
-        bool moved_up;
-        a[qb] = move_ref(qb, swap_halves_max(mx) * c, trig, moved_up);  // -inf stays -inf (c > 0)
-        up |= moved_up;
-        ps0[qb][0] = ps0[qb][1] = 0.f;
-      }
-      if (__builtin_amdgcn_ballot_w64(up) != 0) rescale_acc(a);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int pair = 0; pair < 4; ++pair) exp_pair(s, 0, qb, t2, pair);
-    }
-  };
-  auto sm_check2 = [&](f32x16 (&s)[NKB][NQB]) __attribute__((always_inline)) {
-    bool over = false;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-      over |= (ps0[qb][0] + ps0[qb][1] + ps1[qb][0] + ps1[qb][1] > kSumLimit) |
-              ((m_run[qb] == -INFINITY) & vis[1][qb]);
-    if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform, rarer still
-      float a[NQB];
-      bool up = false;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const bool trig = row_any(ps0[qb][0] + ps0[qb][1] + ps1[qb][0] + ps1[qb][1] > kSumLimit) |
-                          ((m_run[qb] == -INFINITY) & vis[1][qb]);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[1][qb][r], s[1][qb][r + 1]);
-        bool moved_up;
-        a[qb] = move_ref(qb, swap_halves_max(mx) * c, trig, moved_up);
-        up |= moved_up;
-        ps0[qb][0] *= a[qb];
-        ps0[qb][1] *= a[qb];
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pacc[qb][t2][e] = (__bf16)((float)pacc[qb][t2][e] * a[qb]);
-        ps1[qb][0] = ps1[qb][1] = 0.f;
-      }
-      if (__builtin_amdgcn_ballot_w64(up) != 0) rescale_acc(a);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int pair = 0; pair < 4; ++pair) exp_pair(s, 1, qb, t2, pair);
-    }
-  };
-  auto sm_end = [&]() {
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) l_run[qb] += (ps0[qb][0] + ps0[qb][1]) + (ps1[qb][0] + ps1[qb][1]);
-  };
-  // Results computed so far must exist here: an empty statement that reads
-  // them keeps the compiler from sinking their arithmetic past the branch
-  // that follows (which would pull it out of the interleaved block).
-  auto pin_weights = [&](int nb) {
-#pragma unroll
+
+    // Per-lane base offsets (elements) of the operand reads.
+    const int kbase = ql * KROW + hl * 8;   // + (32 nb) KROW + 16 kb
+    const int vbase = (4 * hl + (lane % 16) / 4) * VROW + ((lane / 16) % 2) * 16 + 4 * (lane % 4);
+                                            // + (32 nb + 16 t2) VROW + 32 db, + 8 VROW for the upper 4 keys
+
+    // K fragment i (kb-major): rows 32 nb .. + 32, columns 16 kb .. + 16.
+    auto fetch_k = [&](const __bf16* Ks, int i) -> bf16x8 {
+      const int kb = i / NKB, nb = i % NKB;
+      return *(const bf16x8*)(Ks + kbase + nb * 32 * KROW + kb * 16);
+    };
+    // V^T fragment i = (nb, t2, db), db fastest.  B operand slot 8*hl + e of
+    // 16-key block (nb, t2) is key 32 nb + 16 t2 + 8 (e / 4) + 4 hl + e % 4 (the
+    // order in which the score layout hands the weights over); the A operand
+    // for the same slots comes from two transposing reads of 4 consecutive keys
+    // each: within a 16-lane group, lane j reads row kbase + j / 4 at column
+    // dsrc + 4 (j % 4), and lane i receives the 4 keys at column dsrc + i.
+    auto fetch_v = [&](const __bf16* Vs, int i) -> bf16x8 {
+      const int nb = i / (2 * DB), t2 = (i / DB) % 2, db = i % DB;
+      const __bf16* a = Vs + vbase + (nb * 32 + t2 * 16) * VROW + db * 32;
+      const s16x4 lo = lds_read_tr16(a);
+      const s16x4 hi = lds_read_tr16(a + 8 * VROW);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    f32x16 oacc[DB][NQB];
+  #pragma unroll
+    for (int db = 0; db < DB; ++db)
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = f32x16{};
+    f32x16 sacc[NKB][NQB];  // score tile: S(t+1), then S(t+2), during iteration t
+    bf16x8 pacc[NQB][NP];   // weight tile: P(t), then P(t+1), during iteration t
+    float m_run[NQB], l_run[NQB];  // reference max (base 2), this lane's part of the sum
+  #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      asm volatile("" ::"v"(pacc[qb][nb * 2]), "v"(pacc[qb][nb * 2 + 1]));
-      asm volatile("" ::"v"(ps0[qb][0]), "v"(ps0[qb][1]), "v"(ps1[qb][0]), "v"(ps1[qb][1]));
+      m_run[qb] = -INFINITY;
+      l_run[qb] = 0.f;
     }
-  };
-  // Scores of keys past a row's last visible key become -inf.  The select is
-  // a sign mask and a bit insert, not a compare: a compare per score writes a
-  // scalar register pair, and the compiler would keep dozens of them live.
-  // With a mask, Ms holds the tile's mask words and key 8 (r / 4) + 4 hl + r % 4
-  // of key block nb is bit 8 (r / 4) + r % 4 of this lane's word shifted down
-  // by 4 hl.
-  auto apply_mask = [&](int e, f32x16 (&s)[NKB][NQB], const uint32_t* Ms) {
-    const int k0 = (tile_index(e) + t0) * BK;
-#pragma unroll
+    // A scale of 0 would turn a masked -inf score into NaN (-inf * 0); a floor
+    // of 1e-30 changes the weights of finite scores by less than 1e-20.
+    const float c = fmaxf(p.scale * kLog2e, 1e-30f);
+
+    // Tiles that cross the diagonal or the kv_len boundary -- and tiles past
+    // the workgroup's last one, whose LDS holds stale data -- are masked
+    // element by element; every other tile is fully visible to the wave.
+    auto need_mask = [&](int e) {
+      const int k0 = (tile_index(e) + t0) * BK;
+      return (BITS && e < 0) || (k0 + BK > kvl) || (UPPER && k0 + BK - 1 > qw0 + off + wr) ||
+             (WINDOW && k0 < qw0 + QW - 1 + off - wl);
+    };
+
+    // ---- softmax of one tile, in small units that the pipeline spreads out ----
+    // The weights of a tile are formed against the current reference m with no
+    // row max at all: the pages subtract the max only to keep the exponentials
+    // finite, and any reference that keeps every weight at most 2^20 (sums of
+    // a million keys stay far inside float32) gives the same l, O and L.  A
+    // weight above that shows in the lane's sum of the tile's weights, so two
+    // cheap checks replace the max:
+    //   EM units (key block 0): weight, sum and bf16 weight of 2 scores;
+    //   check 1 (after the EM units and the P V products of the previous tile,
+    //     block-0 scores intact): a lane's block-0 sum above 2^20, or a row
+    //     with no reference yet (m = -inf) that sees a key of block 0, moves
+    //     the reference up to block 0's row max (rare): l and the output
+    //     accumulator are rescaled and key block 0 is computed again;
+    //   EX units (key block 1): as EM;
+    //   check 2 (after the EX units, block-1 scores intact): the same for the
+    //     whole tile's sum and block 1 (rarer still): l, the output
+    //     accumulator and block 0's weights and sum are rescaled and key block
+    //     1 is computed again.
+    // Once a row has a reference, its l is at least 1 (the key that set it
+    // weighs exactly 1), so weights that underflow are negligible.  Each score
+    // is read from the accumulator once and consumed at once.
+    constexpr int NU_EM = NQB * 8, NU_EX = NQB * 8;
+    constexpr float kSumLimit = 1048576.0f;  // 2^20
+    float m_use[NQB], ps0[NQB][2], ps1[NQB][2];  // reference in use; block 0 and block 1 sums
+    bool vis[NKB][NQB];  // the row sees a key of key block nb
+    auto sm_begin = [&]() {
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        ps0[qb][0] = ps0[qb][1] = ps1[qb][0] = ps1[qb][1] = 0.f;
+        m_use[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+      }
+    };
+    // weights of 2 scores (pair `pair` of 16-key half t2 of key block nb)
+    auto exp_pair = [&](f32x16 (&s)[NKB][NQB], int nb, int qb, int t2, int pair) {
+  #pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = 2 * pair + h, r = (2 * t2 + e / 4) * 4 + (e % 4);
+        const float pv = fast_exp2(fmaf(s[nb][qb][r], c, -m_use[qb]));
+        (nb == 0 ? ps0 : ps1)[qb][h] += pv;
+        pacc[qb][nb * 2 + t2][e] = (__bf16)pv;
+      }
+    };
+    // EM unit u: t2-major, so that the units of the first 16-key half come
+    // first (the P V products release that half of the weight tile first)
+    auto unit_em = [&](f32x16 (&s)[NKB][NQB], auto uc) {
+      constexpr int u = decltype(uc)::value, t2 = u / 8, qb = (u / 4) % 2, pair = u % 4;
+      exp_pair(s, 0, qb, t2, pair);
+    };
+    auto unit_ex = [&](f32x16 (&s)[NKB][NQB], auto uc) {
+      constexpr int u = decltype(uc)::value, qb = u / 8, t2 = (u / 4) % 2, pair = u % 4;
+      exp_pair(s, 1, qb, t2, pair);
+    };
+    // Move row qb's reference to mx (its new row max, base 2): returns the
+    // factor e^(m_old - m_new) for everything accumulated so far.
+    // Only the rows that ask for it move (trig); the others keep their
+    // reference (factor 1).  A row that moves from -inf has accumulated
+    // nothing (factor 0 on zeros), so the output accumulator is rescaled only
+    // when some row with a reference moves it up (rescale_acc).  Both half-waves
+    // hold every row and must take the same decision: trig is combined over
+    // the pair first.
+    auto row_any = [&](bool x) -> bool {
+      const uint32_t v = x ? 1u : 0u;
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (r[0] | r[1]) != 0u;
+    };
+    auto move_ref = [&](int qb, float mx, bool trig, bool& moved_up) -> float {
+      const float m_new = trig ? fmaxf(m_run[qb], mx) : m_run[qb];
+      const float a = m_run[qb] == -INFINITY ? 0.f : fast_exp2(m_run[qb] - m_new);  // nothing accumulated yet
+      moved_up = (m_run[qb] != -INFINITY) & (m_new > m_run[qb]);
+      l_run[qb] *= a;
+      m_run[qb] = m_new;
+      m_use[qb] = m_new == -INFINITY ? 0.f : m_new;
+      return a;
+    };
+    auto rescale_acc = [&](const float (&a)[NQB]) {
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+  #pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          // read inside the branch, in place: no copy of the accumulator
+          // outside it
+          asm volatile("" : "+a"(oacc[db][qb]));
+          oacc[db][qb] *= a[qb];
+        }
+    };
+    auto sm_check1 = [&](f32x16 (&s)[NKB][NQB]) __attribute__((always_inline)) {
+      bool over = false;
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        over |= (ps0[qb][0] + ps0[qb][1] > kSumLimit) | ((m_run[qb] == -INFINITY) & vis[0][qb]);
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform, rare
+        float a[NQB];
+        bool up = false;
+  #pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const bool trig = row_any(ps0[qb][0] + ps0[qb][1] > kSumLimit) |
+                            ((m_run[qb] == -INFINITY) & vis[0][qb]);
+          float mx = -INFINITY;
+  #pragma unroll
+          for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[0][qb][r], s[0][qb][r + 1]);
+          bool moved_up;
+          a[qb] = move_ref(qb, swap_halves_max(mx) * c, trig, moved_up);  // -inf stays -inf (c > 0)
+          up |= moved_up;
+          ps0[qb][0] = ps0[qb][1] = 0.f;
+        }
+        if (__builtin_amdgcn_ballot_w64(up) != 0) rescale_acc(a);
+  #pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+  #pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2)
+  #pragma unroll
+            for (int pair = 0; pair < 4; ++pair) exp_pair(s, 0, qb, t2, pair);
+      }
+    };
+    auto sm_check2 = [&](f32x16 (&s)[NKB][NQB]) __attribute__((always_inline)) {
+      bool over = false;
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        over |= (ps0[qb][0] + ps0[qb][1] + ps1[qb][0] + ps1[qb][1] > kSumLimit) |
+                ((m_run[qb] == -INFINITY) & vis[1][qb]);
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform, rarer still
+        float a[NQB];
+        bool up = false;
+  #pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const bool trig = row_any(ps0[qb][0] + ps0[qb][1] + ps1[qb][0] + ps1[qb][1] > kSumLimit) |
+                            ((m_run[qb] == -INFINITY) & vis[1][qb]);
+          float mx = -INFINITY;
+  #pragma unroll
+          for (int r = 0; r < 16; r += 2) mx = max3f(mx, s[1][qb][r], s[1][qb][r + 1]);
+          bool moved_up;
+          a[qb] = move_ref(qb, swap_halves_max(mx) * c, trig, moved_up);
+          up |= moved_up;
+          ps0[qb][0] *= a[qb];
+          ps0[qb][1] *= a[qb];
+  #pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2)
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) pacc[qb][t2][e] = (__bf16)((float)pacc[qb][t2][e] * a[qb]);
+          ps1[qb][0] = ps1[qb][1] = 0.f;
+        }
+        if (__builtin_amdgcn_ballot_w64(up) != 0) rescale_acc(a);
+  #pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+  #pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2)
+  #pragma unroll
+            for (int pair = 0; pair < 4; ++pair) exp_pair(s, 1, qb, t2, pair);
+      }
+    };
+    auto sm_end = [&]() {
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) l_run[qb] += (ps0[qb][0] + ps0[qb][1]) + (ps1[qb][0] + ps1[qb][1]);
+    };
+    // Results computed so far must exist here: an empty statement that reads
+    // them keeps the compiler from sinking their arithmetic past the branch
+    // that follows (which would pull it out of the interleaved block).
+    auto pin_weights = [&](int nb) {
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        asm volatile("" ::"v"(pacc[qb][nb * 2]), "v"(pacc[qb][nb * 2 + 1]));
+        asm volatile("" ::"v"(ps0[qb][0]), "v"(ps0[qb][1]), "v"(ps1[qb][0]), "v"(ps1[qb][1]));
+      }
+    };
+    // Scores of keys past a row's last visible key become -inf.  The select is
+    // a sign mask and a bit insert, not a compare: a compare per score writes a
+    // scalar register pair, and the compiler would keep dozens of them live.
+    // With a mask, Ms holds the tile's mask words and key 8 (r / 4) + 4 hl + r % 4
+    // of key block nb is bit 8 (r / 4) + r % 4 of this lane's word shifted down
+    // by 4 hl.
+    auto apply_mask = [&](int e, f32x16 (&s)[NKB][NQB], const uint32_t* Ms) {
+      const int k0 = (tile_index(e) + t0) * BK;
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int qrow = qw0 + 32 * qb + ql;
+        const int lim = UPPER ? min(kvl - 1, qrow + off + wr) : kvl - 1;  // last visible key
+        const int lo = qrow + off - wl;                                   // first (window)
+        uint32_t hid[NKB];  // masked-out keys of the row's two key blocks (bit set)
+  #pragma unroll
+        for (int nb = 0; nb < NKB; ++nb) {
+          vis[nb][qb] = lim >= k0 + 32 * nb && (!WINDOW || lo <= k0 + 32 * nb + 31);
+          if constexpr (BITS) {
+            // a tile the mask keeps whole has no words in LDS: all ones
+            const uint32_t w = Ms[ws * 128 + nb * 64 + 32 * qb + ql] | ~(uint32_t)(e >> 31);
+            vis[nb][qb] = vis[nb][qb] && w != 0u;  // a hint: a false "sees" only costs time
+            hid[nb] = ~w >> (4 * hl);
+          }
+        }
+        const int base = lim - (k0 + 4 * hl);  // >= 0 iff key k0 + 4 hl is visible
+        const int base_lo = k0 + 4 * hl - lo;  // >= 0 iff key k0 + 4 hl is past the window start
+  #pragma unroll
+        for (int nb = 0; nb < NKB; ++nb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int idx = nb * 32 + 8 * (r / 4) + (r % 4);
+            uint32_t hide = (uint32_t)((base - idx) >> 31);
+            if constexpr (WINDOW) hide |= (uint32_t)((base_lo + idx) >> 31);
+            if constexpr (BITS) hide |= (uint32_t)__builtin_amdgcn_sbfe((int)hid[nb], 8 * (r / 4) + r % 4, 1);
+            const uint32_t v = __float_as_uint(s[nb][qb][r]);
+            s[nb][qb][r] = __uint_as_float((hide & 0xFF800000u) | (~hide & v));
+          }
+      }
+    };
+    // Whole softmax of the tile with entry e (prologue only).
+    auto softmax_all = [&](int e, f32x16 (&s)[NKB][NQB], const uint32_t* Ms) {
+      mfma_guard();  // compute_s just wrote the scores
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
+      if (need_mask(e)) apply_mask(e, s, Ms);
+      sm_begin();
+      static_for<NU_EM>([&](auto uc) { unit_em(s, uc); });
+      sm_check1(s);
+      static_for<NU_EX>([&](auto uc) { unit_ex(s, uc); });
+      sm_check2(s);
+      sm_end();
+    };
+    // S^T = K Q^T for one tile, not interleaved (prologue only).
+    auto compute_s = [&](const __bf16* Ks, f32x16 (&s)[NKB][NQB]) {
+  #pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        const bf16x8 kf = fetch_k(Ks, i);
+        const int kb = i / NKB, nb = i % NKB;
+  #pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          if (kb == 0) mfma_s_first(s[nb][qb], kf, qf[qb][kb]);
+          else mfma_s_acc(s[nb][qb], kf, qf[qb][kb]);
+        }
+      }
+    };
+
+    // ---- one pipelined iteration ----
+    // Work of iteration t: O += P(t) V(t), the softmax of S(t+1) into P(t+1),
+    // S(t+2) = K(t+2) Q^T.  One score and one weight tile suffice because the
+    // steps run in three phases, one MFMA per step:
+    //   A: the P V MFMAs (fragment j / 2, query block j % 2), with the EM
+    //      units; then check 1;
+    //   B: the S MFMAs of key block 0 -- whose scores have been consumed --
+    //      with the EX units; then check 2;
+    //   C: the S MFMAs of key block 1, with the tile loads.
+    // Operands are read PF fragments ahead; tile load item k goes at step
+    // 3k + 1 (measured: spreading them over all steps gains nothing).
+    constexpr int PF = 2;
+    constexpr int NSA = 2 * NF, NSB = NQB * DK;  // steps of phases A and B (C = B)
+    auto iteration = [&](int eK, int eV, int eM, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst,
+                         __bf16* Vdst, uint32_t* Mdst) {
+      sm_begin();
+      // K operands: a ring of PF + 2, so that a read overwrites a register two
+      // fragments after the asm MFMAs last used it
+      constexpr int KR = PF + 2;
+      bf16x8 vr[PF + 1], kr[KR];
+  #pragma unroll
+      for (int i = 0; i < PF; ++i) vr[i] = fetch_v(Vs, i);
+      // phase A
+      static_for<NSA>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int i = j / 2, qb = j % 2;
+        constexpr int nb = i / (2 * DB), t2 = (i / DB) % 2, db = i % DB;
+        oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % (PF + 1)], pacc[qb][nb * 2 + t2],
+                                                              oacc[db][qb], 0, 0, 0);
+        if constexpr (qb == 0 && i + PF < NF) vr[(i + PF) % (PF + 1)] = fetch_v(Vs, i + PF);
+        // EM units over the last three quarters of the steps: an EM unit of
+        // 16-key half t2 overwrites weight fragment t2 of P(t), which the P V
+        // MFMAs of fragment t2 (steps 2 DB t2 .. + 2 DB) read first
+        constexpr int Q1 = NSA / 4;
+        if constexpr (j >= Q1) {
+          constexpr int W = NSA - Q1;
+          constexpr int u0 = ((j - Q1) * NU_EM + W - 1) / W, u1 = ((j - Q1 + 1) * NU_EM + W - 1) / W;
+          static_for<u1 - u0>([&](auto uc) {
+            constexpr int u = u0 + decltype(uc)::value;
+            static_assert(j >= 2 * DB * (u / (NU_EM / 2) + 1), "EM unit after the P V MFMAs of its fragment");
+            unit_em(sacc, std::integral_constant<int, u>{});
+          });
+        }
+        // the first K operands of phase B, during the last steps of phase A
+        if constexpr (j >= NSA - PF) kr[j - (NSA - PF)] = fetch_k(Ks, (j - (NSA - PF)) * NKB);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      pin_weights(0);
+      sm_check1(sacc);
+      // phases B and C: S fragments (kb, nb) in order nb-major, kb, query block
+      static_for<2 * NSB>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (j == NSB) {
+          // check 2, before phase C overwrites key block 1's scores
+          pin_weights(1);
+          sm_check2(sacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        constexpr int f = j / NQB, qb = j % NQB;     // f-th S fragment of this iteration
+        constexpr int nb = f / DK, kb = f % DK;
+        if constexpr (kb == 0) mfma_s_first(sacc[nb][qb], kr[f % KR], qf[qb][kb]);
+        else mfma_s_acc(sacc[nb][qb], kr[f % KR], qf[qb][kb]);
+        if constexpr (qb == 0 && f + PF < NF) {
+          constexpr int f2 = f + PF;
+          kr[f2 % KR] = fetch_k(Ks, (f2 % DK) * NKB + f2 / DK);
+        }
+        // tile loads in phase C, which carries no VALU work: item i at step
+        // NSB + i NSB / NITEM
+        if constexpr (j >= NSB) {
+          static_for<NITEM>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (NSB + i * NSB / NITEM == j) load_item(i, eK, eV, eM, Kdst, Vdst, Mdst);
+          });
+        }
+        if constexpr (j < NSB) {
+          constexpr int u0 = (j * NU_EX + NSB - 1) / NSB, u1 = ((j + 1) * NU_EX + NSB - 1) / NSB;
+          static_for<u1 - u0>([&](auto uc) { unit_ex(sacc, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      pin_weights(1);
+      sm_end();
+    };
+    // Iteration t: K(t+2) in Ks, V(t) in Vs; loads K(t+4) into Kdst and V(t+2)
+    // into Vdst.  Every wave runs the whole pipeline every iteration: a tile
+    // that none of a wave's queries sees is fully masked and adds weights of
+    // exactly 0 (at most two iterations per workgroup and the diagonal tiles of
+    // the later waves; one code path keeps the interleave and the register
+    // assignment fixed).
+    // With a mask, Ms holds the words of tile t+1 and Mdst receives those of
+    // tile t+3.
+    auto step_tile = [&](int t, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst,
+                         const uint32_t* Ms, uint32_t* Mdst) {
+      const int e1 = tile_entry(t + 1), e2 = tile_entry(t + 2), e3 = tile_entry(t + 3),
+                e4 = tile_entry(t + 4);
+      mfma_guard();  // the last iteration's final MFMAs wrote the scores
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
+      if (need_mask(e1)) apply_mask(e1, sacc, Ms);
+      iteration(e4, e2, e3, Ks, Vs, Kdst, Vdst, Mdst);
+      // This wave's loads of the previous iteration (K(t+3), V(t+1)) are done
+      // (loads complete in order: only this iteration's NITEM may be pending),
+      // and so are its LDS reads; the barrier then makes every wave's loads
+      // visible and frees the buffers read in this iteration for the next
+      // iteration's loads.
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NITEM) : "memory");
+    };
+
+    // Prologue: K(0) .. K(2), V(0), V(1) in LDS; S(0) and its softmax, S(1);
+    // K(3) loaded over K(0) once every wave has read K(0).
+    const int e0 = tile_entry(0);
+    if (n_tiles > 0) {
+      const int e1 = tile_entry(1), e2 = tile_entry(2);
+      load_k(tile_index(e0), Kb0);
+      load_k(tile_index(e1), Kb1);
+      load_k(tile_index(e2), Kb2);
+      load_v(tile_index(e0), Vb0);
+      load_v(tile_index(e1), Vb1);
+      load_mask(e0, Mb0);
+      load_mask(e1, Mb1);
+      load_mask(e2, Mb2);
+    }
+    __syncthreads();
+    compute_s(Kb0, sacc);
+    __syncthreads();  // every wave is done with K(0) before K(3) goes over it
+    if (n_tiles > 0) load_k(tile_index(tile_entry(3)), Kb0);
+    softmax_all(e0, sacc, Mb0);
+    compute_s(Kb1, sacc);
+    // K(1) is read by every wave before iteration 0 loads K(4) over it; K(3)
+    // may still be in flight (iteration 0 waits for it)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    for (int t = 0; t < n_tiles; t += 3) {
+      step_tile(t, Kb2, Vb0, Kb1, Vb2, Mb1, Mb0);
+      if (t + 1 >= n_tiles) break;
+      step_tile(t + 1, Kb0, Vb1, Kb2, Vb0, Mb2, Mb1);
+      if (t + 2 >= n_tiles) break;
+      step_tile(t + 2, Kb1, Vb2, Kb0, Vb1, Mb0, Mb2);
+    }
+
+    // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
+  #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qrow = qw0 + 32 * qb + ql;
-      const int lim = UPPER ? min(kvl - 1, qrow + off + wr) : kvl - 1;  // last visible key
-      const int lo = qrow + off - wl;                                   // first (window)
-      uint32_t hid[NKB];  // masked-out keys of the row's two key blocks (bit set)
-#pragma unroll
-      for (int nb = 0; nb < NKB; ++nb) {
-        vis[nb][qb] = lim >= k0 + 32 * nb && (!WINDOW || lo <= k0 + 32 * nb + 31);
-        if constexpr (BITS) {
-          // a tile the mask keeps whole has no words in LDS: all ones
-          const uint32_t w = Ms[ws * 128 + nb * 64 + 32 * qb + ql] | ~(uint32_t)(e >> 31);
-          vis[nb][qb] = vis[nb][qb] && w != 0u;  // a hint: a false "sees" only costs time
-          hid[nb] = ~w >> (4 * hl);
-        }
-      }
-      const int base = lim - (k0 + 4 * hl);  // >= 0 iff key k0 + 4 hl is visible
-      const int base_lo = k0 + 4 * hl - lo;  // >= 0 iff key k0 + 4 hl is past the window start
-#pragma unroll
-      for (int nb = 0; nb < NKB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int idx = nb * 32 + 8 * (r / 4) + (r % 4);
-          uint32_t hide = (uint32_t)((base - idx) >> 31);
-          if constexpr (WINDOW) hide |= (uint32_t)((base_lo + idx) >> 31);
-          if constexpr (BITS) hide |= (uint32_t)__builtin_amdgcn_sbfe((int)hid[nb], 8 * (r / 4) + r % 4, 1);
-          const uint32_t v = __float_as_uint(s[nb][qb][r]);
-          s[nb][qb][r] = __uint_as_float((hide & 0xFF800000u) | (~hide & v));
-        }
-    }
-  };
-  // Whole softmax of the tile with entry e (prologue only).
-  auto softmax_all = [&](int e, f32x16 (&s)[NKB][NQB], const uint32_t* Ms) {
-    mfma_guard();  // compute_s just wrote the scores
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-    if (need_mask(e)) apply_mask(e, s, Ms);
-    sm_begin();
-    static_for<NU_EM>([&](auto uc) { unit_em(s, uc); });
-    sm_check1(s);
-    static_for<NU_EX>([&](auto uc) { unit_ex(s, uc); });
-    sm_check2(s);
-    sm_end();
-  };
-  // S^T = K Q^T for one tile, not interleaved (prologue only).
-  auto compute_s = [&](const __bf16* Ks, f32x16 (&s)[NKB][NQB]) {
-#pragma unroll
-    for (int i = 0; i < NF; ++i) {
-      const bf16x8 kf = fetch_k(Ks, i);
-      const int kb = i / NKB, nb = i % NKB;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        if (kb == 0) mfma_s_first(s[nb][qb], kf, qf[qb][kb]);
-        else mfma_s_acc(s[nb][qb], kf, qf[qb][kb]);
+      const float l_tot = swap_halves_sum(l_run[qb]);
+      if (qrow < N) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        __bf16* Orow = (__bf16*)p.o + (size_t)bh * N * D + (size_t)qrow * D;
+  #pragma unroll
+        for (int db = 0; db < DB; ++db)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bf16x4 ov;
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[db][qb][4 * j + i] * inv);
+            *(bf16x4*)(Orow + db * 32 + 8 * j + 4 * hl) = ov;
+          }
+        if (hl == 0)
+          p.lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run[qb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
       }
     }
-  };
-
-  // ---- one pipelined iteration ----
-  // Work of iteration t: O += P(t) V(t), the softmax of S(t+1) into P(t+1),
-  // S(t+2) = K(t+2) Q^T.  One score and one weight tile suffice because the
-  // steps run in three phases, one MFMA per step:
-  //   A: the P V MFMAs (fragment j / 2, query block j % 2), with the EM
-  //      units; then check 1;
-  //   B: the S MFMAs of key block 0 -- whose scores have been consumed --
-  //      with the EX units; then check 2;
-  //   C: the S MFMAs of key block 1, with the tile loads.
-  // Operands are read PF fragments ahead; tile load item k goes at step
-  // 3k + 1 (measured: spreading them over all steps gains nothing).
-  constexpr int PF = 2;
-  constexpr int NSA = 2 * NF, NSB = NQB * DK;  // steps of phases A and B (C = B)
-  auto iteration = [&](int eK, int eV, int eM, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst,
-                       __bf16* Vdst, uint32_t* Mdst) {
-    sm_begin();
-    // K operands: a ring of PF + 2, so that a read overwrites a register two
-    // fragments after the asm MFMAs last used it
-    constexpr int KR = PF + 2;
-    bf16x8 vr[PF + 1], kr[KR];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) vr[i] = fetch_v(Vs, i);
-    // phase A
-    static_for<NSA>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      __builtin_amdgcn_sched_barrier(0);
-      constexpr int i = j / 2, qb = j % 2;
-      constexpr int nb = i / (2 * DB), t2 = (i / DB) % 2, db = i % DB;
-      oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[i % (PF + 1)], pacc[qb][nb * 2 + t2],
-                                                            oacc[db][qb], 0, 0, 0);
-      if constexpr (qb == 0 && i + PF < NF) vr[(i + PF) % (PF + 1)] = fetch_v(Vs, i + PF);
-      // EM units over the last three quarters of the steps: an EM unit of
-      // 16-key half t2 overwrites weight fragment t2 of P(t), which the P V
-      // MFMAs of fragment t2 (steps 2 DB t2 .. + 2 DB) read first
-      constexpr int Q1 = NSA / 4;
-      if constexpr (j >= Q1) {
-        constexpr int W = NSA - Q1;
-        constexpr int u0 = ((j - Q1) * NU_EM + W - 1) / W, u1 = ((j - Q1 + 1) * NU_EM + W - 1) / W;
-        static_for<u1 - u0>([&](auto uc) {
-          constexpr int u = u0 + decltype(uc)::value;
-          static_assert(j >= 2 * DB * (u / (NU_EM / 2) + 1), "EM unit after the P V MFMAs of its fragment");
-          unit_em(sacc, std::integral_constant<int, u>{});
-        });
-      }
-      // the first K operands of phase B, during the last steps of phase A
-      if constexpr (j >= NSA - PF) kr[j - (NSA - PF)] = fetch_k(Ks, (j - (NSA - PF)) * NKB);
-    });
-    __builtin_amdgcn_sched_barrier(0);
-    pin_weights(0);
-    sm_check1(sacc);
-    // phases B and C: S fragments (kb, nb) in order nb-major, kb, query block
-    static_for<2 * NSB>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (j == NSB) {
-        // check 2, before phase C overwrites key block 1's scores
-        pin_weights(1);
-        sm_check2(sacc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      constexpr int f = j / NQB, qb = j % NQB;     // f-th S fragment of this iteration
-      constexpr int nb = f / DK, kb = f % DK;
-      if constexpr (kb == 0) mfma_s_first(sacc[nb][qb], kr[f % KR], qf[qb][kb]);
-      else mfma_s_acc(sacc[nb][qb], kr[f % KR], qf[qb][kb]);
-      if constexpr (qb == 0 && f + PF < NF) {
-        constexpr int f2 = f + PF;
-        kr[f2 % KR] = fetch_k(Ks, (f2 % DK) * NKB + f2 / DK);
-      }
-      // tile loads in phase C, which carries no VALU work: item i at step
-      // NSB + i NSB / NITEM
-      if constexpr (j >= NSB) {
-        static_for<NITEM>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          if constexpr (NSB + i * NSB / NITEM == j) load_item(i, eK, eV, eM, Kdst, Vdst, Mdst);
-        });
-      }
-      if constexpr (j < NSB) {
-        constexpr int u0 = (j * NU_EX + NSB - 1) / NSB, u1 = ((j + 1) * NU_EX + NSB - 1) / NSB;
-        static_for<u1 - u0>([&](auto uc) { unit_ex(sacc, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
-      }
-    });
-    __builtin_amdgcn_sched_barrier(0);
-    pin_weights(1);
-    sm_end();
-  };
-  // Iteration t: K(t+2) in Ks, V(t) in Vs; loads K(t+4) into Kdst and V(t+2)
-  // into Vdst.  Every wave runs the whole pipeline every iteration: a tile
-  // that none of a wave's queries sees is fully masked and adds weights of
-  // exactly 0 (at most two iterations per workgroup and the diagonal tiles of
-  // the later waves; one code path keeps the interleave and the register
-  // assignment fixed).
-  // With a mask, Ms holds the words of tile t+1 and Mdst receives those of
-  // tile t+3.
-  auto step_tile = [&](int t, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst,
-                       const uint32_t* Ms, uint32_t* Mdst) {
-    const int e1 = tile_entry(t + 1), e2 = tile_entry(t + 2), e3 = tile_entry(t + 3),
-              e4 = tile_entry(t + 4);
-    mfma_guard();  // the last iteration's final MFMAs wrote the scores
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-    if (need_mask(e1)) apply_mask(e1, sacc, Ms);
-    iteration(e4, e2, e3, Ks, Vs, Kdst, Vdst, Mdst);
-    // This wave's loads of the previous iteration (K(t+3), V(t+1)) are done
-    // (loads complete in order: only this iteration's NITEM may be pending),
-    // and so are its LDS reads; the barrier then makes every wave's loads
-    // visible and frees the buffers read in this iteration for the next
-    // iteration's loads.
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NITEM) : "memory");
-  };
-
-  // Prologue: K(0) .. K(2), V(0), V(1) in LDS; S(0) and its softmax, S(1);
-  // K(3) loaded over K(0) once every wave has read K(0).
-  const int e0 = tile_entry(0);
-  if (n_tiles > 0) {
-    const int e1 = tile_entry(1), e2 = tile_entry(2);
-    load_k(tile_index(e0), Kb0);
-    load_k(tile_index(e1), Kb1);
-    load_k(tile_index(e2), Kb2);
-    load_v(tile_index(e0), Vb0);
-    load_v(tile_index(e1), Vb1);
-    load_mask(e0, Mb0);
-    load_mask(e1, Mb1);
-    load_mask(e2, Mb2);
   }
-  __syncthreads();
-  compute_s(Kb0, sacc);
-  __syncthreads();  // every wave is done with K(0) before K(3) goes over it
-  if (n_tiles > 0) load_k(tile_index(tile_entry(3)), Kb0);
-  softmax_all(e0, sacc, Mb0);
-  compute_s(Kb1, sacc);
-  // K(1) is read by every wave before iteration 0 loads K(4) over it; K(3)
-  // may still be in flight (iteration 0 waits for it)
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  for (int t = 0; t < n_tiles; t += 3) {
-    step_tile(t, Kb2, Vb0, Kb1, Vb2, Mb1, Mb0);
-    if (t + 1 >= n_tiles) break;
-    step_tile(t + 1, Kb0, Vb1, Kb2, Vb0, Mb2, Mb1);
-    if (t + 2 >= n_tiles) break;
-    step_tile(t + 2, Kb1, Vb2, Kb0, Vb1, Mb0, Mb2);
-  }
-
-  // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qrow = qw0 + 32 * qb + ql;
-    const float l_tot = swap_halves_sum(l_run[qb]);
-    if (qrow < N) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      __bf16* Orow = (__bf16*)p.o + (size_t)bh * N * D + (size_t)qrow * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x4 ov;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[db][qb][4 * j + i] * inv);
-          *(bf16x4*)(Orow + db * 32 + 8 * j + 4 * hl) = ov;
-        }
-      if (hl == 0)
-        p.lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run[qb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
-    }
   }
 }
 

@@ -50,7 +50,10 @@ def test_planner_paths():
     p = fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True)
     assert p["path_name"] == "prefill" and p["block_k"] == 64
     assert p["block_q"] == p["threads"] and p["block_q"] % 64 == 0  # 64 queries per wave
-    assert p["grid"] == -(-8192 // p["block_q"]) * 64 and p["workspace_bytes"] == 0
+    assert p["grid"] == 256 and p["workspace_bytes"] == 0         # persistent: one per CU
+    assert fa.plan(2, 32, 8192, 8192, 128, fa.BF16, False)["grid"] == 32 * 64
+    assert fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True, window=(127, 0))["grid"] == 32 * 64
+    assert fa.plan(1, 3, 300, 300, 128, fa.BF16, True)["grid"] == 8   # 6 items, rounded up
     assert p["lds_bytes"] <= 160 * 1024                      # fits one compute unit's LDS
     p = fa.plan(1, 1, 128, 128, 64, fa.F32, False)
     assert p["path_name"] == "f32" and p["grid"] == 8
