@@ -58,6 +58,7 @@
 //    forward does (lane = query, a word per 32 keys), dK/dV transposed
 //    (lane = key: words stored [word][query row], so one 16-byte read gives
 //    a lane the words of four consecutive queries).
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -191,356 +192,379 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   __shared__ __attribute__((aligned(256))) uint32_t Ms1[BITS ? 512 : 1];
   __shared__ int tlist[BITS ? kMaskMaxTiles : 1];   // the key tile's listed query stages
 
-  const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int kt = (int)(logical % n_ktiles);   // causal: low key tiles see the most queries
-  const int64_t bh = logical / n_ktiles;
-  const int b = (int)(bh / p.H);
-  const int N = p.N, M = p.M;
-  const int tid = threadIdx.x;
-  const int lane = tid % 64, h = lane / 32, l32 = lane % 32;
-  const int ws = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int kvl = __builtin_amdgcn_readfirstlane(clamp_kv(p.kv_len, b, M));
-  const int off = kvl - N;                    // key j visible to query i iff j <= i + off
-  const int k0 = kt * kBwdBlockKV;
-  const int jw0 = k0 + ws * KW;               // first key of this wave
-
-  const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
-  const __bf16* Gg = (const __bf16*)p.dout + (size_t)bh * N * D;
-  const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D;
-  const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D;
-  const float* Wg = p.ws + (size_t)bh * 2 * p.Npad;
-
-  // Local window: key j is seen by queries j - off - wr .. j - off + wl
-  // (causal: wr = 0).  LOWQ: a key has a first query; WINDOW: and a last.
-  constexpr bool LOWQ = CAUSAL || WINDOW;
-  const int wl = WINDOW ? min(p.wl, N + kvl) : 0;
-  const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
-  // Query stages this workgroup visits.
-  const int n_stage_all = (N + St::ROWS - 1) / St::ROWS;
-  int s_lo = 0;
-  if (LOWQ) s_lo = min(max(k0 - off - wr, 0) / St::ROWS, n_stage_all);
-  int s_end = n_stage_all;
-  if (WINDOW) s_end = clampi(floor_div(k0 + kBwdBlockKV - 1 - off + wl, St::ROWS) + 1, s_lo, n_stage_all);
-  int n_stages = k0 < kvl ? s_end - s_lo : 0;
-  // Element mask: the listed stages in [s_lo, s_lo + n_stages), from list
-  // position lo (the list ascends).
-  int lo = 0;
-  if constexpr (BITS) {
-    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
-    const int stride = mask_stage_stride(N);
-    const int32_t* L = p.stage_lists + ((int64_t)(bm * p.mask_h + hm) * n_ktiles + kt) * stride;
-    const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
-    for (int i = tid; i < cnt; i += kBwdThreads) tlist[i] = L[1 + i] & 0x7FFFFFFF;
-    __syncthreads();
-    int below_lo = 0, below_hi = 0;
-    for (int i0 = 0; i0 < cnt; i0 += 64) {
-      const int e = i0 + lane < cnt ? tlist[i0 + lane] : 0x7FFFFFFF;
-      below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < s_lo));
-      below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < s_lo + n_stages));
+  // Causal without a window or a mask: persistent workgroups walking their
+  // XCD's tiles, heavy and light alternating round by round, as in the
+  // forward prefill.
+  constexpr bool PERSIST = CAUSAL && !WINDOW && !BITS;
+  const int64_t n_items = (int64_t)n_ktiles * p.B * p.H;
+  const int xcd = blockIdx.x % kNumXcd, u = blockIdx.x / kNumXcd, W = gridDim.x / kNumXcd;
+  const int64_t qx = n_items / kNumXcd, rx = n_items % kNumXcd;
+  const int64_t x_start = xcd * qx + (xcd < rx ? xcd : rx), x_count = qx + (xcd < rx ? 1 : 0);
+  for (int64_t k = 0;; ++k) {
+    int64_t logical;
+    if constexpr (PERSIST) {
+      const int64_t within = k * W + ((k & 1) ? W - 1 - u : u);
+      if (within >= x_count) break;
+      logical = x_start + within;
+      // the previous item's loads into LDS have landed, every wave is done
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    } else {
+      if (k > 0) break;
+      logical = xcd_logical(blockIdx.x, gridDim.x);
     }
-    lo = __builtin_amdgcn_readfirstlane(below_lo);
-    n_stages = __builtin_amdgcn_readfirstlane(below_hi) - lo;
-  }
-  // query stage of the t-th visited stage
-  auto stage_of = [&](int t) -> int {
-    if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + t]);
-    else return s_lo + t;
-  };
+  {
+    const int kt = (int)(logical % n_ktiles);   // causal: low key tiles see the most queries
+    const int64_t bh = logical / n_ktiles;
+    const int b = (int)(bh / p.H);
+    const int N = p.N, M = p.M;
+    const int tid = threadIdx.x;
+    const int lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int ws = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int kvl = __builtin_amdgcn_readfirstlane(clamp_kv(p.kv_len, b, M));
+    const int off = kvl - N;                    // key j visible to query i iff j <= i + off
+    const int k0 = kt * kBwdBlockKV;
+    const int jw0 = k0 + ws * KW;               // first key of this wave
 
-  // ---- K and V fragments of the wave's keys (B operands), zero past kv_len ----
-  bf16x8 kf[KBW][DK], vf[KBW][DK];
-#pragma unroll
-  for (int kb2 = 0; kb2 < KBW; ++kb2) {
-    const int key = jw0 + 32 * kb2 + l32;
-    const bool ok = key < kvl;
-#pragma unroll
-    for (int kb = 0; kb < DK; ++kb) {
-      const size_t e = (size_t)(ok ? key : 0) * D + kb * 16 + h * 8;
-      kf[kb2][kb] = ok ? *(const bf16x8*)(Kg + e) : bf16x8{};
-      vf[kb2][kb] = ok ? *(const bf16x8*)(Vg + e) : bf16x8{};
-    }
-  }
+    const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
+    const __bf16* Gg = (const __bf16*)p.dout + (size_t)bh * N * D;
+    const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D;
+    const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D;
+    const float* Wg = p.ws + (size_t)bh * 2 * p.Npad;
 
-  // ---- stage loads: rows [64 s, 64 s + 64) of Q, dO, Lg, D ----
-  uint32_t soff[St::BPW];
-#pragma unroll
-  for (int i = 0; i < St::BPW; ++i) soff[i] = St::slot_src((ws + i * NW) * 64 + lane);
-  const int nrec_q = N * 2 * D;  // the planner keeps this below 2^31
-  // Lane l of wave 0's extra block: Lg (l < 16) or D (16 <= l < 32) chunk.
-  const uint32_t loff = (uint32_t)((lane < 16 ? lane : (lane < 32 ? p.Npad / 4 + lane - 16 : 0)) * 16);
-  // Element mask: wave ws loads words 2 ws and 2 ws + 1 of the workgroup's
-  // 256 keys for the stage's 64 rows (lane = row; rows past N read row N - 1).
-  const uint32_t* Mg = nullptr;
-  int mbytes = 0;
-  if constexpr (BITS) {
-    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
-    Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
-    mbytes = N * p.mask_w * 4;
-  }
-  auto load_stage = [&](int s, char* Qd, char* Gd, float* Ld, uint32_t* Md) __attribute__((always_inline)) {
-    const uint32_t rb = (uint32_t)s * St::ROWS * 2 * D;
-#pragma unroll
-    for (int i = 0; i < St::BPW; ++i) {
-      int wofs = (ws + i * NW) * 1024;
-      asm volatile("" : "+s"(wofs));
-      buffer_load_lds16(Qg, nrec_q, soff[i] + rb, (lds_ptr)(Qd + wofs));
-      buffer_load_lds16(Gg, nrec_q, soff[i] + rb, (lds_ptr)(Gd + wofs));
-    }
-    if (ws == 0)
-      buffer_load_lds16(Wg + s * St::ROWS, (int)((2 * p.Npad - s * St::ROWS) * 4), loff, (lds_ptr)Ld);
+    // Local window: key j is seen by queries j - off - wr .. j - off + wl
+    // (causal: wr = 0).  LOWQ: a key has a first query; WINDOW: and a last.
+    constexpr bool LOWQ = CAUSAL || WINDOW;
+    const int wl = WINDOW ? min(p.wl, N + kvl) : 0;
+    const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
+    // Query stages this workgroup visits.
+    const int n_stage_all = (N + St::ROWS - 1) / St::ROWS;
+    int s_lo = 0;
+    if (LOWQ) s_lo = min(max(k0 - off - wr, 0) / St::ROWS, n_stage_all);
+    int s_end = n_stage_all;
+    if (WINDOW) s_end = clampi(floor_div(k0 + kBwdBlockKV - 1 - off + wl, St::ROWS) + 1, s_lo, n_stage_all);
+    int n_stages = k0 < kvl ? s_end - s_lo : 0;
+    // Element mask: the listed stages in [s_lo, s_lo + n_stages), from list
+    // position lo (the list ascends).
+    int lo = 0;
     if constexpr (BITS) {
-      const uint32_t row = (uint32_t)min(s * St::ROWS + lane, N - 1);
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        int mofs = (2 * ws + w) * 64;
-        asm volatile("" : "+s"(mofs));
-        buffer_load_lds4(Mg, mbytes, (row * (uint32_t)p.mask_w + (uint32_t)(k0 / 32 + 2 * ws + w)) * 4u,
-                         (lds_ptr)(Md + mofs));
+      const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+      const int stride = mask_stage_stride(N);
+      const int32_t* L = p.stage_lists + ((int64_t)(bm * p.mask_h + hm) * n_ktiles + kt) * stride;
+      const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
+      for (int i = tid; i < cnt; i += kBwdThreads) tlist[i] = L[1 + i] & 0x7FFFFFFF;
+      __syncthreads();
+      int below_lo = 0, below_hi = 0;
+      for (int i0 = 0; i0 < cnt; i0 += 64) {
+        const int e = i0 + lane < cnt ? tlist[i0 + lane] : 0x7FFFFFFF;
+        below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < s_lo));
+        below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < s_lo + n_stages));
       }
+      lo = __builtin_amdgcn_readfirstlane(below_lo);
+      n_stages = __builtin_amdgcn_readfirstlane(below_hi) - lo;
     }
-  };
-
-  // ---- per-lane LDS read bases ----
-  // Row reads (A operand of S and dP): row 32 u + l32, chunk 2 kb + h.
-  const int G = (l32 >> 2) & 3;
-  const int rbase0 = l32 * ROWB + 16 * ((0 + h) ^ G);   // kb even; + 32 u ROWB + 64 (kb / 2)
-  const int rbase1 = l32 * ROWB + 16 * ((2 + h) ^ G);   // kb odd
-  // Transposing reads (A operand of dV^T, dK^T): lane j of 16-lane group g
-  // reads row 32 u + 16 s' + 8 hi + 4 h + j / 4, columns 32 db + 16 (g % 2) +
-  // 4 (j % 4) .. + 4.
-  const int j16 = lane % 16, g2 = (lane / 16) % 2;
-  const int tbase0 = (4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (0 + h)) + 8 * (j16 % 2);
-  const int tbase1 = (8 + 4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (2 + h)) + 8 * (j16 % 2);
-
-  f32x16 dkacc[KBW][DB], dvacc[KBW][DB];
-#pragma unroll
-  for (int kb2 = 0; kb2 < KBW; ++kb2)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      dkacc[kb2][db] = f32x16{};
-      dvacc[kb2][db] = f32x16{};
-      agpr_guard(dkacc[kb2][db]);
-      agpr_guard(dvacc[kb2][db]);
-    }
-  const float c = fmaxf(p.scale * kLog2e, 1e-30f);
-  // Query i sees the lane's key j iff j - off - wr <= i (causal, window) and
-  // i <= j - off + wl (window); register r of a step holds query
-  // qs0 + 8 (r / 4) + 4 h + r % 4, masked iff qs0 + 8 (r / 4) + r % 4 < thr
-  // or > thr_hi.
-  int thr[KBW], thr_hi[KBW];
-#pragma unroll
-  for (int kb2 = 0; kb2 < KBW; ++kb2) {
-    thr[kb2] = jw0 + 32 * kb2 + l32 - off - wr - 4 * h;
-    thr_hi[kb2] = jw0 + 32 * kb2 + l32 - off + wl - 4 * h;
-  }
-
-  // One 32-query step of stage s from buffers (Qs, Gs, Ls, Ms).
-  auto qstep = [&](int s, int u, const char* Qs, const char* Gs, const float* Ls, const uint32_t* Ms,
-                   auto MASK) __attribute__((always_inline)) {
-    constexpr bool mask = decltype(MASK)::value;
-    const int qs0 = s * St::ROWS + 32 * u;
-    f32x16 sacc[KBW], pacc[KBW];
-    // Operands are read one fragment ahead of their MFMAs, in a ring of
-    // three: a read overwrites a register two fragments after the asm MFMAs
-    // last read it.  Scheduling barriers keep the reads where they are (the
-    // scheduler would otherwise sink them next to their use and expose the
-    // LDS latency before every fragment).
-    bf16x8 qa[3], ga[3];
-    auto read_qg = [&](int kb) __attribute__((always_inline)) {
-      const int o = 32 * u * ROWB + 64 * (kb / 2) + ((kb & 1) ? rbase1 : rbase0);
-      qa[kb % 3] = *lds_at<bf16x8>(Qs, o);
-      ga[kb % 3] = *lds_at<bf16x8>(Gs, o);
+    // query stage of the t-th visited stage
+    auto stage_of = [&](int t) -> int {
+      if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + t]);
+      else return s_lo + t;
     };
-    read_qg(0);
-    static_for<DK>([&](auto kc) {
-      constexpr int kb = decltype(kc)::value;
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kb + 1 < DK) read_qg(kb + 1);
-#pragma unroll
-      for (int kb2 = 0; kb2 < KBW; ++kb2) {
-        if constexpr (kb == 0) {
-          mfma_vv0(sacc[kb2], qa[kb % 3], kf[kb2][kb]);
-          mfma_vv0(pacc[kb2], ga[kb % 3], vf[kb2][kb]);
-        } else {
-          mfma_vv(sacc[kb2], qa[kb % 3], kf[kb2][kb]);
-          mfma_vv(pacc[kb2], ga[kb % 3], vf[kb2][kb]);
-        }
+
+    // ---- K and V fragments of the wave's keys (B operands), zero past kv_len ----
+    bf16x8 kf[KBW][DK], vf[KBW][DK];
+  #pragma unroll
+    for (int kb2 = 0; kb2 < KBW; ++kb2) {
+      const int key = jw0 + 32 * kb2 + l32;
+      const bool ok = key < kvl;
+  #pragma unroll
+      for (int kb = 0; kb < DK; ++kb) {
+        const size_t e = (size_t)(ok ? key : 0) * D + kb * 16 + h * 8;
+        kf[kb2][kb] = ok ? *(const bf16x8*)(Kg + e) : bf16x8{};
+        vf[kb2][kb] = ok ? *(const bf16x8*)(Vg + e) : bf16x8{};
       }
-    });
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kb2 = 0; kb2 < KBW; ++kb2) mfma_guard_v(sacc[kb2], pacc[kb2]);
-    // P = 2^(S c - Lg), dS = P (dP - D).  Lane: key jw0 + 32 kb2 + l32,
-    // register r: query qs0 + 8 (r / 4) + 4 h + r % 4.
-    bf16x8 pf[KBW][2], sf[KBW][2];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 L4 = *(const float4*)(Ls + 32 * u + 8 * g + 4 * h);
-      const float4 D4 = *(const float4*)(Ls + 64 + 32 * u + 8 * g + 4 * h);
-      const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
-      const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
-      // mask words of the four queries 32 u + 8 g + 4 h + e, for each of the
-      // wave's 32-key blocks: bit l32 is the lane's key; the eight bits the
-      // lane needs are gathered into one register, bit 4 kb2 + e
-      [[maybe_unused]] uint32_t mvis = 0u;
+    }
+
+    // ---- stage loads: rows [64 s, 64 s + 64) of Q, dO, Lg, D ----
+    uint32_t soff[St::BPW];
+  #pragma unroll
+    for (int i = 0; i < St::BPW; ++i) soff[i] = St::slot_src((ws + i * NW) * 64 + lane);
+    const int nrec_q = N * 2 * D;  // the planner keeps this below 2^31
+    // Lane l of wave 0's extra block: Lg (l < 16) or D (16 <= l < 32) chunk.
+    const uint32_t loff = (uint32_t)((lane < 16 ? lane : (lane < 32 ? p.Npad / 4 + lane - 16 : 0)) * 16);
+    // Element mask: wave ws loads words 2 ws and 2 ws + 1 of the workgroup's
+    // 256 keys for the stage's 64 rows (lane = row; rows past N read row N - 1).
+    const uint32_t* Mg = nullptr;
+    int mbytes = 0;
+    if constexpr (BITS) {
+      const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+      Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
+      mbytes = N * p.mask_w * 4;
+    }
+    auto load_stage = [&](int s, char* Qd, char* Gd, float* Ld, uint32_t* Md) __attribute__((always_inline)) {
+      const uint32_t rb = (uint32_t)s * St::ROWS * 2 * D;
+  #pragma unroll
+      for (int i = 0; i < St::BPW; ++i) {
+        int wofs = (ws + i * NW) * 1024;
+        asm volatile("" : "+s"(wofs));
+        buffer_load_lds16(Qg, nrec_q, soff[i] + rb, (lds_ptr)(Qd + wofs));
+        buffer_load_lds16(Gg, nrec_q, soff[i] + rb, (lds_ptr)(Gd + wofs));
+      }
+      if (ws == 0)
+        buffer_load_lds16(Wg + s * St::ROWS, (int)((2 * p.Npad - s * St::ROWS) * 4), loff, (lds_ptr)Ld);
       if constexpr (BITS) {
-#pragma unroll
-        for (int kb2 = 0; kb2 < KBW; ++kb2) {
-          const uint4 w4 = *(const uint4*)(Ms + (2 * ws + kb2) * 64 + 32 * u + 8 * g + 4 * h);
-          const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mvis |= ((w[e] >> l32) & 1u) << (4 * kb2 + e);
+        const uint32_t row = (uint32_t)min(s * St::ROWS + lane, N - 1);
+  #pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          int mofs = (2 * ws + w) * 64;
+          asm volatile("" : "+s"(mofs));
+          buffer_load_lds4(Mg, mbytes, (row * (uint32_t)p.mask_w + (uint32_t)(k0 / 32 + 2 * ws + w)) * 4u,
+                           (lds_ptr)(Md + mofs));
         }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-#pragma unroll
-        for (int kb2 = 0; kb2 < KBW; ++kb2) {
-          float pv = fast_exp2(fmaf(sacc[kb2][r], c, -Lv[e]));
-          if constexpr (mask) {
-            const int qi = qs0 + 8 * g + e;
-            bool hide = false;
-            if constexpr (LOWQ) hide = qi < thr[kb2];
-            if constexpr (WINDOW) hide = hide | (qi > thr_hi[kb2]);
-            if constexpr (BITS) hide = hide | (((mvis >> (4 * kb2 + e)) & 1u) == 0u);
-            pv = hide ? 0.f : pv;
-          }
-          const float dsv = pv * (pacc[kb2][r] - Dv[e]);
-          pf[kb2][r / 8][r % 8] = (__bf16)pv;
-          sf[kb2][r / 8][r % 8] = (__bf16)dsv;
-        }
-      }
-    }
-#pragma unroll
-    for (int kb2 = 0; kb2 < KBW; ++kb2) valu_guard(pf[kb2][0], sf[kb2][0]), valu_guard(pf[kb2][1], sf[kb2][1]);
-    // dV^T += dO^T P, dK^T += Q^T dS over the step's 32 queries; fragment
-    // i = (sp, db), operands read one fragment ahead in a ring of three.
-    bf16x8 gt[3], qt[3];
-    auto read_t = [&](int i) __attribute__((always_inline)) {
-      const int o = (32 * u + 16 * (i / DB)) * ROWB + 64 * (i % DB);
-      const s16x4 glo = lds_read_tr16((const __bf16*)(Gs + o + tbase0));
-      const s16x4 ghi = lds_read_tr16((const __bf16*)(Gs + o + tbase1));
-      const s16x4 qlo = lds_read_tr16((const __bf16*)(Qs + o + tbase0));
-      const s16x4 qhi = lds_read_tr16((const __bf16*)(Qs + o + tbase1));
-      gt[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
-      qt[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    read_t(0);
-    static_for<2 * DB>([&](auto ic) {
-      constexpr int i = decltype(ic)::value, sp = i / DB, db = i % DB;
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (i + 1 < 2 * DB) read_t(i + 1);
-#pragma unroll
-      for (int kb2 = 0; kb2 < KBW; ++kb2) {
-        mfma_aa(dvacc[kb2][db], gt[i % 3], pf[kb2][sp]);
-        mfma_aa(dkacc[kb2][db], qt[i % 3], sf[kb2][sp]);
+
+    // ---- per-lane LDS read bases ----
+    // Row reads (A operand of S and dP): row 32 u + l32, chunk 2 kb + h.
+    const int G = (l32 >> 2) & 3;
+    const int rbase0 = l32 * ROWB + 16 * ((0 + h) ^ G);   // kb even; + 32 u ROWB + 64 (kb / 2)
+    const int rbase1 = l32 * ROWB + 16 * ((2 + h) ^ G);   // kb odd
+    // Transposing reads (A operand of dV^T, dK^T): lane j of 16-lane group g
+    // reads row 32 u + 16 s' + 8 hi + 4 h + j / 4, columns 32 db + 16 (g % 2) +
+    // 4 (j % 4) .. + 4.
+    const int j16 = lane % 16, g2 = (lane / 16) % 2;
+    const int tbase0 = (4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (0 + h)) + 8 * (j16 % 2);
+    const int tbase1 = (8 + 4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (2 + h)) + 8 * (j16 % 2);
+
+    f32x16 dkacc[KBW][DB], dvacc[KBW][DB];
+  #pragma unroll
+    for (int kb2 = 0; kb2 < KBW; ++kb2)
+  #pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dkacc[kb2][db] = f32x16{};
+        dvacc[kb2][db] = f32x16{};
+        agpr_guard(dkacc[kb2][db]);
+        agpr_guard(dvacc[kb2][db]);
       }
-    });
-    __builtin_amdgcn_sched_barrier(0);
-  };
+    const float c = fmaxf(p.scale * kLog2e, 1e-30f);
+    // Query i sees the lane's key j iff j - off - wr <= i (causal, window) and
+    // i <= j - off + wl (window); register r of a step holds query
+    // qs0 + 8 (r / 4) + 4 h + r % 4, masked iff qs0 + 8 (r / 4) + r % 4 < thr
+    // or > thr_hi.
+    int thr[KBW], thr_hi[KBW];
+  #pragma unroll
+    for (int kb2 = 0; kb2 < KBW; ++kb2) {
+      thr[kb2] = jw0 + 32 * kb2 + l32 - off - wr - 4 * h;
+      thr_hi[kb2] = jw0 + 32 * kb2 + l32 - off + wl - 4 * h;
+    }
 
-  // Every branch below is uniform over the workgroup and no step is skipped
-  // inside a loop: control flow that joins with the accumulators live makes
-  // the register allocator shuffle them between AGPRs.
-  auto iteration = [&](int t, const char* Qs, const char* Gs, const float* Ls, const uint32_t* Ms,
-                       char* Qn, char* Gn, float* Ln, uint32_t* Mn, auto MASK) __attribute__((always_inline)) {
-    wait_vm0();
-    __syncthreads();
-    const int s_cur = stage_of(t);
-    if (t + 1 < n_stages) load_stage(stage_of(t + 1), Qn, Gn, Ln, Mn);
-    qstep(s_cur, 0, Qs, Gs, Ls, Ms, MASK);
-    qstep(s_cur, 1, Qs, Gs, Ls, Ms, MASK);
-  };
+    // One 32-query step of stage s from buffers (Qs, Gs, Ls, Ms).
+    auto qstep = [&](int s, int u, const char* Qs, const char* Gs, const float* Ls, const uint32_t* Ms,
+                     auto MASK) __attribute__((always_inline)) {
+      constexpr bool mask = decltype(MASK)::value;
+      const int qs0 = s * St::ROWS + 32 * u;
+      f32x16 sacc[KBW], pacc[KBW];
+      // Operands are read one fragment ahead of their MFMAs, in a ring of
+      // three: a read overwrites a register two fragments after the asm MFMAs
+      // last read it.  Scheduling barriers keep the reads where they are (the
+      // scheduler would otherwise sink them next to their use and expose the
+      // LDS latency before every fragment).
+      bf16x8 qa[3], ga[3];
+      auto read_qg = [&](int kb) __attribute__((always_inline)) {
+        const int o = 32 * u * ROWB + 64 * (kb / 2) + ((kb & 1) ? rbase1 : rbase0);
+        qa[kb % 3] = *lds_at<bf16x8>(Qs, o);
+        ga[kb % 3] = *lds_at<bf16x8>(Gs, o);
+      };
+      read_qg(0);
+      static_for<DK>([&](auto kc) {
+        constexpr int kb = decltype(kc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kb + 1 < DK) read_qg(kb + 1);
+  #pragma unroll
+        for (int kb2 = 0; kb2 < KBW; ++kb2) {
+          if constexpr (kb == 0) {
+            mfma_vv0(sacc[kb2], qa[kb % 3], kf[kb2][kb]);
+            mfma_vv0(pacc[kb2], ga[kb % 3], vf[kb2][kb]);
+          } else {
+            mfma_vv(sacc[kb2], qa[kb % 3], kf[kb2][kb]);
+            mfma_vv(pacc[kb2], ga[kb % 3], vf[kb2][kb]);
+          }
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int kb2 = 0; kb2 < KBW; ++kb2) mfma_guard_v(sacc[kb2], pacc[kb2]);
+      // P = 2^(S c - Lg), dS = P (dP - D).  Lane: key jw0 + 32 kb2 + l32,
+      // register r: query qs0 + 8 (r / 4) + 4 h + r % 4.
+      bf16x8 pf[KBW][2], sf[KBW][2];
+  #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 L4 = *(const float4*)(Ls + 32 * u + 8 * g + 4 * h);
+        const float4 D4 = *(const float4*)(Ls + 64 + 32 * u + 8 * g + 4 * h);
+        const float Lv[4] = {L4.x, L4.y, L4.z, L4.w};
+        const float Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+        // mask words of the four queries 32 u + 8 g + 4 h + e, for each of the
+        // wave's 32-key blocks: bit l32 is the lane's key; the eight bits the
+        // lane needs are gathered into one register, bit 4 kb2 + e
+        [[maybe_unused]] uint32_t mvis = 0u;
+        if constexpr (BITS) {
+  #pragma unroll
+          for (int kb2 = 0; kb2 < KBW; ++kb2) {
+            const uint4 w4 = *(const uint4*)(Ms + (2 * ws + kb2) * 64 + 32 * u + 8 * g + 4 * h);
+            const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) mvis |= ((w[e] >> l32) & 1u) << (4 * kb2 + e);
+          }
+        }
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+  #pragma unroll
+          for (int kb2 = 0; kb2 < KBW; ++kb2) {
+            float pv = fast_exp2(fmaf(sacc[kb2][r], c, -Lv[e]));
+            if constexpr (mask) {
+              const int qi = qs0 + 8 * g + e;
+              bool hide = false;
+              if constexpr (LOWQ) hide = qi < thr[kb2];
+              if constexpr (WINDOW) hide = hide | (qi > thr_hi[kb2]);
+              if constexpr (BITS) hide = hide | (((mvis >> (4 * kb2 + e)) & 1u) == 0u);
+              pv = hide ? 0.f : pv;
+            }
+            const float dsv = pv * (pacc[kb2][r] - Dv[e]);
+            pf[kb2][r / 8][r % 8] = (__bf16)pv;
+            sf[kb2][r / 8][r % 8] = (__bf16)dsv;
+          }
+        }
+      }
+  #pragma unroll
+      for (int kb2 = 0; kb2 < KBW; ++kb2) valu_guard(pf[kb2][0], sf[kb2][0]), valu_guard(pf[kb2][1], sf[kb2][1]);
+      // dV^T += dO^T P, dK^T += Q^T dS over the step's 32 queries; fragment
+      // i = (sp, db), operands read one fragment ahead in a ring of three.
+      bf16x8 gt[3], qt[3];
+      auto read_t = [&](int i) __attribute__((always_inline)) {
+        const int o = (32 * u + 16 * (i / DB)) * ROWB + 64 * (i % DB);
+        const s16x4 glo = lds_read_tr16((const __bf16*)(Gs + o + tbase0));
+        const s16x4 ghi = lds_read_tr16((const __bf16*)(Gs + o + tbase1));
+        const s16x4 qlo = lds_read_tr16((const __bf16*)(Qs + o + tbase0));
+        const s16x4 qhi = lds_read_tr16((const __bf16*)(Qs + o + tbase1));
+        gt[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
+        qt[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      read_t(0);
+      static_for<2 * DB>([&](auto ic) {
+        constexpr int i = decltype(ic)::value, sp = i / DB, db = i % DB;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (i + 1 < 2 * DB) read_t(i + 1);
+  #pragma unroll
+        for (int kb2 = 0; kb2 < KBW; ++kb2) {
+          mfma_aa(dvacc[kb2][db], gt[i % 3], pf[kb2][sp]);
+          mfma_aa(dkacc[kb2][db], qt[i % 3], sf[kb2][sp]);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-  if (n_stages > 0) load_stage(stage_of(0), Qs0, Gs0, Ls0, Ms0);
-  if constexpr (BITS) {
-    // element mask: every listed stage applies its bits (and the causal
-    // and window rules)
-    int t = 0;
-    for (; t + 1 < n_stages; t += 2) {
-      iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
-      iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, std::true_type{});
-    }
-    if (t < n_stages) iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
-  } else if constexpr (!WINDOW) {
-    // Causal: the first n_mask stages hold queries that do not see every key
-    // of the workgroup and are masked element by element (an even number, so
-    // that the unmasked loop starts on buffer 0, or all stages).
-    int n_mask = 0;
-    if (CAUSAL) {
-      const int rows = k0 + kBwdBlockKV - 1 - off - s_lo * St::ROWS;  // masked rows from stage s_lo on
-      n_mask = rows > 0 ? min((rows + 2 * St::ROWS - 1) / (2 * St::ROWS) * 2, n_stages) : 0;
-    }
-    int t = 0;
-    for (; t + 1 < n_mask; t += 2) {
-      iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
-      iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, std::true_type{});
-    }
-    if (t < n_mask) {  // n_mask == n_stages, odd: the last stage
-      iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
-      ++t;
-    }
-    for (; t + 1 < n_stages; t += 2) {
-      iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::false_type{});
-      iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, std::false_type{});
-    }
-    if (t < n_stages) iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::false_type{});
-  } else {
-    // Window: stages before nA hold queries before some key's first viewer,
-    // stages from nC on queries past some key's last viewer; both masked,
-    // the stages between are seen whole.  Stage t uses buffer t % 2.
-    const int nA = clampi(floor_div(k0 + kBwdBlockKV - 1 - off - wr + St::ROWS - 1, St::ROWS) - s_lo,
-                          0, n_stages);
-    const int nC = clampi(floor_div(k0 - off + wl - (St::ROWS - 1), St::ROWS) + 1 - s_lo, nA, n_stages);
-    auto segment = [&](int t, int t_end, auto MASK) __attribute__((always_inline)) {
-      if ((t & 1) && t < t_end) {
-        iteration(t, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, MASK);
+    // Every branch below is uniform over the workgroup and no step is skipped
+    // inside a loop: control flow that joins with the accumulators live makes
+    // the register allocator shuffle them between AGPRs.
+    auto iteration = [&](int t, const char* Qs, const char* Gs, const float* Ls, const uint32_t* Ms,
+                         char* Qn, char* Gn, float* Ln, uint32_t* Mn, auto MASK) __attribute__((always_inline)) {
+      wait_vm0();
+      __syncthreads();
+      const int s_cur = stage_of(t);
+      if (t + 1 < n_stages) load_stage(stage_of(t + 1), Qn, Gn, Ln, Mn);
+      qstep(s_cur, 0, Qs, Gs, Ls, Ms, MASK);
+      qstep(s_cur, 1, Qs, Gs, Ls, Ms, MASK);
+    };
+
+    if (n_stages > 0) load_stage(stage_of(0), Qs0, Gs0, Ls0, Ms0);
+    if constexpr (BITS) {
+      // element mask: every listed stage applies its bits (and the causal
+      // and window rules)
+      int t = 0;
+      for (; t + 1 < n_stages; t += 2) {
+        iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
+        iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, std::true_type{});
+      }
+      if (t < n_stages) iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
+    } else if constexpr (!WINDOW) {
+      // Causal: the first n_mask stages hold queries that do not see every key
+      // of the workgroup and are masked element by element (an even number, so
+      // that the unmasked loop starts on buffer 0, or all stages).
+      int n_mask = 0;
+      if (CAUSAL) {
+        const int rows = k0 + kBwdBlockKV - 1 - off - s_lo * St::ROWS;  // masked rows from stage s_lo on
+        n_mask = rows > 0 ? min((rows + 2 * St::ROWS - 1) / (2 * St::ROWS) * 2, n_stages) : 0;
+      }
+      int t = 0;
+      for (; t + 1 < n_mask; t += 2) {
+        iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
+        iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, std::true_type{});
+      }
+      if (t < n_mask) {  // n_mask == n_stages, odd: the last stage
+        iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::true_type{});
         ++t;
       }
-      for (; t + 1 < t_end; t += 2) {
-        iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, MASK);
-        iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, MASK);
+      for (; t + 1 < n_stages; t += 2) {
+        iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::false_type{});
+        iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, std::false_type{});
       }
-      if (t < t_end) iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, MASK);
-    };
-    segment(0, nA, std::true_type{});
-    segment(nA, nC, std::false_type{});
-    segment(nC, n_stages, std::true_type{});
-  }
-
-#pragma unroll
-  for (int kb2 = 0; kb2 < KBW; ++kb2)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      mfma_guard_a(dkacc[kb2][db]);
-      mfma_guard_a(dvacc[kb2][db]);
-    }
-  // ---- write dK = scale * dK^T^T and dV (zero for keys at or past kv_len) ----
-  // Accumulator (kb2, db), register r: d = 32 db + 8 (r / 4) + 4 h + r % 4,
-  // key jw0 + 32 kb2 + l32.
-  __bf16* dK = (__bf16*)p.dk + (size_t)bh * M * D;
-  __bf16* dV = (__bf16*)p.dv + (size_t)bh * M * D;
-  const float sc = p.scale;
-#pragma unroll
-  for (int kb2 = 0; kb2 < KBW; ++kb2) {
-    const int key = jw0 + 32 * kb2 + l32;
-    if (key >= M) continue;
-    const bool ok = key < kvl;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 kv4, vv4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kv4[e] = (__bf16)(ok ? dkacc[kb2][db][4 * g + e] * sc : 0.f);
-          vv4[e] = (__bf16)(ok ? dvacc[kb2][db][4 * g + e] : 0.f);
+      if (t < n_stages) iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, std::false_type{});
+    } else {
+      // Window: stages before nA hold queries before some key's first viewer,
+      // stages from nC on queries past some key's last viewer; both masked,
+      // the stages between are seen whole.  Stage t uses buffer t % 2.
+      const int nA = clampi(floor_div(k0 + kBwdBlockKV - 1 - off - wr + St::ROWS - 1, St::ROWS) - s_lo,
+                            0, n_stages);
+      const int nC = clampi(floor_div(k0 - off + wl - (St::ROWS - 1), St::ROWS) + 1 - s_lo, nA, n_stages);
+      auto segment = [&](int t, int t_end, auto MASK) __attribute__((always_inline)) {
+        if ((t & 1) && t < t_end) {
+          iteration(t, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, MASK);
+          ++t;
         }
-        const size_t at = (size_t)key * D + 32 * db + 8 * g + 4 * h;
-        *(bf16x4*)(dK + at) = kv4;
-        *(bf16x4*)(dV + at) = vv4;
+        for (; t + 1 < t_end; t += 2) {
+          iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, MASK);
+          iteration(t + 1, Qs1, Gs1, Ls1, Ms1, Qs0, Gs0, Ls0, Ms0, MASK);
+        }
+        if (t < t_end) iteration(t, Qs0, Gs0, Ls0, Ms0, Qs1, Gs1, Ls1, Ms1, MASK);
+      };
+      segment(0, nA, std::true_type{});
+      segment(nA, nC, std::false_type{});
+      segment(nC, n_stages, std::true_type{});
+    }
+
+  #pragma unroll
+    for (int kb2 = 0; kb2 < KBW; ++kb2)
+  #pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        mfma_guard_a(dkacc[kb2][db]);
+        mfma_guard_a(dvacc[kb2][db]);
       }
+    // ---- write dK = scale * dK^T^T and dV (zero for keys at or past kv_len) ----
+    // Accumulator (kb2, db), register r: d = 32 db + 8 (r / 4) + 4 h + r % 4,
+    // key jw0 + 32 kb2 + l32.
+    __bf16* dK = (__bf16*)p.dk + (size_t)bh * M * D;
+    __bf16* dV = (__bf16*)p.dv + (size_t)bh * M * D;
+    const float sc = p.scale;
+  #pragma unroll
+    for (int kb2 = 0; kb2 < KBW; ++kb2) {
+      const int key = jw0 + 32 * kb2 + l32;
+      if (key >= M) continue;
+      const bool ok = key < kvl;
+  #pragma unroll
+      for (int db = 0; db < DB; ++db)
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 kv4, vv4;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv4[e] = (__bf16)(ok ? dkacc[kb2][db][4 * g + e] * sc : 0.f);
+            vv4[e] = (__bf16)(ok ? dvacc[kb2][db][4 * g + e] : 0.f);
+          }
+          const size_t at = (size_t)key * D + 32 * db + 8 * g + 4 * h;
+          *(bf16x4*)(dK + at) = kv4;
+          *(bf16x4*)(dV + at) = vv4;
+        }
+    }
+  }
   }
 }
 
@@ -569,294 +593,323 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   __shared__ __attribute__((aligned(256))) uint32_t Mq0[BITS ? NW * 128 : 1];
   __shared__ __attribute__((aligned(256))) uint32_t Mq1[BITS ? NW * 128 : 1];
 
-  const int64_t logical = xcd_logical(blockIdx.x, gridDim.x);
-  int qt = (int)(logical % n_qtiles);
-  const int64_t bh = logical / n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;   // heaviest query tiles first
-  const int b = (int)(bh / p.H);
-  const int N = p.N, M = p.M;
-  const int tid = threadIdx.x;
-  const int lane = tid % 64, h = lane / 32, l32 = lane % 32;
-  const int ws = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int kvl = __builtin_amdgcn_readfirstlane(clamp_kv(p.kv_len, b, M));
-  const int off = kvl - N;
-  const int q0 = qt * kBwdBlockQ;
-  const int qw0 = q0 + ws * QW;
-  const int q_last = min(q0 + kBwdBlockQ, N) - 1;
-  // Local window: query i sees keys i + off - wl .. i + off + wr (causal: wr = 0).
-  constexpr bool UPPER = CAUSAL || WINDOW;
-  const int wl = WINDOW ? min(p.wl, N + kvl) : 0;
-  const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
-  const int kv_end = UPPER ? min(kvl, q_last + off + wr + 1) : kvl;
-  // first key stage (window: the first query's first key)
-  const int t0 = WINDOW ? max(0, q0 + off - wl) / St::ROWS : 0;
-  int n_stages = kv_end > t0 * St::ROWS ? (kv_end + St::ROWS - 1) / St::ROWS - t0 : 0;
-  // Element mask: the listed stages in [t0, t0 + n_stages), from list
-  // position lo (the list ascends; see the forward).
-  int lo = 0;
-  if constexpr (BITS) {
-    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
-    const int stride = mask_list_stride(M);
-    const int32_t* L = p.lists + ((int64_t)(bm * p.mask_h + hm) * n_qtiles + qt) * stride;
-    const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
-    for (int i = tid; i < cnt; i += kBwdThreads) tlist[i] = L[1 + i] & 0x7FFFFFFF;
-    __syncthreads();
-    int below_lo = 0, below_hi = 0;
-    for (int i0 = 0; i0 < cnt; i0 += 64) {
-      const int e = i0 + lane < cnt ? tlist[i0 + lane] : 0x7FFFFFFF;
-      below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t0));
-      below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t0 + n_stages));
+  // Causal without a window or a mask: persistent workgroups walking their
+  // XCD's tiles, heavy and light alternating round by round, as in the
+  // forward prefill.
+  constexpr bool PERSIST = CAUSAL && !WINDOW && !BITS;
+  const int64_t n_items = (int64_t)n_qtiles * p.B * p.H;
+  const int xcd = blockIdx.x % kNumXcd, u = blockIdx.x / kNumXcd, W = gridDim.x / kNumXcd;
+  const int64_t qx = n_items / kNumXcd, rx = n_items % kNumXcd;
+  const int64_t x_start = xcd * qx + (xcd < rx ? xcd : rx), x_count = qx + (xcd < rx ? 1 : 0);
+  for (int64_t k = 0;; ++k) {
+    int64_t logical;
+    if constexpr (PERSIST) {
+      const int64_t within = k * W + ((k & 1) ? W - 1 - u : u);
+      if (within >= x_count) break;
+      logical = x_start + within;
+      // the previous item's loads into LDS have landed, every wave is done
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    } else {
+      if (k > 0) break;
+      logical = xcd_logical(blockIdx.x, gridDim.x);
     }
-    lo = __builtin_amdgcn_readfirstlane(below_lo);
-    n_stages = __builtin_amdgcn_readfirstlane(below_hi) - lo;
-  }
-  // key stage of the t-th visited stage
-  auto stage_of = [&](int t) -> int {
-    if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + t]);
-    else return t0 + t;
-  };
-
-  const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
-  const __bf16* Gg = (const __bf16*)p.dout + (size_t)bh * N * D;
-  const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D;
-  const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D;
-  const float* Wg = p.ws + (size_t)bh * 2 * p.Npad;
-
-  // ---- Q and dO fragments of the wave's queries (B operands) ----
-  // Rows past N hold zeros; their Lg is +inf, so their weights are 0.
-  bf16x8 qf[NQB][DK], gf[NQB][DK];
-  float Lq[NQB], Dq[NQB];
-  int lim[NQB];                  // last key the lane's query sees
-  int lim_lo[NQB];               // first key (window)
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int row = qw0 + 32 * qb + l32;
-    const bool ok = row < N;
-#pragma unroll
-    for (int kb = 0; kb < DK; ++kb) {
-      const size_t e = (size_t)(ok ? row : 0) * D + kb * 16 + h * 8;
-      qf[qb][kb] = ok ? *(const bf16x8*)(Qg + e) : bf16x8{};
-      gf[qb][kb] = ok ? *(const bf16x8*)(Gg + e) : bf16x8{};
-    }
-    Lq[qb] = Wg[row];            // row < Npad
-    Dq[qb] = Wg[p.Npad + row];
-    lim[qb] = UPPER ? min(row + off + wr, kvl - 1) : kvl - 1;
-    lim_lo[qb] = row + off - wl;
-  }
-
-  uint32_t soff[St::BPW];
-#pragma unroll
-  for (int i = 0; i < St::BPW; ++i) soff[i] = St::slot_src((ws + i * NW) * 64 + lane);
-  const int nrec_k = kvl * 2 * D;  // the planner keeps M * D * 2 below 2^31
-  // Element mask: words 2 s and 2 s + 1 of the wave's 64 query rows (lane =
-  // row; rows past N read row N - 1).
-  const uint32_t* Mg = nullptr;
-  int mbytes = 0;
-  uint32_t mrow = 0;
-  if constexpr (BITS) {
-    const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
-    Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
-    mbytes = N * p.mask_w * 4;
-    mrow = (uint32_t)min(qw0 + lane, N - 1) * (uint32_t)p.mask_w;
-  }
-  auto load_stage = [&](int s, char* Kd, char* Vd, uint32_t* Md) __attribute__((always_inline)) {
+  {
+    int qt = (int)(logical % n_qtiles);
+    const int64_t bh = logical / n_qtiles;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;   // heaviest query tiles first
+    const int b = (int)(bh / p.H);
+    const int N = p.N, M = p.M;
+    const int tid = threadIdx.x;
+    const int lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int ws = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int kvl = __builtin_amdgcn_readfirstlane(clamp_kv(p.kv_len, b, M));
+    const int off = kvl - N;
+    const int q0 = qt * kBwdBlockQ;
+    const int qw0 = q0 + ws * QW;
+    const int q_last = min(q0 + kBwdBlockQ, N) - 1;
+    // Local window: query i sees keys i + off - wl .. i + off + wr (causal: wr = 0).
+    constexpr bool UPPER = CAUSAL || WINDOW;
+    const int wl = WINDOW ? min(p.wl, N + kvl) : 0;
+    const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
+    const int kv_end = UPPER ? min(kvl, q_last + off + wr + 1) : kvl;
+    // first key stage (window: the first query's first key)
+    const int t0 = WINDOW ? max(0, q0 + off - wl) / St::ROWS : 0;
+    int n_stages = kv_end > t0 * St::ROWS ? (kv_end + St::ROWS - 1) / St::ROWS - t0 : 0;
+    // Element mask: the listed stages in [t0, t0 + n_stages), from list
+    // position lo (the list ascends; see the forward).
+    int lo = 0;
     if constexpr (BITS) {
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        int mofs = ws * 128 + w * 64;
-        asm volatile("" : "+s"(mofs));
-        buffer_load_lds4(Mg, mbytes, (mrow + 2u * (uint32_t)s + (uint32_t)w) * 4u, (lds_ptr)(Md + mofs));
+      const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+      const int stride = mask_list_stride(M);
+      const int32_t* L = p.lists + ((int64_t)(bm * p.mask_h + hm) * n_qtiles + qt) * stride;
+      const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
+      for (int i = tid; i < cnt; i += kBwdThreads) tlist[i] = L[1 + i] & 0x7FFFFFFF;
+      __syncthreads();
+      int below_lo = 0, below_hi = 0;
+      for (int i0 = 0; i0 < cnt; i0 += 64) {
+        const int e = i0 + lane < cnt ? tlist[i0 + lane] : 0x7FFFFFFF;
+        below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t0));
+        below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t0 + n_stages));
       }
+      lo = __builtin_amdgcn_readfirstlane(below_lo);
+      n_stages = __builtin_amdgcn_readfirstlane(below_hi) - lo;
     }
-    const uint32_t rb = (uint32_t)s * St::ROWS * 2 * D;
-#pragma unroll
-    for (int i = 0; i < St::BPW; ++i) {
-      int wofs = (ws + i * NW) * 1024;
-      asm volatile("" : "+s"(wofs));
-      buffer_load_lds16(Kg, nrec_k, soff[i] + rb, (lds_ptr)(Kd + wofs));
-      buffer_load_lds16(Vg, nrec_k, soff[i] + rb, (lds_ptr)(Vd + wofs));
-    }
-  };
-
-  const int G = (l32 >> 2) & 3;
-  const int rbase0 = l32 * ROWB + 16 * ((0 + h) ^ G);
-  const int rbase1 = l32 * ROWB + 16 * ((2 + h) ^ G);
-  const int j16 = lane % 16, g2 = (lane / 16) % 2;
-  const int tbase0 = (4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (0 + h)) + 8 * (j16 % 2);
-  const int tbase1 = (8 + 4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (2 + h)) + 8 * (j16 % 2);
-
-  f32x16 dqacc[NQB][DB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      dqacc[qb][db] = f32x16{};
-      agpr_guard(dqacc[qb][db]);
-    }
-  const float c = fmaxf(p.scale * kLog2e, 1e-30f);
-
-  // 32 keys (block kb2) of stage s.
-  auto kstep = [&](int s, int kb2, const char* Ks, const char* Vs, const uint32_t* Ms, auto MASK)
-                   __attribute__((always_inline)) {
-    constexpr bool mask = decltype(MASK)::value;
-    const int kk0 = s * St::ROWS + 32 * kb2;
-    f32x16 sacc[NQB], pacc[NQB];
-    // Operands one fragment ahead, in a ring of three (as in the dK/dV pass).
-    bf16x8 ka[3], va[3];
-    auto read_kv = [&](int kb) __attribute__((always_inline)) {
-      const int o = 32 * kb2 * ROWB + 64 * (kb / 2) + ((kb & 1) ? rbase1 : rbase0);
-      ka[kb % 3] = *lds_at<bf16x8>(Ks, o);
-      va[kb % 3] = *lds_at<bf16x8>(Vs, o);
+    // key stage of the t-th visited stage
+    auto stage_of = [&](int t) -> int {
+      if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + t]);
+      else return t0 + t;
     };
-    read_kv(0);
-    static_for<DK>([&](auto kc) {
-      constexpr int kb = decltype(kc)::value;
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kb + 1 < DK) read_kv(kb + 1);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        if constexpr (kb == 0) {
-          mfma_vv0(sacc[qb], ka[kb % 3], qf[qb][kb]);
-          mfma_vv0(pacc[qb], va[kb % 3], gf[qb][kb]);
-        } else {
-          mfma_vv(sacc[qb], ka[kb % 3], qf[qb][kb]);
-          mfma_vv(pacc[qb], va[kb % 3], gf[qb][kb]);
+
+    const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
+    const __bf16* Gg = (const __bf16*)p.dout + (size_t)bh * N * D;
+    const __bf16* Kg = (const __bf16*)p.k + (size_t)bh * M * D;
+    const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D;
+    const float* Wg = p.ws + (size_t)bh * 2 * p.Npad;
+
+    // ---- Q and dO fragments of the wave's queries (B operands) ----
+    // Rows past N hold zeros; their Lg is +inf, so their weights are 0.
+    bf16x8 qf[NQB][DK], gf[NQB][DK];
+    float Lq[NQB], Dq[NQB];
+    int lim[NQB];                  // last key the lane's query sees
+    int lim_lo[NQB];               // first key (window)
+  #pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int row = qw0 + 32 * qb + l32;
+      const bool ok = row < N;
+  #pragma unroll
+      for (int kb = 0; kb < DK; ++kb) {
+        const size_t e = (size_t)(ok ? row : 0) * D + kb * 16 + h * 8;
+        qf[qb][kb] = ok ? *(const bf16x8*)(Qg + e) : bf16x8{};
+        gf[qb][kb] = ok ? *(const bf16x8*)(Gg + e) : bf16x8{};
+      }
+      Lq[qb] = Wg[row];            // row < Npad
+      Dq[qb] = Wg[p.Npad + row];
+      lim[qb] = UPPER ? min(row + off + wr, kvl - 1) : kvl - 1;
+      lim_lo[qb] = row + off - wl;
+    }
+
+    uint32_t soff[St::BPW];
+  #pragma unroll
+    for (int i = 0; i < St::BPW; ++i) soff[i] = St::slot_src((ws + i * NW) * 64 + lane);
+    const int nrec_k = kvl * 2 * D;  // the planner keeps M * D * 2 below 2^31
+    // Element mask: words 2 s and 2 s + 1 of the wave's 64 query rows (lane =
+    // row; rows past N read row N - 1).
+    const uint32_t* Mg = nullptr;
+    int mbytes = 0;
+    uint32_t mrow = 0;
+    if constexpr (BITS) {
+      const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
+      Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
+      mbytes = N * p.mask_w * 4;
+      mrow = (uint32_t)min(qw0 + lane, N - 1) * (uint32_t)p.mask_w;
+    }
+    auto load_stage = [&](int s, char* Kd, char* Vd, uint32_t* Md) __attribute__((always_inline)) {
+      if constexpr (BITS) {
+  #pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          int mofs = ws * 128 + w * 64;
+          asm volatile("" : "+s"(mofs));
+          buffer_load_lds4(Mg, mbytes, (mrow + 2u * (uint32_t)s + (uint32_t)w) * 4u, (lds_ptr)(Md + mofs));
         }
       }
-    });
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) mfma_guard_v(sacc[qb], pacc[qb]);
-    // Lane: query qw0 + 32 qb + l32; register r: key kk0 + 8 (r / 4) + 4 h + r % 4.
-    bf16x8 sf[NQB][2];
-    // mask: key kk0 + 8 (r / 4) + 4 h + r % 4 is bit 8 (r / 4) + r % 4 of the
-    // row's word shifted down by 4 h (bit set: hidden)
-    [[maybe_unused]] uint32_t hid[NQB];
-    if constexpr (BITS) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) hid[qb] = ~Ms[ws * 128 + kb2 * 64 + 32 * qb + l32] >> (4 * h);
-    }
-#pragma unroll
+      const uint32_t rb = (uint32_t)s * St::ROWS * 2 * D;
+  #pragma unroll
+      for (int i = 0; i < St::BPW; ++i) {
+        int wofs = (ws + i * NW) * 1024;
+        asm volatile("" : "+s"(wofs));
+        buffer_load_lds16(Kg, nrec_k, soff[i] + rb, (lds_ptr)(Kd + wofs));
+        buffer_load_lds16(Vg, nrec_k, soff[i] + rb, (lds_ptr)(Vd + wofs));
+      }
+    };
+
+    const int G = (l32 >> 2) & 3;
+    const int rbase0 = l32 * ROWB + 16 * ((0 + h) ^ G);
+    const int rbase1 = l32 * ROWB + 16 * ((2 + h) ^ G);
+    const int j16 = lane % 16, g2 = (lane / 16) % 2;
+    const int tbase0 = (4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (0 + h)) + 8 * (j16 % 2);
+    const int tbase1 = (8 + 4 * h + j16 / 4) * ROWB + 16 * ((2 * g2 + (j16 % 4) / 2) ^ (2 + h)) + 8 * (j16 % 2);
+
+    f32x16 dqacc[NQB][DB];
+  #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(sacc[qb][r], c, -Lq[qb]));
-        if constexpr (mask) {
-          const int key = kk0 + 8 * (r / 4) + 4 * h + r % 4;
-          bool hide = key > lim[qb];
-          if constexpr (WINDOW) hide = hide | (key < lim_lo[qb]);
-          if constexpr (BITS) hide = hide | (((hid[qb] >> (8 * (r / 4) + r % 4)) & 1u) != 0u);
-          pv = hide ? 0.f : pv;
+  #pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dqacc[qb][db] = f32x16{};
+        agpr_guard(dqacc[qb][db]);
+      }
+    const float c = fmaxf(p.scale * kLog2e, 1e-30f);
+
+    // 32 keys (block kb2) of stage s.
+    auto kstep = [&](int s, int kb2, const char* Ks, const char* Vs, const uint32_t* Ms, auto MASK)
+                     __attribute__((always_inline)) {
+      constexpr bool mask = decltype(MASK)::value;
+      const int kk0 = s * St::ROWS + 32 * kb2;
+      f32x16 sacc[NQB], pacc[NQB];
+      // Operands one fragment ahead, in a ring of three (as in the dK/dV pass).
+      bf16x8 ka[3], va[3];
+      auto read_kv = [&](int kb) __attribute__((always_inline)) {
+        const int o = 32 * kb2 * ROWB + 64 * (kb / 2) + ((kb & 1) ? rbase1 : rbase0);
+        ka[kb % 3] = *lds_at<bf16x8>(Ks, o);
+        va[kb % 3] = *lds_at<bf16x8>(Vs, o);
+      };
+      read_kv(0);
+      static_for<DK>([&](auto kc) {
+        constexpr int kb = decltype(kc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kb + 1 < DK) read_kv(kb + 1);
+  #pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          if constexpr (kb == 0) {
+            mfma_vv0(sacc[qb], ka[kb % 3], qf[qb][kb]);
+            mfma_vv0(pacc[qb], va[kb % 3], gf[qb][kb]);
+          } else {
+            mfma_vv(sacc[qb], ka[kb % 3], qf[qb][kb]);
+            mfma_vv(pacc[qb], va[kb % 3], gf[qb][kb]);
+          }
         }
-        sf[qb][r / 8][r % 8] = (__bf16)(pv * (pacc[qb][r] - Dq[qb]));
-      }
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) valu_guard(sf[qb][0], sf[qb][1]);
-    // dQ^T += K^T dS^T over the 32 keys; fragment i = (sp, db), operands
-    // one fragment ahead in a ring of three.
-    bf16x8 kt[3];
-    auto read_t = [&](int i) __attribute__((always_inline)) {
-      const int o = (32 * kb2 + 16 * (i / DB)) * ROWB + 64 * (i % DB);
-      const s16x4 klo = lds_read_tr16((const __bf16*)(Ks + o + tbase0));
-      const s16x4 khi = lds_read_tr16((const __bf16*)(Ks + o + tbase1));
-      kt[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(klo, khi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    read_t(0);
-    static_for<2 * DB>([&](auto ic) {
-      constexpr int i = decltype(ic)::value, sp = i / DB, db = i % DB;
+      });
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (i + 1 < 2 * DB) read_t(i + 1);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) mfma_aa(dqacc[qb][db], kt[i % 3], sf[qb][sp]);
-    });
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // As in the dK/dV pass: uniform branches only, no step skipped in a loop.
-  auto iteration = [&](int t, const char* Ks, const char* Vs, const uint32_t* Ms, char* Kn, char* Vn,
-                       uint32_t* Mn, auto MASK) __attribute__((always_inline)) {
-    wait_vm0();
-    __syncthreads();
-    const int s_cur = stage_of(t);
-    if (t + 1 < n_stages) load_stage(stage_of(t + 1), Kn, Vn, Mn);
-    kstep(s_cur, 0, Ks, Vs, Ms, MASK);
-    kstep(s_cur, 1, Ks, Vs, Ms, MASK);
-  };
-
-  // Stages before n_clean (an even number) are seen whole by every query of
-  // the workgroup: no key past kv_len and, causal, none past the first
-  // query's last key.  The rest are masked element by element.
-  if (n_stages > 0) load_stage(stage_of(0), Ks0, Vs0, Mq0);
-  if constexpr (BITS) {
-    // element mask: every listed stage applies its bits (and the causal,
-    // window and kv_len rules)
-    int t = 0;
-    for (; t + 1 < n_stages; t += 2) {
-      iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
-      iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, std::true_type{});
-    }
-    if (t < n_stages) iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
-  } else if constexpr (!WINDOW) {
-    int n_clean = kvl / St::ROWS;
-    if (CAUSAL) n_clean = min(n_clean, q0 + off + 1 > 0 ? (q0 + off + 1) / St::ROWS : 0);
-    n_clean = min(n_clean, n_stages) / 2 * 2;
-    int t = 0;
-    for (; t < n_clean; t += 2) {
-      iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::false_type{});
-      iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, std::false_type{});
-    }
-    for (; t + 1 < n_stages; t += 2) {
-      iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
-      iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, std::true_type{});
-    }
-    if (t < n_stages) iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
-  } else {
-    // Window: stages before nA hold keys before the last query's first key,
-    // stages from nC on keys past the first query's last key (or kv_len);
-    // both masked, the stages between are seen whole.  Stage t uses buffer
-    // t % 2.
-    const int nA = clampi(floor_div(q_last + off - wl + St::ROWS - 1, St::ROWS) - t0, 0, n_stages);
-    const int last_all = min(UPPER ? q0 + off + wr : kvl - 1, kvl - 1);  // last key every query sees
-    const int nC = clampi(floor_div(last_all - (St::ROWS - 1), St::ROWS) + 1 - t0, nA, n_stages);
-    auto segment = [&](int t, int t_end, auto MASK) __attribute__((always_inline)) {
-      if ((t & 1) && t < t_end) {
-        iteration(t, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, MASK);
-        ++t;
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) mfma_guard_v(sacc[qb], pacc[qb]);
+      // Lane: query qw0 + 32 qb + l32; register r: key kk0 + 8 (r / 4) + 4 h + r % 4.
+      bf16x8 sf[NQB][2];
+      // mask: key kk0 + 8 (r / 4) + 4 h + r % 4 is bit 8 (r / 4) + r % 4 of the
+      // row's word shifted down by 4 h (bit set: hidden)
+      [[maybe_unused]] uint32_t hid[NQB];
+      if constexpr (BITS) {
+  #pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) hid[qb] = ~Ms[ws * 128 + kb2 * 64 + 32 * qb + l32] >> (4 * h);
       }
-      for (; t + 1 < t_end; t += 2) {
-        iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, MASK);
-        iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, MASK);
-      }
-      if (t < t_end) iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, MASK);
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = fast_exp2(fmaf(sacc[qb][r], c, -Lq[qb]));
+          if constexpr (mask) {
+            const int key = kk0 + 8 * (r / 4) + 4 * h + r % 4;
+            bool hide = key > lim[qb];
+            if constexpr (WINDOW) hide = hide | (key < lim_lo[qb]);
+            if constexpr (BITS) hide = hide | (((hid[qb] >> (8 * (r / 4) + r % 4)) & 1u) != 0u);
+            pv = hide ? 0.f : pv;
+          }
+          sf[qb][r / 8][r % 8] = (__bf16)(pv * (pacc[qb][r] - Dq[qb]));
+        }
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) valu_guard(sf[qb][0], sf[qb][1]);
+      // dQ^T += K^T dS^T over the 32 keys; fragment i = (sp, db), operands
+      // one fragment ahead in a ring of three.
+      bf16x8 kt[3];
+      auto read_t = [&](int i) __attribute__((always_inline)) {
+        const int o = (32 * kb2 + 16 * (i / DB)) * ROWB + 64 * (i % DB);
+        const s16x4 klo = lds_read_tr16((const __bf16*)(Ks + o + tbase0));
+        const s16x4 khi = lds_read_tr16((const __bf16*)(Ks + o + tbase1));
+        kt[i % 3] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(klo, khi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      read_t(0);
+      static_for<2 * DB>([&](auto ic) {
+        constexpr int i = decltype(ic)::value, sp = i / DB, db = i % DB;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (i + 1 < 2 * DB) read_t(i + 1);
+  #pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) mfma_aa(dqacc[qb][db], kt[i % 3], sf[qb][sp]);
+      });
+      __builtin_amdgcn_sched_barrier(0);
     };
-    segment(0, nA, std::true_type{});
-    segment(nA, nC, std::false_type{});
-    segment(nC, n_stages, std::true_type{});
-  }
 
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) mfma_guard_a(dqacc[qb][db]);
-  // ---- write dQ = scale * (dQ^T)^T ----
-  // Accumulator (qb, db), register r: d = 32 db + 8 (r / 4) + 4 h + r % 4,
-  // query qw0 + 32 qb + l32.
-  __bf16* dQ = (__bf16*)p.dq + (size_t)bh * N * D;
-  const float sc = p.scale;
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int row = qw0 + 32 * qb + l32;
-    if (row >= N) continue;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 q4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) q4[e] = (__bf16)(dqacc[qb][db][4 * g + e] * sc);
-        *(bf16x4*)(dQ + (size_t)row * D + 32 * db + 8 * g + 4 * h) = q4;
+    // As in the dK/dV pass: uniform branches only, no step skipped in a loop.
+    auto iteration = [&](int t, const char* Ks, const char* Vs, const uint32_t* Ms, char* Kn, char* Vn,
+                         uint32_t* Mn, auto MASK) __attribute__((always_inline)) {
+      wait_vm0();
+      __syncthreads();
+      const int s_cur = stage_of(t);
+      if (t + 1 < n_stages) load_stage(stage_of(t + 1), Kn, Vn, Mn);
+      kstep(s_cur, 0, Ks, Vs, Ms, MASK);
+      kstep(s_cur, 1, Ks, Vs, Ms, MASK);
+    };
+
+    // Stages before n_clean (an even number) are seen whole by every query of
+    // the workgroup: no key past kv_len and, causal, none past the first
+    // query's last key.  The rest are masked element by element.
+    if (n_stages > 0) load_stage(stage_of(0), Ks0, Vs0, Mq0);
+    if constexpr (BITS) {
+      // element mask: every listed stage applies its bits (and the causal,
+      // window and kv_len rules)
+      int t = 0;
+      for (; t + 1 < n_stages; t += 2) {
+        iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
+        iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, std::true_type{});
       }
+      if (t < n_stages) iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
+    } else if constexpr (!WINDOW) {
+      int n_clean = kvl / St::ROWS;
+      if (CAUSAL) n_clean = min(n_clean, q0 + off + 1 > 0 ? (q0 + off + 1) / St::ROWS : 0);
+      n_clean = min(n_clean, n_stages) / 2 * 2;
+      int t = 0;
+      for (; t < n_clean; t += 2) {
+        iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::false_type{});
+        iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, std::false_type{});
+      }
+      for (; t + 1 < n_stages; t += 2) {
+        iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
+        iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, std::true_type{});
+      }
+      if (t < n_stages) iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, std::true_type{});
+    } else {
+      // Window: stages before nA hold keys before the last query's first key,
+      // stages from nC on keys past the first query's last key (or kv_len);
+      // both masked, the stages between are seen whole.  Stage t uses buffer
+      // t % 2.
+      const int nA = clampi(floor_div(q_last + off - wl + St::ROWS - 1, St::ROWS) - t0, 0, n_stages);
+      const int last_all = min(UPPER ? q0 + off + wr : kvl - 1, kvl - 1);  // last key every query sees
+      const int nC = clampi(floor_div(last_all - (St::ROWS - 1), St::ROWS) + 1 - t0, nA, n_stages);
+      auto segment = [&](int t, int t_end, auto MASK) __attribute__((always_inline)) {
+        if ((t & 1) && t < t_end) {
+          iteration(t, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, MASK);
+          ++t;
+        }
+        for (; t + 1 < t_end; t += 2) {
+          iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, MASK);
+          iteration(t + 1, Ks1, Vs1, Mq1, Ks0, Vs0, Mq0, MASK);
+        }
+        if (t < t_end) iteration(t, Ks0, Vs0, Mq0, Ks1, Vs1, Mq1, MASK);
+      };
+      segment(0, nA, std::true_type{});
+      segment(nA, nC, std::false_type{});
+      segment(nC, n_stages, std::true_type{});
+    }
+
+  #pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+  #pragma unroll
+      for (int db = 0; db < DB; ++db) mfma_guard_a(dqacc[qb][db]);
+    // ---- write dQ = scale * (dQ^T)^T ----
+    // Accumulator (qb, db), register r: d = 32 db + 8 (r / 4) + 4 h + r % 4,
+    // query qw0 + 32 qb + l32.
+    __bf16* dQ = (__bf16*)p.dq + (size_t)bh * N * D;
+    const float sc = p.scale;
+  #pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int row = qw0 + 32 * qb + l32;
+      if (row >= N) continue;
+  #pragma unroll
+      for (int db = 0; db < DB; ++db)
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 q4;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) q4[e] = (__bf16)(dqacc[qb][db][4 * g + e] * sc);
+          *(bf16x4*)(dQ + (size_t)row * D + 32 * db + 8 * g + 4 * h) = q4;
+        }
+    }
   }
+  }
+}
+
+// Workgroups of a pass: one per item, or, persistent, at most one per CU (a
+// multiple of the 8 XCDs).
+int64_t persist_grid(int64_t items, bool persistent) {
+  return persistent ? std::min<int64_t>((items + 7) / 8 * 8, kPrefillPersistGrid) : items;
 }
 
 template <int D, bool BITS>
@@ -865,7 +918,7 @@ void launch_bwd_passes(const BwdProblem& p, hipStream_t stream) {
   const dim3 block(kBwdThreads);
   if (p.M > 0) {
     const int n_kt = (p.M + kBwdBlockKV - 1) / kBwdBlockKV;
-    const dim3 grid((unsigned)(bh * n_kt));
+    const dim3 grid((unsigned)persist_grid(bh * n_kt, p.causal && !p.window && !BITS));
     if (p.window) {
       if (p.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true, BITS>), grid, block, 0, stream, p, n_kt);
       else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true, BITS>), grid, block, 0, stream, p, n_kt);
@@ -876,7 +929,7 @@ void launch_bwd_passes(const BwdProblem& p, hipStream_t stream) {
   }
   if (p.N > 0) {
     const int n_qt = (p.N + kBwdBlockQ - 1) / kBwdBlockQ;
-    const dim3 grid((unsigned)(bh * n_qt));
+    const dim3 grid((unsigned)persist_grid(bh * n_qt, p.causal && !p.window && !BITS));
     if (p.window) {
       if (p.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, BITS>), grid, block, 0, stream, p, n_qt);
       else hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, BITS>), grid, block, 0, stream, p, n_qt);

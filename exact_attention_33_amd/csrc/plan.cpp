@@ -37,7 +37,6 @@ int32_t auto_split_keys(const fa_shape& s) {
 
 fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
                     const fa_options* opt, Plan* plan, const char** why) {
-  (void)causal;
   *plan = Plan{};
   if (s.B < 0 || s.H < 0 || s.N < 0 || s.M < 0 || s.D < 0) {
     *why = "B, H, N, M and D must be non-negative";
@@ -205,6 +204,8 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
       plan->threads = kFp8Threads;
       plan->lds_bytes = 4 * 64 * s.D;
       plan->grid = ceil_div(s.N, kFp8BlockQ) * bh;
+      if (causal)  // persistent, as the causal bf16 prefill
+        plan->grid = std::min<int64_t>((plan->grid + 7) / 8 * 8, kPrefillPersistGrid);
       break;
     case FA_PATH_KVOUTER: {
       if ((int64_t)s.M * s.D * 2 > INT32_MAX) {

@@ -237,7 +237,8 @@ def test_kvouter_plan():
 
 def test_fp8_plan():
     p = fa.plan(2, 32, 8192, 8192, 128, fa.FP8, True)
-    assert p["path_name"] == "fp8" and p["threads"] == 512 and p["grid"] == 32 * 64
+    assert p["path_name"] == "fp8" and p["threads"] == 512 and p["grid"] == 256   # persistent
+    assert fa.plan(2, 32, 8192, 8192, 128, fa.FP8, False)["grid"] == 32 * 64
     assert fa.plan(4, 2, 1, 5000, 64, fa.FP8)["path_name"] == "fp8"   # no split-KV for fp8
     for kw, st in ((dict(window=(3, 0)), "FA_ERR_UNSUPPORTED"),
                    (dict(path=fa.PATH_PREFILL), "FA_ERR_UNSUPPORTED"),
