@@ -20,10 +20,12 @@
 //    Q stays in registers as the B operand; one query per lane, 16 keys per
 //    lane per 32-key block, so the row max and row sum are in-lane plus one
 //    swap between half-waves;
-//  * weights against a lazy reference m: m moves to the tile's row max only
-//    when that max exceeds m by more than 8 (log2 units), so every weight is
-//    at most 2^8 and fits E4M3 (largest finite 448); moving m rescales l and
-//    the output accumulator by 2^(m_old - m_new) ("The Correction Factor");
+//  * weights against a lazy reference m with no row max per tile: a lane's
+//    sum of at most 2^8 bounds each of its weights by 2^8, which E4M3 holds
+//    (largest finite 448).  A larger sum, a row with no reference yet, or
+//    (checked only then) a row max more than 8 (log2 units) above m moves m
+//    to that max, rescales l and the output accumulator by 2^(m_old - m_new)
+//    ("The Correction Factor") and forms the tile's weights again;
 //  * O^T += V8^T P8^T: the fp8 weights go straight into the B operand in the
 //    order the score layout hands them over (32 keys per lane), and V8^T
 //    comes from ds_read_b64_tr_b8 transposing reads of V's [key][d] rows;
@@ -244,38 +246,52 @@ void prefill_fp8_kernel(Problem p, int n_qtiles) {
             s[kb2][r] = key > lim ? -INFINITY : s[kb2][r];
           }
       }
-      float mx = -INFINITY;
-  #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
-      mx = swap_halves_max(mx) * c;
-      // move the reference when the tile would give a weight above 2^8
-      const bool move = mx > m_ref + 8.f;
-      if (__builtin_amdgcn_ballot_w64(move)) {
-        const float m_new = move ? mx : m_ref;
-        const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
-        l_run *= alpha;
-  #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        m_ref = m_new;
-      }
-      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      // weights, row sum, fp8 B operand: byte t = 16 kb2 + r
+      // Weights against the current reference with no row max: a lane's sum
+      // of at most 2^8 bounds each of its weights by 2^8 (E4M3 holds them).
+      // A larger sum, or a row with no reference yet, takes the rare path:
+      // such rows, and rows whose tile max exceeds the reference by more than
+      // 8, move it to that max (l and the output accumulator rescaled) and the
+      // weights are formed again.
       i32x8 pf;
       float ps = 0.f;
+      auto weights = [&](float m_use) __attribute__((always_inline)) {
+        ps = 0.f;
   #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int kb2 = w / 4, r0 = 4 * (w % 4);
-        float e[4];
+        for (int w = 0; w < 8; ++w) {
+          const int kb2 = w / 4, r0 = 4 * (w % 4);
+          float e[4];
   #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          e[i] = fast_exp2(fmaf(s[kb2][r0 + i], c, -m_use));
-          ps += e[i];
+          for (int i = 0; i < 4; ++i) {
+            e[i] = fast_exp2(fmaf(s[kb2][r0 + i], c, -m_use));
+            ps += e[i];
+          }
+          int packed = cvt_fp8x2<false>(e[0], e[1], 0);
+          packed = cvt_fp8x2<true>(e[2], e[3], packed);
+          pf[w] = packed;
         }
-        int packed = cvt_fp8x2<false>(e[0], e[1], 0);
-        packed = cvt_fp8x2<true>(e[2], e[3], packed);
-        pf[w] = packed;
+      };
+      weights(m_ref == -INFINITY ? 0.f : m_ref);
+      if (__builtin_amdgcn_ballot_w64(!(ps <= 256.f) || m_ref == -INFINITY)) {
+        float mx = -INFINITY;
+  #pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb2][r]);
+        mx = swap_halves_max(mx) * c;
+        // a row whose sum went over moves up to its max (weights <= 1), so
+        // the following tiles do not come back here; any row moves when its
+        // max is more than 8 above the reference
+        const float over = swap_halves_max(!(ps <= 256.f) ? 1.f : 0.f);
+        const bool move = (over > 0.f && mx > m_ref) || mx > m_ref + 8.f;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+          const float m_new = move ? mx : m_ref;
+          const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
+          l_run *= alpha;
+  #pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+          m_ref = m_new;
+          weights(m_ref == -INFINITY ? 0.f : m_ref);
+        }
       }
       l_run += ps;
       valu8_guard(pf);
