@@ -82,6 +82,13 @@ def lib():
         raise ImportError(
             f"{library_path} is missing: build it with "
             "`python -m exact_attention_33_amd.build` (hipcc, gfx950)")
+    # torch first: the library then binds to the HIP runtime torch already
+    # loaded.  Loaded the other way round, the process holds two runtimes
+    # and the library's launches find no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - the binding needs torch anyway
+        pass
     L = ctypes.CDLL(library_path)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     L.fa_plan_query.argtypes = [Shape, i32, i32, ctypes.POINTER(Options), ctypes.POINTER(PlanInfo)]
