@@ -200,6 +200,30 @@ def pack_mask(allowed):
     return words.to(torch.int32).contiguous()
 
 
+def _torch_stream(stream, dev):
+    """The stream to run on as a torch stream object: the current stream when
+    None, a torch stream as given, or a raw hipStream_t (int) wrapped."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=dev)
+
+
+def _kv_len_arg(kv_len, B, dev):
+    """kv_len as a contiguous int32 device tensor of B entries (or None)."""
+    import torch
+    if kv_len is None:
+        return None
+    if not isinstance(kv_len, torch.Tensor):
+        kv_len = torch.as_tensor(kv_len, dtype=torch.int32)
+    kv_len = kv_len.to(device=dev, dtype=torch.int32).contiguous()
+    if kv_len.numel() != B:
+        raise ValueError("kv_len must have B entries")
+    return kv_len
+
+
 def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
         workspace=None, path=None, split_keys=0, window=None, kvouter_query_tiles=0,
         descale=None, mask=None, stream=None):
@@ -231,31 +255,31 @@ def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
     dev = q.device
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if kv_len is not None:
-        if not isinstance(kv_len, torch.Tensor):
-            kv_len = torch.as_tensor(kv_len, dtype=torch.int32)
-        kv_len = kv_len.to(device=dev, dtype=torch.int32).contiguous()
-        if kv_len.numel() != B:
-            raise ValueError("kv_len must have B entries")
-    if out is None:
-        out = torch.empty((B, H, N, D), dtype=torch.bfloat16 if dt == FP8 else q.dtype, device=dev)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    opts = _options(path, split_keys, window, kvouter_query_tiles, descale,
-                    _mask_arg(mask, B, H, N, M, dev))
-    shape = Shape(B, H, N, M, D)
-    ws_need = int(L.fa_fwd_workspace_bytes(shape, dt, int(bool(causal)), _opt_ptr(opts)))
-    if ws_need and workspace is None:
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    st = L.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                     kv_len.data_ptr() if kv_len is not None else None,
-                     out.data_ptr(), lse.data_ptr(), shape, dt, float(scale),
-                     int(bool(causal)), ws_ptr, ws_len, sptr or None, _opt_ptr(opts))
+    stream = _torch_stream(stream, dev)
+    # Every temporary (the device copy of kv_len, the workspace) and the
+    # outputs are made on the stream the kernels run on, so that the caching
+    # allocator never hands their memory to other work while they are in use.
+    with torch.cuda.stream(stream):
+        kv_len = _kv_len_arg(kv_len, B, dev)
+        if out is None:
+            out = torch.empty((B, H, N, D), dtype=torch.bfloat16 if dt == FP8 else q.dtype,
+                              device=dev)
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        opts = _options(path, split_keys, window, kvouter_query_tiles, descale,
+                        _mask_arg(mask, B, H, N, M, dev))
+        shape = Shape(B, H, N, M, D)
+        ws_need = int(L.fa_fwd_workspace_bytes(shape, dt, int(bool(causal)), _opt_ptr(opts)))
+        if ws_need and workspace is None:
+            workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                kv_len.data_ptr() if kv_len is not None else None,
+                out.data_ptr(), lse.data_ptr(), shape, dt, float(scale),
+                int(bool(causal)), ws_ptr, ws_len, stream.cuda_stream or None)
+        # the plain entry point when no option is set, the extended one otherwise
+        st = L.fa_fwd(*args) if opts is None else L.fa_fwd_ex(*args, _opt_ptr(opts))
     _check(st)
     return out, lse
 
@@ -313,28 +337,23 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_len=None, *, dq=None, 
     dev = q.device
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if kv_len is not None:
-        if not isinstance(kv_len, torch.Tensor):
-            kv_len = torch.as_tensor(kv_len, dtype=torch.int32)
-        kv_len = kv_len.to(device=dev, dtype=torch.int32).contiguous()
-        if kv_len.numel() != B:
-            raise ValueError("kv_len must have B entries")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    shape = Shape(B, H, N, M, D)
-    opts = _options(None, 0, window, mask=_mask_arg(mask, B, H, N, M, dev))
-    need = int(L.fa_bwd_workspace_bytes_ex(shape, dt, int(bool(causal)), _opt_ptr(opts)))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    st = L.fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                     do.data_ptr(), kv_len.data_ptr() if kv_len is not None else None,
-                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), shape, dt, float(scale),
-                     int(bool(causal)), ws_ptr, ws_len, sptr or None, _opt_ptr(opts))
+    stream = _torch_stream(stream, dev)
+    with torch.cuda.stream(stream):  # temporaries and outputs on the kernels' stream
+        kv_len = _kv_len_arg(kv_len, B, dev)
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        shape = Shape(B, H, N, M, D)
+        opts = _options(None, 0, window, mask=_mask_arg(mask, B, H, N, M, dev))
+        need = int(L.fa_bwd_workspace_bytes_ex(shape, dt, int(bool(causal)), _opt_ptr(opts)))
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        st = L.fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         do.data_ptr(), kv_len.data_ptr() if kv_len is not None else None,
+                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), shape, dt, float(scale),
+                         int(bool(causal)), ws_ptr, ws_len, stream.cuda_stream or None,
+                         _opt_ptr(opts))
     _check(st)
     return dq, dk, dv

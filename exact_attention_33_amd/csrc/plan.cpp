@@ -3,12 +3,15 @@
 // The tile sizes follow the counting argument of "FlashAttention: attention
 // was never compute-bound", How big should a tile be?: K and V are re-read
 // once per query tile, so the query tile is the largest that keeps its
-// working set on chip.  On gfx950 the working set lives in registers (Q, the
-// score tile, the output accumulator) and LDS (one K tile and one V tile,
-// 34 KB at D = 128), so two workgroups of 128 queries fit one compute unit.
-// Batch, heads and query tiles are independent ("Understanding
-// FlashAttention", Attention: batch and heads only repeat the problem), so
-// the grid spans all three.
+// working set on chip.  On gfx950 the prefill's working set lives in
+// registers (Q, the score and weight tiles, the output accumulator: one wave
+// of 64 queries per SIMD with all 512 registers) and LDS (a ring of K and V
+// tiles of 64 keys, about 120 KB at D = 128), so a workgroup holds 256
+// queries and one workgroup runs per compute unit.  Batch, heads and query
+// tiles are independent ("Understanding FlashAttention", Attention: batch
+// and heads only repeat the problem), so the grid spans all three; causal
+// attention without a window or mask gets a persistent grid of one
+// workgroup per compute unit that walks the query tiles of its XCD.
 #include <algorithm>
 #include <climits>
 #include <cstdint>

@@ -46,7 +46,7 @@ Readings where the pages leave a step open (each listed in the design notes):
 import numpy as np
 
 __all__ = ["visible_mask", "safe_softmax", "attention_ref", "attention_rows",
-           "attention_probs", "clamp_kv_len", "mask_of_head"]
+           "clamp_kv_len", "mask_of_head"]
 
 
 def clamp_kv_len(kv_len, B, M):
@@ -201,13 +201,3 @@ def attention_rows(q, k, v, scale, causal, kv_len, picks, window=None, mask=None
         outO = np.zeros((0, 0))
     return outO, outL
 
-
-def attention_probs(q, k, scale, causal=False, kv_len_b=None):
-    """The probability matrix P [N, kv_len] of one head (for invariant checks)."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    kvl = k.shape[0] if kv_len_b is None else int(kv_len_b)
-    S = np.where(visible_mask(q.shape[0], kvl, causal),
-                 _scores(q, k[:kvl], scale), -np.inf)
-    return np.stack([safe_softmax(S[r])[0] for r in range(S.shape[0])]) \
-        if S.shape[0] else np.zeros((0, kvl))

@@ -15,29 +15,39 @@ __all__ = ["online_softmax", "online_normalizer", "per_key_attention",
            "tiled_attention", "split_merge_attention"]
 
 
-def online_softmax(row, block=8, rescale=True):
-    """Softmax of ``row`` with the running max m and running sum l.
+def _absorb_block(state, block, correct):
+    """One step of the online normaliser over a block of scores.
 
-    "FlashAttention: attention was never compute-bound", The one formula:
-    each block updates m to max(m, block max) and l to
-    e^(m_old - m_new) * l_old + sum over the block of e^(x - m_new).
-    "Flash Attention: The Hidden Gem", Online Softmax: start from m = -inf,
-    l = 0, and at the end the weights are e^(x - m) / l.
-
-    ``rescale=False`` drops the correction factor on l -- the deliberate bug of
-    the explainer's "Now break it" section.  The final weights are produced
-    with the final m (the second read the pages describe).
+    ``state`` is (m, l): the largest score seen and the running sum of
+    e^(x - m) over the scores seen.  "FlashAttention: attention was never
+    compute-bound", The one formula: the new maximum is the larger of m and
+    the block's maximum, and l becomes e^(m_old - m_new) l + sum of
+    e^(x - m_new) over the block.  ``correct=False`` keeps l as it is instead
+    of multiplying it by e^(m_old - m_new) (the mistake the same page's
+    "Now break it" section makes on purpose).  Starting from (-inf, 0), the
+    factor e^(-inf) is 0 and multiplies an empty sum.
     """
-    x = np.asarray(row, dtype=np.float64)
-    m, l = -np.inf, 0.0
-    for start in range(0, x.size, block):
-        blk = x[start:start + block]
-        m_new = max(m, float(blk.max()))
-        if rescale and l != 0.0:
-            l *= math.exp(m - m_new)        # e^(m_old - m_new) * l_old
-        l += float(np.exp(blk - m_new).sum())
-        m = m_new
-    return np.exp(x - m) / l
+    m_old, l_old = state
+    m_new = max(m_old, float(np.max(block)))
+    factor = math.exp(m_old - m_new) if correct else 1.0
+    return m_new, factor * l_old + float(np.exp(block - m_new).sum())
+
+
+def online_softmax(scores, block_len=8, correct=True):
+    """Softmax of a 1-D score vector from a single streamed sweep.
+
+    The scores are cut into consecutive blocks of ``block_len``; the state
+    (m, l) starts at (-inf, 0) ("Flash Attention: The Hidden Gem", Online
+    Softmax) and absorbs the blocks in order (``_absorb_block``).  A second
+    read then turns every score into e^(x - m) / l with the final m and l.
+    """
+    x = np.asarray(scores, dtype=np.float64).reshape(-1)
+    blocks = [x[a:a + block_len] for a in range(0, x.size, block_len)]
+    state = (-math.inf, 0.0)
+    for blk in blocks:
+        state = _absorb_block(state, blk, correct)
+    m_fin, l_fin = state
+    return np.exp(x - m_fin) / l_fin
 
 
 def online_normalizer(x):
@@ -85,57 +95,80 @@ def per_key_attention(q, k, v, scale=1.0):
     return out
 
 
-def tiled_attention(q, k, v, scale, Br, Bc, causal=False, kv_len=None,
-                    rescale=True):
-    """The tiled forward of one head: Q tiles outside, K/V tiles inside.
+class _RowBlockState:
+    """Running state of one block of query rows: per row the largest visible
+    score m, the sum l of e^(s - m) and the unnormalised output acc, all
+    relative to the same m ("FlashAttention: attention was never
+    compute-bound", The one formula: O is rescaled alongside l because its
+    weights moved)."""
 
-    "Flash Attention: The Hidden Gem", The Algorithm (the FlashAttention-2
-    forward) and The Correction Factor: for each Q tile start from O = 0,
-    l = 0, m = -inf; for each K/V tile form the score tile, take
-    m_new = max(rowmax(S), m_old), P = exp(S - m_new),
-    l = e^(m_old - m_new) l + rowsum(P), O = diag(e^(m_old - m_new)) O + P V;
-    after the last tile O = diag(l)^-1 O and L = m + log(l).
+    def __init__(self, rows, d, correct):
+        self.m = np.full(rows, -np.inf)
+        self.l = np.zeros(rows)
+        self.acc = np.zeros((rows, d))
+        self.correct = correct
 
-    The mask (causal, bottom-right aligned; keys >= kv_len dropped) is applied
-    to each score tile before the max.  A correction e^(-inf - (-inf)) is
-    taken as 0 ("Understanding FlashAttention", What is left to the
-    implementation); a row with no visible key ends with O = 0, L = -inf.
+    def absorb(self, s, v_tile):
+        """Fold in one score tile s [rows, keys] (masked entries -inf) and the
+        matching value rows.  Rows that still see no key keep m = -inf and
+        add nothing; their correction factor is taken as 0 instead of
+        e^(-inf - (-inf)) ("Understanding FlashAttention", What is left to
+        the implementation)."""
+        m_new = np.maximum(self.m, s.max(axis=1))
+        seen = m_new > -np.inf
+        ref = np.where(seen, m_new, 0.0)                 # finite baseline per row
+        w = np.exp(s - ref[:, None])                     # e^(S - m_new); 0 where masked
+        if self.correct:
+            alpha = np.where(self.m > -np.inf, np.exp(self.m - ref), 0.0)
+        else:
+            alpha = np.ones_like(self.l)
+        self.l = alpha * self.l + w.sum(axis=1)
+        self.acc = alpha[:, None] * self.acc + w @ v_tile
+        self.m = m_new
+
+    def finish(self):
+        """O = acc / l and L = m + ln l; rows that saw no key give 0 and -inf
+        ("Flash Attention: The Hidden Gem", The Algorithm, the last step)."""
+        live = self.l > 0
+        O = np.zeros_like(self.acc)
+        L = np.full(self.l.shape, -np.inf)
+        O[live] = self.acc[live] / self.l[live, None]
+        L[live] = self.m[live] + np.log(self.l[live])
+        return O, L
+
+
+def tiled_attention(q, k, v, scale, Br, Bc, causal=False, kv_len=None, correct=True):
+    """The tiled forward of one head: blocks of Br query rows, each sweeping
+    the keys in tiles of Bc.
+
+    "Flash Attention: The Hidden Gem", The Algorithm and The Correction
+    Factor: for every query block and every key tile, form the score tile,
+    move the running maximum, rescale l and the output accumulator by
+    e^(m_old - m_new) and add the tile's weights and weighted values; divide
+    once at the end.  The mask -- keys >= kv_len dropped, and with ``causal``
+    key j visible to query i iff j <= i + (kv_len - N) -- is applied to each
+    score tile before it is absorbed.  ``correct=False`` omits the rescale.
     q [N, D], k/v [M, D]; returns (O [N, D], L [N]).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    N, D = q.shape
-    kvl = k.shape[0] if kv_len is None else int(kv_len)
-    O = np.zeros((N, D))
-    L = np.full(N, -np.inf)
-    for i0 in range(0, N, Br):
-        qi = q[i0:i0 + Br]
-        rows = np.arange(i0, i0 + qi.shape[0])[:, None]
-        acc = np.zeros((qi.shape[0], D))
-        l = np.zeros((qi.shape[0], 1))
-        m = np.full((qi.shape[0], 1), -np.inf)
-        for j0 in range(0, kvl, Bc):
-            kj, vj = k[j0:min(j0 + Bc, kvl)], v[j0:min(j0 + Bc, kvl)]
-            cols = np.arange(j0, j0 + kj.shape[0])[None, :]
-            s = float(scale) * (qi @ kj.T)
+    n_q, d = q.shape
+    n_k = k.shape[0] if kv_len is None else int(kv_len)
+    O = np.zeros((n_q, d))
+    L = np.full(n_q, -np.inf)
+    for r0 in range(0, n_q, Br):
+        r1 = min(r0 + Br, n_q)
+        state = _RowBlockState(r1 - r0, d, correct)
+        qi = np.arange(r0, r1)
+        for c0 in range(0, n_k, Bc):
+            c1 = min(c0 + Bc, n_k)
+            s = float(scale) * (q[r0:r1] @ k[c0:c1].T)
             if causal:
-                s = np.where(cols <= rows + (kvl - N), s, -np.inf)
-            m_new = np.maximum(m, s.max(axis=1, keepdims=True))
-            # rows still without a visible key keep a zero tile
-            base = np.where(m_new == -np.inf, 0.0, m_new)
-            p = np.exp(s - base)
-            if rescale:
-                corr = np.where(m == -np.inf, 0.0, np.exp(m - base))
-                l = corr * l + p.sum(axis=1, keepdims=True)
-                acc = corr * acc + p @ vj
-            else:
-                l = l + p.sum(axis=1, keepdims=True)
-                acc = acc + p @ vj
-            m = m_new
-        ok = (l[:, 0] > 0)
-        O[i0:i0 + qi.shape[0]][ok] = acc[ok] / l[ok]
-        L[i0:i0 + qi.shape[0]][ok] = m[ok, 0] + np.log(l[ok, 0])
+                kj = np.arange(c0, c1)
+                s = np.where(kj[None, :] <= qi[:, None] + (n_k - n_q), s, -np.inf)
+            state.absorb(s, v[c0:c1])
+        O[r0:r1], L[r0:r1] = state.finish()
     return O, L
 
 

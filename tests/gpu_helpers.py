@@ -50,8 +50,15 @@ def sample_picks(B, H, N, n_heads=6, seed=0, extra_rows=6):
     return picks
 
 
+def abi_scale(s):
+    """The scale as the kernels receive it: the C ABI takes a float32, and
+    the oracle is handed that same value, upcast exactly."""
+    return float(np.float32(s))
+
+
 def default_scale(D):
-    return 1.0 / math.sqrt(D)
+    """1/sqrt(D) rounded to float32, the value the C ABI carries."""
+    return abi_scale(1.0 / math.sqrt(D))
 
 
 # ---- backward ----

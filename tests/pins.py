@@ -363,8 +363,8 @@ def pin_p2_online_row(safe_softmax, online_softmax):
     blk = int(g["block"][0][0])
     row = np.random.default_rng(seed).standard_normal(n) * scale
     ordinary = safe_softmax(row)[0]
-    online = online_softmax(row, block=blk)
-    broken = online_softmax(row, block=blk, rescale=False)
+    online = online_softmax(row, block_len=blk)
+    broken = online_softmax(row, block_len=blk, correct=False)
     as_f = lambda key: np.array([float(x) for x in g[key][0]])
     assert np.allclose(ordinary[:6], as_f("correct_first6"), rtol=0, atol=5e-7)
     assert np.allclose(online[:6], as_f("online_first6"), rtol=0, atol=5e-7)

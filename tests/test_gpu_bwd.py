@@ -6,7 +6,6 @@ given.  Each gradient element must lie within twice the elementwise bound
 that ``gpu_helpers.bwd_bound`` derives from the kernels' arithmetic; masked
 keys get exactly zero gradients and rows with no visible key exactly zero dQ.
 """
-import math
 
 import numpy as np
 import pytest
@@ -15,7 +14,7 @@ import exact_attention_33_amd as fa
 from exact_attention_33_amd import inputs
 from oracle.attention import clamp_kv_len
 from oracle.backward import head_backward
-from tests.gpu_helpers import bwd_bound, compare_bwd, host64
+from tests.gpu_helpers import bwd_bound, compare_bwd, default_scale, host64
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +29,7 @@ def _run(B, H, N, M, D, causal, kv_len, seed, device, poison=True, window=None, 
         kvt = torch.tensor(kv_len, dtype=torch.int32, device=device)
         if poison:
             inputs.poison_tail(k, v, kv_len)
-    scale = 1.0 / math.sqrt(D)
+    scale = default_scale(D)
     o, lse = fa.fwd(q, k, v, scale=scale, causal=causal, kv_len=kvt, window=window, mask=words)
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale=scale, causal=causal, kv_len=kvt, window=window,
                         mask=words)

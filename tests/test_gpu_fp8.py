@@ -2,7 +2,6 @@
 factors) against the fp64 oracle run on the exact dequantized inputs
 (descale * E4M3 value), within the elementwise bound derived in
 ``gpu_helpers.fp8_bound``; LSE within 1e-3."""
-import math
 
 import numpy as np
 import pytest
@@ -11,7 +10,7 @@ import torch
 import exact_attention_33_amd as fa
 from exact_attention_33_amd import inputs
 from oracle.attention import attention_ref
-from tests.gpu_helpers import fp8_bound, host64
+from tests.gpu_helpers import default_scale, fp8_bound, host64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -72,7 +71,7 @@ def test_fp8_matches_oracle(case):
     v = torch.randn(B, H, M, D, generator=g, device=DEV)
     (q8, dq), (k8, dk), (v8, dv) = quantize(q), quantize(k), quantize(v)
     kvt = None if kvl is None else torch.tensor(kvl, dtype=torch.int32, device=DEV)
-    scale = 1.0 / math.sqrt(D)
+    scale = default_scale(D)
     o, l = fa.fwd(q8, k8, v8, scale=scale, causal=causal, kv_len=kvt, descale=(dq, dk, dv))
     torch.cuda.synchronize()
     assert o.dtype == torch.bfloat16
@@ -84,7 +83,7 @@ def test_fp8_long_workload_heads():
     w = inputs.WORKLOADS["prefill_long_d128"]
     q, k, v = inputs.qkv_device(w.seed, w.B, w.H, w.N, w.M, w.D, "bf16", torch.device(DEV))
     (q8, dq), (k8, dk), (v8, dv) = quantize(q.float()), quantize(k.float()), quantize(v.float())
-    scale = 1.0 / math.sqrt(w.D)
+    scale = default_scale(w.D)
     o, l = fa.fwd(q8, k8, v8, scale=scale, causal=True, descale=(dq, dk, dv))
     torch.cuda.synchronize()
     for b, h in ((0, 0), (1, 31)):

@@ -17,7 +17,7 @@ import torch
 import exact_attention_33_amd as fa
 from exact_attention_33_amd import inputs
 from oracle.attention import attention_ref, attention_rows
-from tests.gpu_helpers import compare, default_scale, host64, sample_picks
+from tests.gpu_helpers import abi_scale, compare, default_scale, host64, sample_picks
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -112,9 +112,9 @@ def test_mask_f32(causal):
     q, k, v = make(72, 1, 2, 150, 170, 64, "f32")
     allowed = inputs.random_mask(73, 1, 2, 150, 170, 0.4)
     words = fa.pack_mask(torch.from_numpy(allowed).to(DEV))
-    o, l = fa.fwd(q, k, v, scale=0.2, causal=causal, mask=words)
+    o, l = fa.fwd(q, k, v, scale=abi_scale(0.2), causal=causal, mask=words)
     torch.cuda.synchronize()
-    Or, Lr = attention_ref(host64(q), host64(k), host64(v), 0.2, causal, mask=allowed)
+    Or, Lr = attention_ref(host64(q), host64(k), host64(v), abi_scale(0.2), causal, mask=allowed)
     compare(host64(o), host64(l), Or, Lr, "f32", f"f32 mask causal={causal}")
 
 

@@ -15,7 +15,7 @@ import torch
 import exact_attention_33_amd as fa
 from exact_attention_33_amd import inputs
 from oracle.attention import attention_ref, attention_rows
-from tests.gpu_helpers import compare, default_scale, host64, sample_picks
+from tests.gpu_helpers import abi_scale, compare, default_scale, host64, sample_picks
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -62,9 +62,9 @@ def test_window_bf16(case):
 @pytest.mark.parametrize("causal,win", [(True, (7, 0)), (False, (5, 9))])
 def test_window_f32(causal, win):
     q, k, v = make(71, 1, 2, 150, 170, 64, "f32")
-    o, l = fa.fwd(q, k, v, scale=0.2, causal=causal, window=win)
+    o, l = fa.fwd(q, k, v, scale=abi_scale(0.2), causal=causal, window=win)
     torch.cuda.synchronize()
-    Or, Lr = attention_ref(host64(q), host64(k), host64(v), 0.2, causal, window=win)
+    Or, Lr = attention_ref(host64(q), host64(k), host64(v), abi_scale(0.2), causal, window=win)
     compare(host64(o), host64(l), Or, Lr, "f32", f"f32 window {win}")
 
 

@@ -77,7 +77,7 @@ def test_tiled_forward_without_rescale_is_wrong():
     rng = np.random.default_rng(8)
     q, k, v = (rng.standard_normal((64, 16)) * 2, rng.standard_normal((64, 16)),
                rng.standard_normal((64, 16)))
-    O, _ = S.tiled_attention(q, k, v, 1.0, 16, 8, rescale=False)
+    O, _ = S.tiled_attention(q, k, v, 1.0, 16, 8, correct=False)
     Or, _ = A.attention_ref(q[None, None], k[None, None], v[None, None], 1.0)
     assert np.max(np.abs(O - Or[0, 0])) > 1e-2
 
@@ -152,6 +152,30 @@ def test_attention_rows_matches_full():
     Os2, Ls2 = A.attention_rows(lambda b, h: q[b, h], lambda b, h: k[b, h],
                                 lambda b, h: v[b, h], 0.3, True, kvl, picks)
     assert np.array_equal(Os, Os2) and np.array_equal(Ls, Ls2)
+
+
+@pytest.mark.parametrize("window,with_mask", [((5, 0), False), ((3, 2), False), (None, True),
+                                              ((6, 1), True)])
+def test_attention_rows_with_window_and_mask(window, with_mask):
+    """The sampled-row entry under a local window and an element mask equals
+    the matching rows of the whole-tensor definition (the large-size window
+    and mask parity checks rest on this).  The mask is shared over heads
+    (size-1 head axis) so the broadcast path is covered too."""
+    rng = np.random.default_rng(14)
+    B, H, N, M, D = 2, 3, 20, 25, 8
+    q, k, v = (rng.standard_normal((B, H, N, D)), rng.standard_normal((B, H, M, D)),
+               rng.standard_normal((B, H, M, D)))
+    kvl = [25, 13]
+    mask = rng.random((B, 1, N, M)) < 0.6 if with_mask else None
+    O, L = A.attention_ref(q, k, v, 0.3, True, kvl, window=window, mask=mask)
+    picks = [(b, h, i) for b in range(B) for h in range(H) for i in (0, 3, 9, 19)]
+    Os, Ls = A.attention_rows(q, k, v, 0.3, True, kvl, picks, window=window, mask=mask)
+    for r, (b, h, i) in enumerate(picks):
+        assert np.max(np.abs(Os[r] - O[b, h, i])) <= 1e-15
+        assert (np.isneginf(Ls[r]) and np.isneginf(L[b, h, i])) or abs(Ls[r] - L[b, h, i]) <= 1e-15
+    # the window and the mask change the answer on these rows (not a vacuous check)
+    O0, _ = A.attention_ref(q, k, v, 0.3, True, kvl)
+    assert np.max(np.abs(O - O0)) > 1e-3
 
 
 def test_oracle_float32_inputs_upcast_exactly():
