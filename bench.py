@@ -20,9 +20,16 @@ the hot path:
      8 packed documents (a query sees its own document's keys), and an
      unstructured mask keeping each (query, key) pair with probability 1/2
      (every tile applies bits); the tile-list pre-pass is inside the timing;
-     the backward under the 8-document mask is timed beside them.
+     the backward under the 8-document mask is timed beside them;
+  8. the other prefill shapes of the workload list, each on its own tensors:
+     B=1 H=8 N=M=1024 D=64 causal (a latency: one launch is a few
+     microseconds), B=4 H=16 N=M=4096 D=128 causal and non-causal, and
+     B=2 H=32 N=M=8192 D=64 causal (the pages' n=8192, d=64 example).
 Inputs are N(0, 1) drawn on the device from fixed seeds and are resident in
-HBM before timing starts.
+HBM before timing starts.  Beside the long prefill the bench prints the HBM
+bytes that the naive (unfused) computation would move for the same shapes
+under the pages' counting model (score and weight matrices written and read
+back once each, Q, K, V read and O written once), in float32 and bf16.
 
 `value` is the prefill throughput in TFLOP/s with the FLOP convention
 4*B*H*N*M*D, halved for causal; the decode throughput (KV-cache bytes read
@@ -64,7 +71,7 @@ SOURCES = {"prefill": ["prefill_bf16.hip", "device_common.h", "fa_internal.h"],
            "backward": ["bwd_bf16.hip", "device_common.h", "fa_internal.h", "mfma_asm.h"],
            "fp8": ["prefill_fp8.hip", "device_common.h", "fa_internal.h"],
            "kvouter": ["kvouter_bf16.hip", "device_common.h", "fa_internal.h", "mfma_asm.h"]}
-SOURCES["window"] = SOURCES["mask"] = SOURCES["prefill"]
+SOURCES["window"] = SOURCES["mask"] = SOURCES["configs"] = SOURCES["prefill"]
 
 
 def measured_traffic(kind, case=None):
@@ -92,7 +99,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "window", "kvouter",
-                                       "fp8", "mask", "copy"],
+                                       "fp8", "mask", "configs", "copy"],
                     default="all",
                     help="run one leg only (for counter runs); 'copy' runs a plain "
                          "device copy of known size for counter calibration")
@@ -140,6 +147,12 @@ def main():
     do_k = args.only in ("all", "kvouter")
     do_8 = args.only in ("all", "fp8")
     do_m = args.only in ("all", "mask")
+    do_c = args.only in ("all", "configs")
+    # the other prefill shapes: (workload, causal, label)
+    CONFIGS = (("prefill_small", True, "B1_H8_N1024_D64_causal"),
+               ("prefill_mid", True, "B4_H16_N4096_D128_causal"),
+               ("prefill_mid", False, "B4_H16_N4096_D128_noncausal"),
+               ("prefill_long_d64", True, "B2_H32_N8192_D64_causal"))
     KVO = (("tile_per_group", 1), ("head_per_group", 1 << 20))  # 256-query tiles per workgroup
     WINDOWS = (128, 2048)  # keys per query (causal band: window_left = W - 1)
 
@@ -212,6 +225,13 @@ def main():
         dqm, dkm, dvm = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
         wsmb = torch.empty(fa.bwd_workspace_bytes(wp.B, wp.H, wp.N, wp.M, wp.D, mask_shape=(1, 1)),
                            dtype=torch.uint8, device=dev)
+    if do_c:
+        cfg_t = {}
+        for name in sorted({c[0] for c in CONFIGS}):
+            w = inputs.WORKLOADS[name]
+            q_, k_, v_ = inputs.qkv_device(w.seed, w.B, w.H, w.N, w.M, w.D, "bf16", dev)
+            cfg_t[name] = (w, q_, k_, v_, torch.empty_like(q_),
+                           torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev))
     torch.cuda.synchronize()
 
     def main_step(evs=None):
@@ -279,6 +299,14 @@ def main():
                                                lse=lk_, workspace=wsk, path=fa.PATH_KVOUTER,
                                                kvouter_query_tiles=tpg, stream=stream),
                         max(2, args.steps // 4), 1) for name, tpg in KVO} if do_k else {}
+    ms_c = {}
+    if do_c:
+        for name, causal, label in CONFIGS:
+            w, q_, k_, v_, o_, l_ = cfg_t[name]
+            ms_c[label] = timed(lambda w=w, q_=q_, k_=k_, v_=v_, o_=o_, l_=l_, causal=causal:
+                                fa.fwd(q_, k_, v_, scale=1.0 / math.sqrt(w.D), causal=causal,
+                                       out=o_, lse=l_, stream=stream),
+                                args.steps, args.warmup)
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": 1e3 * wall / max(1, args.steps), "higher_is_better": True,
@@ -412,6 +440,29 @@ def main():
         cfg["kvouter"] = {"B": wp.B, "H": wp.H, "N": wp.N, "M": wp.M, "D": wp.D, "causal": True}
         if not (do_p or do_d or do_b or do_w):
             out.update({"value": res["tile_per_group"]["tflops"], "unit": "TFLOP/s"})
+    if do_c:
+        res = {}
+        for name, causal, label in CONFIGS:
+            w = cfg_t[name][0]
+            avg = sum(ms_c[label]) / len(ms_c[label])
+            flop = 4.0 * w.B * w.H * w.N * w.M * w.D / (2.0 if causal else 1.0)
+            tf = flop / (avg * 1e-3) / 1e12
+            res[label] = {"B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "causal": causal,
+                          "seed": w.seed, "ms_mean": avg, "ms_min": min(ms_c[label]),
+                          "ms_median": sorted(ms_c[label])[len(ms_c[label]) // 2],
+                          "tflops": tf, "flop_per_launch": flop,
+                          "roofline": {"bound": "mfma",
+                                       "kernel": f"prefill_bf16_kernel<{w.D}, {str(causal).lower()}, false, false>",
+                                       "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": tf / PEAK_BF16_TFLOPS,
+                                       "traffic": measured_traffic("configs", label)}}
+        res["B1_H8_N1024_D64_causal"]["note"] = (
+            "latency: 32 workgroups (1/8 of the CUs) and a few microseconds per launch; "
+            "the TFLOP/s figure is not a throughput claim")
+        out["configs"] = dict(res, flop_convention="4 B H N M D, halved for causal")
+        cfg["configs"] = {label: name for name, _, label in CONFIGS}
+    if do_p:
+        out["naive_hbm_bytes"] = naive_traffic_report(wp)
     out["config"] = cfg
 
     if not args.no_cpu_baseline and args.only == "all":
@@ -419,8 +470,81 @@ def main():
                                            qd, kd, vd, od, ld, kvl_h, scale_d, wd)
         out["cpu_baseline"]["backward"] = cpu_baseline_bwd(np, qp, kp, vp, gb, dqb, dkb, dvb,
                                                            scale_p, wp)
+        out["cpu_baseline"]["configs"] = cpu_baseline_configs(np, CONFIGS, cfg_t)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def naive_traffic_report(wp):
+    """HBM bytes of the naive (unfused) forward for the long prefill's batch
+    and heads at D = 64 and 128, from the counting model of "FlashAttention:
+    attention was never compute-bound", Where the time actually goes: per
+    head, Q and K read, the n x n score matrix written and read, the weight
+    matrix written and read, V read and O written, i.e. 4 n^2 + 4 n d
+    elements (float32 on the page: 1032 MB per head at n = 8192, d = 64)."""
+    n, heads = wp.N, wp.B * wp.H
+    rep = {"model": "per head (4 n^2 + 4 n d) elements; MiB = 2^20 bytes", "n": n,
+           "heads": heads}
+    for d in (64, 128):
+        elems = 4 * n * n + 4 * n * d
+        for name, size in (("fp32", 4), ("bf16", 2)):
+            rep[f"d{d}_{name}_bytes"] = heads * elems * size
+            rep[f"d{d}_{name}_mib_per_head"] = elems * size / float(1 << 20)
+    return rep
+
+
+def host_description(blas_threads):
+    """The host the oracle runs on: logical CPUs, the CPUs this process may
+    use, BLAS threads and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = None
+    return {"os_cpu_count": os.cpu_count(), "usable_cpus": usable,
+            "blas_threads": blas_threads, "cpu_model": model}
+
+
+def cpu_baseline_configs(np, configs, tensors, heads_per_config=(8, 1, 1, 1)):
+    """The oracle on whole heads of each other prefill shape's tensors (all
+    8 heads of the small one, one head of the others); their outputs are
+    compared with the GPU's (the bench's launches, element by element)."""
+    import torch
+
+    import exact_attention_33_amd as fa
+    from oracle.attention import attention_ref
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    res = {}
+    for (name, causal, label), n_heads in zip(configs, heads_per_config):
+        w, q_, k_, v_, o_, l_ = tensors[name]
+        # the causal and non-causal legs of one shape share o_, l_: launch this
+        # leg once more so that they hold its output
+        fa.fwd(q_, k_, v_, scale=1.0 / math.sqrt(w.D), causal=causal, out=o_, lse=l_)
+        torch.cuda.synchronize()
+        scale = float(np.float32(1.0 / math.sqrt(w.D)))
+        t_cpu, eo, el = 0.0, 0.0, 0.0
+        heads = [divmod(i, w.H) for i in range(n_heads)]
+        for b, h in heads:
+            q, k, v = f64(q_[b, h])[None, None], f64(k_[b, h])[None, None], f64(v_[b, h])[None, None]
+            t0 = time.perf_counter()
+            O, L = attention_ref(q, k, v, scale, causal)
+            t_cpu += time.perf_counter() - t0
+            eo = max(eo, float(np.max(np.abs(f64(o_[b, h]) - O[0, 0]))))
+            el = max(el, float(np.max(np.abs(f64(l_[b, h]) - L[0, 0]))))
+        flop = len(heads) * 4.0 * w.N * w.M * w.D / (2.0 if causal else 1.0)
+        res[label] = {"value": flop / t_cpu / 1e12, "unit": "TFLOP/s", "seconds": t_cpu,
+                      "sample": f"{len(heads)} whole head(s) of this shape's tensors, fp64 NumPy, "
+                                "same FLOP convention",
+                      "parity_vs_gpu": {"O_max_abs": eo, "LSE_max_abs": el, "tol": [2e-2, 1e-3]}}
+    return res
 
 
 def cpu_baseline(args, np, torch, qp, kp, vp, op, lp, scale_p, wp, qd, kd, vd, od, ld, kvl_h,
@@ -434,6 +558,8 @@ def cpu_baseline(args, np, torch, qp, kp, vp, op, lp, scale_p, wp, qd, kd, vd, o
     except Exception:  # pragma: no cover
         blas_threads = None
     f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    # the scales as the C ABI carries them (float32), upcast exactly
+    scale_p, scale_d = float(np.float32(scale_p)), float(np.float32(scale_d))
     rng = np.random.default_rng(0)
     # prefill sample: whole heads (every query row, all keys)
     heads = [(0, 0), (wp.B - 1, wp.H - 1)] + [
@@ -448,7 +574,7 @@ def cpu_baseline(args, np, torch, qp, kp, vp, op, lp, scale_p, wp, qd, kd, vd, o
         el = max(el, float(np.max(np.abs(f64(lp[b, h]) - L[0, 0]))))
     flop = len(heads) * 4.0 * wp.N * wp.M * wp.D / 2.0
     res = {"value": flop / t_cpu / 1e12, "unit": "TFLOP/s", "cores": blas_threads,
-           "kind": "oracle", "seconds": t_cpu,
+           "kind": "oracle", "seconds": t_cpu, "host": host_description(blas_threads),
            "sample": f"{len(heads)} whole heads (N=M=8192, D=128, causal) of the bench's "
                      f"prefill tensors, fp64 NumPy, same FLOP convention",
            "parity_vs_gpu": {"O_max_abs": eo, "LSE_max_abs": el, "tol": [2e-2, 1e-3]}}
@@ -475,6 +601,7 @@ def cpu_baseline_bwd(np, qp, kp, vp, gb, dqb, dkb, dvb, scale_p, wp, heads=((0, 
     """The backward oracle timed on whole heads of the bench's tensors."""
     from oracle.backward import head_backward
     f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)
+    scale_p = float(np.float32(scale_p))  # as the C ABI carries it
     t_cpu, err = 0.0, {"dq": 0.0, "dk": 0.0, "dv": 0.0}
     for b, h in heads:
         q, k, v, g = f64(qp[b, h]), f64(kp[b, h]), f64(vp[b, h]), f64(gb[b, h])

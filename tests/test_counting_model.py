@@ -66,3 +66,20 @@ def test_long_prefill_naive_bytes():
     assert 64 * C.naive_bytes(8192, 64) == 69_256_347_648
     assert 64 * C.naive_bytes(8192, 128, elem=2) == 34_896_609_280
     assert math.isclose(C.attention_flops(8192, 64) / 1e9, 17.179869184)
+
+
+def test_bench_naive_bytes_match_the_counting_model():
+    """The naive-path bytes the bench prints beside the long prefill are the
+    counting model's (float32: 1032 MB per head at n = 8192, d = 64, as the
+    page prints; bf16 half of that)."""
+    import bench
+    from exact_attention_33_amd import inputs
+    from oracle import counting
+    wp = inputs.WORKLOADS["prefill_long_d128"]
+    rep = bench.naive_traffic_report(wp)
+    heads = wp.B * wp.H
+    for d in (64, 128):
+        assert rep[f"d{d}_fp32_bytes"] == heads * counting.naive_bytes(wp.N, d, elem=4)
+        assert rep[f"d{d}_bf16_bytes"] == heads * counting.naive_bytes(wp.N, d, elem=2)
+    assert rep["d64_fp32_mib_per_head"] == 1032.0
+    assert rep["d128_bf16_bytes"] == 34_896_609_280
