@@ -22,11 +22,11 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "plan", "workspace_bytes", "pack_mask", "lib",
+__all__ = ["fwd", "fwd_noalloc", "bwd", "bwd_workspace_bytes", "plan", "workspace_bytes", "pack_mask", "lib",
            "library_path", "FaError",
            "PATH_AUTO", "PATH_PREFILL", "PATH_SPLITKV", "PATH_F32", "PATH_KVOUTER", "PATH_FP8",
            "FP8",
-           "F32", "BF16", "EXPORTS"]
+           "F32", "BF16", "EXPORTS", "NOALLOC_SCRATCH_BYTES"]
 
 F32, BF16, FP8 = 0, 1, 2
 PATH_AUTO, PATH_PREFILL, PATH_SPLITKV, PATH_F32, PATH_KVOUTER, PATH_FP8 = 0, 1, 2, 3, 4, 5
@@ -34,9 +34,13 @@ PATH_NAMES = {PATH_PREFILL: "prefill", PATH_SPLITKV: "splitkv", PATH_F32: "f32",
               PATH_KVOUTER: "kvouter", PATH_FP8: "fp8"}
 
 # Every symbol include/fa_mi355x.h declares.
-EXPORTS = ["fa_plan_query", "fa_fwd_workspace_bytes", "fa_fwd", "fa_fwd_ex",
+EXPORTS = ["fa_plan_query", "fa_fwd_workspace_bytes", "fa_fwd", "fa_fwd_ex", "fa_fwd_noalloc",
            "fa_bwd_workspace_bytes", "fa_bwd_workspace_bytes_ex", "fa_bwd", "fa_bwd_ex",
            "fa_status_str", "fa_last_error", "fa_abi_version"]
+
+# Bytes of the library's static scratch behind fa_fwd_noalloc
+# (FA_NOALLOC_SCRATCH_BYTES in include/fa_mi355x.h).
+NOALLOC_SCRATCH_BYTES = 48 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "lib", "libfa_mi355x.so")
@@ -100,6 +104,8 @@ def lib():
     L.fa_fwd.restype = i32
     L.fa_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(Options)]
     L.fa_fwd_ex.restype = i32
+    L.fa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, Shape, i32, f32, i32, vp]
+    L.fa_fwd_noalloc.restype = i32
     L.fa_bwd_workspace_bytes.argtypes = [Shape, i32, i32]
     L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.fa_bwd_workspace_bytes_ex.argtypes = [Shape, i32, i32, ctypes.POINTER(Options)]
@@ -280,6 +286,35 @@ def fwd(q, k, v, scale=None, causal=False, kv_len=None, *, out=None, lse=None,
                 int(bool(causal)), ws_ptr, ws_len, stream.cuda_stream or None)
         # the plain entry point when no option is set, the extended one otherwise
         st = L.fa_fwd(*args) if opts is None else L.fa_fwd_ex(*args, _opt_ptr(opts))
+    _check(st)
+    return out, lse
+
+
+def fwd_noalloc(q, k, v, scale=None, causal=False, kv_len=None, *, out, lse, stream=None):
+    """The forward through fa_fwd_noalloc: no workspace, the library's static
+    scratch instead.  For callers that cannot allocate, so the outputs must
+    be given and ``kv_len`` must be None or an int32 device tensor of B
+    entries (nothing is allocated or copied here)."""
+    import torch
+    L = lib()
+    B, H, N, D = q.shape
+    M = k.shape[2]
+    if tuple(k.shape) != (B, H, M, D) or tuple(v.shape) != (B, H, M, D):
+        raise ValueError("k and v must be [B, H, M, D] matching q [B, H, N, D]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if kv_len is not None and (not isinstance(kv_len, torch.Tensor) or not kv_len.is_cuda
+                               or kv_len.dtype != torch.int32 or kv_len.numel() != B
+                               or not kv_len.is_contiguous()):
+        raise ValueError("kv_len must be None or a contiguous int32 device tensor of B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    stream = _torch_stream(stream, q.device)
+    st = L.fa_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          kv_len.data_ptr() if kv_len is not None else None, out.data_ptr(),
+                          lse.data_ptr(), Shape(B, H, N, M, D), _dtype_code(q), float(scale),
+                          int(bool(causal)), stream.cuda_stream or None)
     _check(st)
     return out, lse
 

@@ -19,7 +19,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["shim.cpp", "plan.cpp", "prefill_bf16.hip", "fwd_f32.hip", "decode_bf16.hip",
            "bwd_bf16.hip", "kvouter_bf16.hip",
-           "prefill_fp8.hip"]
+           "prefill_fp8.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions are switched off for device code (the host pass

@@ -176,4 +176,8 @@ inline int bwd_dq_lds_bytes(int D) { return 2 * (2 * kBwdStageK * bwd_lds_row_by
 
 hipError_t launch_bwd_bf16(const BwdProblem& p, hipStream_t stream);
 
+// Records a failure for fa_last_error() on the calling thread (printf-style
+// detail) and returns `st`; shared by every C entry point.
+fa_status report_error(fa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 }  // namespace fa

@@ -13,11 +13,16 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
+fa_status vfail(fa_status st, const char* fmt, va_list ap) {
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  return st;
+}
+
 fa_status fail(fa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 fa_status fail(fa_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  vfail(st, fmt, ap);
   va_end(ap);
   return st;
 }
@@ -25,6 +30,14 @@ fa_status fail(fa_status st, const char* fmt, ...) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
+
+fa_status fa::report_error(fa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(st, fmt, ap);
+  va_end(ap);
+  return st;
+}
 
 extern "C" {
 

@@ -28,8 +28,9 @@
  *
  * Memory and ownership.  Every pointer argument except `stream` is a device
  * pointer on the current HIP device.  The caller allocates and frees every
- * buffer, including the workspace; the library allocates nothing, holds no
- * device state, never synchronises and never copies to the host.  Calls are
+ * buffer, including the workspace; the library allocates nothing, never
+ * synchronises and never copies to the host, and it holds no device state
+ * except the static scratch of fa_fwd_noalloc (below).  Calls are
  * enqueued on `stream` (NULL = the default stream) and return at once; the
  * outputs are ready when the stream reaches that point.  Functions are
  * reentrant and never throw across the ABI.
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 /* FA_FP8: OCP E4M3 (finite max 448, no infinities) Q, K, V with per-tensor
  * descale factors (fa_options); O is then bf16 and LSE float32. */
@@ -177,6 +178,33 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v,
                     fa_shape s, fa_dtype dtype, float scale, int causal,
                     void* workspace, size_t workspace_bytes, void* stream,
                     const fa_options* opt);
+
+/*
+ * fa_fwd_noalloc -- fa_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same computation, arguments, checks and errors as fa_fwd
+ * with no options, without the workspace arguments: the workspace fa_fwd
+ * would take (the split-KV path's partial results) comes from a static
+ * device array of FA_NOALLOC_SCRATCH_BYTES inside the library.  Each GPU
+ * the library runs on holds its own copy from the library's load until the
+ * process ends; on the first call on a device its address is resolved
+ * (hipGetSymbolAddress, with that device current) and kept.  The call makes
+ * no hipMalloc, hipFree or other allocating call.
+ * Limit: a shape whose fa_fwd_workspace_bytes(s, dtype, causal, NULL)
+ * exceeds FA_NOALLOC_SCRATCH_BYTES is rejected with FA_ERR_WORKSPACE before
+ * anything is enqueued (the split-KV decode of B * H * ceil(M / 512) splits
+ * at D = 128 needs about 516 bytes per split; 48 MiB hold 97,000 splits,
+ * e.g. B = 32, H = 32, M = 48,000).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero: the kernels write every
+ * partial result they later read).  Calls that overlap on one GPU -- on two
+ * streams, or from two threads without ordering -- race on the array: the
+ * caller must order them.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+fa_status fa_fwd_noalloc(const void* q, const void* k, const void* v,
+                         const int32_t* kv_len, void* o, float* lse,
+                         fa_shape s, fa_dtype dtype, float scale, int causal, void* stream);
 
 /*
  * ---- Backward ----

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
     assert sorted(fa.EXPORTS) == declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.fa_abi_version() == 6
+    assert L.fa_abi_version() == 7
 
 
 def test_status_strings():
@@ -329,3 +329,23 @@ def test_pack_mask_layout():
         padded[..., :M] = a
         want = np.packbits(padded, axis=-1, bitorder="little").view("<u4")
         assert got.shape == (2, 3, 5, W) and np.array_equal(got, want), M
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """fa_fwd_noalloc turns away a shape whose workspace exceeds the static
+    scratch with FA_ERR_WORKSPACE and a message naming both sizes, before any
+    device call (this runs without a GPU).  The limit is the header's."""
+    L = fa.lib()
+    src = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.NOALLOC_SCRATCH_BYTES
+    # split-KV decode: 32 x 32 heads, 2^20 keys -> 2048 splits each, far above 48 MiB
+    shape = (32, 32, 1, 1 << 20, 128)
+    need = fa.workspace_bytes(*shape)
+    assert need > fa.NOALLOC_SCRATCH_BYTES
+    st = L.fa_fwd_noalloc(P, P, P, None, P, P, Shape(*shape), fa.BF16, 0.1, 0, None)
+    assert L.fa_status_str(st).decode() == "FA_ERR_WORKSPACE"
+    msg = L.fa_last_error().decode()
+    assert str(need) in msg and str(fa.NOALLOC_SCRATCH_BYTES) in msg
+    # the largest decode cache the header quotes fits
+    assert fa.workspace_bytes(32, 32, 1, 48000, 128) <= fa.NOALLOC_SCRATCH_BYTES
