@@ -391,7 +391,7 @@ def main():
                          "visible_fraction_of_causal": pairs_m[name] / (wp.N * (wp.N + 1) / 2),
                          "speedup_vs_unmasked_causal": ((sum(ms_p) / len(ms_p)) / avg) if do_p else None,
                          "roofline": {"bound": "mfma",
-                                      "kernel": "mask_tiles_kernel + prefill_bf16_kernel<128, true, false, true>",
+                                      "kernel": "mask_blocks_kernel + mask_lists_kernel + prefill_bf16_kernel<128, true, false, true>",
                                       "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                       "frac": tf / PEAK_BF16_TFLOPS,
                                       "traffic": measured_traffic("mask", name)}}

@@ -17,7 +17,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libfa_mi355x.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["shim.cpp", "plan.cpp", "prefill_bf16.hip", "fwd_f32.hip", "decode_bf16.hip",
+SOURCES = ["shim.cpp", "plan.cpp", "prefill_bf16.hip", "mask_prep.hip", "fwd_f32.hip", "decode_bf16.hip",
            "bwd_bf16.hip", "kvouter_bf16.hip",
            "prefill_fp8.hip", "noalloc.hip"]
 

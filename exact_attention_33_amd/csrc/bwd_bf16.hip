@@ -112,61 +112,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rowstat_kernel(BwdProblem p, 
 }
 
 // ---------------------------------------------------------------------------
-// Stage lists of an element mask for pass 2: one workgroup per (mask batch,
-// mask head, 256-key tile).  Wave w classifies query stages w, w + 4, ...
-// (lane = row) by OR and AND over the 8 words of the tile's keys (bits of
-// keys >= M and rows >= N do not count); wave 0 then compacts the stages
-// that keep some key, ascending, bit 31 set where the stage does not keep
-// the whole tile.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void mask_stages_kernel(const uint32_t* __restrict__ mask, int N,
-                                                          int M, int W, int n_ktiles, int stride,
-                                                          int32_t* __restrict__ lists) {
-  const int g = blockIdx.x, kt = g % n_ktiles;
-  const int64_t mbh = g / n_ktiles;
-  const uint32_t* rows = mask + (size_t)mbh * N * W;
-  const int n_st = stride - 1;
-  int32_t* L = lists + (size_t)g * stride;
-  __shared__ signed char cls[kMaskMaxTiles];  // 0: no key kept; 1: all; -1: some
-  const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
-  const int w0 = kt * (kBwdBlockKV / 32);     // the tile's first word
-  for (int st = wv; st < n_st; st += 4) {
-    const int r = st * kBwdStageQ + lane;
-    bool any = false, all = true;
-    if (r < N) {
-      uint32_t o = 0u, a = ~0u;
-#pragma unroll
-      for (int w = 0; w < kBwdBlockKV / 32; ++w) {
-        const int n = min(max(M - (w0 + w) * 32, 0), 32);
-        const uint32_t v = n == 32 ? ~0u : (1u << n) - 1u;  // keys < M of the word
-        const uint32_t x = w0 + w < W ? rows[(size_t)r * W + w0 + w] : 0u;
-        o |= x & v;
-        a &= x | ~v;
-      }
-      any = o != 0u;
-      all = a == ~0u;
-    }
-    const bool st_any = __builtin_amdgcn_ballot_w64(any) != 0;
-    const bool st_all = __builtin_amdgcn_ballot_w64(!all) == 0;
-    if (lane == 0) cls[st] = st_any ? (st_all ? 1 : -1) : 0;
-  }
-  __syncthreads();
-  if (wv == 0) {
-    int base = 0;
-    for (int c = 0; c < n_st; c += 64) {
-      const int st = c + lane;
-      const int k = st < n_st ? cls[st] : 0;
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(k != 0);
-      if (k != 0)
-        L[1 + base + __builtin_popcountll(bal & ((1ull << lane) - 1ull))] =
-            k > 0 ? st : (int32_t)((uint32_t)st | 0x80000000u);
-      base += __builtin_popcountll(bal);
-    }
-    if (lane == 0) L[0] = base;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Pass 2: dK and dV.  Workgroup = 4 waves x 64 keys; query stages of 64.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool WINDOW, bool BITS>
@@ -252,22 +197,24 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
       const int stride = mask_stage_stride(N);
       const int32_t* L = p.stage_lists + ((int64_t)(bm * p.mask_h + hm) * n_ktiles + kt) * stride;
       const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
-      for (int i = tid; i < cnt; i += kBwdThreads) tlist[i] = L[1 + i] & 0x7FFFFFFF;
+      for (int i = tid; i < cnt; i += kBwdThreads) tlist[i] = L[1 + i];
       __syncthreads();
       int below_lo = 0, below_hi = 0;
       for (int i0 = 0; i0 < cnt; i0 += 64) {
-        const int e = i0 + lane < cnt ? tlist[i0 + lane] : 0x7FFFFFFF;
+        const int e = i0 + lane < cnt ? (tlist[i0 + lane] & 0x7FFFFFFF) : 0x7FFFFFFF;
         below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < s_lo));
         below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < s_lo + n_stages));
       }
       lo = __builtin_amdgcn_readfirstlane(below_lo);
       n_stages = __builtin_amdgcn_readfirstlane(below_hi) - lo;
     }
-    // query stage of the t-th visited stage
-    auto stage_of = [&](int t) -> int {
+    // List entry of the t-th visited stage (bit 31 set where the mask does
+    // not keep the whole tile), and its query stage.
+    auto entry_of = [&](int t) -> int {
       if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + t]);
       else return s_lo + t;
     };
+    auto stage_of = [&](int t) -> int { return entry_of(t) & 0x7FFFFFFF; };
 
     // ---- K and V fragments of the wave's keys (B operands), zero past kv_len ----
     bf16x8 kf[KBW][DK], vf[KBW][DK];
@@ -291,15 +238,21 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
     // Lane l of wave 0's extra block: Lg (l < 16) or D (16 <= l < 32) chunk.
     const uint32_t loff = (uint32_t)((lane < 16 ? lane : (lane < 32 ? p.Npad / 4 + lane - 16 : 0)) * 16);
     // Element mask: wave ws loads words 2 ws and 2 ws + 1 of the workgroup's
-    // 256 keys for the stage's 64 rows (lane = row; rows past N read row N - 1).
+    // 256 keys for the stage's 64 rows (lane = row) from the stage's block,
+    // where the pre-pass stored them [word][row] (rows past N copy row N - 1):
+    // 256 contiguous bytes per wave and word.  A stage the mask keeps whole
+    // reads the key tile's all-ones block (block 0; stage s has block s + 1),
+    // every lane the same word, so the wave touches one line.
     const uint32_t* Mg = nullptr;
     int mbytes = 0;
     if constexpr (BITS) {
       const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
-      Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
-      mbytes = N * p.mask_w * 4;
+      const int n_st = mask_stage_stride(N) - 1;
+      Mg = p.stage_blocks + ((size_t)(bm * p.mask_h + hm) * n_ktiles + kt) * (n_st + 1) * (kMaskBlockBytes / 4);
+      mbytes = (n_st + 1) * kMaskBlockBytes;
     }
-    auto load_stage = [&](int s, char* Qd, char* Gd, float* Ld, uint32_t* Md) __attribute__((always_inline)) {
+    auto load_stage = [&](int e, char* Qd, char* Gd, float* Ld, uint32_t* Md) __attribute__((always_inline)) {
+      const int s = e & 0x7FFFFFFF;
       const uint32_t rb = (uint32_t)s * St::ROWS * 2 * D;
   #pragma unroll
       for (int i = 0; i < St::BPW; ++i) {
@@ -311,13 +264,13 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
       if (ws == 0)
         buffer_load_lds16(Wg + s * St::ROWS, (int)((2 * p.Npad - s * St::ROWS) * 4), loff, (lds_ptr)Ld);
       if constexpr (BITS) {
-        const uint32_t row = (uint32_t)min(s * St::ROWS + lane, N - 1);
   #pragma unroll
         for (int w = 0; w < 2; ++w) {
           int mofs = (2 * ws + w) * 64;
           asm volatile("" : "+s"(mofs));
-          buffer_load_lds4(Mg, mbytes, (row * (uint32_t)p.mask_w + (uint32_t)(k0 / 32 + 2 * ws + w)) * 4u,
-                           (lds_ptr)(Md + mofs));
+          const uint32_t at = ((uint32_t)(s + 1) * (uint32_t)kMaskBlockBytes + (uint32_t)(mofs + lane) * 4u) &
+                              (uint32_t)(e >> 31);  // whole: every lane reads word 0 of the all-ones block
+          buffer_load_lds4<true>(Mg, mbytes, at, (lds_ptr)(Md + mofs));
         }
       }
     };
@@ -470,12 +423,12 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
       wait_vm0();
       __syncthreads();
       const int s_cur = stage_of(t);
-      if (t + 1 < n_stages) load_stage(stage_of(t + 1), Qn, Gn, Ln, Mn);
+      if (t + 1 < n_stages) load_stage(entry_of(t + 1), Qn, Gn, Ln, Mn);
       qstep(s_cur, 0, Qs, Gs, Ls, Ms, MASK);
       qstep(s_cur, 1, Qs, Gs, Ls, Ms, MASK);
     };
 
-    if (n_stages > 0) load_stage(stage_of(0), Qs0, Gs0, Ls0, Ms0);
+    if (n_stages > 0) load_stage(entry_of(0), Qs0, Gs0, Ls0, Ms0);
     if constexpr (BITS) {
       // element mask: every listed stage applies its bits (and the causal
       // and window rules)
@@ -644,22 +597,24 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
       const int stride = mask_list_stride(M);
       const int32_t* L = p.lists + ((int64_t)(bm * p.mask_h + hm) * n_qtiles + qt) * stride;
       const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
-      for (int i = tid; i < cnt; i += kBwdThreads) tlist[i] = L[1 + i] & 0x7FFFFFFF;
+      for (int i = tid; i < cnt; i += kBwdThreads) tlist[i] = L[1 + i];
       __syncthreads();
       int below_lo = 0, below_hi = 0;
       for (int i0 = 0; i0 < cnt; i0 += 64) {
-        const int e = i0 + lane < cnt ? tlist[i0 + lane] : 0x7FFFFFFF;
+        const int e = i0 + lane < cnt ? (tlist[i0 + lane] & 0x7FFFFFFF) : 0x7FFFFFFF;
         below_lo += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t0));
         below_hi += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < t0 + n_stages));
       }
       lo = __builtin_amdgcn_readfirstlane(below_lo);
       n_stages = __builtin_amdgcn_readfirstlane(below_hi) - lo;
     }
-    // key stage of the t-th visited stage
-    auto stage_of = [&](int t) -> int {
+    // List entry of the t-th visited stage (bit 31 set where the mask does
+    // not keep the whole tile), and its key stage.
+    auto entry_of = [&](int t) -> int {
       if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + t]);
       else return t0 + t;
     };
+    auto stage_of = [&](int t) -> int { return entry_of(t) & 0x7FFFFFFF; };
 
     const __bf16* Qg = (const __bf16*)p.q + (size_t)bh * N * D;
     const __bf16* Gg = (const __bf16*)p.dout + (size_t)bh * N * D;
@@ -694,23 +649,29 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
     for (int i = 0; i < St::BPW; ++i) soff[i] = St::slot_src((ws + i * NW) * 64 + lane);
     const int nrec_k = kvl * 2 * D;  // the planner keeps M * D * 2 below 2^31
     // Element mask: words 2 s and 2 s + 1 of the wave's 64 query rows (lane =
-    // row; rows past N read row N - 1).
+    // row) from the (query tile, key stage) block, stored by the pre-pass as
+    // the forward's (rows past N copy row N - 1): 256 contiguous bytes per
+    // wave and word.  A stage the mask keeps whole reads the query tile's
+    // all-ones block (block 0; stage s has block s + 1), every lane the same
+    // word, so the wave touches one line.
     const uint32_t* Mg = nullptr;
     int mbytes = 0;
-    uint32_t mrow = 0;
     if constexpr (BITS) {
       const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
-      Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
-      mbytes = N * p.mask_w * 4;
-      mrow = (uint32_t)min(qw0 + lane, N - 1) * (uint32_t)p.mask_w;
+      const int n_kt = mask_list_stride(M) - 1;
+      Mg = p.blocks + ((size_t)(bm * p.mask_h + hm) * n_qtiles + qt) * (n_kt + 1) * (kMaskBlockBytes / 4);
+      mbytes = (n_kt + 1) * kMaskBlockBytes;
     }
-    auto load_stage = [&](int s, char* Kd, char* Vd, uint32_t* Md) __attribute__((always_inline)) {
+    auto load_stage = [&](int e, char* Kd, char* Vd, uint32_t* Md) __attribute__((always_inline)) {
+      const int s = e & 0x7FFFFFFF;
       if constexpr (BITS) {
   #pragma unroll
         for (int w = 0; w < 2; ++w) {
           int mofs = ws * 128 + w * 64;
           asm volatile("" : "+s"(mofs));
-          buffer_load_lds4(Mg, mbytes, (mrow + 2u * (uint32_t)s + (uint32_t)w) * 4u, (lds_ptr)(Md + mofs));
+          const uint32_t at = ((uint32_t)(s + 1) * (uint32_t)kMaskBlockBytes + (uint32_t)(mofs + lane) * 4u) &
+                              (uint32_t)(e >> 31);  // whole: every lane reads word 0 of the all-ones block
+          buffer_load_lds4<true>(Mg, mbytes, at, (lds_ptr)(Md + mofs));
         }
       }
       const uint32_t rb = (uint32_t)s * St::ROWS * 2 * D;
@@ -823,7 +784,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
       wait_vm0();
       __syncthreads();
       const int s_cur = stage_of(t);
-      if (t + 1 < n_stages) load_stage(stage_of(t + 1), Kn, Vn, Mn);
+      if (t + 1 < n_stages) load_stage(entry_of(t + 1), Kn, Vn, Mn);
       kstep(s_cur, 0, Ks, Vs, Ms, MASK);
       kstep(s_cur, 1, Ks, Vs, Ms, MASK);
     };
@@ -831,7 +792,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
     // Stages before n_clean (an even number) are seen whole by every query of
     // the workgroup: no key past kv_len and, causal, none past the first
     // query's last key.  The rest are masked element by element.
-    if (n_stages > 0) load_stage(stage_of(0), Ks0, Vs0, Mq0);
+    if (n_stages > 0) load_stage(entry_of(0), Ks0, Vs0, Mq0);
     if constexpr (BITS) {
       // element mask: every listed stage applies its bits (and the causal,
       // window and kv_len rules)
@@ -951,13 +912,10 @@ hipError_t launch_bwd_d(const BwdProblem& p, hipStream_t stream) {
   if (p.mask) {
     // the dQ pass's tile lists (the forward's) and the dK/dV pass's stage
     // lists, then both passes with bits
-    if (p.N > 0) launch_mask_tiles(p.mask, p.N, p.M, p.mask_w, p.mask_b, p.mask_h, p.lists, stream);
-    if (p.M > 0) {
-      const int n_kt = (p.M + kBwdBlockKV - 1) / kBwdBlockKV;
-      hipLaunchKernelGGL(mask_stages_kernel, dim3((unsigned)((int64_t)p.mask_b * p.mask_h * n_kt)),
-                         dim3(256), 0, stream, p.mask, p.N, p.M, p.mask_w, n_kt,
-                         mask_stage_stride(p.N), p.stage_lists);
-    }
+    const fa_shape s{p.B, p.H, p.N, p.M, p.D};
+    launch_mask_prep(p.mask, p.N, p.M, p.mask_w, p.mask_b, p.mask_h, p.ws,
+                     mask_workspace(p.N, p.M, p.mask_b, p.mask_h, bwd_mask_lists_offset(s), true), true,
+                     stream);
     launch_bwd_passes<D, true>(p, stream);
   } else {
     launch_bwd_passes<D, false>(p, stream);

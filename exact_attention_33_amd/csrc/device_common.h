@@ -98,12 +98,15 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, int nbytes, 
 }
 
 // 4 bytes per lane from base + voff into LDS at dst + 4 * lane, as above.
+// STREAM marks the load non-temporal (data read once, so it should not push
+// reused lines out of L2).
+template <bool STREAM = false>
 __device__ __forceinline__ void buffer_load_lds4(const void* base, int nbytes, uint32_t voff,
                                                  lds_ptr dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags), dst,
-      4, voff, 0, 0, 0);
+      4, voff, 0, 0, STREAM ? 2 : 0);
 #endif
 }
 

@@ -62,10 +62,6 @@ hipError_t launch_splitkv_bf16(const Problem& p, const Plan& plan, void* workspa
 hipError_t launch_kvouter_bf16(const Problem& p, const Plan& plan, void* workspace,
                                hipStream_t stream);
 hipError_t launch_prefill_fp8(const Problem& p, const Plan& plan, hipStream_t stream);
-// Tile lists of an element mask (layout below), one per (mask batch, mask
-// head, 256-query tile), into `lists`.
-void launch_mask_tiles(const uint32_t* mask, int N, int M, int mask_w, int mask_b, int mask_h,
-                       int32_t* lists, hipStream_t stream);
 
 // Tile constants shared by the planner and the kernels.
 constexpr int kPrefillBlockQ = 256;   // 4 waves x 64 queries
@@ -83,6 +79,14 @@ constexpr int kPrefillPersistGrid = 256;
 constexpr int kMaskMaxTiles = 4096;
 __host__ __device__ inline int32_t mask_list_stride(int M) { return (M + kPrefillBlockK - 1) / kPrefillBlockK + 1; }
 __host__ __device__ inline int32_t mask_words(int M) { return (M + 31) / 32; }
+// Mask words of one (query tile, key tile) pair, copied by the pre-pass into
+// a contiguous block so that each wave reads its rows' words with one
+// coalesced load: 256 rows x 2 words, stored [wave][word][row of the wave]
+// (2 KB).  The dK/dV pass's blocks hold one (256-key tile, 64-query stage)
+// pair: 64 rows x 8 words, stored [word][row] (2 KB).  Only pairs the mask
+// keeps in part have a block (tile t: block t + 1 of its row of blocks);
+// block 0 of each row is all ones and stands for the pairs kept whole.
+constexpr int kMaskBlockBytes = 2048;
 
 constexpr int kF32BlockQ = 16;        // 16 query rows x 16 lanes
 constexpr int kF32BlockK = 32;
@@ -129,12 +133,14 @@ struct BwdProblem {
   int window;            // as in Problem
   int32_t wl, wr;
   // Element mask, as in Problem (nullptr: none); with a mask the workspace
-  // continues, at byte offset bwd_mask_lists_offset, with the tile lists of
-  // the dQ pass (the forward's lists).
+  // continues, at byte offset bwd_mask_lists_offset, with the pre-pass
+  // output (mask_workspace with stages).
   const uint32_t* mask;
   int32_t mask_b, mask_h, mask_w;
   int32_t* lists;        // dQ pass: per 256-query tile, the key stages (64 keys)
   int32_t* stage_lists;  // dK/dV pass: per 256-key tile, the query stages (64 queries)
+  const uint32_t* blocks;        // dQ pass: words of each listed (query tile, key stage)
+  const uint32_t* stage_blocks;  // dK/dV pass: words of each listed (key tile, query stage)
 };
 
 constexpr int kBwdThreads = 256;
@@ -153,21 +159,39 @@ inline size_t bwd_mask_lists_offset(const fa_shape& s) { return (bwd_stats_bytes
 // count and then the ascending 64-query stages in which some query keeps
 // one of the tile's keys.
 __host__ __device__ inline int32_t mask_stage_stride(int N) { return (N + kBwdStageQ - 1) / kBwdStageQ + 1; }
-inline size_t bwd_lists_bytes(const fa_shape& s, int mask_b, int mask_h) {
-  const size_t n = (size_t)mask_b * (size_t)mask_h * (size_t)((s.N + kBwdBlockQ - 1) / kBwdBlockQ) *
-                   (size_t)mask_list_stride(s.M) * sizeof(int32_t);
-  return (n + 255) / 256 * 256;
-}
-inline size_t bwd_stage_lists_bytes(const fa_shape& s, int mask_b, int mask_h) {
-  const size_t n = (size_t)mask_b * (size_t)mask_h * (size_t)((s.M + kBwdBlockKV - 1) / kBwdBlockKV) *
-                   (size_t)mask_stage_stride(s.N) * sizeof(int32_t);
-  return (n + 255) / 256 * 256;
+
+// Byte offsets of the element-mask pre-pass output in a workspace, from
+// `base`: the forward's tile lists (per mask batch, mask head and 256-query
+// tile: mask_list_stride(M) int32), with stages the dK/dV pass's stage lists
+// (per 256-key tile: mask_stage_stride(N) int32); then one class byte per
+// (query tile, 64-key tile) (0: no key kept, 1: all, 2: some) and per query
+// tile a row of 1 + ceil(M / 64) blocks; with stages, one class byte per
+// (256-key tile, 64-query stage) and per key tile a row of 1 + ceil(N / 64)
+// blocks.  Every region starts on 256 bytes.
+struct MaskWorkspace {
+  size_t lists, stage_lists, cls, blocks, stage_cls, stage_blocks, end;
+};
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+inline MaskWorkspace mask_workspace(int N, int M, int mask_b, int mask_h, size_t base, bool stages) {
+  const size_t mbh = (size_t)mask_b * (size_t)mask_h;
+  const size_t n_qt = (size_t)((N + kPrefillBlockQ - 1) / kPrefillBlockQ);
+  const size_t n_kt = (size_t)(mask_list_stride(M) - 1);
+  const size_t n_kt256 = (size_t)((M + kBwdBlockKV - 1) / kBwdBlockKV);
+  const size_t n_st = (size_t)(mask_stage_stride(N) - 1);
+  MaskWorkspace w{};
+  w.lists = base;
+  w.stage_lists = align256(w.lists + mbh * n_qt * (n_kt + 1) * sizeof(int32_t));
+  w.cls = stages ? align256(w.stage_lists + mbh * n_kt256 * (n_st + 1) * sizeof(int32_t)) : w.stage_lists;
+  w.blocks = align256(w.cls + mbh * n_qt * n_kt);
+  w.stage_cls = align256(w.blocks + mbh * n_qt * (n_kt + 1) * kMaskBlockBytes);
+  w.stage_blocks = stages ? align256(w.stage_cls + mbh * n_kt256 * n_st) : w.stage_cls;
+  w.end = stages ? w.stage_blocks + mbh * n_kt256 * (n_st + 1) * kMaskBlockBytes : w.stage_cls;
+  return w;
 }
 // mask_b, mask_h: 0 without a mask
 inline size_t bwd_workspace_bytes(const fa_shape& s, int mask_b = 0, int mask_h = 0) {
   if (!mask_b) return bwd_stats_bytes(s);
-  return bwd_mask_lists_offset(s) + bwd_lists_bytes(s, mask_b, mask_h) +
-         bwd_stage_lists_bytes(s, mask_b, mask_h);
+  return mask_workspace(s.N, s.M, mask_b, mask_h, bwd_mask_lists_offset(s), true).end;
 }
 // Row stride in LDS of a staged [rows][D] bf16 tile: 64 bytes of padding.
 inline int bwd_lds_row_bytes(int D) { return 2 * D + 64; }
@@ -175,6 +199,13 @@ inline int bwd_dkdv_lds_bytes(int D) { return 2 * (2 * kBwdStageQ * bwd_lds_row_
 inline int bwd_dq_lds_bytes(int D) { return 2 * (2 * kBwdStageK * bwd_lds_row_bytes(D)); }
 
 hipError_t launch_bwd_bf16(const BwdProblem& p, hipStream_t stream);
+
+// Element-mask pre-pass: classifies the mask's tiles, lists them, and copies
+// the words of the tiles the mask keeps in part into blocks (layout above),
+// into the workspace regions `w` names relative to `ws`; with stages also
+// the dK/dV pass's stage lists and blocks.
+void launch_mask_prep(const uint32_t* mask, int N, int M, int mask_w, int mask_b, int mask_h,
+                      void* ws, const MaskWorkspace& w, bool stages, hipStream_t stream);
 
 // Records a failure for fa_last_error() on the calling thread (printf-style
 // detail) and returns `st`; shared by every C entry point.

@@ -172,8 +172,8 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
           *why = "an element mask on FA_PATH_PREFILL needs N * ceil(M / 32) * 4 < 2^31";
           return FA_ERR_UNSUPPORTED;
         }
-        plan->ws_bytes = align_up((size_t)mask_b * (size_t)mask_h * (size_t)ceil_div(s.N, kPrefillBlockQ) *
-                                      (size_t)plan->mask_tiles * sizeof(int32_t), 256);
+        // the pre-pass's tile lists, tile classes and blocks of mask words
+        plan->ws_bytes = mask_workspace(s.N, s.M, mask_b, mask_h, 0, false).end;
       }
       break;
     case FA_PATH_F32:

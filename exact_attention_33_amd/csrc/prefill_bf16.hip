@@ -81,10 +81,11 @@
 //    mask over each 256-query x 64-key tile and lists, per query tile, the
 //    key tiles in which some query keeps a key, flagging those it does not
 //    keep whole.  The workgroup copies its list to LDS and visits only the
-//    listed tiles (the general form of the causal tile skip).  Each wave's
-//    mask words for a tile (64 rows x 2 words) travel HBM -> LDS with the
-//    tile loads, three tiles ahead, and the bits are applied only on flagged
-//    tiles.
+//    listed tiles (the general form of the causal tile skip).  The pre-pass
+//    also copies each flagged tile's words into a contiguous 2 KB block, so
+//    each wave's words for a tile (64 rows x 2 words) travel HBM -> LDS as
+//    two coalesced 256-byte loads with the tile loads, three tiles ahead,
+//    and the bits are applied only on flagged tiles.
 #include <cmath>
 #include <type_traits>
 #include <utility>
@@ -128,60 +129,10 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 __device__ __forceinline__ void mfma_guard() { asm volatile("s_nop 7\n\ts_nop 7"); }
 
 
-// Tile lists of an element mask: one workgroup per (mask batch, mask head,
-// 256-query tile); thread t classifies key tiles t, t + 256, ... by OR and
-// AND over the tile's real query rows (bits of keys >= M do not count), and
-// the wave ballots compact the non-empty tiles in ascending order.
-__global__ __launch_bounds__(256) void mask_tiles_kernel(const uint32_t* __restrict__ mask, int N,
-                                                         int M, int W, int n_qtiles, int stride,
-                                                         int32_t* __restrict__ lists) {
-  const int g = blockIdx.x, qt = g % n_qtiles;
-  const int64_t mbh = g / n_qtiles;
-  const uint32_t* rows = mask + (size_t)mbh * N * W;
-  const int r0 = qt * kPrefillBlockQ, r1 = min(r0 + kPrefillBlockQ, N);
-  const int n_kt = stride - 1;
-  int32_t* L = lists + (size_t)g * stride;
-  __shared__ int wave_n[4];
-  const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
-  int base = 0;
-  for (int c = 0; c < n_kt; c += 256) {
-    const int kt = c + tid;
-    bool any = false, all = true;
-    if (kt < n_kt) {
-      const int k0 = kt * kPrefillBlockK;
-      const int n0 = min(max(M - k0, 0), 32), n1 = min(max(M - k0 - 32, 0), 32);
-      const uint32_t v0 = n0 == 32 ? ~0u : (1u << n0) - 1u;  // keys < M of each word
-      const uint32_t v1 = n1 == 32 ? ~0u : (1u << n1) - 1u;
-      const bool has1 = 2 * kt + 1 < W;
-      uint32_t o0 = 0u, o1 = 0u, a0 = ~0u, a1 = ~0u;
-#pragma unroll 8
-      for (int r = r0; r < r1; ++r) {
-        const uint32_t* row = rows + (size_t)r * W + 2 * kt;
-        const uint32_t w0 = row[0], w1 = has1 ? row[1] : 0u;
-        o0 |= w0;
-        o1 |= w1;
-        a0 &= w0;
-        a1 &= w1;
-      }
-      any = ((o0 & v0) | (o1 & v1)) != 0u;
-      all = ((a0 | ~v0) & (a1 | ~v1)) == ~0u;
-    }
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(any);
-    if (lane == 0) wave_n[wv] = __builtin_popcountll(bal);
-    __syncthreads();
-    int pos = base + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-    for (int w = 0; w < wv; ++w) pos += wave_n[w];
-    if (any) L[1 + pos] = all ? kt : (int32_t)((uint32_t)kt | 0x80000000u);
-    base += wave_n[0] + wave_n[1] + wave_n[2] + wave_n[3];
-    __syncthreads();
-  }
-  if (tid == 0) L[0] = base;
-}
-
 template <int D, bool CAUSAL, bool WINDOW, bool BITS>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ tile_lists,
-                         int list_stride) {
+                         int list_stride, const uint32_t* __restrict__ mask_blocks) {
   constexpr int BQ = kPrefillBlockQ, BK = kPrefillBlockK;
   constexpr int NW = kPrefillThreads / 64;   // waves per workgroup
   constexpr int QW = BQ / NW;                // queries per wave
@@ -352,27 +303,31 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
     };
     auto load_k_item = [&](int i, int t, __bf16* dst) { load_block(Kg, t, dst, koff[i / 2], i); };
     auto load_v_item = [&](int i, int t, __bf16* dst) { load_block(Vg, t, dst, voff[i / 2], i); };
-    // Mask word w of key tile t for the wave's 64 query rows (lane = row; rows
-    // past N read row N - 1): one 4-byte buffer load per lane into LDS.
+    // Mask word w of key tile t for the wave's 64 query rows (lane = row):
+    // from the tile's block of the query tile's blocks (the pre-pass copied
+    // rows past N from row N - 1), 256 contiguous bytes per wave and word,
+    // one 4-byte buffer load per lane into LDS.
     const uint32_t* Mg = nullptr;
     int mbytes = 0;
-    uint32_t mrow = 0;
+    uint32_t mlane = 0;
     if constexpr (BITS) {
       const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
-      Mg = p.mask + (size_t)(bm * p.mask_h + hm) * N * p.mask_w;
-      mbytes = N * p.mask_w * 4;
-      mrow = (uint32_t)min(qw0 + lane, N - 1) * (uint32_t)p.mask_w;
+      const int n_kt = list_stride - 1;  // tile t has block t + 1
+      Mg = mask_blocks + ((size_t)(bm * p.mask_h + hm) * n_qtiles + qt) * (n_kt + 1) * (kMaskBlockBytes / 4);
+      mbytes = (n_kt + 1) * kMaskBlockBytes;
+      mlane = (uint32_t)(ws * 512 + lane * 4);
     }
-    // A tile the mask keeps whole (entry e >= 0) never reads its words: its
-    // load still goes out (the end-of-iteration wait counts every load) but
-    // from one address, so it touches one line instead of 64 rows.
+    // A tile the mask keeps whole (entry e >= 0) has no block and never reads
+    // its words: its load still goes out (the end-of-iteration wait counts
+    // every load) but from offset 0 (the all-ones block).
     auto load_mask_item = [&](int w, int e, uint32_t* dst) {
       if constexpr (BITS) {
         int wofs = ws * 128 + w * 64;
         asm volatile("" : "+s"(wofs));
         const uint32_t part = (uint32_t)(e >> 31);  // all ones for a partial tile
-        const uint32_t at = ((mrow + 2u * (uint32_t)tile_index(e) + (uint32_t)w) * 4u) & part;
-        buffer_load_lds4(Mg, mbytes, at, (lds_ptr)(dst + wofs));
+        const uint32_t at =
+            ((uint32_t)(tile_index(e) + 1) * (uint32_t)kMaskBlockBytes + mlane + (uint32_t)w * 256u) & part;
+        buffer_load_lds4<true>(Mg, mbytes, at, (lds_ptr)(dst + wofs));
       }
     };
     auto load_k = [&](int t, __bf16* dst) {
@@ -856,52 +811,47 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
 
 template <int D, bool BITS>
 void launch_prefill_dm(const Problem& p, dim3 grid, hipStream_t stream, int n_qtiles,
-                       const int32_t* lists, int stride) {
+                       const int32_t* lists, int stride, const uint32_t* blocks) {
   const dim3 block(kPrefillThreads);
   if (p.window) {
     if (p.causal)
-      hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride);
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride, blocks);
     else
-      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride);
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride, blocks);
   } else {
     if (p.causal)
-      hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride);
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride, blocks);
     else
-      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride);
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, BITS>), grid, block, 0, stream, p, n_qtiles, lists, stride, blocks);
   }
 }
 
 template <int D>
 void launch_prefill_d(const Problem& p, dim3 grid, hipStream_t stream, int n_qtiles,
-                      const int32_t* lists, int stride) {
-  if (p.mask) launch_prefill_dm<D, true>(p, grid, stream, n_qtiles, lists, stride);
-  else launch_prefill_dm<D, false>(p, grid, stream, n_qtiles, lists, stride);
+                      const int32_t* lists, int stride, const uint32_t* blocks) {
+  if (p.mask) launch_prefill_dm<D, true>(p, grid, stream, n_qtiles, lists, stride, blocks);
+  else launch_prefill_dm<D, false>(p, grid, stream, n_qtiles, lists, stride, blocks);
 }
 
 }  // namespace
-
-void launch_mask_tiles(const uint32_t* mask, int N, int M, int mask_w, int mask_b, int mask_h,
-                       int32_t* lists, hipStream_t stream) {
-  const int n_qtiles = (N + kPrefillBlockQ - 1) / kPrefillBlockQ;
-  const int64_t n_lists = (int64_t)mask_b * mask_h * n_qtiles;
-  if (n_lists == 0) return;
-  hipLaunchKernelGGL(mask_tiles_kernel, dim3((unsigned)n_lists), dim3(256), 0, stream, mask, N, M,
-                     mask_w, n_qtiles, mask_list_stride(M), lists);
-}
 
 hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, void* workspace,
                                hipStream_t stream) {
   if (plan.grid == 0) return hipSuccess;
   const int n_qtiles = (p.N + kPrefillBlockQ - 1) / kPrefillBlockQ;
   const dim3 grid((unsigned)plan.grid);
-  int32_t* lists = nullptr;
+  const int32_t* lists = nullptr;
+  const uint32_t* blocks = nullptr;
   if (p.mask) {
-    // the tile lists, one per (mask batch, mask head, query tile)
-    lists = (int32_t*)workspace;
-    launch_mask_tiles(p.mask, p.N, p.M, p.mask_w, p.mask_b, p.mask_h, lists, stream);
+    // the tile lists, one per (mask batch, mask head, query tile), and the
+    // words of the tiles the mask keeps in part
+    const MaskWorkspace w = mask_workspace(p.N, p.M, p.mask_b, p.mask_h, 0, false);
+    launch_mask_prep(p.mask, p.N, p.M, p.mask_w, p.mask_b, p.mask_h, workspace, w, false, stream);
+    lists = (const int32_t*)((char*)workspace + w.lists);
+    blocks = (const uint32_t*)((char*)workspace + w.blocks);
   }
-  if (p.D == 64) launch_prefill_d<64>(p, grid, stream, n_qtiles, lists, plan.mask_tiles);
-  else launch_prefill_d<128>(p, grid, stream, n_qtiles, lists, plan.mask_tiles);
+  if (p.D == 64) launch_prefill_d<64>(p, grid, stream, n_qtiles, lists, plan.mask_tiles, blocks);
+  else launch_prefill_d<128>(p, grid, stream, n_qtiles, lists, plan.mask_tiles, blocks);
   return hipGetLastError();
 }
 

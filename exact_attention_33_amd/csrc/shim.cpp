@@ -242,14 +242,17 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
     if (!aligned(workspace, 256))
       return fail(FA_ERR_ALIGN, "fa_bwd: workspace must be 256-byte aligned");
   }
+  // with a mask: the pre-pass output after the row statistics
+  const fa::MaskWorkspace mw = fa::mask_workspace(s.N, s.M, mask_b, mask_h, fa::bwd_mask_lists_offset(s), true);
+  char* const wsb = (char*)workspace;
   fa::BwdProblem p{q, k, v, o, dout, lse, kv_len, dq, dk, dv, (float*)workspace,
                    s.B, s.H, s.N, s.M, s.D, (int32_t)fa::bwd_npad(s.N), scale, causal ? 1 : 0,
                    win ? 1 : 0, win ? opt->window_left : 0, win ? opt->window_right : 0,
                    mask, mask_b, mask_h, fa::mask_words(s.M),
-                   mask ? (int32_t*)((char*)workspace + fa::bwd_mask_lists_offset(s)) : nullptr,
-                   mask ? (int32_t*)((char*)workspace + fa::bwd_mask_lists_offset(s) +
-                                     fa::bwd_lists_bytes(s, mask_b, mask_h))
-                        : nullptr};
+                   mask ? (int32_t*)(wsb + mw.lists) : nullptr,
+                   mask ? (int32_t*)(wsb + mw.stage_lists) : nullptr,
+                   mask ? (const uint32_t*)(wsb + mw.blocks) : nullptr,
+                   mask ? (const uint32_t*)(wsb + mw.stage_blocks) : nullptr};
   const hipError_t err = fa::launch_bwd_bf16(p, (hipStream_t)stream);
   if (err != hipSuccess)
     return fail(FA_ERR_HIP, "fa_bwd: launch failed: %s", hipGetErrorString(err));

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 /* FA_FP8: OCP E4M3 (finite max 448, no infinities) Q, K, V with per-tensor
  * descale factors (fa_options); O is then bf16 and LSE float32. */
@@ -121,9 +121,12 @@ typedef struct {
    * mask_batches == 1; h' likewise), in addition to kv_len, the causal rule
    * and the window.  Bits of keys >= M are ignored.  4-byte aligned; the
    * caller keeps it alive until the call's work on the stream is done.
-   * Paths: FA_PATH_PREFILL (which then needs workspace for its list of
-   * key tiles per query tile: fa_fwd_workspace_bytes; M up to 262080 and
-   * N * W * 4 below 2^31) and FA_PATH_F32.                                  */
+   * Paths: FA_PATH_PREFILL (which then needs workspace: a pre-pass lists,
+   * per query tile of 256, the 64-key tiles in which some query keeps a
+   * key and copies the words of the tiles the mask keeps in part into 2 KB
+   * blocks, about N * M / 8 bytes (the size of the mask) per (mask batch,
+   * mask head): fa_fwd_workspace_bytes; M up to 262080 and N * W * 4 below
+   * 2^31) and FA_PATH_F32, which reads the words directly.                 */
   const uint32_t* mask;
   int32_t mask_batches;  /* 1 or B (0 means 1)                               */
   int32_t mask_heads;    /* 1 or H (0 means 1)                               */
@@ -253,8 +256,10 @@ size_t fa_bwd_workspace_bytes(fa_shape s, fa_dtype dtype, int causal);
 
 /* fa_bwd_workspace_bytes_ex -- the same for fa_bwd_ex with options `opt`
  * (NULL = none): with an element mask the workspace also holds the dQ
- * pass's lists of key tiles, as the forward's prefill path does (0 for an
- * unsupported dtype or mask shape). */
+ * pass's lists and blocks of mask words, as the forward's prefill path
+ * does, and the same for the dK/dV pass (per 256-key tile, the 64-query
+ * stages): about twice the forward's (0 for an unsupported dtype or mask
+ * shape). */
 size_t fa_bwd_workspace_bytes_ex(fa_shape s, fa_dtype dtype, int causal, const fa_options* opt);
 
 /* fa_bwd -- dq, dk, dv as defined above. */

@@ -12,6 +12,7 @@ import pytest
 
 import exact_attention_33_amd as fa
 from exact_attention_33_amd import Options, Shape
+from tests.mask_layout import mask_layout
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
@@ -35,7 +36,7 @@ def test_exports_every_declared_symbol():
     assert sorted(fa.EXPORTS) == declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.fa_abi_version() == 7
+    assert L.fa_abi_version() == 8
 
 
 def test_status_strings():
@@ -258,12 +259,17 @@ def test_fp8_plan():
 
 def test_mask_plan():
     """An element mask runs on the prefill path (also for N = 1) and the
-    fp32 path; the prefill path then needs workspace for its tile lists."""
+    fp32 path; the prefill path then needs workspace for its tile lists,
+    tile classes and blocks of mask words."""
     p = fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True, mask_shape=(1, 1))
     assert p["path_name"] == "prefill"
-    assert p["workspace_bytes"] == 16640      # 32 lists of 129 int32, rounded up to 256 B
+    # 32 lists of 129 int32 (16,512 B -> 16,640), 32 x 128 class bytes, then
+    # 32 rows of 1 + 128 blocks of 2 KB
+    assert p["workspace_bytes"] == 16640 + 4096 + 32 * 129 * 2048 == mask_layout(8192, 8192, 1, 1)["end"]
     p2 = fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True, mask_shape=(2, 32))
-    assert p2["workspace_bytes"] >= 2 * 32 * 32 * 129 * 4
+    assert p2["workspace_bytes"] == mask_layout(8192, 8192, 2, 32)["end"]
+    assert fa.plan(3, 2, 600, 700, 64, fa.BF16, mask_shape=(3, 1))["workspace_bytes"] == \
+        mask_layout(600, 700, 3, 1)["end"]
     assert fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True)["workspace_bytes"] == 0
     assert fa.plan(4, 2, 1, 5000, 64, fa.BF16, mask_shape=(4, 1))["path_name"] == "prefill"
     assert fa.plan(4, 2, 5, 50, 64, fa.F32, mask_shape=(1, 2))["workspace_bytes"] == 0
@@ -286,15 +292,20 @@ def test_mask_plan():
 
 
 def test_bwd_mask_checks():
-    """The backward takes an element mask: its workspace adds the dQ pass's
-    tile lists; bad mask shapes and sizes are rejected before any launch."""
+    """The backward takes an element mask: its workspace adds both passes'
+    tile lists, classes and blocks of mask words; bad mask shapes and sizes
+    are rejected before any launch."""
     L = fa.lib()
     base = fa.bwd_workspace_bytes(2, 4, 1000, 1000, 64)
     with_mask = fa.bwd_workspace_bytes(2, 4, 1000, 1000, 64, mask_shape=(2, 1))
     lists = 2 * 1 * 4 * (16 + 1) * 4                    # 4 query tiles, 16 key tiles + count
     stages = 2 * 1 * 4 * (16 + 1) * 4                   # 4 key tiles, 16 query stages + count
-    assert with_mask == (base + 255) // 256 * 256 + (lists + 255) // 256 * 256 + \
-        (stages + 255) // 256 * 256
+    cls = 2 * 4 * 16                                    # one byte per (query tile, key tile)
+    a = lambda n: (n + 255) // 256 * 256
+    off_blocks = a(base) + a(lists) + a(stages) + a(cls)
+    rows = 2 * 4                                        # rows of 1 + 16 blocks, each pass
+    assert with_mask == a(off_blocks + rows * 17 * 2048) + a(cls) + rows * 17 * 2048
+    assert with_mask == mask_layout(1000, 1000, 2, 1, a(base), stages=True)["end"]
     assert fa.bwd_workspace_bytes(2, 4, 1000, 1000, 64, mask_shape=(3, 1)) == 0
     for mb, mh, shape, st_want in ((3, 1, (2, 4, 16, 16, 64), "FA_ERR_ARG"),
                                    (1, 5, (2, 4, 16, 16, 64), "FA_ERR_ARG"),

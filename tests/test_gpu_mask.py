@@ -18,6 +18,7 @@ import exact_attention_33_amd as fa
 from exact_attention_33_amd import inputs
 from oracle.attention import attention_ref, attention_rows
 from tests.gpu_helpers import abi_scale, compare, default_scale, host64, sample_picks
+from tests.mask_layout import mask_layout
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -200,3 +201,85 @@ def test_tile_lists_match_the_mask():
     stride_s = (N + 63) // 64 + 1
     assert _read_lists(words_b[off_st // 4:], B * n_kt, stride_s) == \
         _expected_lists(allowed, 256, 64, transpose=True)
+
+
+def _tile_classes(allowed, rows_per, cols_per, transpose=False):
+    """[Bm * Hm, row tiles, column tiles] of 0 (nothing kept), 1 (all kept),
+    2 (some kept), over the real rows and columns of each tile."""
+    a = allowed.transpose(0, 1, 3, 2) if transpose else allowed
+    Bm, Hm, R, C = a.shape
+    out = np.zeros((Bm * Hm, -(-R // rows_per), -(-C // cols_per)), dtype=np.uint8)
+    for g in range(Bm * Hm):
+        for i, r0 in enumerate(range(0, R, rows_per)):
+            for j, c0 in enumerate(range(0, C, cols_per)):
+                blk = a[g // Hm, g % Hm, r0:r0 + rows_per, c0:c0 + cols_per]
+                out[g, i, j] = 1 if blk.all() else (2 if blk.any() else 0)
+    return out
+
+
+@pytest.mark.parametrize("N,M", [(600, 700), (300, 2100)])
+def test_mask_blocks_hold_the_words(N, M):
+    """The pre-passes' class bytes and blocks of mask words, read back from
+    the workspace (layout of include/fa_mi355x.h): a block for every tile
+    (and, in the backward, every dK/dV stage) the mask keeps in part, each
+    word where the kernels' wave loads expect it (rows past N copy row N - 1;
+    words past the row are 0), and an all-ones block 0 in every row of
+    blocks."""
+    B, H, D = 2, 2, 64
+    allowed = inputs.block_mask(123, B, 1, N, M, 32, 32, 0.5)
+    allowed[1, 0, :, M - 300:] = True       # tiles (and 256-key tiles) kept whole
+    allowed[0, 0, :256, 64:320] = False     # tiles kept nowhere
+    q, k, v = make(124, B, H, N, M, D, "bf16")
+    words = fa.pack_mask(torch.from_numpy(allowed).to(DEV))
+    wn = words.cpu().numpy().view(np.uint32).reshape(B, N, -1)
+    lay = mask_layout(N, M, B, 1)
+    n_qt, n_kt, n_kt256, n_st = lay["n_qt"], lay["n_kt"], lay["n_kt256"], lay["n_st"]
+    # the words the kernels load: rows padded by copies of row N - 1, columns by 0
+    cols = max(2 * n_kt, 8 * n_kt256)
+    P = np.zeros((B, n_qt * 256, cols), dtype=np.uint32)
+    P[:, :N, :wn.shape[2]] = wn
+    P[:, N:, :wn.shape[2]] = wn[:, N - 1:N, :]
+
+    def fwd_block(g, qt, kt):   # [wave][word][row of the wave]
+        return P[g, qt * 256:(qt + 1) * 256, 2 * kt:2 * kt + 2].reshape(4, 64, 2).transpose(0, 2, 1).ravel()
+
+    def stage_block(g, kt, st):  # [word][row]
+        return P[g, st * 64:st * 64 + 64, 8 * kt:8 * kt + 8].T.ravel()
+
+    cls = _tile_classes(allowed, 256, 64)
+    scls = _tile_classes(allowed, 256, 64, transpose=True)
+    assert (cls == 1).any() and (cls == 2).any() and (cls == 0).any()
+
+    def check_fwd(wsb, lay):
+        got_cls = wsb[lay["cls"]:lay["cls"] + B * n_qt * n_kt].reshape(B, n_qt, n_kt)
+        assert np.array_equal(got_cls, cls)
+        blocks = wsb[lay["blocks"]:lay["blocks"] + B * n_qt * (n_kt + 1) * 2048].view(np.uint32)
+        blocks = blocks.reshape(B, n_qt, n_kt + 1, 512)
+        assert (blocks[:, :, 0] == 0xFFFFFFFF).all()
+        for g, qt, kt in zip(*np.nonzero(cls == 2)):
+            assert np.array_equal(blocks[g, qt, kt + 1], fwd_block(g, qt, kt)), (g, qt, kt)
+
+    ws = torch.zeros(fa.workspace_bytes(B, H, N, M, D, mask_shape=(B, 1)), dtype=torch.uint8, device=DEV)
+    assert ws.numel() == lay["end"]
+    o, l = fa.fwd(q, k, v, mask=words, workspace=ws)
+    torch.cuda.synchronize()
+    check_fwd(ws.cpu().numpy(), lay)
+
+    g_ = inputs.to_device(inputs.normal_f32(125, (B, H, N, D)), "bf16", DEV)
+    base = (B * H * ((N + 255) // 256 * 256) * 8 + 255) // 256 * 256
+    layb = mask_layout(N, M, B, 1, base, stages=True)
+    wsb = torch.zeros(fa.bwd_workspace_bytes(B, H, N, M, D, mask_shape=(B, 1)), dtype=torch.uint8,
+                      device=DEV)
+    assert wsb.numel() == layb["end"]
+    fa.bwd(q, k, v, o, l, g_, mask=words, workspace=wsb)
+    torch.cuda.synchronize()
+    wb = wsb.cpu().numpy()
+    check_fwd(wb, layb)
+    got_s = wb[layb["stage_cls"]:layb["stage_cls"] + B * n_kt256 * n_st].reshape(B, n_kt256, n_st)
+    assert np.array_equal(got_s, scls)
+    sblocks = wb[layb["stage_blocks"]:layb["stage_blocks"] + B * n_kt256 * (n_st + 1) * 2048].view(np.uint32)
+    sblocks = sblocks.reshape(B, n_kt256, n_st + 1, 512)
+    assert (sblocks[:, :, 0] == 0xFFFFFFFF).all()
+    assert (scls == 2).any() and (scls == 1).any()
+    for g, kt, st in zip(*np.nonzero(scls == 2)):
+        assert np.array_equal(sblocks[g, kt, st + 1], stage_block(g, kt, st)), (g, kt, st)
