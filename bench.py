@@ -47,6 +47,7 @@ import math
 import os
 import sys
 import time
+from statistics import median
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -71,7 +72,8 @@ SOURCES = {"prefill": ["prefill_bf16.hip", "device_common.h", "fa_internal.h"],
            "backward": ["bwd_bf16.hip", "device_common.h", "fa_internal.h", "mfma_asm.h"],
            "fp8": ["prefill_fp8.hip", "device_common.h", "fa_internal.h"],
            "kvouter": ["kvouter_bf16.hip", "device_common.h", "fa_internal.h", "mfma_asm.h"]}
-SOURCES["window"] = SOURCES["mask"] = SOURCES["configs"] = SOURCES["prefill"]
+SOURCES["window"] = SOURCES["configs"] = SOURCES["prefill"]
+SOURCES["mask"] = SOURCES["prefill"] + ["mask_prep.hip"]
 
 
 def measured_traffic(kind, case=None):
@@ -322,7 +324,7 @@ def main():
         avg_p = sum(ms_p) / len(ms_p)
         tfs = flop_p / (avg_p * 1e-3) / 1e12
         out.update({"value": tfs, "unit": "TFLOP/s"})
-        out["prefill"] = {"ms_mean": avg_p, "ms_min": min(ms_p), "tflops": tfs,
+        out["prefill"] = {"ms_mean": avg_p, "ms_min": min(ms_p), "ms_median": median(ms_p), "tflops": tfs,
                           "frac_bf16_peak": tfs / PEAK_BF16_TFLOPS, "flop_per_launch": flop_p}
         traffic = measured_traffic("prefill")
         out["roofline"] = {"bound": "mfma", "kernel": "prefill_bf16_kernel<128, true, false, false>",
@@ -331,7 +333,7 @@ def main():
     if do_d:
         avg_d = sum(ms_d) / len(ms_d)
         gbs = kv_bytes / (avg_d * 1e-3) / 1e9
-        out["decode"] = {"ms_mean": avg_d, "ms_min": min(ms_d), "kv_bytes": kv_bytes,
+        out["decode"] = {"ms_mean": avg_d, "ms_min": min(ms_d), "ms_median": median(ms_d), "kv_bytes": kv_bytes,
                          "value": gbs, "unit": "GB/s", "frac_hbm_peak": gbs / PEAK_HBM_GBS,
                          "splits": plan_d["splits"], "split_keys": plan_d["block_k"],
                          "roofline": {"bound": "hbm", "kernel": "splitkv partial + merge",
@@ -343,7 +345,7 @@ def main():
     if do_b:
         avg_b = sum(ms_b) / len(ms_b)
         tfb = flop_b / (avg_b * 1e-3) / 1e12
-        out["backward"] = {"ms_mean": avg_b, "ms_min": min(ms_b), "value": tfb, "unit": "TFLOP/s",
+        out["backward"] = {"ms_mean": avg_b, "ms_min": min(ms_b), "ms_median": median(ms_b), "value": tfb, "unit": "TFLOP/s",
                            "frac_bf16_peak": tfb / PEAK_BF16_TFLOPS, "flop_per_call": flop_b,
                            "flop_convention": "10 B H N M D / 2 (S recomputed, dP, dV, dK, dQ; "
                                               "causal halved)",
@@ -371,7 +373,7 @@ def main():
                      "frac": gbs / PEAK_HBM_GBS})
             roof.update({"kernel": "prefill_bf16_kernel<128, true, true, false>",
                          "traffic": measured_traffic("window", f"w{W}")})
-            res[f"w{W}"] = {"window": [W - 1, 0], "ms_mean": avg, "ms_min": min(ms_w[W]),
+            res[f"w{W}"] = {"window": [W - 1, 0], "ms_mean": avg, "ms_min": min(ms_w[W]), "ms_median": median(ms_w[W]),
                             "tflops": tf, "gbs": gbs, "flop_per_launch": flop,
                             "bytes_per_launch": bytes_w, "roofline": roof}
         out["window"] = dict(res, flop_convention="4 D x visible (query, key) pairs per head "
@@ -386,7 +388,7 @@ def main():
             avg = sum(ms_m[name]) / len(ms_m[name])
             flop = 4.0 * wp.D * pairs_m[name] * wp.B * wp.H
             tf = flop / (avg * 1e-3) / 1e12
-            res[name] = {"ms_mean": avg, "ms_min": min(ms_m[name]), "tflops": tf,
+            res[name] = {"ms_mean": avg, "ms_min": min(ms_m[name]), "ms_median": median(ms_m[name]), "tflops": tf,
                          "visible_pairs_per_head": pairs_m[name],
                          "visible_fraction_of_causal": pairs_m[name] / (wp.N * (wp.N + 1) / 2),
                          "speedup_vs_unmasked_causal": ((sum(ms_p) / len(ms_p)) / avg) if do_p else None,
@@ -399,7 +401,7 @@ def main():
         flop_mb = 10.0 * wp.D * pairs_m["documents8"] * wp.B * wp.H
         tf_mb = flop_mb / (avg_b * 1e-3) / 1e12
         res["backward_documents8"] = {
-            "ms_mean": avg_b, "ms_min": min(ms_mb), "tflops": tf_mb,
+            "ms_mean": avg_b, "ms_min": min(ms_mb), "ms_median": median(ms_mb), "tflops": tf_mb,
             "speedup_vs_unmasked_backward": ((sum(ms_b) / len(ms_b)) / avg_b) if do_b else None,
             "roofline": {"bound": "mfma", "kernel": "fa_bwd with a mask: rowstat + dkdv + dq (whole call)",
                          "achieved": tf_mb, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -414,7 +416,7 @@ def main():
     if do_8:
         avg8 = sum(ms_8) / len(ms_8)
         tf8 = flop_8 / (avg8 * 1e-3) / 1e12
-        out["fp8"] = {"ms_mean": avg8, "ms_min": min(ms_8), "value": tf8, "unit": "TFLOP/s",
+        out["fp8"] = {"ms_mean": avg8, "ms_min": min(ms_8), "ms_median": median(ms_8), "value": tf8, "unit": "TFLOP/s",
                       "frac_fp8_peak": tf8 / PEAK_FP8_TFLOPS, "flop_per_launch": flop_8,
                       "speedup_vs_bf16_prefill": ((sum(ms_p) / len(ms_p)) / avg8) if do_p else None,
                       "roofline": {"bound": "mfma", "kernel": "prefill_fp8_kernel<128, true>",
@@ -430,7 +432,7 @@ def main():
             avg = sum(ms_k[name]) / len(ms_k[name])
             tf = flop_k / (avg * 1e-3) / 1e12
             res[name] = {"query_tiles_per_group": min(tpg, -(-wp.N // 256)), "ms_mean": avg,
-                         "ms_min": min(ms_k[name]), "tflops": tf,
+                         "ms_min": min(ms_k[name]), "ms_median": median(ms_k[name]), "tflops": tf,
                          "frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
                          "slowdown_vs_prefill": (avg / (sum(ms_p) / len(ms_p))) if do_p else None,
                          "traffic": measured_traffic("kvouter", name)}
@@ -448,8 +450,7 @@ def main():
             flop = 4.0 * w.B * w.H * w.N * w.M * w.D / (2.0 if causal else 1.0)
             tf = flop / (avg * 1e-3) / 1e12
             res[label] = {"B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "causal": causal,
-                          "seed": w.seed, "ms_mean": avg, "ms_min": min(ms_c[label]),
-                          "ms_median": sorted(ms_c[label])[len(ms_c[label]) // 2],
+                          "seed": w.seed, "ms_mean": avg, "ms_min": min(ms_c[label]), "ms_median": median(ms_c[label]),
                           "tflops": tf, "flop_per_launch": flop,
                           "roofline": {"bound": "mfma",
                                        "kernel": f"prefill_bf16_kernel<{w.D}, {str(causal).lower()}, false, false>",
