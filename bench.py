@@ -108,11 +108,17 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8, help="prefill heads the oracle times")
     ap.add_argument("--cpu-decode-heads", type=int, default=1024)
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="write the profiles/ summaries from the rocprofv3 output under DIR "
+                         "(see summarize_profiles) and exit; needs no GPU")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.profile_summary:
+        summarize_profiles(args.profile_summary)
+        return 0
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU "
               "only (no collectives, no sharding); run with --gpus 1", file=sys.stderr)
@@ -616,6 +622,244 @@ def cpu_baseline_bwd(np, qp, kp, vp, gb, dqb, dkb, dvb, scale_p, wp, heads=((0, 
             "sample": f"{len(heads)} whole head(s) (N=M=8192, D=128, causal) of the bench's "
                       "backward tensors, fp64 NumPy, same FLOP convention",
             "max_abs_vs_gpu": err}
+
+
+# ---------------------------------------------------------------------------
+# profiles/ summaries from rocprofv3 output (no GPU needed)
+# ---------------------------------------------------------------------------
+# The runs that produce DIR, all on committed files, from /tmp (TMPDIR=/tmp):
+#   rocprofv3 --kernel-trace --stats --output-format csv -d DIR/ktrace -o run --
+#       python3 <repo>/bench.py --steps 10 --warmup 3 --no-cpu-baseline
+#   for leg in copy prefill decode backward window mask fp8 kvouter configs,
+#   c in FETCH_SIZE WRITE_SIZE (one counter per run):
+#     rocprofv3 --pmc c --output-format csv -d DIR/pmc_c_leg -o run --
+#       python3 <repo>/bench.py --only leg --steps 2 --warmup 0 --no-cpu-baseline
+#   for leg in prefill backward fp8:
+#     rocprofv3 --pmc <UTIL_COUNTERS> --output-format csv -d DIR/pmc_util_leg -o run -- (same)
+UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_BUSY_CU_CYCLES",
+                 "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE")
+KTRACE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/ktrace -o run -- "
+              "python3 <repo>/bench.py --steps 10 --warmup 3 --no-cpu-baseline")
+PMC_CMD = ("cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <out>/pmc_{c}_{leg} -o run -- "
+           "python3 <repo>/bench.py --only {leg} --steps 2 --warmup 0 --no-cpu-baseline")
+# leg: (case, first kernel of a call of that case, calls averaged), in the
+# order the bench makes them; the last calls of each kind belong to the last case
+COUNTER_LEGS = {
+    "prefill": [(None, "prefill_bf16", 2)],
+    "decode": [(None, "splitkv_partial", 2)],
+    "backward": [(None, "bwd_rowstat", 2)],
+    "window": [("w128", "prefill_bf16", 2), ("w2048", "prefill_bf16", 2)],
+    "mask": [("documents8", "mask_blocks", 2), ("random50", "mask_blocks", 2),
+             ("backward_documents8", "bwd_rowstat", 2)],
+    "configs": [("B1_H8_N1024_D64_causal", "prefill_bf16", 2), ("B4_H16_N4096_D128_causal", "prefill_bf16", 2),
+                ("B4_H16_N4096_D128_noncausal", "prefill_bf16", 2), ("B2_H32_N8192_D64_causal", "prefill_bf16", 2)],
+    "fp8": [(None, "prefill_fp8", 2)],
+    "kvouter": [("tile_per_group", "kvouter", 3), ("head_per_group", "kvouter", 3)],
+}
+
+
+def _short_kernel(name):
+    """'prefill_bf16_kernel<128, true, false, false>' for the library's kernels,
+    '__amd_rocclr_copyBuffer' for the calibration copy, else None."""
+    if "__amd_rocclr_copyBuffer" in name:
+        return "__amd_rocclr_copyBuffer"
+    if "fa::" not in name or "(anonymous namespace)::" not in name:
+        return None
+    return name.split("(anonymous namespace)::")[1].split("(")[0]
+
+
+def _leg_of_dispatches(rows):
+    """Label the library's launches of the default bench sequence by leg, from
+    their order (the bench's call order is fixed)."""
+    seen_kvo, n = False, {"win": 0, "maskp": 0, "d64": 0, "kvo": 0}
+    out = []
+    for i, (_, s, ns) in enumerate(rows):
+        nxt = rows[i + 1][1] if i + 1 < len(rows) else ""
+        seen_kvo |= s.startswith("kvouter")
+        if s == "prefill_bf16_kernel<128, true, false, false>":
+            leg = ("prefill B2 H32 N8192 D128 causal (bench step)" if nxt.startswith("splitkv_partial") else
+                   "configs B4 H16 N4096 D128 causal" if seen_kvo else
+                   "setup (untimed forward for the backward's O, LSE)")
+        elif s.startswith("splitkv"):
+            leg = "decode B32 H32 D128 (bench step)"
+        elif s.startswith("bwd_rowstat"):
+            leg = "backward (rowstat, both legs)"
+        elif s.startswith("bwd_"):
+            leg = "backward B2 H32 N8192 D128 causal" if s.endswith("false>") else "backward under the 8-document mask"
+        elif s == "prefill_bf16_kernel<128, true, true, false>":
+            n["win"] += 1
+            leg = "window 128 keys" if n["win"] <= 13 else "window 2048 keys"
+        elif s == "prefill_bf16_kernel<128, true, false, true>" or s.startswith("mask_"):
+            if s.startswith("prefill"):
+                n["maskp"] += 1
+            k = n["maskp"] if s.startswith("prefill") else n["maskp"] + 1   # a pre-pass precedes its prefill
+            leg = ("setup (untimed masked forward for the masked backward)" if k == 1 else
+                   "mask, 8 documents" if k <= 14 else
+                   "mask, unstructured p = 1/2" if k <= 27 else "backward under the 8-document mask")
+        elif s.startswith("prefill_fp8"):
+            leg = "fp8 B2 H32 N8192 D128 causal"
+        elif s.startswith("kvouter"):
+            n["kvo"] += 1
+            leg = "kvouter, one query tile per group" if n["kvo"] <= 3 else "kvouter, one head per group"
+        elif s == "prefill_bf16_kernel<64, true, false, false>":
+            n["d64"] += 1
+            leg = "configs B1 H8 N1024 D64 causal" if n["d64"] <= 13 else "configs B2 H32 N8192 D64 causal"
+        elif s == "prefill_bf16_kernel<128, false, false, false>":
+            leg = "configs B4 H16 N4096 D128 non-causal"
+        else:
+            leg = "other"
+        out.append((leg, s, ns))
+    return out
+
+
+def summarize_profiles(d):
+    """Write the profiles/ summaries (kernel durations, HBM traffic per leg
+    with the copy calibration, matrix-pipe counters) from rocprofv3 output."""
+    import csv
+    import statistics
+    from collections import defaultdict
+    prof = os.path.join(ROOT, "profiles")
+
+    def write(name, lines):
+        lines = lines[:2] + ["# summarised by: python3 <repo>/bench.py --profile-summary <out>"] + lines[2:]
+        with open(os.path.join(prof, name), "w") as f:
+            f.write("\n".join(lines) + "\n")
+
+    # kernel durations: rocprofv3 --stats, and the same trace split by leg
+    lines = ["# rocprofv3 --stats kernel summary of the default bench sequence (durations in ns), the library's kernels",
+             f"# command: {KTRACE_CMD}",
+             "# rows aggregate by kernel name: prefill_bf16_kernel<128, true, false, false> serves the bench step (N = 8192),",
+             "# the configs leg (N = 4096) and one untimed setup call, and prefill_bf16_kernel<64, true, false, false> two configs;",
+             "# kernel_trace_by_leg_default_bench.txt splits the same trace by leg", "#",
+             "# kernel, calls, average_ns, min_ns, max_ns, stddev_ns"]
+    for r in csv.DictReader(open(os.path.join(d, "ktrace", "run_kernel_stats.csv"))):
+        s = _short_kernel(r["Name"])
+        if s and s != "__amd_rocclr_copyBuffer":
+            lines.append(f"{s}, {r['Calls']}, {float(r['AverageNs']):.0f}, {r['MinNs']}, {r['MaxNs']}, "
+                         f"{float(r['StdDev']):.0f}")
+    write("kernel_stats_default_bench.txt", lines)
+    rows = []
+    for r in csv.DictReader(open(os.path.join(d, "ktrace", "run_kernel_trace.csv"))):
+        s = _short_kernel(r["Kernel_Name"])
+        if s and s != "__amd_rocclr_copyBuffer":
+            rows.append((int(r["Dispatch_Id"]), s, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    agg, order = defaultdict(list), []
+    for leg, s, ns in _leg_of_dispatches(rows):
+        if (leg, s) not in agg:
+            order.append((leg, s))
+        agg[(leg, s)].append(ns)
+    lines = ["# rocprofv3 kernel trace of the default bench sequence, split by leg (durations in ns)",
+             f"# command: {KTRACE_CMD}",
+             "# each leg's launches are told apart by their place in the bench's fixed call order (run_kernel_trace.csv);",
+             "# every leg runs 3 warmup + 10 timed calls (kvouter 1 + 2); averages include the warmup calls", "#",
+             "# leg, kernel, calls, average_ns, min_ns, max_ns, stddev_ns"]
+    for leg, s in order:
+        v = agg[(leg, s)]
+        lines.append(f"{leg}, {s}, {len(v)}, {statistics.mean(v):.0f}, {min(v)}, {max(v)}, {statistics.pstdev(v):.0f}")
+    write("kernel_trace_by_leg_default_bench.txt", lines)
+
+    # HBM traffic: per leg, the last calls of each case, calibrated by a copy
+    def dispatches(leg, ctr):
+        out = []
+        for r in csv.DictReader(open(os.path.join(d, f"pmc_{ctr}_{leg}", "run_counter_collection.csv"))):
+            s = _short_kernel(r["Kernel_Name"])
+            if s:
+                out.append((int(r["Dispatch_Id"]), s, float(r["Counter_Value"])))
+        return sorted(out)
+
+    def calls_of(rows):
+        calls = []
+        for _, k, v in rows:
+            first = calls[-1][0][0] if calls else ""
+            if not calls or k.startswith("bwd_rowstat"):
+                start = True
+            elif first.startswith("bwd_rowstat") or k.startswith("splitkv_merge"):
+                start = False   # a backward call runs to the next rowstat; a decode call ends with its merge
+            elif first.startswith("mask_blocks") and (k.startswith("mask_lists") or
+                                                      (k.startswith("prefill_bf16") and len(calls[-1]) == 2)):
+                start = False   # the forward's pre-pass (two launches), then its prefill
+            else:
+                start = True
+            if start:
+                calls.append([])
+            calls[-1].append((k, v))
+        return calls
+
+    def copy_kib(ctr):
+        v = [x for _, s, x in dispatches("copy", ctr) if s == "__amd_rocclr_copyBuffer"]
+        return sum(v) / len(v)
+    cf, cw = copy_kib("FETCH_SIZE"), copy_kib("WRITE_SIZE")
+    copy_bytes = 1 << 30
+    ff, wf = copy_bytes / 1024 / cf, copy_bytes / 1024 / cw
+    traffic = {"calibration": {"copy_bytes": copy_bytes, "fetch_factor": ff, "write_factor": wf,
+                               "copy_fetch_kib": cf, "copy_write_kib": cw}}
+    lines = []
+    for leg, spec in COUNTER_LEGS.items():
+        per = {}
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            kinds = {}
+            for c in calls_of([r for r in dispatches(leg, ctr) if r[1] != "__amd_rocclr_copyBuffer"]):
+                kinds.setdefault(c[0][0].split("<")[0].split("_kernel")[0], []).append(c)
+            used = {}
+            for case, kind, n in reversed(spec):
+                pool = [c for key, cs in kinds.items() if key.startswith(kind) for c in cs]
+                k0 = used.get(kind, 0)
+                kern = defaultdict(float)
+                for c in pool[len(pool) - k0 - n:len(pool) - k0]:
+                    for k, v in c:
+                        kern[k] += v / n
+                used[kind] = k0 + n
+                per.setdefault(case, {})[ctr] = dict(kern)
+        rec = {"source_sha": kernel_source_sha(SOURCES[leg])}
+        for case, _, _ in spec:
+            kerns, tot = {}, 0.0
+            for k, f in per[case]["FETCH_SIZE"].items():
+                w = per[case]["WRITE_SIZE"].get(k, 0.0)
+                fb, wb = f * 1024 * ff, w * 1024 * wf
+                kerns[k] = {"fetch_kib": f, "write_kib": w, "fetch_bytes": fb, "write_bytes": wb}
+                tot += fb + wb
+                lines.append(f"{leg}{'/' + case if case else ''}, {k}, {f:.0f}, {w:.0f}, {fb:.4g}, {wb:.4g}")
+            body = {"bytes_per_launch": tot, "kernels": kerns}
+            if case is None:
+                rec.update(body)
+            else:
+                rec.setdefault("cases", {})[case] = body
+        traffic[leg] = rec
+    head = ["# HBM traffic per library call from rocprofv3 --pmc (KiB per dispatch of each kernel the call launches, "
+            "averaged over the timed calls)",
+            "# calibration: a 1 GiB device-to-device copy (__amd_rocclr_copyBuffer) reads",
+            f"#   FETCH_SIZE {cf:.0f} KiB -> factor {ff:.4f}; WRITE_SIZE {cw:.0f} KiB -> factor {wf:.4f}",
+            "# commands, for leg in copy " + " ".join(COUNTER_LEGS) + " and c in FETCH_SIZE WRITE_SIZE:",
+            "#   " + PMC_CMD, "#",
+            "# leg[/case], kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, scaled fetch bytes, scaled write bytes"]
+    write("hbm_traffic_all_legs_n8192_d128.txt", head + lines)
+    with open(PROFILE_TRAFFIC, "w") as f:
+        json.dump(traffic, f, indent=1)
+
+    # matrix pipe and LDS
+    lines = ["# MFMA utilisation and LDS counters per dispatch (rocprofv3 --pmc, one pass)",
+             "# command: " + PMC_CMD.replace("pmc_{c}", "pmc_util").replace("{c}", " ".join(UTIL_COUNTERS))
+             + "   (leg in prefill backward fp8)",
+             "# GRBM_GUI_ACTIVE is summed over the 8 XCDs; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "(256 CUs x 4 SIMDs x GUI cycles per XCD)", "#"]
+    for leg in ("prefill", "backward", "fp8"):
+        agg, calls = defaultdict(lambda: defaultdict(float)), defaultdict(set)
+        for r in csv.DictReader(open(os.path.join(d, f"pmc_util_{leg}", "run_counter_collection.csv"))):
+            s = _short_kernel(r["Kernel_Name"])
+            if s and s != "__amd_rocclr_copyBuffer":
+                agg[s][r["Counter_Name"]] += float(r["Counter_Value"])
+                calls[s].add(r["Dispatch_Id"])
+        for s, c in agg.items():
+            n = len(calls[s])
+            g = c["GRBM_GUI_ACTIVE"] / n / 8
+            busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / n / (256 * 4 * g)
+            lines.append(f"{s}, dispatches {n}, GRBM_GUI_ACTIVE/XCD {g:.4g} cycles, MFMA busy {busy:.3f} of SIMD-cycles, "
+                         f"LDS bank conflicts / LDS active {c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.4f}, "
+                         f"wait-inst fraction of wave cycles {c['SQ_WAIT_INST_ANY'] / max(c['SQ_WAVE_CYCLES'], 1):.3f}, "
+                         f"VALU insts {c['SQ_INSTS_VALU'] / n:.4g} per dispatch; raw per dispatch: "
+                         + ", ".join(f"{k} {v / n:.4g}" for k, v in sorted(c.items())))
+    write("counters_mfma_lds_prefill_backward_fp8_n8192_d128.txt", lines)
 
 
 if __name__ == "__main__":
