@@ -161,6 +161,9 @@ def main():
                ("prefill_mid", True, "B4_H16_N4096_D128_causal"),
                ("prefill_mid", False, "B4_H16_N4096_D128_noncausal"),
                ("prefill_long_d64", True, "B2_H32_N8192_D64_causal"))
+    # the small prefill once more with its keys in chunks of 256 (four
+    # workgroups per query tile instead of one: 128 of the 256 CUs)
+    SPLIT_SMALL, SPLIT_LABEL = 256, "B1_H8_N1024_D64_causal_split_keys256"
     KVO = (("tile_per_group", 1), ("head_per_group", 1 << 20))  # 256-query tiles per workgroup
     WINDOWS = (128, 2048)  # keys per query (causal band: window_left = W - 1)
 
@@ -315,6 +318,12 @@ def main():
                                 fa.fwd(q_, k_, v_, scale=1.0 / math.sqrt(w.D), causal=causal,
                                        out=o_, lse=l_, stream=stream),
                                 args.steps, args.warmup)
+        w, q_, k_, v_, o_, l_ = cfg_t["prefill_small"]
+        wsc = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.M, w.D, causal=True, split_keys=SPLIT_SMALL),
+                          dtype=torch.uint8, device=dev)
+        ms_c[SPLIT_LABEL] = timed(lambda: fa.fwd(q_, k_, v_, scale=1.0 / math.sqrt(w.D), causal=True, out=o_,
+                                                 lse=l_, split_keys=SPLIT_SMALL, workspace=wsc, stream=stream),
+                                  args.steps, args.warmup)
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": 1e3 * wall / max(1, args.steps), "higher_is_better": True,
@@ -466,6 +475,20 @@ def main():
         res["B1_H8_N1024_D64_causal"]["note"] = (
             "latency: 32 workgroups (1/8 of the CUs) and a few microseconds per launch; "
             "the TFLOP/s figure is not a throughput claim")
+        w = cfg_t["prefill_small"][0]
+        avg = sum(ms_c[SPLIT_LABEL]) / len(ms_c[SPLIT_LABEL])
+        flop = 4.0 * w.B * w.H * w.N * w.M * w.D / 2.0
+        tf = flop / (avg * 1e-3) / 1e12
+        res[SPLIT_LABEL] = {
+            "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "causal": True, "seed": w.seed,
+            "split_keys": SPLIT_SMALL, "ms_mean": avg, "ms_min": min(ms_c[SPLIT_LABEL]),
+            "ms_median": median(ms_c[SPLIT_LABEL]), "tflops": tf, "flop_per_launch": flop,
+            "speedup_vs_no_split": (sum(ms_c["B1_H8_N1024_D64_causal"]) / len(ms_c["B1_H8_N1024_D64_causal"])) / avg,
+            "roofline": {"bound": "mfma", "kernel": "prefill_split_kernel<64, true> + prefill_merge_kernel<64>",
+                         "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_BF16_TFLOPS, "traffic": measured_traffic("configs", SPLIT_LABEL)},
+            "note": "the same latency case with each query tile's keys in chunks of 256 (128 workgroups), "
+                    "merged by log-sum-exp in a second launch"}
         out["configs"] = dict(res, flop_convention="4 B H N M D, halved for causal")
         cfg["configs"] = {label: name for name, _, label in CONFIGS}
     if do_p:
@@ -652,7 +675,8 @@ COUNTER_LEGS = {
     "mask": [("documents8", "mask_blocks", 2), ("random50", "mask_blocks", 2),
              ("backward_documents8", "bwd_rowstat", 2)],
     "configs": [("B1_H8_N1024_D64_causal", "prefill_bf16", 2), ("B4_H16_N4096_D128_causal", "prefill_bf16", 2),
-                ("B4_H16_N4096_D128_noncausal", "prefill_bf16", 2), ("B2_H32_N8192_D64_causal", "prefill_bf16", 2)],
+                ("B4_H16_N4096_D128_noncausal", "prefill_bf16", 2), ("B2_H32_N8192_D64_causal", "prefill_bf16", 2),
+                ("B1_H8_N1024_D64_causal_split_keys256", "prefill_split", 2)],
     "fp8": [(None, "prefill_fp8", 2)],
     "kvouter": [("tile_per_group", "kvouter", 3), ("head_per_group", "kvouter", 3)],
 }
@@ -706,6 +730,8 @@ def _leg_of_dispatches(rows):
             leg = "configs B1 H8 N1024 D64 causal" if n["d64"] <= 13 else "configs B2 H32 N8192 D64 causal"
         elif s == "prefill_bf16_kernel<128, false, false, false>":
             leg = "configs B4 H16 N4096 D128 non-causal"
+        elif s.startswith(("prefill_split", "prefill_merge")):
+            leg = "configs B1 H8 N1024 D64 causal, keys in chunks of 256"
         else:
             leg = "other"
         out.append((leg, s, ns))
@@ -774,8 +800,8 @@ def summarize_profiles(d):
             first = calls[-1][0][0] if calls else ""
             if not calls or k.startswith("bwd_rowstat"):
                 start = True
-            elif first.startswith("bwd_rowstat") or k.startswith("splitkv_merge"):
-                start = False   # a backward call runs to the next rowstat; a decode call ends with its merge
+            elif first.startswith("bwd_rowstat") or k.startswith(("splitkv_merge", "prefill_merge")):
+                start = False   # a backward call runs to the next rowstat; split calls end with their merge
             elif first.startswith("mask_blocks") and (k.startswith("mask_lists") or
                                                       (k.startswith("prefill_bf16") and len(calls[-1]) == 2)):
                 start = False   # the forward's pre-pass (two launches), then its prefill

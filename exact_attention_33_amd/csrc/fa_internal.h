@@ -47,6 +47,7 @@ struct Plan {
   size_t ws_bytes;
   size_t ws_lse_offset;  // split-KV: byte offset of the partial LSE array
   int32_t mask_tiles;    // prefill with a mask: int32 entries per tile list
+  int32_t split_tiles;   // prefill with key splits: 64-key tiles per chunk (0: none)
 };
 
 // Returns FA_OK and fills `plan`, or an error status with `why` set.

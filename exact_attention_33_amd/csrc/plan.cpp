@@ -155,6 +155,25 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
       plan->threads = kPrefillThreads;
       plan->lds_bytes = prefill_lds_bytes(s.D);
       plan->grid = ceil_div(s.N, kPrefillBlockQ) * bh;
+      if (opt && opt->split_keys > 0) {
+        // key splits: one workgroup per (query tile, chunk of split_keys
+        // keys), each writing float32 partial results, then one merge launch
+        if (window || mask) {
+          *why = "key splits (options.split_keys) on FA_PATH_PREFILL take no window and no element mask";
+          return FA_ERR_UNSUPPORTED;
+        }
+        plan->split_tiles = opt->split_keys / kPrefillBlockK;
+        plan->splits = (int32_t)std::max<int64_t>(1, ceil_div(s.M, opt->split_keys));
+        plan->grid *= plan->splits;
+        if (plan->grid > INT32_MAX) {
+          *why = "too many key splits: B * H * ceil(N / 256) * ceil(M / split_keys) must stay below 2^31";
+          return FA_ERR_UNSUPPORTED;
+        }
+        const size_t rows = (size_t)bh * (size_t)s.N * (size_t)plan->splits;
+        plan->ws_lse_offset = align_up(rows * (size_t)s.D * sizeof(float), 256);
+        plan->ws_bytes = rows ? align_up(plan->ws_lse_offset + rows * sizeof(float), 256) : 0;
+        break;
+      }
       // causal without a window or a mask: persistent workgroups, one per CU
       // (a multiple of the 8 XCDs), each walking several query tiles
       if (causal && !window && !mask)

@@ -129,10 +129,22 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 __device__ __forceinline__ void mfma_guard() { asm volatile("s_nop 7\n\ts_nop 7"); }
 
 
-template <int D, bool CAUSAL, bool WINDOW, bool BITS>
-__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ tile_lists,
-                         int list_stride, const uint32_t* __restrict__ mask_blocks) {
+// Key splits of the prefill: each query tile's keys in chunks of
+// split_tiles tiles, one workgroup per (query tile, chunk), each writing its
+// chunk's normalised output and log-sum-exp (float32) for the merge.
+struct SplitArgs {
+  float* part_o;    // [splits][B H][N][D]
+  float* part_lse;  // [splits][B H][N]
+  int split_tiles;  // 64-key tiles per chunk
+  int splits;
+};
+
+// The kernel body, shared by the prefill kernel and its key-split form.
+template <int D, bool CAUSAL, bool WINDOW, bool BITS, bool SPLIT>
+__device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, const int32_t* __restrict__ tile_lists,
+                                             int list_stride, const uint32_t* __restrict__ mask_blocks,
+                                             const SplitArgs& sp) {
+  static_assert(!SPLIT || (!WINDOW && !BITS), "key splits take no window and no mask");
   constexpr int BQ = kPrefillBlockQ, BK = kPrefillBlockK;
   constexpr int NW = kPrefillThreads / 64;   // waves per workgroup
   constexpr int QW = BQ / NW;                // queries per wave
@@ -175,8 +187,8 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
   // tiles alternate (measured on MI355X: -3% at N = 8192, -14% at N = 4096
   // against one workgroup per item, results identical; with uneven work
   // per item -- windows, masks -- the dispatcher's own balancing wins).
-  constexpr bool PERSIST = CAUSAL && !WINDOW && !BITS;
-  const int64_t n_items = (int64_t)n_qtiles * p.B * p.H;
+  constexpr bool PERSIST = CAUSAL && !WINDOW && !BITS && !SPLIT;
+  const int64_t n_items = (int64_t)n_qtiles * p.B * p.H * (SPLIT ? sp.splits : 1);
   const int xcd = blockIdx.x % kNumXcd, u = blockIdx.x / kNumXcd, W = gridDim.x / kNumXcd;
   const int64_t qx = n_items / kNumXcd, rx = n_items % kNumXcd;
   const int64_t x_start = xcd * qx + (xcd < rx ? xcd : rx), x_count = qx + (xcd < rx ? 1 : 0);
@@ -195,8 +207,10 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
       logical = xcd_logical(blockIdx.x, gridDim.x);
     }
   {
-    int qt = (int)(logical % n_qtiles);
-    const int64_t bh = logical / n_qtiles;
+    const int split = SPLIT ? (int)(logical % sp.splits) : 0;  // key chunk
+    const int64_t item = SPLIT ? logical / sp.splits : logical;
+    int qt = (int)(item % n_qtiles);
+    const int64_t bh = item / n_qtiles;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest query tiles first
     const int b = (int)(bh / p.H);
     const int N = p.N, M = p.M;
@@ -215,12 +229,15 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
     const int wl = WINDOW ? min(p.wl, N + kvl) : 0;
     const int wr = CAUSAL ? 0 : (WINDOW ? min(p.wr, N + kvl) : 0);
     const int q_last = min(q0 + BQ, N) - 1;
-    const int kv_end = UPPER ? min(kvl, q_last + off + wr + 1) : kvl;
+    // Keys past kend are not this workgroup's: kv_len, or the end of its key
+    // chunk (the causal alignment off stays that of kv_len).
+    const int kend = SPLIT ? min(kvl, (split + 1) * sp.split_tiles * BK) : kvl;
+    const int kv_end = UPPER ? min(kend, q_last + off + wr + 1) : kend;
     // Window: tiles before the first query's first key are never visited.
     // Without a mask the K/V descriptors start at that tile, t0, and the loop
     // counts tiles from there; with a mask the loop walks the listed tiles in
     // [tw, t_end) and tiles are addressed from 0.
-    const int tw = WINDOW ? max(0, q0 + off - wl) / BK : 0;
+    const int tw = WINDOW ? max(0, q0 + off - wl) / BK : (SPLIT ? split * sp.split_tiles : 0);
     const int t_end = kv_end > tw * BK ? (kv_end + BK - 1) / BK : tw;
     const int t0 = BITS ? 0 : tw;
     int n_tiles = t_end - tw;
@@ -289,7 +306,7 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
       voff[i / 2] = slot_off(ws + i * NW, VCH) | (i + 1 < VPW ? slot_off(ws + (i + 1) * NW, VCH) << 16 : 0u);
     // K and V bytes this (batch, head) may read; the planner keeps M * D * 2
     // below 2^31, so every offset below fits 32 bits.
-    const int nrec = (kvl - t0 * BK) * ROWB;
+    const int nrec = (SPLIT ? max(kend - t0 * BK, 0) : kend - t0 * BK) * ROWB;
     // Block i of this wave: its slots of tile t of src into dst.  The wave's
     // block offset goes through an empty asm so that the compiler forms each
     // LDS address next to its load instead of keeping all of them (three
@@ -408,7 +425,7 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
     // element by element; every other tile is fully visible to the wave.
     auto need_mask = [&](int e) {
       const int k0 = (tile_index(e) + t0) * BK;
-      return (BITS && e < 0) || (k0 + BK > kvl) || (UPPER && k0 + BK - 1 > qw0 + off + wr) ||
+      return (BITS && e < 0) || (k0 + BK > kend) || (UPPER && k0 + BK - 1 > qw0 + off + wr) ||
              (WINDOW && k0 < qw0 + QW - 1 + off - wl);
     };
 
@@ -587,7 +604,7 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
   #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const int qrow = qw0 + 32 * qb + ql;
-        const int lim = UPPER ? min(kvl - 1, qrow + off + wr) : kvl - 1;  // last visible key
+        const int lim = UPPER ? min(kend - 1, qrow + off + wr) : kend - 1;  // last visible key
         const int lo = qrow + off - wl;                                   // first (window)
         uint32_t hid[NKB];  // masked-out keys of the row's two key blocks (bit set)
   #pragma unroll
@@ -789,7 +806,24 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
     for (int qb = 0; qb < NQB; ++qb) {
       const int qrow = qw0 + 32 * qb + ql;
       const float l_tot = swap_halves_sum(l_run[qb]);
-      if (qrow < N) {
+      if (SPLIT && qrow < N) {
+        // the chunk's normalised output and log-sum-exp, in float32
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const size_t prow = ((size_t)split * p.B * p.H + bh) * N + qrow;
+        float* Orow = sp.part_o + prow * D;
+  #pragma unroll
+        for (int db = 0; db < DB; ++db)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float4 ov;
+            ov.x = oacc[db][qb][4 * j] * inv;
+            ov.y = oacc[db][qb][4 * j + 1] * inv;
+            ov.z = oacc[db][qb][4 * j + 2] * inv;
+            ov.w = oacc[db][qb][4 * j + 3] * inv;
+            *(float4*)(Orow + db * 32 + 8 * j + 4 * hl) = ov;
+          }
+        if (hl == 0) sp.part_lse[prow] = l_tot > 0.f ? (m_run[qb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      } else if (qrow < N) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         __bf16* Orow = (__bf16*)p.o + (size_t)bh * N * D + (size_t)qrow * D;
   #pragma unroll
@@ -807,6 +841,63 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
     }
   }
   }
+}
+
+template <int D, bool CAUSAL, bool WINDOW, bool BITS>
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ tile_lists,
+                         int list_stride, const uint32_t* __restrict__ mask_blocks) {
+  prefill_body<D, CAUSAL, WINDOW, BITS, false>(p, n_qtiles, tile_lists, list_stride, mask_blocks, SplitArgs{});
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_split_kernel(Problem p, int n_qtiles, SplitArgs sp) {
+  prefill_body<D, CAUSAL, false, false, true>(p, n_qtiles, nullptr, 0, nullptr, sp);
+}
+
+// Merge of the key chunks of each row ("Understanding FlashAttention", the
+// correction factor: partial results over disjoint key sets combine through
+// their log-sum-exps): L = log sum_s e^(L_s), O = sum_s e^(L_s - L) O_s, in
+// chunk order.  D / 8 threads per row, 8 elements each; a row no chunk sees
+// a key of gets O = 0 and L = -inf.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(Problem p, SplitArgs sp) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;  // threads per row, rows per block
+  const int64_t rows = (int64_t)p.B * p.H * p.N;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  if (r >= rows) return;
+  const int S = sp.splits;
+  // the loads of each pass are independent: unrolled, so that several are in
+  // flight at once instead of one latency per chunk
+  float mx = -INFINITY;
+#pragma unroll 8
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, sp.part_lse[(size_t)s * rows + r]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) {
+      const float ls = sp.part_lse[(size_t)s * rows + r];
+      // a chunk with no key for this row takes no part (weight 0, and its
+      // O_s is not read into the sum)
+      const bool none = ls == -INFINITY;
+      const float w = none ? 0.f : fast_exp2((ls - mx) * kLog2e);
+      sum += w;
+      const float4* src = (const float4*)(sp.part_o + ((size_t)s * rows + r) * D + 8 * c);
+      const float4 z = {0.f, 0.f, 0.f, 0.f};
+      const float4 a = none ? z : src[0], b = none ? z : src[1];
+      acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+      acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+    }
+  }
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  bf16x8 ov;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ov[i] = (__bf16)(acc[i] * inv);
+  *(bf16x8*)((__bf16*)p.o + r * D + 8 * c) = ov;
+  if (c == 0) p.lse[r] = sum > 0.f ? mx + fast_log2(sum) * kLn2 : -INFINITY;
 }
 
 template <int D, bool BITS>
@@ -840,6 +931,25 @@ hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, void* workspa
   if (plan.grid == 0) return hipSuccess;
   const int n_qtiles = (p.N + kPrefillBlockQ - 1) / kPrefillBlockQ;
   const dim3 grid((unsigned)plan.grid);
+  if (plan.split_tiles > 0) {
+    // key chunks, then their merge
+    const SplitArgs sp{(float*)workspace, (float*)((char*)workspace + plan.ws_lse_offset), plan.split_tiles,
+                       plan.splits};
+    const dim3 block(kPrefillThreads);
+    if (p.D == 64) {
+      if (p.causal) hipLaunchKernelGGL((prefill_split_kernel<64, true>), grid, block, 0, stream, p, n_qtiles, sp);
+      else hipLaunchKernelGGL((prefill_split_kernel<64, false>), grid, block, 0, stream, p, n_qtiles, sp);
+    } else {
+      if (p.causal) hipLaunchKernelGGL((prefill_split_kernel<128, true>), grid, block, 0, stream, p, n_qtiles, sp);
+      else hipLaunchKernelGGL((prefill_split_kernel<128, false>), grid, block, 0, stream, p, n_qtiles, sp);
+    }
+    const int64_t rows = (int64_t)p.B * p.H * p.N;
+    const int rpb = 256 / (p.D / 8);
+    const dim3 mgrid((unsigned)((rows + rpb - 1) / rpb));
+    if (p.D == 64) hipLaunchKernelGGL(prefill_merge_kernel<64>, mgrid, dim3(256), 0, stream, p, sp);
+    else hipLaunchKernelGGL(prefill_merge_kernel<128>, mgrid, dim3(256), 0, stream, p, sp);
+    return hipGetLastError();
+  }
   const int32_t* lists = nullptr;
   const uint32_t* blocks = nullptr;
   if (p.mask) {

@@ -94,7 +94,18 @@ typedef enum {
  * struct means the defaults too. */
 typedef struct {
   int32_t path;        /* fa_path                                                */
-  int32_t split_keys;  /* split-KV: keys per split, a multiple of 64; 0 = auto   */
+  int32_t split_keys;  /* a multiple of 64.  FA_PATH_SPLITKV: keys per split
+                          (0 = auto).  FA_PATH_PREFILL (N > 1 under
+                          FA_PATH_AUTO): 0 = none; otherwise each query tile's
+                          keys go in chunks of split_keys to separate
+                          workgroups, whose float32 partial results are merged
+                          by their log-sum-exps ("Understanding
+                          FlashAttention", the correction factor) in one more
+                          launch: more workgroups for a small B * H * N (up to
+                          256 CUs), at the cost of workspace
+                          (fa_fwd_workspace_bytes: (D + 1) * 4 bytes per
+                          (chunk, batch, head, query row)); no window, no
+                          element mask                                         */
   int32_t window;      /* 0: no window.  1: local (banded) attention: key j is
                           visible to query i only if
                             i + off - window_left <= j <= i + off + window_right

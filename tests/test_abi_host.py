@@ -360,3 +360,22 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
     assert str(need) in msg and str(fa.NOALLOC_SCRATCH_BYTES) in msg
     # the largest decode cache the header quotes fits
     assert fa.workspace_bytes(32, 32, 1, 48000, 128) <= fa.NOALLOC_SCRATCH_BYTES
+
+
+def test_prefill_key_split_plan():
+    """options.split_keys on the prefill path: one workgroup per (query tile,
+    chunk of keys), workspace for the float32 partial results and their
+    log-sum-exps, no window and no element mask."""
+    p = fa.plan(1, 8, 1024, 1024, 64, fa.BF16, True, split_keys=256)
+    assert p["path_name"] == "prefill" and p["splits"] == 4 and p["grid"] == 4 * 8 * 4
+    rows = 4 * 8 * 1024
+    assert p["workspace_bytes"] == (rows * 64 * 4 + 255) // 256 * 256 + rows * 4
+    assert fa.plan(1, 8, 1024, 1024, 64, fa.BF16, True)["workspace_bytes"] == 0     # no split: none
+    assert fa.plan(2, 2, 300, 0, 128, fa.BF16, False, split_keys=64)["splits"] == 1  # M = 0: one chunk
+    assert fa.plan(2, 2, 1, 700, 64, fa.BF16, False, split_keys=256)["path_name"] == "splitkv"
+    q = fa.plan(2, 2, 1, 700, 64, fa.BF16, False, split_keys=256, path=fa.PATH_PREFILL)
+    assert q["path_name"] == "prefill" and q["splits"] == 3
+    for kw in (dict(window=(127, 0)), dict(mask_shape=(1, 1))):
+        with pytest.raises(fa.FaError) as e:
+            fa.plan(1, 2, 300, 300, 64, fa.BF16, True, split_keys=128, **kw)
+        assert e.value.name == "FA_ERR_UNSUPPORTED", kw
