@@ -490,7 +490,8 @@ def main():
             "note": "the same latency case with each query tile's keys in chunks of 256 (128 workgroups), "
                     "merged by log-sum-exp in a second launch"}
         out["configs"] = dict(res, flop_convention="4 B H N M D, halved for causal")
-        cfg["configs"] = {label: name for name, _, label in CONFIGS}
+        cfg["configs"] = dict({label: name for name, _, label in CONFIGS},
+                              **{SPLIT_LABEL: f"prefill_small, split_keys={SPLIT_SMALL}"})
     if do_p:
         out["naive_hbm_bytes"] = naive_traffic_report(wp)
     out["config"] = cfg
