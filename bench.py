@@ -120,7 +120,7 @@ def main():
         summarize_profiles(args.profile_summary)
         return 0
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library runs on one GPU "
               "only (no collectives, no sharding); run with --gpus 1", file=sys.stderr)
         return 2
 
