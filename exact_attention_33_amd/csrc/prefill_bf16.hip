@@ -869,27 +869,40 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(Problem p, SplitArgs
   const int c = threadIdx.x % TPR;
   if (r >= rows) return;
   const int S = sp.splits;
-  // the loads of each pass are independent: unrolled, so that several are in
-  // flight at once instead of one latency per chunk
-  float mx = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, sp.part_lse[(size_t)s * rows + r]);
+  // Groups of four chunks: all of a group's loads go out before any is used
+  // (one memory latency per group), then the group folds into a running
+  // max, sum and output, rescaled when the max moves (the same identity).
+  constexpr int G = 4;
+  float mx = -INFINITY, sum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float sum = 0.f;
-  if (mx != -INFINITY) {
-#pragma unroll 4
-    for (int s = 0; s < S; ++s) {
-      const float ls = sp.part_lse[(size_t)s * rows + r];
-      // a chunk with no key for this row takes no part (weight 0, and its
-      // O_s is not read into the sum)
-      const bool none = ls == -INFINITY;
-      const float w = none ? 0.f : fast_exp2((ls - mx) * kLog2e);
-      sum += w;
+  for (int s0 = 0; s0 < S; s0 += G) {
+    float ls[G];
+    float4 a[G], b[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int s = min(s0 + g, S - 1);  // in bounds; chunks past S are left out below
+      ls[g] = sp.part_lse[(size_t)s * rows + r];
       const float4* src = (const float4*)(sp.part_o + ((size_t)s * rows + r) * D + 8 * c);
+      a[g] = src[0];
+      b[g] = src[1];
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      // a chunk with no key for this row (LSE -inf) takes no part, nor do
+      // its outputs (selected away, not multiplied by 0)
+      const bool use = s0 + g < S && ls[g] != -INFINITY;
+      const float lg = use ? ls[g] : mx;
+      const float m_new = fmaxf(mx, lg);
+      const float f = mx == -INFINITY ? 0.f : fast_exp2((mx - m_new) * kLog2e);
+      const float w = use ? fast_exp2((lg - m_new) * kLog2e) : 0.f;
       const float4 z = {0.f, 0.f, 0.f, 0.f};
-      const float4 a = none ? z : src[0], b = none ? z : src[1];
-      acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
-      acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+      const float4 av = use ? a[g] : z, bv = use ? b[g] : z;
+      sum = sum * f + w;
+      acc[0] = acc[0] * f + w * av.x; acc[1] = acc[1] * f + w * av.y;
+      acc[2] = acc[2] * f + w * av.z; acc[3] = acc[3] * f + w * av.w;
+      acc[4] = acc[4] * f + w * bv.x; acc[5] = acc[5] * f + w * bv.y;
+      acc[6] = acc[6] * f + w * bv.z; acc[7] = acc[7] * f + w * bv.w;
+      mx = m_new;
     }
   }
   const float inv = sum > 0.f ? 1.f / sum : 0.f;
