@@ -1,0 +1,102 @@
+"""GPU parity of the causal prefill's persistent walk run as one pipeline.
+
+With causal attention, no window, mask or kv_len, M >= N >= 256 and more
+work items than workgroups, each persistent workgroup walks several items (256-query tiles of some
+(batch, head)) and its iterations on the last tiles of one item already load,
+score and weigh the first tiles of the next ("Understanding FlashAttention",
+From loops to tiling: the tiles of one query block are independent of every
+other block's, so the order of the blocks is free).  These cases give every
+workgroup two or three items, end items in ragged query tiles, move the row
+reference on an item's first tile, and compare every element with the fp64
+oracle -- and bit for bit with the same launch given kv_len = M, which runs
+each item on its own (same arithmetic, same order).
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_33_amd as fa
+from exact_attention_33_amd import inputs
+from oracle.attention import attention_ref
+from tests.gpu_helpers import compare, default_scale, host64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def make(seed, B, H, N, M, D):
+    q, k, v = inputs.qkv_host(seed, B, H, N, M, D)
+    return tuple(inputs.to_device(x, "bf16", DEV) for x in (q, k, v))
+
+
+def check_walk(q, k, v, scale, what, rel_o=0.0):
+    B, H, N, D = q.shape
+    M = k.shape[2]
+    items = B * H * ((N + 255) // 256)
+    say(f"{what}: B={B} H={H} N={N} M={M} D={D}, {items} work items over 256 workgroups")
+    o, l = fa.fwd(q, k, v, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    say(f"{what}: same launch item by item (kv_len = M)")
+    o2, l2 = fa.fwd(q, k, v, scale=scale, causal=True, kv_len=[M] * B)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2), f"{what}: output differs from the item-by-item walk"
+    assert torch.equal(l, l2), f"{what}: LSE differs from the item-by-item walk"
+    say(f"{what}: oracle")
+    Or, Lr = attention_ref(host64(q), host64(k), host64(v), scale, True)
+    O = host64(o)
+    if rel_o:
+        # the part of the output error that scales with |O|: bf16 rounding
+        # of the output itself, at most half an ulp, 2^-8 |O|
+        excess = np.abs(O - Or) - rel_o * np.abs(Or)
+        say(f"{what}: O error beyond {rel_o:g} |O|: {float(excess.max()):.2e}")
+        O = Or + np.sign(O - Or) * np.maximum(excess, 0.0)
+    eo, el = compare(O, host64(l), Or, Lr, "bf16", what)
+    say(f"{what}: O {eo:.2e} LSE {el:.2e}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_walk_several_items_per_workgroup(D):
+    """600 items of 2 query tiles: workgroups run 2 or 3 items back to back."""
+    q, k, v = make(400 + D, 2, 150, 512, 512, D)
+    check_walk(q, k, v, default_scale(D), f"walk D={D}")
+
+
+@pytest.mark.parametrize("N,M,D", [(700, 700, 128), (300, 333, 64), (256, 256, 128)])
+def test_walk_ragged_and_shortest_items(N, M, D):
+    """A partial last query tile (700), more keys than queries (333 > 300), and
+    items of exactly four key tiles (256, the fewest the walk takes)."""
+    B = 2
+    H = 600 // (B * ((N + 255) // 256))
+    q, k, v = make(410 + N, B, H, N, M, D)
+    check_walk(q, k, v, default_scale(D), f"walk N={N} M={M} D={D}")
+
+
+def test_walk_reference_moves_on_an_item_first_tile():
+    """Scores that jump by ~29 (base 2) in key block 1 of tile 0 and in key
+    block 0 of tile 4: the first tile of every item moves its rows' reference
+    inside the tile -- in the iteration that still finishes the previous
+    item's output -- and the rows of the second query tile move it again."""
+    D, N = 128, 512
+    q, k, v = make(420, 2, 150, N, N, D)
+    scale = default_scale(D)
+    lam = 20.0 / scale
+    b = torch.zeros(N)
+    b[32:64] = 1.0      # tile 0, key block 1
+    b[256:288] = 2.0    # tile 4, key block 0
+    q[..., 0] = torch.tensor(lam, dtype=torch.bfloat16)
+    k[..., 0] = b.to(device=DEV, dtype=torch.bfloat16)
+    check_walk(q, k, v, scale, "walk reference moves")
+
+
+def test_walk_large_scores():
+    """Q x 16 (scores of several hundred): no overflow across item changes.
+    Rows this peaked take O from one or two values of V, up to about 4.5 in
+    magnitude, where half an ulp of bf16 is 2^-6: the output's own rounding
+    is allowed on top of the absolute bound."""
+    q, k, v = make(430, 2, 150, 512, 512, 128)
+    q = (q.float() * 16).to(torch.bfloat16)
+    check_walk(q, k, v, default_scale(128), "walk x16", rel_o=2.0 ** -8)
