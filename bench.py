@@ -342,7 +342,7 @@ def main():
         out["prefill"] = {"ms_mean": avg_p, "ms_min": min(ms_p), "ms_median": median(ms_p), "tflops": tfs,
                           "frac_bf16_peak": tfs / PEAK_BF16_TFLOPS, "flop_per_launch": flop_p}
         traffic = measured_traffic("prefill")
-        out["roofline"] = {"bound": "mfma", "kernel": "prefill_cont_kernel<128>",
+        out["roofline"] = {"bound": "mfma", "kernel": "prefill_cont_kernel<128, true, false>",
                            "achieved": tfs, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": tfs / PEAK_BF16_TFLOPS, "traffic": traffic}
     if do_d:
@@ -386,7 +386,7 @@ def main():
                      "frac": tf / PEAK_BF16_TFLOPS} if mfma_bound else
                     {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS})
-            roof.update({"kernel": "prefill_bf16_kernel<128, true, true, false>",
+            roof.update({"kernel": "prefill_cont_kernel<128, true, true>",
                          "traffic": measured_traffic("window", f"w{W}")})
             res[f"w{W}"] = {"window": [W - 1, 0], "ms_mean": avg, "ms_min": min(ms_w[W]), "ms_median": median(ms_w[W]),
                             "tflops": tf, "gbs": gbs, "flop_per_launch": flop,
@@ -672,11 +672,11 @@ COUNTER_LEGS = {
     "prefill": [(None, "prefill_cont", 2)],
     "decode": [(None, "splitkv_partial", 2)],
     "backward": [(None, "bwd_rowstat", 2)],
-    "window": [("w128", "prefill_bf16", 2), ("w2048", "prefill_bf16", 2)],
+    "window": [("w128", "prefill_cont", 2), ("w2048", "prefill_cont", 2)],
     "mask": [("documents8", "mask_blocks", 2), ("random50", "mask_blocks", 2),
              ("backward_documents8", "bwd_rowstat", 2)],
     "configs": [("B1_H8_N1024_D64_causal", "prefill_bf16", 2), ("B4_H16_N4096_D128_causal", "prefill_cont", 2),
-                ("B4_H16_N4096_D128_noncausal", "prefill_bf16", 2), ("B2_H32_N8192_D64_causal", "prefill_cont", 2),
+                ("B4_H16_N4096_D128_noncausal", "prefill_bf16", 2), ("B2_H32_N8192_D64_causal", "prefill_bf16", 2),
                 ("B1_H8_N1024_D64_causal_split_keys256", "prefill_split", 2)],
     "fp8": [(None, "prefill_fp8", 2)],
     "kvouter": [("tile_per_group", "kvouter", 3), ("head_per_group", "kvouter", 3)],
@@ -685,10 +685,10 @@ COUNTER_LEGS = {
 
 def prefill_kernel_name(w, causal):
     """The kernel the library runs for a prefill without window, mask or
-    kv_len: causal with more 256-query work items than the 256 persistent
-    workgroups runs the walk as one pipeline."""
-    if causal and w.N >= 256 and w.M >= w.N and w.B * w.H * ((w.N + 255) // 256) > 256:
-        return f"prefill_cont_kernel<{w.D}>"
+    kv_len: causal at D = 128 with more 256-query work items than the 256
+    persistent workgroups runs the walk as one pipeline."""
+    if causal and w.D == 128 and w.N >= 256 and w.M >= w.N and w.B * w.H * ((w.N + 255) // 256) > 256:
+        return f"prefill_cont_kernel<{w.D}, true, false>"
     return f"prefill_bf16_kernel<{w.D}, {str(causal).lower()}, false, false>"
 
 
@@ -710,7 +710,7 @@ def _leg_of_dispatches(rows):
     for i, (_, s, ns) in enumerate(rows):
         nxt = rows[i + 1][1] if i + 1 < len(rows) else ""
         seen_kvo |= s.startswith("kvouter")
-        if s == "prefill_cont_kernel<128>":
+        if s == "prefill_cont_kernel<128, true, false>":
             leg = ("prefill B2 H32 N8192 D128 causal (bench step)" if nxt.startswith("splitkv_partial") else
                    "configs B4 H16 N4096 D128 causal" if seen_kvo else
                    "setup (untimed forward for the backward's O, LSE)")
@@ -720,7 +720,7 @@ def _leg_of_dispatches(rows):
             leg = "backward (rowstat, both legs)"
         elif s.startswith("bwd_"):
             leg = "backward B2 H32 N8192 D128 causal" if s.endswith("false>") else "backward under the 8-document mask"
-        elif s == "prefill_bf16_kernel<128, true, true, false>":
+        elif s == "prefill_cont_kernel<128, true, true>":
             n["win"] += 1
             leg = "window 128 keys" if n["win"] <= 13 else "window 2048 keys"
         elif s == "prefill_bf16_kernel<128, true, false, true>" or s.startswith("mask_"):
@@ -736,9 +736,8 @@ def _leg_of_dispatches(rows):
             n["kvo"] += 1
             leg = "kvouter, one query tile per group" if n["kvo"] <= 3 else "kvouter, one head per group"
         elif s == "prefill_bf16_kernel<64, true, false, false>":
-            leg = "configs B1 H8 N1024 D64 causal"
-        elif s == "prefill_cont_kernel<64>":
-            leg = "configs B2 H32 N8192 D64 causal"
+            n["d64"] += 1
+            leg = "configs B1 H8 N1024 D64 causal" if n["d64"] <= 13 else "configs B2 H32 N8192 D64 causal"
         elif s == "prefill_bf16_kernel<128, false, false, false>":
             leg = "configs B4 H16 N4096 D128 non-causal"
         elif s.startswith(("prefill_split", "prefill_merge")):
@@ -765,8 +764,8 @@ def summarize_profiles(d):
     # kernel durations: rocprofv3 --stats, and the same trace split by leg
     lines = ["# rocprofv3 --stats kernel summary of the default bench sequence (durations in ns), the library's kernels",
              f"# command: {KTRACE_CMD}",
-             "# rows aggregate by kernel name: prefill_cont_kernel<128> serves the bench step (N = 8192),",
-             "# the configs leg (N = 4096) and one untimed setup call;",
+             "# rows aggregate by kernel name: prefill_cont_kernel<128, true, false> serves the bench step (N = 8192),",
+             "# the configs leg (N = 4096) and one untimed setup call, and prefill_bf16_kernel<64, true, false, false> two configs;",
              "# kernel_trace_by_leg_default_bench.txt splits the same trace by leg", "#",
              "# kernel, calls, average_ns, min_ns, max_ns, stddev_ns"]
     for r in csv.DictReader(open(os.path.join(d, "ktrace", "run_kernel_stats.csv"))):

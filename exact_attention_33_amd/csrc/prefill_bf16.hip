@@ -97,6 +97,7 @@
 //    each wave's words for a tile (64 rows x 2 words) travel HBM -> LDS as
 //    two coalesced 256-byte loads with the tile loads, three tiles ahead,
 //    and the bits are applied only on flagged tiles.
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 #include <utility>
@@ -166,7 +167,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
                                              int list_stride, const uint32_t* __restrict__ mask_blocks,
                                              const SplitArgs& sp) {
   static_assert(!SPLIT || (!WINDOW && !BITS), "key splits take no window and no mask");
-  static_assert(!CONT || (CAUSAL && !WINDOW && !BITS && !SPLIT), "one pipeline over the causal walk");
+  static_assert(!CONT || (!BITS && !SPLIT), "one pipeline over the walk: no element mask, no key splits");
   constexpr int BQ = kPrefillBlockQ, BK = kPrefillBlockK;
   constexpr int NW = kPrefillThreads / 64;   // waves per workgroup
   constexpr int QW = BQ / NW;                // queries per wave
@@ -216,7 +217,8 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
   const int64_t x_start = xcd * qx + (xcd < rx ? xcd : rx), x_count = qx + (xcd < rx ? 1 : 0);
   // CONT: the same walk, as one software pipeline: the body below starts with
   // the workgroup's first item and runs into each next item without draining
-  // (key/value tiles of every (batch, head) are all M keys, M >= N >= 256).
+  // (no kv_len, so every (batch, head) has M keys; the launcher checks that
+  // every item visits at least 4 key tiles).
   for (int64_t k = 0;; ++k) {
     int64_t logical;
     if constexpr (CONT) {
@@ -267,7 +269,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     // [tw, t_end) and tiles are addressed from 0.
     const int tw = WINDOW ? max(0, q0 + off - wl) / BK : (SPLIT ? split * sp.split_tiles : 0);
     const int t_end = kv_end > tw * BK ? (kv_end + BK - 1) / BK : tw;
-    const int t0 = BITS ? 0 : tw;
+    int t0 = BITS ? 0 : tw;  // (CONT: of the current item)
     int n_tiles = t_end - tw;
     int lo = 0;  // with a mask: list position of the first tile visited
     if constexpr (BITS) {
@@ -304,22 +306,34 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     const __bf16* Vg = (const __bf16*)p.v + (size_t)bh * M * D + (size_t)t0 * BK * D;
     // CONT: the item after the current one in the walk (has_nx false past the
     // last), round kw being the current one's.  Every item has at least 4
-    // tiles (M >= N >= 256).
+    // tiles (the launcher checks).
     int64_t kw = 0, bh_n = 0;
     bool has_nx = false;
-    int qw0_n = 0, n_n = 0;
+    int qw0_n = 0, n_n = 0, t0_n = 0;
     const __bf16 *Qg_n = nullptr, *Kg_n = nullptr, *Vg_n = nullptr;
+    // Round k of a causal walk pairs heavy and light query tiles (above);
+    // with a window the items are nearly equal but for a head's first query
+    // tiles, and round k takes item k W + (u + k S) mod W (S = W / 8), so
+    // that each workgroup's rounds step through the query tiles and meet the
+    // short ones as often as any other workgroup.
     auto walk_next = [&]() {
-      const int64_t kn = kw + 1, within = kn * W + ((kn & 1) ? W - 1 - u : u);
+      const int64_t kn = kw + 1;
+      const int64_t within = kn * W + (CAUSAL && !WINDOW ? ((kn & 1) ? W - 1 - u : u)
+                                                         : (u + kn * max(1, W / 8)) % W);
       has_nx = within < x_count;
       const int64_t it = x_start + (has_nx ? within : 0);
-      const int qt_n = n_qtiles - 1 - (int)(it % n_qtiles);
+      int qt_n = (int)(it % n_qtiles);
+      if (CAUSAL) qt_n = n_qtiles - 1 - qt_n;
       bh_n = it / n_qtiles;
-      qw0_n = qt_n * BQ + QW * ws;
-      n_n = (min(M, min(qt_n * BQ + BQ, N) + off) + BK - 1) / BK;
+      // the item's tiles, as for the current item above (kv_len = M)
+      const int q0_n = qt_n * BQ, ql_n = min(q0_n + BQ, N) - 1;
+      const int kv_end_n = UPPER ? min(kend, ql_n + off + wr + 1) : kend;
+      t0_n = WINDOW ? max(0, q0_n + off - wl) / BK : 0;
+      n_n = (kv_end_n > t0_n * BK ? (kv_end_n + BK - 1) / BK : t0_n) - t0_n;
+      qw0_n = q0_n + QW * ws;
       Qg_n = (const __bf16*)p.q + (size_t)bh_n * N * D;
-      Kg_n = (const __bf16*)p.k + (size_t)bh_n * M * D;
-      Vg_n = (const __bf16*)p.v + (size_t)bh_n * M * D;
+      Kg_n = (const __bf16*)p.k + (size_t)bh_n * M * D + (size_t)t0_n * BK * D;
+      Vg_n = (const __bf16*)p.v + (size_t)bh_n * M * D + (size_t)t0_n * BK * D;
     };
     if constexpr (CONT) walk_next();
 
@@ -497,9 +511,10 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     // Tiles that cross the diagonal or the kv_len boundary -- and tiles past
     // the workgroup's last one, whose LDS holds stale data -- are masked
     // element by element; every other tile is fully visible to the wave.
-    // qwx: the wave's first query in the tile's work item.
-    auto need_mask = [&](int e, int qwx) {
-      const int k0 = (tile_index(e) + t0) * BK;
+    // qwx, t0x: the wave's first query and the first tile of the tile's
+    // work item.
+    auto need_mask = [&](int e, int qwx, int t0x) {
+      const int k0 = (tile_index(e) + t0x) * BK;
       return (BITS && e < 0) | (k0 + BK > kend) | (UPPER && k0 + BK - 1 > qwx + off + wr) |
              (WINDOW && k0 < qwx + QW - 1 + off - wl);
     };
@@ -681,8 +696,8 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     // With a mask, Ms holds the tile's mask words and key 8 (r / 4) + 4 hl + r % 4
     // of key block nb is bit 8 (r / 4) + r % 4 of this lane's word shifted down
     // by 4 hl.
-    auto apply_mask = [&](int e, int qwx, f32x16 (&s)[NKB][NQB], const uint32_t* Ms) {
-      const int k0 = (tile_index(e) + t0) * BK;
+    auto apply_mask = [&](int e, int qwx, int t0x, f32x16 (&s)[NKB][NQB], const uint32_t* Ms) {
+      const int k0 = (tile_index(e) + t0x) * BK;
   #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const int qrow = qwx + 32 * qb + ql;
@@ -719,7 +734,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
       mfma_guard();  // compute_s just wrote the scores
   #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-      if (need_mask(e, qw0)) apply_mask(e, qw0, s, Ms);
+      if (need_mask(e, qw0, t0)) apply_mask(e, qw0, t0, s, Ms);
       sm_begin();
       static_for<NU_EM>([&](auto uc) { unit_em(s, uc); });
       sm_check1(s, false);
@@ -846,7 +861,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
       mfma_guard();  // the last iteration's final MFMAs wrote the scores
   #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-      if (need_mask(e1, qw0)) apply_mask(e1, qw0, sacc, Ms);
+      if (need_mask(e1, qw0, t0)) apply_mask(e1, qw0, t0, sacc, Ms);
       iteration(e4, e2, e3, Ks, Vs, Kdst, Vdst, Mdst, Kg, Vg, false, false);
       // This wave's loads of the previous iteration (K(t+3), V(t+1)) are done
       // (loads complete in order: only this iteration's NITEM may be pending),
@@ -953,10 +968,10 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         }
       };
       int t = 0;  // tile of the current item
-      // first rows of the current and the next item's head; byte offsets of
-      // the last K and V tiles loaded (K(3) and V(1) in the prologue)
-      int row_nx = (int)bh_n * M;
-      int kofs = ((int)bh * M + 3 * BK) * ROWB, vofs = ((int)bh * M + BK) * ROWB;
+      // first row of the next item's first tile; byte offsets of the last K
+      // and V tiles loaded (K(3) and V(1) in the prologue)
+      int row_nx = (int)bh_n * M + t0_n * BK;
+      int kofs = ((int)bh * M + (t0 + 3) * BK) * ROWB, vofs = ((int)bh * M + (t0 + 1) * BK) * ROWB;
       float m_fin[NQB], l_fin[NQB];
   #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) m_fin[qb] = l_fin[qb] = 0.f;
@@ -967,7 +982,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         // item's once past this one's last
         const bool sm_nx = has_nx && t + 1 >= n;
         const int e1 = sm_nx ? t + 1 - n : t + 1;
-        const int qw_sm = sm_nx ? qw0_n : qw0;
+        const int qw_sm = sm_nx ? qw0_n : qw0, t0_sm = sm_nx ? t0_n : t0;
         // first bytes of K(t+4) and V(t+2) in the whole tensors: a tile on
         // from the last, or the next item's first tile
         kofs = t + 4 == n && has_nx ? row_nx * ROWB : kofs + BK * ROWB;
@@ -975,7 +990,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         mfma_guard();  // the last iteration's final MFMAs wrote the scores
   #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-        if (need_mask(e1, qw_sm)) apply_mask(e1, qw_sm, sacc, Mb0);
+        if (need_mask(e1, qw_sm, t0_sm)) apply_mask(e1, qw_sm, t0_sm, sacc, Mb0);
         iteration(kofs, vofs, 0, Ks, Vs, Kdst, Vdst, Mb0, nullptr, nullptr, t == n - 1, has_nx && t == n - 2);
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NITEM) : "memory");
         if (__builtin_expect(t < n - 3, 1)) {
@@ -1007,12 +1022,13 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         ++kw;
         bh = bh_n;
         qw0 = qw0_n;
+        t0 = t0_n;
         n_tiles = n_n;
         Qg = Qg_n;
         Kg = Kg_n;
         Vg = Vg_n;
         walk_next();
-        row_nx = (int)bh_n * M;
+        row_nx = (int)bh_n * M + t0_n * BK;
         t = 0;
         return false;
       };
@@ -1042,12 +1058,12 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
   prefill_body<D, CAUSAL, WINDOW, BITS, false>(p, n_qtiles, tile_lists, list_stride, mask_blocks, SplitArgs{});
 }
 
-// Causal, no window, mask or kv_len, M >= N >= 256, several items per
-// workgroup: the persistent walk as one pipeline.
-template <int D>
+// Causal or windowed, no mask, key splits or kv_len, M >= N >= 256,
+// several items per workgroup: a persistent walk as one pipeline.
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_cont_kernel(Problem p, int n_qtiles) {
-  prefill_body<D, true, false, false, false, true>(p, n_qtiles, nullptr, 0, nullptr, SplitArgs{});
+  prefill_body<D, CAUSAL, WINDOW, false, false, true>(p, n_qtiles, nullptr, 0, nullptr, SplitArgs{});
 }
 
 template <int D, bool CAUSAL>
@@ -1130,6 +1146,37 @@ void launch_prefill_dm(const Problem& p, dim3 grid, hipStream_t stream, int n_qt
   }
 }
 
+// Fewest key tiles any work item visits, by the kernel's own arithmetic for
+// kv_len = M (no mask): the pipelined walk needs at least 4 (it loads K four
+// tiles ahead).
+int min_item_tiles(const Problem& p, int n_qtiles) {
+  const int N = p.N, M = p.M, off = M - N, BQ = kPrefillBlockQ, BK = kPrefillBlockK;
+  const int wl = p.window ? std::min<int64_t>(p.wl, (int64_t)N + M) : 0;
+  const int wr = p.causal ? 0 : (p.window ? std::min<int64_t>(p.wr, (int64_t)N + M) : 0);
+  int fewest = INT32_MAX;
+  for (int qt = 0; qt < n_qtiles; ++qt) {
+    const int q0 = qt * BQ, q_last = std::min(q0 + BQ, N) - 1;
+    const int kv_end = (p.causal || p.window) ? std::min(M, q_last + off + wr + 1) : M;
+    const int tw = p.window ? std::max(0, q0 + off - wl) / BK : 0;
+    const int t_end = kv_end > tw * BK ? (kv_end + BK - 1) / BK : tw;
+    fewest = std::min(fewest, t_end - tw);
+  }
+  return fewest;
+}
+
+void launch_prefill_cont(const Problem& p, dim3 grid, hipStream_t stream, int n_qtiles) {
+  const dim3 block(kPrefillThreads);
+  // windowed, or causal at D = 128 (the caller checks)
+  if (p.D == 64) {
+    if (p.causal) hipLaunchKernelGGL((prefill_cont_kernel<64, true, true>), grid, block, 0, stream, p, n_qtiles);
+    else hipLaunchKernelGGL((prefill_cont_kernel<64, false, true>), grid, block, 0, stream, p, n_qtiles);
+  } else {
+    if (!p.window) hipLaunchKernelGGL((prefill_cont_kernel<128, true, false>), grid, block, 0, stream, p, n_qtiles);
+    else if (p.causal) hipLaunchKernelGGL((prefill_cont_kernel<128, true, true>), grid, block, 0, stream, p, n_qtiles);
+    else hipLaunchKernelGGL((prefill_cont_kernel<128, false, true>), grid, block, 0, stream, p, n_qtiles);
+  }
+}
+
 template <int D>
 void launch_prefill_d(const Problem& p, dim3 grid, hipStream_t stream, int n_qtiles,
                       const int32_t* lists, int stride, const uint32_t* blocks) {
@@ -1163,15 +1210,19 @@ hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, void* workspa
     else hipLaunchKernelGGL(prefill_merge_kernel<128>, mgrid, dim3(256), 0, stream, p, sp);
     return hipGetLastError();
   }
-  if (p.causal && !p.window && !p.mask && !p.kv_len && p.N >= kPrefillBlockQ && p.M >= p.N &&
-      (int64_t)p.B * p.H * p.M * p.D * 2 <= INT32_MAX && (int64_t)p.B * p.H * n_qtiles > plan.grid) {
+  const int64_t n_items = (int64_t)p.B * p.H * n_qtiles;
+  if ((p.window || (p.causal && p.D == 128)) && !p.mask && !p.kv_len && p.N >= kPrefillBlockQ && p.M >= p.N &&
+      (int64_t)p.B * p.H * p.M * p.D * 2 <= INT32_MAX && n_items > kPrefillPersistGrid &&
+      min_item_tiles(p, n_qtiles) >= 4) {
     // every work item has at least 4 key tiles, one buffer descriptor covers
-    // all of K (and of V), and some workgroup walks more than one item: one
-    // pipeline per workgroup (with one item each, the item-by-item kernel
-    // measured 3-4% faster)
-    const dim3 block(kPrefillThreads);
-    if (p.D == 64) hipLaunchKernelGGL(prefill_cont_kernel<64>, grid, block, 0, stream, p, n_qtiles);
-    else hipLaunchKernelGGL(prefill_cont_kernel<128>, grid, block, 0, stream, p, n_qtiles);
+    // all of K (and of V), and each workgroup walks more than one item: one
+    // pipeline per persistent workgroup (one per CU; with one item each, the
+    // item-by-item kernel measured 3-4% faster).  Not for plain non-causal
+    // attention, whose long uniform items gain little and whose D = 128 form
+    // the compiler cannot allocate without spills, nor for plain causal
+    // attention at D = 64, whose iterations are half as long, so that the
+    // per-iteration cost of the walk eats the gain (measured -0.5%).
+    launch_prefill_cont(p, dim3(kPrefillPersistGrid), stream, n_qtiles);
     return hipGetLastError();
   }
   const int32_t* lists = nullptr;

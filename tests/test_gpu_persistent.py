@@ -1,7 +1,7 @@
 """GPU parity of the causal prefill's persistent walk run as one pipeline.
 
-With causal attention, no window, mask or kv_len, M >= N >= 256 and more
-work items than workgroups, each persistent workgroup walks several items (256-query tiles of some
+With causal or windowed attention, no mask or kv_len, M >= N >= 256 and
+more work items than workgroups, each persistent workgroup walks several items (256-query tiles of some
 (batch, head)) and its iterations on the last tiles of one item already load,
 score and weigh the first tiles of the next ("Understanding FlashAttention",
 From loops to tiling: the tiles of one query block are independent of every
@@ -33,20 +33,21 @@ def make(seed, B, H, N, M, D):
     return tuple(inputs.to_device(x, "bf16", DEV) for x in (q, k, v))
 
 
-def check_walk(q, k, v, scale, what, rel_o=0.0):
+def check_walk(q, k, v, scale, what, rel_o=0.0, causal=True, window=None):
     B, H, N, D = q.shape
     M = k.shape[2]
     items = B * H * ((N + 255) // 256)
-    say(f"{what}: B={B} H={H} N={N} M={M} D={D}, {items} work items over 256 workgroups")
-    o, l = fa.fwd(q, k, v, scale=scale, causal=True)
+    say(f"{what}: B={B} H={H} N={N} M={M} D={D} causal={causal} window={window}, "
+        f"{items} work items over 256 workgroups")
+    o, l = fa.fwd(q, k, v, scale=scale, causal=causal, window=window)
     torch.cuda.synchronize()
     say(f"{what}: same launch item by item (kv_len = M)")
-    o2, l2 = fa.fwd(q, k, v, scale=scale, causal=True, kv_len=[M] * B)
+    o2, l2 = fa.fwd(q, k, v, scale=scale, causal=causal, window=window, kv_len=[M] * B)
     torch.cuda.synchronize()
     assert torch.equal(o, o2), f"{what}: output differs from the item-by-item walk"
     assert torch.equal(l, l2), f"{what}: LSE differs from the item-by-item walk"
     say(f"{what}: oracle")
-    Or, Lr = attention_ref(host64(q), host64(k), host64(v), scale, True)
+    Or, Lr = attention_ref(host64(q), host64(k), host64(v), scale, causal, window=window)
     O = host64(o)
     if rel_o:
         # the part of the output error that scales with |O|: bf16 rounding
@@ -60,7 +61,8 @@ def check_walk(q, k, v, scale, what, rel_o=0.0):
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_walk_several_items_per_workgroup(D):
-    """600 items of 2 query tiles: workgroups run 2 or 3 items back to back."""
+    """600 items of 2 query tiles: workgroups run 2 or 3 items back to back
+    (plain causal D = 64 runs item by item; its bits must still agree)."""
     q, k, v = make(400 + D, 2, 150, 512, 512, D)
     check_walk(q, k, v, default_scale(D), f"walk D={D}")
 
@@ -100,3 +102,22 @@ def test_walk_large_scores():
     q, k, v = make(430, 2, 150, 512, 512, 128)
     q = (q.float() * 16).to(torch.bfloat16)
     check_walk(q, k, v, default_scale(128), "walk x16", rel_o=2.0 ** -8)
+
+
+@pytest.mark.parametrize("N,M,D,causal,window", [
+    (512, 512, 128, True, (127, 0)),    # the pages' 128-wide window
+    (700, 700, 64, True, (300, 0)),     # ragged last query tile
+    (512, 512, 128, True, (0, 0)),      # the diagonal only: items of 4-5 tiles
+    (512, 512, 128, False, (100, 200)),
+    (512, 600, 128, False, (100, 150)),  # more keys than queries (offset 88)
+    (300, 333, 64, False, (50, 50)),    # a last item of 3 tiles: item by item
+    (512, 512, 64, True, (5000, 0)),    # wider than the sequence: plain causal
+])
+def test_walk_windows(N, M, D, causal, window):
+    """Local windows: items of a few tiles that start at the window's first
+    tile, each workgroup walking two or three of them."""
+    B = 2
+    H = 600 // (B * ((N + 255) // 256))
+    q, k, v = make(440 + N + D, B, H, N, M, D)
+    check_walk(q, k, v, default_scale(D), f"walk window {window} N={N} M={M} D={D}",
+               causal=causal, window=window)
