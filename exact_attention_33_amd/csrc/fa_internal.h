@@ -78,6 +78,10 @@ constexpr int kPrefillPersistGrid = 256;
 // kernel copies a list into LDS, so a list holds at most kMaskMaxTiles - 1
 // tiles.
 constexpr int kMaskMaxTiles = 4096;
+// The causal prefill's pipelined walk with a mask holds the lists of all of a
+// workgroup's work items in LDS (at most kMaskMaxTiles - 5 entries), for at
+// most kWalkMaxItems items.
+constexpr int kWalkMaxItems = 64;
 __host__ __device__ inline int32_t mask_list_stride(int M) { return (M + kPrefillBlockK - 1) / kPrefillBlockK + 1; }
 __host__ __device__ inline int32_t mask_words(int M) { return (M + 31) / 32; }
 // Mask words of one (query tile, key tile) pair, copied by the pre-pass into
@@ -168,12 +172,15 @@ __host__ __device__ inline int32_t mask_stage_stride(int N) { return (N + kBwdSt
 // (query tile, 64-key tile) (0: no key kept, 1: all, 2: some) and per query
 // tile a row of 1 + ceil(M / 64) blocks; with stages, one class byte per
 // (256-key tile, 64-query stage) and per key tile a row of 1 + ceil(N / 64)
-// blocks.  Every region starts on 256 bytes.
+// blocks; without stages, `items` int32 (the order in which the causal
+// prefill's pipelined walk takes the work items).  Every region starts on 256
+// bytes.
 struct MaskWorkspace {
-  size_t lists, stage_lists, cls, blocks, stage_cls, stage_blocks, end;
+  size_t lists, stage_lists, cls, blocks, stage_cls, stage_blocks, order, end;
 };
 inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
-inline MaskWorkspace mask_workspace(int N, int M, int mask_b, int mask_h, size_t base, bool stages) {
+inline MaskWorkspace mask_workspace(int N, int M, int mask_b, int mask_h, size_t base, bool stages,
+                                    int64_t items = 0) {
   const size_t mbh = (size_t)mask_b * (size_t)mask_h;
   const size_t n_qt = (size_t)((N + kPrefillBlockQ - 1) / kPrefillBlockQ);
   const size_t n_kt = (size_t)(mask_list_stride(M) - 1);
@@ -186,7 +193,10 @@ inline MaskWorkspace mask_workspace(int N, int M, int mask_b, int mask_h, size_t
   w.blocks = align256(w.cls + mbh * n_qt * n_kt);
   w.stage_cls = align256(w.blocks + mbh * n_qt * (n_kt + 1) * kMaskBlockBytes);
   w.stage_blocks = stages ? align256(w.stage_cls + mbh * n_kt256 * n_st) : w.stage_cls;
-  w.end = stages ? w.stage_blocks + mbh * n_kt256 * (n_st + 1) * kMaskBlockBytes : w.stage_cls;
+  w.order = w.stage_cls;
+  w.end = stages ? w.stage_blocks + mbh * n_kt256 * (n_st + 1) * kMaskBlockBytes
+                 : (items > 0 ? align256(w.stage_cls) + (size_t)items * sizeof(int32_t) : w.stage_cls);
+  if (!stages && items > 0) w.order = align256(w.stage_cls);
   return w;
 }
 // mask_b, mask_h: 0 without a mask
@@ -204,9 +214,14 @@ hipError_t launch_bwd_bf16(const BwdProblem& p, hipStream_t stream);
 // Element-mask pre-pass: classifies the mask's tiles, lists them, and copies
 // the words of the tiles the mask keeps in part into blocks (layout above),
 // into the workspace regions `w` names relative to `ws`; with stages also
-// the dK/dV pass's stage lists and blocks.
+// the dK/dV pass's stage lists and blocks.  walk (B, H given): the forward
+// lists are cut at the causal limit (no kv_len, M >= N >= 256) and filled up
+// to 4 tiles with fully masked ones, and the work items of each XCD's range
+// are ordered by tile count, most first, into w.order, for the causal
+// prefill's pipelined walk.
 void launch_mask_prep(const uint32_t* mask, int N, int M, int mask_w, int mask_b, int mask_h,
-                      void* ws, const MaskWorkspace& w, bool stages, hipStream_t stream);
+                      void* ws, const MaskWorkspace& w, bool stages, hipStream_t stream, bool walk = false,
+                      int B = 0, int H = 0);
 
 // Records a failure for fa_last_error() on the calling thread (printf-style
 // detail) and returns `st`; shared by every C entry point.

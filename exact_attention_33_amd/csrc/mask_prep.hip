@@ -9,6 +9,7 @@
 //      per row); pairs kept whole share one all-ones block per row of blocks;
 //   2. mask_lists_kernel compacts the classes into the ascending tile lists
 //      the kernels walk (bit 31 set on tiles the mask keeps in part only).
+#include "device_common.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -157,11 +158,20 @@ __global__ __launch_bounds__(256) void mask_blocks_kernel(const uint32_t* __rest
 // One workgroup per list: lists [0, n_fwd) take `n` classes each from cls,
 // the rest (stage lists) `n_s` classes each from stage_cls.  Entries ascend;
 // bit 31 marks class 2; entry 0 of a list holds its length.
+// walk_n_qt > 0 (causal forward on the pipelined walk, N >= 256, M >= N,
+// no kv_len): each forward list (query tile qt = list % walk_n_qt) is cut at
+// the causal limit, the first tile past the tile's last query's last key,
+// and a list left with fewer than 4 tiles is filled up to 4 with tiles the
+// mask does not touch, flagged as kept in part and given an all-zero block
+// (every key masked: weights of exactly 0).  A list of such a query tile
+// then holds exactly the tiles the prefill visits.
 __global__ __launch_bounds__(256) void mask_lists_kernel(const uint8_t* __restrict__ cls, int n,
                                                          int32_t* __restrict__ lists, int64_t n_fwd,
                                                          const uint8_t* __restrict__ stage_cls, int n_s,
-                                                         int32_t* __restrict__ stage_lists) {
+                                                         int32_t* __restrict__ stage_lists, int walk_n_qt,
+                                                         int N, int M, uint32_t* __restrict__ blocks) {
   __shared__ int wave_n[4];
+  __shared__ int pad_tiles[4], n_pad;
   const int64_t g = blockIdx.x;
   const bool fwd = g < n_fwd;
   const int len = fwd ? n : n_s;
@@ -181,13 +191,108 @@ __global__ __launch_bounds__(256) void mask_lists_kernel(const uint8_t* __restri
     base += wave_n[0] + wave_n[1] + wave_n[2] + wave_n[3];
     __syncthreads();
   }
-  if (tid == 0) L[0] = base;
+  if (!fwd || walk_n_qt == 0) {
+    if (tid == 0) L[0] = base;
+    return;
+  }
+  __syncthreads();  // the entries are written
+  const int qt = (int)(g % walk_n_qt);
+  const int kv_end = min(M, min(qt * kPrefillBlockQ + kPrefillBlockQ, N) + (M - N));
+  const int t_end = (kv_end + kPrefillBlockK - 1) / kPrefillBlockK;
+  // entries below t_end (the list ascends)
+  int keep = 0;
+  for (int c0 = 0; c0 < base; c0 += 256) {
+    const int idx = c0 + tid;
+    const bool below = idx < base && (L[1 + idx] & 0x7FFFFFFF) < t_end;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(below);
+    if (lane == 0) wave_n[wv] = __builtin_popcountll(bal);
+    __syncthreads();
+    keep += wave_n[0] + wave_n[1] + wave_n[2] + wave_n[3];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int np = 0;
+    if (keep < 4) {
+      // merge the kept entries with the first untouched tiles, in order
+      int out[4], nk = 0, pos = 0;
+      for (int t = 0; t < t_end && nk < 4; ++t) {
+        if (C[t] != 0) {
+          out[nk++] = L[1 + pos++];
+        } else if (np < 4 - keep) {
+          out[nk++] = (int32_t)((uint32_t)t | 0x80000000u);
+          pad_tiles[np++] = t;
+        }
+      }
+      for (int i = 0; i < nk; ++i) L[1 + i] = out[i];
+      keep = nk;
+    }
+    n_pad = np;
+    L[0] = keep;
+  }
+  __syncthreads();
+  // zero the blocks of the filler tiles (tile t: block t + 1 of the row)
+  constexpr int BW = kMaskBlockBytes / 4;
+  uint32_t* frow = blocks + g * (int64_t)(n + 1) * BW;
+  for (int i = 0; i < n_pad; ++i) {
+    frow[(int64_t)(pad_tiles[i] + 1) * BW + tid] = 0u;
+    frow[(int64_t)(pad_tiles[i] + 1) * BW + tid + 256] = 0u;
+  }
+}
+
+// Order of the causal prefill's pipelined walk.  The walk deals each XCD a
+// contiguous range of work items (as the prefill's persistent grid does) and
+// takes them round by round, W workgroups a round, alternating direction; in
+// mask order, round k takes the k-th W items of the range sorted by tile
+// count, most first (ties by item), so that a workgroup's items are as heavy
+// as any other's: a snake over the sorted range.  One workgroup per XCD;
+// at most kOrderMax items per range.
+constexpr int kOrderMax = 4096;
+__global__ __launch_bounds__(1024) void mask_order_kernel(const int32_t* __restrict__ lists, int stride,
+                                                          int64_t n_items, int n_qt, int H, int mask_b,
+                                                          int mask_h, int32_t* __restrict__ order) {
+  __shared__ uint64_t key[kOrderMax];
+  const int x = blockIdx.x, tid = threadIdx.x;
+  const int64_t qx = n_items / kNumXcd, rx = n_items % kNumXcd;
+  const int64_t x_start = x * qx + (x < rx ? x : rx);
+  const int x_count = (int)(qx + (x < rx ? 1 : 0));
+  int P = 1;
+  while (P < x_count) P *= 2;
+  for (int j = tid; j < P; j += 1024) {
+    uint64_t kj = ~0ull;  // past the range: sorts last
+    if (j < x_count) {
+      const int64_t it = x_start + j, bh = it / n_qt;
+      const int qt = n_qt - 1 - (int)(it % n_qt);
+      const int bm = mask_b > 1 ? (int)(bh / H) : 0, hm = mask_h > 1 ? (int)(bh % H) : 0;
+      const uint32_t n = (uint32_t)lists[((int64_t)(bm * mask_h + hm) * n_qt + qt) * stride];
+      kj = ((uint64_t)(~n) << 32) | (uint32_t)j;  // most tiles first, then by item
+    }
+    key[j] = kj;
+  }
+  __syncthreads();
+  // bitonic sort, ascending
+  for (int size = 2; size <= P; size *= 2)
+    for (int stride2 = size / 2; stride2 > 0; stride2 /= 2) {
+      for (int j = tid; j < P; j += 1024) {
+        const int partner = j ^ stride2;
+        if (partner > j) {
+          const bool up = (j & size) == 0;
+          const uint64_t a = key[j], b = key[partner];
+          if ((a > b) == up) {
+            key[j] = b;
+            key[partner] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int j = tid; j < x_count; j += 1024) order[x_start + j] = (int32_t)(uint32_t)(key[j] & 0xFFFFFFFFu);
 }
 
 }  // namespace
 
 void launch_mask_prep(const uint32_t* mask, int N, int M, int mask_w, int mask_b, int mask_h,
-                      void* ws, const MaskWorkspace& w, bool stages, hipStream_t stream) {
+                      void* ws, const MaskWorkspace& w, bool stages, hipStream_t stream, bool walk, int B,
+                      int H) {
   char* base = (char*)ws;
   const int64_t mbh = (int64_t)mask_b * mask_h;
   const int n_qt = (N + kPrefillBlockQ - 1) / kPrefillBlockQ;
@@ -205,7 +310,11 @@ void launch_mask_prep(const uint32_t* mask, int N, int M, int mask_w, int mask_b
     hipLaunchKernelGGL(mask_lists_kernel, dim3((unsigned)(n_fwd + n_bwd)), dim3(256), 0, stream,
                      (const uint8_t*)(base + w.cls), mask_list_stride(M) - 1, (int32_t*)(base + w.lists),
                      n_fwd, (const uint8_t*)(base + w.stage_cls), mask_stage_stride(N) - 1,
-                     (int32_t*)(base + w.stage_lists));
+                     (int32_t*)(base + w.stage_lists), walk ? n_qt : 0, N, M, (uint32_t*)(base + w.blocks));
+  if (walk && n_qt > 0 && (int64_t)B * H > 0)
+    hipLaunchKernelGGL(mask_order_kernel, dim3(kNumXcd), dim3(1024), 0, stream, (const int32_t*)(base + w.lists),
+                       mask_list_stride(M), (int64_t)B * H * n_qt, n_qt, H, mask_b, mask_h,
+                       (int32_t*)(base + w.order));
 }
 
 }  // namespace fa

@@ -191,8 +191,9 @@ fa_status make_plan(const fa_shape& s, fa_dtype dt, int causal,
           *why = "an element mask on FA_PATH_PREFILL needs N * ceil(M / 32) * 4 < 2^31";
           return FA_ERR_UNSUPPORTED;
         }
-        // the pre-pass's tile lists, tile classes and blocks of mask words
-        plan->ws_bytes = mask_workspace(s.N, s.M, mask_b, mask_h, 0, false).end;
+        // the pre-pass's tile lists, tile classes and blocks of mask words,
+        // and the order of the work items for the pipelined causal walk
+        plan->ws_bytes = mask_workspace(s.N, s.M, mask_b, mask_h, 0, false, causal ? bh * ceil_div(s.N, kPrefillBlockQ) : 0).end;
       }
       break;
     case FA_PATH_F32:

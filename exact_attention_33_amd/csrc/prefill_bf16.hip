@@ -165,9 +165,10 @@ struct SplitArgs {
 template <int D, bool CAUSAL, bool WINDOW, bool BITS, bool SPLIT, bool CONT = false>
 __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, const int32_t* __restrict__ tile_lists,
                                              int list_stride, const uint32_t* __restrict__ mask_blocks,
-                                             const SplitArgs& sp) {
+                                             const SplitArgs& sp, const int32_t* __restrict__ walk_order = nullptr) {
   static_assert(!SPLIT || (!WINDOW && !BITS), "key splits take no window and no mask");
-  static_assert(!CONT || (!BITS && !SPLIT), "one pipeline over the walk: no element mask, no key splits");
+  static_assert(!CONT || (!SPLIT && (!BITS || (CAUSAL && !WINDOW))),
+                "one pipeline over the walk: no key splits; a mask only with causal attention");
   constexpr int BQ = kPrefillBlockQ, BK = kPrefillBlockK;
   constexpr int NW = kPrefillThreads / 64;   // waves per workgroup
   constexpr int QW = BQ / NW;                // queries per wave
@@ -197,6 +198,10 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
   // Element mask: the workgroup's list of key tiles, and a ring of three
   // tiles' mask words, per wave [word][64 rows].
   __shared__ int tlist[BITS ? kMaskMaxTiles : 1];
+  // CONT with a mask: tlist holds the workgroup's whole tile stream (its
+  // items' lists one after another), walk_n the tiles of each item
+  __shared__ int walk_n[CONT && BITS ? kWalkMaxItems : 1];
+  __shared__ int walk_item[CONT && BITS ? kWalkMaxItems : 1];
   __shared__ __attribute__((aligned(256))) uint32_t Mb0[BITS ? NW * 128 : 1];
   __shared__ __attribute__((aligned(256))) uint32_t Mb1[BITS ? NW * 128 : 1];
   __shared__ __attribute__((aligned(256))) uint32_t Mb2[BITS ? NW * 128 : 1];
@@ -223,7 +228,8 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     int64_t logical;
     if constexpr (CONT) {
       if (k > 0 || u >= x_count) break;
-      logical = x_start + u;
+      // with a mask, the pre-pass's order (the range sorted by tile count)
+      logical = x_start + (BITS ? walk_order[x_start + u] : u);
     } else if constexpr (PERSIST) {
       const int64_t within = k * W + ((k & 1) ? W - 1 - u : u);
       if (within >= x_count) break;
@@ -272,7 +278,53 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     int t0 = BITS ? 0 : tw;  // (CONT: of the current item)
     int n_tiles = t_end - tw;
     int lo = 0;  // with a mask: list position of the first tile visited
-    if constexpr (BITS) {
+    if constexpr (CONT && BITS) {
+      // The workgroup's items in walk order and their tiles, one stream: the
+      // pre-pass cut each list at the causal limit and filled it up to 4
+      // tiles, so a list holds exactly the item's visited tiles.  Past the
+      // last item, 5 entries one past kv_len (zeros, all masked).
+      __shared__ int walk_off[kWalkMaxItems + 1];
+      __shared__ int walk_list[kWalkMaxItems];
+      int n_wk = 0;
+      while (n_wk < kWalkMaxItems) {
+        const int64_t within = (int64_t)n_wk * W + ((n_wk & 1) ? W - 1 - u : u);
+        if (within >= x_count) break;
+        ++n_wk;
+      }
+      if (tid < n_wk) {
+        const int64_t within = (int64_t)tid * W + ((tid & 1) ? W - 1 - u : u);
+        const int64_t it = x_start + walk_order[x_start + within];
+        walk_item[tid] = (int)it;
+        const int qt_i = n_qtiles - 1 - (int)(it % n_qtiles);
+        const int64_t bh_i = it / n_qtiles;
+        const int bm = p.mask_b > 1 ? (int)(bh_i / p.H) : 0, hm = p.mask_h > 1 ? (int)(bh_i % p.H) : 0;
+        const int li = (int)(((int64_t)(bm * p.mask_h + hm) * n_qtiles + qt_i) * list_stride);
+        walk_list[tid] = li;
+        walk_n[tid] = tile_lists[li];
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int acc = 0;
+        for (int i = 0; i < n_wk; ++i) {
+          walk_off[i] = acc;
+          acc += walk_n[i];
+        }
+        walk_off[n_wk] = acc;
+      }
+      __syncthreads();
+      const int total = walk_off[n_wk];
+      for (int j = tid; j < total + 5; j += kPrefillThreads) {
+        int e = (kvl + BK - 1) / BK;
+        if (j < total) {
+          int i = 0;
+          while (walk_off[i + 1] <= j) ++i;
+          e = tile_lists[walk_list[i] + 1 + (j - walk_off[i])];
+        }
+        tlist[j] = e;
+      }
+      __syncthreads();
+      n_tiles = __builtin_amdgcn_readfirstlane(walk_n[0]);
+    } else if constexpr (BITS) {
       const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
       const int32_t* L = tile_lists + ((int64_t)(bm * p.mask_h + hm) * n_qtiles + qt) * list_stride;
       const int cnt = __builtin_amdgcn_readfirstlane(L[0]);
@@ -295,8 +347,10 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     }
     // Entry of the t-th visited tile: its index (relative to t0), with bit 31
     // set when the mask does not keep it whole.  Without a mask, t itself.
+    int gb = 0;  // CONT with a mask: stream position of the current item's first tile
     auto tile_entry = [&](int t) -> int {
-      if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + min(t, n_tiles)]);
+      if constexpr (CONT && BITS) return __builtin_amdgcn_readfirstlane(tlist[gb + t]);
+      else if constexpr (BITS) return __builtin_amdgcn_readfirstlane(tlist[lo + min(t, n_tiles)]);
       else return t;
     };
     auto tile_index = [&](int e) -> int { return BITS ? (e & 0x7FFFFFFF) : e; };
@@ -307,9 +361,14 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     // CONT: the item after the current one in the walk (has_nx false past the
     // last), round kw being the current one's.  Every item has at least 4
     // tiles (the launcher checks).
+    // CONT: byte offset of an item's row of blocks among all rows
+    auto mask_row = [&](int64_t bhx, int qtx) -> int {
+      const int bm = p.mask_b > 1 ? (int)(bhx / p.H) : 0, hm = p.mask_h > 1 ? (int)(bhx % p.H) : 0;
+      return (int)(((int64_t)(bm * p.mask_h + hm) * n_qtiles + qtx) * list_stride * kMaskBlockBytes);
+    };
     int64_t kw = 0, bh_n = 0;
     bool has_nx = false;
-    int qw0_n = 0, n_n = 0, t0_n = 0;
+    int qw0_n = 0, n_n = 0, t0_n = 0, mrow_n = 0;
     const __bf16 *Qg_n = nullptr, *Kg_n = nullptr, *Vg_n = nullptr;
     // Round k of a causal walk pairs heavy and light query tiles (above);
     // with a window the items are nearly equal but for a head's first query
@@ -321,7 +380,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
       const int64_t within = kn * W + (CAUSAL && !WINDOW ? ((kn & 1) ? W - 1 - u : u)
                                                          : (u + kn * max(1, W / 8)) % W);
       has_nx = within < x_count;
-      const int64_t it = x_start + (has_nx ? within : 0);
+      const int64_t it = BITS ? (has_nx ? (int64_t)walk_item[kw + 1] : x_start) : x_start + (has_nx ? within : 0);
       int qt_n = (int)(it % n_qtiles);
       if (CAUSAL) qt_n = n_qtiles - 1 - qt_n;
       bh_n = it / n_qtiles;
@@ -331,6 +390,11 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
       t0_n = WINDOW ? max(0, q0_n + off - wl) / BK : 0;
       n_n = (kv_end_n > t0_n * BK ? (kv_end_n + BK - 1) / BK : t0_n) - t0_n;
       qw0_n = q0_n + QW * ws;
+      if constexpr (BITS) {
+        // the pre-pass's list of the item holds exactly its tiles
+        n_n = has_nx ? __builtin_amdgcn_readfirstlane(walk_n[kw + 1]) : 0;
+        mrow_n = mask_row(bh_n, qt_n);
+      }
       Qg_n = (const __bf16*)p.q + (size_t)bh_n * N * D;
       Kg_n = (const __bf16*)p.k + (size_t)bh_n * M * D + (size_t)t0_n * BK * D;
       Vg_n = (const __bf16*)p.v + (size_t)bh_n * M * D + (size_t)t0_n * BK * D;
@@ -389,24 +453,30 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     const uint32_t* Mg = nullptr;
     int mbytes = 0;
     uint32_t mlane = 0;
+    int mrow_c = 0;
     if constexpr (BITS) {
       const int bm = p.mask_b > 1 ? b : 0, hm = p.mask_h > 1 ? (int)(bh % p.H) : 0;
       const int n_kt = list_stride - 1;  // tile t has block t + 1
       Mg = mask_blocks + ((size_t)(bm * p.mask_h + hm) * n_qtiles + qt) * (n_kt + 1) * (kMaskBlockBytes / 4);
       mbytes = (n_kt + 1) * kMaskBlockBytes;
       mlane = (uint32_t)(ws * 512 + lane * 4);
+      if constexpr (CONT) mrow_c = mask_row(bh, qt);
     }
     // A tile the mask keeps whole (entry e >= 0) has no block and never reads
     // its words: its load still goes out (the end-of-iteration wait counts
-    // every load) but from offset 0 (the all-ones block).
-    auto load_mask_item = [&](int w, int e, uint32_t* dst) {
+    // every load) but from offset 0 (the all-ones block).  CONT: one
+    // descriptor over every row of blocks (below 2^31 bytes), mrow the byte
+    // offset of the tile's item's row.
+    const int nrec_m = CONT && BITS ? p.mask_b * p.mask_h * n_qtiles * list_stride * kMaskBlockBytes : 0;
+    auto load_mask_item = [&](int w, int e, uint32_t* dst, int mrow) {
       if constexpr (BITS) {
         int wofs = ws * 128 + w * 64;
         asm volatile("" : "+s"(wofs));
         const uint32_t part = (uint32_t)(e >> 31);  // all ones for a partial tile
         const uint32_t at =
             ((uint32_t)(tile_index(e) + 1) * (uint32_t)kMaskBlockBytes + mlane + (uint32_t)w * 256u) & part;
-        buffer_load_lds4<true>(Mg, mbytes, at, (lds_ptr)(dst + wofs));
+        if constexpr (CONT) buffer_load_lds4<true>(mask_blocks, nrec_m, at + (uint32_t)mrow, (lds_ptr)(dst + wofs));
+        else buffer_load_lds4<true>(Mg, mbytes, at, (lds_ptr)(dst + wofs));
       }
     };
     auto load_k = [&](int t, __bf16* dst) {
@@ -419,7 +489,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     };
     auto load_mask = [&](int e, uint32_t* dst) {
   #pragma unroll
-      for (int w = 0; w < NMI; ++w) load_mask_item(w, e, dst);
+      for (int w = 0; w < NMI; ++w) load_mask_item(w, e, dst, mrow_c);
     };
     // Load item j of iteration t: K(t+4) blocks into Kdst, then V(t+2) blocks
     // into Vdst, then (mask) the mask words of tile t+3 into Mdst; eK, eV, eM
@@ -429,8 +499,12 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     // tiles of the current and the next item differ only in the offset.
     const int nrec_all = CONT ? p.B * p.H * M * ROWB : 0;
     auto load_item = [&](int j, int eK, int eV, int eM, __bf16* Kdst, __bf16* Vdst, uint32_t* Mdst,
-                         const __bf16* Ksrc, const __bf16* Vsrc) {
+                         const __bf16* Ksrc, const __bf16* Vsrc, int mrow) {
       if constexpr (CONT) {
+        if (j >= KPW + VPW) {
+          load_mask_item(j - KPW - VPW, eM, Mdst, mrow);
+          return;
+        }
         const uint32_t packed = j < KPW ? koff[j / 2] : voff[(j - KPW) / 2];
         const int i = j < KPW ? j : j - KPW;
         uint32_t pk = packed;
@@ -444,7 +518,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
       }
       if (j < KPW) load_k_item(j, tile_index(eK), Kdst, Ksrc);
       else if (j < KPW + VPW) load_v_item(j - KPW, tile_index(eV), Vdst, Vsrc);
-      else if (j < NITEM) load_mask_item(j - KPW - VPW, eM, Mdst);
+      else if (j < NITEM) load_mask_item(j - KPW - VPW, eM, Mdst, 0);
     };
 
     // ---- Q in registers: B operand of S^T = K Q^T ----
@@ -775,7 +849,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     // reloaded for S(t+2) (CONT), and its loads are waited for before phase B.
     auto iteration = [&](int eK, int eV, int eM, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst,
                          __bf16* Vdst, uint32_t* Mdst, const __bf16* Ksrc, const __bf16* Vsrc, bool fresh,
-                         bool qwait) {
+                         bool qwait, int mrow) {
       sm_begin();
       // K operands: a ring of PF + 2, so that a read overwrites a register two
       // fragments after the asm MFMAs last used it
@@ -834,7 +908,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         if constexpr (j >= NSB) {
           static_for<NITEM>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            if constexpr (NSB + i * NSB / NITEM == j) load_item(i, eK, eV, eM, Kdst, Vdst, Mdst, Ksrc, Vsrc);
+            if constexpr (NSB + i * NSB / NITEM == j) load_item(i, eK, eV, eM, Kdst, Vdst, Mdst, Ksrc, Vsrc, mrow);
           });
         }
         if constexpr (j < NSB) {
@@ -862,7 +936,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
   #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
       if (need_mask(e1, qw0, t0)) apply_mask(e1, qw0, t0, sacc, Ms);
-      iteration(e4, e2, e3, Ks, Vs, Kdst, Vdst, Mdst, Kg, Vg, false, false);
+      iteration(e4, e2, e3, Ks, Vs, Kdst, Vdst, Mdst, Kg, Vg, false, false, 0);
       // This wave's loads of the previous iteration (K(t+3), V(t+1)) are done
       // (loads complete in order: only this iteration's NITEM may be pending),
       // and so are its LDS reads; the barrier then makes every wave's loads
@@ -970,28 +1044,40 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
       int t = 0;  // tile of the current item
       // first row of the next item's first tile; byte offsets of the last K
       // and V tiles loaded (K(3) and V(1) in the prologue)
-      int row_nx = (int)bh_n * M + t0_n * BK;
+      int row_c = (int)bh * M, row_nx = (int)bh_n * M + t0_n * BK;
       int kofs = ((int)bh * M + (t0 + 3) * BK) * ROWB, vofs = ((int)bh * M + (t0 + 1) * BK) * ROWB;
       float m_fin[NQB], l_fin[NQB];
   #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) m_fin[qb] = l_fin[qb] = 0.f;
-      auto cont_step = [&](const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst)
-                           __attribute__((always_inline)) -> bool {
+      auto cont_step = [&](const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst, const uint32_t* Ms,
+                           uint32_t* Mdst) __attribute__((always_inline)) -> bool {
         const int n = n_tiles;
-        // tiles t+1 (weighed), t+2 (V loaded), t+4 (K loaded): the next
-        // item's once past this one's last
+        // tiles t+1 (weighed), t+2 (V loaded), t+3 (mask words loaded), t+4
+        // (K loaded): the next item's once past this one's last
         const bool sm_nx = has_nx && t + 1 >= n;
-        const int e1 = sm_nx ? t + 1 - n : t + 1;
         const int qw_sm = sm_nx ? qw0_n : qw0, t0_sm = sm_nx ? t0_n : t0;
-        // first bytes of K(t+4) and V(t+2) in the whole tensors: a tile on
-        // from the last, or the next item's first tile
-        kofs = t + 4 == n && has_nx ? row_nx * ROWB : kofs + BK * ROWB;
-        vofs = t + 2 == n && has_nx ? row_nx * ROWB : vofs + BK * ROWB;
+        int e1, e3 = 0, mrow = 0;
+        if constexpr (BITS) {
+          // the stream runs on into the next item's entries
+          e1 = tile_entry(t + 1);
+          e3 = tile_entry(t + 3);
+          const int e2 = tile_entry(t + 2), e4 = tile_entry(t + 4);
+          kofs = ((has_nx && t + 4 >= n ? row_nx : row_c) + tile_index(e4) * BK) * ROWB;
+          vofs = ((has_nx && t + 2 >= n ? row_nx : row_c) + tile_index(e2) * BK) * ROWB;
+          mrow = has_nx && t + 3 >= n ? mrow_n : mrow_c;
+        } else {
+          e1 = sm_nx ? t + 1 - n : t + 1;
+          // first bytes of K(t+4) and V(t+2) in the whole tensors: a tile on
+          // from the last, or the next item's first tile
+          kofs = t + 4 == n && has_nx ? row_nx * ROWB : kofs + BK * ROWB;
+          vofs = t + 2 == n && has_nx ? row_nx * ROWB : vofs + BK * ROWB;
+        }
         mfma_guard();  // the last iteration's final MFMAs wrote the scores
   #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-        if (need_mask(e1, qw_sm, t0_sm)) apply_mask(e1, qw_sm, t0_sm, sacc, Mb0);
-        iteration(kofs, vofs, 0, Ks, Vs, Kdst, Vdst, Mb0, nullptr, nullptr, t == n - 1, has_nx && t == n - 2);
+        if (need_mask(e1, qw_sm, t0_sm)) apply_mask(e1, qw_sm, t0_sm, sacc, Ms);
+        iteration(kofs, vofs, e3, Ks, Vs, Kdst, Vdst, Mdst, nullptr, nullptr, t == n - 1, has_nx && t == n - 2,
+                  mrow);
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NITEM) : "memory");
         if (__builtin_expect(t < n - 3, 1)) {
           ++t;
@@ -1020,22 +1106,25 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
           for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = f32x16{};
         if (!has_nx) return true;
         ++kw;
+        gb += n;
         bh = bh_n;
         qw0 = qw0_n;
         t0 = t0_n;
+        mrow_c = mrow_n;
         n_tiles = n_n;
         Qg = Qg_n;
         Kg = Kg_n;
         Vg = Vg_n;
         walk_next();
+        row_c = (int)bh * M;
         row_nx = (int)bh_n * M + t0_n * BK;
         t = 0;
         return false;
       };
       for (;;) {
-        if (cont_step(Kb2, Vb0, Kb1, Vb2)) break;
-        if (cont_step(Kb0, Vb1, Kb2, Vb0)) break;
-        if (cont_step(Kb1, Vb2, Kb0, Vb1)) break;
+        if (cont_step(Kb2, Vb0, Kb1, Vb2, Mb1, Mb0)) break;
+        if (cont_step(Kb0, Vb1, Kb2, Vb0, Mb2, Mb1)) break;
+        if (cont_step(Kb1, Vb2, Kb0, Vb1, Mb0, Mb2)) break;
       }
     } else {
       for (int t = 0; t < n_tiles; t += 3) {
@@ -1060,10 +1149,12 @@ void prefill_bf16_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ ti
 
 // Causal or windowed, no mask, key splits or kv_len, M >= N >= 256,
 // several items per workgroup: a persistent walk as one pipeline.
-template <int D, bool CAUSAL, bool WINDOW>
+template <int D, bool CAUSAL, bool WINDOW, bool BITS>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefill_cont_kernel(Problem p, int n_qtiles) {
-  prefill_body<D, CAUSAL, WINDOW, false, false, true>(p, n_qtiles, nullptr, 0, nullptr, SplitArgs{});
+void prefill_cont_kernel(Problem p, int n_qtiles, const int32_t* __restrict__ tile_lists, int list_stride,
+                         const uint32_t* __restrict__ mask_blocks, const int32_t* __restrict__ walk_order) {
+  prefill_body<D, CAUSAL, WINDOW, BITS, false, true>(p, n_qtiles, tile_lists, list_stride, mask_blocks,
+                                                      SplitArgs{}, walk_order);
 }
 
 template <int D, bool CAUSAL>
@@ -1164,16 +1255,34 @@ int min_item_tiles(const Problem& p, int n_qtiles) {
   return fewest;
 }
 
-void launch_prefill_cont(const Problem& p, dim3 grid, hipStream_t stream, int n_qtiles) {
+void launch_prefill_cont(const Problem& p, dim3 grid, hipStream_t stream, int n_qtiles, const int32_t* lists,
+                         int stride, const uint32_t* blocks, const int32_t* order) {
   const dim3 block(kPrefillThreads);
-  // windowed, or causal at D = 128 (the caller checks)
-  if (p.D == 64) {
-    if (p.causal) hipLaunchKernelGGL((prefill_cont_kernel<64, true, true>), grid, block, 0, stream, p, n_qtiles);
-    else hipLaunchKernelGGL((prefill_cont_kernel<64, false, true>), grid, block, 0, stream, p, n_qtiles);
+  // causal with a mask, windowed, or causal at D = 128 (the caller checks)
+  if (p.mask) {
+    if (p.D == 64)
+      hipLaunchKernelGGL((prefill_cont_kernel<64, true, false, true>), grid, block, 0, stream, p, n_qtiles, lists,
+                         stride, blocks, order);
+    else
+      hipLaunchKernelGGL((prefill_cont_kernel<128, true, false, true>), grid, block, 0, stream, p, n_qtiles, lists,
+                         stride, blocks, order);
+  } else if (p.D == 64) {
+    if (p.causal)
+      hipLaunchKernelGGL((prefill_cont_kernel<64, true, true, false>), grid, block, 0, stream, p, n_qtiles, nullptr,
+                         0, nullptr, nullptr);
+    else
+      hipLaunchKernelGGL((prefill_cont_kernel<64, false, true, false>), grid, block, 0, stream, p, n_qtiles, nullptr,
+                         0, nullptr, nullptr);
   } else {
-    if (!p.window) hipLaunchKernelGGL((prefill_cont_kernel<128, true, false>), grid, block, 0, stream, p, n_qtiles);
-    else if (p.causal) hipLaunchKernelGGL((prefill_cont_kernel<128, true, true>), grid, block, 0, stream, p, n_qtiles);
-    else hipLaunchKernelGGL((prefill_cont_kernel<128, false, true>), grid, block, 0, stream, p, n_qtiles);
+    if (!p.window)
+      hipLaunchKernelGGL((prefill_cont_kernel<128, true, false, false>), grid, block, 0, stream, p, n_qtiles, nullptr,
+                         0, nullptr, nullptr);
+    else if (p.causal)
+      hipLaunchKernelGGL((prefill_cont_kernel<128, true, true, false>), grid, block, 0, stream, p, n_qtiles, nullptr,
+                         0, nullptr, nullptr);
+    else
+      hipLaunchKernelGGL((prefill_cont_kernel<128, false, true, false>), grid, block, 0, stream, p, n_qtiles, nullptr,
+                         0, nullptr, nullptr);
   }
 }
 
@@ -1211,18 +1320,19 @@ hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, void* workspa
     return hipGetLastError();
   }
   const int64_t n_items = (int64_t)p.B * p.H * n_qtiles;
-  if ((p.window || (p.causal && p.D == 128)) && !p.mask && !p.kv_len && p.N >= kPrefillBlockQ && p.M >= p.N &&
-      (int64_t)p.B * p.H * p.M * p.D * 2 <= INT32_MAX && n_items > kPrefillPersistGrid &&
-      min_item_tiles(p, n_qtiles) >= 4) {
-    // every work item has at least 4 key tiles, one buffer descriptor covers
-    // all of K (and of V), and each workgroup walks more than one item: one
-    // pipeline per persistent workgroup (one per CU; with one item each, the
-    // item-by-item kernel measured 3-4% faster).  Not for plain non-causal
-    // attention, whose long uniform items gain little and whose D = 128 form
-    // the compiler cannot allocate without spills, nor for plain causal
-    // attention at D = 64, whose iterations are half as long, so that the
-    // per-iteration cost of the walk eats the gain (measured -0.5%).
-    launch_prefill_cont(p, dim3(kPrefillPersistGrid), stream, n_qtiles);
+  // The pipelined walk: no kv_len, M >= N >= 256, one buffer descriptor over
+  // all of K (and of V), and more items than the 256 persistent workgroups.
+  const bool walk = !p.kv_len && p.N >= kPrefillBlockQ && p.M >= p.N &&
+                    (int64_t)p.B * p.H * p.M * p.D * 2 <= INT32_MAX && n_items > kPrefillPersistGrid;
+  if (walk && !p.mask && (p.window || (p.causal && p.D == 128)) && min_item_tiles(p, n_qtiles) >= 4) {
+    // every work item has at least 4 key tiles, and each workgroup walks more
+    // than one: one pipeline per persistent workgroup (one per CU; with one
+    // item each, the item-by-item kernel measured 3-4% faster).  Not for
+    // plain non-causal attention, whose long uniform items gain little and
+    // whose D = 128 form the compiler cannot allocate without spills, nor for
+    // plain causal attention at D = 64, whose iterations are half as long, so
+    // that the per-iteration cost of the walk eats the gain (measured -0.5%).
+    launch_prefill_cont(p, dim3(kPrefillPersistGrid), stream, n_qtiles, nullptr, 0, nullptr, nullptr);
     return hipGetLastError();
   }
   const int32_t* lists = nullptr;
@@ -1230,10 +1340,26 @@ hipError_t launch_prefill_bf16(const Problem& p, const Plan& plan, void* workspa
   if (p.mask) {
     // the tile lists, one per (mask batch, mask head, query tile), and the
     // words of the tiles the mask keeps in part
-    const MaskWorkspace w = mask_workspace(p.N, p.M, p.mask_b, p.mask_h, 0, false);
-    launch_mask_prep(p.mask, p.N, p.M, p.mask_w, p.mask_b, p.mask_h, workspace, w, false, stream);
+    const MaskWorkspace w = mask_workspace(p.N, p.M, p.mask_b, p.mask_h, 0, false, p.causal ? n_items : 0);
+    // Causal masks take the pipelined walk when the workgroup's lists fit
+    // in LDS (the pre-pass then cuts each list at the causal limit and fills
+    // short ones up to 4 tiles) and one descriptor covers every row of blocks.
+    const int64_t per_wg = ((n_items + kNumXcd - 1) / kNumXcd + kPrefillPersistGrid / kNumXcd - 1) /
+                           (kPrefillPersistGrid / kNumXcd);
+    const int64_t n_kt = (p.M + kPrefillBlockK - 1) / kPrefillBlockK;
+    const bool walk_mask = walk && p.causal && !p.window && per_wg <= kWalkMaxItems &&
+                           (n_items + kNumXcd - 1) / kNumXcd <= 4096 &&
+                           per_wg * std::max<int64_t>(n_kt, 4) + 5 <= kMaskMaxTiles &&
+                           (int64_t)p.mask_b * p.mask_h * n_qtiles * plan.mask_tiles * kMaskBlockBytes <= INT32_MAX;
+    launch_mask_prep(p.mask, p.N, p.M, p.mask_w, p.mask_b, p.mask_h, workspace, w, false, stream, walk_mask, p.B,
+                     p.H);
     lists = (const int32_t*)((char*)workspace + w.lists);
     blocks = (const uint32_t*)((char*)workspace + w.blocks);
+    if (walk_mask) {
+      launch_prefill_cont(p, dim3(kPrefillPersistGrid), stream, n_qtiles, lists, plan.mask_tiles, blocks,
+                          (const int32_t*)((char*)workspace + w.order));
+      return hipGetLastError();
+    }
   }
   if (p.D == 64) launch_prefill_d<64>(p, grid, stream, n_qtiles, lists, plan.mask_tiles, blocks);
   else launch_prefill_d<128>(p, grid, stream, n_qtiles, lists, plan.mask_tiles, blocks);

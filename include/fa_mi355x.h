@@ -136,8 +136,10 @@ typedef struct {
    * per query tile of 256, the 64-key tiles in which some query keeps a
    * key and copies the words of the tiles the mask keeps in part into 2 KB
    * blocks, about N * M / 8 bytes (the size of the mask) per (mask batch,
-   * mask head): fa_fwd_workspace_bytes; M up to 262080 and N * W * 4 below
-   * 2^31) and FA_PATH_F32, which reads the words directly.                 */
+   * mask head), and, when causal, 4 bytes per 256-query work item for the
+   * order in which persistent workgroups take them: fa_fwd_workspace_bytes;
+   * M up to 262080 and N * W * 4 below 2^31) and FA_PATH_F32, which reads
+   * the words directly.                                                    */
   const uint32_t* mask;
   int32_t mask_batches;  /* 1 or B (0 means 1)                               */
   int32_t mask_heads;    /* 1 or H (0 means 1)                               */

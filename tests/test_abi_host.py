@@ -264,10 +264,12 @@ def test_mask_plan():
     p = fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True, mask_shape=(1, 1))
     assert p["path_name"] == "prefill"
     # 32 lists of 129 int32 (16,512 B -> 16,640), 32 x 128 class bytes, then
-    # 32 rows of 1 + 128 blocks of 2 KB
-    assert p["workspace_bytes"] == 16640 + 4096 + 32 * 129 * 2048 == mask_layout(8192, 8192, 1, 1)["end"]
+    # 32 rows of 1 + 128 blocks of 2 KB, then (causal) the walk order of the
+    # 2 x 32 x 32 work items
+    assert p["workspace_bytes"] == 16640 + 4096 + 32 * 129 * 2048 + 2048 * 4 == \
+        mask_layout(8192, 8192, 1, 1, items=2048)["end"]
     p2 = fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True, mask_shape=(2, 32))
-    assert p2["workspace_bytes"] == mask_layout(8192, 8192, 2, 32)["end"]
+    assert p2["workspace_bytes"] == mask_layout(8192, 8192, 2, 32, items=2048)["end"]
     assert fa.plan(3, 2, 600, 700, 64, fa.BF16, mask_shape=(3, 1))["workspace_bytes"] == \
         mask_layout(600, 700, 3, 1)["end"]
     assert fa.plan(2, 32, 8192, 8192, 128, fa.BF16, True)["workspace_bytes"] == 0

@@ -1,7 +1,8 @@
 """GPU parity of the causal prefill's persistent walk run as one pipeline.
 
-With causal or windowed attention, no mask or kv_len, M >= N >= 256 and
-more work items than workgroups, each persistent workgroup walks several items (256-query tiles of some
+With causal or windowed attention (or causal with an element mask), no
+kv_len, M >= N >= 256 and more work items than workgroups, each persistent
+workgroup walks several items (256-query tiles of some
 (batch, head)) and its iterations on the last tiles of one item already load,
 score and weigh the first tiles of the next ("Understanding FlashAttention",
 From loops to tiling: the tiles of one query block are independent of every
@@ -33,21 +34,22 @@ def make(seed, B, H, N, M, D):
     return tuple(inputs.to_device(x, "bf16", DEV) for x in (q, k, v))
 
 
-def check_walk(q, k, v, scale, what, rel_o=0.0, causal=True, window=None):
+def check_walk(q, k, v, scale, what, rel_o=0.0, causal=True, window=None, allowed=None):
     B, H, N, D = q.shape
     M = k.shape[2]
     items = B * H * ((N + 255) // 256)
-    say(f"{what}: B={B} H={H} N={N} M={M} D={D} causal={causal} window={window}, "
-        f"{items} work items over 256 workgroups")
-    o, l = fa.fwd(q, k, v, scale=scale, causal=causal, window=window)
+    say(f"{what}: B={B} H={H} N={N} M={M} D={D} causal={causal} window={window} "
+        f"mask={None if allowed is None else allowed.shape}, {items} work items over 256 workgroups")
+    words = None if allowed is None else fa.pack_mask(torch.from_numpy(allowed).to(DEV))
+    o, l = fa.fwd(q, k, v, scale=scale, causal=causal, window=window, mask=words)
     torch.cuda.synchronize()
     say(f"{what}: same launch item by item (kv_len = M)")
-    o2, l2 = fa.fwd(q, k, v, scale=scale, causal=causal, window=window, kv_len=[M] * B)
+    o2, l2 = fa.fwd(q, k, v, scale=scale, causal=causal, window=window, mask=words, kv_len=[M] * B)
     torch.cuda.synchronize()
     assert torch.equal(o, o2), f"{what}: output differs from the item-by-item walk"
     assert torch.equal(l, l2), f"{what}: LSE differs from the item-by-item walk"
     say(f"{what}: oracle")
-    Or, Lr = attention_ref(host64(q), host64(k), host64(v), scale, causal, window=window)
+    Or, Lr = attention_ref(host64(q), host64(k), host64(v), scale, causal, window=window, mask=allowed)
     O = host64(o)
     if rel_o:
         # the part of the output error that scales with |O|: bf16 rounding
@@ -121,3 +123,26 @@ def test_walk_windows(N, M, D, causal, window):
     q, k, v = make(440 + N + D, B, H, N, M, D)
     check_walk(q, k, v, default_scale(D), f"walk window {window} N={N} M={M} D={D}",
                causal=causal, window=window)
+
+
+@pytest.mark.parametrize("kind,N,D", [
+    ("documents", 512, 128),       # random document cuts: short lists filled up to 4 tiles
+    ("documents", 700, 64),        # ragged last query tile
+    ("random_per_head", 512, 64),  # long lists, one mask per head
+    ("blocks", 512, 128),          # 64 x 64 blocks kept with p = 0.3: items with no tile at all
+])
+def test_walk_masks(kind, N, D):
+    """Causal with an element mask: each workgroup's items' tile lists run as
+    one stream; the pre-pass cuts the lists at the causal limit and fills the
+    short ones up to four tiles with fully masked ones (their weights are
+    exactly 0, so the bits agree with the item-by-item walk)."""
+    B = 2
+    H = 600 // (B * ((N + 255) // 256))
+    if kind == "documents":
+        allowed = inputs.document_mask(450 + N, N, N, 7)
+    elif kind == "random_per_head":
+        allowed = inputs.random_mask(451, 1, H, N, N, 0.5)
+    else:
+        allowed = inputs.block_mask(452, B, H, N, N, 64, 64, 0.3)
+    q, k, v = make(460 + N + D, B, H, N, N, D)
+    check_walk(q, k, v, default_scale(D), f"walk mask {kind} N={N} D={D}", allowed=allowed)
