@@ -342,7 +342,7 @@ def main():
         out["prefill"] = {"ms_mean": avg_p, "ms_min": min(ms_p), "ms_median": median(ms_p), "tflops": tfs,
                           "frac_bf16_peak": tfs / PEAK_BF16_TFLOPS, "flop_per_launch": flop_p}
         traffic = measured_traffic("prefill")
-        out["roofline"] = {"bound": "mfma", "kernel": "prefill_cont_kernel<128, true, false>",
+        out["roofline"] = {"bound": "mfma", "kernel": "prefill_cont_kernel<128, true, false, false>",
                            "achieved": tfs, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": tfs / PEAK_BF16_TFLOPS, "traffic": traffic}
     if do_d:
@@ -386,7 +386,7 @@ def main():
                      "frac": tf / PEAK_BF16_TFLOPS} if mfma_bound else
                     {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS})
-            roof.update({"kernel": "prefill_cont_kernel<128, true, true>",
+            roof.update({"kernel": "prefill_cont_kernel<128, true, true, false>",
                          "traffic": measured_traffic("window", f"w{W}")})
             res[f"w{W}"] = {"window": [W - 1, 0], "ms_mean": avg, "ms_min": min(ms_w[W]), "ms_median": median(ms_w[W]),
                             "tflops": tf, "gbs": gbs, "flop_per_launch": flop,
@@ -408,7 +408,7 @@ def main():
                          "visible_fraction_of_causal": pairs_m[name] / (wp.N * (wp.N + 1) / 2),
                          "speedup_vs_unmasked_causal": ((sum(ms_p) / len(ms_p)) / avg) if do_p else None,
                          "roofline": {"bound": "mfma",
-                                      "kernel": "mask_blocks_kernel + mask_lists_kernel + prefill_bf16_kernel<128, true, false, true>",
+                                      "kernel": "mask_blocks_kernel + mask_lists_kernel + mask_order_kernel + prefill_cont_kernel<128, true, false, true>",
                                       "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                       "frac": tf / PEAK_BF16_TFLOPS,
                                       "traffic": measured_traffic("mask", name)}}
@@ -688,7 +688,7 @@ def prefill_kernel_name(w, causal):
     kv_len: causal at D = 128 with more 256-query work items than the 256
     persistent workgroups runs the walk as one pipeline."""
     if causal and w.D == 128 and w.N >= 256 and w.M >= w.N and w.B * w.H * ((w.N + 255) // 256) > 256:
-        return f"prefill_cont_kernel<{w.D}, true, false>"
+        return f"prefill_cont_kernel<{w.D}, true, false, false>"
     return f"prefill_bf16_kernel<{w.D}, {str(causal).lower()}, false, false>"
 
 
@@ -710,7 +710,7 @@ def _leg_of_dispatches(rows):
     for i, (_, s, ns) in enumerate(rows):
         nxt = rows[i + 1][1] if i + 1 < len(rows) else ""
         seen_kvo |= s.startswith("kvouter")
-        if s == "prefill_cont_kernel<128, true, false>":
+        if s == "prefill_cont_kernel<128, true, false, false>":
             leg = ("prefill B2 H32 N8192 D128 causal (bench step)" if nxt.startswith("splitkv_partial") else
                    "configs B4 H16 N4096 D128 causal" if seen_kvo else
                    "setup (untimed forward for the backward's O, LSE)")
@@ -720,10 +720,10 @@ def _leg_of_dispatches(rows):
             leg = "backward (rowstat, both legs)"
         elif s.startswith("bwd_"):
             leg = "backward B2 H32 N8192 D128 causal" if s.endswith("false>") else "backward under the 8-document mask"
-        elif s == "prefill_cont_kernel<128, true, true>":
+        elif s == "prefill_cont_kernel<128, true, true, false>":
             n["win"] += 1
             leg = "window 128 keys" if n["win"] <= 13 else "window 2048 keys"
-        elif s == "prefill_bf16_kernel<128, true, false, true>" or s.startswith("mask_"):
+        elif s == "prefill_cont_kernel<128, true, false, true>" or s.startswith("mask_"):
             if s.startswith("prefill"):
                 n["maskp"] += 1
             k = n["maskp"] if s.startswith("prefill") else n["maskp"] + 1   # a pre-pass precedes its prefill
@@ -764,7 +764,7 @@ def summarize_profiles(d):
     # kernel durations: rocprofv3 --stats, and the same trace split by leg
     lines = ["# rocprofv3 --stats kernel summary of the default bench sequence (durations in ns), the library's kernels",
              f"# command: {KTRACE_CMD}",
-             "# rows aggregate by kernel name: prefill_cont_kernel<128, true, false> serves the bench step (N = 8192),",
+             "# rows aggregate by kernel name: prefill_cont_kernel<128, true, false, false> serves the bench step (N = 8192),",
              "# the configs leg (N = 4096) and one untimed setup call, and prefill_bf16_kernel<64, true, false, false> two configs;",
              "# kernel_trace_by_leg_default_bench.txt splits the same trace by leg", "#",
              "# kernel, calls, average_ns, min_ns, max_ns, stddev_ns"]
@@ -812,9 +812,9 @@ def summarize_profiles(d):
                 start = True
             elif first.startswith("bwd_rowstat") or k.startswith(("splitkv_merge", "prefill_merge")):
                 start = False   # a backward call runs to the next rowstat; split calls end with their merge
-            elif first.startswith("mask_blocks") and (k.startswith("mask_lists") or
-                                                      (k.startswith("prefill_bf16") and len(calls[-1]) == 2)):
-                start = False   # the forward's pre-pass (two launches), then its prefill
+            elif first.startswith("mask_blocks") and not k.startswith("mask_blocks") and (
+                    k.startswith("mask_") or (k.startswith("prefill") and calls[-1][-1][0].startswith("mask_"))):
+                start = False   # the forward's pre-pass (three launches), then its prefill
             else:
                 start = True
             if start:
