@@ -14,6 +14,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -107,6 +108,15 @@ __device__ __forceinline__ void buffer_load_lds4(const void* base, int nbytes, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, kBufferFlags), dst,
       4, voff, 0, 0, STREAM ? 2 : 0);
+#endif
+}
+
+// 16 bytes per lane to base + voff, against a descriptor of `nbytes` bytes:
+// stores of lanes whose offset is out of range are dropped.
+__device__ __forceinline__ void buffer_store16(void* base, int nbytes, uint32_t voff, u32x4 v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_buffer_store_b128(v, __builtin_amdgcn_make_buffer_rsrc(base, (short)0, nbytes, kBufferFlags),
+                                         voff, 0, 0);
 #endif
 }
 

@@ -205,6 +205,14 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
   __shared__ __attribute__((aligned(256))) uint32_t Mb0[BITS ? NW * 128 : 1];
   __shared__ __attribute__((aligned(256))) uint32_t Mb1[BITS ? NW * 128 : 1];
   __shared__ __attribute__((aligned(256))) uint32_t Mb2[BITS ? NW * 128 : 1];
+  // Output staging: a wave writes the normalised output of 32 of its rows
+  // here and reads it back as 16-byte pieces of whole rows, so that each
+  // store to O covers whole rows instead of 16 bytes of 32 rows (measured:
+  // the scattered stores held an item's write-out to about 8,000 cycles).
+  // With a mask at D = 128 the LDS has no room for it.
+  constexpr bool OSTAGE = !SPLIT && !(BITS && D == 128);
+  constexpr int OSTR = 2 * D + 16;  // staging row stride in bytes
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[OSTAGE ? NW * 32 * OSTR : 16];
 
   // Causal without a window or a mask: persistent workgroups, one per CU
   // (the planner's grid), each walking the work items of its XCD.  Round k
@@ -999,6 +1007,46 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
             *(float4*)(Orow + db * 32 + 8 * j + 4 * hl) = ov;
           }
         if (hl == 0) sp.part_lse[prow] = l_tot > 0.f ? (mr[qb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
+      } else if constexpr (OSTAGE) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        // lane-dependent addresses are formed here, not hoisted to the
+        // kernel's start and kept live (or spilled) across the whole walk
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        uint8_t* st = ostage + ws * 32 * OSTR;
+  #pragma unroll
+        for (int db = 0; db < DB; ++db)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bf16x4 ov;
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[db][qb][4 * j + i] * inv);
+            *(bf16x4*)(st + (ln % 32) * OSTR + (db * 32 + 8 * j + 4 * (ln / 32)) * 2) = ov;
+          }
+        // the wave's LDS writes before its reads of other lanes' rows
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // the block's rows of O, as one buffer: stores to rows past N drop
+        // (block offset and size are wave-uniform: scalar registers)
+        const int q_blk = __builtin_amdgcn_readfirstlane(qw0 + 32 * qb);
+        const int64_t blk = ((int64_t)bh * N + q_blk) * D;
+        __bf16* Oblk = (__bf16*)p.o + (((int64_t)__builtin_amdgcn_readfirstlane((int)(blk >> 32)) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readfirstlane((int)blk));
+        const int blk_bytes = __builtin_amdgcn_readfirstlane(max(0, min(32, N - q_blk)) * D * 2);
+        constexpr int RPI = 64 / CPR;  // rows per read: 16-byte piece lane % CPR of row lane / CPR
+  #pragma unroll
+        for (int r0 = 0; r0 < 32; r0 += RPI) {
+          const int r = r0 + ln / CPR, c16 = ln % CPR;
+          const u32x4 v = *(const u32x4*)(st + r * OSTR + c16 * 16);
+          buffer_store16(Oblk, blk_bytes, (uint32_t)(r * D * 2 + c16 * 16), v);
+        }
+        // every lane has read the rows before the next block overwrites them
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (hl == 0 && qrow < N)
+          p.lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (mr[qb] + fast_log2(l_tot)) * kLn2 : -INFINITY;
       } else if (qrow < N) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         __bf16* Orow = (__bf16*)p.o + (size_t)bh * N * D + (size_t)qrow * D;
