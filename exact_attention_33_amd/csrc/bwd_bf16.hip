@@ -75,6 +75,55 @@ static_assert(NW == kBwdThreads / 64, "waves per workgroup");
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Output staging: 32 rows of a wave's accumulator go out through the wave's
+// LDS area (32 rows of 2 D + 16 bytes) as 16-byte pieces of whole rows, not
+// as 8 bytes of 32 rows per store.  acc[db] register r holds row l32,
+// d = 32 db + 8 (r / 4) + 4 h + r % 4 of the block; the row gets acc * sc,
+// or zeros where `ok` is false.  dst is the block's first row (row stride
+// D); rows from `rows` on are not written (a buffer descriptor of `rows`
+// rows drops their stores).  `rows` and dst are wave-uniform.
+template <int D>
+__device__ __forceinline__ void store_block_staged(uint8_t* st, const f32x16 (&acc)[D / 32], float sc, bool ok,
+                                                   __bf16* dst, int rows) {
+  constexpr int OSTR = 2 * D + 16, CPR = D / 8, RPI = 64 / CPR;
+  // lane-dependent addresses formed here (not hoisted and kept live)
+  int ln = (int)threadIdx.x % 64;
+  asm volatile("" : "+v"(ln));
+  const int l32 = ln % 32, h = ln / 32;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(ok ? acc[db][4 * g + e] * sc : 0.f);
+      *(bf16x4*)(st + l32 * OSTR + (32 * db + 8 * g + 4 * h) * 2) = v4;
+    }
+  // the wave's LDS writes before its reads of other lanes' rows
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int bytes = __builtin_amdgcn_readfirstlane(rows < 0 ? 0 : (rows > 32 ? 32 : rows) * D * 2);
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int r = r0 + ln / CPR, c16 = ln % CPR;
+    const u32x4 v = *(const u32x4*)(st + r * OSTR + c16 * 16);
+    buffer_store16(dst, bytes, (uint32_t)(r * D * 2 + c16 * 16), v);
+  }
+  // every lane has read the rows before the area is written again
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// A wave-uniform pointer kept in scalar registers.
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* x) {
+  const uint64_t v = (uint64_t)x;
+  return (T*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v));
+}
+
 // ---------------------------------------------------------------------------
 // Pass 1: Lg[i] = LSE_i * log2(e) (+inf where LSE = -inf or i >= N) and
 // D_i = rowsum(dO_i * O_i), per (batch, head), Npad rows.
@@ -136,6 +185,7 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   __shared__ __attribute__((aligned(256))) uint32_t Ms0[BITS ? 512 : 1];
   __shared__ __attribute__((aligned(256))) uint32_t Ms1[BITS ? 512 : 1];
   __shared__ int tlist[BITS ? kMaskMaxTiles : 1];   // the key tile's listed query stages
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[NW * 32 * (2 * D + 16)];  // output staging
 
   // Causal without a window or a mask: persistent workgroups walking their
   // XCD's tiles, heavy and light alternating round by round, as in the
@@ -494,28 +544,15 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
     // ---- write dK = scale * dK^T^T and dV (zero for keys at or past kv_len) ----
     // Accumulator (kb2, db), register r: d = 32 db + 8 (r / 4) + 4 h + r % 4,
     // key jw0 + 32 kb2 + l32.
-    __bf16* dK = (__bf16*)p.dk + (size_t)bh * M * D;
-    __bf16* dV = (__bf16*)p.dv + (size_t)bh * M * D;
     const float sc = p.scale;
+    uint8_t* st = ostage + (tid / 64) * 32 * (2 * D + 16);
   #pragma unroll
     for (int kb2 = 0; kb2 < KBW; ++kb2) {
-      const int key = jw0 + 32 * kb2 + l32;
-      if (key >= M) continue;
-      const bool ok = key < kvl;
-  #pragma unroll
-      for (int db = 0; db < DB; ++db)
-  #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 kv4, vv4;
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kv4[e] = (__bf16)(ok ? dkacc[kb2][db][4 * g + e] * sc : 0.f);
-            vv4[e] = (__bf16)(ok ? dvacc[kb2][db][4 * g + e] : 0.f);
-          }
-          const size_t at = (size_t)key * D + 32 * db + 8 * g + 4 * h;
-          *(bf16x4*)(dK + at) = kv4;
-          *(bf16x4*)(dV + at) = vv4;
-        }
+      const int k_blk = __builtin_amdgcn_readfirstlane(jw0 + 32 * kb2);
+      const bool ok = k_blk + l32 < kvl;
+      const size_t at = ((size_t)bh * M + k_blk) * D;
+      store_block_staged<D>(st, dkacc[kb2], sc, ok, uniform_ptr((__bf16*)p.dk + at), M - k_blk);
+      store_block_staged<D>(st, dvacc[kb2], 1.f, ok, uniform_ptr((__bf16*)p.dv + at), M - k_blk);
     }
   }
   }
@@ -545,6 +582,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   __shared__ int tlist[BITS ? kMaskMaxTiles : 1];
   __shared__ __attribute__((aligned(256))) uint32_t Mq0[BITS ? NW * 128 : 1];
   __shared__ __attribute__((aligned(256))) uint32_t Mq1[BITS ? NW * 128 : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[NW * 32 * (2 * D + 16)];  // output staging
 
   // Causal without a window or a mask: persistent workgroups walking their
   // XCD's tiles, heavy and light alternating round by round, as in the
@@ -847,21 +885,13 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
     // ---- write dQ = scale * (dQ^T)^T ----
     // Accumulator (qb, db), register r: d = 32 db + 8 (r / 4) + 4 h + r % 4,
     // query qw0 + 32 qb + l32.
-    __bf16* dQ = (__bf16*)p.dq + (size_t)bh * N * D;
     const float sc = p.scale;
+    uint8_t* st = ostage + (tid / 64) * 32 * (2 * D + 16);
   #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      const int row = qw0 + 32 * qb + l32;
-      if (row >= N) continue;
-  #pragma unroll
-      for (int db = 0; db < DB; ++db)
-  #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 q4;
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) q4[e] = (__bf16)(dqacc[qb][db][4 * g + e] * sc);
-          *(bf16x4*)(dQ + (size_t)row * D + 32 * db + 8 * g + 4 * h) = q4;
-        }
+      const int q_blk = __builtin_amdgcn_readfirstlane(qw0 + 32 * qb);
+      store_block_staged<D>(st, dqacc[qb], sc, true, uniform_ptr((__bf16*)p.dq + ((size_t)bh * N + q_blk) * D),
+                            N - q_blk);
     }
   }
   }
