@@ -20,6 +20,7 @@ import exact_attention_33_amd as fa
 from exact_attention_33_amd import inputs
 from oracle.attention import attention_ref
 from tests.gpu_helpers import compare, default_scale, host64
+from tests.mask_layout import mask_layout
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -146,3 +147,59 @@ def test_walk_masks(kind, N, D):
         allowed = inputs.block_mask(452, B, H, N, N, 64, 64, 0.3)
     q, k, v = make(460 + N + D, B, H, N, N, D)
     check_walk(q, k, v, default_scale(D), f"walk mask {kind} N={N} D={D}", allowed=allowed)
+
+
+def test_walk_mask_prepass_lists_and_order():
+    """The pre-pass output the masked walk runs on, read back from the
+    workspace: each query tile's list is the mask's tiles below the causal
+    limit (the tile after the tile's last query's last key), a list shorter
+    than four tiles is filled with tiles the mask does not touch, in tile
+    order and flagged with all-zero words, and each XCD's range of work
+    items is ordered by tile count, most first, ties by item."""
+    B, H, N, D = 2, 150, 512, 64
+    M = N
+    allowed = np.zeros((1, 1, N, M), dtype=bool)
+    allowed[0, 0, 130:140, 140:150] = True    # query tile 0: one tile kept in part, three fillers
+    allowed[0, 0, 256:, :384] = True          # query tile 1: six whole tiles, none past them
+    q, k, v = make(471, B, H, N, M, D)
+    words = fa.pack_mask(torch.from_numpy(allowed).to(DEV))
+    n_qt, n_kt = (N + 255) // 256, (M + 63) // 64
+    items = B * H * n_qt
+    assert items > 256
+    ws = torch.zeros(fa.workspace_bytes(B, H, N, M, D, causal=True, mask_shape=(1, 1)),
+                     dtype=torch.uint8, device=DEV)
+    say(f"pre-pass of the masked walk: {items} items, mask [1, 1, {N}, {M}]")
+    fa.fwd(q, k, v, causal=True, mask=words, workspace=ws)
+    torch.cuda.synchronize()
+    lay = mask_layout(N, M, 1, 1, items=items)
+    wsb = ws.cpu().numpy()
+    w32 = wsb.view(np.uint32)
+    stride = n_kt + 1
+    sizes = []
+    for qt in range(n_qt):
+        row = w32[lay["lists"] // 4 + qt * stride:][:stride]
+        got = [int(x) for x in row[1:1 + int(row[0])]]
+        blk = allowed[0, 0, qt * 256:(qt + 1) * 256]
+        t_end = (min(M, min(qt * 256 + 256, N) + (M - N)) + 63) // 64
+        cls = [0 if not blk[:, t * 64:(t + 1) * 64].any() else (1 if blk[:, t * 64:(t + 1) * 64].all() else 2)
+               for t in range(t_end)]
+        want = [t | (1 << 31) if cls[t] == 2 else t for t in range(t_end) if cls[t]]
+        if len(want) < 4:
+            pads = [t for t in range(t_end) if cls[t] == 0][:4 - len(want)]
+            want = sorted(want + [t | (1 << 31) for t in pads], key=lambda e: e & 0x7FFFFFFF)
+            for t in pads:   # the filler tile's words: all zero
+                at = lay["blocks"] + (qt * stride + t + 1) * 2048
+                assert not wsb[at:at + 2048].any(), f"query tile {qt}: filler tile {t} has mask words"
+        assert got == want, f"query tile {qt}: list {got} != {want}"
+        sizes.append(len(want))
+    order = w32[lay["order"] // 4:][:items].astype(np.int64)
+    qx, rx = divmod(items, 8)
+    for x in range(8):
+        start, cnt = x * qx + min(x, rx), qx + (1 if x < rx else 0)
+        size = [sizes[n_qt - 1 - (start + j) % n_qt] for j in range(cnt)]
+        want = sorted(range(cnt), key=lambda j: (-size[j], j))
+        assert order[start:start + cnt].tolist() == want, f"XCD {x}: walk order"
+    say("lists, filler words and walk order as expected")
+    # and the output: rows that see no key at all (O = 0, LSE = -inf) beside
+    # items that start on filler tiles
+    check_walk(q, k, v, default_scale(D), "walk mask with fillers", allowed=allowed)
