@@ -438,6 +438,30 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
   #pragma unroll
     for (int i = 0; i < VPW; i += 2)
       voff[i / 2] = slot_off(ws + i * NW, VCH) | (i + 1 < VPW ? slot_off(ws + (i + 1) * NW, VCH) << 16 : 0u);
+    // Lane's slot offset (half `hi` of a packed pair) plus a wave-uniform byte
+    // offset, as one instruction next to the load that uses it (the volatile
+    // asm also keeps the compiler from unpacking every offset once, outside
+    // the loop, into registers of their own).
+    auto slot_plus = [&](uint32_t packed, int hi, int add) -> uint32_t {
+      uint32_t v;
+      if (hi)
+        asm volatile("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 src1_sel:DWORD"
+                     : "=v"(v) : "v"(packed), "s"(add));
+      else
+        asm volatile("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_0 src1_sel:DWORD"
+                     : "=v"(v) : "v"(packed), "s"(add));
+      return v;
+    };
+    // Byte offset of the wave's first block in an LDS tile buffer, passed
+    // through an empty asm once per iteration (relaunder_wofs), so that each
+    // load forms its LDS address (M0) with one add next to it instead of the
+    // compiler keeping all of them (three buffers x NITEM blocks) in scalar
+    // registers across the loop.
+    int wofs_it = ws * 1024;
+    auto relaunder_wofs = [&]() {
+      wofs_it = ws * 1024;
+      asm volatile("" : "+s"(wofs_it));
+    };
     // K and V bytes this (batch, head) may read; the planner keeps M * D * 2
     // below 2^31, so every offset below fits 32 bits.
     const int nrec = (SPLIT ? max(kend - t0 * BK, 0) : kend - t0 * BK) * ROWB;
@@ -446,11 +470,8 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     // LDS address next to its load instead of keeping all of them (three
     // buffers x NITEM blocks) in scalar registers.
     auto load_block = [&](const __bf16* src, int t, __bf16* dst, uint32_t packed, int i) {
-      asm volatile("" : "+v"(packed));  // keep the unpacking next to its use
-      const uint32_t u = (i % 2 ? packed >> 16 : packed & 0xFFFFu) + (uint32_t)t * (BK * ROWB);
-      int wofs = ws * 512;
-      asm volatile("" : "+s"(wofs));
-      buffer_load_lds16(src, nrec, u, (lds_ptr)(dst + wofs + i * NW * 512));
+      const uint32_t u = slot_plus(packed, i % 2, t * (BK * ROWB));
+      buffer_load_lds16(src, nrec, u, (lds_ptr)((char*)dst + wofs_it + i * NW * 1024));
     };
     auto load_k_item = [&](int i, int t, __bf16* dst, const __bf16* src) { load_block(src, t, dst, koff[i / 2], i); };
     auto load_v_item = [&](int i, int t, __bf16* dst, const __bf16* src) { load_block(src, t, dst, voff[i / 2], i); };
@@ -515,13 +536,9 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         }
         const uint32_t packed = j < KPW ? koff[j / 2] : voff[(j - KPW) / 2];
         const int i = j < KPW ? j : j - KPW;
-        uint32_t pk = packed;
-        asm volatile("" : "+v"(pk));  // keep the unpacking next to its use
-        const uint32_t u = (i % 2 ? pk >> 16 : pk & 0xFFFFu) + (uint32_t)(j < KPW ? eK : eV);
-        int wofs = ws * 512;
-        asm volatile("" : "+s"(wofs));
+        const uint32_t u = slot_plus(packed, i % 2, j < KPW ? eK : eV);
         buffer_load_lds16(j < KPW ? (const void*)p.k : (const void*)p.v, nrec_all, u,
-                          (lds_ptr)((j < KPW ? Kdst : Vdst) + wofs + i * NW * 512));
+                          (lds_ptr)((char*)(j < KPW ? Kdst : Vdst) + wofs_it + i * NW * 1024));
         return;
       }
       if (j < KPW) load_k_item(j, tile_index(eK), Kdst, Ksrc);
@@ -858,6 +875,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     auto iteration = [&](int eK, int eV, int eM, const __bf16* Ks, const __bf16* Vs, __bf16* Kdst,
                          __bf16* Vdst, uint32_t* Mdst, const __bf16* Ksrc, const __bf16* Vsrc, bool fresh,
                          bool qwait, int mrow) {
+      relaunder_wofs();
       sm_begin();
       // K operands: a ring of PF + 2, so that a read overwrites a register two
       // fragments after the asm MFMAs last used it
@@ -1097,6 +1115,24 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
       float m_fin[NQB], l_fin[NQB];
   #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) m_fin[qb] = l_fin[qb] = 0.f;
+      // Per item, without a mask: the iterations t at which the loads jump to
+      // the next item's first tile (K at t = n - 4, V at t = n - 2; -1 without
+      // a next item), and, causal without a window, mth: the weighed tile
+      // t + 1 needs masking iff t + 1 >= mth.  A causal wave's tiles that
+      // cross the diagonal or end past kv_len are a suffix of its item: tile
+      // e is masked iff (e + 1) BK > min(kend, qw0 + off + wr + 1), i.e.
+      // e >= that bound / BK.  The next item's first tile (t + 1 = n) always
+      // counts as masked: masking a tile that needs none gives the same
+      // scores, and it saves the per-iteration test of which item the
+      // weighed tile belongs to.
+      int kjump = -1, vjump = -1, jump_to = 0, mth = 0;
+      auto item_marks = [&]() {
+        kjump = has_nx ? n_tiles - 4 : -1;
+        vjump = has_nx ? n_tiles - 2 : -1;
+        jump_to = row_nx * ROWB;
+        mth = min(min(kend, qw0 + off + wr + 1) / BK - t0, n_tiles);
+      };
+      if constexpr (!BITS) item_marks();
       auto cont_step = [&](const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst, const uint32_t* Ms,
                            uint32_t* Mdst) __attribute__((always_inline)) -> bool {
         const int n = n_tiles;
@@ -1105,6 +1141,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         const bool sm_nx = has_nx && t + 1 >= n;
         const int qw_sm = sm_nx ? qw0_n : qw0, t0_sm = sm_nx ? t0_n : t0;
         int e1, e3 = 0, mrow = 0;
+        constexpr bool MTH = CAUSAL && !BITS && !WINDOW;  // the masking test is t + 1 >= mth
         if constexpr (BITS) {
           // the stream runs on into the next item's entries
           e1 = tile_entry(t + 1);
@@ -1117,13 +1154,13 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
           e1 = sm_nx ? t + 1 - n : t + 1;
           // first bytes of K(t+4) and V(t+2) in the whole tensors: a tile on
           // from the last, or the next item's first tile
-          kofs = t + 4 == n && has_nx ? row_nx * ROWB : kofs + BK * ROWB;
-          vofs = t + 2 == n && has_nx ? row_nx * ROWB : vofs + BK * ROWB;
+          kofs = t == kjump ? jump_to : kofs + BK * ROWB;
+          vofs = t == vjump ? jump_to : vofs + BK * ROWB;
         }
         mfma_guard();  // the last iteration's final MFMAs wrote the scores
   #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-        if (need_mask(e1, qw_sm, t0_sm)) apply_mask(e1, qw_sm, t0_sm, sacc, Ms);
+        if (MTH ? t + 1 >= mth : need_mask(e1, qw_sm, t0_sm)) apply_mask(e1, qw_sm, t0_sm, sacc, Ms);
         iteration(kofs, vofs, e3, Ks, Vs, Kdst, Vdst, Mdst, nullptr, nullptr, t == n - 1, has_nx && t == n - 2,
                   mrow);
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NITEM) : "memory");
@@ -1166,6 +1203,7 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         walk_next();
         row_c = (int)bh * M;
         row_nx = (int)bh_n * M + t0_n * BK;
+        if constexpr (!BITS) item_marks();
         t = 0;
         return false;
       };
