@@ -588,6 +588,15 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   // XCD's tiles, heavy and light alternating round by round, as in the
   // forward prefill.
   constexpr bool PERSIST = CAUSAL && !WINDOW && !BITS;
+  // A stage as one pipeline (stage_piped) rather than two ksteps: for plain
+  // causal attention, the one form whose registers hold the scores and dP of
+  // both blocks at D = 128 without spills.  Measured (B = 2, H = 32,
+  // N = 8192, causal, one box, interleaved, bit-identical): the whole
+  // backward 3.556 -> 3.470 ms at D = 128 and 2.140 -> 2.083 ms at D = 64.
+  // With only the second overlap (dS of block 1 under the dQ MFMAs of block
+  // 0), which is all that fits beside a mask or a window, the pass ran 1-2%
+  // slower than two ksteps, so those keep kstep.
+  constexpr bool PIPE = CAUSAL && !WINDOW && !BITS;
   const int64_t n_items = (int64_t)n_qtiles * p.B * p.H;
   const int xcd = blockIdx.x % kNumXcd, u = blockIdx.x / kNumXcd, W = gridDim.x / kNumXcd;
   const int64_t qx = n_items / kNumXcd, rx = n_items % kNumXcd;
@@ -816,6 +825,137 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
+    // A whole stage (64 keys, two 32-key blocks) as a software pipeline, so
+    // that the VALU work of one block runs under the MFMAs of the other:
+    //   1: S and dP of block 0;
+    //   2: S and dP of block 1, with dS of block 0 (one pair of scores every
+    //      second MFMA);
+    //   3: dQ^T += K^T dS^T of block 0, with dS of block 1 (a pair per MFMA);
+    //   4: the same product for block 1.
+    // The arithmetic of every score and every product is kstep's, in the same
+    // order per accumulator, so the result is bitwise the same.  dO sits in
+    // AGPRs as the B operand of dP (Q stays in VGPRs), which leaves room in
+    // the VGPRs for the scores and dP of both blocks.
+    auto stage_piped = [&](int s, const char* Ks, const char* Vs, const uint32_t* Ms, auto MASK)
+                           __attribute__((always_inline)) {
+      constexpr bool mask = decltype(MASK)::value;
+      f32x16 sa[2][NQB], pa[2][NQB];  // scores and dP of blocks 0 and 1
+      bf16x8 sd[2][NQB][2];           // dS of blocks 0 and 1 (16 keys per vector)
+      [[maybe_unused]] uint32_t hid[2][NQB];
+      bf16x8 ka[3], va[3], kt[3];
+      // fragment kb of block kb2 into ring slot `slot`
+      auto read_kv = [&](int kb2, int kb, int slot) __attribute__((always_inline)) {
+        const int o = 32 * kb2 * ROWB + 64 * (kb / 2) + ((kb & 1) ? rbase1 : rbase0);
+        ka[slot] = *lds_at<bf16x8>(Ks, o);
+        va[slot] = *lds_at<bf16x8>(Vs, o);
+      };
+      // MFMA m of the S and dP products of block kb2: fragment kb = m / 4, then
+      // S of query block 0, dP of 0, S of 1, dP of 1 (kstep's order).  Ring
+      // slots continue from block 0 into block 1 (fragment DK kb2 + kb), so a
+      // slot is rewritten only after the MFMAs of the fragments between.
+      auto sdp_step = [&](auto kbc, auto mc) __attribute__((always_inline)) {
+        constexpr int kb2 = decltype(kbc)::value, m = decltype(mc)::value;
+        constexpr int kb = m / 4, qb = (m / 2) % 2, w = m % 2, f = DK * kb2 + kb;
+        if constexpr (m % 4 == 0 && kb + 1 < DK) read_kv(kb2, kb + 1, (f + 1) % 3);
+        if constexpr (w == 0) {
+          if constexpr (kb == 0) mfma_vv0(sa[kb2][qb], ka[f % 3], qf[qb][kb]);
+          else mfma_vv(sa[kb2][qb], ka[f % 3], qf[qb][kb]);
+        } else {
+          if constexpr (kb == 0) mfma_va0(pa[kb2][qb], va[f % 3], gf[qb][kb]);
+          else mfma_va(pa[kb2][qb], va[f % 3], gf[qb][kb]);
+        }
+      };
+      // dS of scores 2 j and 2 j + 1 of query block qb of block kb2 (unit
+      // u = 8 qb + j), as kstep computes each.
+      auto ds_unit = [&](auto kbc, auto uc) __attribute__((always_inline)) {
+        constexpr int kb2 = decltype(kbc)::value, u = decltype(uc)::value, qb = u / 8;
+        const int kk0 = s * St::ROWS + 32 * kb2;
+  #pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * (u % 8) + e;
+          float pv = fast_exp2(fmaf(sa[kb2][qb][r], c, -Lq[qb]));
+          if constexpr (mask) {
+            const int key = kk0 + 8 * (r / 4) + 4 * h + r % 4;
+            bool hide = key > lim[qb];
+            if constexpr (WINDOW) hide = hide | (key < lim_lo[qb]);
+            if constexpr (BITS) hide = hide | (((hid[kb2][qb] >> (8 * (r / 4) + r % 4)) & 1u) != 0u);
+            pv = hide ? 0.f : pv;
+          }
+          sd[kb2][qb][r / 8][r % 8] = (__bf16)(pv * (pa[kb2][qb][r] - Dq[qb]));
+        }
+        // keep the pair's pack here (IR passes would sink it past the
+        // scheduling barrier that follows)
+        asm volatile("" ::"v"(sd[kb2][qb][(2 * (u % 8)) / 8]));
+      };
+      // K^T fragment i of block kb2 (as kstep's read_t) into ring slot `slot`
+      auto read_t = [&](int kb2, int i, int slot) __attribute__((always_inline)) {
+        const int o = (32 * kb2 + 16 * (i / DB)) * ROWB + 64 * (i % DB);
+        const s16x4 klo = lds_read_tr16((const __bf16*)(Ks + o + tbase0));
+        const s16x4 khi = lds_read_tr16((const __bf16*)(Ks + o + tbase1));
+        kt[slot] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(klo, khi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      // MFMA j of dQ^T += K^T dS^T for block kb2: fragment i = j / 2 =
+      // (sp, db), query block j % 2 (kstep's order).
+      auto dq_step = [&](auto kbc, auto jc) __attribute__((always_inline)) {
+        constexpr int kb2 = decltype(kbc)::value, j = decltype(jc)::value;
+        constexpr int i = j / 2, qb = j % 2, sp = i / DB, db = i % DB, f = 2 * DB * kb2 + i;
+        if constexpr (qb == 0 && i + 1 < 2 * DB) read_t(kb2, i + 1, (f + 1) % 3);
+        mfma_aa(dqacc[qb][db], kt[f % 3], sd[kb2][qb][sp]);
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      if constexpr (BITS) {
+  #pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+  #pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) hid[kb2][qb] = ~Ms[ws * 128 + kb2 * 64 + 32 * qb + l32] >> (4 * h);
+      }
+      // 1
+      read_kv(0, 0, 0);
+      static_for<4 * DK>([&](auto mc) {
+        __builtin_amdgcn_sched_barrier(0);
+        sdp_step(I0{}, mc);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) mfma_guard_v(sa[0][qb], pa[0][qb]);
+      // 2
+      read_kv(1, 0, DK % 3);
+      static_for<4 * DK>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        sdp_step(I1{}, mc);
+        constexpr int u0 = m * 16 / (4 * DK), u1 = (m + 1) * 16 / (4 * DK);
+        static_for<u1 - u0>([&](auto uc) { ds_unit(I0{}, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        mfma_guard_v(sa[1][qb], pa[1][qb]);
+        valu_guard(sd[0][qb][0], sd[0][qb][1]);
+      }
+      // 3
+      read_t(0, 0, 0);
+      static_for<4 * DB>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        dq_step(I0{}, jc);
+        constexpr int u0 = j * 16 / (4 * DB), u1 = (j + 1) * 16 / (4 * DB);
+        static_for<u1 - u0>([&](auto uc) { ds_unit(I1{}, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) valu_guard(sd[1][qb][0], sd[1][qb][1]);
+      // 4
+      read_t(1, 0, (2 * DB) % 3);
+      static_for<4 * DB>([&](auto jc) {
+        __builtin_amdgcn_sched_barrier(0);
+        dq_step(I1{}, jc);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_assert(16 % (4 * DB) == 0 && (4 * DK) % 16 == 0, "dS units (16 pairs per block) spread evenly");
+
     // As in the dK/dV pass: uniform branches only, no step skipped in a loop.
     auto iteration = [&](int t, const char* Ks, const char* Vs, const uint32_t* Ms, char* Kn, char* Vn,
                          uint32_t* Mn, auto MASK) __attribute__((always_inline)) {
@@ -823,8 +963,12 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
       __syncthreads();
       const int s_cur = stage_of(t);
       if (t + 1 < n_stages) load_stage(entry_of(t + 1), Kn, Vn, Mn);
-      kstep(s_cur, 0, Ks, Vs, Ms, MASK);
-      kstep(s_cur, 1, Ks, Vs, Ms, MASK);
+      if constexpr (PIPE) {
+        stage_piped(s_cur, Ks, Vs, Ms, MASK);
+      } else {
+        kstep(s_cur, 0, Ks, Vs, Ms, MASK);
+        kstep(s_cur, 1, Ks, Vs, Ms, MASK);
+      }
     };
 
     // Stages before n_clean (an even number) are seen whole by every query of
