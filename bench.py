@@ -676,7 +676,7 @@ COUNTER_LEGS = {
     "mask": [("documents8", "mask_blocks", 2), ("random50", "mask_blocks", 2),
              ("backward_documents8", "bwd_rowstat", 2)],
     "configs": [("B1_H8_N1024_D64_causal", "prefill_bf16", 2), ("B4_H16_N4096_D128_causal", "prefill_cont", 2),
-                ("B4_H16_N4096_D128_noncausal", "prefill_bf16", 2), ("B2_H32_N8192_D64_causal", "prefill_bf16", 2),
+                ("B4_H16_N4096_D128_noncausal", "prefill_bf16", 2), ("B2_H32_N8192_D64_causal", "prefill_cont", 2),
                 ("B1_H8_N1024_D64_causal_split_keys256", "prefill_split", 2)],
     "fp8": [(None, "prefill_fp8", 2)],
     "kvouter": [("tile_per_group", "kvouter", 3), ("head_per_group", "kvouter", 3)],
@@ -685,9 +685,9 @@ COUNTER_LEGS = {
 
 def prefill_kernel_name(w, causal):
     """The kernel the library runs for a prefill without window, mask or
-    kv_len: causal at D = 128 with more 256-query work items than the 256
-    persistent workgroups runs the walk as one pipeline."""
-    if causal and w.D == 128 and w.N >= 256 and w.M >= w.N and w.B * w.H * ((w.N + 255) // 256) > 256:
+    kv_len: causal with more 256-query work items than the 256 persistent
+    workgroups runs the walk as one pipeline."""
+    if causal and w.N >= 256 and w.M >= w.N and w.B * w.H * ((w.N + 255) // 256) > 256:
         return f"prefill_cont_kernel<{w.D}, true, false, false>"
     return f"prefill_bf16_kernel<{w.D}, {str(causal).lower()}, false, false>"
 
@@ -705,7 +705,7 @@ def _short_kernel(name):
 def _leg_of_dispatches(rows):
     """Label the library's launches of the default bench sequence by leg, from
     their order (the bench's call order is fixed)."""
-    seen_kvo, n = False, {"win": 0, "maskp": 0, "d64": 0, "kvo": 0}
+    seen_kvo, n = False, {"win": 0, "maskp": 0, "kvo": 0}
     out = []
     for i, (_, s, ns) in enumerate(rows):
         nxt = rows[i + 1][1] if i + 1 < len(rows) else ""
@@ -736,8 +736,9 @@ def _leg_of_dispatches(rows):
             n["kvo"] += 1
             leg = "kvouter, one query tile per group" if n["kvo"] <= 3 else "kvouter, one head per group"
         elif s == "prefill_bf16_kernel<64, true, false, false>":
-            n["d64"] += 1
-            leg = "configs B1 H8 N1024 D64 causal" if n["d64"] <= 13 else "configs B2 H32 N8192 D64 causal"
+            leg = "configs B1 H8 N1024 D64 causal"
+        elif s == "prefill_cont_kernel<64, true, false, false>":
+            leg = "configs B2 H32 N8192 D64 causal"
         elif s == "prefill_bf16_kernel<128, false, false, false>":
             leg = "configs B4 H16 N4096 D128 non-causal"
         elif s.startswith(("prefill_split", "prefill_merge")):
@@ -765,7 +766,7 @@ def summarize_profiles(d):
     lines = ["# rocprofv3 --stats kernel summary of the default bench sequence (durations in ns), the library's kernels",
              f"# command: {KTRACE_CMD}",
              "# rows aggregate by kernel name: prefill_cont_kernel<128, true, false, false> serves the bench step (N = 8192),",
-             "# the configs leg (N = 4096) and one untimed setup call, and prefill_bf16_kernel<64, true, false, false> two configs;",
+             "# the configs leg (N = 4096) and one untimed setup call;",
              "# kernel_trace_by_leg_default_bench.txt splits the same trace by leg", "#",
              "# kernel, calls, average_ns, min_ns, max_ns, stddev_ns"]
     for r in csv.DictReader(open(os.path.join(d, "ktrace", "run_kernel_stats.csv"))):

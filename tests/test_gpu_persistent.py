@@ -64,8 +64,7 @@ def check_walk(q, k, v, scale, what, rel_o=0.0, causal=True, window=None, allowe
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_walk_several_items_per_workgroup(D):
-    """600 items of 2 query tiles: workgroups run 2 or 3 items back to back
-    (plain causal D = 64 runs item by item; its bits must still agree)."""
+    """600 items of 2 query tiles: workgroups run 2 or 3 items back to back."""
     q, k, v = make(400 + D, 2, 150, 512, 512, D)
     check_walk(q, k, v, default_scale(D), f"walk D={D}")
 
