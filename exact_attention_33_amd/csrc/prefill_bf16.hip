@@ -1125,12 +1125,21 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
       // counts as masked: masking a tile that needs none gives the same
       // scores, and it saves the per-iteration test of which item the
       // weighed tile belongs to.
-      int kjump = -1, vjump = -1, jump_to = 0, mth = 0;
+      // With a window the tiles masked at the band's lower edge are a prefix:
+      // tile e is masked there iff (e + t0) BK < qw0 + QW - 1 + off - wl, i.e.
+      // e < mlo.
+      int kjump = -1, vjump = -1, jump_to = 0, mth = 0, mlo = 0;
       auto item_marks = [&]() {
         kjump = has_nx ? n_tiles - 4 : -1;
         vjump = has_nx ? n_tiles - 2 : -1;
         jump_to = row_nx * ROWB;
         mth = min(min(kend, qw0 + off + wr + 1) / BK - t0, n_tiles);
+        if constexpr (WINDOW) {
+          const int lo_key = qw0 + QW - 1 + off - wl;  // the wave's last query's first key
+          // ceil(lo_key / BK), rounding toward minus infinity for negatives
+          const int lo_tiles = lo_key > 0 ? (lo_key + BK - 1) / BK : -((-lo_key) / BK);
+          mlo = lo_tiles - t0;
+        }
       };
       if constexpr (!BITS) item_marks();
       auto cont_step = [&](const __bf16* Ks, const __bf16* Vs, __bf16* Kdst, __bf16* Vdst, const uint32_t* Ms,
@@ -1141,7 +1150,8 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         const bool sm_nx = has_nx && t + 1 >= n;
         const int qw_sm = sm_nx ? qw0_n : qw0, t0_sm = sm_nx ? t0_n : t0;
         int e1, e3 = 0, mrow = 0;
-        constexpr bool MTH = CAUSAL && !BITS && !WINDOW;  // the masking test is t + 1 >= mth
+        // the masking test is t + 1 >= mth (or t + 1 < mlo with a window)
+        constexpr bool MTH = !BITS && (CAUSAL || WINDOW);
         if constexpr (BITS) {
           // the stream runs on into the next item's entries
           e1 = tile_entry(t + 1);
@@ -1160,7 +1170,8 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         mfma_guard();  // the last iteration's final MFMAs wrote the scores
   #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-        if (MTH ? t + 1 >= mth : need_mask(e1, qw_sm, t0_sm)) apply_mask(e1, qw_sm, t0_sm, sacc, Ms);
+        if (MTH ? (t + 1 >= mth) | (WINDOW && t + 1 < mlo) : need_mask(e1, qw_sm, t0_sm))
+          apply_mask(e1, qw_sm, t0_sm, sacc, Ms);
         iteration(kofs, vofs, e3, Ks, Vs, Kdst, Vdst, Mdst, nullptr, nullptr, t == n - 1, has_nx && t == n - 2,
                   mrow);
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NITEM) : "memory");
