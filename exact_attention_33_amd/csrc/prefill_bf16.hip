@@ -650,13 +650,17 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
         m_use[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
       }
     };
-    // weights of 2 scores (pair `pair` of 16-key half t2 of key block nb)
-    auto exp_pair = [&](f32x16 (&s)[NKB][NQB], int nb, int qb, int t2, int pair) {
+    // weights of 2 scores (pair `pair` of 16-key half t2 of key block nb);
+    // `first`: the pair starts the lane's sums of the block (they were 0, and
+    // 0 + w is w for the weights, which are never -0); not used with a mask,
+    // where the changed code makes the allocator spill more at D = 128
+    auto exp_pair = [&](f32x16 (&s)[NKB][NQB], int nb, int qb, int t2, int pair, bool first = false) {
   #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int e = 2 * pair + h, r = (2 * t2 + e / 4) * 4 + (e % 4);
         const float pv = fast_exp2(fmaf(s[nb][qb][r], c, -m_use[qb]));
-        (nb == 0 ? ps0 : ps1)[qb][h] += pv;
+        if (first) (nb == 0 ? ps0 : ps1)[qb][h] = pv;
+        else (nb == 0 ? ps0 : ps1)[qb][h] += pv;
         pacc[qb][nb * 2 + t2][e] = (__bf16)pv;
       }
     };
@@ -664,11 +668,11 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     // first (the P V products release that half of the weight tile first)
     auto unit_em = [&](f32x16 (&s)[NKB][NQB], auto uc) {
       constexpr int u = decltype(uc)::value, t2 = u / 8, qb = (u / 4) % 2, pair = u % 4;
-      exp_pair(s, 0, qb, t2, pair);
+      exp_pair(s, 0, qb, t2, pair, !BITS && t2 == 0 && pair == 0);
     };
     auto unit_ex = [&](f32x16 (&s)[NKB][NQB], auto uc) {
       constexpr int u = decltype(uc)::value, qb = u / 8, t2 = (u / 4) % 2, pair = u % 4;
-      exp_pair(s, 1, qb, t2, pair);
+      exp_pair(s, 1, qb, t2, pair, !BITS && t2 == 0 && pair == 0);
     };
     // Move row qb's reference to mx (its new row max, base 2): returns the
     // factor e^(m_old - m_new) for everything accumulated so far.
@@ -958,10 +962,15 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
                          const uint32_t* Ms, uint32_t* Mdst) {
       const int e1 = tile_entry(t + 1), e2 = tile_entry(t + 2), e3 = tile_entry(t + 3),
                 e4 = tile_entry(t + 4);
-      mfma_guard();  // the last iteration's final MFMAs wrote the scores
   #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-      if (need_mask(e1, qw0, t0)) apply_mask(e1, qw0, t0, sacc, Ms);
+      // The last iteration's final MFMAs wrote the scores: the mask reads them
+      // at once and waits first; unmasked, the first read is 8 MFMAs into
+      // phase A.
+      if (need_mask(e1, qw0, t0)) {
+        mfma_guard();
+        apply_mask(e1, qw0, t0, sacc, Ms);
+      }
       iteration(e4, e2, e3, Ks, Vs, Kdst, Vdst, Mdst, Kg, Vg, false, false, 0);
       // This wave's loads of the previous iteration (K(t+3), V(t+1)) are done
       // (loads complete in order: only this iteration's NITEM may be pending),
@@ -1167,11 +1176,19 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
           kofs = t == kjump ? jump_to : kofs + BK * ROWB;
           vofs = t == vjump ? jump_to : vofs + BK * ROWB;
         }
-        mfma_guard();  // the last iteration's final MFMAs wrote the scores
+        // the scores' guard only where the mask reads them at once (as
+        // step_tile), but for the masked walk, whose D = 128 form spills more
+        // registers with the guard inside the branch
+        if constexpr (BITS) mfma_guard();
   #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) vis[0][qb] = vis[1][qb] = true;
-        if (MTH ? (t + 1 >= mth) | (WINDOW && t + 1 < mlo) : need_mask(e1, qw_sm, t0_sm))
+        bool nm;
+        if constexpr (MTH) nm = (t + 1 >= mth) | (WINDOW && t + 1 < mlo);
+        else nm = need_mask(e1, qw_sm, t0_sm);
+        if (nm) {
+          if constexpr (!BITS) mfma_guard();
           apply_mask(e1, qw_sm, t0_sm, sacc, Ms);
+        }
         iteration(kofs, vofs, e3, Ks, Vs, Kdst, Vdst, Mdst, nullptr, nullptr, t == n - 1, has_nx && t == n - 2,
                   mrow);
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NITEM) : "memory");
