@@ -164,12 +164,16 @@ def test_bwd_mask_matches_oracle(case):
                         allow=mask_of_head(allowed, b, h))
 
 
-def test_bwd_all_ones_mask_matches_unmasked():
+@pytest.mark.parametrize("D", [64, 128])
+def test_bwd_all_ones_mask_matches_unmasked(D):
     """A mask that keeps every key gives the unmasked gradients bit for bit
-    (the same tiles, the same arithmetic on the kept entries)."""
+    (the same tiles, the same arithmetic on the kept entries; the unmasked
+    causal dQ pass runs a stage as one pipeline, the masked one as two plain
+    steps)."""
     import torch
     dev = torch.device("cuda:0")
-    t = _run(1, 2, 600, 600, 128, True, None, seed=91, device=dev)
+    print(f"[bwd] all-ones mask D={D}", flush=True)
+    t = _run(1, 2, 600, 600, D, True, None, seed=91, device=dev)
     words = fa.pack_mask(torch.ones((1, 1, 600, 600), dtype=torch.bool, device=dev))
     dq, dk, dv = fa.bwd(t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], causal=True, mask=words)
     torch.cuda.synchronize()
