@@ -393,8 +393,7 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
         }
       });
       __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-      for (int kb2 = 0; kb2 < KBW; ++kb2) mfma_guard_v(sacc[kb2], pacc[kb2]);
+      mfma_guard_v4(sacc[0], pacc[0], sacc[1], pacc[1]);
       // P = 2^(S c - Lg), dS = P (dP - D).  Lane: key jw0 + 32 kb2 + l32,
       // register r: query qs0 + 8 (r / 4) + 4 h + r % 4.
       bf16x8 pf[KBW][2], sf[KBW][2];
@@ -778,8 +777,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
         }
       });
       __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) mfma_guard_v(sacc[qb], pacc[qb]);
+      mfma_guard_v4(sacc[0], pacc[0], sacc[1], pacc[1]);
       // Lane: query qw0 + 32 qb + l32; register r: key kk0 + 8 (r / 4) + 4 h + r % 4.
       bf16x8 sf[NQB][2];
       // mask: key kk0 + 8 (r / 4) + 4 h + r % 4 is bit 8 (r / 4) + r % 4 of the
@@ -917,8 +915,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
         sdp_step(I0{}, mc);
       });
       __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) mfma_guard_v(sa[0][qb], pa[0][qb]);
+      mfma_guard_v4(sa[0][0], pa[0][0], sa[0][1], pa[0][1]);
       // 2
       read_kv(1, 0, DK % 3);
       static_for<4 * DK>([&](auto mc) {
@@ -929,11 +926,9 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
         static_for<u1 - u0>([&](auto uc) { ds_unit(I0{}, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
       });
       __builtin_amdgcn_sched_barrier(0);
+      mfma_guard_v4(sa[1][0], pa[1][0], sa[1][1], pa[1][1]);
   #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        mfma_guard_v(sa[1][qb], pa[1][qb]);
-        valu_guard(sd[0][qb][0], sd[0][qb][1]);
-      }
+      for (int qb = 0; qb < NQB; ++qb) valu_guard(sd[0][qb][0], sd[0][qb][1]);
       // 3
       read_t(0, 0, 0);
       static_for<4 * DB>([&](auto jc) {

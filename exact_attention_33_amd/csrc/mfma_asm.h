@@ -43,6 +43,10 @@ __device__ __forceinline__ void mfma_aa(f32x16& d, const bf16x8& a, const bf16x8
 __device__ __forceinline__ void mfma_guard_v(f32x16& x, f32x16& y) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
+// The same for four results at once (one wait covers all of them).
+__device__ __forceinline__ void mfma_guard_v4(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
 __device__ __forceinline__ void mfma_guard_a(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 7" : "+a"(x)); }
 __device__ __forceinline__ void valu_guard(bf16x8& x, bf16x8& y) {
   asm volatile("s_nop 4" : "+v"(x), "+v"(y));

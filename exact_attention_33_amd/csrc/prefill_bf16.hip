@@ -711,12 +711,24 @@ __device__ __forceinline__ void prefill_body(const Problem& p, int n_qtiles, con
     // path is taken to wait for the loads there (its recomputation of a block
     // whose rows keep their reference reproduces the same weights and sum).
     auto sm_check1 = [&](f32x16 (&s)[NKB][NQB], bool qwait) __attribute__((always_inline)) {
-      bool over = CONT && qwait;
+      if constexpr (CONT && !BITS) {
+        if (qwait) {
+          // the reloaded Q is read by the S MFMAs that follow: wait for its
+          // loads, and tie the wait to the Q registers so that no MFMA moves
+          // above it
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  #pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+  #pragma unroll
+            for (int kb = 0; kb < DK; ++kb) asm volatile("" : "+a"(qf[qb][kb]));
+        }
+      }
+      bool over = CONT && BITS && qwait;
   #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
         over |= (ps0[qb][0] + ps0[qb][1] > kSumLimit) | ((m_run[qb] == -INFINITY) & vis[0][qb]);
       if (__builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform, rare
-        if constexpr (CONT) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (CONT && BITS) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         float a[NQB];
         bool up = false;
   #pragma unroll
