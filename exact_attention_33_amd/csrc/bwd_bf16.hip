@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   using St = Stage<D>;
   constexpr int ROWB = St::ROWB;
-  constexpr int KBW = 2;             // 32-key blocks per wave
+  constexpr int KBW = 2;             // 32-key blocks per wave (the guards below name both)
   constexpr int KW = 32 * KBW;       // keys per wave
   constexpr int DK = D / 16;         // k-steps over d
   constexpr int DB = D / 32;         // 32-wide d blocks
@@ -436,8 +436,8 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
           }
         }
       }
-  #pragma unroll
-      for (int kb2 = 0; kb2 < KBW; ++kb2) valu_guard(pf[kb2][0], sf[kb2][0]), valu_guard(pf[kb2][1], sf[kb2][1]);
+      asm volatile("s_nop 4" : "+v"(pf[0][0]), "+v"(sf[0][0]), "+v"(pf[0][1]), "+v"(sf[0][1]),
+                   "+v"(pf[1][0]), "+v"(sf[1][0]), "+v"(pf[1][1]), "+v"(sf[1][1]));  // valu_guard, all eight
       // dV^T += dO^T P, dK^T += Q^T dS over the step's 32 queries; fragment
       // i = (sp, db), operands read one fragment ahead in a ring of three.
       bf16x8 gt[3], qt[3];
@@ -566,7 +566,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   using St = Stage<D>;
   constexpr int ROWB = St::ROWB;
   constexpr int QW = 64;             // queries per wave
-  constexpr int NQB = QW / 32;       // 32-query blocks per wave
+  constexpr int NQB = QW / 32;       // 32-query blocks per wave (two; the guards name both)
   constexpr int DK = D / 16;
   constexpr int DB = D / 32;
   static_assert(NW * QW == kBwdBlockQ, "queries per workgroup");
@@ -801,8 +801,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
           }
           sf[qb][r / 8][r % 8] = (__bf16)(pv * (pacc[qb][r] - Dq[qb]));
         }
-  #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) valu_guard(sf[qb][0], sf[qb][1]);
+      valu_guard4(sf[0][0], sf[0][1], sf[1][0], sf[1][1]);
       // dQ^T += K^T dS^T over the 32 keys; fragment i = (sp, db), operands
       // one fragment ahead in a ring of three.
       bf16x8 kt[3];
@@ -927,8 +926,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
       });
       __builtin_amdgcn_sched_barrier(0);
       mfma_guard_v4(sa[1][0], pa[1][0], sa[1][1], pa[1][1]);
-  #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) valu_guard(sd[0][qb][0], sd[0][qb][1]);
+      valu_guard4(sd[0][0][0], sd[0][0][1], sd[0][1][0], sd[0][1][1]);
       // 3
       read_t(0, 0, 0);
       static_for<4 * DB>([&](auto jc) {
@@ -939,8 +937,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
         static_for<u1 - u0>([&](auto uc) { ds_unit(I1{}, std::integral_constant<int, u0 + decltype(uc)::value>{}); });
       });
       __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) valu_guard(sd[1][qb][0], sd[1][qb][1]);
+      valu_guard4(sd[1][0][0], sd[1][0][1], sd[1][1][0], sd[1][1][1]);
       // 4
       read_t(1, 0, (2 * DB) % 3);
       static_for<4 * DB>([&](auto jc) {

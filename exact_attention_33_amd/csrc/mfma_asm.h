@@ -51,6 +51,10 @@ __device__ __forceinline__ void mfma_guard_a(f32x16& x) { asm volatile("s_nop 7\
 __device__ __forceinline__ void valu_guard(bf16x8& x, bf16x8& y) {
   asm volatile("s_nop 4" : "+v"(x), "+v"(y));
 }
+// The same for four operands at once.
+__device__ __forceinline__ void valu_guard4(bf16x8& a, bf16x8& b, bf16x8& c, bf16x8& d) {
+  asm volatile("s_nop 4" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
 __device__ __forceinline__ void agpr_guard(f32x16& x) { asm volatile("s_nop 4" : "+a"(x)); }
 
 // vmcnt(0), other counters untouched (gfx9 s_waitcnt encoding).
