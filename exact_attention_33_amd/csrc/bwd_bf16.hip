@@ -384,11 +384,11 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
   #pragma unroll
         for (int kb2 = 0; kb2 < KBW; ++kb2) {
           if constexpr (kb == 0) {
-            mfma_vv0(sacc[kb2], qa[kb % 3], kf[kb2][kb]);
-            mfma_vv0(pacc[kb2], ga[kb % 3], vf[kb2][kb]);
+            mfma_vv0_nw(sacc[kb2], qa[kb % 3], kf[kb2][kb]);
+            mfma_vv0_nw(pacc[kb2], ga[kb % 3], vf[kb2][kb]);
           } else {
-            mfma_vv(sacc[kb2], qa[kb % 3], kf[kb2][kb]);
-            mfma_vv(pacc[kb2], ga[kb % 3], vf[kb2][kb]);
+            mfma_vv_nw(sacc[kb2], qa[kb % 3], kf[kb2][kb]);
+            mfma_vv_nw(pacc[kb2], ga[kb % 3], vf[kb2][kb]);
           }
         }
       });
@@ -457,8 +457,8 @@ void bwd_dkdv_kernel(BwdProblem p, int n_ktiles) {
         if constexpr (i + 1 < 2 * DB) read_t(i + 1);
   #pragma unroll
         for (int kb2 = 0; kb2 < KBW; ++kb2) {
-          mfma_aa(dvacc[kb2][db], gt[i % 3], pf[kb2][sp]);
-          mfma_aa(dkacc[kb2][db], qt[i % 3], sf[kb2][sp]);
+          mfma_aa_nw(dvacc[kb2][db], gt[i % 3], pf[kb2][sp]);
+          mfma_aa_nw(dkacc[kb2][db], qt[i % 3], sf[kb2][sp]);
         }
       });
       __builtin_amdgcn_sched_barrier(0);

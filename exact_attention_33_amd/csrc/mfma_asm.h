@@ -38,6 +38,19 @@ __device__ __forceinline__ void mfma_va(f32x16& d, const bf16x8& a, const bf16x8
 __device__ __forceinline__ void mfma_aa(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
+// The same without the 2 leading wait states, for kernels whose compiled code
+// puts no VALU write of an operand within 2 wait states ahead of any MFMA,
+// branch targets included (the assembly scan in the tests checks every
+// kernel for both cases).
+__device__ __forceinline__ void mfma_vv0_nw(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vv_nw(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_aa_nw(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
 // 16 wait states, ordered after the MFMAs that wrote x and y and before
 // every later access to them.
 __device__ __forceinline__ void mfma_guard_v(f32x16& x, f32x16& y) {

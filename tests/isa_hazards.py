@@ -15,8 +15,14 @@ code for:
 
 Wait states: `s_nop N` counts N + 1, every other instruction 1.  The scan is
 linear over the kernel's text (it follows fall-through, not branches), so it
-checks every straight-line stretch the way it is laid out; the guards in the
-kernels do not rely on branch targets.
+checks every straight-line stretch the way it is laid out.  An MFMA right
+after a label may also be reached by a branch: the branch itself counts 1
+wait state, so the instruction before each branch to that label is checked
+as well (3. below); the result guards do not rely on branch targets.
+
+  3. an MFMA reached by a branch fewer than 2 wait states after a VALU write
+     of a register it reads (an MFMA right at the label, after a branch whose
+     previous instruction writes an operand).
 """
 import re
 
@@ -56,11 +62,25 @@ def kernels(asm_text):
         if cur is None:
             continue
         s = line.split(";")[0].strip()
-        if not s or s.endswith(":") or s.startswith("."):
+        if not s:
+            continue
+        if s.endswith(":"):
+            s = "<label> " + s[:-1]   # a branch target
+        elif s.startswith("."):
             continue
         out[cur].append(s)
         if s.startswith("s_endpgm"):
             cur = None
+    return out
+
+
+def _before_branches(lines, name):
+    """The instruction ahead of each branch to label `name`."""
+    out = []
+    for j, s in enumerate(lines):
+        w = s.split()
+        if len(w) == 2 and w[0].startswith(("s_branch", "s_cbranch")) and w[1] == name:
+            out.append(lines[j - 1] if j else "<label>")
     return out
 
 
@@ -70,15 +90,26 @@ def scan(lines):
     mfma_w = {}   # register -> (clock of the MFMA that last wrote it, wait states needed)
     valu_w = {}   # register -> clock of the last VALU write
     found = []
+    label = None  # (clock, name) of the last label
     for i, s in enumerate(lines):
         op = s.split()[0]
+        if op == "<label>":
+            label = (clock, s.split()[1] if len(s.split()) > 1 else "")
+            continue
         if op.startswith("s_nop"):
             clock += int(s.split()[1], 0) + 1
             continue
         clock += 1
         parts = [p.strip() for p in s[len(op):].split(",")]
         if "mfma" in op:
-            for r in set().union(*[_regs(p) for p in parts[1:]]):
+            reads = set().union(*[_regs(p) for p in parts[1:]])
+            if label is not None and clock - label[0] - 1 == 0:
+                # right at a branch target: the branch gives 1 wait state, so
+                # the instruction ahead of it must not write an operand
+                for prev in _before_branches(lines, label[1]):
+                    if prev.startswith("<label>") or (prev.startswith("v_") and _regs(prev.split(",")[0]) & reads):
+                        found.append((i, op, "branch target", 1, 2))
+            for r in reads:
                 if r in valu_w and clock - valu_w[r] < 3:
                     found.append((i, op, r, clock - valu_w[r] - 1, 2))
             need = _NEED[_passes(op)]

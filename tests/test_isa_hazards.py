@@ -40,6 +40,15 @@ def test_scan_catches_planted_hazards():
             "s_nop 1",
             "v_mfma_f32_32x32x16_bf16 v[40:55], v[16:19], v[20:23], 0"]
     assert isa_hazards.scan(good) == []
+    # an MFMA at a branch target: the branch counts one wait state, so the
+    # instruction ahead of each branch to the label is checked too
+    mf = "v_mfma_f32_32x32x16_bf16 v[40:55], v[16:19], v[20:23], 0"
+    tgt = ["v_mov_b32_e32 v17, v3", "s_cbranch_scc1 .L1", "s_nop 7", "<label> .L1", mf]
+    assert [f[2] for f in isa_hazards.scan(tgt)] == ["branch target"]
+    assert isa_hazards.scan(["v_mov_b32_e32 v99, v3"] + tgt[1:]) == []
+    assert isa_hazards.scan(tgt[:4] + ["s_waitcnt lgkmcnt(0)", mf]) == []   # branch + 1
+    ks = isa_hazards.kernels("_Zk:\n  s_nop 0\n.LBB0_1:\n  .p2align 6\n  s_endpgm\n")
+    assert ks["_Zk"] == ["s_nop 0", "<label> .LBB0_1", "s_endpgm"]
     # a 16-pass (fp8) MFMA needs 19
     fp8 = ["v_mfma_f32_32x32x64_f8f6f4 v[0:15], v[16:23], v[24:31], 0", "s_nop 7", "s_nop 7",
            "v_add_f32_e32 v30, v1, v2"]
