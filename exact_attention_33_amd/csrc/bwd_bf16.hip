@@ -768,11 +768,11 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
   #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
           if constexpr (kb == 0) {
-            mfma_vv0(sacc[qb], ka[kb % 3], qf[qb][kb]);
-            mfma_vv0(pacc[qb], va[kb % 3], gf[qb][kb]);
+            mfma_vv0_nw(sacc[qb], ka[kb % 3], qf[qb][kb]);
+            mfma_vv0_nw(pacc[qb], va[kb % 3], gf[qb][kb]);
           } else {
-            mfma_vv(sacc[qb], ka[kb % 3], qf[qb][kb]);
-            mfma_vv(pacc[qb], va[kb % 3], gf[qb][kb]);
+            mfma_vv_nw(sacc[qb], ka[kb % 3], qf[qb][kb]);
+            mfma_vv_nw(pacc[qb], va[kb % 3], gf[qb][kb]);
           }
         }
       });
@@ -817,7 +817,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (i + 1 < 2 * DB) read_t(i + 1);
   #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) mfma_aa(dqacc[qb][db], kt[i % 3], sf[qb][sp]);
+        for (int qb = 0; qb < NQB; ++qb) mfma_aa_nw(dqacc[qb][db], kt[i % 3], sf[qb][sp]);
       });
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -855,9 +855,10 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
         constexpr int kb = m / 4, qb = (m / 2) % 2, w = m % 2, f = DK * kb2 + kb;
         if constexpr (m % 4 == 0 && kb + 1 < DK) read_kv(kb2, kb + 1, (f + 1) % 3);
         if constexpr (w == 0) {
-          if constexpr (kb == 0) mfma_vv0(sa[kb2][qb], ka[f % 3], qf[qb][kb]);
-          else mfma_vv(sa[kb2][qb], ka[f % 3], qf[qb][kb]);
+          if constexpr (kb == 0) mfma_vv0_nw(sa[kb2][qb], ka[f % 3], qf[qb][kb]);
+          else mfma_vv_nw(sa[kb2][qb], ka[f % 3], qf[qb][kb]);
         } else {
+          // dO's fragments are copied into AGPRs right before some of these: keep the wait
           if constexpr (kb == 0) mfma_va0(pa[kb2][qb], va[f % 3], gf[qb][kb]);
           else mfma_va(pa[kb2][qb], va[f % 3], gf[qb][kb]);
         }
@@ -897,7 +898,7 @@ void bwd_dq_kernel(BwdProblem p, int n_qtiles) {
         constexpr int kb2 = decltype(kbc)::value, j = decltype(jc)::value;
         constexpr int i = j / 2, qb = j % 2, sp = i / DB, db = i % DB, f = 2 * DB * kb2 + i;
         if constexpr (qb == 0 && i + 1 < 2 * DB) read_t(kb2, i + 1, (f + 1) % 3);
-        mfma_aa(dqacc[qb][db], kt[f % 3], sd[kb2][qb][sp]);
+        mfma_aa_nw(dqacc[qb][db], kt[f % 3], sd[kb2][qb][sp]);
       };
       using I0 = std::integral_constant<int, 0>;
       using I1 = std::integral_constant<int, 1>;
