@@ -52,14 +52,18 @@ constexpr int kNW8 = kFp8Threads / 64;  // waves per workgroup
 constexpr int kQW8 = 32;                // queries per wave
 
 // D = A B (+ D) on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3).  Inline asm
-// fixes every operand in VGPRs; each MFMA starts with 2 wait states (a VALU
-// write of an operand needs them, and the compiler cannot see into the
-// asm); results are read after mfma8_guard (16 wait states, tied to them).
+// fixes every operand in VGPRs; the compiler cannot see into the asm, so the
+// hazards are kept by hand: a VALU write of an operand needs 2 wait states
+// before the MFMA (the compiled kernels place none closer, branch targets
+// included, which the assembly scan in the tests checks on every build;
+// valu8_guard covers the weights the kernel itself writes), and results are
+// read after mfma8_guard (16 wait states, tied to them; the scan checks that
+// 19 have passed at every read).
 __device__ __forceinline__ void mfma8_0(f32x16& d, const i32x8& a, const i32x8& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma8(f32x16& d, const i32x8& a, const i32x8& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  asm("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma8_guard(f32x16& x, f32x16& y) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
